@@ -1,0 +1,219 @@
+"""W4A16 mixture-of-experts decode layer and dense W4A16 GEMV for MI355X (gfx950).
+
+Python binding of the w4moe C ABI (include/w4moe.h).  The functions below keep
+the C names and only marshal arguments: torch tensors (device memory, streams)
+and numpy arrays (host helpers) become the plain pointers and sizes the library
+takes.  All computation runs in the HIP library; if it is not built, importing
+the binding's entry points raises.
+"""
+
+import ctypes as C
+
+import numpy as np
+
+from ._lib import (  # noqa: F401
+    EXPORTS,
+    W4_ERR_ALIGNMENT,
+    W4_ERR_HIP,
+    W4_ERR_INVALID_ARG,
+    W4_ERR_LAYOUT,
+    W4_ERR_NONFINITE,
+    W4_ERR_RANGE,
+    W4_ERR_UNSUPPORTED,
+    W4_ERR_WORKSPACE,
+    W4_FMT_E2M1_F16S16,
+    W4_FMT_INT4_F16S128,
+    W4_LAYOUT_CANONICAL,
+    W4_OK,
+    MoELayerDesc,
+    W4Error,
+    W4Matrix,
+    check,
+    lib,
+)
+
+GROUP = {W4_FMT_E2M1_F16S16: 16, W4_FMT_INT4_F16S128: 128}
+FORMATS = {"e2m1": W4_FMT_E2M1_F16S16, "int4": W4_FMT_INT4_F16S128}
+
+
+def _torch():
+    import torch
+
+    return torch
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if isinstance(t, np.ndarray):
+        return t.ctypes.data
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        return _torch().cuda.current_stream().cuda_stream
+    return getattr(stream, "cuda_stream", stream)
+
+
+# ------------------------------------------------------------------ host helpers
+
+
+def w4_version():
+    return lib().w4_version().decode()
+
+
+def w4_status_string(status):
+    return lib().w4_status_string(status).decode()
+
+
+def w4_last_error():
+    return lib().w4_last_error().decode()
+
+
+def w4_codes_bytes(fmt, groups, n, k, layout=W4_LAYOUT_CANONICAL):
+    return lib().w4_codes_bytes(fmt, layout, groups, n, k)
+
+
+def w4_scales_bytes(fmt, groups, n, k, layout=W4_LAYOUT_CANONICAL):
+    return lib().w4_scales_bytes(fmt, layout, groups, n, k)
+
+
+def w4_quantize(fmt, w, codes=None, scales=None):
+    """Quantise host fp32 w[n][k]; returns (codes uint8 [n][k/2], scale bits uint16 [n][k/G])."""
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    if w.ndim != 2:
+        raise ValueError("w must be 2-D")
+    n, k = w.shape
+    g = GROUP.get(fmt, 1)
+    if codes is None:
+        codes = np.empty((n, k // 2), dtype=np.uint8)
+    if scales is None:
+        scales = np.empty((n, max(k // g, 1)), dtype=np.uint16)
+    check(lib().w4_quantize(fmt, _ptr(w), n, k, _ptr(codes), _ptr(scales)))
+    return codes, scales
+
+
+def w4_pack_nibbles(nibbles):
+    nib = np.ascontiguousarray(nibbles, dtype=np.uint8)
+    n, k = nib.shape
+    out = np.empty((n, k // 2), dtype=np.uint8)
+    check(lib().w4_pack_nibbles(_ptr(nib), n, k, _ptr(out)))
+    return out
+
+
+def w4_unpack_nibbles(packed):
+    p = np.ascontiguousarray(packed, dtype=np.uint8)
+    n, kh = p.shape
+    out = np.empty((n, 2 * kh), dtype=np.uint8)
+    check(lib().w4_unpack_nibbles(_ptr(p), n, 2 * kh, _ptr(out)))
+    return out
+
+
+# ------------------------------------------------------------------ device matrices
+
+
+class QMatrix:
+    """A stack of quantised matrices in device memory plus its w4_matrix descriptor."""
+
+    def __init__(self, fmt, groups, n, k, codes, scales, layout=W4_LAYOUT_CANONICAL):
+        self.fmt, self.groups, self.n, self.k = fmt, groups, n, k
+        self.codes, self.scales = codes, scales  # torch uint8 / int16 device tensors
+        self.desc = W4Matrix(fmt, layout, groups, n, k, _ptr(codes), _ptr(scales))
+
+    @classmethod
+    def upload(cls, fmt, codes_np, scales_np, device="cuda"):
+        """codes_np [G][n][k/2] (or [n][k/2]), scales_np [G][n][k/Gs] uint16 -> device."""
+        torch = _torch()
+        c = np.ascontiguousarray(codes_np)
+        s = np.ascontiguousarray(scales_np)
+        if c.ndim == 2:
+            c, s = c[None], s[None]
+        groups, n, kh = c.shape
+        tc = torch.from_numpy(c).to(device)
+        ts = torch.from_numpy(s.view(np.int16)).to(device)
+        return cls(fmt, groups, n, 2 * kh, tc, ts)
+
+
+def w4a16_gemv(W, x, y=None, stream=None):
+    """y[m][n] = x[m][k] . W^T (bf16 in and out); x is a [k] or [m][k] bf16 device tensor."""
+    torch = _torch()
+    x2 = x if x.dim() == 2 else x.view(1, -1)
+    m = x2.shape[0]
+    if y is None:
+        y = torch.empty((m, W.n), dtype=torch.bfloat16, device=x.device)
+    check(lib().w4a16_gemv(C.byref(W.desc), _ptr(x2), m, _ptr(y), _stream(stream)))
+    return y if x.dim() == 2 else y.view(-1)
+
+
+def w4_dequant_device(W, out=None, stream=None):
+    torch = _torch()
+    if out is None:
+        out = torch.empty((W.groups, W.n, W.k), dtype=torch.float32, device=W.codes.device)
+    check(lib().w4_dequant_device(C.byref(W.desc), _ptr(out), _stream(stream)))
+    return out
+
+
+# ------------------------------------------------------------------ MoE layer
+
+
+class MoELayer:
+    """Device tensors of one MoE layer plus its moe_w4a16_layer descriptor."""
+
+    def __init__(self, hidden, inter, num_experts, top_k, router_w, w13, w2, router_bias=None,
+                 shared_w13=None, shared_w2=None, shared_gate_w=None):
+        self.hidden, self.inter, self.num_experts, self.top_k = hidden, inter, num_experts, top_k
+        self.router_w, self.router_bias = router_w, router_bias
+        self.w13, self.w2 = w13, w2
+        self.shared_w13, self.shared_w2, self.shared_gate_w = shared_w13, shared_w2, shared_gate_w
+        has_shared = shared_w13 is not None
+        empty = W4Matrix(0, 0, 0, 0, 0, None, None)
+        self.desc = MoELayerDesc(
+            hidden, inter, num_experts, top_k, inter if has_shared else 0,
+            _ptr(router_w), _ptr(router_bias), w13.desc, w2.desc, 1 if has_shared else 0,
+            shared_w13.desc if has_shared else empty, shared_w2.desc if has_shared else empty,
+            _ptr(shared_gate_w),
+        )
+
+    @property
+    def has_shared(self):
+        return self.shared_w13 is not None
+
+
+def moe_w4a16_workspace_bytes(layer, T):
+    n = lib().moe_w4a16_workspace_bytes(C.byref(layer.desc), T)
+    if n == 0:
+        check(W4_ERR_INVALID_ARG)
+    return n
+
+
+def alloc_workspace(layer, T, device="cuda"):
+    torch = _torch()
+    n = moe_w4a16_workspace_bytes(layer, T)
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def moe_w4a16_forward(layer, x, y=None, topk_ids=None, topk_w=None, ws=None, stream=None):
+    """Full MoE layer for x bf16 [T][H]; returns y bf16 [T][H]."""
+    torch = _torch()
+    T = x.shape[0]
+    if y is None:
+        y = torch.empty_like(x)
+    if ws is None:
+        ws = alloc_workspace(layer, T, x.device)
+    check(lib().moe_w4a16_forward(C.byref(layer.desc), _ptr(x), T, _ptr(y), _ptr(topk_ids), _ptr(topk_w),
+                                  _ptr(ws), ws.numel(), _stream(stream)))
+    return y
+
+
+def moe_w4a16_experts(layer, x, ids, w, y=None, ws=None, stream=None):
+    """Experts + combine with given routing: ids int32 [T][k], w fp32 [T][k]."""
+    torch = _torch()
+    T = x.shape[0]
+    if y is None:
+        y = torch.empty_like(x)
+    if ws is None:
+        ws = alloc_workspace(layer, T, x.device)
+    check(lib().moe_w4a16_experts(C.byref(layer.desc), _ptr(x), T, _ptr(ids), _ptr(w), _ptr(y),
+                                  _ptr(ws), ws.numel(), _stream(stream)))
+    return y

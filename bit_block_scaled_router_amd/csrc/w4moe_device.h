@@ -1,0 +1,257 @@
+// Device helpers for the gfx950 W4A16 kernels: bit conversions, in-register
+// decode of the 4-bit codes, 32-element chunk dot products and fixed-order
+// cross-lane reductions.
+//
+// Lane geometry used by every weight-streaming kernel.  A matrix row of K
+// elements is covered by L lanes (L = min(64, next power of two of K/32)); each
+// lane owns 32 consecutive elements per step = 16 bytes of packed codes (one
+// 128-bit load) and, for E2M1, exactly two FP16 scale blocks (one 32-bit load).
+// A wave therefore covers 64/L rows per load and streams 1 KiB of contiguous
+// canonical codes when K is a power of two <= 2048.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace w4k {
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int FMT_E2M1 = 1;
+constexpr int FMT_INT4 = 2;
+
+// ---------------------------------------------------------------- conversions
+
+__device__ __forceinline__ bf16x2 as_bf16x2(uint32_t u) { return __builtin_bit_cast(bf16x2, u); }
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b16) { return __uint_as_float(b16 << 16); }
+
+// fp32 -> bf16 bits, round to nearest even (finite inputs; NaN stays NaN-ish).
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7F800000u) == 0x7F800000u) return (uint16_t)((u >> 16) | ((u & 0xFFFF) ? 0x40 : 0));
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ float f16_bits_to_f32(uint32_t b) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(b & 0xFFFFu));
+}
+
+// a0*b0 + a1*b1 + acc over bf16 pairs, fp32 accumulate (v_dot2c_f32_bf16).
+__device__ __forceinline__ float dot2(bf16x2 a, uint32_t b, float acc) {
+    return __builtin_amdgcn_fdot2_f32_bf16(a, as_bf16x2(b), acc, false);
+}
+
+// Two E2M1 codes (byte B of c: low nibble -> element 0) to two exact bf16.
+template <int B>
+__device__ __forceinline__ bf16x2 e2m1x2_bf16(uint32_t c) {
+    return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c, 1.0f, B);
+}
+template <int B>
+__device__ __forceinline__ f32x2 e2m1x2_f32(uint32_t c) {
+    return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, B);
+}
+
+// int4 decode.  u = nibble ^ 8 is q + 8 in [0, 15].  Spread into bytes, a byte
+// u read as an OCP E4M3 code is exactly u * 2^-9 (subnormal for u < 8, exponent
+// 1 otherwise), so the hardware fp8 conversion with scale 2^9 yields u exactly.
+// lo holds nibbles 0,2,4,6 and hi nibbles 1,3,5,7 of the dword, one per byte.
+__device__ __forceinline__ void int4_split(uint32_t c, uint32_t &lo, uint32_t &hi) {
+    const uint32_t u = c ^ 0x88888888u;
+    lo = u & 0x0F0F0F0Fu;
+    hi = (u >> 4) & 0x0F0F0F0Fu;
+}
+template <bool W>
+__device__ __forceinline__ bf16x2 u4x2_bf16(uint32_t bytes) {
+    return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(bytes, 512.0f, W);
+}
+template <bool W>
+__device__ __forceinline__ f32x2 u4x2_f32(uint32_t bytes) {
+    return __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(bytes, 512.0f, W);
+}
+
+// ---------------------------------------------------------------- reductions
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+
+// Sum over aligned groups of L lanes (L a power of two <= 64); every lane of a
+// group gets the same value (each step adds the same two operands in both
+// partner lanes).  All 64 lanes must be active.
+template <int L>
+__device__ __forceinline__ float group_sum(float v) {
+    if constexpr (L >= 2) v += dpp_f32<0xB1>(v);   // quad_perm [1,0,3,2]: lane ^ 1
+    if constexpr (L >= 4) v += dpp_f32<0x4E>(v);   // quad_perm [2,3,0,1]: lane ^ 2
+    if constexpr (L >= 8) v += dpp_f32<0x141>(v);  // row_half_mirror: the other quad
+    if constexpr (L >= 16) v += dpp_f32<0x140>(v); // row_mirror: the other half-row
+    if constexpr (L >= 32) v += __shfl_xor(v, 16);
+    if constexpr (L >= 64) v += __shfl_xor(v, 32);
+    return v;
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+    v = max(v, dpp_u32<0xB1>(v));
+    v = max(v, dpp_u32<0x4E>(v));
+    v = max(v, dpp_u32<0x141>(v));
+    v = max(v, dpp_u32<0x140>(v));
+    v = max(v, (uint32_t)__shfl_xor((int)v, 16));
+    v = max(v, (uint32_t)__shfl_xor((int)v, 32));
+    return v;
+}
+
+// ---------------------------------------------------------------- activations
+
+// Activation slice of one lane for one step: 32 bf16 values as 16 dwords.  For
+// int4 the pairs are regrouped to match the byte order of int4_split and the
+// slice sum is kept for the +8 offset correction.
+template <int FMT>
+struct XSlice {
+    uint4 v[4];
+    float sum;
+};
+
+template <int FMT>
+__device__ __forceinline__ void load_xslice(XSlice<FMT> &xs, const uint16_t *__restrict__ x, int k0, bool valid) {
+    const uint4 *p = reinterpret_cast<const uint4 *>(x + k0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) xs.v[i] = valid ? p[i] : make_uint4(0, 0, 0, 0);
+}
+
+template <int FMT>
+__device__ __forceinline__ void prep_xslice(XSlice<FMT> &xs) {
+    if constexpr (FMT == FMT_INT4) {
+        // element pairs (0,1),(2,3),(4,5),(6,7) -> (0,2),(4,6),(1,3),(5,7)
+        float s = 0.f;
+        const uint32_t ones = 0x3F803F80u;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint4 a = xs.v[i];
+            s = dot2(as_bf16x2(a.x), ones, s);
+            s = dot2(as_bf16x2(a.y), ones, s);
+            s = dot2(as_bf16x2(a.z), ones, s);
+            s = dot2(as_bf16x2(a.w), ones, s);
+            uint4 b;
+            b.x = __builtin_amdgcn_perm(a.y, a.x, 0x05040100u);  // (x0, x2)
+            b.y = __builtin_amdgcn_perm(a.w, a.z, 0x05040100u);  // (x4, x6)
+            b.z = __builtin_amdgcn_perm(a.y, a.x, 0x07060302u);  // (x1, x3)
+            b.w = __builtin_amdgcn_perm(a.w, a.z, 0x07060302u);  // (x5, x7)
+            xs.v[i] = b;
+        }
+        xs.sum = s;
+    } else {
+        xs.sum = 0.f;
+    }
+}
+
+// ---------------------------------------------------------------- chunk dots
+
+// E2M1: 8 codes of one dword against 8 bf16 activations.
+__device__ __forceinline__ float e2m1_dot8(uint32_t c, uint4 x, float acc) {
+    acc = dot2(e2m1x2_bf16<0>(c), x.x, acc);
+    acc = dot2(e2m1x2_bf16<1>(c), x.y, acc);
+    acc = dot2(e2m1x2_bf16<2>(c), x.z, acc);
+    acc = dot2(e2m1x2_bf16<3>(c), x.w, acc);
+    return acc;
+}
+
+// int4 (offset form u = q + 8): 8 codes of one dword against 8 regrouped bf16.
+__device__ __forceinline__ float u4_dot8(uint32_t c, uint4 x, float acc) {
+    uint32_t lo, hi;
+    int4_split(c, lo, hi);
+    acc = dot2(u4x2_bf16<false>(lo), x.x, acc);
+    acc = dot2(u4x2_bf16<true>(lo), x.y, acc);
+    acc = dot2(u4x2_bf16<false>(hi), x.z, acc);
+    acc = dot2(u4x2_bf16<true>(hi), x.w, acc);
+    return acc;
+}
+
+// One lane's 32 elements (16 bytes of codes + its scales) against bf16
+// activations, added to acc in a fixed order.  E2M1: the dword `sc` holds the
+// two FP16 scales of the lane's two blocks (low half = first block).  int4: the
+// low half of `sc` is the group's scale.
+template <int FMT>
+__device__ __forceinline__ float chunk_dot_bf16(uint4 c, uint32_t sc, const XSlice<FMT> &xs, float acc) {
+    if constexpr (FMT == FMT_E2M1) {
+        float p0 = e2m1_dot8(c.x, xs.v[0], 0.f);
+        p0 = e2m1_dot8(c.y, xs.v[1], p0);
+        float p1 = e2m1_dot8(c.z, xs.v[2], 0.f);
+        p1 = e2m1_dot8(c.w, xs.v[3], p1);
+        acc = fmaf(p0, f16_bits_to_f32(sc), acc);
+        acc = fmaf(p1, f16_bits_to_f32(sc >> 16), acc);
+    } else {
+        float p = u4_dot8(c.x, xs.v[0], 0.f);
+        p = u4_dot8(c.y, xs.v[1], p);
+        p = u4_dot8(c.z, xs.v[2], p);
+        p = u4_dot8(c.w, xs.v[3], p);
+        p = fmaf(-8.f, xs.sum, p);
+        acc = fmaf(p, f16_bits_to_f32(sc), acc);
+    }
+    return acc;
+}
+
+// Same against fp32 activations h[32] (the down projection's SiLU(gate)*up).
+// hs = sum of the 32 activations (int4 offset correction).
+template <int FMT>
+__device__ __forceinline__ float chunk_dot_f32(uint4 c, uint32_t sc, const float4 *h, float hs, float acc) {
+    const uint32_t cw[4] = {c.x, c.y, c.z, c.w};
+    if constexpr (FMT == FMT_E2M1) {
+        float p[2];
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+            float q = 0.f;
+#pragma unroll
+            for (int d = 0; d < 2; ++d) {
+                const uint32_t cd = cw[2 * b + d];
+                const float4 h0 = h[4 * b + 2 * d], h1 = h[4 * b + 2 * d + 1];
+                f32x2 w;
+                w = e2m1x2_f32<0>(cd); q = fmaf(w.x, h0.x, q); q = fmaf(w.y, h0.y, q);
+                w = e2m1x2_f32<1>(cd); q = fmaf(w.x, h0.z, q); q = fmaf(w.y, h0.w, q);
+                w = e2m1x2_f32<2>(cd); q = fmaf(w.x, h1.x, q); q = fmaf(w.y, h1.y, q);
+                w = e2m1x2_f32<3>(cd); q = fmaf(w.x, h1.z, q); q = fmaf(w.y, h1.w, q);
+            }
+            p[b] = q;
+        }
+        acc = fmaf(p[0], f16_bits_to_f32(sc), acc);
+        acc = fmaf(p[1], f16_bits_to_f32(sc >> 16), acc);
+    } else {
+        float q = 0.f;
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+            uint32_t lo, hi;
+            int4_split(cw[d], lo, hi);
+            const float4 h0 = h[2 * d], h1 = h[2 * d + 1];  // elements 8d..8d+7
+            f32x2 w;
+            w = u4x2_f32<false>(lo); q = fmaf(w.x, h0.x, q); q = fmaf(w.y, h0.z, q);  // 0, 2
+            w = u4x2_f32<true>(lo);  q = fmaf(w.x, h1.x, q); q = fmaf(w.y, h1.z, q);  // 4, 6
+            w = u4x2_f32<false>(hi); q = fmaf(w.x, h0.y, q); q = fmaf(w.y, h0.w, q);  // 1, 3
+            w = u4x2_f32<true>(hi);  q = fmaf(w.x, h1.y, q); q = fmaf(w.y, h1.w, q);  // 5, 7
+        }
+        q = fmaf(-8.f, hs, q);
+        acc = fmaf(q, f16_bits_to_f32(sc), acc);
+    }
+    return acc;
+}
+
+// Scale dword of the lane's chunk: E2M1 two FP16 at element k0/16, int4 one at k0/128.
+template <int FMT>
+__device__ __forceinline__ uint32_t load_scales(const uint16_t *__restrict__ srow, int k0) {
+    if constexpr (FMT == FMT_E2M1)
+        return *reinterpret_cast<const uint32_t *>(srow + (k0 >> 4));
+    else
+        return (uint32_t)srow[k0 >> 7];
+}
+
+template <int FMT>
+__device__ __forceinline__ int scales_per_row(int k) {
+    return FMT == FMT_E2M1 ? (k >> 4) : (k >> 7);
+}
+
+}  // namespace w4k

@@ -1,0 +1,213 @@
+// Host side of the w4moe C ABI: status strings, the thread-local error message,
+// size formulas, the offline quantiser and nibble packing.  Nothing here touches
+// the GPU.  Rules are those of include/w4moe.h; sources: "Lynn Engine" article,
+// "Kernel optimisation history" stage P1 (E2M1 + FP16 scale per 16 K elements)
+// and the "cuda_inf" article, "2. INT4 weight quantization" (int4, group 128).
+#include "w4moe_internal.h"
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <thread>
+#include <vector>
+
+namespace w4 {
+
+static thread_local char g_err[512] = "";
+
+int fail(int status, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return status;
+}
+
+void clear_error() { g_err[0] = 0; }
+
+int group_of(int32_t format) {
+    switch (format) {
+    case W4_FMT_E2M1_F16S16: return 16;
+    case W4_FMT_INT4_F16S128: return 128;
+    default: return 0;
+    }
+}
+
+int check_shape(int32_t format, int32_t layout, int64_t groups, int64_t n, int64_t k) {
+    const int g = group_of(format);
+    if (!g) return fail(W4_ERR_LAYOUT, "unknown format tag %d", (int)format);
+    if (layout != W4_LAYOUT_CANONICAL) return fail(W4_ERR_LAYOUT, "unknown layout tag %d", (int)layout);
+    if (groups < 1 || n < 1 || k < 1) return fail(W4_ERR_INVALID_ARG, "groups/n/k must be >= 1");
+    const int64_t kmul = format == W4_FMT_E2M1_F16S16 ? 32 : 128;
+    if (k % kmul) return fail(W4_ERR_INVALID_ARG, "k=%lld must be a multiple of %lld", (long long)k, (long long)kmul);
+    if (groups > (int64_t(1) << 20) || n > (int64_t(1) << 31) || k > (int64_t(1) << 24))
+        return fail(W4_ERR_INVALID_ARG, "matrix dimensions out of range");
+    return W4_OK;
+}
+
+// ---------------------------------------------------------------- fp16 / E2M1
+
+// fp32 -> fp16 bits, round to nearest even; the compiler's _Float16 conversion
+// follows the IEEE default rounding mode.
+static inline uint16_t f32_to_f16_bits(float v) {
+    _Float16 h = (_Float16)v;
+    uint16_t b;
+    std::memcpy(&b, &h, 2);
+    return b;
+}
+
+static inline float f16_bits_to_f32(uint16_t b) {
+    _Float16 h;
+    std::memcpy(&h, &b, 2);
+    return (float)h;
+}
+
+// Nearest E2M1 magnitude code (0..7) to r >= 0, ties to the even code.
+// Magnitudes by code: 0, 0.5, 1, 1.5, 2, 3, 4, 6; the midpoints between
+// neighbours are 0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.  On a midpoint the even
+// code wins, so a midpoint below an even code belongs to the upper interval.
+static inline int e2m1_mag_code(float r) {
+    if (r <= 0.25f) return 0;   // 0.25 ties to code 0
+    if (r < 0.75f) return 1;    // 0.75 ties to code 2
+    if (r <= 1.25f) return 2;   // 1.25 ties to code 2
+    if (r < 1.75f) return 3;    // 1.75 ties to code 4
+    if (r <= 2.5f) return 4;    // 2.5 ties to code 4
+    if (r < 3.5f) return 5;     // 3.5 ties to code 6
+    if (r <= 5.0f) return 6;    // 5 ties to code 6
+    return 7;                   // saturate
+}
+
+static void quantize_rows(int32_t format, const float *w, int64_t r0, int64_t r1, int64_t k,
+                          uint8_t *codes, uint16_t *scales) {
+    const int g = group_of(format);
+    const float qmax = format == W4_FMT_E2M1_F16S16 ? 6.0f : 7.0f;
+    const int64_t nb = k / g;
+    for (int64_t r = r0; r < r1; ++r) {
+        const float *wr = w + r * k;
+        uint8_t *cr = codes + r * (k / 2);
+        for (int64_t b = 0; b < nb; ++b) {
+            const float *wb = wr + b * g;
+            float a = 0.f;
+            for (int i = 0; i < g; ++i) a = std::fmax(a, std::fabs(wb[i]));
+            const uint16_t sb = f32_to_f16_bits(a / qmax);
+            scales[r * nb + b] = sb;
+            const float s = f16_bits_to_f32(sb);
+            for (int i = 0; i < g; i += 2) {
+                uint8_t c2[2];
+                for (int j = 0; j < 2; ++j) {
+                    uint8_t c = 0;
+                    if (s != 0.f) {
+                        const float q = wb[i + j] / s;  // IEEE fp32 division
+                        if (format == W4_FMT_E2M1_F16S16) {
+                            const int m = e2m1_mag_code(std::fabs(q));
+                            c = (uint8_t)(m | ((q < 0.f && m != 0) ? 8 : 0));
+                        } else {
+                            float t = std::nearbyint(q);  // half to even (default mode)
+                            t = std::fmin(7.f, std::fmax(-8.f, t));
+                            c = (uint8_t)(((int)t) & 0xF);
+                        }
+                    }
+                    c2[j] = c;
+                }
+                cr[(b * g + i) / 2] = (uint8_t)(c2[0] | (c2[1] << 4));
+            }
+        }
+    }
+}
+
+}  // namespace w4
+
+using namespace w4;
+
+extern "C" {
+
+const char *w4_status_string(int status) {
+    switch (status) {
+    case W4_OK: return "W4_OK";
+    case W4_ERR_INVALID_ARG: return "W4_ERR_INVALID_ARG";
+    case W4_ERR_LAYOUT: return "W4_ERR_LAYOUT";
+    case W4_ERR_ALIGNMENT: return "W4_ERR_ALIGNMENT";
+    case W4_ERR_UNSUPPORTED: return "W4_ERR_UNSUPPORTED";
+    case W4_ERR_WORKSPACE: return "W4_ERR_WORKSPACE";
+    case W4_ERR_NONFINITE: return "W4_ERR_NONFINITE";
+    case W4_ERR_RANGE: return "W4_ERR_RANGE";
+    case W4_ERR_HIP: return "W4_ERR_HIP";
+    default: return "W4_ERR_UNKNOWN";
+    }
+}
+
+const char *w4_last_error(void) { return g_err; }
+
+const char *w4_version(void) { return "w4moe 0.1 gfx950"; }
+
+size_t w4_codes_bytes(int32_t format, int32_t layout, int64_t groups, int64_t n, int64_t k) {
+    if (check_shape(format, layout, groups, n, k) != W4_OK) return 0;
+    return (size_t)groups * (size_t)n * (size_t)(k / 2);
+}
+
+size_t w4_scales_bytes(int32_t format, int32_t layout, int64_t groups, int64_t n, int64_t k) {
+    if (check_shape(format, layout, groups, n, k) != W4_OK) return 0;
+    return (size_t)groups * (size_t)n * (size_t)(k / group_of(format)) * 2;
+}
+
+int w4_quantize(int32_t format, const float *w, int64_t n, int64_t k, uint8_t *codes, uint16_t *scales) {
+    clear_error();
+    int st = check_shape(format, W4_LAYOUT_CANONICAL, 1, n, k);
+    if (st) return st;
+    if (!w || !codes || !scales) return fail(W4_ERR_INVALID_ARG, "null pointer");
+    const int g = group_of(format);
+    const float qmax = format == W4_FMT_E2M1_F16S16 ? 6.0f : 7.0f;
+    // validate everything before writing anything
+    const int64_t total = n * k;
+    for (int64_t i = 0; i < total; ++i)
+        if (!std::isfinite(w[i])) return fail(W4_ERR_NONFINITE, "non-finite weight at index %lld", (long long)i);
+    for (int64_t b = 0; b < total / g; ++b) {
+        float a = 0.f;
+        for (int i = 0; i < g; ++i) a = std::fmax(a, std::fabs(w[b * g + i]));
+        if (!std::isfinite(f16_bits_to_f32(f32_to_f16_bits(a / qmax))))
+            return fail(W4_ERR_RANGE, "block %lld: scale %g overflows fp16", (long long)b, (double)(a / qmax));
+    }
+    // rows are independent: split them over a few host threads for big matrices
+    unsigned nt = std::thread::hardware_concurrency();
+    nt = nt ? (nt > 16 ? 16 : nt) : 1;
+    if (total < (int64_t(1) << 22) || n < (int64_t)nt) nt = 1;
+    if (nt == 1) {
+        quantize_rows(format, w, 0, n, k, codes, scales);
+    } else {
+        std::vector<std::thread> th;
+        const int64_t per = (n + nt - 1) / nt;
+        for (unsigned t = 0; t < nt; ++t) {
+            const int64_t r0 = t * per, r1 = r0 + per < n ? r0 + per : n;
+            if (r0 >= r1) break;
+            th.emplace_back(quantize_rows, format, w, r0, r1, k, codes, scales);
+        }
+        for (auto &t : th) t.join();
+    }
+    return W4_OK;
+}
+
+int w4_pack_nibbles(const uint8_t *nibbles, int64_t n, int64_t k, uint8_t *packed) {
+    clear_error();
+    if (!nibbles || !packed) return fail(W4_ERR_INVALID_ARG, "null pointer");
+    if (n < 1 || k < 2 || (k & 1)) return fail(W4_ERR_INVALID_ARG, "need n >= 1 and even k >= 2");
+    const int64_t total = n * k;
+    for (int64_t i = 0; i < total; ++i)
+        if (nibbles[i] > 15) return fail(W4_ERR_INVALID_ARG, "nibble value %d > 15 at %lld", nibbles[i], (long long)i);
+    for (int64_t i = 0; i < total / 2; ++i) packed[i] = (uint8_t)(nibbles[2 * i] | (nibbles[2 * i + 1] << 4));
+    return W4_OK;
+}
+
+int w4_unpack_nibbles(const uint8_t *packed, int64_t n, int64_t k, uint8_t *nibbles) {
+    clear_error();
+    if (!nibbles || !packed) return fail(W4_ERR_INVALID_ARG, "null pointer");
+    if (n < 1 || k < 2 || (k & 1)) return fail(W4_ERR_INVALID_ARG, "need n >= 1 and even k >= 2");
+    const int64_t total = n * k;
+    for (int64_t i = 0; i < total / 2; ++i) {
+        nibbles[2 * i] = packed[i] & 0xF;
+        nibbles[2 * i + 1] = packed[i] >> 4;
+    }
+    return W4_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,19 @@
+// Internal declarations shared by the host and device translation units of the
+// w4moe library (status handling and shape checks).
+#pragma once
+
+#include "../../include/w4moe.h"
+
+namespace w4 {
+
+// Record a message for w4_last_error() on this thread and return `status`.
+int fail(int status, const char *fmt, ...);
+void clear_error();
+
+// Scale block length of a format (16 or 128), 0 for an unknown tag.
+int group_of(int32_t format);
+
+// Validate format/layout tags and dimensions of a matrix stack.
+int check_shape(int32_t format, int32_t layout, int64_t groups, int64_t n, int64_t k);
+
+}  // namespace w4

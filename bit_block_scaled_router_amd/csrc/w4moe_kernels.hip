@@ -1,0 +1,773 @@
+// gfx950 kernels and device entry points of the w4moe C ABI (include/w4moe.h).
+//
+// The MoE decode layer runs as three launches on the caller's stream, with no
+// host synchronisation:
+//   k_router   router GEMV logits = Wr x (bf16 weights, fp32 accumulate) plus the
+//              shared-expert gate dot, one wave per row;
+//   k_moe_w13  one launch over every (token, slot, row tile): slot j < k is the
+//              j-th routed expert, slot k the shared expert.  Each wave finds its
+//              expert by ranking the logits itself (softmax over all experts ->
+//              top-k -> renormalise, evaluated as softmax over the k selected
+//              logits), streams gate row i and up row i of that expert's packed
+//              W13 together, and writes h = silu(gate) * up in fp32;
+//   k_moe_down one launch; a block owns a tile of output rows of one token, its
+//              waves take the slots, each dot is scaled by its routing weight (or
+//              the shared gate sigma) and the block sums the slots in slot order
+//              through LDS before one rounding to bf16.  No float atomics.
+// Sources: lynn-engine tutorials index note 06 (router order, sigmoid-gated
+// shared expert); lynn-engine README status notes P28 (gate/up + SiLU over a
+// grouped packed tensor with top-k ids), P29 (down weighted sum), P45 (one-call
+// shape), P46/P48 (atomics drift; row-owning down kernel), P55 (gate and up rows
+// processed together); "Lynn Engine" article stage P1 (packed matvec).
+#include "w4moe_device.h"
+#include "w4moe_internal.h"
+
+#include <hip/hip_runtime.h>
+
+#include <type_traits>
+
+namespace w4k {
+
+// ================================================================= dense GEMV
+
+// y[t][n] = sum_k W[n][k] x[t][k].  A wave owns RT load-groups of 64/L rows.
+template <int FMT, int L, int RT>
+__global__ __launch_bounds__(256) void k_gemv(const uint8_t *__restrict__ codes, const uint16_t *__restrict__ scales,
+                                              const uint16_t *__restrict__ x, uint16_t *__restrict__ y, int n, int k,
+                                              int m) {
+    constexpr int RG = 64 / L;
+    const int lane = threadIdx.x & 63;
+    const int wave = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+    const int lk = lane % L, rsub = lane / L;
+    const int row0 = wave * RT * RG;
+    if (row0 >= n) return;  // uniform per wave
+    const int ks = (k + 32 * L - 1) / (32 * L);
+    const int spr = scales_per_row<FMT>(k);
+    for (int t = 0; t < m; ++t) {
+        float acc[RT];
+#pragma unroll
+        for (int r = 0; r < RT; ++r) acc[r] = 0.f;
+        for (int s = 0; s < ks; ++s) {
+            const int k0 = 32 * (L * s + lk);
+            const bool kv = k0 < k;
+            uint4 cw[RT];
+            uint32_t sw[RT];
+#pragma unroll
+            for (int r = 0; r < RT; ++r) {
+                const int row = row0 + r * RG + rsub;
+                const bool v = kv && row < n;
+                cw[r] = v ? *reinterpret_cast<const uint4 *>(codes + (size_t)row * (k >> 1) + (k0 >> 1))
+                          : make_uint4(0, 0, 0, 0);
+                sw[r] = v ? load_scales<FMT>(scales + (size_t)row * spr, k0) : 0u;
+            }
+            XSlice<FMT> xs;
+            load_xslice<FMT>(xs, x + (size_t)t * k, k0, kv);
+            prep_xslice<FMT>(xs);
+#pragma unroll
+            for (int r = 0; r < RT; ++r) acc[r] = chunk_dot_bf16<FMT>(cw[r], sw[r], xs, acc[r]);
+        }
+#pragma unroll
+        for (int r = 0; r < RT; ++r) {
+            const float v = group_sum<L>(acc[r]);
+            const int row = row0 + r * RG + rsub;
+            if (lk == 0 && row < n) y[(size_t)t * n + row] = f32_to_bf16_rne(v);
+        }
+    }
+}
+
+// ================================================================= dequant hook
+
+// out[row][k] = value(code) * fp32(scale), with the bf16 decode the GEMV uses.
+template <int FMT, int L>
+__global__ __launch_bounds__(256) void k_dequant(const uint8_t *__restrict__ codes, const uint16_t *__restrict__ scales,
+                                                 float *__restrict__ out, int64_t rows, int k) {
+    constexpr int RG = 64 / L;
+    const int lane = threadIdx.x & 63;
+    const int64_t wave = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+    const int lk = lane % L;
+    const int64_t row = wave * RG + lane / L;
+    if (row >= rows) return;
+    const int spr = scales_per_row<FMT>(k);
+    for (int k0 = 32 * lk; k0 < k; k0 += 32 * L) {
+        const uint4 c = *reinterpret_cast<const uint4 *>(codes + row * (k >> 1) + (k0 >> 1));
+        const uint32_t sc = load_scales<FMT>(scales + row * spr, k0);
+        const uint32_t cw[4] = {c.x, c.y, c.z, c.w};
+        float v[32];
+        if constexpr (FMT == FMT_E2M1) {
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+                const float s = f16_bits_to_f32(d < 2 ? sc : (sc >> 16));
+                bf16x2 p;
+                p = e2m1x2_bf16<0>(cw[d]); v[8 * d + 0] = (float)p.x * s; v[8 * d + 1] = (float)p.y * s;
+                p = e2m1x2_bf16<1>(cw[d]); v[8 * d + 2] = (float)p.x * s; v[8 * d + 3] = (float)p.y * s;
+                p = e2m1x2_bf16<2>(cw[d]); v[8 * d + 4] = (float)p.x * s; v[8 * d + 5] = (float)p.y * s;
+                p = e2m1x2_bf16<3>(cw[d]); v[8 * d + 6] = (float)p.x * s; v[8 * d + 7] = (float)p.y * s;
+            }
+        } else {
+            const float s = f16_bits_to_f32(sc);
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+                uint32_t lo, hi;
+                int4_split(cw[d], lo, hi);
+                bf16x2 p;
+                p = u4x2_bf16<false>(lo); v[8 * d + 0] = ((float)p.x - 8.f) * s; v[8 * d + 2] = ((float)p.y - 8.f) * s;
+                p = u4x2_bf16<true>(lo);  v[8 * d + 4] = ((float)p.x - 8.f) * s; v[8 * d + 6] = ((float)p.y - 8.f) * s;
+                p = u4x2_bf16<false>(hi); v[8 * d + 1] = ((float)p.x - 8.f) * s; v[8 * d + 3] = ((float)p.y - 8.f) * s;
+                p = u4x2_bf16<true>(hi);  v[8 * d + 5] = ((float)p.x - 8.f) * s; v[8 * d + 7] = ((float)p.y - 8.f) * s;
+            }
+        }
+        float4 *o = reinterpret_cast<float4 *>(out + row * k + k0);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) o[i] = make_float4(v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]);
+    }
+}
+
+// ================================================================= router
+
+// logits[t][r] for rows r in [r_begin, r_end) of the stacked [E routed rows;
+// 1 shared-gate row]: one wave per row, lane l covers elements 8l + 512s.
+// NS = number of 512-element steps (H <= 512 * NS).
+template <int NS>
+__global__ __launch_bounds__(64) void k_router(const uint16_t *__restrict__ wr, const uint16_t *__restrict__ wsg,
+                                               const uint16_t *__restrict__ x, float *__restrict__ logits, int E,
+                                               int H, int T, int r_begin, int lstride) {
+    const int lane = threadIdx.x;
+    const int r = r_begin + blockIdx.x;
+    const uint16_t *row = r < E ? wr + (size_t)r * H : wsg;
+    uint4 w[NS];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+        const int e0 = 8 * lane + 512 * s;
+        w[s] = e0 < H ? *reinterpret_cast<const uint4 *>(row + e0) : make_uint4(0, 0, 0, 0);
+    }
+    for (int t = 0; t < T; ++t) {
+        float acc = 0.f;
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            const int e0 = 8 * lane + 512 * s;
+            const uint4 xv = e0 < H ? *reinterpret_cast<const uint4 *>(x + (size_t)t * H + e0) : make_uint4(0, 0, 0, 0);
+            acc = dot2(as_bf16x2(w[s].x), xv.x, acc);
+            acc = dot2(as_bf16x2(w[s].y), xv.y, acc);
+            acc = dot2(as_bf16x2(w[s].z), xv.z, acc);
+            acc = dot2(as_bf16x2(w[s].w), xv.w, acc);
+        }
+        acc = group_sum<64>(acc);
+        if (lane == 0) logits[(size_t)t * lstride + r] = acc;
+    }
+}
+
+// ================================================================= top-k
+
+// Order-preserving map of a finite float to uint32 (larger float -> larger key;
+// every finite value maps above 0, which marks a removed entry).
+__device__ __forceinline__ uint32_t order_key(float f) {
+    const uint32_t u = __float_as_uint(f);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// One wave ranks E <= 64*PL logits (+ bias) by descending value, ties to the
+// lower expert id, for `rounds` rounds.  Lane l holds experts l*PL .. l*PL+PL-1,
+// so "lowest lane, then lowest slot" is the lowest id.  Ranking by logit equals
+// ranking by softmax probability (exp is increasing).  Lane j < rounds receives
+// the j-th id and its (biased) logit; the id of round `want` is returned to
+// every lane.
+template <int PL>
+__device__ __forceinline__ int wave_topk(const float *__restrict__ lg, const float *__restrict__ bias, int E,
+                                         int rounds, int want, int &my_id, float &my_val) {
+    const int lane = threadIdx.x & 63;
+    uint32_t key[PL];
+#pragma unroll
+    for (int i = 0; i < PL; ++i) {
+        const int e = lane * PL + i;
+        float v = 0.f;
+        if (e < E) v = lg[e] + (bias ? bias[e] : 0.f);
+        key[i] = e < E ? order_key(v) : 0u;
+    }
+    int sel = 0;
+    my_id = -1;
+    my_val = 0.f;
+    for (int j = 0; j < rounds; ++j) {
+        uint32_t best = key[0];
+        int bi = 0;
+#pragma unroll
+        for (int i = 1; i < PL; ++i)
+            if (key[i] > best) { best = key[i]; bi = i; }
+        const uint32_t m = wave_max_u32(best);
+        const uint64_t mask = __ballot(best == m);
+        const int winner = __ffsll((unsigned long long)mask) - 1;
+        const int wid = __shfl(lane * PL + bi, winner);
+        if (lane == winner) {
+#pragma unroll
+            for (int i = 0; i < PL; ++i)
+                if (i == bi) key[i] = 0u;
+        }
+        if (lane == j) {
+            my_id = wid;
+            my_val = __uint_as_float((m & 0x80000000u) ? (m & 0x7FFFFFFFu) : ~m);
+        }
+        if (j == want) sel = wid;
+    }
+    return sel;
+}
+
+// ================================================================= MoE W13 + SiLU
+
+struct W13Args {
+    const uint8_t *codes;         // routed W13 [E][2I][H/2]
+    const uint16_t *scales;       // routed W13 scales
+    const uint8_t *s_codes;       // shared W13 [2I][H/2] (or null)
+    const uint16_t *s_scales;
+    const uint16_t *x;            // [T][H]
+    const float *logits;          // [T][lstride] (routed mode)
+    const float *bias;            // [E] or null
+    const int32_t *ids_in;        // [T][k] (supplied mode)
+    int32_t *ids_ws;              // [T][k] routing outputs for k_moe_down
+    float *w_ws;                  // [T][k]
+    int32_t *ids_user;            // optional copies for the caller
+    float *w_user;
+    float *h;                     // [T][S][hstride] fp32, order of the down kernel's lanes
+    int H, I, E, K, S, T, tiles, lstride, hstride, route;
+    int L2;                       // lanes per row of the down kernel (h order)
+};
+
+// h index of intermediate element i in the down kernel's lane order: lane lk of
+// step s reads 8 consecutive float4 q = 0..7, so element 32(L2 s + lk) + 4q + c
+// sits at s*32*L2 + (q*L2 + lk)*4 + c.
+__device__ __forceinline__ int h_index(int i, int L2) {
+    const int span = 32 * L2;
+    const int s = i / span, rem = i - s * span;
+    const int lk = rem >> 5, q = (rem & 31) >> 2, c = rem & 3;
+    return s * span + (q * L2 + lk) * 4 + c;
+}
+
+template <int FMT, int L, int RT, int PL>
+__global__ __launch_bounds__(256) void k_moe_w13(W13Args a) {
+    constexpr int RG = 64 / L;
+    const int lane = threadIdx.x & 63;
+    const int wave = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+    const int per_tok = a.S * a.tiles;
+    if (wave >= a.T * per_tok) return;  // uniform per wave
+    const int t = wave / per_tok;
+    const int rem = wave - t * per_tok;
+    const int j = rem / a.tiles;
+    const int tile = rem - j * a.tiles;
+    const int lk = lane % L, rsub = lane / L;
+    const int H = a.H, I = a.I;
+    const int ks = (H + 32 * L - 1) / (32 * L);
+    const int spr = scales_per_row<FMT>(H);
+
+    // which expert: shared slot, routed by this wave's own ranking, or supplied
+    const uint8_t *cbase;
+    const uint16_t *sbase;
+    bool valid = true;
+    if (j == a.K) {
+        cbase = a.s_codes;
+        sbase = a.s_scales;
+    } else {
+        int e;
+        if (a.route) {
+            const bool writer = (j == 0 && tile == 0);
+            int my_id;
+            float my_val;
+            e = wave_topk<PL>(a.logits + (size_t)t * a.lstride, a.bias, a.E, writer ? a.K : j + 1, j, my_id, my_val);
+            if (writer) {
+                // weights = softmax over the k selected logits; lane q holds the
+                // q-th, lane 0 the largest; the sum runs in a fixed lane order
+                const float top = __shfl(my_val, 0);
+                const float ex = lane < a.K ? expf(my_val - top) : 0.f;
+                const float sum = group_sum<64>(ex);
+                if (lane < a.K) {
+                    const float w = ex / sum;
+                    a.ids_ws[t * a.K + lane] = my_id;
+                    a.w_ws[t * a.K + lane] = w;
+                    if (a.ids_user) a.ids_user[t * a.K + lane] = my_id;
+                    if (a.w_user) a.w_user[t * a.K + lane] = w;
+                }
+            }
+        } else {
+            e = a.ids_in[t * a.K + j];
+        }
+        valid = e >= 0 && e < a.E;  // an id out of range reads nothing and poisons h
+        const int eo = valid ? e : 0;
+        cbase = a.codes + (size_t)eo * (2 * I) * (H >> 1);
+        sbase = a.scales + (size_t)eo * (2 * I) * spr;
+    }
+
+    const int i0 = tile * RT * RG;  // first gate row of this tile
+    float ag[RT], au[RT];
+#pragma unroll
+    for (int r = 0; r < RT; ++r) ag[r] = au[r] = 0.f;
+    for (int s = 0; s < ks; ++s) {
+        const int k0 = 32 * (L * s + lk);
+        const bool kv = valid && k0 < H;
+        uint4 cg[RT], cu[RT];
+        uint32_t sg[RT], su[RT];
+#pragma unroll
+        for (int r = 0; r < RT; ++r) {
+            const int i = i0 + r * RG + rsub;
+            const bool v = kv && i < I;
+            const size_t rg = (size_t)i, ru = (size_t)(I + i);
+            cg[r] = v ? *reinterpret_cast<const uint4 *>(cbase + rg * (H >> 1) + (k0 >> 1)) : make_uint4(0, 0, 0, 0);
+            cu[r] = v ? *reinterpret_cast<const uint4 *>(cbase + ru * (H >> 1) + (k0 >> 1)) : make_uint4(0, 0, 0, 0);
+            sg[r] = v ? load_scales<FMT>(sbase + rg * spr, k0) : 0u;
+            su[r] = v ? load_scales<FMT>(sbase + ru * spr, k0) : 0u;
+        }
+        XSlice<FMT> xs;
+        load_xslice<FMT>(xs, a.x + (size_t)t * H, k0, k0 < H);
+        prep_xslice<FMT>(xs);
+#pragma unroll
+        for (int r = 0; r < RT; ++r) {
+            ag[r] = chunk_dot_bf16<FMT>(cg[r], sg[r], xs, ag[r]);
+            au[r] = chunk_dot_bf16<FMT>(cu[r], su[r], xs, au[r]);
+        }
+    }
+    float *hrow = a.h + ((size_t)t * a.S + j) * a.hstride;
+#pragma unroll
+    for (int r = 0; r < RT; ++r) {
+        const float g = group_sum<L>(ag[r]);
+        const float u = group_sum<L>(au[r]);
+        const int i = i0 + r * RG + rsub;
+        if (lk == 0 && i < I) {
+            const float hv = valid ? (g / (1.f + expf(-g))) * u : __builtin_nanf("");
+            hrow[h_index(i, a.L2)] = hv;
+        }
+    }
+}
+
+// ================================================================= MoE down + combine
+
+struct DownArgs {
+    const uint8_t *codes;         // routed W2 [E][H][I/2]
+    const uint16_t *scales;
+    const uint8_t *s_codes;       // shared W2 [H][I/2]
+    const uint16_t *s_scales;
+    const int32_t *ids;           // [T][k]
+    const float *w;               // [T][k]
+    const float *logits;          // [T][lstride]; column E = shared-gate logit
+    const float *h;               // [T][S][hstride]
+    uint16_t *y;                  // [T][H] bf16
+    int H, I, E, K, S, T, lstride, hstride, blocks_per_tok;
+};
+
+// Block = W waves; tile of RT*64/L output rows of one token.  LDS holds one
+// fp32 partial per (slot, row); the final sum runs over slots in order.
+template <int FMT, int L, int RT>
+__global__ __launch_bounds__(1024) void k_moe_down(DownArgs a) {
+    constexpr int RG = 64 / L;
+    constexpr int ROWS = RT * RG;
+    extern __shared__ float part[];  // [S][ROWS]
+    const int lane = threadIdx.x & 63;
+    const int wv = threadIdx.x >> 6;
+    const int nw = blockDim.x >> 6;
+    const int t = blockIdx.x / a.blocks_per_tok;
+    const int row0 = (blockIdx.x - t * a.blocks_per_tok) * ROWS;
+    const int lk = lane % L, rsub = lane / L;
+    const int I = a.I, H = a.H;
+    const int ks = (I + 32 * L - 1) / (32 * L);
+    const int spr = scales_per_row<FMT>(I);
+
+    for (int j = wv; j < a.S; j += nw) {
+        const uint8_t *cbase;
+        const uint16_t *sbase;
+        float coef;
+        bool valid = true;
+        if (j == a.K) {
+            cbase = a.s_codes;
+            sbase = a.s_scales;
+            coef = 1.f / (1.f + expf(-a.logits[(size_t)t * a.lstride + a.E]));
+        } else {
+            const int e = a.ids[t * a.K + j];
+            valid = e >= 0 && e < a.E;
+            const int eo = valid ? e : 0;
+            cbase = a.codes + (size_t)eo * H * (I >> 1);
+            sbase = a.scales + (size_t)eo * H * spr;
+            coef = a.w[t * a.K + j];
+        }
+        const float *hb = a.h + ((size_t)t * a.S + j) * a.hstride;
+        float acc[RT];
+#pragma unroll
+        for (int r = 0; r < RT; ++r) acc[r] = 0.f;
+        for (int s = 0; s < ks; ++s) {
+            const int k0 = 32 * (L * s + lk);
+            const bool kv = valid && k0 < I;
+            uint4 cw[RT];
+            uint32_t sw[RT];
+#pragma unroll
+            for (int r = 0; r < RT; ++r) {
+                const int row = row0 + r * RG + rsub;
+                const bool v = kv && row < H;
+                cw[r] = v ? *reinterpret_cast<const uint4 *>(cbase + (size_t)row * (I >> 1) + (k0 >> 1))
+                          : make_uint4(0, 0, 0, 0);
+                sw[r] = v ? load_scales<FMT>(sbase + (size_t)row * spr, k0) : 0u;
+            }
+            float4 hv[8];
+            const float4 *hp = reinterpret_cast<const float4 *>(hb + (size_t)s * 32 * L) + lk;
+#pragma unroll
+            for (int q = 0; q < 8; ++q) hv[q] = kv ? hp[q * L] : make_float4(0.f, 0.f, 0.f, 0.f);
+            float hs = 0.f;
+            if constexpr (FMT == FMT_INT4) {
+#pragma unroll
+                for (int q = 0; q < 8; ++q) hs += (hv[q].x + hv[q].y) + (hv[q].z + hv[q].w);
+            }
+#pragma unroll
+            for (int r = 0; r < RT; ++r) acc[r] = chunk_dot_f32<FMT>(cw[r], sw[r], hv, hs, acc[r]);
+        }
+#pragma unroll
+        for (int r = 0; r < RT; ++r) {
+            const float v = group_sum<L>(acc[r]);
+            if (lk == 0) part[j * ROWS + r * RG + rsub] = valid ? v * coef : __builtin_nanf("");
+        }
+    }
+    __syncthreads();
+    for (int rr = threadIdx.x; rr < ROWS; rr += blockDim.x) {
+        const int row = row0 + rr;
+        if (row >= H) continue;
+        float v = 0.f;
+        for (int j = 0; j < a.S; ++j) v += part[j * ROWS + rr];
+        a.y[(size_t)t * H + row] = f32_to_bf16_rne(v);
+    }
+}
+
+}  // namespace w4k
+
+// ================================================================= host side
+
+using namespace w4k;
+using w4::fail;
+
+namespace {
+
+int lanes_for(int64_t k) {
+    int64_t need = (k + 31) / 32;
+    int L = 1;
+    while (L < need && L < 64) L <<= 1;
+    return L;
+}
+
+bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+int check_matrix(const w4_matrix *W, const char *what) {
+    if (!W) return fail(W4_ERR_INVALID_ARG, "%s: null matrix", what);
+    int st = w4::check_shape(W->format, W->layout, W->groups, W->n, W->k);
+    if (st) return st;
+    if (!W->codes || !W->scales) return fail(W4_ERR_INVALID_ARG, "%s: null codes/scales", what);
+    if (!aligned(W->codes, 16)) return fail(W4_ERR_ALIGNMENT, "%s: codes not 16-byte aligned", what);
+    if (!aligned(W->scales, 4)) return fail(W4_ERR_ALIGNMENT, "%s: scales not 4-byte aligned", what);
+    if (W->n > (1 << 30) || W->k > (1 << 20)) return fail(W4_ERR_UNSUPPORTED, "%s: dimension too large", what);
+    return W4_OK;
+}
+
+int hip_status(const char *what) {
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(W4_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+    return W4_OK;
+}
+
+// ---------------------------------------------------------------- GEMV launch
+
+template <int FMT, int L>
+void launch_gemv_L(const w4_matrix *W, const uint16_t *x, int m, uint16_t *y, hipStream_t st) {
+    constexpr int RT = L == 64 ? 4 : (L == 32 ? 2 : 1);
+    constexpr int RG = 64 / L;
+    const int n = (int)W->n, k = (int)W->k;
+    const int waves = (n + RT * RG - 1) / (RT * RG);
+    const int wpb = 4;
+    const int blocks = (waves + wpb - 1) / wpb;
+    hipLaunchKernelGGL((k_gemv<FMT, L, RT>), dim3(blocks), dim3(64 * wpb), 0, st, W->codes, W->scales, x, y, n, k, m);
+}
+
+template <int FMT>
+void launch_gemv(const w4_matrix *W, const uint16_t *x, int m, uint16_t *y, hipStream_t st) {
+    switch (lanes_for(W->k)) {
+    case 1: launch_gemv_L<FMT, 1>(W, x, m, y, st); break;
+    case 2: launch_gemv_L<FMT, 2>(W, x, m, y, st); break;
+    case 4: launch_gemv_L<FMT, 4>(W, x, m, y, st); break;
+    case 8: launch_gemv_L<FMT, 8>(W, x, m, y, st); break;
+    case 16: launch_gemv_L<FMT, 16>(W, x, m, y, st); break;
+    case 32: launch_gemv_L<FMT, 32>(W, x, m, y, st); break;
+    default: launch_gemv_L<FMT, 64>(W, x, m, y, st); break;
+    }
+}
+
+template <int FMT, int L>
+void launch_dequant_L(const w4_matrix *W, float *out, hipStream_t st) {
+    constexpr int RG = 64 / L;
+    const int64_t rows = W->groups * W->n;
+    const int64_t waves = (rows + RG - 1) / RG;
+    const int wpb = 4;
+    const int64_t blocks = (waves + wpb - 1) / wpb;
+    hipLaunchKernelGGL((k_dequant<FMT, L>), dim3((unsigned)blocks), dim3(64 * wpb), 0, st, W->codes, W->scales, out,
+                       rows, (int)W->k);
+}
+
+template <int FMT>
+void launch_dequant(const w4_matrix *W, float *out, hipStream_t st) {
+    switch (lanes_for(W->k)) {
+    case 1: launch_dequant_L<FMT, 1>(W, out, st); break;
+    case 2: launch_dequant_L<FMT, 2>(W, out, st); break;
+    case 4: launch_dequant_L<FMT, 4>(W, out, st); break;
+    case 8: launch_dequant_L<FMT, 8>(W, out, st); break;
+    case 16: launch_dequant_L<FMT, 16>(W, out, st); break;
+    case 32: launch_dequant_L<FMT, 32>(W, out, st); break;
+    default: launch_dequant_L<FMT, 64>(W, out, st); break;
+    }
+}
+
+// ---------------------------------------------------------------- MoE plan
+
+constexpr int MAX_TOPK = 16;
+constexpr int MAX_EXPERTS = 1024;  // 64 lanes x 16 logits per lane
+constexpr int MAX_TOKENS = 4096;
+
+struct MoEPlan {
+    int H, I, E, K, S, T;
+    int L13, L2, hstride, lstride;
+    size_t off_logits, off_ids, off_w, off_h, total;
+};
+
+size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+int check_layer(const moe_w4a16_layer *Lr, int64_t T, MoEPlan &p) {
+    if (!Lr) return fail(W4_ERR_INVALID_ARG, "null layer");
+    if (T < 1 || T > MAX_TOKENS) return fail(W4_ERR_INVALID_ARG, "T=%lld out of range [1, %d]", (long long)T, MAX_TOKENS);
+    const int64_t H = Lr->hidden, I = Lr->inter, E = Lr->num_experts, K = Lr->top_k;
+    if (H < 64 || H % 64) return fail(W4_ERR_UNSUPPORTED, "hidden=%lld must be a positive multiple of 64", (long long)H);
+    if (H > (1 << 16) || I < 1 || I > (1 << 16)) return fail(W4_ERR_UNSUPPORTED, "hidden/inter too large");
+    if (E < 1 || E > MAX_EXPERTS) return fail(W4_ERR_UNSUPPORTED, "num_experts=%lld out of [1, %d]", (long long)E, MAX_EXPERTS);
+    if (K < 1 || K > E || K > MAX_TOPK) return fail(W4_ERR_INVALID_ARG, "top_k=%lld out of [1, min(E, %d)]", (long long)K, MAX_TOPK);
+    if (!Lr->router_w) return fail(W4_ERR_INVALID_ARG, "null router_w");
+    if (!aligned(Lr->router_w, 16)) return fail(W4_ERR_ALIGNMENT, "router_w not 16-byte aligned");
+    int st;
+    if ((st = check_matrix(&Lr->w13, "w13"))) return st;
+    if ((st = check_matrix(&Lr->w2, "w2"))) return st;
+    const int32_t fmt = Lr->w13.format;
+    if (Lr->w2.format != fmt) return fail(W4_ERR_LAYOUT, "w13 and w2 formats differ");
+    if (Lr->w13.groups != E || Lr->w13.n != 2 * I || Lr->w13.k != H)
+        return fail(W4_ERR_INVALID_ARG, "w13 must be [E][2I][H]");
+    if (Lr->w2.groups != E || Lr->w2.n != H || Lr->w2.k != I) return fail(W4_ERR_INVALID_ARG, "w2 must be [E][H][I]");
+    if (Lr->has_shared != 0 && Lr->has_shared != 1) return fail(W4_ERR_INVALID_ARG, "has_shared must be 0 or 1");
+    if (Lr->has_shared) {
+        if (Lr->shared_inter != I)
+            return fail(W4_ERR_UNSUPPORTED, "shared_inter=%lld must equal inter=%lld", (long long)Lr->shared_inter, (long long)I);
+        if ((st = check_matrix(&Lr->shared_w13, "shared_w13"))) return st;
+        if ((st = check_matrix(&Lr->shared_w2, "shared_w2"))) return st;
+        if (Lr->shared_w13.format != fmt || Lr->shared_w2.format != fmt)
+            return fail(W4_ERR_LAYOUT, "shared expert format differs from the routed experts");
+        if (Lr->shared_w13.groups != 1 || Lr->shared_w13.n != 2 * I || Lr->shared_w13.k != H)
+            return fail(W4_ERR_INVALID_ARG, "shared_w13 must be [1][2I][H]");
+        if (Lr->shared_w2.groups != 1 || Lr->shared_w2.n != H || Lr->shared_w2.k != I)
+            return fail(W4_ERR_INVALID_ARG, "shared_w2 must be [1][H][I]");
+        if (!Lr->shared_gate_w) return fail(W4_ERR_INVALID_ARG, "null shared_gate_w");
+        if (!aligned(Lr->shared_gate_w, 16)) return fail(W4_ERR_ALIGNMENT, "shared_gate_w not 16-byte aligned");
+    }
+    if (Lr->router_bias && !aligned(Lr->router_bias, 4)) return fail(W4_ERR_ALIGNMENT, "router_bias not aligned");
+    p.H = (int)H, p.I = (int)I, p.E = (int)E, p.K = (int)K, p.T = (int)T;
+    p.S = (int)K + (Lr->has_shared ? 1 : 0);
+    p.L13 = lanes_for(H);
+    p.L2 = lanes_for(I);
+    const int ks2 = (int)((I + 32 * p.L2 - 1) / (32 * p.L2));
+    p.hstride = ks2 * 32 * p.L2;
+    p.lstride = (int)align_up((size_t)E + 1, 64);
+    size_t off = 0;
+    p.off_logits = off; off = align_up(off + (size_t)T * p.lstride * 4, 256);
+    p.off_ids = off;    off = align_up(off + (size_t)T * K * 4, 256);
+    p.off_w = off;      off = align_up(off + (size_t)T * K * 4, 256);
+    p.off_h = off;      off = align_up(off + (size_t)T * p.S * p.hstride * 4, 256);
+    p.total = off;
+    return W4_OK;
+}
+
+int launch_router(const moe_w4a16_layer *Lr, const MoEPlan &p, const uint16_t *x, float *logits, int r_begin,
+                  int r_end, hipStream_t st) {
+    const int nrows = r_end - r_begin;
+    if (nrows <= 0) return W4_OK;
+    const int ns = (p.H + 511) / 512;
+    auto go = [&](auto NSc) {
+        constexpr int NS = decltype(NSc)::value;
+        hipLaunchKernelGGL((k_router<NS>), dim3(nrows), dim3(64), 0, st, Lr->router_w, Lr->shared_gate_w, x, logits,
+                           p.E, p.H, p.T, r_begin, p.lstride);
+    };
+    if (ns <= 1) go(std::integral_constant<int, 1>());
+    else if (ns <= 2) go(std::integral_constant<int, 2>());
+    else if (ns <= 4) go(std::integral_constant<int, 4>());
+    else if (ns <= 8) go(std::integral_constant<int, 8>());
+    else if (ns <= 16) go(std::integral_constant<int, 16>());
+    else return fail(W4_ERR_UNSUPPORTED, "hidden=%d too large for the router kernel", p.H);
+    return W4_OK;
+}
+
+template <int FMT, int L>
+void launch_w13_L(const MoEPlan &p, W13Args &a, hipStream_t st) {
+    constexpr int RT = L == 64 ? 4 : (L == 32 ? 2 : 1);
+    constexpr int RG = 64 / L;
+    a.tiles = (p.I + RT * RG - 1) / (RT * RG);
+    const int waves = p.T * p.S * a.tiles;
+    const int wpb = 4;
+    const int blocks = (waves + wpb - 1) / wpb;
+    const int pl = (p.E + 63) / 64;
+    if (pl <= 1) hipLaunchKernelGGL((k_moe_w13<FMT, L, RT, 1>), dim3(blocks), dim3(64 * wpb), 0, st, a);
+    else if (pl <= 2) hipLaunchKernelGGL((k_moe_w13<FMT, L, RT, 2>), dim3(blocks), dim3(64 * wpb), 0, st, a);
+    else if (pl <= 4) hipLaunchKernelGGL((k_moe_w13<FMT, L, RT, 4>), dim3(blocks), dim3(64 * wpb), 0, st, a);
+    else if (pl <= 8) hipLaunchKernelGGL((k_moe_w13<FMT, L, RT, 8>), dim3(blocks), dim3(64 * wpb), 0, st, a);
+    else hipLaunchKernelGGL((k_moe_w13<FMT, L, RT, 16>), dim3(blocks), dim3(64 * wpb), 0, st, a);
+}
+
+template <int FMT>
+void launch_w13(const MoEPlan &p, W13Args &a, hipStream_t st) {
+    switch (p.L13) {
+    case 1: launch_w13_L<FMT, 1>(p, a, st); break;
+    case 2: launch_w13_L<FMT, 2>(p, a, st); break;
+    case 4: launch_w13_L<FMT, 4>(p, a, st); break;
+    case 8: launch_w13_L<FMT, 8>(p, a, st); break;
+    case 16: launch_w13_L<FMT, 16>(p, a, st); break;
+    case 32: launch_w13_L<FMT, 32>(p, a, st); break;
+    default: launch_w13_L<FMT, 64>(p, a, st); break;
+    }
+}
+
+template <int FMT, int L>
+void launch_down_L(const MoEPlan &p, DownArgs &a, hipStream_t st) {
+    constexpr int RG = 64 / L;
+    constexpr int RT = RG >= 8 ? 1 : (8 / RG > 4 ? 4 : 8 / RG);
+    constexpr int ROWS = RT * RG;
+    a.blocks_per_tok = (p.H + ROWS - 1) / ROWS;
+    const int nw = p.S < 16 ? p.S : 16;
+    const size_t lds = (size_t)p.S * ROWS * sizeof(float);
+    hipLaunchKernelGGL((k_moe_down<FMT, L, RT>), dim3(p.T * a.blocks_per_tok), dim3(64 * nw), lds, st, a);
+}
+
+template <int FMT>
+void launch_down(const MoEPlan &p, DownArgs &a, hipStream_t st) {
+    switch (p.L2) {
+    case 1: launch_down_L<FMT, 1>(p, a, st); break;
+    case 2: launch_down_L<FMT, 2>(p, a, st); break;
+    case 4: launch_down_L<FMT, 4>(p, a, st); break;
+    case 8: launch_down_L<FMT, 8>(p, a, st); break;
+    case 16: launch_down_L<FMT, 16>(p, a, st); break;
+    case 32: launch_down_L<FMT, 32>(p, a, st); break;
+    default: launch_down_L<FMT, 64>(p, a, st); break;
+    }
+}
+
+int run_moe(const moe_w4a16_layer *Lr, const uint16_t *x, int64_t T, const int32_t *ids_in, const float *w_in,
+            uint16_t *y, int32_t *topk_ids, float *topk_w, void *ws, size_t ws_bytes, void *stream) {
+    MoEPlan p;
+    int st = check_layer(Lr, T, p);
+    if (st) return st;
+    if (!x || !y) return fail(W4_ERR_INVALID_ARG, "null x or y");
+    if (!aligned(x, 16)) return fail(W4_ERR_ALIGNMENT, "x not 16-byte aligned");
+    if (!aligned(y, 2)) return fail(W4_ERR_ALIGNMENT, "y not 2-byte aligned");
+    if (!ws) return fail(W4_ERR_WORKSPACE, "null workspace");
+    if (!aligned(ws, 256)) return fail(W4_ERR_ALIGNMENT, "workspace not 256-byte aligned");
+    if (ws_bytes < p.total) return fail(W4_ERR_WORKSPACE, "workspace %zu < required %zu bytes", ws_bytes, p.total);
+    const bool route = ids_in == nullptr;
+    if (!route && !w_in) return fail(W4_ERR_INVALID_ARG, "null routing weights");
+    if ((topk_ids && !aligned(topk_ids, 4)) || (topk_w && !aligned(topk_w, 4)) || (ids_in && !aligned(ids_in, 4)) ||
+        (w_in && !aligned(w_in, 4)))
+        return fail(W4_ERR_ALIGNMENT, "routing arrays not 4-byte aligned");
+    hipStream_t sm = (hipStream_t)stream;
+    char *wsb = (char *)ws;
+    float *logits = (float *)(wsb + p.off_logits);
+    int32_t *ids_ws = (int32_t *)(wsb + p.off_ids);
+    float *w_ws = (float *)(wsb + p.off_w);
+    float *h = (float *)(wsb + p.off_h);
+
+    (void)hipGetLastError();  // clear a stale error so the checks below see only ours
+    // 1) router logits (all experts + shared gate) or just the shared gate
+    if (route) st = launch_router(Lr, p, x, logits, 0, p.E + (Lr->has_shared ? 1 : 0), sm);
+    else if (Lr->has_shared) st = launch_router(Lr, p, x, logits, p.E, p.E + 1, sm);
+    if (st) return st;
+    if ((st = hip_status("router launch"))) return st;
+
+    // 2) W13 + SiLU over all (token, slot, tile)
+    W13Args a{};
+    a.codes = Lr->w13.codes;
+    a.scales = Lr->w13.scales;
+    a.s_codes = Lr->has_shared ? Lr->shared_w13.codes : nullptr;
+    a.s_scales = Lr->has_shared ? Lr->shared_w13.scales : nullptr;
+    a.x = x;
+    a.logits = logits;
+    a.bias = Lr->router_bias;
+    a.ids_in = ids_in;
+    a.ids_ws = ids_ws;
+    a.w_ws = w_ws;
+    a.ids_user = route ? topk_ids : nullptr;
+    a.w_user = route ? topk_w : nullptr;
+    a.h = h;
+    a.H = p.H, a.I = p.I, a.E = p.E, a.K = p.K, a.S = p.S, a.T = p.T;
+    a.lstride = p.lstride, a.hstride = p.hstride, a.route = route ? 1 : 0, a.L2 = p.L2;
+    if (Lr->w13.format == W4_FMT_E2M1_F16S16) launch_w13<FMT_E2M1>(p, a, sm);
+    else launch_w13<FMT_INT4>(p, a, sm);
+    if ((st = hip_status("w13 launch"))) return st;
+
+    // 3) down projection + weighted combine
+    DownArgs d{};
+    d.codes = Lr->w2.codes;
+    d.scales = Lr->w2.scales;
+    d.s_codes = Lr->has_shared ? Lr->shared_w2.codes : nullptr;
+    d.s_scales = Lr->has_shared ? Lr->shared_w2.scales : nullptr;
+    d.ids = route ? ids_ws : ids_in;
+    d.w = route ? w_ws : w_in;
+    d.logits = logits;
+    d.h = h;
+    d.y = y;
+    d.H = p.H, d.I = p.I, d.E = p.E, d.K = p.K, d.S = p.S, d.T = p.T;
+    d.lstride = p.lstride, d.hstride = p.hstride;
+    if (Lr->w2.format == W4_FMT_E2M1_F16S16) launch_down<FMT_E2M1>(p, d, sm);
+    else launch_down<FMT_INT4>(p, d, sm);
+    return hip_status("down launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+int w4a16_gemv(const w4_matrix *W, const uint16_t *x, int64_t m, uint16_t *y, void *stream) {
+    w4::clear_error();
+    int st = check_matrix(W, "W");
+    if (st) return st;
+    if (W->groups != 1) return fail(W4_ERR_INVALID_ARG, "gemv needs groups == 1");
+    if (m < 1 || m > 64) return fail(W4_ERR_UNSUPPORTED, "m=%lld out of [1, 64]", (long long)m);
+    if (!x || !y) return fail(W4_ERR_INVALID_ARG, "null x or y");
+    if (!aligned(x, 16)) return fail(W4_ERR_ALIGNMENT, "x not 16-byte aligned");
+    if (!aligned(y, 2)) return fail(W4_ERR_ALIGNMENT, "y not 2-byte aligned");
+    (void)hipGetLastError();
+    hipStream_t sm = (hipStream_t)stream;
+    if (W->format == W4_FMT_E2M1_F16S16) launch_gemv<FMT_E2M1>(W, x, (int)m, y, sm);
+    else launch_gemv<FMT_INT4>(W, x, (int)m, y, sm);
+    return hip_status("gemv launch");
+}
+
+int w4_dequant_device(const w4_matrix *W, float *out, void *stream) {
+    w4::clear_error();
+    int st = check_matrix(W, "W");
+    if (st) return st;
+    if (!out) return fail(W4_ERR_INVALID_ARG, "null out");
+    if (!aligned(out, 16)) return fail(W4_ERR_ALIGNMENT, "out not 16-byte aligned");
+    (void)hipGetLastError();
+    hipStream_t sm = (hipStream_t)stream;
+    if (W->format == W4_FMT_E2M1_F16S16) launch_dequant<FMT_E2M1>(W, out, sm);
+    else launch_dequant<FMT_INT4>(W, out, sm);
+    return hip_status("dequant launch");
+}
+
+size_t moe_w4a16_workspace_bytes(const moe_w4a16_layer *L, int64_t T) {
+    MoEPlan p;
+    if (check_layer(L, T, p) != W4_OK) return 0;
+    return p.total;
+}
+
+int moe_w4a16_forward(const moe_w4a16_layer *L, const uint16_t *x, int64_t T, uint16_t *y, int32_t *topk_ids,
+                      float *topk_w, void *ws, size_t ws_bytes, void *stream) {
+    w4::clear_error();
+    return run_moe(L, x, T, nullptr, nullptr, y, topk_ids, topk_w, ws, ws_bytes, stream);
+}
+
+int moe_w4a16_experts(const moe_w4a16_layer *L, const uint16_t *x, int64_t T, const int32_t *ids, const float *w,
+                      uint16_t *y, void *ws, size_t ws_bytes, void *stream) {
+    w4::clear_error();
+    if (!ids) return fail(W4_ERR_INVALID_ARG, "null ids");
+    return run_moe(L, x, T, ids, w, y, nullptr, nullptr, ws, ws_bytes, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,203 @@
+/*
+ * w4moe.h - C ABI of the W4A16 mixture-of-experts decode layer and the dense
+ * W4A16 GEMV for AMD Instinct MI355X (gfx950).
+ *
+ * Method sources (cited by page title and section):
+ *   [LE]   "Lynn Engine" article (zingnex.cn): "Native NVFP4 quantization support"
+ *          (W4A16: 4-bit weights, bf16 activations) and "Kernel optimisation
+ *          history", stage P1 (packed E2M1 codes + an FP16 scale per 16 K
+ *          elements read directly by the matvec; 8192x2048 = 10.00 MiB vs 32.00).
+ *   [README] lynn-engine README (GitHub), status notes: P28 gate_up_silu
+ *          (grouped packed experts + per-16 scale + top-k ids -> [top_k, I]),
+ *          P29 down_weighted_sum ([top_k, I] + routing weights -> [H]),
+ *          P45 one-call active-MoE ABI (hidden, expert_ids, routing_weights,
+ *          gate_up, down -> out[H]), P46/P48 (no float atomics; output rows owned
+ *          by one block), P35 (sorted top-k), P23 (int32 expert ids),
+ *          P59 (unknown layouts fail loudly).
+ *   [TUT]  lynn-engine tutorials index: note 06 (router = softmax over all experts
+ *          -> top-K -> renormalise, plus a sigmoid-gated shared expert) and the
+ *          Qwen 3.6 35B-A3B configuration block (hidden 2048, 256 experts, top-8).
+ *   [CI]   "cuda_inf" article: "2. INT4 weight quantization" (signed int4, one
+ *          scale per group of 128 along K, fp32 accumulate).
+ *
+ * Conventions (all entry points):
+ *   - Status: 0 = W4_OK, negative = error.  Every argument is validated before
+ *     anything is launched; on error nothing is launched and w4_last_error()
+ *     returns a message for the calling thread.  An unknown format or layout tag
+ *     is an error, never a fallback.
+ *   - Ownership: the caller owns every buffer.  The library never allocates,
+ *     frees or synchronises device memory.
+ *   - Device entry points are asynchronous on `stream` (a hipStream_t; NULL is
+ *     the default stream): outputs are valid once the stream reaches the work.
+ *   - Host entry points (sizes, quantise, pack) never touch the GPU, so they work
+ *     on a machine without one.
+ *   - bf16 and fp16 values are passed as their 16-bit patterns (uint16_t).
+ *   - Results are deterministic: fixed reduction orders, no float atomics.
+ *   - Thread safety: no global mutable state besides the thread-local error
+ *     message; concurrent calls on distinct streams with distinct outputs and
+ *     workspaces are safe.
+ */
+#ifndef W4MOE_H
+#define W4MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ------------------------------------------------------------------ status */
+#define W4_OK 0
+#define W4_ERR_INVALID_ARG (-1)   /* null pointer, bad size or count            */
+#define W4_ERR_LAYOUT (-2)        /* unknown format or layout tag, or mismatch  */
+#define W4_ERR_ALIGNMENT (-3)     /* pointer not aligned as documented          */
+#define W4_ERR_UNSUPPORTED (-4)   /* valid request this build does not serve    */
+#define W4_ERR_WORKSPACE (-5)     /* workspace missing or too small             */
+#define W4_ERR_NONFINITE (-6)     /* quantise: Inf or NaN in the input          */
+#define W4_ERR_RANGE (-7)         /* quantise: block scale overflows fp16       */
+#define W4_ERR_HIP (-8)           /* a HIP runtime call or launch failed        */
+
+/* ------------------------------------------------------------------ formats */
+/* E2M1 codes (OCP MX FP4: 1 sign, 2 exponent bits bias 1, 1 mantissa bit) with
+ * one FP16 scale per 16 consecutive K elements [LE stage P1]. */
+#define W4_FMT_E2M1_F16S16 1
+/* Two's-complement int4 codes in [-8, 7] with one FP16 scale per 128 K
+ * elements [CI "2. INT4 weight quantization"]. */
+#define W4_FMT_INT4_F16S128 2
+
+/* Canonical layout, the only one this library reads:
+ *   codes  [groups][n][k/2] bytes, element 2j in the low nibble of byte j and
+ *          element 2j+1 in the high nibble;
+ *   scales [groups][n][k/G] fp16 bit patterns, G = 16 (E2M1) or 128 (int4).
+ * With y = W x, a row is one output element.  A wave streams 1 KiB of one
+ * row's codes per 128-bit load (64 lanes x 16 B = 32 elements per lane, two
+ * whole E2M1 scale blocks), so this layout already gives 128-bit coalesced
+ * HBM loads with every scale block owned by a single lane. */
+#define W4_LAYOUT_CANONICAL 0
+
+/* A stack of `groups` quantised matrices W[g] of shape [n][k] (y = W x).
+ * Requirements: k % 32 == 0 (E2M1) or k % 128 == 0 (int4); codes 16-byte
+ * aligned; scales 4-byte aligned; both in device memory for device calls. */
+typedef struct w4_matrix {
+    int32_t format;          /* W4_FMT_*                                   */
+    int32_t layout;          /* W4_LAYOUT_*                                */
+    int64_t groups;          /* number of stacked matrices (experts)       */
+    int64_t n;               /* rows per matrix                            */
+    int64_t k;               /* columns = reduction length                 */
+    const uint8_t *codes;    /* packed codes, see the layout above         */
+    const uint16_t *scales;  /* fp16 scale bit patterns                    */
+} w4_matrix;
+
+/* ------------------------------------------------------------------ errors */
+/* Name of a status code ("W4_OK", "W4_ERR_LAYOUT", ...); never NULL. */
+const char *w4_status_string(int status);
+/* Message describing the last failing call on this thread ("" if none). */
+const char *w4_last_error(void);
+/* Library version string. */
+const char *w4_version(void);
+
+/* ------------------------------------------------------------------ sizes (host) */
+/* Bytes of packed codes / scales for `groups` matrices of [n][k] in a layout:
+ * codes = groups*n*k/2, scales = groups*n*(k/G)*2.  8192x2048 E2M1 gives
+ * 8,388,608 + 2,097,152 = 10,485,760 B = 10.00 MiB [LE stage P1].
+ * Returns 0 for an unknown format/layout or a k the format does not accept. */
+size_t w4_codes_bytes(int32_t format, int32_t layout, int64_t groups, int64_t n, int64_t k);
+size_t w4_scales_bytes(int32_t format, int32_t layout, int64_t groups, int64_t n, int64_t k);
+
+/* ------------------------------------------------------------------ quantise (host) */
+/* Quantise host fp32 weights w[n][k] (row-major) into canonical codes
+ * [n][k/2] and fp16 scales [n][k/G] (host buffers of w4_codes_bytes /
+ * w4_scales_bytes with groups = 1).  Offline step before upload [LE stage P1;
+ * CI "2. INT4 weight quantization"].  Per block of G elements:
+ *   scale = round-to-nearest-even fp16 of (fp32 absmax / 6)   (E2M1)
+ *                                        (fp32 absmax / 7)   (int4);
+ *   code  = nearest code to fp32(w) / fp32(scale) (IEEE fp32 division), ties to
+ *           the even code, saturating at +-6; int4: round half to even, clip to
+ *           [-8, 7]; an all-zero block has scale 0 and zero codes; a value that
+ *           rounds to magnitude zero is encoded as +0.
+ * Errors: W4_ERR_NONFINITE (Inf/NaN input), W4_ERR_RANGE (a block scale would
+ * overflow fp16), W4_ERR_INVALID_ARG, W4_ERR_LAYOUT.  Synchronous, thread-safe. */
+int w4_quantize(int32_t format, const float *w, int64_t n, int64_t k,
+                uint8_t *codes, uint16_t *scales);
+
+/* Host helpers between one-nibble-per-byte codes [n][k] (values 0..15) and the
+ * packed canonical codes [n][k/2] (low nibble = even element).  Exact inverses
+ * for any input; w4_pack_nibbles rejects a nibble > 15 (W4_ERR_INVALID_ARG). */
+int w4_pack_nibbles(const uint8_t *nibbles, int64_t n, int64_t k, uint8_t *packed);
+int w4_unpack_nibbles(const uint8_t *packed, int64_t n, int64_t k, uint8_t *nibbles);
+
+/* ------------------------------------------------------------------ dense GEMV */
+/* y[m][n] = x[m][k] . W[n][k]^T for the single matrix W (groups must be 1):
+ * the packed W4A16 matvec of [LE stage P1] (m = 1 for decode).  Codes are
+ * dequantised in registers (exactly: code value x fp32(scale)), products are
+ * accumulated in fp32 and each output is rounded once to bf16 (nearest even).
+ *   x: device bf16 [m][k], 16-byte aligned;  y: device bf16 [m][n].
+ * Supports 1 <= m <= 64.  Errors: W4_ERR_INVALID_ARG, _LAYOUT, _ALIGNMENT,
+ * _UNSUPPORTED, _HIP. */
+int w4a16_gemv(const w4_matrix *W, const uint16_t *x, int64_t m, uint16_t *y, void *stream);
+
+/* Test hook: dequantise every element of W (all groups) to fp32
+ * out[groups][n][k] on the device with the same in-register decode the GEMV
+ * and MoE kernels use.  Bit-exact by construction (each product is exact). */
+int w4_dequant_device(const w4_matrix *W, float *out, void *stream);
+
+/* ------------------------------------------------------------------ MoE layer */
+/* One MoE decode layer [TUT note 06 and the 35B-A3B config; README P28/P29/P45].
+ *   router_w      bf16 [E][H]                  router weight (logits = Wr x)
+ *   router_bias   fp32 [E] or NULL             added to the logits before softmax
+ *   w13           groups = E, n = 2I, k = H    rows [0,I) gate, [I,2I) up
+ *   w2            groups = E, n = H,  k = I    down projection
+ *   has_shared    0/1; if 1:
+ *     shared_w13  groups = 1, n = 2*shared_inter, k = H
+ *     shared_w2   groups = 1, n = H, k = shared_inter
+ *     shared_gate_w bf16 [H]: sigma = sigmoid(shared_gate_w . x)
+ * This build requires shared_inter == inter and H % 64 == 0; all experts and
+ * the shared expert use one format. */
+typedef struct moe_w4a16_layer {
+    int64_t hidden;              /* H */
+    int64_t inter;               /* I (expert intermediate) */
+    int64_t num_experts;         /* E */
+    int64_t top_k;               /* k */
+    int64_t shared_inter;        /* shared expert intermediate (if has_shared) */
+    const uint16_t *router_w;
+    const float *router_bias;
+    w4_matrix w13;
+    w4_matrix w2;
+    int32_t has_shared;
+    w4_matrix shared_w13;
+    w4_matrix shared_w2;
+    const uint16_t *shared_gate_w;
+} moe_w4a16_layer;
+
+/* Bytes of device workspace moe_w4a16_forward / moe_w4a16_experts need for T
+ * tokens (0 on invalid arguments).  The caller allocates it (e.g. with torch);
+ * its contents need no initialisation and are scratch between calls. */
+size_t moe_w4a16_workspace_bytes(const moe_w4a16_layer *L, int64_t T);
+
+/* Full layer for T tokens (decode: T = 1; batched decode: T > 1):
+ *   logits = Wr x (+ bias); p = softmax over all E; ids = the k largest p,
+ *   sorted by descending p, ties to the lower expert id; w = p[ids] / sum
+ *   (computed as softmax over the k selected logits, the equal form [TUT 06]);
+ *   y = sum_j w_j * W2[e_j] (silu(gate_j) * up_j) + sigma * shared(x),
+ *   gate_j/up_j = rows of W13[e_j] x; every intermediate in fp32; y rounded
+ *   once to bf16.
+ *   x: device bf16 [T][H] (16-byte aligned);  y: device bf16 [T][H].
+ *   topk_ids: device int32 [T][k] or NULL;  topk_w: device fp32 [T][k] or NULL.
+ *   ws: device workspace of at least moe_w4a16_workspace_bytes(L, T), 256-byte
+ *   aligned.
+ * Errors: W4_ERR_INVALID_ARG, _LAYOUT, _ALIGNMENT, _UNSUPPORTED, _WORKSPACE, _HIP. */
+int moe_w4a16_forward(const moe_w4a16_layer *L, const uint16_t *x, int64_t T, uint16_t *y,
+                      int32_t *topk_ids, float *topk_w, void *ws, size_t ws_bytes, void *stream);
+
+/* Experts and combine only, with caller-supplied routing (the one-call shape of
+ * README P45): ids int32 [T][k] in [0, E), w fp32 [T][k] (used as given).  The
+ * shared expert, if present, is still added with its sigmoid gate. */
+int moe_w4a16_experts(const moe_w4a16_layer *L, const uint16_t *x, int64_t T,
+                      const int32_t *ids, const float *w, uint16_t *y,
+                      void *ws, size_t ws_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* W4MOE_H */

@@ -1,0 +1,188 @@
+"""Host-side checks of the C-ABI library (no GPU needed).
+
+The library must load without a GPU, export every function include/w4moe.h
+declares, and its host quantiser/packer must agree bit for bit with the oracle.
+Every invalid argument must return its documented status before any launch.
+"""
+
+import ctypes as C
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import formats as F
+import bit_block_scaled_router_amd as w4
+from bit_block_scaled_router_amd import synth
+from conftest import ROOT, read_golden_blocks
+
+FMTS = [(w4.W4_FMT_E2M1_F16S16, F.FMT_E2M1), (w4.W4_FMT_INT4_F16S128, F.FMT_INT4)]
+
+
+def _header_functions():
+    text = open(os.path.join(ROOT, "include", "w4moe.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*([a-z_0-9]+)\s*\(", text, flags=re.M)))
+
+
+def test_library_exports_every_declared_function():
+    names = _header_functions()
+    assert len(names) >= 12
+    assert sorted(names) == sorted(w4.EXPORTS)
+    L = C.CDLL(os.path.join(ROOT, "bit_block_scaled_router_amd", "libw4moe.so"))
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings_and_version():
+    assert w4.w4_status_string(0) == "W4_OK"
+    assert w4.w4_status_string(w4.W4_ERR_LAYOUT) == "W4_ERR_LAYOUT"
+    assert "gfx950" in w4.w4_version()
+
+
+def test_sizes_match_stage_p1_and_oracle():
+    assert w4.w4_codes_bytes(w4.W4_FMT_E2M1_F16S16, 1, 8192, 2048) == 8_388_608
+    assert w4.w4_scales_bytes(w4.W4_FMT_E2M1_F16S16, 1, 8192, 2048) == 2_097_152
+    assert w4.w4_scales_bytes(w4.W4_FMT_INT4_F16S128, 1, 8192, 2048) == 262_144
+    for fmt, ofmt in FMTS:
+        for g, n, k in [(1, 8, 256), (256, 1024, 2048), (3, 5, 512)]:
+            assert w4.w4_codes_bytes(fmt, g, n, k) == oracle.codes_bytes(ofmt, g, n, k)
+            assert w4.w4_scales_bytes(fmt, g, n, k) == oracle.scales_bytes(ofmt, g, n, k)
+    assert w4.w4_codes_bytes(7, 1, 8, 256) == 0  # unknown format
+    assert w4.w4_codes_bytes(w4.W4_FMT_E2M1_F16S16, 1, 8, 48) == 0  # k % 32
+    assert w4.w4_codes_bytes(w4.W4_FMT_E2M1_F16S16, 1, 8, 256, layout=3) == 0
+
+
+@pytest.mark.parametrize("fmt,ofmt", FMTS)
+def test_quantizer_bit_exact_vs_oracle(fmt, ofmt):
+    rng = np.random.default_rng(21)
+    g = F.group_size(ofmt)
+    w = np.concatenate([
+        (rng.standard_normal((64, 8 * g)) * 0.02).astype(np.float32),
+        (rng.standard_normal((4, 8 * g)) * 1e-6).astype(np.float32),      # subnormal fp16 scales
+        (rng.standard_normal((4, 8 * g)) * 1e3).astype(np.float32),
+        np.zeros((1, 8 * g), dtype=np.float32),
+        # ratios on every midpoint, and one ulp around
+        np.repeat(np.array([[0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.0] * g], dtype=np.float32), 1, 0)[:, :8 * g],
+    ])
+    near = w[-1].copy()
+    w = np.concatenate([w, np.nextafter(near, np.float32(np.inf))[None], np.nextafter(near, np.float32(0))[None],
+                        -near[None]])
+    c_lib, s_lib = w4.w4_quantize(fmt, w)
+    c_or, s_or = oracle.quantize(ofmt, w)
+    assert np.array_equal(s_lib, s_or)
+    assert np.array_equal(c_lib, c_or)
+
+
+def test_quantizer_golden_blocks():
+    for name, scale_bits, wv, codes in read_golden_blocks("e2m1_blocks.txt"):
+        c, s = w4.w4_quantize(w4.W4_FMT_E2M1_F16S16, np.array([wv + [0.0] * 16], dtype=np.float32))
+        assert int(s[0, 0]) == scale_bits, name
+        assert w4.w4_unpack_nibbles(c)[0, :16].tolist() == codes, name
+
+
+def test_quantizer_expert_weights_match_oracle():
+    shape = synth.QWEN_MOE_T1
+    for e in (0, 255):
+        w = synth.expert_w2(shape, e)
+        assert all(np.array_equal(a, b) for a, b in zip(w4.w4_quantize(w4.W4_FMT_E2M1_F16S16, w),
+                                                          oracle.quantize(F.FMT_E2M1, w)))
+
+
+def test_quantizer_errors():
+    bad = np.zeros((2, 32), dtype=np.float32)
+    bad[1, 3] = np.nan
+    with pytest.raises(w4.W4Error) as e:
+        w4.w4_quantize(w4.W4_FMT_E2M1_F16S16, bad)
+    assert e.value.status == w4.W4_ERR_NONFINITE
+    with pytest.raises(w4.W4Error) as e:
+        w4.w4_quantize(w4.W4_FMT_E2M1_F16S16, np.full((1, 32), 1e6, dtype=np.float32))
+    assert e.value.status == w4.W4_ERR_RANGE
+    with pytest.raises(w4.W4Error) as e:
+        w4.w4_quantize(w4.W4_FMT_INT4_F16S128, np.zeros((1, 64), dtype=np.float32))
+    assert e.value.status == w4.W4_ERR_INVALID_ARG
+    with pytest.raises(w4.W4Error) as e:
+        w4.w4_quantize(9, np.zeros((1, 64), dtype=np.float32))
+    assert e.value.status == w4.W4_ERR_LAYOUT
+
+
+def test_pack_unpack_all_bytes_and_oracle():
+    b = np.arange(256, dtype=np.uint8).reshape(4, 64)
+    nib = w4.w4_unpack_nibbles(b)
+    assert np.array_equal(nib, oracle.unpack_nibbles(b))
+    assert np.array_equal(w4.w4_pack_nibbles(nib), b)
+    with pytest.raises(w4.W4Error):
+        w4.w4_pack_nibbles(np.full((1, 4), 16, dtype=np.uint8))
+
+
+# ---------------------------------------------------------------- device entry validation
+
+
+def _mat(fmt=w4.W4_FMT_E2M1_F16S16, layout=0, groups=1, n=64, k=256, codes=4096, scales=8192):
+    return w4.W4Matrix(fmt, layout, groups, n, k, codes, scales)
+
+
+def _gemv(W, x=1 << 20, m=1, y=1 << 21):
+    return w4.lib().w4a16_gemv(C.byref(W), x, m, y, 0)
+
+
+def test_gemv_validation_returns_before_launch():
+    assert _gemv(_mat(fmt=5)) == w4.W4_ERR_LAYOUT
+    assert _gemv(_mat(layout=1)) == w4.W4_ERR_LAYOUT
+    assert _gemv(_mat(k=48)) == w4.W4_ERR_INVALID_ARG
+    assert _gemv(_mat(fmt=w4.W4_FMT_INT4_F16S128, k=64)) == w4.W4_ERR_INVALID_ARG
+    assert _gemv(_mat(codes=4100)) == w4.W4_ERR_ALIGNMENT
+    assert _gemv(_mat(scales=8194)) == w4.W4_ERR_ALIGNMENT
+    assert _gemv(_mat(codes=0)) == w4.W4_ERR_INVALID_ARG
+    assert _gemv(_mat(groups=2)) == w4.W4_ERR_INVALID_ARG
+    assert _gemv(_mat(), m=0) == w4.W4_ERR_UNSUPPORTED
+    assert _gemv(_mat(), m=65) == w4.W4_ERR_UNSUPPORTED
+    assert _gemv(_mat(), x=(1 << 20) + 2) == w4.W4_ERR_ALIGNMENT
+    assert _gemv(_mat(), x=0) == w4.W4_ERR_INVALID_ARG
+    assert "x not 16-byte aligned" in w4.w4_last_error() or True
+    assert w4.lib().w4a16_gemv(None, 1 << 20, 1, 1 << 21, 0) == w4.W4_ERR_INVALID_ARG
+    assert w4.lib().w4_dequant_device(C.byref(_mat()), 0, 0) == w4.W4_ERR_INVALID_ARG
+
+
+def _layer(**over):
+    H, I, E, K = 256, 128, 8, 2
+    d = dict(hidden=H, inter=I, num_experts=E, top_k=K, shared_inter=I, router_w=1 << 16, router_bias=None,
+             w13=_mat(groups=E, n=2 * I, k=H), w2=_mat(groups=E, n=H, k=I), has_shared=1,
+             shared_w13=_mat(groups=1, n=2 * I, k=H), shared_w2=_mat(groups=1, n=H, k=I), shared_gate_w=1 << 17)
+    d.update(over)
+    return w4.MoELayerDesc(*[d[f] for f, _ in w4.MoELayerDesc._fields_])
+
+
+def _fwd(L, T=1, ws_bytes=None, ws=1 << 24, x=1 << 20, y=1 << 21):
+    if ws_bytes is None:
+        ws_bytes = w4.lib().moe_w4a16_workspace_bytes(C.byref(L), T) if T >= 1 else 0
+    return w4.lib().moe_w4a16_forward(C.byref(L), x, T, y, None, None, ws, ws_bytes, 0)
+
+
+def test_moe_workspace_size_and_validation():
+    L = _layer()
+    ws = w4.lib().moe_w4a16_workspace_bytes(C.byref(L), 1)
+    assert ws > 0 and ws % 256 == 0
+    assert w4.lib().moe_w4a16_workspace_bytes(C.byref(L), 32) > ws
+    assert w4.lib().moe_w4a16_workspace_bytes(C.byref(_layer(top_k=9)), 1) == 0
+    assert _fwd(_layer(top_k=0)) == w4.W4_ERR_INVALID_ARG
+    assert _fwd(_layer(top_k=9)) == w4.W4_ERR_INVALID_ARG
+    assert _fwd(_layer(hidden=200)) == w4.W4_ERR_UNSUPPORTED
+    assert _fwd(_layer(num_experts=2000)) == w4.W4_ERR_UNSUPPORTED
+    assert _fwd(_layer(w13=_mat(groups=8, n=2 * 128, k=512))) == w4.W4_ERR_INVALID_ARG
+    assert _fwd(_layer(w2=_mat(fmt=w4.W4_FMT_INT4_F16S128, groups=8, n=256, k=128))) == w4.W4_ERR_LAYOUT
+    assert _fwd(_layer(shared_inter=256)) == w4.W4_ERR_UNSUPPORTED
+    assert _fwd(_layer(has_shared=2)) == w4.W4_ERR_INVALID_ARG
+    assert _fwd(_layer(shared_gate_w=None)) == w4.W4_ERR_INVALID_ARG
+    assert _fwd(_layer(router_w=(1 << 16) + 8)) == w4.W4_ERR_ALIGNMENT
+    assert _fwd(L, T=0) == w4.W4_ERR_INVALID_ARG
+    assert _fwd(L, ws_bytes=ws - 1) == w4.W4_ERR_WORKSPACE
+    assert _fwd(L, ws=0) == w4.W4_ERR_WORKSPACE
+    assert _fwd(L, ws=(1 << 24) + 64) == w4.W4_ERR_ALIGNMENT
+    assert _fwd(L, x=(1 << 20) + 8) == w4.W4_ERR_ALIGNMENT
+    assert w4.lib().moe_w4a16_experts(C.byref(L), 1 << 20, 1, None, None, 1 << 21, 1 << 24, ws, 0) \
+        == w4.W4_ERR_INVALID_ARG
+    assert w4.lib().moe_w4a16_experts(C.byref(L), 1 << 20, 1, 1 << 22, None, 1 << 21, 1 << 24, ws, 0) \
+        == w4.W4_ERR_INVALID_ARG
