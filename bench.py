@@ -1,0 +1,416 @@
+"""Benchmark: W4A16 MoE decode layer (and dense GEMV) on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--gpus 1]
+
+Prints ONE JSON line.  A step is one full pass of the hot path over one batch of
+synthetic input: for the default workload, one token through the whole MoE layer
+of the Qwen 3.6 35B-A3B shape (router GEMV, softmax/top-8/renormalise, grouped
+W13 + SiLU over 8 routed + 1 shared expert, down projection + weighted combine).
+Inputs are resident in HBM before the timed region.  To keep the 256 MB
+Infinity Cache from serving the weights, steps rotate over layer replicas and a
+pool of tokens (distinct expert sets), so a step streams cold weights as a real
+40-layer decode would.
+
+The K timed steps are captured once in a HIP graph (removing host launch cost)
+and replayed; W eager warm-up steps and one untimed replay precede the timed
+replay.  The library's measurement entry point records HIP events between its
+launches on the stream they run on, giving each kernel's average duration over
+the timed region; the dominant one is reported in `roofline`.
+
+`cpu_baseline` times the CPU oracle on a bounded sample of the same workload
+(a few tokens, weights pre-quantised untimed, dequantisation on the fly).
+"""
+
+import argparse
+import ctypes as C
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X published HBM3E bandwidth
+METRIC = "MoE-layer µs/token and achieved HBM GB/s (% of peak), W4A16 decode"
+
+
+# ----------------------------------------------------------------------------- HIP events
+
+
+class HipEvents:
+    """Raw hipEvent_t handles from the HIP runtime torch has loaded."""
+
+    def __init__(self):
+        path = None
+        for ln in open("/proc/self/maps"):
+            if "libamdhip64" in ln:
+                path = ln.split()[-1]
+                break
+        self.hip = C.CDLL(path or "libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [C.POINTER(C.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [C.POINTER(C.c_float), C.c_void_p, C.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [C.c_void_p]
+
+    def create(self, n):
+        out = []
+        for _ in range(n):
+            e = C.c_void_p()
+            if self.hip.hipEventCreate(C.byref(e)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            out.append(e.value)
+        return out
+
+    def elapsed_ms(self, a, b):
+        ms = C.c_float()
+        if self.hip.hipEventElapsedTime(C.byref(ms), a, b) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
+    def destroy(self, evs):
+        for e in evs:
+            self.hip.hipEventDestroy(e)
+
+
+# ----------------------------------------------------------------------------- helpers
+
+
+def source_digest():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "bit_block_scaled_router_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel, workload):
+    """HBM bytes per dispatch from committed rocprofv3 counter runs, if still current."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        db = json.load(f)
+    rec = db.get(workload, {}).get(kernel)
+    if not rec or rec.get("source_digest") != source_digest():
+        return None
+    return rec.get("hbm_bytes_per_dispatch")
+
+
+def clone_layer(w4, layer):
+    """A deep copy of a device MoE layer (new addresses, same contents)."""
+    def cq(q):
+        return w4.QMatrix(q.fmt, q.groups, q.n, q.k, q.codes.clone(), q.scales.clone())
+
+    kw = {}
+    if layer.has_shared:
+        kw = dict(shared_w13=cq(layer.shared_w13), shared_w2=cq(layer.shared_w2),
+                  shared_gate_w=layer.shared_gate_w.clone())
+    rb = layer.router_bias.clone() if layer.router_bias is not None else None
+    return w4.MoELayer(layer.hidden, layer.inter, layer.num_experts, layer.top_k, layer.router_w.clone(),
+                       cq(layer.w13), cq(layer.w2), router_bias=rb, **kw)
+
+
+def moe_bytes(shape, distinct):
+    """Algorithmic HBM bytes of one MoE step: every byte the method must move once.
+
+    router bf16 [E][H]; for each distinct selected expert and the shared expert,
+    W13 and W2 codes (half a byte per element) and FP16 scales (2 B per 16);
+    shared-gate bf16 [H]; x and y bf16 [T][H]."""
+    H, I, E, T = shape.hidden, shape.inter, shape.num_experts, shape.tokens
+    per_expert = 3 * H * I // 2 + 3 * H * I // 16 * 2
+    b = E * H * 2 + distinct * per_expert + 2 * T * H * 2
+    if shape.has_shared:
+        b += per_expert + H * 2
+    return b
+
+
+def stage_bytes(shape, distinct):
+    """Algorithmic bytes per launch of each MoE kernel (T = shape.tokens)."""
+    H, I, E, T, K = shape.hidden, shape.inter, shape.num_experts, shape.tokens, shape.top_k
+    S = K + (1 if shape.has_shared else 0)
+    w13 = 2 * I * H // 2 + 2 * I * H // 16 * 2
+    w2 = H * I // 2 + H * I // 16 * 2
+    nexp = distinct + (1 if shape.has_shared else 0)
+    return {
+        "k_router": E * H * 2 + (H * 2 if shape.has_shared else 0) + T * H * 2 + T * (E + 1) * 4,
+        "k_moe_w13": nexp * w13 + T * H * 2 + T * E * 4 + T * S * I * 4,
+        "k_moe_down": nexp * w2 + T * S * I * 4 + T * K * 8 + T * H * 2,
+    }
+
+
+# ----------------------------------------------------------------------------- CPU baseline
+
+
+def cpu_baseline_moe(shape, tokens, reps):
+    """Oracle forward per token (float64, dequantisation on the fly), bounded sample."""
+    import oracle
+    from oracle import ops
+    from bit_block_scaled_router_amd import synth
+
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover - optional
+        blas_threads = 1
+    rw = synth.router_weight(shape)
+    xs = np.stack([synth.x_row(shape.seed, shape.hidden, t) for t in range(tokens)])
+    bias = synth.router_bias(shape)
+    need = set()
+    for t in range(tokens):
+        ids, _ = ops.route(ops.router_logits(rw, xs[t], bias), shape.top_k)
+        need.update(int(e) for e in ids)
+    fmt = oracle.FMT_E2M1
+    q13 = {e: oracle.quantize(fmt, synth.expert_w13(shape, e)) for e in need}
+    q2 = {e: oracle.quantize(fmt, synth.expert_w2(shape, e)) for e in need}
+    kw = {}
+    if shape.has_shared:
+        kw = dict(shared_w13=oracle.quantize(fmt, synth.shared_w13(shape)),
+                  shared_w2=oracle.quantize(fmt, synth.shared_w2(shape)),
+                  shared_gate_w=synth.shared_gate_weight(shape))
+    times = []
+    for _ in range(reps):
+        layer = ops.MoELayer(fmt, shape.hidden, shape.inter, shape.num_experts, shape.top_k, rw,
+                             lambda e: q13[e], lambda e: q2[e], router_bias=bias, **kw)
+        t0 = time.perf_counter()
+        ops.moe_forward(layer, xs)
+        times.append(time.perf_counter() - t0)
+    per_token_us = float(np.median(times)) / tokens * 1e6
+    return {
+        "value": per_token_us,
+        "unit": "us/layer-token",
+        "cores": int(blas_threads),
+        "kind": "oracle",
+        "sample": f"{tokens} token(s) of the same layer shape, float64 oracle forward with on-the-fly "
+                  f"dequantisation, weights pre-quantised untimed; median of {reps} runs",
+        "host_cores_available": len(os.sched_getaffinity(0)),
+    }
+
+
+def cpu_baseline_gemv(shape, reps):
+    import oracle
+    from bit_block_scaled_router_amd import synth
+
+    ofmt = oracle.FMT_E2M1 if shape.fmt == "e2m1" else oracle.FMT_INT4
+    codes, scales = oracle.quantize(ofmt, synth.dense_weight(shape))
+    x = synth.dense_x(shape)
+    times = []
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        oracle.gemv(ofmt, codes, scales, x)
+        times.append(time.perf_counter() - t0)
+    return {"value": float(np.median(times)) * 1e6, "unit": "us/call", "cores": 1, "kind": "oracle",
+            "sample": f"the full {shape.n}x{shape.k} GEMV, median of {reps} runs",
+            "host_cores_available": len(os.sched_getaffinity(0))}
+
+
+# ----------------------------------------------------------------------------- GPU runs
+
+
+def run_moe(args, torch, w4, wl, synth):
+    shape = {"qwen-t1": synth.QWEN_MOE_T1, "qwen-t32": synth.QWEN_MOE_T32, "tiny": synth.TINY_MOE}[args.workload]
+    T = shape.tokens
+    print(f"[bench] building {shape.name} ({args.replicas} replicas)", file=sys.stderr, flush=True)
+    base = wl.build_moe_layer(shape, device="cuda")
+    layers = [base] + [clone_layer(w4, base) for _ in range(args.replicas - 1)]
+    pool = np.stack([np.stack([synth.x_row(shape.seed, shape.hidden, p * T + t) for t in range(T)])
+                     for p in range(args.pool)])
+    xs = wl.bf16_tensor(pool, "cuda")  # [P][T][H]
+    y = torch.empty((T, shape.hidden), dtype=torch.bfloat16, device="cuda")
+    ids = torch.empty((T, shape.top_k), dtype=torch.int32, device="cuda")
+    ws = w4.alloc_workspace(base, T)
+    # distinct routed experts per step (for the algorithmic byte count)
+    distinct = []
+    for p in range(args.pool):
+        w4.moe_w4a16_forward(base, xs[p], y=y, topk_ids=ids, ws=ws)
+        distinct.append(len(set(ids.cpu().numpy().ravel().tolist())))
+    torch.cuda.synchronize()
+    n_steps = args.steps
+    R, P = len(layers), args.pool
+    for i in range(args.warmup):
+        w4.moe_w4a16_forward(layers[i % R], xs[i % P], y=y, ws=ws)
+    torch.cuda.synchronize()
+
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            for i in range(n_steps):
+                w4.moe_w4a16_forward(layers[i % R], xs[i % P], y=y, ws=ws)
+    torch.cuda.synchronize()
+    g.replay()  # untimed warm replay
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    start.record()
+    g.replay()
+    end.record()
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    ms_total = start.elapsed_time(end)
+
+    # per-kernel durations: the same K steps launched eagerly through the
+    # measurement entry point, whose kernels carry start/stop HIP events
+    hip = HipEvents()
+    evs = hip.create(6 * n_steps)
+    for i in range(n_steps):
+        w4.moe_w4a16_forward_timed(layers[i % R], xs[i % P], y, ws, evs[6 * i:6 * i + 6])
+    torch.cuda.synchronize()
+    stage = {"k_router": [], "k_moe_w13": [], "k_moe_down": []}
+    for i in range(n_steps):
+        e = evs[6 * i:6 * i + 6]
+        stage["k_router"].append(hip.elapsed_ms(e[0], e[1]))
+        stage["k_moe_w13"].append(hip.elapsed_ms(e[2], e[3]))
+        stage["k_moe_down"].append(hip.elapsed_ms(e[4], e[5]))
+    hip.destroy(evs)
+    stage_us = {k: float(np.mean(v)) * 1e3 for k, v in stage.items()}
+
+    # eager (no graph) rate for context
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(min(n_steps, 200)):
+        w4.moe_w4a16_forward(layers[i % R], xs[i % P], y=y, ws=ws)
+    torch.cuda.synchronize()
+    eager_ms = (time.perf_counter() - t0) / min(n_steps, 200) * 1e3
+
+    d_mean = float(np.mean(distinct))
+    ms_step = ms_total / n_steps
+    us_token = ms_step * 1e3 / T
+    step_bytes = moe_bytes(shape, d_mean)
+    sb = stage_bytes(shape, d_mean)
+    dom = max(stage_us, key=stage_us.get)
+    achieved = sb[dom] / (stage_us[dom] * 1e-6) / 1e9
+    traffic = load_traffic(dom, shape.name)
+    res = {
+        "metric": METRIC,
+        "value": us_token,
+        "unit": "us/layer-token",
+        "n_gpus": 1,
+        "steps": n_steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": shape.name, "hidden": shape.hidden, "experts": shape.num_experts,
+            "top_k": shape.top_k, "inter": shape.inter, "shared_inter": shape.shared_inter,
+            "tokens_per_step": T, "zipf_s": shape.zipf_s, "weights": "E2M1 codes + FP16 scale per 16",
+            "activations": "bf16", "accumulate": "fp32", "layer_replicas": R, "token_pool": P,
+            "mean_distinct_experts": d_mean, "timing": "HIP graph replay of the K steps",
+        },
+        "hbm_gbps": step_bytes / (ms_step * 1e-3) / 1e9,
+        "pct_hbm_peak": 100.0 * step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "algorithmic_bytes_per_step": step_bytes,
+        "stage_us": stage_us,
+        "eager_ms_per_step": eager_ms,
+        "wall_s_timed": t_wall,
+        "roofline": {
+            "bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS,
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": sb[dom], "avg_launch_us": stage_us[dom],
+            "note": "avg launch duration from start/stop HIP events the runtime records around each "
+                    "kernel (hipExtLaunchKernel) over K eager steps of the same workload",
+        },
+    }
+    return res, shape
+
+
+def run_gemv(args, torch, w4, wl, synth):
+    shape = {"gemv-e2m1": synth.GEMV_E2M1, "gemv-int4": synth.GEMV_INT4}[args.workload]
+    print(f"[bench] building {shape.name} ({args.replicas} replicas)", file=sys.stderr, flush=True)
+    base = wl.build_dense(shape, "cuda")
+    reps = [base] + [w4.QMatrix(base.fmt, 1, base.n, base.k, base.codes.clone(), base.scales.clone())
+                     for _ in range(args.replicas - 1)]
+    x = wl.bf16_tensor(synth.dense_x(shape), "cuda")
+    y = torch.empty(shape.n, dtype=torch.bfloat16, device="cuda")
+    R = len(reps)
+    for i in range(args.warmup):
+        w4.w4a16_gemv(reps[i % R], x, y=y)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            for i in range(args.steps):
+                w4.w4a16_gemv(reps[i % R], x, y=y)
+    g.replay()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    g.replay()
+    end.record()
+    torch.cuda.synchronize()
+    ms_step = start.elapsed_time(end) / args.steps
+    g_bytes = shape.n * shape.k // 2 + shape.n * shape.k // (16 if shape.fmt == "e2m1" else 128) * 2 \
+        + shape.k * 2 + shape.n * 2
+    gbs = g_bytes / (ms_step * 1e-3) / 1e9
+    res = {
+        "metric": METRIC, "value": ms_step * 1e3, "unit": "us/call", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": False, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": shape.name, "n": shape.n, "k": shape.k, "format": shape.fmt,
+                   "replicas": R, "timing": "HIP graph replay of the K steps"},
+        "hbm_gbps": gbs, "pct_hbm_peak": 100 * gbs / HBM_PEAK_GBS, "algorithmic_bytes_per_step": g_bytes,
+        "roofline": {"bound": "hbm", "kernel": "k_gemv", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": gbs / HBM_PEAK_GBS, "traffic": load_traffic("k_gemv", shape.name),
+                     "algorithmic_bytes_per_launch": g_bytes, "avg_launch_us": ms_step * 1e3,
+                     "note": "graph replay time per launch (one kernel per step)"},
+    }
+    return res, shape
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--workload", default="qwen-t1",
+                    choices=["qwen-t1", "qwen-t32", "tiny", "gemv-e2m1", "gemv-int4"])
+    ap.add_argument("--replicas", type=int, default=0, help="weight replicas (0 = workload default)")
+    ap.add_argument("--pool", type=int, default=64, help="token pool (MoE workloads)")
+    ap.add_argument("--cpu-tokens", type=int, default=1)
+    ap.add_argument("--cpu-reps", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+    if args.replicas <= 0:
+        args.replicas = 128 if args.workload.startswith("gemv") else 4
+    if args.workload == "qwen-t32":
+        args.pool = min(args.pool, 8)
+
+    import torch
+
+    import bit_block_scaled_router_amd as w4
+    from bit_block_scaled_router_amd import synth, workloads as wl
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    w4.lib()
+    if args.workload.startswith("gemv"):
+        res, shape = run_gemv(args, torch, w4, wl, synth)
+        cpu = None if args.no_cpu_baseline else cpu_baseline_gemv(shape, args.cpu_reps)
+    else:
+        res, shape = run_moe(args, torch, w4, wl, synth)
+        cpu = None if args.no_cpu_baseline else cpu_baseline_moe(
+            shape, args.cpu_tokens if shape.tokens == 1 else 4, args.cpu_reps if shape.tokens == 1 else 2)
+    res["cpu_baseline"] = cpu
+    res["device"] = torch.cuda.get_device_name(0)
+    res["source_digest"] = source_digest()
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -206,6 +206,14 @@ def moe_w4a16_forward(layer, x, y=None, topk_ids=None, topk_w=None, ws=None, str
     return y
 
 
+def moe_w4a16_forward_timed(layer, x, y, ws, events, topk_ids=None, topk_w=None, stream=None):
+    """moe_w4a16_forward with start/stop events per kernel (6 hipEvent_t handles)."""
+    arr = (C.c_void_p * 6)(*events)
+    check(lib().moe_w4a16_forward_timed(C.byref(layer.desc), _ptr(x), x.shape[0], _ptr(y), _ptr(topk_ids),
+                                        _ptr(topk_w), _ptr(ws), ws.numel(), _stream(stream), arr))
+    return y
+
+
 def moe_w4a16_experts(layer, x, ids, w, y=None, ws=None, stream=None):
     """Experts + combine with given routing: ids int32 [T][k], w fp32 [T][k]."""
     torch = _torch()

@@ -31,7 +31,7 @@ EXPORTS = (
     "w4_codes_bytes", "w4_scales_bytes", "w4_quantize",
     "w4_pack_nibbles", "w4_unpack_nibbles",
     "w4a16_gemv", "w4_dequant_device",
-    "moe_w4a16_workspace_bytes", "moe_w4a16_forward", "moe_w4a16_experts",
+    "moe_w4a16_workspace_bytes", "moe_w4a16_forward", "moe_w4a16_forward_timed", "moe_w4a16_experts",
 )
 
 
@@ -78,6 +78,10 @@ def lib():
     """The loaded library (raises if it has not been built)."""
     global _lib
     if _lib is None:
+        try:  # share the HIP runtime torch loads (one runtime per process)
+            import torch  # noqa: F401
+        except ImportError:
+            pass
         if not os.path.exists(LIB_PATH):
             raise ImportError(
                 f"{LIB_PATH} is missing: build it with `python -m bit_block_scaled_router_amd.build`"
@@ -97,6 +101,7 @@ def lib():
             "w4_dequant_device": (C.c_int, [C.POINTER(W4Matrix), P, P]),
             "moe_w4a16_workspace_bytes": (SZ, [C.POINTER(MoELayerDesc), I64]),
             "moe_w4a16_forward": (C.c_int, [C.POINTER(MoELayerDesc), P, I64, P, P, P, P, SZ, P]),
+            "moe_w4a16_forward_timed": (C.c_int, [C.POINTER(MoELayerDesc), P, I64, P, P, P, P, SZ, P, P]),
             "moe_w4a16_experts": (C.c_int, [C.POINTER(MoELayerDesc), P, I64, P, P, P, P, SZ, P]),
         }
         for name, (res, args) in sig.items():

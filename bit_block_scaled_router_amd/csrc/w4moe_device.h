@@ -83,28 +83,72 @@ __device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
     return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
 }
 
-// Sum over aligned groups of L lanes (L a power of two <= 64); every lane of a
-// group gets the same value (each step adds the same two operands in both
-// partner lanes).  All 64 lanes must be active.
+// Sum over aligned groups of L lanes (L a power of two <= 64), in a fixed order.
+// L <= 16: butterfly within the row, every lane of the group gets the sum.
+// L = 32, 64: the row sums are then combined with row broadcasts and the sum
+// is valid in the LAST lane of each group (lane % L == L - 1).  Use
+// group_leader<L>() to pick the lane that owns the result.  All 64 lanes must
+// be active.
 template <int L>
 __device__ __forceinline__ float group_sum(float v) {
     if constexpr (L >= 2) v += dpp_f32<0xB1>(v);   // quad_perm [1,0,3,2]: lane ^ 1
     if constexpr (L >= 4) v += dpp_f32<0x4E>(v);   // quad_perm [2,3,0,1]: lane ^ 2
     if constexpr (L >= 8) v += dpp_f32<0x141>(v);  // row_half_mirror: the other quad
     if constexpr (L >= 16) v += dpp_f32<0x140>(v); // row_mirror: the other half-row
-    if constexpr (L >= 32) v += __shfl_xor(v, 16);
-    if constexpr (L >= 64) v += __shfl_xor(v, 32);
+    if constexpr (L >= 32) {                       // row_bcast:15 into rows 1 and 3
+        v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x142, 0xA, 0xF, false));
+    }
+    if constexpr (L >= 64) {                       // row_bcast:31 into row 3
+        v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x143, 0x8, 0xF, false));
+    }
     return v;
 }
 
+template <int L>
+__device__ __forceinline__ bool group_leader(int lane) {
+    return (lane & (L - 1)) == L - 1;
+}
+
+// Maximum over the wave, returned to every lane (wave-uniform).
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
     v = max(v, dpp_u32<0xB1>(v));
     v = max(v, dpp_u32<0x4E>(v));
     v = max(v, dpp_u32<0x141>(v));
     v = max(v, dpp_u32<0x140>(v));
-    v = max(v, (uint32_t)__shfl_xor((int)v, 16));
-    v = max(v, (uint32_t)__shfl_xor((int)v, 32));
-    return v;
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xA, 0xF, false));
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0x8, 0xF, false));
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
+// Global wave index, marked wave-uniform (a scalar register) so that pointers
+// and buffer resources derived from it need no per-lane handling.
+__device__ __forceinline__ int wave_id() {
+    return __builtin_amdgcn_readfirstlane((int)(blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6)));
+}
+
+// ---------------------------------------------------------------- buffer loads
+
+// Raw buffer resources: a load whose byte offset lies at or beyond the
+// resource's size returns zero instead of touching memory, so masked lanes
+// need no branch.  Sizes are below 2 GiB per resource.
+constexpr uint32_t OOB = 0x80000000u;
+
+struct Buf {
+    __amdgpu_buffer_rsrc_t r;
+};
+
+__device__ __forceinline__ Buf make_buf(const void *p, uint32_t bytes) {
+    return Buf{__builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)bytes, 0x00020000)};
+}
+
+__device__ __forceinline__ uint4 ld128(Buf b, uint32_t off) {
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(b.r, off, 0, 0));
+}
+__device__ __forceinline__ uint32_t ld32(Buf b, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b32(b.r, off, 0, 0);
+}
+__device__ __forceinline__ uint32_t ld16(Buf b, uint32_t off) {
+    return (uint32_t)(uint16_t)__builtin_amdgcn_raw_buffer_load_b16(b.r, off, 0, 0);
 }
 
 // ---------------------------------------------------------------- activations
@@ -118,11 +162,11 @@ struct XSlice {
     float sum;
 };
 
+// Load the slice at byte offset `off` of the activation buffer (OOB -> zeros).
 template <int FMT>
-__device__ __forceinline__ void load_xslice(XSlice<FMT> &xs, const uint16_t *__restrict__ x, int k0, bool valid) {
-    const uint4 *p = reinterpret_cast<const uint4 *>(x + k0);
+__device__ __forceinline__ void load_xslice(XSlice<FMT> &xs, Buf xb, uint32_t off) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) xs.v[i] = valid ? p[i] : make_uint4(0, 0, 0, 0);
+    for (int i = 0; i < 4; ++i) xs.v[i] = ld128(xb, off + 16u * i);
 }
 
 template <int FMT>
@@ -240,13 +284,19 @@ __device__ __forceinline__ float chunk_dot_f32(uint4 c, uint32_t sc, const float
     return acc;
 }
 
-// Scale dword of the lane's chunk: E2M1 two FP16 at element k0/16, int4 one at k0/128.
+// Scale dword of the lane's chunk from a scale buffer: E2M1 two FP16 at
+// element k0/16 of the row, int4 one at k0/128.  `row_off` is the row's first
+// scale element; an out-of-range offset yields zero.
 template <int FMT>
-__device__ __forceinline__ uint32_t load_scales(const uint16_t *__restrict__ srow, int k0) {
+__device__ __forceinline__ uint32_t scale_off(uint32_t row_elem0, int k0) {
+    return FMT == FMT_E2M1 ? (row_elem0 + (uint32_t)(k0 >> 4)) * 2u : (row_elem0 + (uint32_t)(k0 >> 7)) * 2u;
+}
+template <int FMT>
+__device__ __forceinline__ uint32_t ld_scales(Buf b, uint32_t off) {
     if constexpr (FMT == FMT_E2M1)
-        return *reinterpret_cast<const uint32_t *>(srow + (k0 >> 4));
+        return ld32(b, off);
     else
-        return (uint32_t)srow[k0 >> 7];
+        return ld16(b, off);
 }
 
 template <int FMT>

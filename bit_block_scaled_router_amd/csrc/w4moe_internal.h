@@ -2,7 +2,7 @@
 // w4moe library (status handling and shape checks).
 #pragma once
 
-#include "../../include/w4moe.h"
+#include "w4moe.h"  // include/ is on the include path
 
 namespace w4 {
 

@@ -22,6 +22,7 @@
 #include "w4moe_device.h"
 #include "w4moe_internal.h"
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <type_traits>
@@ -30,19 +31,23 @@ namespace w4k {
 
 // ================================================================= dense GEMV
 
-// y[t][n] = sum_k W[n][k] x[t][k].  A wave owns RT load-groups of 64/L rows.
+// y[t][n] = sum_k W[n][k] x[t][k].  A wave owns RT load-groups of 64/L rows and
+// issues all of its weight loads before the first use.
 template <int FMT, int L, int RT>
 __global__ __launch_bounds__(256) void k_gemv(const uint8_t *__restrict__ codes, const uint16_t *__restrict__ scales,
                                               const uint16_t *__restrict__ x, uint16_t *__restrict__ y, int n, int k,
                                               int m) {
     constexpr int RG = 64 / L;
     const int lane = threadIdx.x & 63;
-    const int wave = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+    const int wave = wave_id();
     const int lk = lane % L, rsub = lane / L;
     const int row0 = wave * RT * RG;
     if (row0 >= n) return;  // uniform per wave
     const int ks = (k + 32 * L - 1) / (32 * L);
-    const int spr = scales_per_row<FMT>(k);
+    const uint32_t spr = (uint32_t)scales_per_row<FMT>(k);
+    const Buf cb = make_buf(codes, (uint32_t)n * (uint32_t)(k >> 1));
+    const Buf sb = make_buf(scales, (uint32_t)n * spr * 2u);
+    const Buf xb = make_buf(x, (uint32_t)m * (uint32_t)k * 2u);
     for (int t = 0; t < m; ++t) {
         float acc[RT];
 #pragma unroll
@@ -50,18 +55,17 @@ __global__ __launch_bounds__(256) void k_gemv(const uint8_t *__restrict__ codes,
         for (int s = 0; s < ks; ++s) {
             const int k0 = 32 * (L * s + lk);
             const bool kv = k0 < k;
+            XSlice<FMT> xs;  // activations first: they return from cache before the weights
+            load_xslice<FMT>(xs, xb, kv ? (uint32_t)(t * k + k0) * 2u : OOB);
             uint4 cw[RT];
             uint32_t sw[RT];
 #pragma unroll
             for (int r = 0; r < RT; ++r) {
                 const int row = row0 + r * RG + rsub;
                 const bool v = kv && row < n;
-                cw[r] = v ? *reinterpret_cast<const uint4 *>(codes + (size_t)row * (k >> 1) + (k0 >> 1))
-                          : make_uint4(0, 0, 0, 0);
-                sw[r] = v ? load_scales<FMT>(scales + (size_t)row * spr, k0) : 0u;
+                cw[r] = ld128(cb, v ? (uint32_t)row * (uint32_t)(k >> 1) + (uint32_t)(k0 >> 1) : OOB);
+                sw[r] = ld_scales<FMT>(sb, v ? scale_off<FMT>((uint32_t)row * spr, k0) : OOB);
             }
-            XSlice<FMT> xs;
-            load_xslice<FMT>(xs, x + (size_t)t * k, k0, kv);
             prep_xslice<FMT>(xs);
 #pragma unroll
             for (int r = 0; r < RT; ++r) acc[r] = chunk_dot_bf16<FMT>(cw[r], sw[r], xs, acc[r]);
@@ -70,7 +74,7 @@ __global__ __launch_bounds__(256) void k_gemv(const uint8_t *__restrict__ codes,
         for (int r = 0; r < RT; ++r) {
             const float v = group_sum<L>(acc[r]);
             const int row = row0 + r * RG + rsub;
-            if (lk == 0 && row < n) y[(size_t)t * n + row] = f32_to_bf16_rne(v);
+            if (group_leader<L>(lane) && row < n) y[(size_t)t * n + row] = f32_to_bf16_rne(v);
         }
     }
 }
@@ -83,14 +87,20 @@ __global__ __launch_bounds__(256) void k_dequant(const uint8_t *__restrict__ cod
                                                  float *__restrict__ out, int64_t rows, int k) {
     constexpr int RG = 64 / L;
     const int lane = threadIdx.x & 63;
-    const int64_t wave = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+    const int64_t wave = wave_id();
     const int lk = lane % L;
-    const int64_t row = wave * RG + lane / L;
-    if (row >= rows) return;
-    const int spr = scales_per_row<FMT>(k);
+    const int64_t row0 = wave * RG;  // wave-uniform
+    if (row0 >= rows) return;
+    const int64_t row = row0 + lane / L;
+    const bool rv = row < rows;
+    const uint32_t spr = (uint32_t)scales_per_row<FMT>(k);
+    const int64_t nrows = rows - row0 < RG ? rows - row0 : RG;
+    const Buf cb = make_buf(codes + row0 * (k >> 1), (uint32_t)(nrows * (k >> 1)));
+    const Buf sb = make_buf(scales + row0 * spr, (uint32_t)(nrows * spr * 2u));
+    const uint32_t rl = (uint32_t)(lane / L);
     for (int k0 = 32 * lk; k0 < k; k0 += 32 * L) {
-        const uint4 c = *reinterpret_cast<const uint4 *>(codes + row * (k >> 1) + (k0 >> 1));
-        const uint32_t sc = load_scales<FMT>(scales + row * spr, k0);
+        const uint4 c = ld128(cb, rv ? rl * (uint32_t)(k >> 1) + (uint32_t)(k0 >> 1) : OOB);
+        const uint32_t sc = ld_scales<FMT>(sb, rv ? scale_off<FMT>(rl * spr, k0) : OOB);
         const uint32_t cw[4] = {c.x, c.y, c.z, c.w};
         float v[32];
         if constexpr (FMT == FMT_E2M1) {
@@ -116,43 +126,46 @@ __global__ __launch_bounds__(256) void k_dequant(const uint8_t *__restrict__ cod
                 p = u4x2_bf16<true>(hi);  v[8 * d + 5] = ((float)p.x - 8.f) * s; v[8 * d + 7] = ((float)p.y - 8.f) * s;
             }
         }
-        float4 *o = reinterpret_cast<float4 *>(out + row * k + k0);
+        if (rv) {
+            float4 *o = reinterpret_cast<float4 *>(out + row * k + k0);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) o[i] = make_float4(v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]);
+            for (int i = 0; i < 8; ++i) o[i] = make_float4(v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]);
+        }
     }
 }
 
 // ================================================================= router
 
-// logits[t][r] for rows r in [r_begin, r_end) of the stacked [E routed rows;
-// 1 shared-gate row]: one wave per row, lane l covers elements 8l + 512s.
-// NS = number of 512-element steps (H <= 512 * NS).
+// logits[t][r] for rows r in [r_begin, r_begin + gridDim.x) of the stacked
+// [E routed rows; 1 shared-gate row]: one wave per row, lane l covers elements
+// 8l + 512s.  NS = number of 512-element steps (H <= 512 * NS).
 template <int NS>
 __global__ __launch_bounds__(64) void k_router(const uint16_t *__restrict__ wr, const uint16_t *__restrict__ wsg,
                                                const uint16_t *__restrict__ x, float *__restrict__ logits, int E,
                                                int H, int T, int r_begin, int lstride) {
     const int lane = threadIdx.x;
     const int r = r_begin + blockIdx.x;
-    const uint16_t *row = r < E ? wr + (size_t)r * H : wsg;
+    const Buf wb = make_buf(r < E ? wr + (size_t)r * H : wsg, (uint32_t)H * 2u);
+    const Buf xb = make_buf(x, (uint32_t)T * (uint32_t)H * 2u);
     uint4 w[NS];
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
         const int e0 = 8 * lane + 512 * s;
-        w[s] = e0 < H ? *reinterpret_cast<const uint4 *>(row + e0) : make_uint4(0, 0, 0, 0);
+        w[s] = ld128(wb, e0 < H ? (uint32_t)e0 * 2u : OOB);
     }
     for (int t = 0; t < T; ++t) {
         float acc = 0.f;
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
             const int e0 = 8 * lane + 512 * s;
-            const uint4 xv = e0 < H ? *reinterpret_cast<const uint4 *>(x + (size_t)t * H + e0) : make_uint4(0, 0, 0, 0);
+            const uint4 xv = ld128(xb, e0 < H ? (uint32_t)(t * H + e0) * 2u : OOB);
             acc = dot2(as_bf16x2(w[s].x), xv.x, acc);
             acc = dot2(as_bf16x2(w[s].y), xv.y, acc);
             acc = dot2(as_bf16x2(w[s].z), xv.z, acc);
             acc = dot2(as_bf16x2(w[s].w), xv.w, acc);
         }
         acc = group_sum<64>(acc);
-        if (lane == 0) logits[(size_t)t * lstride + r] = acc;
+        if (group_leader<64>(lane)) logits[(size_t)t * lstride + r] = acc;
     }
 }
 
@@ -165,47 +178,68 @@ __device__ __forceinline__ uint32_t order_key(float f) {
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// (key, id) order of the ranking: larger key first, equal keys by lower id.
+__device__ __forceinline__ bool ranks_before(uint32_t ka, int ia, uint32_t kb, int ib) {
+    return ka > kb || (ka == kb && ia < ib);
+}
+
+// Compare-exchange so that slot a ranks before slot b.
+__device__ __forceinline__ void rank_cx(uint32_t &ka, int &ia, uint32_t &kb, int &ib) {
+    const bool sw = ranks_before(kb, ib, ka, ia);
+    const uint32_t k = sw ? kb : ka, k2 = sw ? ka : kb;
+    const int i = sw ? ib : ia, i2 = sw ? ia : ib;
+    ka = k, kb = k2, ia = i, ib = i2;
+}
+
 // One wave ranks E <= 64*PL logits (+ bias) by descending value, ties to the
-// lower expert id, for `rounds` rounds.  Lane l holds experts l*PL .. l*PL+PL-1,
-// so "lowest lane, then lowest slot" is the lowest id.  Ranking by logit equals
-// ranking by softmax probability (exp is increasing).  Lane j < rounds receives
-// the j-th id and its (biased) logit; the id of round `want` is returned to
-// every lane.
+// lower expert id, for `rounds` rounds.  Ranking by logit equals ranking by
+// softmax probability (exp is increasing).  Each lane first sorts its own PL
+// entries by that order; a round then takes the wave maximum of the lane heads
+// and the lowest lane holding it, whose head is the lowest id with that value
+// (lane l holds experts l*PL .. l*PL+PL-1), and that lane pops its head.  Lane
+// j < rounds receives the j-th id and its (biased) logit; the id of round
+// `want` is returned to every lane.
 template <int PL>
 __device__ __forceinline__ int wave_topk(const float *__restrict__ lg, const float *__restrict__ bias, int E,
                                          int rounds, int want, int &my_id, float &my_val) {
     const int lane = threadIdx.x & 63;
+    const Buf lb = make_buf(lg, (uint32_t)E * 4u);
+    const Buf bb = make_buf(bias, bias ? (uint32_t)E * 4u : 0u);
     uint32_t key[PL];
+    int id[PL];
 #pragma unroll
     for (int i = 0; i < PL; ++i) {
         const int e = lane * PL + i;
-        float v = 0.f;
-        if (e < E) v = lg[e] + (bias ? bias[e] : 0.f);
+        const uint32_t off = e < E ? (uint32_t)e * 4u : OOB;
+        const float v = __uint_as_float(ld32(lb, off)) + __uint_as_float(ld32(bb, off));
         key[i] = e < E ? order_key(v) : 0u;
+        id[i] = e;
+    }
+    // per-lane sort (odd-even transposition, PL passes)
+#pragma unroll
+    for (int pass = 0; pass < PL; ++pass) {
+#pragma unroll
+        for (int i = pass & 1; i + 1 < PL; i += 2) rank_cx(key[i], id[i], key[i + 1], id[i + 1]);
     }
     int sel = 0;
     my_id = -1;
     my_val = 0.f;
     for (int j = 0; j < rounds; ++j) {
-        uint32_t best = key[0];
-        int bi = 0;
-#pragma unroll
-        for (int i = 1; i < PL; ++i)
-            if (key[i] > best) { best = key[i]; bi = i; }
-        const uint32_t m = wave_max_u32(best);
-        const uint64_t mask = __ballot(best == m);
+        const uint32_t m = wave_max_u32(key[0]);
+        const uint64_t mask = __ballot(key[0] == m);
         const int winner = __ffsll((unsigned long long)mask) - 1;
-        const int wid = __shfl(lane * PL + bi, winner);
-        if (lane == winner) {
+        const int wid = __builtin_amdgcn_readlane(id[0], winner);
+        const bool pop = lane == winner;
 #pragma unroll
-            for (int i = 0; i < PL; ++i)
-                if (i == bi) key[i] = 0u;
+        for (int i = 0; i + 1 < PL; ++i) {
+            key[i] = pop ? key[i + 1] : key[i];
+            id[i] = pop ? id[i + 1] : id[i];
         }
-        if (lane == j) {
-            my_id = wid;
-            my_val = __uint_as_float((m & 0x80000000u) ? (m & 0x7FFFFFFFu) : ~m);
-        }
-        if (j == want) sel = wid;
+        key[PL - 1] = pop ? 0u : key[PL - 1];
+        const bool mine = lane == j;
+        my_id = mine ? wid : my_id;
+        my_val = mine ? __uint_as_float((m & 0x80000000u) ? (m & 0x7FFFFFFFu) : ~m) : my_val;
+        sel = j == want ? wid : sel;
     }
     return sel;
 }
@@ -240,23 +274,37 @@ __device__ __forceinline__ int h_index(int i, int L2) {
     return s * span + (q * L2 + lk) * 4 + c;
 }
 
+// Blocks are laid out so that all WPB waves of a block work on one (token,
+// slot): block b covers tiles [tb*WPB, tb*WPB + WPB) of slot j of token t.  For
+// a routed slot, wave 0 of the block ranks the experts once and publishes the
+// ids through LDS; the block's writer (token t, slot 0, first tile block) also
+// stores the routing weights for the down kernel and the caller.
 template <int FMT, int L, int RT, int PL>
-__global__ __launch_bounds__(256) void k_moe_w13(W13Args a) {
+__global__ __launch_bounds__(1024) void k_moe_w13(W13Args a) {
     constexpr int RG = 64 / L;
+    __shared__ int s_ids[16];
     const int lane = threadIdx.x & 63;
-    const int wave = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
-    const int per_tok = a.S * a.tiles;
-    if (wave >= a.T * per_tok) return;  // uniform per wave
-    const int t = wave / per_tok;
-    const int rem = wave - t * per_tok;
-    const int j = rem / a.tiles;
-    const int tile = rem - j * a.tiles;
+    const int wib = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave in block
+    const int wpb = blockDim.x >> 6;
+    const int tblocks = (a.tiles + wpb - 1) / wpb;  // tile blocks per slot
+    const int b = blockIdx.x;
+    const int t = b / (a.S * tblocks);
+    const int rem = b - t * (a.S * tblocks);
+    const int j = rem / tblocks;
+    const int tb = rem - j * tblocks;
+    const int tile = tb * wpb + wib;
+    const bool tile_ok = tile < a.tiles;
     const int lk = lane % L, rsub = lane / L;
     const int H = a.H, I = a.I;
     const int ks = (H + 32 * L - 1) / (32 * L);
-    const int spr = scales_per_row<FMT>(H);
+    const uint32_t spr = (uint32_t)scales_per_row<FMT>(H);
+    const uint32_t mat_codes = (uint32_t)(2 * I) * (uint32_t)(H >> 1);
+    const uint32_t mat_scales = (uint32_t)(2 * I) * spr * 2u;
+    const Buf xb = make_buf(a.x + (size_t)t * H, (uint32_t)H * 2u);
+    XSlice<FMT> xs0;  // step-0 activations, in flight while the experts are ranked
+    load_xslice<FMT>(xs0, xb, 32 * lk < H ? (uint32_t)(32 * lk) * 2u : OOB);
 
-    // which expert: shared slot, routed by this wave's own ranking, or supplied
+    // which expert: shared slot, ranked once per block, or supplied
     const uint8_t *cbase;
     const uint16_t *sbase;
     bool valid = true;
@@ -266,32 +314,40 @@ __global__ __launch_bounds__(256) void k_moe_w13(W13Args a) {
     } else {
         int e;
         if (a.route) {
-            const bool writer = (j == 0 && tile == 0);
-            int my_id;
-            float my_val;
-            e = wave_topk<PL>(a.logits + (size_t)t * a.lstride, a.bias, a.E, writer ? a.K : j + 1, j, my_id, my_val);
-            if (writer) {
-                // weights = softmax over the k selected logits; lane q holds the
-                // q-th, lane 0 the largest; the sum runs in a fixed lane order
-                const float top = __shfl(my_val, 0);
-                const float ex = lane < a.K ? expf(my_val - top) : 0.f;
-                const float sum = group_sum<64>(ex);
-                if (lane < a.K) {
-                    const float w = ex / sum;
-                    a.ids_ws[t * a.K + lane] = my_id;
-                    a.w_ws[t * a.K + lane] = w;
-                    if (a.ids_user) a.ids_user[t * a.K + lane] = my_id;
-                    if (a.w_user) a.w_user[t * a.K + lane] = w;
+            if (wib == 0) {
+                const bool writer = (j == 0 && tb == 0);
+                int my_id;
+                float my_val;
+                wave_topk<PL>(a.logits + (size_t)t * a.lstride, a.bias, a.E, writer ? a.K : j + 1, j, my_id, my_val);
+                if (lane <= j) s_ids[lane] = my_id;
+                if (writer) {
+                    // weights = softmax over the k selected logits; lane q holds the
+                    // q-th, lane 0 the largest; the sum runs in a fixed lane order
+                    const float vmax = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_val), 0));
+                    const float ex = lane < a.K ? expf(my_val - vmax) : 0.f;
+                    const float sum = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(group_sum<64>(ex)), 63));
+                    if (lane < a.K) {
+                        const float w = ex / sum;
+                        a.ids_ws[t * a.K + lane] = my_id;
+                        a.w_ws[t * a.K + lane] = w;
+                        if (a.ids_user) a.ids_user[t * a.K + lane] = my_id;
+                        if (a.w_user) a.w_user[t * a.K + lane] = w;
+                    }
                 }
             }
+            __syncthreads();
+            e = __builtin_amdgcn_readfirstlane(s_ids[j]);
         } else {
             e = a.ids_in[t * a.K + j];
         }
         valid = e >= 0 && e < a.E;  // an id out of range reads nothing and poisons h
         const int eo = valid ? e : 0;
-        cbase = a.codes + (size_t)eo * (2 * I) * (H >> 1);
-        sbase = a.scales + (size_t)eo * (2 * I) * spr;
+        cbase = a.codes + (size_t)eo * mat_codes;
+        sbase = a.scales + (size_t)eo * (mat_scales >> 1);
     }
+    if (!tile_ok) return;  // after the block's barrier; uniform per wave
+    const Buf cb = make_buf(cbase, valid ? mat_codes : 0u);
+    const Buf sb = make_buf(sbase, valid ? mat_scales : 0u);
 
     const int i0 = tile * RT * RG;  // first gate row of this tile
     float ag[RT], au[RT];
@@ -299,21 +355,22 @@ __global__ __launch_bounds__(256) void k_moe_w13(W13Args a) {
     for (int r = 0; r < RT; ++r) ag[r] = au[r] = 0.f;
     for (int s = 0; s < ks; ++s) {
         const int k0 = 32 * (L * s + lk);
-        const bool kv = valid && k0 < H;
+        const bool kv = k0 < H;
+        XSlice<FMT> xs;
+        if (s == 0) xs = xs0;
+        else load_xslice<FMT>(xs, xb, kv ? (uint32_t)k0 * 2u : OOB);
         uint4 cg[RT], cu[RT];
         uint32_t sg[RT], su[RT];
 #pragma unroll
         for (int r = 0; r < RT; ++r) {
             const int i = i0 + r * RG + rsub;
             const bool v = kv && i < I;
-            const size_t rg = (size_t)i, ru = (size_t)(I + i);
-            cg[r] = v ? *reinterpret_cast<const uint4 *>(cbase + rg * (H >> 1) + (k0 >> 1)) : make_uint4(0, 0, 0, 0);
-            cu[r] = v ? *reinterpret_cast<const uint4 *>(cbase + ru * (H >> 1) + (k0 >> 1)) : make_uint4(0, 0, 0, 0);
-            sg[r] = v ? load_scales<FMT>(sbase + rg * spr, k0) : 0u;
-            su[r] = v ? load_scales<FMT>(sbase + ru * spr, k0) : 0u;
+            const uint32_t rg = (uint32_t)i, ru = (uint32_t)(I + i);
+            cg[r] = ld128(cb, v ? rg * (uint32_t)(H >> 1) + (uint32_t)(k0 >> 1) : OOB);
+            cu[r] = ld128(cb, v ? ru * (uint32_t)(H >> 1) + (uint32_t)(k0 >> 1) : OOB);
+            sg[r] = ld_scales<FMT>(sb, v ? scale_off<FMT>(rg * spr, k0) : OOB);
+            su[r] = ld_scales<FMT>(sb, v ? scale_off<FMT>(ru * spr, k0) : OOB);
         }
-        XSlice<FMT> xs;
-        load_xslice<FMT>(xs, a.x + (size_t)t * H, k0, k0 < H);
         prep_xslice<FMT>(xs);
 #pragma unroll
         for (int r = 0; r < RT; ++r) {
@@ -327,7 +384,7 @@ __global__ __launch_bounds__(256) void k_moe_w13(W13Args a) {
         const float g = group_sum<L>(ag[r]);
         const float u = group_sum<L>(au[r]);
         const int i = i0 + r * RG + rsub;
-        if (lk == 0 && i < I) {
+        if (group_leader<L>(lane) && i < I) {
             const float hv = valid ? (g / (1.f + expf(-g))) * u : __builtin_nanf("");
             hrow[h_index(i, a.L2)] = hv;
         }
@@ -357,16 +414,27 @@ __global__ __launch_bounds__(1024) void k_moe_down(DownArgs a) {
     constexpr int ROWS = RT * RG;
     extern __shared__ float part[];  // [S][ROWS]
     const int lane = threadIdx.x & 63;
-    const int wv = threadIdx.x >> 6;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
     const int nw = blockDim.x >> 6;
     const int t = blockIdx.x / a.blocks_per_tok;
     const int row0 = (blockIdx.x - t * a.blocks_per_tok) * ROWS;
     const int lk = lane % L, rsub = lane / L;
     const int I = a.I, H = a.H;
     const int ks = (I + 32 * L - 1) / (32 * L);
-    const int spr = scales_per_row<FMT>(I);
+    const uint32_t spr = (uint32_t)scales_per_row<FMT>(I);
+    const uint32_t mat_codes = (uint32_t)H * (uint32_t)(I >> 1);
+    const uint32_t mat_scales = (uint32_t)H * spr * 2u;
 
     for (int j = wv; j < a.S; j += nw) {
+        // step-0 activations first: they do not depend on the routing
+        const Buf hb = make_buf(a.h + ((size_t)t * a.S + j) * a.hstride, (uint32_t)a.hstride * 4u);
+        float4 hv0[8];
+        {
+            const uint32_t h0 = (uint32_t)lk * 16u;
+#pragma unroll
+            for (int q = 0; q < 8; ++q)
+                hv0[q] = __builtin_bit_cast(float4, ld128(hb, 32 * lk < I ? h0 + (uint32_t)q * L * 16u : OOB));
+        }
         const uint8_t *cbase;
         const uint16_t *sbase;
         float coef;
@@ -379,31 +447,37 @@ __global__ __launch_bounds__(1024) void k_moe_down(DownArgs a) {
             const int e = a.ids[t * a.K + j];
             valid = e >= 0 && e < a.E;
             const int eo = valid ? e : 0;
-            cbase = a.codes + (size_t)eo * H * (I >> 1);
-            sbase = a.scales + (size_t)eo * H * spr;
+            cbase = a.codes + (size_t)eo * mat_codes;
+            sbase = a.scales + (size_t)eo * (mat_scales >> 1);
             coef = a.w[t * a.K + j];
         }
-        const float *hb = a.h + ((size_t)t * a.S + j) * a.hstride;
+        const Buf cb = make_buf(cbase, valid ? mat_codes : 0u);
+        const Buf sb = make_buf(sbase, valid ? mat_scales : 0u);
         float acc[RT];
 #pragma unroll
         for (int r = 0; r < RT; ++r) acc[r] = 0.f;
         for (int s = 0; s < ks; ++s) {
             const int k0 = 32 * (L * s + lk);
-            const bool kv = valid && k0 < I;
+            const bool kv = k0 < I;
+            float4 hv[8];  // activations first
+            if (s == 0) {
+#pragma unroll
+                for (int q = 0; q < 8; ++q) hv[q] = hv0[q];
+            } else {
+                const uint32_t h0 = ((uint32_t)s * 32u * L + (uint32_t)lk * 4u) * 4u;
+#pragma unroll
+                for (int q = 0; q < 8; ++q)
+                    hv[q] = __builtin_bit_cast(float4, ld128(hb, kv ? h0 + (uint32_t)q * L * 16u : OOB));
+            }
             uint4 cw[RT];
             uint32_t sw[RT];
 #pragma unroll
             for (int r = 0; r < RT; ++r) {
                 const int row = row0 + r * RG + rsub;
                 const bool v = kv && row < H;
-                cw[r] = v ? *reinterpret_cast<const uint4 *>(cbase + (size_t)row * (I >> 1) + (k0 >> 1))
-                          : make_uint4(0, 0, 0, 0);
-                sw[r] = v ? load_scales<FMT>(sbase + (size_t)row * spr, k0) : 0u;
+                cw[r] = ld128(cb, v ? (uint32_t)row * (uint32_t)(I >> 1) + (uint32_t)(k0 >> 1) : OOB);
+                sw[r] = ld_scales<FMT>(sb, v ? scale_off<FMT>((uint32_t)row * spr, k0) : OOB);
             }
-            float4 hv[8];
-            const float4 *hp = reinterpret_cast<const float4 *>(hb + (size_t)s * 32 * L) + lk;
-#pragma unroll
-            for (int q = 0; q < 8; ++q) hv[q] = kv ? hp[q * L] : make_float4(0.f, 0.f, 0.f, 0.f);
             float hs = 0.f;
             if constexpr (FMT == FMT_INT4) {
 #pragma unroll
@@ -415,7 +489,7 @@ __global__ __launch_bounds__(1024) void k_moe_down(DownArgs a) {
 #pragma unroll
         for (int r = 0; r < RT; ++r) {
             const float v = group_sum<L>(acc[r]);
-            if (lk == 0) part[j * ROWS + r * RG + rsub] = valid ? v * coef : __builtin_nanf("");
+            if (group_leader<L>(lane)) part[j * ROWS + r * RG + rsub] = valid ? v * coef : __builtin_nanf("");
         }
     }
     __syncthreads();
@@ -437,6 +511,21 @@ using w4::fail;
 
 namespace {
 
+// A launch target: the stream and, for the measurement entry point, the pair of
+// events the runtime records at the kernel's start and end.
+struct Launch {
+    hipStream_t st;
+    hipEvent_t start = nullptr, stop = nullptr;
+};
+
+template <typename F, typename... Args>
+void go(const Launch &l, F kernel, dim3 grid, dim3 block, uint32_t shmem, Args... args) {
+    if (l.start)
+        hipExtLaunchKernelGGL(kernel, grid, block, shmem, l.st, l.start, l.stop, 0u, args...);
+    else
+        hipLaunchKernelGGL(kernel, grid, block, shmem, l.st, args...);
+}
+
 int lanes_for(int64_t k) {
     int64_t need = (k + 31) / 32;
     int L = 1;
@@ -454,6 +543,9 @@ int check_matrix(const w4_matrix *W, const char *what) {
     if (!aligned(W->codes, 16)) return fail(W4_ERR_ALIGNMENT, "%s: codes not 16-byte aligned", what);
     if (!aligned(W->scales, 4)) return fail(W4_ERR_ALIGNMENT, "%s: scales not 4-byte aligned", what);
     if (W->n > (1 << 30) || W->k > (1 << 20)) return fail(W4_ERR_UNSUPPORTED, "%s: dimension too large", what);
+    // one matrix of the stack is addressed through 32-bit buffer offsets
+    if ((uint64_t)W->n * (uint64_t)W->k / 2 >= (1ull << 31))
+        return fail(W4_ERR_UNSUPPORTED, "%s: one matrix must hold fewer than 2^31 code bytes", what);
     return W4_OK;
 }
 
@@ -465,13 +557,20 @@ int hip_status(const char *what) {
 
 // ---------------------------------------------------------------- GEMV launch
 
+#ifndef W4_GEMV_ROWS
+#define W4_GEMV_ROWS 4  // rows per wave of the dense GEMV (at least one load group)
+#endif
+#ifndef W4_GEMV_WPB
+#define W4_GEMV_WPB 4  // waves per block of the dense GEMV
+#endif
+
 template <int FMT, int L>
 void launch_gemv_L(const w4_matrix *W, const uint16_t *x, int m, uint16_t *y, hipStream_t st) {
-    constexpr int RT = L == 64 ? 4 : (L == 32 ? 2 : 1);
     constexpr int RG = 64 / L;
+    constexpr int RT = RG >= W4_GEMV_ROWS ? 1 : W4_GEMV_ROWS / RG;
     const int n = (int)W->n, k = (int)W->k;
     const int waves = (n + RT * RG - 1) / (RT * RG);
-    const int wpb = 4;
+    const int wpb = W4_GEMV_WPB;
     const int blocks = (waves + wpb - 1) / wpb;
     hipLaunchKernelGGL((k_gemv<FMT, L, RT>), dim3(blocks), dim3(64 * wpb), 0, st, W->codes, W->scales, x, y, n, k, m);
 }
@@ -578,42 +677,50 @@ int check_layer(const moe_w4a16_layer *Lr, int64_t T, MoEPlan &p) {
 }
 
 int launch_router(const moe_w4a16_layer *Lr, const MoEPlan &p, const uint16_t *x, float *logits, int r_begin,
-                  int r_end, hipStream_t st) {
+                  int r_end, const Launch &st) {
     const int nrows = r_end - r_begin;
     if (nrows <= 0) return W4_OK;
     const int ns = (p.H + 511) / 512;
-    auto go = [&](auto NSc) {
+    auto with_ns = [&](auto NSc) {
         constexpr int NS = decltype(NSc)::value;
-        hipLaunchKernelGGL((k_router<NS>), dim3(nrows), dim3(64), 0, st, Lr->router_w, Lr->shared_gate_w, x, logits,
-                           p.E, p.H, p.T, r_begin, p.lstride);
+        go(st, k_router<NS>, dim3(nrows), dim3(64), 0, Lr->router_w, Lr->shared_gate_w, x, logits, p.E, p.H, p.T,
+           r_begin, p.lstride);
     };
-    if (ns <= 1) go(std::integral_constant<int, 1>());
-    else if (ns <= 2) go(std::integral_constant<int, 2>());
-    else if (ns <= 4) go(std::integral_constant<int, 4>());
-    else if (ns <= 8) go(std::integral_constant<int, 8>());
-    else if (ns <= 16) go(std::integral_constant<int, 16>());
+    if (ns <= 1) with_ns(std::integral_constant<int, 1>());
+    else if (ns <= 2) with_ns(std::integral_constant<int, 2>());
+    else if (ns <= 4) with_ns(std::integral_constant<int, 4>());
+    else if (ns <= 8) with_ns(std::integral_constant<int, 8>());
+    else if (ns <= 16) with_ns(std::integral_constant<int, 16>());
     else return fail(W4_ERR_UNSUPPORTED, "hidden=%d too large for the router kernel", p.H);
     return W4_OK;
 }
 
+#ifndef W4_W13_ROWS
+#define W4_W13_ROWS 2  // gate rows (and as many up rows) per wave of the W13 kernel
+#endif
+#ifndef W4_W13_WPB
+#define W4_W13_WPB 4  // waves per block of the W13 kernel
+#endif
+
 template <int FMT, int L>
-void launch_w13_L(const MoEPlan &p, W13Args &a, hipStream_t st) {
-    constexpr int RT = L == 64 ? 4 : (L == 32 ? 2 : 1);
+void launch_w13_L(const MoEPlan &p, W13Args &a, const Launch &st) {
     constexpr int RG = 64 / L;
+    constexpr int RT = RG >= W4_W13_ROWS ? 1 : W4_W13_ROWS / RG;
     a.tiles = (p.I + RT * RG - 1) / (RT * RG);
-    const int waves = p.T * p.S * a.tiles;
-    const int wpb = 4;
-    const int blocks = (waves + wpb - 1) / wpb;
+    const int wpb = a.tiles < W4_W13_WPB ? a.tiles : W4_W13_WPB;
+    const int tblocks = (a.tiles + wpb - 1) / wpb;
+    const int blocks = p.T * p.S * tblocks;
     const int pl = (p.E + 63) / 64;
-    if (pl <= 1) hipLaunchKernelGGL((k_moe_w13<FMT, L, RT, 1>), dim3(blocks), dim3(64 * wpb), 0, st, a);
-    else if (pl <= 2) hipLaunchKernelGGL((k_moe_w13<FMT, L, RT, 2>), dim3(blocks), dim3(64 * wpb), 0, st, a);
-    else if (pl <= 4) hipLaunchKernelGGL((k_moe_w13<FMT, L, RT, 4>), dim3(blocks), dim3(64 * wpb), 0, st, a);
-    else if (pl <= 8) hipLaunchKernelGGL((k_moe_w13<FMT, L, RT, 8>), dim3(blocks), dim3(64 * wpb), 0, st, a);
-    else hipLaunchKernelGGL((k_moe_w13<FMT, L, RT, 16>), dim3(blocks), dim3(64 * wpb), 0, st, a);
+    const dim3 g(blocks), bl(64 * wpb);
+    if (pl <= 1) go(st, k_moe_w13<FMT, L, RT, 1>, g, bl, 0, a);
+    else if (pl <= 2) go(st, k_moe_w13<FMT, L, RT, 2>, g, bl, 0, a);
+    else if (pl <= 4) go(st, k_moe_w13<FMT, L, RT, 4>, g, bl, 0, a);
+    else if (pl <= 8) go(st, k_moe_w13<FMT, L, RT, 8>, g, bl, 0, a);
+    else go(st, k_moe_w13<FMT, L, RT, 16>, g, bl, 0, a);
 }
 
 template <int FMT>
-void launch_w13(const MoEPlan &p, W13Args &a, hipStream_t st) {
+void launch_w13(const MoEPlan &p, W13Args &a, const Launch &st) {
     switch (p.L13) {
     case 1: launch_w13_L<FMT, 1>(p, a, st); break;
     case 2: launch_w13_L<FMT, 2>(p, a, st); break;
@@ -625,19 +732,27 @@ void launch_w13(const MoEPlan &p, W13Args &a, hipStream_t st) {
     }
 }
 
+#ifndef W4_DOWN_ROWS
+#define W4_DOWN_ROWS 8  // output rows per block of the down kernel (at least one load group)
+#endif
+#ifndef W4_DOWN_WAVES
+#define W4_DOWN_WAVES 16  // at most this many waves per block; the slots are spread over them
+#endif
+
 template <int FMT, int L>
-void launch_down_L(const MoEPlan &p, DownArgs &a, hipStream_t st) {
+void launch_down_L(const MoEPlan &p, DownArgs &a, const Launch &st) {
     constexpr int RG = 64 / L;
-    constexpr int RT = RG >= 8 ? 1 : (8 / RG > 4 ? 4 : 8 / RG);
+    constexpr int RT = RG >= W4_DOWN_ROWS ? 1 : W4_DOWN_ROWS / RG;
     constexpr int ROWS = RT * RG;
     a.blocks_per_tok = (p.H + ROWS - 1) / ROWS;
-    const int nw = p.S < 16 ? p.S : 16;
+    int nw = p.S < W4_DOWN_WAVES ? p.S : W4_DOWN_WAVES;
+    nw = (p.S + ((p.S + nw - 1) / nw) - 1) / ((p.S + nw - 1) / nw);  // equal slots per wave
     const size_t lds = (size_t)p.S * ROWS * sizeof(float);
-    hipLaunchKernelGGL((k_moe_down<FMT, L, RT>), dim3(p.T * a.blocks_per_tok), dim3(64 * nw), lds, st, a);
+    go(st, k_moe_down<FMT, L, RT>, dim3(p.T * a.blocks_per_tok), dim3(64 * nw), (uint32_t)lds, a);
 }
 
 template <int FMT>
-void launch_down(const MoEPlan &p, DownArgs &a, hipStream_t st) {
+void launch_down(const MoEPlan &p, DownArgs &a, const Launch &st) {
     switch (p.L2) {
     case 1: launch_down_L<FMT, 1>(p, a, st); break;
     case 2: launch_down_L<FMT, 2>(p, a, st); break;
@@ -650,7 +765,8 @@ void launch_down(const MoEPlan &p, DownArgs &a, hipStream_t st) {
 }
 
 int run_moe(const moe_w4a16_layer *Lr, const uint16_t *x, int64_t T, const int32_t *ids_in, const float *w_in,
-            uint16_t *y, int32_t *topk_ids, float *topk_w, void *ws, size_t ws_bytes, void *stream) {
+            uint16_t *y, int32_t *topk_ids, float *topk_w, void *ws, size_t ws_bytes, void *stream,
+            void *const *events = nullptr) {
     MoEPlan p;
     int st = check_layer(Lr, T, p);
     if (st) return st;
@@ -672,10 +788,19 @@ int run_moe(const moe_w4a16_layer *Lr, const uint16_t *x, int64_t T, const int32
     float *w_ws = (float *)(wsb + p.off_w);
     float *h = (float *)(wsb + p.off_h);
 
+    if (events)
+        for (int i = 0; i < 6; ++i)
+            if (!events[i]) return fail(W4_ERR_INVALID_ARG, "null stage event %d", i);
+    Launch l_router{sm}, l_w13{sm}, l_down{sm};
+    if (events) {
+        l_router.start = (hipEvent_t)events[0], l_router.stop = (hipEvent_t)events[1];
+        l_w13.start = (hipEvent_t)events[2], l_w13.stop = (hipEvent_t)events[3];
+        l_down.start = (hipEvent_t)events[4], l_down.stop = (hipEvent_t)events[5];
+    }
     (void)hipGetLastError();  // clear a stale error so the checks below see only ours
     // 1) router logits (all experts + shared gate) or just the shared gate
-    if (route) st = launch_router(Lr, p, x, logits, 0, p.E + (Lr->has_shared ? 1 : 0), sm);
-    else if (Lr->has_shared) st = launch_router(Lr, p, x, logits, p.E, p.E + 1, sm);
+    if (route) st = launch_router(Lr, p, x, logits, 0, p.E + (Lr->has_shared ? 1 : 0), l_router);
+    else if (Lr->has_shared) st = launch_router(Lr, p, x, logits, p.E, p.E + 1, l_router);
     if (st) return st;
     if ((st = hip_status("router launch"))) return st;
 
@@ -696,8 +821,8 @@ int run_moe(const moe_w4a16_layer *Lr, const uint16_t *x, int64_t T, const int32
     a.h = h;
     a.H = p.H, a.I = p.I, a.E = p.E, a.K = p.K, a.S = p.S, a.T = p.T;
     a.lstride = p.lstride, a.hstride = p.hstride, a.route = route ? 1 : 0, a.L2 = p.L2;
-    if (Lr->w13.format == W4_FMT_E2M1_F16S16) launch_w13<FMT_E2M1>(p, a, sm);
-    else launch_w13<FMT_INT4>(p, a, sm);
+    if (Lr->w13.format == W4_FMT_E2M1_F16S16) launch_w13<FMT_E2M1>(p, a, l_w13);
+    else launch_w13<FMT_INT4>(p, a, l_w13);
     if ((st = hip_status("w13 launch"))) return st;
 
     // 3) down projection + weighted combine
@@ -713,8 +838,8 @@ int run_moe(const moe_w4a16_layer *Lr, const uint16_t *x, int64_t T, const int32
     d.y = y;
     d.H = p.H, d.I = p.I, d.E = p.E, d.K = p.K, d.S = p.S, d.T = p.T;
     d.lstride = p.lstride, d.hstride = p.hstride;
-    if (Lr->w2.format == W4_FMT_E2M1_F16S16) launch_down<FMT_E2M1>(p, d, sm);
-    else launch_down<FMT_INT4>(p, d, sm);
+    if (Lr->w2.format == W4_FMT_E2M1_F16S16) launch_down<FMT_E2M1>(p, d, l_down);
+    else launch_down<FMT_INT4>(p, d, l_down);
     return hip_status("down launch");
 }
 
@@ -761,6 +886,13 @@ int moe_w4a16_forward(const moe_w4a16_layer *L, const uint16_t *x, int64_t T, ui
                       float *topk_w, void *ws, size_t ws_bytes, void *stream) {
     w4::clear_error();
     return run_moe(L, x, T, nullptr, nullptr, y, topk_ids, topk_w, ws, ws_bytes, stream);
+}
+
+int moe_w4a16_forward_timed(const moe_w4a16_layer *L, const uint16_t *x, int64_t T, uint16_t *y, int32_t *topk_ids,
+                            float *topk_w, void *ws, size_t ws_bytes, void *stream, void *const *events) {
+    w4::clear_error();
+    if (!events) return fail(W4_ERR_INVALID_ARG, "null events");
+    return run_moe(L, x, T, nullptr, nullptr, y, topk_ids, topk_w, ws, ws_bytes, stream, events);
 }
 
 int moe_w4a16_experts(const moe_w4a16_layer *L, const uint16_t *x, int64_t T, const int32_t *ids, const float *w,

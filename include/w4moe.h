@@ -190,6 +190,18 @@ size_t moe_w4a16_workspace_bytes(const moe_w4a16_layer *L, int64_t T);
 int moe_w4a16_forward(const moe_w4a16_layer *L, const uint16_t *x, int64_t T, uint16_t *y,
                       int32_t *topk_ids, float *topk_w, void *ws, size_t ws_bytes, void *stream);
 
+/* Measurement variant of moe_w4a16_forward: identical work, with each of the
+ * three kernels launched through hipExtLaunchKernel so that the runtime
+ * records the caller's events at the kernel's start and end on `stream`.
+ * `events` is an array of six hipEvent_t: start/stop of the router kernel,
+ * start/stop of the grouped W13 kernel, start/stop of the down/combine kernel
+ * (the router pair is not recorded for a layer whose router is skipped).  Not
+ * for use under stream capture.  Errors as moe_w4a16_forward, plus
+ * W4_ERR_INVALID_ARG for a null event. */
+int moe_w4a16_forward_timed(const moe_w4a16_layer *L, const uint16_t *x, int64_t T, uint16_t *y,
+                            int32_t *topk_ids, float *topk_w, void *ws, size_t ws_bytes, void *stream,
+                            void *const *events);
+
 /* Experts and combine only, with caller-supplied routing (the one-call shape of
  * README P45): ids int32 [T][k] in [0, E), w fp32 [T][k] (used as given).  The
  * shared expert, if present, is still added with its sigmoid gate. */
