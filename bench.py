@@ -381,6 +381,8 @@ def main():
     ap.add_argument("--cpu-tokens", type=int, default=1)
     ap.add_argument("--cpu-reps", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="first copy 256 MiB device-to-device 3 times (a plain copy of known size for counter runs)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1).", file=sys.stderr)
@@ -399,6 +401,13 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     w4.lib()
+    if args.calibrate_copy:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     if args.workload.startswith("gemv"):
         res, shape = run_gemv(args, torch, w4, wl, synth)
         cpu = None if args.no_cpu_baseline else cpu_baseline_gemv(shape, args.cpu_reps)

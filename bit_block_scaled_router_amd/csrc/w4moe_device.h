@@ -126,6 +126,17 @@ __device__ __forceinline__ int wave_id() {
     return __builtin_amdgcn_readfirstlane((int)(blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6)));
 }
 
+// Wave-uniform loads through the scalar cache (constant address space): used
+// for routing ids and weights so that they do not queue behind vector loads.
+typedef const __attribute__((address_space(4))) int32_t c4_i32;
+typedef const __attribute__((address_space(4))) float c4_f32;
+__device__ __forceinline__ int32_t ld_uniform(const int32_t *p, int idx) {
+    return ((c4_i32 *)p)[__builtin_amdgcn_readfirstlane(idx)];
+}
+__device__ __forceinline__ float ld_uniform(const float *p, int idx) {
+    return ((c4_f32 *)p)[__builtin_amdgcn_readfirstlane(idx)];
+}
+
 // ---------------------------------------------------------------- buffer loads
 
 // Raw buffer resources: a load whose byte offset lies at or beyond the

@@ -178,27 +178,14 @@ __device__ __forceinline__ uint32_t order_key(float f) {
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// (key, id) order of the ranking: larger key first, equal keys by lower id.
-__device__ __forceinline__ bool ranks_before(uint32_t ka, int ia, uint32_t kb, int ib) {
-    return ka > kb || (ka == kb && ia < ib);
-}
-
-// Compare-exchange so that slot a ranks before slot b.
-__device__ __forceinline__ void rank_cx(uint32_t &ka, int &ia, uint32_t &kb, int &ib) {
-    const bool sw = ranks_before(kb, ib, ka, ia);
-    const uint32_t k = sw ? kb : ka, k2 = sw ? ka : kb;
-    const int i = sw ? ib : ia, i2 = sw ? ia : ib;
-    ka = k, kb = k2, ia = i, ib = i2;
-}
-
 // One wave ranks E <= 64*PL logits (+ bias) by descending value, ties to the
 // lower expert id, for `rounds` rounds.  Ranking by logit equals ranking by
-// softmax probability (exp is increasing).  Each lane first sorts its own PL
-// entries by that order; a round then takes the wave maximum of the lane heads
-// and the lowest lane holding it, whose head is the lowest id with that value
-// (lane l holds experts l*PL .. l*PL+PL-1), and that lane pops its head.  Lane
-// j < rounds receives the j-th id and its (biased) logit; the id of round
-// `want` is returned to every lane.
+// softmax probability (exp is increasing).  Lane l holds experts l*PL ..
+// l*PL+PL-1, so "lowest lane, then lowest slot" is the lowest id.  A round
+// takes each lane's best remaining entry (first index on equal keys), the
+// wave maximum of those and the lowest lane holding it; that lane removes the
+// entry.  Lane j < rounds receives the j-th id and its (biased) logit; the id
+// of round `want` is returned to every lane.
 template <int PL>
 __device__ __forceinline__ int wave_topk(const float *__restrict__ lg, const float *__restrict__ bias, int E,
                                          int rounds, int want, int &my_id, float &my_val) {
@@ -206,36 +193,32 @@ __device__ __forceinline__ int wave_topk(const float *__restrict__ lg, const flo
     const Buf lb = make_buf(lg, (uint32_t)E * 4u);
     const Buf bb = make_buf(bias, bias ? (uint32_t)E * 4u : 0u);
     uint32_t key[PL];
-    int id[PL];
 #pragma unroll
     for (int i = 0; i < PL; ++i) {
         const int e = lane * PL + i;
         const uint32_t off = e < E ? (uint32_t)e * 4u : OOB;
         const float v = __uint_as_float(ld32(lb, off)) + __uint_as_float(ld32(bb, off));
         key[i] = e < E ? order_key(v) : 0u;
-        id[i] = e;
-    }
-    // per-lane sort (odd-even transposition, PL passes)
-#pragma unroll
-    for (int pass = 0; pass < PL; ++pass) {
-#pragma unroll
-        for (int i = pass & 1; i + 1 < PL; i += 2) rank_cx(key[i], id[i], key[i + 1], id[i + 1]);
     }
     int sel = 0;
     my_id = -1;
     my_val = 0.f;
     for (int j = 0; j < rounds; ++j) {
-        const uint32_t m = wave_max_u32(key[0]);
-        const uint64_t mask = __ballot(key[0] == m);
+        uint32_t best = key[0];
+        int bi = 0;
+#pragma unroll
+        for (int i = 1; i < PL; ++i) {
+            const bool gt = key[i] > best;
+            best = gt ? key[i] : best;
+            bi = gt ? i : bi;
+        }
+        const uint32_t m = wave_max_u32(best);
+        const uint64_t mask = __ballot(best == m);
         const int winner = __ffsll((unsigned long long)mask) - 1;
-        const int wid = __builtin_amdgcn_readlane(id[0], winner);
+        const int wid = __builtin_amdgcn_readlane(lane * PL + bi, winner);
         const bool pop = lane == winner;
 #pragma unroll
-        for (int i = 0; i + 1 < PL; ++i) {
-            key[i] = pop ? key[i + 1] : key[i];
-            id[i] = pop ? id[i + 1] : id[i];
-        }
-        key[PL - 1] = pop ? 0u : key[PL - 1];
+        for (int i = 0; i < PL; ++i) key[i] = (pop && i == bi) ? 0u : key[i];
         const bool mine = lane == j;
         my_id = mine ? wid : my_id;
         my_val = mine ? __uint_as_float((m & 0x80000000u) ? (m & 0x7FFFFFFFu) : ~m) : my_val;
@@ -338,7 +321,7 @@ __global__ __launch_bounds__(1024) void k_moe_w13(W13Args a) {
             __syncthreads();
             e = __builtin_amdgcn_readfirstlane(s_ids[j]);
         } else {
-            e = a.ids_in[t * a.K + j];
+            e = ld_uniform(a.ids_in, t * a.K + j);
         }
         valid = e >= 0 && e < a.E;  // an id out of range reads nothing and poisons h
         const int eo = valid ? e : 0;
@@ -442,14 +425,14 @@ __global__ __launch_bounds__(1024) void k_moe_down(DownArgs a) {
         if (j == a.K) {
             cbase = a.s_codes;
             sbase = a.s_scales;
-            coef = 1.f / (1.f + expf(-a.logits[(size_t)t * a.lstride + a.E]));
+            coef = 1.f / (1.f + expf(-ld_uniform(a.logits, t * a.lstride + a.E)));
         } else {
-            const int e = a.ids[t * a.K + j];
+            const int e = ld_uniform(a.ids, t * a.K + j);
             valid = e >= 0 && e < a.E;
             const int eo = valid ? e : 0;
             cbase = a.codes + (size_t)eo * mat_codes;
             sbase = a.scales + (size_t)eo * (mat_scales >> 1);
-            coef = a.w[t * a.K + j];
+            coef = ld_uniform(a.w, t * a.K + j);
         }
         const Buf cb = make_buf(cbase, valid ? mat_codes : 0u);
         const Buf sb = make_buf(sbase, valid ? mat_scales : 0u);
