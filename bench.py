@@ -128,18 +128,37 @@ def moe_bytes(shape, distinct):
     return b
 
 
-def stage_bytes(shape, distinct):
-    """Algorithmic bytes per launch of each MoE kernel (T = shape.tokens)."""
+def stage_bytes(shape, distinct, n_stages=3):
+    """Algorithmic bytes per launch of each MoE kernel (T = shape.tokens).
+
+    Single-token path (3 kernels): router, W13 + SiLU over all (token, slot),
+    down + combine.  Batched path (5 kernels): router, top-k + grouping, W13 per
+    expert group, W2 per expert group, ordered combine.  Weights count once per
+    distinct expert (the batched path reads each active expert once)."""
     H, I, E, T, K = shape.hidden, shape.inter, shape.num_experts, shape.tokens, shape.top_k
     S = K + (1 if shape.has_shared else 0)
     w13 = 2 * I * H // 2 + 2 * I * H // 16 * 2
     w2 = H * I // 2 + H * I // 16 * 2
     nexp = distinct + (1 if shape.has_shared else 0)
+    router = E * H * 2 + (H * 2 if shape.has_shared else 0) + T * H * 2 + T * (E + 1) * 4
+    if n_stages == 3:
+        return {
+            "k_router": router,
+            "k_moe_w13": nexp * w13 + T * H * 2 + T * E * 4 + T * S * I * 4,
+            "k_moe_down": nexp * w2 + T * S * I * 4 + T * K * 8 + T * H * 2,
+        }
+    rows = T * K + T  # routed pairs + shared rows
     return {
-        "k_router": E * H * 2 + (H * 2 if shape.has_shared else 0) + T * H * 2 + T * (E + 1) * 4,
-        "k_moe_w13": nexp * w13 + T * H * 2 + T * E * 4 + T * S * I * 4,
-        "k_moe_down": nexp * w2 + T * S * I * 4 + T * K * 8 + T * H * 2,
+        "k_router": router,
+        "k_moe_route_group": T * E * 4 + T * K * 8 + rows * 4,
+        "k_moe_gw13": nexp * w13 + T * H * 2 + rows * I * 4,
+        "k_moe_gw2": nexp * w2 + rows * I * 4 + rows * H * 4,
+        "k_moe_gcombine": rows * H * 4 + T * K * 8 + T * H * 2,
     }
+
+
+STAGES = {3: ["k_router", "k_moe_w13", "k_moe_down"],
+          5: ["k_router", "k_moe_route_group", "k_moe_gw13", "k_moe_gw2", "k_moe_gcombine"]}
 
 
 # ----------------------------------------------------------------------------- CPU baseline
@@ -256,17 +275,19 @@ def run_moe(args, torch, w4, wl, synth):
 
     # per-kernel durations: the same K steps launched eagerly through the
     # measurement entry point, whose kernels carry start/stop HIP events
+    n_stages = w4.moe_w4a16_stage_count(base, T)
+    names = STAGES[n_stages]
     hip = HipEvents()
-    evs = hip.create(6 * n_steps)
+    ne = 2 * n_stages
+    evs = hip.create(ne * n_steps)
     for i in range(n_steps):
-        w4.moe_w4a16_forward_timed(layers[i % R], xs[i % P], y, ws, evs[6 * i:6 * i + 6])
+        w4.moe_w4a16_forward_timed(layers[i % R], xs[i % P], y, ws, evs[ne * i:ne * i + ne])
     torch.cuda.synchronize()
-    stage = {"k_router": [], "k_moe_w13": [], "k_moe_down": []}
+    stage = {k: [] for k in names}
     for i in range(n_steps):
-        e = evs[6 * i:6 * i + 6]
-        stage["k_router"].append(hip.elapsed_ms(e[0], e[1]))
-        stage["k_moe_w13"].append(hip.elapsed_ms(e[2], e[3]))
-        stage["k_moe_down"].append(hip.elapsed_ms(e[4], e[5]))
+        e = evs[ne * i:ne * i + ne]
+        for si, k in enumerate(names):
+            stage[k].append(hip.elapsed_ms(e[2 * si], e[2 * si + 1]))
     hip.destroy(evs)
     stage_us = {k: float(np.mean(v)) * 1e3 for k, v in stage.items()}
 
@@ -282,7 +303,7 @@ def run_moe(args, torch, w4, wl, synth):
     ms_step = ms_total / n_steps
     us_token = ms_step * 1e3 / T
     step_bytes = moe_bytes(shape, d_mean)
-    sb = stage_bytes(shape, d_mean)
+    sb = stage_bytes(shape, d_mean, n_stages)
     dom = max(stage_us, key=stage_us.get)
     achieved = sb[dom] / (stage_us[dom] * 1e-6) / 1e9
     traffic = load_traffic(dom, shape.name)

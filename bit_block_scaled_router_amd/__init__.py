@@ -206,11 +206,18 @@ def moe_w4a16_forward(layer, x, y=None, topk_ids=None, topk_w=None, ws=None, str
     return y
 
 
+def moe_w4a16_stage_count(layer, T):
+    n = lib().moe_w4a16_stage_count(C.byref(layer.desc), T)
+    if n == 0:
+        check(W4_ERR_INVALID_ARG)
+    return n
+
+
 def moe_w4a16_forward_timed(layer, x, y, ws, events, topk_ids=None, topk_w=None, stream=None):
-    """moe_w4a16_forward with start/stop events per kernel (6 hipEvent_t handles)."""
-    arr = (C.c_void_p * 6)(*events)
+    """moe_w4a16_forward with start/stop events per kernel (2 hipEvent_t per kernel)."""
+    arr = (C.c_void_p * len(events))(*events)
     check(lib().moe_w4a16_forward_timed(C.byref(layer.desc), _ptr(x), x.shape[0], _ptr(y), _ptr(topk_ids),
-                                        _ptr(topk_w), _ptr(ws), ws.numel(), _stream(stream), arr))
+                                        _ptr(topk_w), _ptr(ws), ws.numel(), _stream(stream), arr, len(events)))
     return y
 
 

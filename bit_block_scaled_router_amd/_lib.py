@@ -31,7 +31,8 @@ EXPORTS = (
     "w4_codes_bytes", "w4_scales_bytes", "w4_quantize",
     "w4_pack_nibbles", "w4_unpack_nibbles",
     "w4a16_gemv", "w4_dequant_device",
-    "moe_w4a16_workspace_bytes", "moe_w4a16_forward", "moe_w4a16_forward_timed", "moe_w4a16_experts",
+    "moe_w4a16_workspace_bytes", "moe_w4a16_forward", "moe_w4a16_forward_timed", "moe_w4a16_stage_count",
+    "moe_w4a16_experts",
 )
 
 
@@ -101,7 +102,8 @@ def lib():
             "w4_dequant_device": (C.c_int, [C.POINTER(W4Matrix), P, P]),
             "moe_w4a16_workspace_bytes": (SZ, [C.POINTER(MoELayerDesc), I64]),
             "moe_w4a16_forward": (C.c_int, [C.POINTER(MoELayerDesc), P, I64, P, P, P, P, SZ, P]),
-            "moe_w4a16_forward_timed": (C.c_int, [C.POINTER(MoELayerDesc), P, I64, P, P, P, P, SZ, P, P]),
+            "moe_w4a16_forward_timed": (C.c_int, [C.POINTER(MoELayerDesc), P, I64, P, P, P, P, SZ, P, P, I32]),
+            "moe_w4a16_stage_count": (C.c_int, [C.POINTER(MoELayerDesc), I64]),
             "moe_w4a16_experts": (C.c_int, [C.POINTER(MoELayerDesc), P, I64, P, P, P, P, SZ, P]),
         }
         for name, (res, args) in sig.items():

@@ -14,7 +14,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libw4moe.so")
-SOURCES = ["w4moe_kernels.hip", "w4moe_host.cpp"]
+SOURCES = ["w4moe_kernels.hip", "w4moe_grouped.hip", "w4moe_host.cpp"]
 ARCH = "gfx950"
 
 

@@ -315,4 +315,115 @@ __device__ __forceinline__ int scales_per_row(int k) {
     return FMT == FMT_E2M1 ? (k >> 4) : (k >> 7);
 }
 
+// ---------------------------------------------------------------- top-k
+
+// Order-preserving map of a finite float to uint32 (larger float -> larger key;
+// every finite value maps above 0, which marks a removed entry).
+__device__ __forceinline__ uint32_t order_key(float f) {
+    const uint32_t u = __float_as_uint(f);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// One wave ranks E <= 64*PL logits (+ bias) by descending value, ties to the
+// lower expert id, for `rounds` rounds.  Ranking by logit equals ranking by
+// softmax probability (exp is increasing).  Lane l holds experts l*PL ..
+// l*PL+PL-1, so "lowest lane, then lowest slot" is the lowest id.  A round
+// takes each lane's best remaining entry (first index on equal keys), the
+// wave maximum of those and the lowest lane holding it; that lane removes the
+// entry.  Lane j < rounds receives the j-th id and its (biased) logit; the id
+// of round `want` is returned to every lane.
+template <int PL>
+__device__ __forceinline__ int wave_topk(const float *__restrict__ lg, const float *__restrict__ bias, int E,
+                                         int rounds, int want, int &my_id, float &my_val) {
+    const int lane = threadIdx.x & 63;
+    const Buf lb = make_buf(lg, (uint32_t)E * 4u);
+    const Buf bb = make_buf(bias, bias ? (uint32_t)E * 4u : 0u);
+    uint32_t key[PL];
+#pragma unroll
+    for (int i = 0; i < PL; ++i) {
+        const int e = lane * PL + i;
+        const uint32_t off = e < E ? (uint32_t)e * 4u : OOB;
+        const float v = __uint_as_float(ld32(lb, off)) + __uint_as_float(ld32(bb, off));
+        key[i] = e < E ? order_key(v) : 0u;
+    }
+    int sel = 0;
+    my_id = -1;
+    my_val = 0.f;
+    for (int j = 0; j < rounds; ++j) {
+        uint32_t best = key[0];
+        int bi = 0;
+#pragma unroll
+        for (int i = 1; i < PL; ++i) {
+            const bool gt = key[i] > best;
+            best = gt ? key[i] : best;
+            bi = gt ? i : bi;
+        }
+        const uint32_t m = wave_max_u32(best);
+        const uint64_t mask = __ballot(best == m);
+        const int winner = __ffsll((unsigned long long)mask) - 1;
+        const int wid = __builtin_amdgcn_readlane(lane * PL + bi, winner);
+        const bool pop = lane == winner;
+#pragma unroll
+        for (int i = 0; i < PL; ++i) key[i] = (pop && i == bi) ? 0u : key[i];
+        const bool mine = lane == j;
+        my_id = mine ? wid : my_id;
+        my_val = mine ? __uint_as_float((m & 0x80000000u) ? (m & 0x7FFFFFFFu) : ~m) : my_val;
+        sel = j == want ? wid : sel;
+    }
+    return sel;
+}
+
+// ---------------------------------------------------------------- MFMA helpers
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// D += A(16x32) B(32x16), bf16 in, fp32 accumulate.  Lane i holds
+// A[i%16][8(i/16)..+8], B[8(i/16)..+8][i%16] and D[4(i/16)+j][i%16], j < 4.
+__device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// Two floats whose values are exact in bf16 -> packed bf16x2 (upper halves).
+__device__ __forceinline__ uint32_t pack_bf16_exact(float a, float b) {
+    return __builtin_amdgcn_perm(__float_as_uint(b), __float_as_uint(a), 0x07060302u);
+}
+
+// Exact two-term split of an FP16 scale s (held in fp32): s_hi keeps the top 6
+// significant bits, s_lo = s - s_hi has at most 5.  An E2M1 value has at most 2
+// significant bits, so code*s_hi (<= 8 bits) and code*s_lo (<= 7 bits) are both
+// exact in bf16 and code*s = code*s_hi + code*s_lo exactly.
+__device__ __forceinline__ void split_scale(float s, float &s_hi, float &s_lo) {
+    s_hi = __uint_as_float(__float_as_uint(s) & 0xFFFC0000u);
+    s_lo = s - s_hi;
+}
+
+// 8 E2M1 codes of one dword (elements 0..7) times a split scale -> bf16x8 hi/lo.
+__device__ __forceinline__ void e2m1x8_split(uint32_t c, float s_hi, float s_lo, bf16x8 &hi, bf16x8 &lo) {
+    uint32_t h[4], l[4];
+    f32x2 v;
+    v = e2m1x2_f32<0>(c); h[0] = pack_bf16_exact(v.x * s_hi, v.y * s_hi); l[0] = pack_bf16_exact(v.x * s_lo, v.y * s_lo);
+    v = e2m1x2_f32<1>(c); h[1] = pack_bf16_exact(v.x * s_hi, v.y * s_hi); l[1] = pack_bf16_exact(v.x * s_lo, v.y * s_lo);
+    v = e2m1x2_f32<2>(c); h[2] = pack_bf16_exact(v.x * s_hi, v.y * s_hi); l[2] = pack_bf16_exact(v.x * s_lo, v.y * s_lo);
+    v = e2m1x2_f32<3>(c); h[3] = pack_bf16_exact(v.x * s_hi, v.y * s_hi); l[3] = pack_bf16_exact(v.x * s_lo, v.y * s_lo);
+    hi = __builtin_bit_cast(bf16x8, make_uint4(h[0], h[1], h[2], h[3]));
+    lo = __builtin_bit_cast(bf16x8, make_uint4(l[0], l[1], l[2], l[3]));
+}
+
+// 8 fp32 activations -> bf16 hi (truncated) + lo (residual rounded to nearest);
+// hi + lo carries about 16 significant bits.
+__device__ __forceinline__ void f32x8_split(float4 a, float4 b, bf16x8 &hi, bf16x8 &lo) {
+    const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+    uint32_t h[4], l[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float h0 = __uint_as_float(__float_as_uint(v[2 * i]) & 0xFFFF0000u);
+        const float h1 = __uint_as_float(__float_as_uint(v[2 * i + 1]) & 0xFFFF0000u);
+        h[i] = pack_bf16_exact(h0, h1);
+        l[i] = (uint32_t)f32_to_bf16_rne(v[2 * i] - h0) | ((uint32_t)f32_to_bf16_rne(v[2 * i + 1] - h1) << 16);
+    }
+    hi = __builtin_bit_cast(bf16x8, make_uint4(h[0], h[1], h[2], h[3]));
+    lo = __builtin_bit_cast(bf16x8, make_uint4(l[0], l[1], l[2], l[3]));
+}
+
 }  // namespace w4k

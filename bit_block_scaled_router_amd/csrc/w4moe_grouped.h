@@ -1,0 +1,69 @@
+// Arguments and launchers of the batched-decode (expert-grouped) MoE kernels,
+// shared by the entry points in w4moe_kernels.hip and their definitions in
+// w4moe_grouped.hip.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace w4k {
+
+// Group table layout in the workspace: grp[0] = number of routed groups n,
+// grp[1 + g] = expert, grp[1 + Gmax + g] = first pair-list entry,
+// grp[1 + 2*Gmax + g] = pair count (g < n).  pairs[0 .. P) holds the routed
+// pair ids p = t*k + j grouped by expert; pairs[P + t] = P + t are the shared
+// expert's rows.
+struct GroupArgs {
+    const float *logits;   // [T][lstride] router logits (routed mode)
+    const float *bias;     // [E] or null
+    const int32_t *ids_in; // [T][k] caller routing (supplied mode)
+    int32_t *ids_ws;       // [T][k] routing ids and weights for the combine
+    float *w_ws;
+    int32_t *ids_user;     // optional caller copies
+    float *w_user;
+    int32_t *grp;
+    int32_t *pairs;
+    int E, K, T, P, Gmax, lstride, route;
+};
+
+struct GW13Args {
+    const uint8_t *codes;   // routed W13 [E][2I][H/2]
+    const uint16_t *scales;
+    const uint8_t *s_codes; // shared W13 [2I][H/2] or null
+    const uint16_t *s_scales;
+    const uint16_t *x;      // [T][H]
+    const int32_t *grp;
+    const int32_t *pairs;
+    float *h;               // [P + T][I]
+    int H, I, K, T, P, Gmax, tiles, mfma_min;
+};
+
+struct GW2Args {
+    const uint8_t *codes;   // routed W2 [E][H][I/2]
+    const uint16_t *scales;
+    const uint8_t *s_codes; // shared W2 [H][I/2] or null
+    const uint16_t *s_scales;
+    const int32_t *grp;
+    const int32_t *pairs;
+    const float *h;         // [P + T][I]
+    float *out;             // [P + T][H]
+    int H, I, K, T, P, Gmax, tiles, mfma_min;
+};
+
+struct GCombineArgs {
+    const int32_t *ids;     // [T][k]
+    const float *w;         // [T][k]
+    const float *logits;    // [T][lstride], column E = shared-gate logit
+    const float *out;       // [P + T][H]
+    uint16_t *y;            // [T][H] bf16
+    int H, E, K, T, P, lstride, has_shared;
+};
+
+size_t grouped_lds_bytes(int E, int P);
+void launch_route_group(GroupArgs &a, hipStream_t st, hipEvent_t e0, hipEvent_t e1);
+void launch_gw13(GW13Args &a, hipStream_t st, hipEvent_t e0, hipEvent_t e1);
+void launch_gw2(GW2Args &a, hipStream_t st, hipEvent_t e0, hipEvent_t e1);
+void launch_gcombine(GCombineArgs &a, hipStream_t st, hipEvent_t e0, hipEvent_t e1);
+
+}  // namespace w4k

@@ -1,0 +1,501 @@
+// Batched-decode path of the MoE layer (T tokens at once): the (token, slot)
+// pairs are grouped by expert so that each active expert's weights are read
+// once per step, and groups of at least W4_MFMA_MIN tokens run on MFMA.
+//
+//   k_moe_route_group  one block: top-k + routing weights per token (as in the
+//                      single-token path), then a counting sort of the pairs by
+//                      expert; writes the group table and the pair lists.
+//   k_moe_gw13         per (group, 16-row tile): gate/up rows of the group's
+//                      expert against the group's token activations, SiLU*up
+//                      -> h[pair] (fp32).  MFMA for big groups (K split over the
+//                      block's waves, fixed-order LDS sum), VALU otherwise.
+//   k_moe_gw2          per (group, 64-row tile): down projection of the group's
+//                      h rows -> out[pair][row] (fp32, unscaled).
+//   k_moe_gcombine     y[t] = sum_j w[t][j] out[t*k+j] + sigma_t out[shared t],
+//                      slots in order, one rounding to bf16.
+//
+// MFMA operands: the per-16 FP16 scale cannot be folded into a coarser
+// hardware block scale without losing accuracy (lynn-engine README, status
+// notes P18/P52), so each dequantised weight code*s is split exactly into two
+// bf16 terms (split_scale) and both are multiplied by the bf16 activations;
+// fp32 activations of the down projection are split into bf16 hi + lo.
+// Placement of pairs inside a group does not affect any result: every MFMA
+// column and every VALU token is computed independently, and the combine reads
+// pairs by (token, slot).
+// Sources: lynn-engine README, R5 notes (tokens_per_expert grouping, inverse
+// scatter to [T, top_k, N]); status notes P85-P92 (per-16 scale applied
+// exactly, split-16); "Lynn Engine" article, "2. MoE 优化" (grouped kernel).
+#include "w4moe_device.h"
+#include "w4moe_grouped.h"
+
+#include <hip/hip_ext.h>
+#include <hip/hip_runtime.h>
+
+namespace w4k {
+
+// ================================================================= route + group
+
+template <int PL>
+__global__ __launch_bounds__(1024) void k_moe_route_group(GroupArgs a) {
+    extern __shared__ int g_lds[];
+    const int E = a.E, K = a.K, T = a.T, P = a.P;
+    int *cnt = g_lds;        // [E]
+    int *off = cnt + E;      // [E]
+    int *e_of = off + E;     // [P]
+    int *pos = e_of + P;     // [P]
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6), nw = blockDim.x >> 6;
+    for (int i = tid; i < E; i += blockDim.x) cnt[i] = 0;
+
+    if (a.route) {
+        for (int t = wv; t < T; t += nw) {
+            int my_id;
+            float my_val;
+            wave_topk<PL>(a.logits + (size_t)t * a.lstride, a.bias, E, K, 0, my_id, my_val);
+            const float vmax = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_val), 0));
+            const float ex = lane < K ? expf(my_val - vmax) : 0.f;
+            const float sum = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(group_sum<64>(ex)), 63));
+            if (lane < K) {
+                const float w = ex / sum;
+                a.ids_ws[t * K + lane] = my_id;
+                a.w_ws[t * K + lane] = w;
+                if (a.ids_user) a.ids_user[t * K + lane] = my_id;
+                if (a.w_user) a.w_user[t * K + lane] = w;
+                e_of[t * K + lane] = my_id;
+            }
+        }
+    } else {
+        for (int p = tid; p < P; p += blockDim.x) {
+            const int e = a.ids_in[p];
+            e_of[p] = (e >= 0 && e < E) ? e : -1;  // invalid ids join no group
+        }
+    }
+    __syncthreads();
+    // position of each pair inside its expert's group (LDS atomics: the order
+    // inside a group is free, see the file header)
+    for (int p = tid; p < P; p += blockDim.x) {
+        const int e = e_of[p];
+        pos[p] = e >= 0 ? atomicAdd(&cnt[e], 1) : -1;
+    }
+    __syncthreads();
+    // exclusive scans over the experts: group offsets and group indices
+    if (wv == 0) {
+        int run = 0, grun = 0;
+        for (int base = 0; base < E; base += 64) {
+            const int e = base + lane;
+            const int c = e < E ? cnt[e] : 0;
+            const int nz = c > 0 ? 1 : 0;
+            int inc = c, ginc = nz;
+#pragma unroll
+            for (int d = 1; d < 64; d <<= 1) {
+                const int u = __shfl_up(inc, d), gu = __shfl_up(ginc, d);
+                if (lane >= d) inc += u, ginc += gu;
+            }
+            const int ex = run + inc - c, gex = grun + ginc - nz;
+            if (e < E) off[e] = ex;
+            if (nz) {
+                a.grp[1 + gex] = e;
+                a.grp[1 + a.Gmax + gex] = ex;
+                a.grp[1 + 2 * a.Gmax + gex] = c;
+            }
+            run += __shfl(inc, 63);
+            grun += __shfl(ginc, 63);
+        }
+        if (lane == 0) a.grp[0] = grun;
+    }
+    __syncthreads();
+    for (int p = tid; p < P; p += blockDim.x) {
+        const int e = e_of[p];
+        if (e >= 0) a.pairs[off[e] + pos[p]] = p;
+    }
+    for (int t = tid; t < T; t += blockDim.x) a.pairs[P + t] = P + t;
+}
+
+// Which expert and which pairs a block works on.  Group index Gmax is the
+// shared expert with pairs P .. P+T-1 (one per token).
+struct GroupView {
+    const uint8_t *codes;
+    const uint16_t *scales;
+    int off, m;  // first entry in the pair list, number of pairs
+    bool live;
+};
+
+__device__ __forceinline__ GroupView group_view(const int32_t *grp, int g, int Gmax, int P, int T, const uint8_t *codes,
+                                                const uint16_t *scales, size_t mat_codes, size_t mat_scales,
+                                                const uint8_t *s_codes, const uint16_t *s_scales) {
+    GroupView v{};
+    if (g == Gmax) {
+        v.live = s_codes != nullptr;
+        v.codes = s_codes, v.scales = s_scales, v.off = P, v.m = T;
+        return v;
+    }
+    const int n = ld_uniform(grp, 0);
+    v.live = g < n;
+    if (!v.live) return v;
+    const int e = ld_uniform(grp, 1 + g);
+    v.off = ld_uniform(grp, 1 + Gmax + g);
+    v.m = ld_uniform(grp, 1 + 2 * Gmax + g);
+    v.codes = codes + (size_t)e * mat_codes;
+    v.scales = scales + (size_t)e * mat_scales;
+    return v;
+}
+
+__device__ __forceinline__ int token_of(int p, int P, int K) { return p < P ? p / K : p - P; }
+
+// ================================================================= grouped W13 + SiLU
+
+template <int L>
+__global__ __launch_bounds__(256) void k_moe_gw13(GW13Args a) {
+    constexpr int RG = 64 / L;
+    __shared__ float red[3][16][64];  // MFMA K-split partials of waves 1..3
+    const int lane = threadIdx.x & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int g = blockIdx.x / a.tiles, tile = blockIdx.x - (blockIdx.x / a.tiles) * a.tiles;
+    const int H = a.H, I = a.I;
+    const uint32_t spr = (uint32_t)(H >> 4);
+    const size_t mat_codes = (size_t)(2 * I) * (H >> 1), mat_scales = (size_t)(2 * I) * spr;
+    const GroupView gv = group_view(a.grp, g, a.Gmax, a.P, a.T, a.codes, a.scales, mat_codes, mat_scales, a.s_codes,
+                                    a.s_scales);
+    if (!gv.live) return;  // uniform per block
+    const Buf cb = make_buf(gv.codes, (uint32_t)mat_codes);
+    const Buf sb = make_buf(gv.scales, (uint32_t)(mat_scales * 2));
+    const int i0 = tile * 16;  // first gate row of the tile
+    const int *plist = a.pairs + gv.off;
+
+    if (gv.m >= a.mfma_min) {
+        // ---- MFMA: 16 gate + 16 up rows x 16-token column tiles; the 128-wide K
+        // chunks are dealt round-robin to the 4 waves and summed in wave order.
+        const int r = lane & 15, q = lane >> 4;
+        const bool rg_ok = i0 + r < I;
+        const uint32_t rowg = (uint32_t)(i0 + r), rowu = (uint32_t)(I + i0 + r);
+        const int nchunks = H >> 7;
+        const Buf xall = make_buf(a.x, (uint32_t)a.T * (uint32_t)H * 2u);
+        for (int n0 = 0; n0 < gv.m; n0 += 32) {
+            // two 16-column tiles: pairs n0 + lane%16 and n0 + 16 + lane%16
+            int pr[2], tk[2];
+            bool pv[2];
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt) {
+                const int idx = n0 + nt * 16 + r;
+                pv[nt] = idx < gv.m;
+                pr[nt] = pv[nt] ? plist[idx] : 0;
+                tk[nt] = token_of(pr[nt], a.P, a.K);
+            }
+            f32x4 ag[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+            f32x4 au[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+            for (int c = wv; c < nchunks; c += 4) {
+                const int k0 = c * 128 + 32 * q;  // this lane's 32 elements
+                // B: 32 activations of each column token
+                uint4 xb[2][4];
+#pragma unroll
+                for (int nt = 0; nt < 2; ++nt) {
+                    const uint32_t xo = (uint32_t)(tk[nt] * H + k0) * 2u;
+#pragma unroll
+                    for (int s = 0; s < 4; ++s) xb[nt][s] = ld128(xall, pv[nt] ? xo + 16u * s : OOB);
+                }
+                const uint4 cg = ld128(cb, rg_ok ? rowg * (uint32_t)(H >> 1) + (uint32_t)(k0 >> 1) : OOB);
+                const uint4 cu = ld128(cb, rg_ok ? rowu * (uint32_t)(H >> 1) + (uint32_t)(k0 >> 1) : OOB);
+                const uint32_t sg = ld32(sb, rg_ok ? (rowg * spr + (uint32_t)(k0 >> 4)) * 2u : OOB);
+                const uint32_t su = ld32(sb, rg_ok ? (rowu * spr + (uint32_t)(k0 >> 4)) * 2u : OOB);
+                const uint32_t cgw[4] = {cg.x, cg.y, cg.z, cg.w}, cuw[4] = {cu.x, cu.y, cu.z, cu.w};
+#pragma unroll
+                for (int s = 0; s < 4; ++s) {
+                    float gh, gl, uh, ul;
+                    split_scale(f16_bits_to_f32(s < 2 ? sg : (sg >> 16)), gh, gl);
+                    split_scale(f16_bits_to_f32(s < 2 ? su : (su >> 16)), uh, ul);
+                    bf16x8 agh, agl, auh, aul;
+                    e2m1x8_split(cgw[s], gh, gl, agh, agl);
+                    e2m1x8_split(cuw[s], uh, ul, auh, aul);
+#pragma unroll
+                    for (int nt = 0; nt < 2; ++nt) {
+                        const bf16x8 b = __builtin_bit_cast(bf16x8, xb[nt][s]);
+                        ag[nt] = mfma16x16x32(agh, b, ag[nt]);
+                        ag[nt] = mfma16x16x32(agl, b, ag[nt]);
+                        au[nt] = mfma16x16x32(auh, b, au[nt]);
+                        au[nt] = mfma16x16x32(aul, b, au[nt]);
+                    }
+                }
+            }
+            // fixed-order sum of the four K partials
+            if (wv > 0) {
+#pragma unroll
+                for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        red[wv - 1][nt * 8 + j][lane] = ag[nt][j];
+                        red[wv - 1][nt * 8 + 4 + j][lane] = au[nt][j];
+                    }
+            }
+            __syncthreads();
+            if (wv == 0) {
+#pragma unroll
+                for (int w = 0; w < 3; ++w)
+#pragma unroll
+                    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) {
+                            ag[nt][j] += red[w][nt * 8 + j][lane];
+                            au[nt][j] += red[w][nt * 8 + 4 + j][lane];
+                        }
+                // lane holds rows i0 + 4q + j of column r
+#pragma unroll
+                for (int nt = 0; nt < 2; ++nt) {
+                    const int idx = n0 + nt * 16 + r;
+                    if (idx < gv.m) {
+                        const int p = plist[idx];
+                        float hv[4];
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) {
+                            const float gg = ag[nt][j], uu = au[nt][j];
+                            hv[j] = (gg / (1.f + expf(-gg))) * uu;
+                        }
+                        float *hp = a.h + (size_t)p * I + i0 + 4 * q;
+                        if (i0 + 4 * q + 3 < I) {
+                            *reinterpret_cast<float4 *>(hp) = make_float4(hv[0], hv[1], hv[2], hv[3]);
+                        } else {
+#pragma unroll
+                            for (int j = 0; j < 4; ++j)
+                                if (i0 + 4 * q + j < I) hp[j] = hv[j];
+                        }
+                    }
+                }
+            }
+            __syncthreads();
+        }
+        return;
+    }
+
+    // ---- VALU: wave wv owns gate rows i0 + 4wv .. +4 (and the matching up rows)
+    // and walks the group's tokens; weights are loaded once per step.
+    constexpr int NLG = RG >= 4 ? 1 : 4 / RG;  // load groups per wave
+    const int lk = lane % L, rsub = lane / L;
+    const int ks = (H + 32 * L - 1) / (32 * L);
+    // one step at a time keeps the register count bounded for any H
+    float accg[NLG], accu[NLG];
+    for (int idx = 0; idx < gv.m; ++idx) {
+        const int p = ld_uniform(plist, idx);
+        const int t = token_of(p, a.P, a.K);
+        const Buf xb = make_buf(a.x + (size_t)t * H, (uint32_t)H * 2u);
+#pragma unroll
+        for (int l = 0; l < NLG; ++l) accg[l] = accu[l] = 0.f;
+        for (int s = 0; s < ks; ++s) {
+            const int k0 = 32 * (L * s + lk);
+            const bool kv = k0 < H;
+            XSlice<FMT_E2M1> xs;
+            load_xslice<FMT_E2M1>(xs, xb, kv ? (uint32_t)k0 * 2u : OOB);
+#pragma unroll
+            for (int l = 0; l < NLG; ++l) {
+                const int i = i0 + 4 * wv + l * RG + rsub;
+                const bool v = kv && i < I && (l * RG + rsub) < 4;
+                const uint32_t rg = (uint32_t)i, ru = (uint32_t)(I + i);
+                const uint4 cg = ld128(cb, v ? rg * (uint32_t)(H >> 1) + (uint32_t)(k0 >> 1) : OOB);
+                const uint4 cu = ld128(cb, v ? ru * (uint32_t)(H >> 1) + (uint32_t)(k0 >> 1) : OOB);
+                const uint32_t sg = ld32(sb, v ? (rg * spr + (uint32_t)(k0 >> 4)) * 2u : OOB);
+                const uint32_t su = ld32(sb, v ? (ru * spr + (uint32_t)(k0 >> 4)) * 2u : OOB);
+                accg[l] = chunk_dot_bf16<FMT_E2M1>(cg, sg, xs, accg[l]);
+                accu[l] = chunk_dot_bf16<FMT_E2M1>(cu, su, xs, accu[l]);
+            }
+        }
+#pragma unroll
+        for (int l = 0; l < NLG; ++l) {
+            const float gg = group_sum<L>(accg[l]);
+            const float uu = group_sum<L>(accu[l]);
+            const int i = i0 + 4 * wv + l * RG + rsub;
+            if (group_leader<L>(lane) && i < I && (l * RG + rsub) < 4)
+                a.h[(size_t)p * I + i] = (gg / (1.f + expf(-gg))) * uu;
+        }
+    }
+}
+
+// ================================================================= grouped W2
+
+template <int L>
+__global__ __launch_bounds__(256) void k_moe_gw2(GW2Args a) {
+    constexpr int RG = 64 / L;
+    const int lane = threadIdx.x & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int g = blockIdx.x / a.tiles, tile = blockIdx.x - (blockIdx.x / a.tiles) * a.tiles;
+    const int H = a.H, I = a.I;
+    const uint32_t spr = (uint32_t)(I >> 4);
+    const size_t mat_codes = (size_t)H * (I >> 1), mat_scales = (size_t)H * spr;
+    const GroupView gv = group_view(a.grp, g, a.Gmax, a.P, a.T, a.codes, a.scales, mat_codes, mat_scales, a.s_codes,
+                                    a.s_scales);
+    if (!gv.live) return;
+    const Buf cb = make_buf(gv.codes, (uint32_t)mat_codes);
+    const Buf sb = make_buf(gv.scales, (uint32_t)(mat_scales * 2));
+    const int row0 = tile * 64 + 16 * wv;  // this wave's 16 output rows
+    const int *plist = a.pairs + gv.off;
+
+    if (gv.m >= a.mfma_min) {
+        // ---- MFMA: 16 rows x 16-column tiles, K = I in 128-wide chunks
+        const int r = lane & 15, q = lane >> 4;
+        const bool rv = row0 + r < H;
+        const uint32_t row = (uint32_t)(row0 + r);
+        const int nchunks = I >> 7;
+        const Buf hall = make_buf(a.h, (uint32_t)(a.P + a.T) * (uint32_t)I * 4u);
+        for (int n0 = 0; n0 < gv.m; n0 += 16) {
+            const int idx = n0 + r;
+            const bool pv = idx < gv.m;
+            const int p = pv ? plist[idx] : 0;
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            for (int c = 0; c < nchunks; ++c) {
+                const int k0 = c * 128 + 32 * q;
+                const uint32_t ho = (uint32_t)(p * I + k0) * 4u;
+                float4 hv[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) hv[i] = __builtin_bit_cast(float4, ld128(hall, pv ? ho + 16u * i : OOB));
+                const uint4 cw = ld128(cb, rv ? row * (uint32_t)(I >> 1) + (uint32_t)(k0 >> 1) : OOB);
+                const uint32_t sc = ld32(sb, rv ? (row * spr + (uint32_t)(k0 >> 4)) * 2u : OOB);
+                const uint32_t cws[4] = {cw.x, cw.y, cw.z, cw.w};
+#pragma unroll
+                for (int s = 0; s < 4; ++s) {
+                    float sh, sl;
+                    split_scale(f16_bits_to_f32(s < 2 ? sc : (sc >> 16)), sh, sl);
+                    bf16x8 ah, al, bh, bl;
+                    e2m1x8_split(cws[s], sh, sl, ah, al);
+                    f32x8_split(hv[2 * s], hv[2 * s + 1], bh, bl);
+                    acc = mfma16x16x32(ah, bh, acc);
+                    acc = mfma16x16x32(ah, bl, acc);
+                    acc = mfma16x16x32(al, bh, acc);
+                    acc = mfma16x16x32(al, bl, acc);
+                }
+            }
+            // lane holds rows row0 + 4q + j of column r
+            if (pv) {
+                float *op = a.out + (size_t)p * H + row0 + 4 * q;
+                if (row0 + 4 * q + 3 < H) {
+                    *reinterpret_cast<float4 *>(op) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+                } else {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        if (row0 + 4 * q + j < H) op[j] = acc[j];
+                }
+            }
+        }
+        return;
+    }
+
+    // ---- VALU: 16 rows per wave in load groups of 64/L rows, tokens in turn
+    constexpr int NLG = RG >= 16 ? 1 : 16 / RG;
+    const int lk = lane % L, rsub = lane / L;
+    const int ks = (I + 32 * L - 1) / (32 * L);
+    float acc[NLG];
+    for (int idx = 0; idx < gv.m; ++idx) {
+        const int p = ld_uniform(plist, idx);
+        const Buf hb = make_buf(a.h + (size_t)p * I, (uint32_t)I * 4u);
+#pragma unroll
+        for (int l = 0; l < NLG; ++l) acc[l] = 0.f;
+        for (int s = 0; s < ks; ++s) {
+            const int k0 = 32 * (L * s + lk);
+            const bool kv = k0 < I;
+            float4 hv[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) hv[i] = __builtin_bit_cast(float4, ld128(hb, kv ? (uint32_t)(k0 + 4 * i) * 4u : OOB));
+            float hs = 0.f;
+#pragma unroll
+            for (int l = 0; l < NLG; ++l) {
+                const int rr = row0 + l * RG + rsub;
+                const bool v = kv && rr < H && (l * RG + rsub) < 16;
+                const uint4 cw = ld128(cb, v ? (uint32_t)rr * (uint32_t)(I >> 1) + (uint32_t)(k0 >> 1) : OOB);
+                const uint32_t sc = ld32(sb, v ? ((uint32_t)rr * spr + (uint32_t)(k0 >> 4)) * 2u : OOB);
+                acc[l] = chunk_dot_f32<FMT_E2M1>(cw, sc, hv, hs, acc[l]);
+            }
+        }
+#pragma unroll
+        for (int l = 0; l < NLG; ++l) {
+            const float v = group_sum<L>(acc[l]);
+            const int rr = row0 + l * RG + rsub;
+            if (group_leader<L>(lane) && rr < H && (l * RG + rsub) < 16) a.out[(size_t)p * H + rr] = v;
+        }
+    }
+}
+
+// ================================================================= combine
+
+__global__ __launch_bounds__(256) void k_moe_gcombine(GCombineArgs a) {
+    const int t = blockIdx.y;
+    const int n = blockIdx.x * blockDim.x + threadIdx.x;
+    if (n >= a.H) return;
+    float v = 0.f;
+    for (int j = 0; j < a.K; ++j) {
+        const int p = t * a.K + j;
+        const int e = ld_uniform(a.ids, p);
+        const float w = ld_uniform(a.w, p);
+        v += (e >= 0 && e < a.E) ? w * a.out[(size_t)p * a.H + n] : __builtin_nanf("");
+    }
+    if (a.has_shared) {
+        const float sig = 1.f / (1.f + expf(-ld_uniform(a.logits, t * a.lstride + a.E)));
+        v += sig * a.out[(size_t)(a.P + t) * a.H + n];
+    }
+    a.y[(size_t)t * a.H + n] = f32_to_bf16_rne(v);
+}
+
+}  // namespace w4k
+
+// ================================================================= launchers
+
+namespace w4k {
+
+namespace {
+int lanes_for_k(int k) {
+    int need = (k + 31) / 32, L = 1;
+    while (L < need && L < 64) L <<= 1;
+    return L;
+}
+
+template <typename F, typename... Args>
+void go_ev(hipStream_t st, hipEvent_t e0, hipEvent_t e1, F kernel, dim3 g, dim3 b, uint32_t shm, Args... args) {
+    if (e0)
+        hipExtLaunchKernelGGL(kernel, g, b, shm, st, e0, e1, 0u, args...);
+    else
+        hipLaunchKernelGGL(kernel, g, b, shm, st, args...);
+}
+}  // namespace
+
+size_t grouped_lds_bytes(int E, int P) { return (size_t)(2 * E + 2 * P) * sizeof(int); }
+
+void launch_route_group(GroupArgs &a, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
+    const int pl = (a.E + 63) / 64;
+    const dim3 g(1), b(1024);
+    const uint32_t shm = (uint32_t)grouped_lds_bytes(a.E, a.P);
+    if (pl <= 1) go_ev(st, e0, e1, k_moe_route_group<1>, g, b, shm, a);
+    else if (pl <= 2) go_ev(st, e0, e1, k_moe_route_group<2>, g, b, shm, a);
+    else if (pl <= 4) go_ev(st, e0, e1, k_moe_route_group<4>, g, b, shm, a);
+    else if (pl <= 8) go_ev(st, e0, e1, k_moe_route_group<8>, g, b, shm, a);
+    else go_ev(st, e0, e1, k_moe_route_group<16>, g, b, shm, a);
+}
+
+void launch_gw13(GW13Args &a, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
+    a.tiles = (a.I + 15) / 16;
+    const dim3 g((unsigned)((a.Gmax + 1) * a.tiles)), b(256);
+    switch (lanes_for_k(a.H)) {
+    case 1: go_ev(st, e0, e1, k_moe_gw13<1>, g, b, 0, a); break;
+    case 2: go_ev(st, e0, e1, k_moe_gw13<2>, g, b, 0, a); break;
+    case 4: go_ev(st, e0, e1, k_moe_gw13<4>, g, b, 0, a); break;
+    case 8: go_ev(st, e0, e1, k_moe_gw13<8>, g, b, 0, a); break;
+    case 16: go_ev(st, e0, e1, k_moe_gw13<16>, g, b, 0, a); break;
+    case 32: go_ev(st, e0, e1, k_moe_gw13<32>, g, b, 0, a); break;
+    default: go_ev(st, e0, e1, k_moe_gw13<64>, g, b, 0, a); break;
+    }
+}
+
+void launch_gw2(GW2Args &a, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
+    a.tiles = (a.H + 63) / 64;
+    const dim3 g((unsigned)((a.Gmax + 1) * a.tiles)), b(256);
+    switch (lanes_for_k(a.I)) {
+    case 1: go_ev(st, e0, e1, k_moe_gw2<1>, g, b, 0, a); break;
+    case 2: go_ev(st, e0, e1, k_moe_gw2<2>, g, b, 0, a); break;
+    case 4: go_ev(st, e0, e1, k_moe_gw2<4>, g, b, 0, a); break;
+    case 8: go_ev(st, e0, e1, k_moe_gw2<8>, g, b, 0, a); break;
+    case 16: go_ev(st, e0, e1, k_moe_gw2<16>, g, b, 0, a); break;
+    case 32: go_ev(st, e0, e1, k_moe_gw2<32>, g, b, 0, a); break;
+    default: go_ev(st, e0, e1, k_moe_gw2<64>, g, b, 0, a); break;
+    }
+}
+
+void launch_gcombine(GCombineArgs &a, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
+    const dim3 g((unsigned)((a.H + 255) / 256), (unsigned)a.T), b(256);
+    go_ev(st, e0, e1, k_moe_gcombine, g, b, 0, a);
+}
+
+}  // namespace w4k

@@ -20,6 +20,7 @@
 // shape), P46/P48 (atomics drift; row-owning down kernel), P55 (gate and up rows
 // processed together); "Lynn Engine" article stage P1 (packed matvec).
 #include "w4moe_device.h"
+#include "w4moe_grouped.h"
 #include "w4moe_internal.h"
 
 #include <hip/hip_ext.h>
@@ -167,64 +168,6 @@ __global__ __launch_bounds__(64) void k_router(const uint16_t *__restrict__ wr, 
         acc = group_sum<64>(acc);
         if (group_leader<64>(lane)) logits[(size_t)t * lstride + r] = acc;
     }
-}
-
-// ================================================================= top-k
-
-// Order-preserving map of a finite float to uint32 (larger float -> larger key;
-// every finite value maps above 0, which marks a removed entry).
-__device__ __forceinline__ uint32_t order_key(float f) {
-    const uint32_t u = __float_as_uint(f);
-    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-
-// One wave ranks E <= 64*PL logits (+ bias) by descending value, ties to the
-// lower expert id, for `rounds` rounds.  Ranking by logit equals ranking by
-// softmax probability (exp is increasing).  Lane l holds experts l*PL ..
-// l*PL+PL-1, so "lowest lane, then lowest slot" is the lowest id.  A round
-// takes each lane's best remaining entry (first index on equal keys), the
-// wave maximum of those and the lowest lane holding it; that lane removes the
-// entry.  Lane j < rounds receives the j-th id and its (biased) logit; the id
-// of round `want` is returned to every lane.
-template <int PL>
-__device__ __forceinline__ int wave_topk(const float *__restrict__ lg, const float *__restrict__ bias, int E,
-                                         int rounds, int want, int &my_id, float &my_val) {
-    const int lane = threadIdx.x & 63;
-    const Buf lb = make_buf(lg, (uint32_t)E * 4u);
-    const Buf bb = make_buf(bias, bias ? (uint32_t)E * 4u : 0u);
-    uint32_t key[PL];
-#pragma unroll
-    for (int i = 0; i < PL; ++i) {
-        const int e = lane * PL + i;
-        const uint32_t off = e < E ? (uint32_t)e * 4u : OOB;
-        const float v = __uint_as_float(ld32(lb, off)) + __uint_as_float(ld32(bb, off));
-        key[i] = e < E ? order_key(v) : 0u;
-    }
-    int sel = 0;
-    my_id = -1;
-    my_val = 0.f;
-    for (int j = 0; j < rounds; ++j) {
-        uint32_t best = key[0];
-        int bi = 0;
-#pragma unroll
-        for (int i = 1; i < PL; ++i) {
-            const bool gt = key[i] > best;
-            best = gt ? key[i] : best;
-            bi = gt ? i : bi;
-        }
-        const uint32_t m = wave_max_u32(best);
-        const uint64_t mask = __ballot(best == m);
-        const int winner = __ffsll((unsigned long long)mask) - 1;
-        const int wid = __builtin_amdgcn_readlane(lane * PL + bi, winner);
-        const bool pop = lane == winner;
-#pragma unroll
-        for (int i = 0; i < PL; ++i) key[i] = (pop && i == bi) ? 0u : key[i];
-        const bool mine = lane == j;
-        my_id = mine ? wid : my_id;
-        my_val = mine ? __uint_as_float((m & 0x80000000u) ? (m & 0x7FFFFFFFu) : ~m) : my_val;
-        sel = j == want ? wid : sel;
-    }
-    return sel;
 }
 
 // ================================================================= MoE W13 + SiLU
@@ -601,10 +544,21 @@ constexpr int MAX_TOPK = 16;
 constexpr int MAX_EXPERTS = 1024;  // 64 lanes x 16 logits per lane
 constexpr int MAX_TOKENS = 4096;
 
+#ifndef W4_GROUPED_MIN_T
+#define W4_GROUPED_MIN_T 4  // batches of at least this many tokens group their pairs by expert
+#endif
+#ifndef W4_MFMA_MIN
+#define W4_MFMA_MIN 16  // expert groups of at least this many rows run on MFMA
+#endif
+constexpr int MAX_GROUPED_PAIRS = 4096;
+
 struct MoEPlan {
     int H, I, E, K, S, T;
     int L13, L2, hstride, lstride;
+    bool grouped;
+    int P, Gmax;
     size_t off_logits, off_ids, off_w, off_h, total;
+    size_t off_grp, off_pairs, off_hp, off_out;
 };
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
@@ -650,11 +604,25 @@ int check_layer(const moe_w4a16_layer *Lr, int64_t T, MoEPlan &p) {
     const int ks2 = (int)((I + 32 * p.L2 - 1) / (32 * p.L2));
     p.hstride = ks2 * 32 * p.L2;
     p.lstride = (int)align_up((size_t)E + 1, 64);
+    // batched decode: group the (token, slot) pairs by expert (E2M1 weights,
+    // 128-wide K chunks for the MFMA tiles)
+    p.P = (int)(T * K);
+    p.Gmax = (int)(E < p.P ? E : p.P);
+    p.grouped = T >= W4_GROUPED_MIN_T && fmt == W4_FMT_E2M1_F16S16 && H % 128 == 0 && I % 128 == 0 &&
+                p.P <= MAX_GROUPED_PAIRS;
     size_t off = 0;
     p.off_logits = off; off = align_up(off + (size_t)T * p.lstride * 4, 256);
     p.off_ids = off;    off = align_up(off + (size_t)T * K * 4, 256);
     p.off_w = off;      off = align_up(off + (size_t)T * K * 4, 256);
-    p.off_h = off;      off = align_up(off + (size_t)T * p.S * p.hstride * 4, 256);
+    if (!p.grouped) {
+        p.off_h = off;  off = align_up(off + (size_t)T * p.S * p.hstride * 4, 256);
+    } else {
+        const size_t rows = (size_t)p.P + (size_t)T;
+        p.off_grp = off;   off = align_up(off + (size_t)(1 + 3 * p.Gmax) * 4, 256);
+        p.off_pairs = off; off = align_up(off + rows * 4, 256);
+        p.off_hp = off;    off = align_up(off + rows * (size_t)I * 4, 256);
+        p.off_out = off;   off = align_up(off + rows * (size_t)H * 4, 256);
+    }
     p.total = off;
     return W4_OK;
 }
@@ -747,9 +715,13 @@ void launch_down(const MoEPlan &p, DownArgs &a, const Launch &st) {
     }
 }
 
+int run_grouped(const moe_w4a16_layer *Lr, const MoEPlan &p, const uint16_t *x, const int32_t *ids_in,
+                const float *w_in, uint16_t *y, int32_t *topk_ids, float *topk_w, char *wsb, hipStream_t sm,
+                void *const *events);
+
 int run_moe(const moe_w4a16_layer *Lr, const uint16_t *x, int64_t T, const int32_t *ids_in, const float *w_in,
             uint16_t *y, int32_t *topk_ids, float *topk_w, void *ws, size_t ws_bytes, void *stream,
-            void *const *events = nullptr) {
+            void *const *events = nullptr, int n_events = 0) {
     MoEPlan p;
     int st = check_layer(Lr, T, p);
     if (st) return st;
@@ -771,9 +743,15 @@ int run_moe(const moe_w4a16_layer *Lr, const uint16_t *x, int64_t T, const int32
     float *w_ws = (float *)(wsb + p.off_w);
     float *h = (float *)(wsb + p.off_h);
 
-    if (events)
-        for (int i = 0; i < 6; ++i)
+    if (events) {
+        const int need = p.grouped ? 10 : 6;
+        if (n_events < need)
+            return fail(W4_ERR_INVALID_ARG, "%s path needs %d events, got %d", p.grouped ? "grouped" : "single-token",
+                        need, n_events);
+        for (int i = 0; i < need; ++i)
             if (!events[i]) return fail(W4_ERR_INVALID_ARG, "null stage event %d", i);
+    }
+    if (p.grouped) return run_grouped(Lr, p, x, ids_in, w_in, y, topk_ids, topk_w, wsb, sm, events);
     Launch l_router{sm}, l_w13{sm}, l_down{sm};
     if (events) {
         l_router.start = (hipEvent_t)events[0], l_router.stop = (hipEvent_t)events[1];
@@ -826,6 +804,64 @@ int run_moe(const moe_w4a16_layer *Lr, const uint16_t *x, int64_t T, const int32
     return hip_status("down launch");
 }
 
+int run_grouped(const moe_w4a16_layer *Lr, const MoEPlan &p, const uint16_t *x, const int32_t *ids_in,
+                const float *w_in, uint16_t *y, int32_t *topk_ids, float *topk_w, char *wsb, hipStream_t sm,
+                void *const *events) {
+    const bool route = ids_in == nullptr;
+    float *logits = (float *)(wsb + p.off_logits);
+    int32_t *ids_ws = (int32_t *)(wsb + p.off_ids);
+    float *w_ws = (float *)(wsb + p.off_w);
+    int32_t *grp = (int32_t *)(wsb + p.off_grp);
+    int32_t *pairs = (int32_t *)(wsb + p.off_pairs);
+    float *hp = (float *)(wsb + p.off_hp);
+    float *outp = (float *)(wsb + p.off_out);
+    auto ev = [&](int i) { return events ? (hipEvent_t)events[i] : (hipEvent_t) nullptr; };
+    int st;
+    (void)hipGetLastError();
+    // 1) router logits (and the shared-gate logit)
+    Launch l_router{sm, ev(0), ev(1)};
+    if (route) st = launch_router(Lr, p, x, logits, 0, p.E + (Lr->has_shared ? 1 : 0), l_router);
+    else if (Lr->has_shared) st = launch_router(Lr, p, x, logits, p.E, p.E + 1, l_router);
+    else st = W4_OK;
+    if (st) return st;
+    if ((st = hip_status("router launch"))) return st;
+    // 2) top-k + grouping
+    GroupArgs ga{};
+    ga.logits = logits, ga.bias = Lr->router_bias, ga.ids_in = ids_in;
+    ga.ids_ws = ids_ws, ga.w_ws = w_ws;
+    ga.ids_user = route ? topk_ids : nullptr, ga.w_user = route ? topk_w : nullptr;
+    ga.grp = grp, ga.pairs = pairs;
+    ga.E = p.E, ga.K = p.K, ga.T = p.T, ga.P = p.P, ga.Gmax = p.Gmax, ga.lstride = p.lstride, ga.route = route ? 1 : 0;
+    launch_route_group(ga, sm, ev(2), ev(3));
+    if ((st = hip_status("route/group launch"))) return st;
+    // 3) grouped W13 + SiLU
+    GW13Args a{};
+    a.codes = Lr->w13.codes, a.scales = Lr->w13.scales;
+    a.s_codes = Lr->has_shared ? Lr->shared_w13.codes : nullptr;
+    a.s_scales = Lr->has_shared ? Lr->shared_w13.scales : nullptr;
+    a.x = x, a.grp = grp, a.pairs = pairs, a.h = hp;
+    a.H = p.H, a.I = p.I, a.K = p.K, a.T = p.T, a.P = p.P, a.Gmax = p.Gmax, a.mfma_min = W4_MFMA_MIN;
+    launch_gw13(a, sm, ev(4), ev(5));
+    if ((st = hip_status("grouped w13 launch"))) return st;
+    // 4) grouped W2
+    GW2Args d{};
+    d.codes = Lr->w2.codes, d.scales = Lr->w2.scales;
+    d.s_codes = Lr->has_shared ? Lr->shared_w2.codes : nullptr;
+    d.s_scales = Lr->has_shared ? Lr->shared_w2.scales : nullptr;
+    d.grp = grp, d.pairs = pairs, d.h = hp, d.out = outp;
+    d.H = p.H, d.I = p.I, d.K = p.K, d.T = p.T, d.P = p.P, d.Gmax = p.Gmax, d.mfma_min = W4_MFMA_MIN;
+    launch_gw2(d, sm, ev(6), ev(7));
+    if ((st = hip_status("grouped w2 launch"))) return st;
+    // 5) ordered combine
+    GCombineArgs c{};
+    c.ids = route ? ids_ws : ids_in;
+    c.w = route ? w_ws : w_in;
+    c.logits = logits, c.out = outp, c.y = y;
+    c.H = p.H, c.E = p.E, c.K = p.K, c.T = p.T, c.P = p.P, c.lstride = p.lstride, c.has_shared = Lr->has_shared;
+    launch_gcombine(c, sm, ev(8), ev(9));
+    return hip_status("combine launch");
+}
+
 }  // namespace
 
 extern "C" {
@@ -872,10 +908,17 @@ int moe_w4a16_forward(const moe_w4a16_layer *L, const uint16_t *x, int64_t T, ui
 }
 
 int moe_w4a16_forward_timed(const moe_w4a16_layer *L, const uint16_t *x, int64_t T, uint16_t *y, int32_t *topk_ids,
-                            float *topk_w, void *ws, size_t ws_bytes, void *stream, void *const *events) {
+                            float *topk_w, void *ws, size_t ws_bytes, void *stream, void *const *events,
+                            int32_t n_events) {
     w4::clear_error();
     if (!events) return fail(W4_ERR_INVALID_ARG, "null events");
-    return run_moe(L, x, T, nullptr, nullptr, y, topk_ids, topk_w, ws, ws_bytes, stream, events);
+    return run_moe(L, x, T, nullptr, nullptr, y, topk_ids, topk_w, ws, ws_bytes, stream, events, n_events);
+}
+
+int moe_w4a16_stage_count(const moe_w4a16_layer *L, int64_t T) {
+    MoEPlan p;
+    if (check_layer(L, T, p) != W4_OK) return 0;
+    return p.grouped ? 5 : 3;
 }
 
 int moe_w4a16_experts(const moe_w4a16_layer *L, const uint16_t *x, int64_t T, const int32_t *ids, const float *w,

@@ -190,17 +190,28 @@ size_t moe_w4a16_workspace_bytes(const moe_w4a16_layer *L, int64_t T);
 int moe_w4a16_forward(const moe_w4a16_layer *L, const uint16_t *x, int64_t T, uint16_t *y,
                       int32_t *topk_ids, float *topk_w, void *ws, size_t ws_bytes, void *stream);
 
-/* Measurement variant of moe_w4a16_forward: identical work, with each of the
- * three kernels launched through hipExtLaunchKernel so that the runtime
- * records the caller's events at the kernel's start and end on `stream`.
- * `events` is an array of six hipEvent_t: start/stop of the router kernel,
- * start/stop of the grouped W13 kernel, start/stop of the down/combine kernel
- * (the router pair is not recorded for a layer whose router is skipped).  Not
- * for use under stream capture.  Errors as moe_w4a16_forward, plus
- * W4_ERR_INVALID_ARG for a null event. */
+/* Measurement variant of moe_w4a16_forward: identical work, with each kernel
+ * launched through hipExtLaunchKernel so that the runtime records the
+ * caller's events at the kernel's start and end on `stream`.  `events` holds
+ * 2 * moe_w4a16_stage_count(L, T) hipEvent_t (start/stop per kernel, in launch
+ * order; n_events gives the array length).  The router pair is not recorded
+ * for a layer whose router is skipped.  Not for use under stream capture.
+ * Errors as moe_w4a16_forward, plus W4_ERR_INVALID_ARG for too few or null
+ * events. */
 int moe_w4a16_forward_timed(const moe_w4a16_layer *L, const uint16_t *x, int64_t T, uint16_t *y,
                             int32_t *topk_ids, float *topk_w, void *ws, size_t ws_bytes, void *stream,
-                            void *const *events);
+                            void *const *events, int32_t n_events);
+
+/* Number of kernels moe_w4a16_forward launches for T tokens (0 on invalid
+ * arguments): 3 for the single-token path (router; grouped W13 + SiLU over
+ * every (token, slot); down + combine), 5 for the batched path (router; top-k
+ * and grouping of the (token, slot) pairs by expert; W13 + SiLU per expert
+ * group, on MFMA for groups of at least 16 tokens; W2 per expert group; ordered
+ * combine).  The batched path serves E2M1 layers with H and I multiples of 128,
+ * T >= 4 and T * top_k <= 4096; other requests take the single-token path.
+ * Sources: lynn-engine README, R5 notes (tokens-per-expert grouping, inverse
+ * scatter) and P85-P92 (per-16 scales applied exactly). */
+int moe_w4a16_stage_count(const moe_w4a16_layer *L, int64_t T);
 
 /* Experts and combine only, with caller-supplied routing (the one-call shape of
  * README P45): ids int32 [T][k] in [0, E), w fp32 [T][k] (used as given).  The

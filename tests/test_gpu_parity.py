@@ -175,6 +175,35 @@ def test_moe_tiny_experts_entry_and_bad_ids(tiny):
     assert np.all(np.isnan(g[1])) and np.all(np.isfinite(g[0])) and np.all(np.isfinite(g[2]))
 
 
+@pytest.mark.parametrize("T", [4, 40, 64])
+def test_moe_tiny_batched_groups(tiny, T):
+    """Batched path: small and MFMA-sized (>= 16 token) expert groups, ragged tiles."""
+    shape, dev_layer, or_layer = tiny
+    assert w4.moe_w4a16_stage_count(dev_layer, T) == 5
+    print(f"moe tiny batched T={T}", flush=True)
+    _check_moe(shape, dev_layer, or_layer, tie_free_tokens(shape, or_layer, T, first=100 + T), f"tiny T={T}")
+
+
+def test_moe_tiny_batched_experts_entry(tiny):
+    shape, dev_layer, or_layer = tiny
+    T = 24
+    xb = tie_free_tokens(shape, or_layer, T, first=300)
+    rng = np.random.default_rng(5)
+    ids = np.stack([rng.choice(shape.num_experts, shape.top_k, replace=False) for _ in range(T)]).astype(np.int32)
+    ids[:20, 0] = 3  # one expert with a group of >= 16 rows (MFMA)
+    ids[:20, 1] = np.where(ids[:20, 1] == 3, 4, ids[:20, 1])
+    w = rng.uniform(0.1, 1.0, size=(T, shape.top_k)).astype(np.float32)
+    y = w4.moe_w4a16_experts(dev_layer, wl.bf16_tensor(xb), torch.from_numpy(ids).to(DEV), torch.from_numpy(w).to(DEV))
+    ref = ops.moe_experts(or_layer, xb, ids, w.astype(np.float64))
+    assert_bf16_close(wl.bf16_bits(y), ref, "batched experts entry")
+    bad = ids.copy()
+    bad[7, 1] = -1
+    y2 = w4.moe_w4a16_experts(dev_layer, wl.bf16_tensor(xb), torch.from_numpy(bad).to(DEV),
+                              torch.from_numpy(w).to(DEV))
+    g = oracle.bf16_bits_to_f64(wl.bf16_bits(y2))
+    assert np.all(np.isnan(g[7])) and np.all(np.isfinite(np.delete(g, 7, axis=0)))
+
+
 def test_moe_tiny_zero_input(tiny):
     shape, dev_layer, _ = tiny
     y = w4.moe_w4a16_forward(dev_layer, torch.zeros((2, shape.hidden), dtype=torch.bfloat16, device=DEV))
@@ -215,7 +244,19 @@ def test_moe_full_batch32_zipf():
     shape = synth.QWEN_MOE_T32
     print("building the batch-32 Zipf layer", flush=True)
     dev_layer = wl.build_moe_layer(shape, device=DEV)
+    assert w4.moe_w4a16_stage_count(dev_layer, shape.tokens) == 5
     or_layer = oracle_layer(shape)
     xb = tie_free_tokens(shape, or_layer, shape.tokens)
+    # the group sizes this batch produces (the oracle's routing): some use MFMA
+    _, rids, _ = ops.moe_forward(or_layer, xb)
+    sizes = np.bincount(rids.ravel(), minlength=shape.num_experts)
+    print("groups", int((sizes > 0).sum()), "of >= 16 rows:", int((sizes >= 16).sum()), "largest", int(sizes.max()),
+          flush=True)
+    assert (sizes >= 16).any()
     rep = _check_moe(shape, dev_layer, or_layer, xb, "batch32")
     print(rep, flush=True)
+    # determinism across runs
+    x = wl.bf16_tensor(xb)
+    y1 = w4.moe_w4a16_forward(dev_layer, x)
+    y2 = w4.moe_w4a16_forward(dev_layer, x)
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
