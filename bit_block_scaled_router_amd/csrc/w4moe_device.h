@@ -410,6 +410,14 @@ __device__ __forceinline__ void e2m1x8_split(uint32_t c, float s_hi, float s_lo,
     lo = __builtin_bit_cast(bf16x8, make_uint4(l[0], l[1], l[2], l[3]));
 }
 
+// One fp32 value -> bf16 hi (truncated) + bf16 lo (residual, rounded to
+// nearest): hi + lo carries about 16 significant bits of v.
+__device__ __forceinline__ void split_bf16(float v, uint16_t &hi, uint16_t &lo) {
+    const float h = __uint_as_float(__float_as_uint(v) & 0xFFFF0000u);
+    hi = (uint16_t)(__float_as_uint(v) >> 16);
+    lo = f32_to_bf16_rne(v - h);
+}
+
 // 8 fp32 activations -> bf16 hi (truncated) + lo (residual rounded to nearest);
 // hi + lo carries about 16 significant bits.
 __device__ __forceinline__ void f32x8_split(float4 a, float4 b, bf16x8 &hi, bf16x8 &lo) {

@@ -35,7 +35,8 @@ struct GW13Args {
     const uint16_t *x;      // [T][H]
     const int32_t *grp;
     const int32_t *pairs;
-    float *h;               // [P + T][I]
+    uint16_t *h_hi;         // [P + T][I] bf16: h = h_hi + h_lo (see split_bf16)
+    uint16_t *h_lo;
     int H, I, K, T, P, Gmax, tiles, mfma_min;
 };
 
@@ -46,7 +47,8 @@ struct GW2Args {
     const uint16_t *s_scales;
     const int32_t *grp;
     const int32_t *pairs;
-    const float *h;         // [P + T][I]
+    const uint16_t *h_hi;   // [P + T][I]
+    const uint16_t *h_lo;
     float *out;             // [P + T][H]
     int H, I, K, T, P, Gmax, tiles, mfma_min;
 };

@@ -7,8 +7,10 @@
 //                      expert; writes the group table and the pair lists.
 //   k_moe_gw13         per (group, 16-row tile): gate/up rows of the group's
 //                      expert against the group's token activations, SiLU*up
-//                      -> h[pair] (fp32).  MFMA for big groups (K split over the
-//                      block's waves, fixed-order LDS sum), VALU otherwise.
+//                      -> h[pair], stored as two bf16 arrays h_hi + h_lo (the
+//                      fp32 value truncated, then its rounded residual).  MFMA
+//                      for big groups (K split over the block's waves,
+//                      fixed-order LDS sum), VALU otherwise.
 //   k_moe_gw2          per (group, 64-row tile): down projection of the group's
 //                      h rows -> out[pair][row] (fp32, unscaled).
 //   k_moe_gcombine     y[t] = sum_j w[t][j] out[t*k+j] + sigma_t out[shared t],
@@ -18,7 +20,7 @@
 // hardware block scale without losing accuracy (lynn-engine README, status
 // notes P18/P52), so each dequantised weight code*s is split exactly into two
 // bf16 terms (split_scale) and both are multiplied by the bf16 activations;
-// fp32 activations of the down projection are split into bf16 hi + lo.
+// the down projection multiplies both weight terms by both h terms.
 // Placement of pairs inside a group does not affect any result: every MFMA
 // column and every VALU token is computed independently, and the combine reads
 // pairs by (token, slot).
@@ -32,6 +34,9 @@
 #include <hip/hip_runtime.h>
 
 namespace w4k {
+
+// k-steps (32 elements per lane each) the VALU small-group paths keep in registers
+constexpr int KS_VALU = 2;
 
 // ================================================================= route + group
 
@@ -249,14 +254,15 @@ __global__ __launch_bounds__(256) void k_moe_gw13(GW13Args a) {
                             const float gg = ag[nt][j], uu = au[nt][j];
                             hv[j] = (gg / (1.f + expf(-gg))) * uu;
                         }
-                        float *hp = a.h + (size_t)p * I + i0 + 4 * q;
-                        if (i0 + 4 * q + 3 < I) {
-                            *reinterpret_cast<float4 *>(hp) = make_float4(hv[0], hv[1], hv[2], hv[3]);
-                        } else {
+                        // I is a multiple of 128 (host check): rows i0 + 4q .. +3 all exist
+                        uint16_t bh[4], bl[4];
 #pragma unroll
-                            for (int j = 0; j < 4; ++j)
-                                if (i0 + 4 * q + j < I) hp[j] = hv[j];
-                        }
+                        for (int j = 0; j < 4; ++j) split_bf16(hv[j], bh[j], bl[j]);
+                        const size_t o = (size_t)p * I + i0 + 4 * q;
+                        *reinterpret_cast<uint2 *>(a.h_hi + o) =
+                            make_uint2(bh[0] | ((uint32_t)bh[1] << 16), bh[2] | ((uint32_t)bh[3] << 16));
+                        *reinterpret_cast<uint2 *>(a.h_lo + o) =
+                            make_uint2(bl[0] | ((uint32_t)bl[1] << 16), bl[2] | ((uint32_t)bl[3] << 16));
                     }
                 }
             }
@@ -265,35 +271,43 @@ __global__ __launch_bounds__(256) void k_moe_gw13(GW13Args a) {
         return;
     }
 
-    // ---- VALU: wave wv owns gate rows i0 + 4wv .. +4 (and the matching up rows)
-    // and walks the group's tokens; weights are loaded once per step.
+    // ---- VALU (small groups): wave wv owns gate rows i0 + 4wv .. +4 and the
+    // matching up rows; their codes are loaded once, then each token in turn.
     constexpr int NLG = RG >= 4 ? 1 : 4 / RG;  // load groups per wave
     const int lk = lane % L, rsub = lane / L;
-    const int ks = (H + 32 * L - 1) / (32 * L);
-    // one step at a time keeps the register count bounded for any H
-    float accg[NLG], accu[NLG];
+    const int ks = (H + 32 * L - 1) / (32 * L);  // at most KS_VALU (checked by the host)
+    uint4 cg[KS_VALU][NLG], cu[KS_VALU][NLG];
+    uint32_t sg[KS_VALU][NLG], su[KS_VALU][NLG];
+#pragma unroll
+    for (int s = 0; s < KS_VALU; ++s)
+#pragma unroll
+        for (int l = 0; l < NLG; ++l) {
+            const int k0 = 32 * (L * s + lk);
+            const int i = i0 + 4 * wv + l * RG + rsub;
+            const bool v = s < ks && k0 < H && i < I && (l * RG + rsub) < 4;
+            const uint32_t rg = (uint32_t)i, ru = (uint32_t)(I + i);
+            cg[s][l] = ld128(cb, v ? rg * (uint32_t)(H >> 1) + (uint32_t)(k0 >> 1) : OOB);
+            cu[s][l] = ld128(cb, v ? ru * (uint32_t)(H >> 1) + (uint32_t)(k0 >> 1) : OOB);
+            sg[s][l] = ld32(sb, v ? (rg * spr + (uint32_t)(k0 >> 4)) * 2u : OOB);
+            su[s][l] = ld32(sb, v ? (ru * spr + (uint32_t)(k0 >> 4)) * 2u : OOB);
+        }
     for (int idx = 0; idx < gv.m; ++idx) {
         const int p = ld_uniform(plist, idx);
         const int t = token_of(p, a.P, a.K);
         const Buf xb = make_buf(a.x + (size_t)t * H, (uint32_t)H * 2u);
+        float accg[NLG], accu[NLG];
 #pragma unroll
         for (int l = 0; l < NLG; ++l) accg[l] = accu[l] = 0.f;
-        for (int s = 0; s < ks; ++s) {
+#pragma unroll
+        for (int s = 0; s < KS_VALU; ++s) {
+            if (s >= ks) break;
             const int k0 = 32 * (L * s + lk);
-            const bool kv = k0 < H;
             XSlice<FMT_E2M1> xs;
-            load_xslice<FMT_E2M1>(xs, xb, kv ? (uint32_t)k0 * 2u : OOB);
+            load_xslice<FMT_E2M1>(xs, xb, k0 < H ? (uint32_t)k0 * 2u : OOB);
 #pragma unroll
             for (int l = 0; l < NLG; ++l) {
-                const int i = i0 + 4 * wv + l * RG + rsub;
-                const bool v = kv && i < I && (l * RG + rsub) < 4;
-                const uint32_t rg = (uint32_t)i, ru = (uint32_t)(I + i);
-                const uint4 cg = ld128(cb, v ? rg * (uint32_t)(H >> 1) + (uint32_t)(k0 >> 1) : OOB);
-                const uint4 cu = ld128(cb, v ? ru * (uint32_t)(H >> 1) + (uint32_t)(k0 >> 1) : OOB);
-                const uint32_t sg = ld32(sb, v ? (rg * spr + (uint32_t)(k0 >> 4)) * 2u : OOB);
-                const uint32_t su = ld32(sb, v ? (ru * spr + (uint32_t)(k0 >> 4)) * 2u : OOB);
-                accg[l] = chunk_dot_bf16<FMT_E2M1>(cg, sg, xs, accg[l]);
-                accu[l] = chunk_dot_bf16<FMT_E2M1>(cu, su, xs, accu[l]);
+                accg[l] = chunk_dot_bf16<FMT_E2M1>(cg[s][l], sg[s][l], xs, accg[l]);
+                accu[l] = chunk_dot_bf16<FMT_E2M1>(cu[s][l], su[s][l], xs, accu[l]);
             }
         }
 #pragma unroll
@@ -301,8 +315,12 @@ __global__ __launch_bounds__(256) void k_moe_gw13(GW13Args a) {
             const float gg = group_sum<L>(accg[l]);
             const float uu = group_sum<L>(accu[l]);
             const int i = i0 + 4 * wv + l * RG + rsub;
-            if (group_leader<L>(lane) && i < I && (l * RG + rsub) < 4)
-                a.h[(size_t)p * I + i] = (gg / (1.f + expf(-gg))) * uu;
+            if (group_leader<L>(lane) && i < I && (l * RG + rsub) < 4) {
+                uint16_t bh, bl;
+                split_bf16((gg / (1.f + expf(-gg))) * uu, bh, bl);
+                a.h_hi[(size_t)p * I + i] = bh;
+                a.h_lo[(size_t)p * I + i] = bl;
+            }
         }
     }
 }
@@ -325,25 +343,38 @@ __global__ __launch_bounds__(256) void k_moe_gw2(GW2Args a) {
     const Buf sb = make_buf(gv.scales, (uint32_t)(mat_scales * 2));
     const int row0 = tile * 64 + 16 * wv;  // this wave's 16 output rows
     const int *plist = a.pairs + gv.off;
+    const uint32_t hbytes = (uint32_t)(a.P + a.T) * (uint32_t)I * 2u;
+    const Buf hhi = make_buf(a.h_hi, hbytes), hlo = make_buf(a.h_lo, hbytes);
 
     if (gv.m >= a.mfma_min) {
-        // ---- MFMA: 16 rows x 16-column tiles, K = I in 128-wide chunks
+        // ---- MFMA: 16 rows x up to 32 columns per pass; each 128-wide K chunk of
+        // the weights is decoded once and used for both 16-column tiles
         const int r = lane & 15, q = lane >> 4;
         const bool rv = row0 + r < H;
         const uint32_t row = (uint32_t)(row0 + r);
         const int nchunks = I >> 7;
-        const Buf hall = make_buf(a.h, (uint32_t)(a.P + a.T) * (uint32_t)I * 4u);
-        for (int n0 = 0; n0 < gv.m; n0 += 16) {
-            const int idx = n0 + r;
-            const bool pv = idx < gv.m;
-            const int p = pv ? plist[idx] : 0;
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        for (int n0 = 0; n0 < gv.m; n0 += 32) {
+            int pr[2];
+            bool pv[2];
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt) {
+                const int idx = n0 + nt * 16 + r;
+                pv[nt] = idx < gv.m;
+                pr[nt] = pv[nt] ? plist[idx] : 0;
+            }
+            f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
             for (int c = 0; c < nchunks; ++c) {
                 const int k0 = c * 128 + 32 * q;
-                const uint32_t ho = (uint32_t)(p * I + k0) * 4u;
-                float4 hv[8];
+                uint4 bh[2][4], bl[2][4];
 #pragma unroll
-                for (int i = 0; i < 8; ++i) hv[i] = __builtin_bit_cast(float4, ld128(hall, pv ? ho + 16u * i : OOB));
+                for (int nt = 0; nt < 2; ++nt) {
+                    const uint32_t ho = (uint32_t)(pr[nt] * I + k0) * 2u;
+#pragma unroll
+                    for (int s = 0; s < 4; ++s) {
+                        bh[nt][s] = ld128(hhi, pv[nt] ? ho + 16u * s : OOB);
+                        bl[nt][s] = ld128(hlo, pv[nt] ? ho + 16u * s : OOB);
+                    }
+                }
                 const uint4 cw = ld128(cb, rv ? row * (uint32_t)(I >> 1) + (uint32_t)(k0 >> 1) : OOB);
                 const uint32_t sc = ld32(sb, rv ? (row * spr + (uint32_t)(k0 >> 4)) * 2u : OOB);
                 const uint32_t cws[4] = {cw.x, cw.y, cw.z, cw.w};
@@ -351,54 +382,70 @@ __global__ __launch_bounds__(256) void k_moe_gw2(GW2Args a) {
                 for (int s = 0; s < 4; ++s) {
                     float sh, sl;
                     split_scale(f16_bits_to_f32(s < 2 ? sc : (sc >> 16)), sh, sl);
-                    bf16x8 ah, al, bh, bl;
+                    bf16x8 ah, al;
                     e2m1x8_split(cws[s], sh, sl, ah, al);
-                    f32x8_split(hv[2 * s], hv[2 * s + 1], bh, bl);
-                    acc = mfma16x16x32(ah, bh, acc);
-                    acc = mfma16x16x32(ah, bl, acc);
-                    acc = mfma16x16x32(al, bh, acc);
-                    acc = mfma16x16x32(al, bl, acc);
+#pragma unroll
+                    for (int nt = 0; nt < 2; ++nt) {
+                        const bf16x8 b0 = __builtin_bit_cast(bf16x8, bh[nt][s]);
+                        const bf16x8 b1 = __builtin_bit_cast(bf16x8, bl[nt][s]);
+                        acc[nt] = mfma16x16x32(ah, b0, acc[nt]);
+                        acc[nt] = mfma16x16x32(ah, b1, acc[nt]);
+                        acc[nt] = mfma16x16x32(al, b0, acc[nt]);
+                        acc[nt] = mfma16x16x32(al, b1, acc[nt]);
+                    }
                 }
             }
             // lane holds rows row0 + 4q + j of column r
-            if (pv) {
-                float *op = a.out + (size_t)p * H + row0 + 4 * q;
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt) {
+                if (!pv[nt]) continue;
+                float *op = a.out + (size_t)pr[nt] * H + row0 + 4 * q;
                 if (row0 + 4 * q + 3 < H) {
-                    *reinterpret_cast<float4 *>(op) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+                    *reinterpret_cast<float4 *>(op) = make_float4(acc[nt][0], acc[nt][1], acc[nt][2], acc[nt][3]);
                 } else {
 #pragma unroll
                     for (int j = 0; j < 4; ++j)
-                        if (row0 + 4 * q + j < H) op[j] = acc[j];
+                        if (row0 + 4 * q + j < H) op[j] = acc[nt][j];
                 }
             }
         }
         return;
     }
 
-    // ---- VALU: 16 rows per wave in load groups of 64/L rows, tokens in turn
+    // ---- VALU (small groups): 16 rows per wave in load groups of 64/L rows;
+    // codes loaded once, then each token: bf16 weights . (h_hi + h_lo)
     constexpr int NLG = RG >= 16 ? 1 : 16 / RG;
     const int lk = lane % L, rsub = lane / L;
-    const int ks = (I + 32 * L - 1) / (32 * L);
-    float acc[NLG];
+    const int ks = (I + 32 * L - 1) / (32 * L);  // at most KS_VALU (checked by the host)
+    uint4 cw[KS_VALU][NLG];
+    uint32_t sc[KS_VALU][NLG];
+#pragma unroll
+    for (int s = 0; s < KS_VALU; ++s)
+#pragma unroll
+        for (int l = 0; l < NLG; ++l) {
+            const int k0 = 32 * (L * s + lk);
+            const int rr = row0 + l * RG + rsub;
+            const bool v = s < ks && k0 < I && rr < H && (l * RG + rsub) < 16;
+            cw[s][l] = ld128(cb, v ? (uint32_t)rr * (uint32_t)(I >> 1) + (uint32_t)(k0 >> 1) : OOB);
+            sc[s][l] = ld32(sb, v ? ((uint32_t)rr * spr + (uint32_t)(k0 >> 4)) * 2u : OOB);
+        }
     for (int idx = 0; idx < gv.m; ++idx) {
         const int p = ld_uniform(plist, idx);
-        const Buf hb = make_buf(a.h + (size_t)p * I, (uint32_t)I * 4u);
+        float acc[NLG];
 #pragma unroll
         for (int l = 0; l < NLG; ++l) acc[l] = 0.f;
-        for (int s = 0; s < ks; ++s) {
-            const int k0 = 32 * (L * s + lk);
-            const bool kv = k0 < I;
-            float4 hv[8];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) hv[i] = __builtin_bit_cast(float4, ld128(hb, kv ? (uint32_t)(k0 + 4 * i) * 4u : OOB));
-            float hs = 0.f;
+        for (int s = 0; s < KS_VALU; ++s) {
+            if (s >= ks) break;
+            const int k0 = 32 * (L * s + lk);
+            const uint32_t ho = (uint32_t)(p * I + k0) * 2u;
+            XSlice<FMT_E2M1> xh, xl;
+            load_xslice<FMT_E2M1>(xh, hhi, k0 < I ? ho : OOB);
+            load_xslice<FMT_E2M1>(xl, hlo, k0 < I ? ho : OOB);
 #pragma unroll
             for (int l = 0; l < NLG; ++l) {
-                const int rr = row0 + l * RG + rsub;
-                const bool v = kv && rr < H && (l * RG + rsub) < 16;
-                const uint4 cw = ld128(cb, v ? (uint32_t)rr * (uint32_t)(I >> 1) + (uint32_t)(k0 >> 1) : OOB);
-                const uint32_t sc = ld32(sb, v ? ((uint32_t)rr * spr + (uint32_t)(k0 >> 4)) * 2u : OOB);
-                acc[l] = chunk_dot_f32<FMT_E2M1>(cw, sc, hv, hs, acc[l]);
+                acc[l] = chunk_dot_bf16<FMT_E2M1>(cw[s][l], sc[s][l], xh, acc[l]);
+                acc[l] = chunk_dot_bf16<FMT_E2M1>(cw[s][l], sc[s][l], xl, acc[l]);
             }
         }
 #pragma unroll

@@ -548,7 +548,7 @@ constexpr int MAX_TOKENS = 4096;
 #define W4_GROUPED_MIN_T 4  // batches of at least this many tokens group their pairs by expert
 #endif
 #ifndef W4_MFMA_MIN
-#define W4_MFMA_MIN 16  // expert groups of at least this many rows run on MFMA
+#define W4_MFMA_MIN 4  // expert groups of at least this many rows run on MFMA (smaller ones on VALU)
 #endif
 constexpr int MAX_GROUPED_PAIRS = 4096;
 
@@ -608,8 +608,9 @@ int check_layer(const moe_w4a16_layer *Lr, int64_t T, MoEPlan &p) {
     // 128-wide K chunks for the MFMA tiles)
     p.P = (int)(T * K);
     p.Gmax = (int)(E < p.P ? E : p.P);
+    // (the VALU small-group path keeps at most 2 k-steps of 32 x 64 elements)
     p.grouped = T >= W4_GROUPED_MIN_T && fmt == W4_FMT_E2M1_F16S16 && H % 128 == 0 && I % 128 == 0 &&
-                p.P <= MAX_GROUPED_PAIRS;
+                p.P <= MAX_GROUPED_PAIRS && H <= 4096 && I <= 4096;
     size_t off = 0;
     p.off_logits = off; off = align_up(off + (size_t)T * p.lstride * 4, 256);
     p.off_ids = off;    off = align_up(off + (size_t)T * K * 4, 256);
@@ -620,7 +621,7 @@ int check_layer(const moe_w4a16_layer *Lr, int64_t T, MoEPlan &p) {
         const size_t rows = (size_t)p.P + (size_t)T;
         p.off_grp = off;   off = align_up(off + (size_t)(1 + 3 * p.Gmax) * 4, 256);
         p.off_pairs = off; off = align_up(off + rows * 4, 256);
-        p.off_hp = off;    off = align_up(off + rows * (size_t)I * 4, 256);
+        p.off_hp = off;    off = align_up(off + rows * (size_t)I * 4, 256);  // h_hi then h_lo, bf16
         p.off_out = off;   off = align_up(off + rows * (size_t)H * 4, 256);
     }
     p.total = off;
@@ -813,7 +814,8 @@ int run_grouped(const moe_w4a16_layer *Lr, const MoEPlan &p, const uint16_t *x, 
     float *w_ws = (float *)(wsb + p.off_w);
     int32_t *grp = (int32_t *)(wsb + p.off_grp);
     int32_t *pairs = (int32_t *)(wsb + p.off_pairs);
-    float *hp = (float *)(wsb + p.off_hp);
+    uint16_t *h_hi = (uint16_t *)(wsb + p.off_hp);
+    uint16_t *h_lo = h_hi + ((size_t)p.P + p.T) * p.I;
     float *outp = (float *)(wsb + p.off_out);
     auto ev = [&](int i) { return events ? (hipEvent_t)events[i] : (hipEvent_t) nullptr; };
     int st;
@@ -839,7 +841,7 @@ int run_grouped(const moe_w4a16_layer *Lr, const MoEPlan &p, const uint16_t *x, 
     a.codes = Lr->w13.codes, a.scales = Lr->w13.scales;
     a.s_codes = Lr->has_shared ? Lr->shared_w13.codes : nullptr;
     a.s_scales = Lr->has_shared ? Lr->shared_w13.scales : nullptr;
-    a.x = x, a.grp = grp, a.pairs = pairs, a.h = hp;
+    a.x = x, a.grp = grp, a.pairs = pairs, a.h_hi = h_hi, a.h_lo = h_lo;
     a.H = p.H, a.I = p.I, a.K = p.K, a.T = p.T, a.P = p.P, a.Gmax = p.Gmax, a.mfma_min = W4_MFMA_MIN;
     launch_gw13(a, sm, ev(4), ev(5));
     if ((st = hip_status("grouped w13 launch"))) return st;
@@ -848,7 +850,7 @@ int run_grouped(const moe_w4a16_layer *Lr, const MoEPlan &p, const uint16_t *x, 
     d.codes = Lr->w2.codes, d.scales = Lr->w2.scales;
     d.s_codes = Lr->has_shared ? Lr->shared_w2.codes : nullptr;
     d.s_scales = Lr->has_shared ? Lr->shared_w2.scales : nullptr;
-    d.grp = grp, d.pairs = pairs, d.h = hp, d.out = outp;
+    d.grp = grp, d.pairs = pairs, d.h_hi = h_hi, d.h_lo = h_lo, d.out = outp;
     d.H = p.H, d.I = p.I, d.K = p.K, d.T = p.T, d.P = p.P, d.Gmax = p.Gmax, d.mfma_min = W4_MFMA_MIN;
     launch_gw2(d, sm, ev(6), ev(7));
     if ((st = hip_status("grouped w2 launch"))) return st;
