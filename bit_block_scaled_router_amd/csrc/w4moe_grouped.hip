@@ -83,7 +83,8 @@ __global__ __launch_bounds__(1024) void k_moe_route_group(GroupArgs a) {
         pos[p] = e >= 0 ? atomicAdd(&cnt[e], 1) : -1;
     }
     __syncthreads();
-    // exclusive scans over the experts: group offsets and group indices
+    // exclusive scans over the experts: where each expert's pair list starts,
+    // and the group index of each active expert (groups in expert order)
     if (wv == 0) {
         int run = 0, grun = 0;
         for (int base = 0; base < E; base += 64) {
@@ -116,52 +117,55 @@ __global__ __launch_bounds__(1024) void k_moe_route_group(GroupArgs a) {
     for (int t = tid; t < T; t += blockDim.x) a.pairs[P + t] = P + t;
 }
 
-// Which expert and which pairs a block works on.  Group index Gmax is the
-// shared expert with pairs P .. P+T-1 (one per token).
+// Which expert and which pairs a work unit covers.  Group slot 0 is the shared
+// expert (pairs P .. P+T-1, one per token) when there is one; the routed groups
+// follow in the order of the group table.
 struct GroupView {
     const uint8_t *codes;
     const uint16_t *scales;
     int off, m;  // first entry in the pair list, number of pairs
-    bool live;
 };
 
-__device__ __forceinline__ GroupView group_view(const int32_t *grp, int g, int Gmax, int P, int T, const uint8_t *codes,
+__device__ __forceinline__ GroupView group_view(const int32_t *grp, int gs, int Gmax, int P, int T, const uint8_t *codes,
                                                 const uint16_t *scales, size_t mat_codes, size_t mat_scales,
                                                 const uint8_t *s_codes, const uint16_t *s_scales) {
     GroupView v{};
-    if (g == Gmax) {
-        v.live = s_codes != nullptr;
-        v.codes = s_codes, v.scales = s_scales, v.off = P, v.m = T;
-        return v;
+    if (s_codes != nullptr) {
+        if (gs == 0) {
+            v.codes = s_codes, v.scales = s_scales, v.off = P, v.m = T;
+            return v;
+        }
+        --gs;
     }
-    const int n = ld_uniform(grp, 0);
-    v.live = g < n;
-    if (!v.live) return v;
-    const int e = ld_uniform(grp, 1 + g);
-    v.off = ld_uniform(grp, 1 + Gmax + g);
-    v.m = ld_uniform(grp, 1 + 2 * Gmax + g);
+    const int e = ld_uniform(grp, 1 + gs);
+    v.off = ld_uniform(grp, 1 + Gmax + gs);
+    v.m = ld_uniform(grp, 1 + 2 * Gmax + gs);
     v.codes = codes + (size_t)e * mat_codes;
     v.scales = scales + (size_t)e * mat_scales;
     return v;
+}
+
+// number of work units: (routed groups + shared) x row tiles
+__device__ __forceinline__ int unit_count(const int32_t *grp, bool shared, int tiles) {
+    return (ld_uniform(grp, 0) + (shared ? 1 : 0)) * tiles;
 }
 
 __device__ __forceinline__ int token_of(int p, int P, int K) { return p < P ? p / K : p - P; }
 
 // ================================================================= grouped W13 + SiLU
 
+// One work unit of the W13 launch: group slot gs, gate rows 16*tile .. +16 (and
+// the matching up rows).
 template <int L>
-__global__ __launch_bounds__(256) void k_moe_gw13(GW13Args a) {
+__device__ __forceinline__ void gw13_unit(const GW13Args &a, int gs, int tile, float (*red)[16][64]) {
     constexpr int RG = 64 / L;
-    __shared__ float red[3][16][64];  // MFMA K-split partials of waves 1..3
     const int lane = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int g = blockIdx.x / a.tiles, tile = blockIdx.x - (blockIdx.x / a.tiles) * a.tiles;
     const int H = a.H, I = a.I;
     const uint32_t spr = (uint32_t)(H >> 4);
     const size_t mat_codes = (size_t)(2 * I) * (H >> 1), mat_scales = (size_t)(2 * I) * spr;
-    const GroupView gv = group_view(a.grp, g, a.Gmax, a.P, a.T, a.codes, a.scales, mat_codes, mat_scales, a.s_codes,
+    const GroupView gv = group_view(a.grp, gs, a.Gmax, a.P, a.T, a.codes, a.scales, mat_codes, mat_scales, a.s_codes,
                                     a.s_scales);
-    if (!gv.live) return;  // uniform per block
     const Buf cb = make_buf(gv.codes, (uint32_t)mat_codes);
     const Buf sb = make_buf(gv.scales, (uint32_t)(mat_scales * 2));
     const int i0 = tile * 16;  // first gate row of the tile
@@ -186,6 +190,7 @@ __global__ __launch_bounds__(256) void k_moe_gw13(GW13Args a) {
                 pr[nt] = pv[nt] ? plist[idx] : 0;
                 tk[nt] = token_of(pr[nt], a.P, a.K);
             }
+            const bool two = n0 + 16 < gv.m;  // second column tile in use (uniform)
             f32x4 ag[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
             f32x4 au[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
             for (int c = wv; c < nchunks; c += 4) {
@@ -196,7 +201,8 @@ __global__ __launch_bounds__(256) void k_moe_gw13(GW13Args a) {
                 for (int nt = 0; nt < 2; ++nt) {
                     const uint32_t xo = (uint32_t)(tk[nt] * H + k0) * 2u;
 #pragma unroll
-                    for (int s = 0; s < 4; ++s) xb[nt][s] = ld128(xall, pv[nt] ? xo + 16u * s : OOB);
+                    for (int s = 0; s < 4; ++s)
+                        xb[nt][s] = (nt == 0 || two) ? ld128(xall, pv[nt] ? xo + 16u * s : OOB) : make_uint4(0, 0, 0, 0);
                 }
                 const uint4 cg = ld128(cb, rg_ok ? rowg * (uint32_t)(H >> 1) + (uint32_t)(k0 >> 1) : OOB);
                 const uint4 cu = ld128(cb, rg_ok ? rowu * (uint32_t)(H >> 1) + (uint32_t)(k0 >> 1) : OOB);
@@ -213,6 +219,7 @@ __global__ __launch_bounds__(256) void k_moe_gw13(GW13Args a) {
                     e2m1x8_split(cuw[s], uh, ul, auh, aul);
 #pragma unroll
                     for (int nt = 0; nt < 2; ++nt) {
+                        if (nt == 1 && !two) break;
                         const bf16x8 b = __builtin_bit_cast(bf16x8, xb[nt][s]);
                         ag[nt] = mfma16x16x32(agh, b, ag[nt]);
                         ag[nt] = mfma16x16x32(agl, b, ag[nt]);
@@ -325,34 +332,45 @@ __global__ __launch_bounds__(256) void k_moe_gw13(GW13Args a) {
     }
 }
 
+// Blocks walk the work units (group slot x row tile) with a grid stride, so the
+// grid needs no bound on the number of active experts.
+template <int L>
+__global__ __launch_bounds__(256) void k_moe_gw13(GW13Args a) {
+    __shared__ float red[3][16][64];  // MFMA K-split partials of waves 1..3
+    const int nu = unit_count(a.grp, a.s_codes != nullptr, a.tiles);
+    for (int u = blockIdx.x; u < nu; u += gridDim.x) {
+        const int gs = u / a.tiles;
+        gw13_unit<L>(a, gs, u - gs * a.tiles, red);
+    }
+}
+
 // ================================================================= grouped W2
 
+// One work unit of the down launch: group slot gs, output rows 64*tile .. +64.
 template <int L>
-__global__ __launch_bounds__(256) void k_moe_gw2(GW2Args a) {
+__device__ __forceinline__ void gw2_unit(const GW2Args &a, int gs, int tile, float (*red)[4][8][64]) {
     constexpr int RG = 64 / L;
     const int lane = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int g = blockIdx.x / a.tiles, tile = blockIdx.x - (blockIdx.x / a.tiles) * a.tiles;
     const int H = a.H, I = a.I;
     const uint32_t spr = (uint32_t)(I >> 4);
     const size_t mat_codes = (size_t)H * (I >> 1), mat_scales = (size_t)H * spr;
-    const GroupView gv = group_view(a.grp, g, a.Gmax, a.P, a.T, a.codes, a.scales, mat_codes, mat_scales, a.s_codes,
+    const GroupView gv = group_view(a.grp, gs, a.Gmax, a.P, a.T, a.codes, a.scales, mat_codes, mat_scales, a.s_codes,
                                     a.s_scales);
-    if (!gv.live) return;
     const Buf cb = make_buf(gv.codes, (uint32_t)mat_codes);
     const Buf sb = make_buf(gv.scales, (uint32_t)(mat_scales * 2));
-    const int row0 = tile * 64 + 16 * wv;  // this wave's 16 output rows
     const int *plist = a.pairs + gv.off;
     const uint32_t hbytes = (uint32_t)(a.P + a.T) * (uint32_t)I * 2u;
     const Buf hhi = make_buf(a.h_hi, hbytes), hlo = make_buf(a.h_lo, hbytes);
 
     if (gv.m >= a.mfma_min) {
-        // ---- MFMA: 16 rows x up to 32 columns per pass; each 128-wide K chunk of
-        // the weights is decoded once and used for both 16-column tiles
+        // ---- MFMA: the 64 rows of the unit x up to 32 columns per pass.  The
+        // 128-wide K chunks are dealt round-robin to the 4 waves, so each h
+        // element is read once per unit; each wave multiplies its chunk into all
+        // four 16-row tiles, and the partials are summed in wave order via LDS.
         const int r = lane & 15, q = lane >> 4;
-        const bool rv = row0 + r < H;
-        const uint32_t row = (uint32_t)(row0 + r);
         const int nchunks = I >> 7;
+        const int u0 = tile * 64;  // first row of the unit
         for (int n0 = 0; n0 < gv.m; n0 += 32) {
             int pr[2];
             bool pv[2];
@@ -362,50 +380,88 @@ __global__ __launch_bounds__(256) void k_moe_gw2(GW2Args a) {
                 pv[nt] = idx < gv.m;
                 pr[nt] = pv[nt] ? plist[idx] : 0;
             }
-            f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-            for (int c = 0; c < nchunks; ++c) {
+            const bool two = n0 + 16 < gv.m;  // second column tile in use (uniform)
+            f32x4 acc[4][2];
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) acc[rt][0] = acc[rt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int c = wv; c < nchunks; c += 4) {
                 const int k0 = c * 128 + 32 * q;
+                uint4 cw[4];
+                uint32_t sc[4];
+#pragma unroll
+                for (int rt = 0; rt < 4; ++rt) {
+                    const int rr = u0 + 16 * rt + r;
+                    const bool rv = rr < H;
+                    cw[rt] = ld128(cb, rv ? (uint32_t)rr * (uint32_t)(I >> 1) + (uint32_t)(k0 >> 1) : OOB);
+                    sc[rt] = ld32(sb, rv ? ((uint32_t)rr * spr + (uint32_t)(k0 >> 4)) * 2u : OOB);
+                }
                 uint4 bh[2][4], bl[2][4];
 #pragma unroll
                 for (int nt = 0; nt < 2; ++nt) {
                     const uint32_t ho = (uint32_t)(pr[nt] * I + k0) * 2u;
 #pragma unroll
                     for (int s = 0; s < 4; ++s) {
-                        bh[nt][s] = ld128(hhi, pv[nt] ? ho + 16u * s : OOB);
-                        bl[nt][s] = ld128(hlo, pv[nt] ? ho + 16u * s : OOB);
+                        const bool on = nt == 0 || two;
+                        bh[nt][s] = on ? ld128(hhi, pv[nt] ? ho + 16u * s : OOB) : make_uint4(0, 0, 0, 0);
+                        bl[nt][s] = on ? ld128(hlo, pv[nt] ? ho + 16u * s : OOB) : make_uint4(0, 0, 0, 0);
                     }
                 }
-                const uint4 cw = ld128(cb, rv ? row * (uint32_t)(I >> 1) + (uint32_t)(k0 >> 1) : OOB);
-                const uint32_t sc = ld32(sb, rv ? (row * spr + (uint32_t)(k0 >> 4)) * 2u : OOB);
-                const uint32_t cws[4] = {cw.x, cw.y, cw.z, cw.w};
 #pragma unroll
-                for (int s = 0; s < 4; ++s) {
-                    float sh, sl;
-                    split_scale(f16_bits_to_f32(s < 2 ? sc : (sc >> 16)), sh, sl);
-                    bf16x8 ah, al;
-                    e2m1x8_split(cws[s], sh, sl, ah, al);
+                for (int rt = 0; rt < 4; ++rt) {
+                    const uint32_t cws[4] = {cw[rt].x, cw[rt].y, cw[rt].z, cw[rt].w};
 #pragma unroll
-                    for (int nt = 0; nt < 2; ++nt) {
-                        const bf16x8 b0 = __builtin_bit_cast(bf16x8, bh[nt][s]);
-                        const bf16x8 b1 = __builtin_bit_cast(bf16x8, bl[nt][s]);
-                        acc[nt] = mfma16x16x32(ah, b0, acc[nt]);
-                        acc[nt] = mfma16x16x32(ah, b1, acc[nt]);
-                        acc[nt] = mfma16x16x32(al, b0, acc[nt]);
-                        acc[nt] = mfma16x16x32(al, b1, acc[nt]);
+                    for (int s = 0; s < 4; ++s) {
+                        float sh, sl;
+                        split_scale(f16_bits_to_f32(s < 2 ? sc[rt] : (sc[rt] >> 16)), sh, sl);
+                        bf16x8 ah, al;
+                        e2m1x8_split(cws[s], sh, sl, ah, al);
+#pragma unroll
+                        for (int nt = 0; nt < 2; ++nt) {
+                            if (nt == 1 && !two) break;
+                            const bf16x8 b0 = __builtin_bit_cast(bf16x8, bh[nt][s]);
+                            const bf16x8 b1 = __builtin_bit_cast(bf16x8, bl[nt][s]);
+                            // all four terms: al can reach 2^-5 of the weight and
+                            // h_lo 2^-8 of h, so al * h_lo is not negligible after
+                            // cancellation in the sum over K
+                            acc[rt][nt] = mfma16x16x32(ah, b0, acc[rt][nt]);
+                            acc[rt][nt] = mfma16x16x32(ah, b1, acc[rt][nt]);
+                            acc[rt][nt] = mfma16x16x32(al, b0, acc[rt][nt]);
+                            acc[rt][nt] = mfma16x16x32(al, b1, acc[rt][nt]);
+                        }
                     }
                 }
             }
-            // lane holds rows row0 + 4q + j of column r
+            // partials of all waves -> LDS; wave w sums row tile w in wave order
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+                for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) red[wv][rt][nt * 4 + j][lane] = acc[rt][nt][j];
+            __syncthreads();
+            float v[2][4];
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    float t = red[0][wv][nt * 4 + j][lane];
+#pragma unroll
+                    for (int w = 1; w < 4; ++w) t += red[w][wv][nt * 4 + j][lane];
+                    v[nt][j] = t;
+                }
+            __syncthreads();  // red is reused by the next pass or unit
+            // lane holds rows u0 + 16wv + 4q + j of column r
+            const int rb = u0 + 16 * wv + 4 * q;
 #pragma unroll
             for (int nt = 0; nt < 2; ++nt) {
                 if (!pv[nt]) continue;
-                float *op = a.out + (size_t)pr[nt] * H + row0 + 4 * q;
-                if (row0 + 4 * q + 3 < H) {
-                    *reinterpret_cast<float4 *>(op) = make_float4(acc[nt][0], acc[nt][1], acc[nt][2], acc[nt][3]);
+                float *op = a.out + (size_t)pr[nt] * H + rb;
+                if (rb + 3 < H) {
+                    *reinterpret_cast<float4 *>(op) = make_float4(v[nt][0], v[nt][1], v[nt][2], v[nt][3]);
                 } else {
 #pragma unroll
                     for (int j = 0; j < 4; ++j)
-                        if (row0 + 4 * q + j < H) op[j] = acc[nt][j];
+                        if (rb + j < H) op[j] = v[nt][j];
                 }
             }
         }
@@ -414,6 +470,7 @@ __global__ __launch_bounds__(256) void k_moe_gw2(GW2Args a) {
 
     // ---- VALU (small groups): 16 rows per wave in load groups of 64/L rows;
     // codes loaded once, then each token: bf16 weights . (h_hi + h_lo)
+    const int row0 = tile * 64 + 16 * wv;  // this wave's 16 output rows
     constexpr int NLG = RG >= 16 ? 1 : 16 / RG;
     const int lk = lane % L, rsub = lane / L;
     const int ks = (I + 32 * L - 1) / (32 * L);  // at most KS_VALU (checked by the host)
@@ -454,6 +511,16 @@ __global__ __launch_bounds__(256) void k_moe_gw2(GW2Args a) {
             const int rr = row0 + l * RG + rsub;
             if (group_leader<L>(lane) && rr < H && (l * RG + rsub) < 16) a.out[(size_t)p * H + rr] = v;
         }
+    }
+}
+
+template <int L>
+__global__ __launch_bounds__(256) void k_moe_gw2(GW2Args a) {
+    __shared__ float red[4][4][8][64];  // MFMA partials: [wave][row tile][column tile x 4 + j][lane]
+    const int nu = unit_count(a.grp, a.s_codes != nullptr, a.tiles);
+    for (int u = blockIdx.x; u < nu; u += gridDim.x) {
+        const int gs = u / a.tiles;
+        gw2_unit<L>(a, gs, u - gs * a.tiles, red);
     }
 }
 
@@ -512,9 +579,19 @@ void launch_route_group(GroupArgs &a, hipStream_t st, hipEvent_t e0, hipEvent_t 
     else go_ev(st, e0, e1, k_moe_route_group<16>, g, b, shm, a);
 }
 
+// blocks of the grid-stride W13 and down launches
+#ifndef W4_GROUPED_BLOCKS
+#define W4_GROUPED_BLOCKS 1024
+#endif
+
+unsigned grouped_grid(int Gmax, int tiles) {
+    const long units = (long)(Gmax + 1) * tiles;
+    return (unsigned)(units < W4_GROUPED_BLOCKS ? units : W4_GROUPED_BLOCKS);
+}
+
 void launch_gw13(GW13Args &a, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
     a.tiles = (a.I + 15) / 16;
-    const dim3 g((unsigned)((a.Gmax + 1) * a.tiles)), b(256);
+    const dim3 g(grouped_grid(a.Gmax, a.tiles)), b(256);
     switch (lanes_for_k(a.H)) {
     case 1: go_ev(st, e0, e1, k_moe_gw13<1>, g, b, 0, a); break;
     case 2: go_ev(st, e0, e1, k_moe_gw13<2>, g, b, 0, a); break;
@@ -528,7 +605,7 @@ void launch_gw13(GW13Args &a, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
 
 void launch_gw2(GW2Args &a, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
     a.tiles = (a.H + 63) / 64;
-    const dim3 g((unsigned)((a.Gmax + 1) * a.tiles)), b(256);
+    const dim3 g(grouped_grid(a.Gmax, a.tiles)), b(256);
     switch (lanes_for_k(a.I)) {
     case 1: go_ev(st, e0, e1, k_moe_gw2<1>, g, b, 0, a); break;
     case 2: go_ev(st, e0, e1, k_moe_gw2<2>, g, b, 0, a); break;
