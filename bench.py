@@ -100,6 +100,57 @@ def load_traffic(kernel, workload):
     return rec.get("hbm_bytes_per_dispatch")
 
 
+COPY_KIB = 256 * 1024  # the --calibrate-copy kernel reads and writes 256 MiB
+
+
+def ingest_counters(paths, workload):
+    """Per-kernel means of rocprofv3 --pmc CSV files (counter_collection.csv).
+
+    Prints one line per (kernel, counter).  When FETCH_SIZE and WRITE_SIZE are
+    both present, each is scaled by what it reads for the plain 256 MiB copy of
+    --calibrate-copy (the first three copyBuffer dispatches) and the HBM bytes
+    per dispatch are stored in profiles/traffic.json under `workload` with the
+    current kernel source digest."""
+    import csv
+    import re
+    vals = {}  # (kernel, counter) -> list
+    calib = {}
+    for path in paths:
+        with open(path, newline="") as f:
+            for row in csv.DictReader(f):
+                name, ctr, v = row["Kernel_Name"], row["Counter_Name"], float(row["Counter_Value"])
+                if "copyBuffer" in name:
+                    calib.setdefault(ctr, []).append(v)
+                    continue
+                m = re.search(r"w4k::(k_\w+)", name)
+                if m:
+                    vals.setdefault((m.group(1), ctr), []).append(v)
+    out = {}
+    for (k, c), v in sorted(vals.items()):
+        print(f"{k:20s} {c:28s} dispatches={len(v):5d} mean={sum(v) / len(v):.3f}")
+        out.setdefault(k, {})[c] = sum(v) / len(v)
+        out[k]["dispatches"] = len(v)
+    factors = {}
+    for c in ("FETCH_SIZE", "WRITE_SIZE"):
+        if c in calib and len(calib[c]) >= 3:
+            factors[c] = COPY_KIB / (sum(calib[c][:3]) / 3)
+            print(f"calibration {c}: {sum(calib[c][:3]) / 3:.1f} KiB per 256 MiB copy -> factor {factors[c]:.5f}")
+    if len(factors) == 2:
+        path = os.path.join(ROOT, "profiles", "traffic.json")
+        db = json.load(open(path)) if os.path.exists(path) else {}
+        rec = db.setdefault(workload, {})
+        for k, d in out.items():
+            if "FETCH_SIZE" in d and "WRITE_SIZE" in d:
+                b = (d["FETCH_SIZE"] * factors["FETCH_SIZE"] + d["WRITE_SIZE"] * factors["WRITE_SIZE"]) * 1024
+                rec[k] = {"hbm_bytes_per_dispatch": round(b), "fetch_kib": round(d["FETCH_SIZE"], 3),
+                          "write_kib": round(d["WRITE_SIZE"], 3), "fetch_factor": round(factors["FETCH_SIZE"], 5),
+                          "write_factor": round(factors["WRITE_SIZE"], 5), "source_digest": source_digest()}
+                print(f"{k:20s} HBM bytes per dispatch {b:,.0f}")
+        with open(path, "w") as f:
+            json.dump(db, f, indent=1)
+            f.write("\n")
+
+
 def clone_layer(w4, layer):
     """A deep copy of a device MoE layer (new addresses, same contents)."""
     def cq(q):
@@ -404,7 +455,15 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first copy 256 MiB device-to-device 3 times (a plain copy of known size for counter runs)")
+    ap.add_argument("--ingest-counters", nargs="+", metavar="CSV",
+                    help="summarise rocprofv3 --pmc CSV files of a run of this workload (no GPU needed)")
     args = ap.parse_args()
+    if args.ingest_counters:
+        from bit_block_scaled_router_amd import synth
+        names = {"qwen-t1": synth.QWEN_MOE_T1, "qwen-t32": synth.QWEN_MOE_T32, "tiny": synth.TINY_MOE,
+                 "gemv-e2m1": synth.GEMV_E2M1, "gemv-int4": synth.GEMV_INT4}
+        ingest_counters(args.ingest_counters, names[args.workload].name)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1).", file=sys.stderr)
         sys.exit(2)

@@ -138,44 +138,48 @@ __global__ __launch_bounds__(256) void k_dequant(const uint8_t *__restrict__ cod
 // ================================================================= router
 
 // logits[t][r] for rows r in [r_begin, r_begin + gridDim.x) of the stacked
-// [E routed rows; 1 shared-gate row]: one wave per row and per TB tokens
-// (tokens TB*blockIdx.y ..), lane l covers elements 8l + 512s.  NS = number of
-// 512-element steps (H <= 512 * NS).  The activations of all TB tokens are
-// loaded before the first dot.
+// [E routed rows; 1 shared-gate row]: one block per row; its waves take the
+// tokens in chunks of TB (wave w: chunks w, w + nw, ...), so the row's weights
+// are fetched from HBM once per block and served to the other waves by the
+// cache.  Lane l covers elements 8l + 512s; NS = number of 512-element steps
+// (H <= 512 * NS).  The activations of a chunk are loaded before its first dot.
 template <int NS, int TB>
-__global__ __launch_bounds__(64) void k_router(const uint16_t *__restrict__ wr, const uint16_t *__restrict__ wsg,
-                                               const uint16_t *__restrict__ x, float *__restrict__ logits, int E,
-                                               int H, int T, int r_begin, int lstride) {
-    const int lane = threadIdx.x;
+__global__ __launch_bounds__(512) void k_router(const uint16_t *__restrict__ wr, const uint16_t *__restrict__ wsg,
+                                                const uint16_t *__restrict__ x, float *__restrict__ logits, int E,
+                                                int H, int T, int r_begin, int lstride) {
+    const int lane = threadIdx.x & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), nw = blockDim.x >> 6;
     const int r = r_begin + blockIdx.x;
-    const int t0 = blockIdx.y * TB;
     const Buf wb = make_buf(r < E ? wr + (size_t)r * H : wsg, (uint32_t)H * 2u);
     const Buf xb = make_buf(x, (uint32_t)T * (uint32_t)H * 2u);
-    uint4 w[NS], xv[TB][NS];
+    uint4 w[NS];
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
         const int e0 = 8 * lane + 512 * s;
         w[s] = ld128(wb, e0 < H ? (uint32_t)e0 * 2u : OOB);
     }
+    for (int t0 = wv * TB; t0 < T; t0 += nw * TB) {
+        uint4 xv[TB][NS];
 #pragma unroll
-    for (int tb = 0; tb < TB; ++tb)
+        for (int tb = 0; tb < TB; ++tb)
 #pragma unroll
-        for (int s = 0; s < NS; ++s) {
-            const int e0 = 8 * lane + 512 * s;
-            xv[tb][s] = ld128(xb, (e0 < H && t0 + tb < T) ? (uint32_t)((t0 + tb) * H + e0) * 2u : OOB);
+            for (int s = 0; s < NS; ++s) {
+                const int e0 = 8 * lane + 512 * s;
+                xv[tb][s] = ld128(xb, (e0 < H && t0 + tb < T) ? (uint32_t)((t0 + tb) * H + e0) * 2u : OOB);
+            }
+#pragma unroll
+        for (int tb = 0; tb < TB; ++tb) {
+            float acc = 0.f;
+#pragma unroll
+            for (int s = 0; s < NS; ++s) {
+                acc = dot2(as_bf16x2(w[s].x), xv[tb][s].x, acc);
+                acc = dot2(as_bf16x2(w[s].y), xv[tb][s].y, acc);
+                acc = dot2(as_bf16x2(w[s].z), xv[tb][s].z, acc);
+                acc = dot2(as_bf16x2(w[s].w), xv[tb][s].w, acc);
+            }
+            acc = group_sum<64>(acc);
+            if (group_leader<64>(lane) && t0 + tb < T) logits[(size_t)(t0 + tb) * lstride + r] = acc;
         }
-#pragma unroll
-    for (int tb = 0; tb < TB; ++tb) {
-        float acc = 0.f;
-#pragma unroll
-        for (int s = 0; s < NS; ++s) {
-            acc = dot2(as_bf16x2(w[s].x), xv[tb][s].x, acc);
-            acc = dot2(as_bf16x2(w[s].y), xv[tb][s].y, acc);
-            acc = dot2(as_bf16x2(w[s].z), xv[tb][s].z, acc);
-            acc = dot2(as_bf16x2(w[s].w), xv[tb][s].w, acc);
-        }
-        acc = group_sum<64>(acc);
-        if (group_leader<64>(lane) && t0 + tb < T) logits[(size_t)(t0 + tb) * lstride + r] = acc;
     }
 }
 
@@ -642,15 +646,18 @@ int launch_router(const moe_w4a16_layer *Lr, const MoEPlan &p, const uint16_t *x
     const int nrows = r_end - r_begin;
     if (nrows <= 0) return W4_OK;
     const int ns = (p.H + 511) / 512;
-    // tokens per wave: 1 for single-token decode, else 4 (activation loads in flight together)
+    // tokens per chunk: 1 for single-token decode, else 4 (activation loads in flight together)
     auto with_ns = [&](auto NSc) {
         constexpr int NS = decltype(NSc)::value;
-        if (p.T == 1)
+        if (p.T == 1) {
             go(st, k_router<NS, 1>, dim3(nrows), dim3(64), 0, Lr->router_w, Lr->shared_gate_w, x, logits, p.E, p.H,
                p.T, r_begin, p.lstride);
-        else
-            go(st, k_router<NS, 4>, dim3(nrows, (p.T + 3) / 4), dim3(64), 0, Lr->router_w, Lr->shared_gate_w, x,
-               logits, p.E, p.H, p.T, r_begin, p.lstride);
+        } else {  // chunks of 4 tokens (2 for the widest rows), up to 8 waves per row
+            constexpr int TB = NS >= 16 ? 2 : 4;
+            const int waves = (p.T + TB - 1) / TB < 8 ? (p.T + TB - 1) / TB : 8;
+            go(st, k_router<NS, TB>, dim3(nrows), dim3(64 * waves), 0, Lr->router_w, Lr->shared_gate_w, x, logits,
+               p.E, p.H, p.T, r_begin, p.lstride);
+        }
     };
     if (ns <= 1) with_ns(std::integral_constant<int, 1>());
     else if (ns <= 2) with_ns(std::integral_constant<int, 2>());
