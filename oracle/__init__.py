@@ -27,12 +27,17 @@ from .formats import (  # noqa: F401
     INT4_GROUP,
     FMT_E2M1,
     FMT_INT4,
+    FMT_NVFP4,
+    E4M3_MAX,
     bf16_bits_to_f64,
     f64_to_bf16_bits,
     e2m1_value,
     int4_value,
+    e4m3_value,
+    f32_to_ue4m3,
     quantize_e2m1,
     quantize_int4,
+    quantize_nvfp4,
     quantize,
     pack_nibbles,
     unpack_nibbles,

@@ -15,6 +15,12 @@ Everything here is written from the definitions, in float32/float64 NumPy:
   block of 16 and the 2-byte scale).
 * Signed int4 with one FP16 scale per group of 128 along K: "cuda_inf" article,
   section "2. INT4 weight quantization".
+* NVFP4 proper: E2M1 codes, one unsigned E4M3 (UE4M3) scale per 16 K elements and
+  one fp32 global scale per matrix.  The lynn-engine README names this variant
+  (status notes P17/P54 "per-16/e4m3" scales, R5-C0 "UE4M3" block-16 scales,
+  P29 a down projection taking "packed/scale/global"); E4M3 is the OCP 8-bit
+  float (1 sign, 4 exponent bits with bias 7, 3 mantissa bits, subnormals, no
+  infinities, S.1111.111 = NaN, largest finite 448).
 
 Readings taken where the pages are silent (each one is also listed in the design
 notes of the repository):
@@ -29,6 +35,13 @@ notes of the repository):
     error (ValueError here);
   - nibble order: element 2j in the low nibble, 2j+1 in the high nibble of byte j;
   - int4 nibbles are two's complement.
+  - NVFP4 (the pages give no recipe; this is the common one, which puts the
+    largest block scale at the top of the E4M3 range): g = fp32(absmax(W)) /
+    fp32(6 * 448) per matrix; block scale s = UE4M3 round-to-nearest-even of
+    fp32(fp32(absmax_block) / 6) / g, saturating at 448; element code = nearest
+    E2M1 value to fp32(w) / fp32(value(s) * g) as for the FP16-scale format; an
+    all-zero matrix gets g = 0 with zero scales and codes; a block whose scale
+    rounds to zero gets zero codes.  Value of an element: code * s * g.
 
 Parity pins (tests/test_oracle_formats.py): the E2M1 closed form against a literal
 table typed from the OCP MX definition; int4 against two's complement; the
@@ -43,11 +56,15 @@ import numpy as np
 
 FMT_E2M1 = 1  # E2M1 codes, FP16 scale per 16 K elements
 FMT_INT4 = 2  # two's-complement int4 codes, FP16 scale per 128 K elements
+FMT_NVFP4 = 3  # E2M1 codes, UE4M3 scale per 16 K elements, fp32 scale per matrix
 
 E2M1_GROUP = 16
 INT4_GROUP = 128
 
-_GROUP = {FMT_E2M1: E2M1_GROUP, FMT_INT4: INT4_GROUP}
+_GROUP = {FMT_E2M1: E2M1_GROUP, FMT_INT4: INT4_GROUP, FMT_NVFP4: E2M1_GROUP}
+_SCALE_BYTES = {FMT_E2M1: 2, FMT_INT4: 2, FMT_NVFP4: 1}
+
+E4M3_MAX = 448.0
 
 
 def group_size(fmt):
@@ -111,8 +128,37 @@ def int4_value(code):
     return (c - 16 * (c >= 8)).astype(np.float64)
 
 
+def e4m3_value(byte):
+    """OCP E4M3 byte -> float64 (closed form): sign s, exponent e (4 bits, bias 7),
+    mantissa m (3 bits); e = 0 is subnormal m/8 * 2**-6; S.1111.111 is NaN."""
+    b = np.asarray(byte, dtype=np.int64)
+    sign = np.where(b & 0x80, -1.0, 1.0)
+    e = (b >> 3) & 0xF
+    m = (b & 0x7).astype(np.float64)
+    mag = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2(e.astype(np.float64) - 7.0))
+    return np.where((b & 0x7F) == 0x7F, np.nan, sign * mag)
+
+
+# the 127 finite non-negative E4M3 values, in code order 0x00..0x7E (increasing)
+_UE4M3 = e4m3_value(np.arange(0x7F))
+
+
+def f32_to_ue4m3(v):
+    """Non-negative fp32 values -> UE4M3 bytes: nearest representable value, ties
+    to the even code (round to nearest even), saturating at 448."""
+    x = np.asarray(v, dtype=np.float32).astype(np.float64)
+    if np.any(x < 0) or not np.all(np.isfinite(x)):
+        raise ValueError("UE4M3 input must be finite and non-negative")
+    x = np.minimum(x, E4M3_MAX)
+    i = np.clip(np.searchsorted(_UE4M3, x, side="left"), 1, 0x7E)  # _UE4M3[i-1] < x <= _UE4M3[i]
+    lo, hi = _UE4M3[i - 1], _UE4M3[i]
+    dl, dh = x - lo, hi - x  # exact in float64
+    pick_hi = (dh < dl) | ((dh == dl) & (i % 2 == 0))
+    return np.where(pick_hi, i, i - 1).astype(np.uint8)
+
+
 def _decode(fmt, code):
-    if fmt == FMT_E2M1:
+    if fmt in (FMT_E2M1, FMT_NVFP4):
         return e2m1_value(code)
     if fmt == FMT_INT4:
         return int4_value(code)
@@ -190,12 +236,41 @@ def quantize_int4(w):
     return codes, s
 
 
+def quantize_nvfp4(w):
+    """fp32 weights [N][K] (one matrix) -> (codes [N][K] uint8 in 0..15,
+    UE4M3 scale bytes [N][K/16] uint8, global scale np.float32)."""
+    w32 = _check_input(w, E2M1_GROUP)
+    n, k = w32.shape
+    amax = np.abs(w32).max() if w32.size else np.float32(0)
+    if amax == 0:
+        return (np.zeros((n, k), np.uint8), np.zeros((n, k // E2M1_GROUP), np.uint8), np.float32(0))
+    g = np.float32(amax) / np.float32(6 * 448)  # IEEE fp32 division
+    a_blk = np.abs(w32.reshape(n, k // E2M1_GROUP, E2M1_GROUP)).max(axis=2)
+    u = (a_blk / np.float32(6)) / g  # two fp32 divisions
+    sb = f32_to_ue4m3(u)
+    d = (e4m3_value(sb).astype(np.float32) * g).astype(np.float32)  # fp32 product
+    d_full = np.repeat(d, E2M1_GROUP, axis=1)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        r = np.where(d_full != 0, w32 / np.where(d_full != 0, d_full, np.float32(1)), np.float32(0))
+    mag = _nearest_e2m1_magnitude_code(np.abs(r))
+    neg = (r < 0) & (mag != 0)
+    codes = (mag + 8 * neg).astype(np.uint8)
+    return codes, sb, np.float32(g)
+
+
 def quantize(fmt, w):
-    """Quantize fp32 [N][K] to canonical (packed codes [N][K/2] uint8, scales bits uint16)."""
+    """Quantize fp32 [N][K] to the canonical layout.
+
+    E2M1 / int4: (packed codes [N][K/2] uint8, scale bits [N][K/G] uint16).
+    NVFP4: (packed codes, UE4M3 scale bytes [N][K/16] uint8, global scale fp32).
+    """
     if fmt == FMT_E2M1:
         c, s = quantize_e2m1(w)
     elif fmt == FMT_INT4:
         c, s = quantize_int4(w)
+    elif fmt == FMT_NVFP4:
+        c, sb, g = quantize_nvfp4(w)
+        return pack_nibbles(c), sb, g
     else:
         raise ValueError(f"unknown format {fmt}")
     return pack_nibbles(c), s.view(np.uint16)
@@ -230,23 +305,38 @@ def codes_bytes(fmt, groups, n, k):
 
 
 def scales_bytes(fmt, groups, n, k):
-    """Bytes of FP16 scales: two bytes per block of 16 (E2M1) or 128 (int4) elements."""
-    return groups * n * (k // group_size(fmt)) * 2
+    """Bytes of block scales: two bytes (FP16) per block of 16 (E2M1) or 128 (int4)
+    elements, one byte (UE4M3) per block of 16 (NVFP4).  NVFP4 adds one fp32
+    global scale per matrix, not counted here."""
+    return groups * n * (k // group_size(fmt)) * _SCALE_BYTES[fmt]
 
 
 # --------------------------------------------------------------------------- dequant
 
 
-def dequant(fmt, packed, scale_bits):
-    """Canonical codes [N][K/2] + scale bits [N][K/G] -> fp32 [N][K].
+def dequant(fmt, packed, scale_bits, gscale=None):
+    """Canonical codes [N][K/2] + block scales [N][K/G] -> fp32 [N][K].
 
     Each product value(code) * fp32(scale) is exact in fp32: an E2M1 value has at
     most 2 significant bits, an int4 value at most 4, an fp16 scale 11, and the
     smallest non-zero product (0.5 * 2**-24) is far above fp32's subnormal range.
+    NVFP4 (scale_bits = UE4M3 bytes, gscale = the matrix's fp32 global scale):
+    value(code) * value(scale) has at most 6 significant bits and is exact; the
+    element is that product times g, rounded once to fp32.
     """
     g = group_size(fmt)
     nib = unpack_nibbles(packed)
     vals = _decode(fmt, nib).astype(np.float32)
+    if fmt == FMT_NVFP4:
+        if gscale is None:
+            raise ValueError("NVFP4 needs the global scale")
+        sb = np.asarray(scale_bits, dtype=np.uint8)
+        s_full = np.repeat(e4m3_value(sb), g, axis=-1)
+        if s_full.shape != vals.shape:
+            raise ValueError("codes and scales disagree in shape")
+        cs = vals.astype(np.float64) * s_full  # exact
+        assert np.array_equal(cs.astype(np.float32).astype(np.float64), cs)
+        return (cs * np.float64(np.float32(gscale))).astype(np.float32)  # one rounding
     s = np.asarray(scale_bits, dtype=np.uint16).view(np.float16).astype(np.float32)
     s_full = np.repeat(s, g, axis=-1)
     if s_full.shape != vals.shape:

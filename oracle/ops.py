@@ -47,9 +47,10 @@ def _as_x(x_bits):
 # --------------------------------------------------------------------------- GEMV
 
 
-def gemv(fmt, packed, scale_bits, x_bits):
-    """y[N] = dequant(W)[N][K] . x[K], float64.  x given as bf16 bits."""
-    w = dequant(fmt, packed, scale_bits).astype(np.float64)
+def gemv(fmt, packed, scale_bits, x_bits, gscale=None):
+    """y[N] = dequant(W)[N][K] . x[K], float64.  x given as bf16 bits; gscale is
+    the global scale of an NVFP4 matrix."""
+    w = dequant(fmt, packed, scale_bits, gscale).astype(np.float64)
     x = _as_x(x_bits)
     if w.shape[1] != x.shape[-1]:
         raise ValueError("K mismatch")
@@ -134,7 +135,8 @@ class MoELayer:
       shared_*   same for the shared expert (groups = 1) or None
       shared_gate_w bf16 bits [H] or None
     The w13/w2 fields may be callables e -> (codes, scales) so that a test can
-    quantise only the experts a token selects.
+    quantise only the experts a token selects.  For NVFP4 every (codes, scales)
+    pair carries a third element, the global scale (stacked: fp32 [E]).
     """
 
     def __init__(self, fmt, hidden, inter, num_experts, top_k, router_w, w13, w2,
@@ -159,22 +161,18 @@ class MoELayer:
 
     def _get(self, src, e):
         if callable(src):
-            return src(e)
-        codes, scales = src
-        return codes[e], scales[e]
+            return tuple(src(e))
+        return tuple(a[e] for a in src)
 
     def expert(self, e):
         if e not in self._cache:
-            c13, s13 = self._get(self._w13, e)
-            c2, s2 = self._get(self._w2, e)
-            self._cache[e] = (dequant(self.fmt, c13, s13), dequant(self.fmt, c2, s2))
+            self._cache[e] = (dequant(self.fmt, *self._get(self._w13, e)),
+                              dequant(self.fmt, *self._get(self._w2, e)))
         return self._cache[e]
 
     def shared(self):
         if "shared" not in self._cache:
-            c13, s13 = self.shared_w13
-            c2, s2 = self.shared_w2
-            self._cache["shared"] = (dequant(self.fmt, c13, s13), dequant(self.fmt, c2, s2))
+            self._cache["shared"] = (dequant(self.fmt, *self.shared_w13), dequant(self.fmt, *self.shared_w2))
         return self._cache["shared"]
 
 
