@@ -154,7 +154,8 @@ def ingest_counters(paths, workload):
 def clone_layer(w4, layer):
     """A deep copy of a device MoE layer (new addresses, same contents)."""
     def cq(q):
-        return w4.QMatrix(q.fmt, q.groups, q.n, q.k, q.codes.clone(), q.scales.clone())
+        g = q.global_scales.clone() if q.global_scales is not None else None
+        return w4.QMatrix(q.fmt, q.groups, q.n, q.k, q.codes.clone(), q.scales.clone(), g)
 
     kw = {}
     if layer.has_shared:
@@ -165,14 +166,22 @@ def clone_layer(w4, layer):
                        cq(layer.w13), cq(layer.w2), router_bias=rb, **kw)
 
 
+def weight_bytes(fmt, n, k):
+    """Bytes of one quantised [n][k] matrix: codes, block scales (FP16 per 16 or per
+    128; NVFP4: one UE4M3 byte per 16 plus a 4-byte global scale)."""
+    if fmt == "nvfp4":
+        return n * k // 2 + n * k // 16 + 4
+    return n * k // 2 + n * k // (128 if fmt == "int4" else 16) * 2
+
+
 def moe_bytes(shape, distinct):
     """Algorithmic HBM bytes of one MoE step: every byte the method must move once.
 
     router bf16 [E][H]; for each distinct selected expert and the shared expert,
-    W13 and W2 codes (half a byte per element) and FP16 scales (2 B per 16);
-    shared-gate bf16 [H]; x and y bf16 [T][H]."""
+    W13 and W2 codes (half a byte per element) and block scales; shared-gate
+    bf16 [H]; x and y bf16 [T][H]."""
     H, I, E, T = shape.hidden, shape.inter, shape.num_experts, shape.tokens
-    per_expert = 3 * H * I // 2 + 3 * H * I // 16 * 2
+    per_expert = weight_bytes(shape.fmt, 2 * I, H) + weight_bytes(shape.fmt, H, I)
     b = E * H * 2 + distinct * per_expert + 2 * T * H * 2
     if shape.has_shared:
         b += per_expert + H * 2
@@ -188,8 +197,8 @@ def stage_bytes(shape, distinct, n_stages=3):
     distinct expert (the batched path reads each active expert once)."""
     H, I, E, T, K = shape.hidden, shape.inter, shape.num_experts, shape.tokens, shape.top_k
     S = K + (1 if shape.has_shared else 0)
-    w13 = 2 * I * H // 2 + 2 * I * H // 16 * 2
-    w2 = H * I // 2 + H * I // 16 * 2
+    w13 = weight_bytes(shape.fmt, 2 * I, H)
+    w2 = weight_bytes(shape.fmt, H, I)
     nexp = distinct + (1 if shape.has_shared else 0)
     router = E * H * 2 + (H * 2 if shape.has_shared else 0) + T * H * 2 + T * (E + 1) * 4
     if n_stages == 3:
@@ -233,7 +242,7 @@ def cpu_baseline_moe(shape, tokens, reps):
     for t in range(tokens):
         ids, _ = ops.route(ops.router_logits(rw, xs[t], bias), shape.top_k)
         need.update(int(e) for e in ids)
-    fmt = oracle.FMT_E2M1
+    fmt = {"e2m1": oracle.FMT_E2M1, "int4": oracle.FMT_INT4, "nvfp4": oracle.FMT_NVFP4}[shape.fmt]
     q13 = {e: oracle.quantize(fmt, synth.expert_w13(shape, e)) for e in need}
     q2 = {e: oracle.quantize(fmt, synth.expert_w2(shape, e)) for e in need}
     kw = {}
@@ -264,13 +273,13 @@ def cpu_baseline_gemv(shape, reps):
     import oracle
     from bit_block_scaled_router_amd import synth
 
-    ofmt = oracle.FMT_E2M1 if shape.fmt == "e2m1" else oracle.FMT_INT4
-    codes, scales = oracle.quantize(ofmt, synth.dense_weight(shape))
+    ofmt = {"e2m1": oracle.FMT_E2M1, "int4": oracle.FMT_INT4, "nvfp4": oracle.FMT_NVFP4}[shape.fmt]
+    q = oracle.quantize(ofmt, synth.dense_weight(shape))
     x = synth.dense_x(shape)
     times = []
     for _ in range(reps):
         t0 = time.perf_counter()
-        oracle.gemv(ofmt, codes, scales, x)
+        oracle.gemv(ofmt, q[0], q[1], x, *q[2:])
         times.append(time.perf_counter() - t0)
     return {"value": float(np.median(times)) * 1e6, "unit": "us/call", "cores": 1, "kind": "oracle",
             "sample": f"the full {shape.n}x{shape.k} GEMV, median of {reps} runs",
@@ -281,7 +290,8 @@ def cpu_baseline_gemv(shape, reps):
 
 
 def run_moe(args, torch, w4, wl, synth):
-    shape = {"qwen-t1": synth.QWEN_MOE_T1, "qwen-t32": synth.QWEN_MOE_T32, "tiny": synth.TINY_MOE}[args.workload]
+    shape = {"qwen-t1": synth.QWEN_MOE_T1, "qwen-t32": synth.QWEN_MOE_T32, "tiny": synth.TINY_MOE,
+             "qwen-t1-nvfp4": synth.QWEN_MOE_T1_NVFP4}[args.workload]
     T = shape.tokens
     print(f"[bench] building {shape.name} ({args.replicas} replicas)", file=sys.stderr, flush=True)
     base = wl.build_moe_layer(shape, device="cuda")
@@ -374,7 +384,9 @@ def run_moe(args, torch, w4, wl, synth):
         "config": {
             "workload": shape.name, "hidden": shape.hidden, "experts": shape.num_experts,
             "top_k": shape.top_k, "inter": shape.inter, "shared_inter": shape.shared_inter,
-            "tokens_per_step": T, "zipf_s": shape.zipf_s, "weights": "E2M1 codes + FP16 scale per 16",
+            "tokens_per_step": T, "zipf_s": shape.zipf_s, "weights": {"e2m1": "E2M1 codes + FP16 scale per 16",
+                        "nvfp4": "E2M1 codes + UE4M3 scale per 16 + fp32 scale per matrix",
+                        "int4": "int4 codes + FP16 scale per 128"}[shape.fmt],
             "activations": "bf16", "accumulate": "fp32", "layer_replicas": R, "token_pool": P,
             "mean_distinct_experts": d_mean, "timing": "HIP graph replay of the K steps",
         },
@@ -397,10 +409,11 @@ def run_moe(args, torch, w4, wl, synth):
 
 
 def run_gemv(args, torch, w4, wl, synth):
-    shape = {"gemv-e2m1": synth.GEMV_E2M1, "gemv-int4": synth.GEMV_INT4}[args.workload]
+    shape = {"gemv-e2m1": synth.GEMV_E2M1, "gemv-int4": synth.GEMV_INT4, "gemv-nvfp4": synth.GEMV_NVFP4}[args.workload]
     print(f"[bench] building {shape.name} ({args.replicas} replicas)", file=sys.stderr, flush=True)
     base = wl.build_dense(shape, "cuda")
-    reps = [base] + [w4.QMatrix(base.fmt, 1, base.n, base.k, base.codes.clone(), base.scales.clone())
+    reps = [base] + [w4.QMatrix(base.fmt, 1, base.n, base.k, base.codes.clone(), base.scales.clone(),
+                                base.global_scales.clone() if base.global_scales is not None else None)
                      for _ in range(args.replicas - 1)]
     x = wl.bf16_tensor(synth.dense_x(shape), "cuda")
     y = torch.empty(shape.n, dtype=torch.bfloat16, device="cuda")
@@ -423,8 +436,7 @@ def run_gemv(args, torch, w4, wl, synth):
     end.record()
     torch.cuda.synchronize()
     ms_step = start.elapsed_time(end) / args.steps
-    g_bytes = shape.n * shape.k // 2 + shape.n * shape.k // (16 if shape.fmt == "e2m1" else 128) * 2 \
-        + shape.k * 2 + shape.n * 2
+    g_bytes = weight_bytes(shape.fmt, shape.n, shape.k) + shape.k * 2 + shape.n * 2
     gbs = g_bytes / (ms_step * 1e-3) / 1e9
     res = {
         "metric": METRIC, "value": ms_step * 1e3, "unit": "us/call", "n_gpus": 1, "steps": args.steps,
@@ -447,7 +459,7 @@ def main():
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="qwen-t1",
-                    choices=["qwen-t1", "qwen-t32", "tiny", "gemv-e2m1", "gemv-int4"])
+                    choices=["qwen-t1", "qwen-t32", "tiny", "gemv-e2m1", "gemv-int4", "qwen-t1-nvfp4", "gemv-nvfp4"])
     ap.add_argument("--replicas", type=int, default=0, help="weight replicas (0 = workload default)")
     ap.add_argument("--pool", type=int, default=64, help="token pool (MoE workloads)")
     ap.add_argument("--cpu-tokens", type=int, default=1)
@@ -461,7 +473,8 @@ def main():
     if args.ingest_counters:
         from bit_block_scaled_router_amd import synth
         names = {"qwen-t1": synth.QWEN_MOE_T1, "qwen-t32": synth.QWEN_MOE_T32, "tiny": synth.TINY_MOE,
-                 "gemv-e2m1": synth.GEMV_E2M1, "gemv-int4": synth.GEMV_INT4}
+                 "gemv-e2m1": synth.GEMV_E2M1, "gemv-int4": synth.GEMV_INT4,
+                 "qwen-t1-nvfp4": synth.QWEN_MOE_T1_NVFP4, "gemv-nvfp4": synth.GEMV_NVFP4}
         ingest_counters(args.ingest_counters, names[args.workload].name)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:

@@ -23,6 +23,7 @@ from ._lib import (  # noqa: F401
     W4_ERR_WORKSPACE,
     W4_FMT_E2M1_F16S16,
     W4_FMT_INT4_F16S128,
+    W4_FMT_NVFP4_E4M3S16,
     W4_LAYOUT_CANONICAL,
     W4_OK,
     MoELayerDesc,
@@ -32,8 +33,10 @@ from ._lib import (  # noqa: F401
     lib,
 )
 
-GROUP = {W4_FMT_E2M1_F16S16: 16, W4_FMT_INT4_F16S128: 128}
-FORMATS = {"e2m1": W4_FMT_E2M1_F16S16, "int4": W4_FMT_INT4_F16S128}
+GROUP = {W4_FMT_E2M1_F16S16: 16, W4_FMT_INT4_F16S128: 128, W4_FMT_NVFP4_E4M3S16: 16}
+FORMATS = {"e2m1": W4_FMT_E2M1_F16S16, "int4": W4_FMT_INT4_F16S128, "nvfp4": W4_FMT_NVFP4_E4M3S16}
+# numpy dtype of one block scale per format (FP16 bit patterns or UE4M3 bytes)
+SCALE_DTYPE = {W4_FMT_E2M1_F16S16: np.uint16, W4_FMT_INT4_F16S128: np.uint16, W4_FMT_NVFP4_E4M3S16: np.uint8}
 
 
 def _torch():
@@ -80,7 +83,10 @@ def w4_scales_bytes(fmt, groups, n, k, layout=W4_LAYOUT_CANONICAL):
 
 
 def w4_quantize(fmt, w, codes=None, scales=None):
-    """Quantise host fp32 w[n][k]; returns (codes uint8 [n][k/2], scale bits uint16 [n][k/G])."""
+    """Quantise host fp32 w[n][k] (one matrix).
+
+    Returns (codes uint8 [n][k/2], scales [n][k/G]): FP16 bit patterns (uint16)
+    for E2M1/int4; for NVFP4 (codes, UE4M3 bytes uint8, global scale float)."""
     w = np.ascontiguousarray(w, dtype=np.float32)
     if w.ndim != 2:
         raise ValueError("w must be 2-D")
@@ -89,8 +95,11 @@ def w4_quantize(fmt, w, codes=None, scales=None):
     if codes is None:
         codes = np.empty((n, k // 2), dtype=np.uint8)
     if scales is None:
-        scales = np.empty((n, max(k // g, 1)), dtype=np.uint16)
-    check(lib().w4_quantize(fmt, _ptr(w), n, k, _ptr(codes), _ptr(scales)))
+        scales = np.empty((n, max(k // g, 1)), dtype=SCALE_DTYPE.get(fmt, np.uint16))
+    gs = np.zeros(1, dtype=np.float32)
+    check(lib().w4_quantize(fmt, _ptr(w), n, k, _ptr(codes), _ptr(scales), _ptr(gs)))
+    if fmt == W4_FMT_NVFP4_E4M3S16:
+        return codes, scales, np.float32(gs[0])
     return codes, scales
 
 
@@ -116,14 +125,17 @@ def w4_unpack_nibbles(packed):
 class QMatrix:
     """A stack of quantised matrices in device memory plus its w4_matrix descriptor."""
 
-    def __init__(self, fmt, groups, n, k, codes, scales, layout=W4_LAYOUT_CANONICAL):
+    def __init__(self, fmt, groups, n, k, codes, scales, global_scales=None, layout=W4_LAYOUT_CANONICAL):
         self.fmt, self.groups, self.n, self.k = fmt, groups, n, k
-        self.codes, self.scales = codes, scales  # torch uint8 / int16 device tensors
-        self.desc = W4Matrix(fmt, layout, groups, n, k, _ptr(codes), _ptr(scales))
+        # torch device tensors: uint8 codes, int16 (FP16 bits) or uint8 (UE4M3) scales,
+        # fp32 [groups] global scales (NVFP4)
+        self.codes, self.scales, self.global_scales = codes, scales, global_scales
+        self.desc = W4Matrix(fmt, layout, groups, n, k, _ptr(codes), _ptr(scales), _ptr(global_scales))
 
     @classmethod
-    def upload(cls, fmt, codes_np, scales_np, device="cuda"):
-        """codes_np [G][n][k/2] (or [n][k/2]), scales_np [G][n][k/Gs] uint16 -> device."""
+    def upload(cls, fmt, codes_np, scales_np, device="cuda", global_np=None):
+        """codes_np [G][n][k/2] (or [n][k/2]), scales_np [G][n][k/Gs] (uint16 FP16 bits,
+        or uint8 UE4M3 for NVFP4), global_np fp32 [G] (NVFP4) -> device."""
         torch = _torch()
         c = np.ascontiguousarray(codes_np)
         s = np.ascontiguousarray(scales_np)
@@ -131,8 +143,11 @@ class QMatrix:
             c, s = c[None], s[None]
         groups, n, kh = c.shape
         tc = torch.from_numpy(c).to(device)
-        ts = torch.from_numpy(s.view(np.int16)).to(device)
-        return cls(fmt, groups, n, 2 * kh, tc, ts)
+        ts = torch.from_numpy(s.view(np.int16) if s.dtype == np.uint16 else s).to(device)
+        tg = None
+        if global_np is not None:
+            tg = torch.from_numpy(np.ascontiguousarray(global_np, dtype=np.float32).reshape(-1)).to(device)
+        return cls(fmt, groups, n, 2 * kh, tc, ts, tg)
 
 
 def w4a16_gemv(W, x, y=None, stream=None):
@@ -167,7 +182,7 @@ class MoELayer:
         self.w13, self.w2 = w13, w2
         self.shared_w13, self.shared_w2, self.shared_gate_w = shared_w13, shared_w2, shared_gate_w
         has_shared = shared_w13 is not None
-        empty = W4Matrix(0, 0, 0, 0, 0, None, None)
+        empty = W4Matrix(0, 0, 0, 0, 0, None, None, None)
         self.desc = MoELayerDesc(
             hidden, inter, num_experts, top_k, inter if has_shared else 0,
             _ptr(router_w), _ptr(router_bias), w13.desc, w2.desc, 1 if has_shared else 0,

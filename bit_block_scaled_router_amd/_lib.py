@@ -23,6 +23,7 @@ W4_ERR_RANGE = -7
 W4_ERR_HIP = -8
 W4_FMT_E2M1_F16S16 = 1
 W4_FMT_INT4_F16S128 = 2
+W4_FMT_NVFP4_E4M3S16 = 3
 W4_LAYOUT_CANONICAL = 0
 
 # every symbol the header declares
@@ -45,6 +46,7 @@ class W4Matrix(C.Structure):
         ("k", C.c_int64),
         ("codes", C.c_void_p),
         ("scales", C.c_void_p),
+        ("global_scales", C.c_void_p),
     ]
 
 
@@ -95,7 +97,7 @@ def lib():
             "w4_version": (C.c_char_p, []),
             "w4_codes_bytes": (SZ, [I32, I32, I64, I64, I64]),
             "w4_scales_bytes": (SZ, [I32, I32, I64, I64, I64]),
-            "w4_quantize": (C.c_int, [I32, P, I64, I64, P, P]),
+            "w4_quantize": (C.c_int, [I32, P, I64, I64, P, P, P]),
             "w4_pack_nibbles": (C.c_int, [P, I64, I64, P]),
             "w4_unpack_nibbles": (C.c_int, [P, I64, I64, P]),
             "w4a16_gemv": (C.c_int, [C.POINTER(W4Matrix), P, I64, P, P]),

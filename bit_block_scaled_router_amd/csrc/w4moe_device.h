@@ -20,6 +20,13 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int FMT_E2M1 = 1;
 constexpr int FMT_INT4 = 2;
+constexpr int FMT_NVFP4 = 3;  // E2M1 codes, UE4M3 scale byte per 16, fp32 global scale per matrix
+
+// bytes per block scale
+template <int FMT>
+constexpr uint32_t scale_bytes() {
+    return FMT == FMT_NVFP4 ? 1u : 2u;
+}
 
 // ---------------------------------------------------------------- conversions
 
@@ -228,19 +235,32 @@ __device__ __forceinline__ float u4_dot8(uint32_t c, uint4 x, float acc) {
     return acc;
 }
 
+// The two block scales of a lane's 32 elements (E2M1: two FP16 in the dword,
+// NVFP4: two UE4M3 bytes in its low half, decoded by the gfx950 fp8 -> fp32
+// conversion with unit scale).
+template <int FMT>
+__device__ __forceinline__ f32x2 block_scales2(uint32_t sc) {
+    if constexpr (FMT == FMT_NVFP4) {
+        return __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(sc, 1.0f, false);
+    } else {
+        return f32x2{f16_bits_to_f32(sc), f16_bits_to_f32(sc >> 16)};
+    }
+}
+
 // One lane's 32 elements (16 bytes of codes + its scales) against bf16
 // activations, added to acc in a fixed order.  E2M1: the dword `sc` holds the
 // two FP16 scales of the lane's two blocks (low half = first block).  int4: the
 // low half of `sc` is the group's scale.
 template <int FMT>
 __device__ __forceinline__ float chunk_dot_bf16(uint4 c, uint32_t sc, const XSlice<FMT> &xs, float acc) {
-    if constexpr (FMT == FMT_E2M1) {
+    if constexpr (FMT == FMT_E2M1 || FMT == FMT_NVFP4) {
         float p0 = e2m1_dot8(c.x, xs.v[0], 0.f);
         p0 = e2m1_dot8(c.y, xs.v[1], p0);
         float p1 = e2m1_dot8(c.z, xs.v[2], 0.f);
         p1 = e2m1_dot8(c.w, xs.v[3], p1);
-        acc = fmaf(p0, f16_bits_to_f32(sc), acc);
-        acc = fmaf(p1, f16_bits_to_f32(sc >> 16), acc);
+        const f32x2 s = block_scales2<FMT>(sc);
+        acc = fmaf(p0, s.x, acc);
+        acc = fmaf(p1, s.y, acc);
     } else {
         float p = u4_dot8(c.x, xs.v[0], 0.f);
         p = u4_dot8(c.y, xs.v[1], p);
@@ -257,7 +277,7 @@ __device__ __forceinline__ float chunk_dot_bf16(uint4 c, uint32_t sc, const XSli
 template <int FMT>
 __device__ __forceinline__ float chunk_dot_f32(uint4 c, uint32_t sc, const float4 *h, float hs, float acc) {
     const uint32_t cw[4] = {c.x, c.y, c.z, c.w};
-    if constexpr (FMT == FMT_E2M1) {
+    if constexpr (FMT == FMT_E2M1 || FMT == FMT_NVFP4) {
         float p[2];
 #pragma unroll
         for (int b = 0; b < 2; ++b) {
@@ -274,8 +294,9 @@ __device__ __forceinline__ float chunk_dot_f32(uint4 c, uint32_t sc, const float
             }
             p[b] = q;
         }
-        acc = fmaf(p[0], f16_bits_to_f32(sc), acc);
-        acc = fmaf(p[1], f16_bits_to_f32(sc >> 16), acc);
+        const f32x2 s = block_scales2<FMT>(sc);
+        acc = fmaf(p[0], s.x, acc);
+        acc = fmaf(p[1], s.y, acc);
     } else {
         float q = 0.f;
 #pragma unroll
@@ -295,24 +316,26 @@ __device__ __forceinline__ float chunk_dot_f32(uint4 c, uint32_t sc, const float
     return acc;
 }
 
-// Scale dword of the lane's chunk from a scale buffer: E2M1 two FP16 at
-// element k0/16 of the row, int4 one at k0/128.  `row_off` is the row's first
-// scale element; an out-of-range offset yields zero.
+// Scales of the lane's chunk from a scale buffer: E2M1 two FP16 at element
+// k0/16 of the row, NVFP4 two UE4M3 bytes at k0/16, int4 one FP16 at k0/128.
+// `row_elem0` is the row's first scale element; an out-of-range offset yields
+// zero.
 template <int FMT>
 __device__ __forceinline__ uint32_t scale_off(uint32_t row_elem0, int k0) {
-    return FMT == FMT_E2M1 ? (row_elem0 + (uint32_t)(k0 >> 4)) * 2u : (row_elem0 + (uint32_t)(k0 >> 7)) * 2u;
+    return FMT == FMT_INT4 ? (row_elem0 + (uint32_t)(k0 >> 7)) * 2u
+                           : (row_elem0 + (uint32_t)(k0 >> 4)) * scale_bytes<FMT>();
 }
 template <int FMT>
 __device__ __forceinline__ uint32_t ld_scales(Buf b, uint32_t off) {
     if constexpr (FMT == FMT_E2M1)
         return ld32(b, off);
     else
-        return ld16(b, off);
+        return ld16(b, off);  // int4: one FP16; NVFP4: two UE4M3 bytes
 }
 
 template <int FMT>
 __device__ __forceinline__ int scales_per_row(int k) {
-    return FMT == FMT_E2M1 ? (k >> 4) : (k >> 7);
+    return FMT == FMT_INT4 ? (k >> 7) : (k >> 4);
 }
 
 // ---------------------------------------------------------------- top-k

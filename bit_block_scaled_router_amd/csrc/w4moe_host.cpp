@@ -1,8 +1,10 @@
 // Host side of the w4moe C ABI: status strings, the thread-local error message,
 // size formulas, the offline quantiser and nibble packing.  Nothing here touches
 // the GPU.  Rules are those of include/w4moe.h; sources: "Lynn Engine" article,
-// "Kernel optimisation history" stage P1 (E2M1 + FP16 scale per 16 K elements)
-// and the "cuda_inf" article, "2. INT4 weight quantization" (int4, group 128).
+// "Kernel optimisation history" stage P1 (E2M1 + FP16 scale per 16 K elements),
+// the "cuda_inf" article, "2. INT4 weight quantization" (int4, group 128), and
+// the lynn-engine README notes P17/P29/R5-C0 (UE4M3 per-16 scales and a global
+// scale: the NVFP4 variant).
 #include "w4moe_internal.h"
 
 #include <cmath>
@@ -30,6 +32,7 @@ int group_of(int32_t format) {
     switch (format) {
     case W4_FMT_E2M1_F16S16: return 16;
     case W4_FMT_INT4_F16S128: return 128;
+    case W4_FMT_NVFP4_E4M3S16: return 16;
     default: return 0;
     }
 }
@@ -39,7 +42,7 @@ int check_shape(int32_t format, int32_t layout, int64_t groups, int64_t n, int64
     if (!g) return fail(W4_ERR_LAYOUT, "unknown format tag %d", (int)format);
     if (layout != W4_LAYOUT_CANONICAL) return fail(W4_ERR_LAYOUT, "unknown layout tag %d", (int)layout);
     if (groups < 1 || n < 1 || k < 1) return fail(W4_ERR_INVALID_ARG, "groups/n/k must be >= 1");
-    const int64_t kmul = format == W4_FMT_E2M1_F16S16 ? 32 : 128;
+    const int64_t kmul = format == W4_FMT_INT4_F16S128 ? 128 : 32;
     if (k % kmul) return fail(W4_ERR_INVALID_ARG, "k=%lld must be a multiple of %lld", (long long)k, (long long)kmul);
     if (groups > (int64_t(1) << 20) || n > (int64_t(1) << 31) || k > (int64_t(1) << 24))
         return fail(W4_ERR_INVALID_ARG, "matrix dimensions out of range");
@@ -63,6 +66,29 @@ static inline float f16_bits_to_f32(uint16_t b) {
     return (float)h;
 }
 
+// Non-negative fp32 -> UE4M3 byte (OCP E4M3 with sign 0: exponent bias 7, 3
+// mantissa bits, subnormals m * 2^-9), round to nearest even, saturating at 448
+// (code 0x7E; 0x7F is NaN and never produced).
+static inline uint8_t f32_to_ue4m3(float x) {
+    if (!(x < 448.0f)) return 0x7E;
+    if (x < 0.015625f) {  // below 2^-6: subnormal grid of 2^-9 (exact scaling)
+        const float m = std::nearbyint(x * 512.0f);  // 0..8; 8 is the first normal
+        return (uint8_t)m;
+    }
+    int e;
+    const float f = std::frexp(x, &e);             // x = f * 2^e, f in [0.5, 1)
+    float m = std::nearbyint((2.0f * f - 1.0f) * 8.0f);  // exact operand, ties to even
+    int be = e - 1 + 7;
+    if (m == 8.0f) m = 0.0f, ++be;
+    const int code = (be << 3) | (int)m;
+    return (uint8_t)(code > 0x7E ? 0x7E : code);
+}
+
+static inline float ue4m3_to_f32(uint8_t c) {
+    const int be = (c >> 3) & 0xF, m = c & 7;
+    return be == 0 ? std::ldexp((float)m, -9) : std::ldexp(1.0f + (float)m / 8.0f, be - 7);
+}
+
 // Nearest E2M1 magnitude code (0..7) to r >= 0, ties to the even code.
 // Magnitudes by code: 0, 0.5, 1, 1.5, 2, 3, 4, 6; the midpoints between
 // neighbours are 0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.  On a midpoint the even
@@ -78,10 +104,11 @@ static inline int e2m1_mag_code(float r) {
     return 7;                   // saturate
 }
 
+// gscale: the matrix's NVFP4 global scale (unused for the FP16-scale formats).
 static void quantize_rows(int32_t format, const float *w, int64_t r0, int64_t r1, int64_t k,
-                          uint8_t *codes, uint16_t *scales) {
+                          uint8_t *codes, void *scales, float gscale) {
     const int g = group_of(format);
-    const float qmax = format == W4_FMT_E2M1_F16S16 ? 6.0f : 7.0f;
+    const float qmax = format == W4_FMT_INT4_F16S128 ? 7.0f : 6.0f;
     const int64_t nb = k / g;
     for (int64_t r = r0; r < r1; ++r) {
         const float *wr = w + r * k;
@@ -90,16 +117,23 @@ static void quantize_rows(int32_t format, const float *w, int64_t r0, int64_t r1
             const float *wb = wr + b * g;
             float a = 0.f;
             for (int i = 0; i < g; ++i) a = std::fmax(a, std::fabs(wb[i]));
-            const uint16_t sb = f32_to_f16_bits(a / qmax);
-            scales[r * nb + b] = sb;
-            const float s = f16_bits_to_f32(sb);
+            float s;  // the divisor of the codes
+            if (format == W4_FMT_NVFP4_E4M3S16) {
+                const uint8_t sb = gscale != 0.f ? f32_to_ue4m3((a / 6.0f) / gscale) : 0;
+                static_cast<uint8_t *>(scales)[r * nb + b] = sb;
+                s = ue4m3_to_f32(sb) * gscale;  // fp32 product
+            } else {
+                const uint16_t sb = f32_to_f16_bits(a / qmax);
+                static_cast<uint16_t *>(scales)[r * nb + b] = sb;
+                s = f16_bits_to_f32(sb);
+            }
             for (int i = 0; i < g; i += 2) {
                 uint8_t c2[2];
                 for (int j = 0; j < 2; ++j) {
                     uint8_t c = 0;
                     if (s != 0.f) {
                         const float q = wb[i + j] / s;  // IEEE fp32 division
-                        if (format == W4_FMT_E2M1_F16S16) {
+                        if (format != W4_FMT_INT4_F16S128) {
                             const int m = e2m1_mag_code(std::fabs(q));
                             c = (uint8_t)(m | ((q < 0.f && m != 0) ? 8 : 0));
                         } else {
@@ -148,39 +182,51 @@ size_t w4_codes_bytes(int32_t format, int32_t layout, int64_t groups, int64_t n,
 
 size_t w4_scales_bytes(int32_t format, int32_t layout, int64_t groups, int64_t n, int64_t k) {
     if (check_shape(format, layout, groups, n, k) != W4_OK) return 0;
-    return (size_t)groups * (size_t)n * (size_t)(k / group_of(format)) * 2;
+    const size_t bytes = format == W4_FMT_NVFP4_E4M3S16 ? 1 : 2;
+    return (size_t)groups * (size_t)n * (size_t)(k / group_of(format)) * bytes;
 }
 
-int w4_quantize(int32_t format, const float *w, int64_t n, int64_t k, uint8_t *codes, uint16_t *scales) {
+int w4_quantize(int32_t format, const float *w, int64_t n, int64_t k, uint8_t *codes, void *scales,
+                float *global_scale) {
     clear_error();
     int st = check_shape(format, W4_LAYOUT_CANONICAL, 1, n, k);
     if (st) return st;
     if (!w || !codes || !scales) return fail(W4_ERR_INVALID_ARG, "null pointer");
+    const bool nv = format == W4_FMT_NVFP4_E4M3S16;
+    if (nv && !global_scale) return fail(W4_ERR_INVALID_ARG, "NVFP4 needs a global_scale output");
     const int g = group_of(format);
-    const float qmax = format == W4_FMT_E2M1_F16S16 ? 6.0f : 7.0f;
+    const float qmax = format == W4_FMT_INT4_F16S128 ? 7.0f : 6.0f;
     // validate everything before writing anything
     const int64_t total = n * k;
     for (int64_t i = 0; i < total; ++i)
         if (!std::isfinite(w[i])) return fail(W4_ERR_NONFINITE, "non-finite weight at index %lld", (long long)i);
-    for (int64_t b = 0; b < total / g; ++b) {
-        float a = 0.f;
-        for (int i = 0; i < g; ++i) a = std::fmax(a, std::fabs(w[b * g + i]));
-        if (!std::isfinite(f16_bits_to_f32(f32_to_f16_bits(a / qmax))))
-            return fail(W4_ERR_RANGE, "block %lld: scale %g overflows fp16", (long long)b, (double)(a / qmax));
+    float gscale = 0.f;
+    if (nv) {  // UE4M3 block scales saturate; only the global scale is computed here
+        float amax = 0.f;
+        for (int64_t i = 0; i < total; ++i) amax = std::fmax(amax, std::fabs(w[i]));
+        gscale = amax / 2688.0f;  // 6 x 448
+        *global_scale = gscale;
+    } else {
+        for (int64_t b = 0; b < total / g; ++b) {
+            float a = 0.f;
+            for (int i = 0; i < g; ++i) a = std::fmax(a, std::fabs(w[b * g + i]));
+            if (!std::isfinite(f16_bits_to_f32(f32_to_f16_bits(a / qmax))))
+                return fail(W4_ERR_RANGE, "block %lld: scale %g overflows fp16", (long long)b, (double)(a / qmax));
+        }
     }
     // rows are independent: split them over a few host threads for big matrices
     unsigned nt = std::thread::hardware_concurrency();
     nt = nt ? (nt > 16 ? 16 : nt) : 1;
     if (total < (int64_t(1) << 22) || n < (int64_t)nt) nt = 1;
     if (nt == 1) {
-        quantize_rows(format, w, 0, n, k, codes, scales);
+        quantize_rows(format, w, 0, n, k, codes, scales, gscale);
     } else {
         std::vector<std::thread> th;
         const int64_t per = (n + nt - 1) / nt;
         for (unsigned t = 0; t < nt; ++t) {
             const int64_t r0 = t * per, r1 = r0 + per < n ? r0 + per : n;
             if (r0 >= r1) break;
-            th.emplace_back(quantize_rows, format, w, r0, r1, k, codes, scales);
+            th.emplace_back(quantize_rows, format, w, r0, r1, k, codes, scales, gscale);
         }
         for (auto &t : th) t.join();
     }

@@ -34,10 +34,11 @@ namespace w4k {
 
 // y[t][n] = sum_k W[n][k] x[t][k].  A wave owns RT load-groups of 64/L rows and
 // issues all of its weight loads before the first use.
+// NVFP4: the row sums are multiplied by the matrix's global scale *gsc.
 template <int FMT, int L, int RT>
-__global__ __launch_bounds__(256) void k_gemv(const uint8_t *__restrict__ codes, const uint16_t *__restrict__ scales,
-                                              const uint16_t *__restrict__ x, uint16_t *__restrict__ y, int n, int k,
-                                              int m) {
+__global__ __launch_bounds__(256) void k_gemv(const uint8_t *__restrict__ codes, const uint8_t *__restrict__ scales,
+                                              const float *__restrict__ gsc, const uint16_t *__restrict__ x,
+                                              uint16_t *__restrict__ y, int n, int k, int m) {
     constexpr int RG = 64 / L;
     const int lane = threadIdx.x & 63;
     const int wave = wave_id();
@@ -47,8 +48,10 @@ __global__ __launch_bounds__(256) void k_gemv(const uint8_t *__restrict__ codes,
     const int ks = (k + 32 * L - 1) / (32 * L);
     const uint32_t spr = (uint32_t)scales_per_row<FMT>(k);
     const Buf cb = make_buf(codes, (uint32_t)n * (uint32_t)(k >> 1));
-    const Buf sb = make_buf(scales, (uint32_t)n * spr * 2u);
+    const Buf sb = make_buf(scales, (uint32_t)n * spr * scale_bytes<FMT>());
     const Buf xb = make_buf(x, (uint32_t)m * (uint32_t)k * 2u);
+    float g = 1.f;
+    if constexpr (FMT == FMT_NVFP4) g = ld_uniform(gsc, 0);
     for (int t = 0; t < m; ++t) {
         float acc[RT];
 #pragma unroll
@@ -73,7 +76,8 @@ __global__ __launch_bounds__(256) void k_gemv(const uint8_t *__restrict__ codes,
         }
 #pragma unroll
         for (int r = 0; r < RT; ++r) {
-            const float v = group_sum<L>(acc[r]);
+            float v = group_sum<L>(acc[r]);
+            if constexpr (FMT == FMT_NVFP4) v *= g;
             const int row = row0 + r * RG + rsub;
             if (group_leader<L>(lane) && row < n) y[(size_t)t * n + row] = f32_to_bf16_rne(v);
         }
@@ -82,10 +86,12 @@ __global__ __launch_bounds__(256) void k_gemv(const uint8_t *__restrict__ codes,
 
 // ================================================================= dequant hook
 
-// out[row][k] = value(code) * fp32(scale), with the bf16 decode the GEMV uses.
+// out[row][k] = value(code) * fp32(scale), with the bf16 decode the GEMV uses
+// (NVFP4: times the global scale of the row's matrix, gsc[row / n]).
 template <int FMT, int L>
-__global__ __launch_bounds__(256) void k_dequant(const uint8_t *__restrict__ codes, const uint16_t *__restrict__ scales,
-                                                 float *__restrict__ out, int64_t rows, int k) {
+__global__ __launch_bounds__(256) void k_dequant(const uint8_t *__restrict__ codes, const uint8_t *__restrict__ scales,
+                                                 const float *__restrict__ gsc, float *__restrict__ out, int64_t rows,
+                                                 int64_t n, int k) {
     constexpr int RG = 64 / L;
     const int lane = threadIdx.x & 63;
     const int64_t wave = wave_id();
@@ -97,17 +103,20 @@ __global__ __launch_bounds__(256) void k_dequant(const uint8_t *__restrict__ cod
     const uint32_t spr = (uint32_t)scales_per_row<FMT>(k);
     const int64_t nrows = rows - row0 < RG ? rows - row0 : RG;
     const Buf cb = make_buf(codes + row0 * (k >> 1), (uint32_t)(nrows * (k >> 1)));
-    const Buf sb = make_buf(scales + row0 * spr, (uint32_t)(nrows * spr * 2u));
+    const Buf sb = make_buf(scales + row0 * spr * scale_bytes<FMT>(), (uint32_t)(nrows * spr * scale_bytes<FMT>()));
     const uint32_t rl = (uint32_t)(lane / L);
+    float g = 1.f;
+    if constexpr (FMT == FMT_NVFP4) g = rv ? gsc[row / n] : 0.f;
     for (int k0 = 32 * lk; k0 < k; k0 += 32 * L) {
         const uint4 c = ld128(cb, rv ? rl * (uint32_t)(k >> 1) + (uint32_t)(k0 >> 1) : OOB);
         const uint32_t sc = ld_scales<FMT>(sb, rv ? scale_off<FMT>(rl * spr, k0) : OOB);
         const uint32_t cw[4] = {c.x, c.y, c.z, c.w};
         float v[32];
-        if constexpr (FMT == FMT_E2M1) {
+        if constexpr (FMT == FMT_E2M1 || FMT == FMT_NVFP4) {
+            const f32x2 s2 = block_scales2<FMT>(sc);
 #pragma unroll
             for (int d = 0; d < 4; ++d) {
-                const float s = f16_bits_to_f32(d < 2 ? sc : (sc >> 16));
+                const float s = d < 2 ? s2.x : s2.y;
                 bf16x2 p;
                 p = e2m1x2_bf16<0>(cw[d]); v[8 * d + 0] = (float)p.x * s; v[8 * d + 1] = (float)p.y * s;
                 p = e2m1x2_bf16<1>(cw[d]); v[8 * d + 2] = (float)p.x * s; v[8 * d + 3] = (float)p.y * s;
@@ -126,6 +135,10 @@ __global__ __launch_bounds__(256) void k_dequant(const uint8_t *__restrict__ cod
                 p = u4x2_bf16<false>(hi); v[8 * d + 1] = ((float)p.x - 8.f) * s; v[8 * d + 3] = ((float)p.y - 8.f) * s;
                 p = u4x2_bf16<true>(hi);  v[8 * d + 5] = ((float)p.x - 8.f) * s; v[8 * d + 7] = ((float)p.y - 8.f) * s;
             }
+        }
+        if constexpr (FMT == FMT_NVFP4) {
+#pragma unroll
+            for (int i = 0; i < 32; ++i) v[i] *= g;  // code * scale is exact: one rounding
         }
         if (rv) {
             float4 *o = reinterpret_cast<float4 *>(out + row * k + k0);
@@ -187,9 +200,10 @@ __global__ __launch_bounds__(512) void k_router(const uint16_t *__restrict__ wr,
 
 struct W13Args {
     const uint8_t *codes;         // routed W13 [E][2I][H/2]
-    const uint16_t *scales;       // routed W13 scales
+    const uint8_t *scales;        // routed W13 scales (bytes)
     const uint8_t *s_codes;       // shared W13 [2I][H/2] (or null)
-    const uint16_t *s_scales;
+    const uint8_t *s_scales;
+    const float *gs, *s_gs;       // NVFP4 global scales: routed [E], shared [1]
     const uint16_t *x;            // [T][H]
     const float *logits;          // [T][lstride] (routed mode)
     const float *bias;            // [E] or null
@@ -238,18 +252,20 @@ __global__ __launch_bounds__(1024) void k_moe_w13(W13Args a) {
     const int ks = (H + 32 * L - 1) / (32 * L);
     const uint32_t spr = (uint32_t)scales_per_row<FMT>(H);
     const uint32_t mat_codes = (uint32_t)(2 * I) * (uint32_t)(H >> 1);
-    const uint32_t mat_scales = (uint32_t)(2 * I) * spr * 2u;
+    const uint32_t mat_scales = (uint32_t)(2 * I) * spr * scale_bytes<FMT>();
     const Buf xb = make_buf(a.x + (size_t)t * H, (uint32_t)H * 2u);
     XSlice<FMT> xs0;  // step-0 activations, in flight while the experts are ranked
     load_xslice<FMT>(xs0, xb, 32 * lk < H ? (uint32_t)(32 * lk) * 2u : OOB);
 
     // which expert: shared slot, ranked once per block, or supplied
     const uint8_t *cbase;
-    const uint16_t *sbase;
+    const uint8_t *sbase;
+    const float *gp = nullptr;  // NVFP4 global scale of the expert's matrix
     bool valid = true;
     if (j == a.K) {
         cbase = a.s_codes;
         sbase = a.s_scales;
+        gp = a.s_gs;
     } else {
         int e;
         if (a.route) {
@@ -282,7 +298,8 @@ __global__ __launch_bounds__(1024) void k_moe_w13(W13Args a) {
         valid = e >= 0 && e < a.E;  // an id out of range reads nothing and poisons h
         const int eo = valid ? e : 0;
         cbase = a.codes + (size_t)eo * mat_codes;
-        sbase = a.scales + (size_t)eo * (mat_scales >> 1);
+        sbase = a.scales + (size_t)eo * mat_scales;
+        gp = a.gs ? a.gs + eo : nullptr;
     }
     if (!tile_ok) return;  // after the block's barrier; uniform per wave
     const Buf cb = make_buf(cbase, valid ? mat_codes : 0u);
@@ -317,11 +334,14 @@ __global__ __launch_bounds__(1024) void k_moe_w13(W13Args a) {
             au[r] = chunk_dot_bf16<FMT>(cu[r], su[r], xs, au[r]);
         }
     }
+    float gsc = 1.f;
+    if constexpr (FMT == FMT_NVFP4) gsc = ld_uniform(gp, 0);
     float *hrow = a.h + ((size_t)t * a.S + j) * a.hstride;
 #pragma unroll
     for (int r = 0; r < RT; ++r) {
-        const float g = group_sum<L>(ag[r]);
-        const float u = group_sum<L>(au[r]);
+        float g = group_sum<L>(ag[r]);
+        float u = group_sum<L>(au[r]);
+        if constexpr (FMT == FMT_NVFP4) g *= gsc, u *= gsc;
         const int i = i0 + r * RG + rsub;
         if (group_leader<L>(lane) && i < I) {
             const float hv = valid ? (g / (1.f + expf(-g))) * u : __builtin_nanf("");
@@ -334,9 +354,10 @@ __global__ __launch_bounds__(1024) void k_moe_w13(W13Args a) {
 
 struct DownArgs {
     const uint8_t *codes;         // routed W2 [E][H][I/2]
-    const uint16_t *scales;
+    const uint8_t *scales;        // (bytes)
     const uint8_t *s_codes;       // shared W2 [H][I/2]
-    const uint16_t *s_scales;
+    const uint8_t *s_scales;
+    const float *gs, *s_gs;       // NVFP4 global scales: routed [E], shared [1]
     const int32_t *ids;           // [T][k]
     const float *w;               // [T][k]
     const float *logits;          // [T][lstride]; column E = shared-gate logit
@@ -362,7 +383,7 @@ __global__ __launch_bounds__(1024) void k_moe_down(DownArgs a) {
     const int ks = (I + 32 * L - 1) / (32 * L);
     const uint32_t spr = (uint32_t)scales_per_row<FMT>(I);
     const uint32_t mat_codes = (uint32_t)H * (uint32_t)(I >> 1);
-    const uint32_t mat_scales = (uint32_t)H * spr * 2u;
+    const uint32_t mat_scales = (uint32_t)H * spr * scale_bytes<FMT>();
 
     for (int j = wv; j < a.S; j += nw) {
         // step-0 activations first: they do not depend on the routing
@@ -375,21 +396,25 @@ __global__ __launch_bounds__(1024) void k_moe_down(DownArgs a) {
                 hv0[q] = __builtin_bit_cast(float4, ld128(hb, 32 * lk < I ? h0 + (uint32_t)q * L * 16u : OOB));
         }
         const uint8_t *cbase;
-        const uint16_t *sbase;
+        const uint8_t *sbase;
+        const float *gp;
         float coef;
         bool valid = true;
         if (j == a.K) {
             cbase = a.s_codes;
             sbase = a.s_scales;
+            gp = a.s_gs;
             coef = 1.f / (1.f + expf(-ld_uniform(a.logits, t * a.lstride + a.E)));
         } else {
             const int e = ld_uniform(a.ids, t * a.K + j);
             valid = e >= 0 && e < a.E;
             const int eo = valid ? e : 0;
             cbase = a.codes + (size_t)eo * mat_codes;
-            sbase = a.scales + (size_t)eo * (mat_scales >> 1);
+            sbase = a.scales + (size_t)eo * mat_scales;
+            gp = a.gs ? a.gs + eo : nullptr;
             coef = ld_uniform(a.w, t * a.K + j);
         }
+        if constexpr (FMT == FMT_NVFP4) coef *= ld_uniform(gp, 0);  // (w x g) x row sum
         const Buf cb = make_buf(cbase, valid ? mat_codes : 0u);
         const Buf sb = make_buf(sbase, valid ? mat_scales : 0u);
         float acc[RT];
@@ -481,6 +506,10 @@ int check_matrix(const w4_matrix *W, const char *what) {
     if (!W->codes || !W->scales) return fail(W4_ERR_INVALID_ARG, "%s: null codes/scales", what);
     if (!aligned(W->codes, 16)) return fail(W4_ERR_ALIGNMENT, "%s: codes not 16-byte aligned", what);
     if (!aligned(W->scales, 4)) return fail(W4_ERR_ALIGNMENT, "%s: scales not 4-byte aligned", what);
+    if (W->format == W4_FMT_NVFP4_E4M3S16) {
+        if (!W->global_scales) return fail(W4_ERR_INVALID_ARG, "%s: NVFP4 needs global_scales", what);
+        if (!aligned(W->global_scales, 4)) return fail(W4_ERR_ALIGNMENT, "%s: global_scales not 4-byte aligned", what);
+    }
     if (W->n > (1 << 30) || W->k > (1 << 20)) return fail(W4_ERR_UNSUPPORTED, "%s: dimension too large", what);
     // one matrix of the stack is addressed through 32-bit buffer offsets
     if ((uint64_t)W->n * (uint64_t)W->k / 2 >= (1ull << 31))
@@ -511,7 +540,8 @@ void launch_gemv_L(const w4_matrix *W, const uint16_t *x, int m, uint16_t *y, hi
     const int waves = (n + RT * RG - 1) / (RT * RG);
     const int wpb = W4_GEMV_WPB;
     const int blocks = (waves + wpb - 1) / wpb;
-    hipLaunchKernelGGL((k_gemv<FMT, L, RT>), dim3(blocks), dim3(64 * wpb), 0, st, W->codes, W->scales, x, y, n, k, m);
+    hipLaunchKernelGGL((k_gemv<FMT, L, RT>), dim3(blocks), dim3(64 * wpb), 0, st, W->codes,
+                       (const uint8_t *)W->scales, W->global_scales, x, y, n, k, m);
 }
 
 template <int FMT>
@@ -534,8 +564,8 @@ void launch_dequant_L(const w4_matrix *W, float *out, hipStream_t st) {
     const int64_t waves = (rows + RG - 1) / RG;
     const int wpb = 4;
     const int64_t blocks = (waves + wpb - 1) / wpb;
-    hipLaunchKernelGGL((k_dequant<FMT, L>), dim3((unsigned)blocks), dim3(64 * wpb), 0, st, W->codes, W->scales, out,
-                       rows, (int)W->k);
+    hipLaunchKernelGGL((k_dequant<FMT, L>), dim3((unsigned)blocks), dim3(64 * wpb), 0, st, W->codes,
+                       (const uint8_t *)W->scales, W->global_scales, out, rows, W->n, (int)W->k);
 }
 
 template <int FMT>
@@ -790,9 +820,11 @@ int run_moe(const moe_w4a16_layer *Lr, const uint16_t *x, int64_t T, const int32
     // 2) W13 + SiLU over all (token, slot, tile)
     W13Args a{};
     a.codes = Lr->w13.codes;
-    a.scales = Lr->w13.scales;
+    a.scales = (const uint8_t *)Lr->w13.scales;
+    a.gs = Lr->w13.global_scales;
     a.s_codes = Lr->has_shared ? Lr->shared_w13.codes : nullptr;
-    a.s_scales = Lr->has_shared ? Lr->shared_w13.scales : nullptr;
+    a.s_scales = Lr->has_shared ? (const uint8_t *)Lr->shared_w13.scales : nullptr;
+    a.s_gs = Lr->has_shared ? Lr->shared_w13.global_scales : nullptr;
     a.x = x;
     a.logits = logits;
     a.bias = Lr->router_bias;
@@ -805,15 +837,18 @@ int run_moe(const moe_w4a16_layer *Lr, const uint16_t *x, int64_t T, const int32
     a.H = p.H, a.I = p.I, a.E = p.E, a.K = p.K, a.S = p.S, a.T = p.T;
     a.lstride = p.lstride, a.hstride = p.hstride, a.route = route ? 1 : 0, a.L2 = p.L2;
     if (Lr->w13.format == W4_FMT_E2M1_F16S16) launch_w13<FMT_E2M1>(p, a, l_w13);
+    else if (Lr->w13.format == W4_FMT_NVFP4_E4M3S16) launch_w13<FMT_NVFP4>(p, a, l_w13);
     else launch_w13<FMT_INT4>(p, a, l_w13);
     if ((st = hip_status("w13 launch"))) return st;
 
     // 3) down projection + weighted combine
     DownArgs d{};
     d.codes = Lr->w2.codes;
-    d.scales = Lr->w2.scales;
+    d.scales = (const uint8_t *)Lr->w2.scales;
+    d.gs = Lr->w2.global_scales;
     d.s_codes = Lr->has_shared ? Lr->shared_w2.codes : nullptr;
-    d.s_scales = Lr->has_shared ? Lr->shared_w2.scales : nullptr;
+    d.s_scales = Lr->has_shared ? (const uint8_t *)Lr->shared_w2.scales : nullptr;
+    d.s_gs = Lr->has_shared ? Lr->shared_w2.global_scales : nullptr;
     d.ids = route ? ids_ws : ids_in;
     d.w = route ? w_ws : w_in;
     d.logits = logits;
@@ -822,6 +857,7 @@ int run_moe(const moe_w4a16_layer *Lr, const uint16_t *x, int64_t T, const int32
     d.H = p.H, d.I = p.I, d.E = p.E, d.K = p.K, d.S = p.S, d.T = p.T;
     d.lstride = p.lstride, d.hstride = p.hstride;
     if (Lr->w2.format == W4_FMT_E2M1_F16S16) launch_down<FMT_E2M1>(p, d, l_down);
+    else if (Lr->w2.format == W4_FMT_NVFP4_E4M3S16) launch_down<FMT_NVFP4>(p, d, l_down);
     else launch_down<FMT_INT4>(p, d, l_down);
     return hip_status("down launch");
 }
@@ -859,18 +895,18 @@ int run_grouped(const moe_w4a16_layer *Lr, const MoEPlan &p, const uint16_t *x, 
     if ((st = hip_status("route/group launch"))) return st;
     // 3) grouped W13 + SiLU
     GW13Args a{};
-    a.codes = Lr->w13.codes, a.scales = Lr->w13.scales;
+    a.codes = Lr->w13.codes, a.scales = (const uint16_t *)Lr->w13.scales;
     a.s_codes = Lr->has_shared ? Lr->shared_w13.codes : nullptr;
-    a.s_scales = Lr->has_shared ? Lr->shared_w13.scales : nullptr;
+    a.s_scales = Lr->has_shared ? (const uint16_t *)Lr->shared_w13.scales : nullptr;
     a.x = x, a.grp = grp, a.pairs = pairs, a.h_hi = h_hi, a.h_lo = h_lo;
     a.H = p.H, a.I = p.I, a.K = p.K, a.T = p.T, a.P = p.P, a.Gmax = p.Gmax, a.mfma_min = W4_MFMA_MIN;
     launch_gw13(a, sm, ev(4), ev(5));
     if ((st = hip_status("grouped w13 launch"))) return st;
     // 4) grouped W2
     GW2Args d{};
-    d.codes = Lr->w2.codes, d.scales = Lr->w2.scales;
+    d.codes = Lr->w2.codes, d.scales = (const uint16_t *)Lr->w2.scales;
     d.s_codes = Lr->has_shared ? Lr->shared_w2.codes : nullptr;
-    d.s_scales = Lr->has_shared ? Lr->shared_w2.scales : nullptr;
+    d.s_scales = Lr->has_shared ? (const uint16_t *)Lr->shared_w2.scales : nullptr;
     d.grp = grp, d.pairs = pairs, d.h_hi = h_hi, d.h_lo = h_lo, d.out = outp;
     d.H = p.H, d.I = p.I, d.K = p.K, d.T = p.T, d.P = p.P, d.Gmax = p.Gmax, d.mfma_min = W4_MFMA_MIN;
     launch_gw2(d, sm, ev(6), ev(7));
@@ -901,6 +937,7 @@ int w4a16_gemv(const w4_matrix *W, const uint16_t *x, int64_t m, uint16_t *y, vo
     (void)hipGetLastError();
     hipStream_t sm = (hipStream_t)stream;
     if (W->format == W4_FMT_E2M1_F16S16) launch_gemv<FMT_E2M1>(W, x, (int)m, y, sm);
+    else if (W->format == W4_FMT_NVFP4_E4M3S16) launch_gemv<FMT_NVFP4>(W, x, (int)m, y, sm);
     else launch_gemv<FMT_INT4>(W, x, (int)m, y, sm);
     return hip_status("gemv launch");
 }
@@ -914,6 +951,7 @@ int w4_dequant_device(const w4_matrix *W, float *out, void *stream) {
     (void)hipGetLastError();
     hipStream_t sm = (hipStream_t)stream;
     if (W->format == W4_FMT_E2M1_F16S16) launch_dequant<FMT_E2M1>(W, out, sm);
+    else if (W->format == W4_FMT_NVFP4_E4M3S16) launch_dequant<FMT_NVFP4>(W, out, sm);
     else launch_dequant<FMT_INT4>(W, out, sm);
     return hip_status("dequant launch");
 }

@@ -59,6 +59,7 @@ class MoEShape:
     tokens: int = 1
     zipf_s: float = 0.0  # > 0: router logit bias -s*ln(rank)
     seed: int = 0
+    fmt: str = "e2m1"  # weight format of the experts: "e2m1", "int4" or "nvfp4"
 
     @property
     def has_shared(self):
@@ -70,7 +71,7 @@ class GemvShape:
     name: str
     n: int
     k: int
-    fmt: str  # "e2m1" or "int4"
+    fmt: str  # "e2m1", "int4" or "nvfp4"
     seed: int = 0
 
 
@@ -78,7 +79,9 @@ TINY_MOE = MoEShape("tiny-moe-h256-e8-k2-i128", 256, 128, 8, 2, 0, 1, 0.0, 0)
 QWEN_MOE_T1 = MoEShape("qwen3.6-35b-a3b-moe-decode-t1", 2048, 512, 256, 8, 512, 1, 0.0, 0)
 GEMV_E2M1 = GemvShape("gemv-e2m1-8192x2048", 8192, 2048, "e2m1", 0)
 GEMV_INT4 = GemvShape("gemv-int4g128-8192x2048", 8192, 2048, "int4", 0)
+GEMV_NVFP4 = GemvShape("gemv-nvfp4-8192x2048", 8192, 2048, "nvfp4", 0)
 QWEN_MOE_T32 = MoEShape("qwen3.6-35b-a3b-moe-batch32-zipf1.1", 2048, 512, 256, 8, 512, 32, 1.1, 0)
+QWEN_MOE_T1_NVFP4 = MoEShape("qwen3.6-35b-a3b-moe-decode-t1-nvfp4", 2048, 512, 256, 8, 512, 1, 0.0, 0, "nvfp4")
 
 
 # --------------------------------------------------------------------------- draws

@@ -11,43 +11,52 @@ from . import synth
 from . import (
     GROUP,
     FORMATS,
+    SCALE_DTYPE,
     MoELayer,
     QMatrix,
-    W4_FMT_E2M1_F16S16,
+    W4_FMT_NVFP4_E4M3S16,
     w4_quantize,
 )
 
 
 def quantize_stack(fmt, gen, groups, n, k):
-    """Quantise `groups` matrices gen(g) -> fp32 [n][k] into stacked host arrays."""
+    """Quantise `groups` matrices gen(g) -> fp32 [n][k] into stacked host arrays:
+    (codes, scales) or, for NVFP4, (codes, scales, global scales fp32 [groups])."""
     codes = np.empty((groups, n, k // 2), dtype=np.uint8)
-    scales = np.empty((groups, n, k // GROUP[fmt]), dtype=np.uint16)
+    scales = np.empty((groups, n, k // GROUP[fmt]), dtype=SCALE_DTYPE[fmt])
+    gsc = np.zeros(groups, dtype=np.float32)
     for g in range(groups):
-        w4_quantize(fmt, gen(g), codes[g], scales[g])
-    return codes, scales
+        r = w4_quantize(fmt, gen(g), codes[g], scales[g])
+        if fmt == W4_FMT_NVFP4_E4M3S16:
+            gsc[g] = r[2]
+    return (codes, scales, gsc) if fmt == W4_FMT_NVFP4_E4M3S16 else (codes, scales)
 
 
-def build_moe_layer(shape, fmt=W4_FMT_E2M1_F16S16, device="cuda"):
-    """Quantise and upload a whole MoE layer of `shape` (a synth.MoEShape)."""
+def upload(fmt, q, device):
+    """QMatrix from the output of quantize_stack / w4_quantize."""
+    return QMatrix.upload(fmt, q[0], q[1], device, global_np=q[2] if len(q) > 2 else None)
+
+
+def build_moe_layer(shape, fmt=None, device="cuda"):
+    """Quantise and upload a whole MoE layer of `shape` (a synth.MoEShape) in the
+    shape's weight format (or `fmt`, a W4_FMT_* tag)."""
     import torch
 
-    c13, s13 = quantize_stack(fmt, lambda e: synth.expert_w13(shape, e), shape.num_experts,
-                              2 * shape.inter, shape.hidden)
-    c2, s2 = quantize_stack(fmt, lambda e: synth.expert_w2(shape, e), shape.num_experts,
-                            shape.hidden, shape.inter)
-    w13 = QMatrix.upload(fmt, c13, s13, device)
-    w2 = QMatrix.upload(fmt, c2, s2, device)
-    del c13, s13, c2, s2
+    fmt = FORMATS[shape.fmt] if fmt is None else fmt
+
+    q13 = quantize_stack(fmt, lambda e: synth.expert_w13(shape, e), shape.num_experts, 2 * shape.inter, shape.hidden)
+    q2 = quantize_stack(fmt, lambda e: synth.expert_w2(shape, e), shape.num_experts, shape.hidden, shape.inter)
+    w13 = upload(fmt, q13, device)
+    w2 = upload(fmt, q2, device)
+    del q13, q2
     router_w = torch.from_numpy(synth.router_weight(shape).view(np.int16)).to(device)
     bias = synth.router_bias(shape)
     router_bias = torch.from_numpy(bias).to(device) if bias is not None else None
     kw = {}
     if shape.has_shared:
-        sc13, ss13 = w4_quantize(fmt, synth.shared_w13(shape))
-        sc2, ss2 = w4_quantize(fmt, synth.shared_w2(shape))
         kw = dict(
-            shared_w13=QMatrix.upload(fmt, sc13, ss13, device),
-            shared_w2=QMatrix.upload(fmt, sc2, ss2, device),
+            shared_w13=upload(fmt, w4_quantize(fmt, synth.shared_w13(shape)), device),
+            shared_w2=upload(fmt, w4_quantize(fmt, synth.shared_w2(shape)), device),
             shared_gate_w=torch.from_numpy(synth.shared_gate_weight(shape).view(np.int16)).to(device),
         )
     return MoELayer(shape.hidden, shape.inter, shape.num_experts, shape.top_k, router_w, w13, w2,
@@ -57,8 +66,7 @@ def build_moe_layer(shape, fmt=W4_FMT_E2M1_F16S16, device="cuda"):
 def build_dense(shape, device="cuda"):
     """Quantise and upload a dense GEMV matrix of `shape` (a synth.GemvShape)."""
     fmt = FORMATS[shape.fmt]
-    codes, scales = w4_quantize(fmt, synth.dense_weight(shape))
-    return QMatrix.upload(fmt, codes, scales, device)
+    return upload(fmt, w4_quantize(fmt, synth.dense_weight(shape)), device)
 
 
 def bf16_tensor(bits, device="cuda"):

@@ -19,6 +19,9 @@
  *          Qwen 3.6 35B-A3B configuration block (hidden 2048, 256 experts, top-8).
  *   [CI]   "cuda_inf" article: "2. INT4 weight quantization" (signed int4, one
  *          scale per group of 128 along K, fp32 accumulate).
+ *   NVFP4 variant: lynn-engine README notes P17/P54 (per-16 E4M3 scales), R5-C0
+ *          (UE4M3 block-16 scales) and P29 (down projection with packed codes,
+ *          scales and a global scale).
  *
  * Conventions (all entry points):
  *   - Status: 0 = W4_OK, negative = error.  Every argument is validated before
@@ -55,7 +58,7 @@ extern "C" {
 #define W4_ERR_UNSUPPORTED (-4)   /* valid request this build does not serve    */
 #define W4_ERR_WORKSPACE (-5)     /* workspace missing or too small             */
 #define W4_ERR_NONFINITE (-6)     /* quantise: Inf or NaN in the input          */
-#define W4_ERR_RANGE (-7)         /* quantise: block scale overflows fp16       */
+#define W4_ERR_RANGE (-7)         /* quantise: block scale overflows its format */
 #define W4_ERR_HIP (-8)           /* a HIP runtime call or launch failed        */
 
 /* ------------------------------------------------------------------ formats */
@@ -65,11 +68,17 @@ extern "C" {
 /* Two's-complement int4 codes in [-8, 7] with one FP16 scale per 128 K
  * elements [CI "2. INT4 weight quantization"]. */
 #define W4_FMT_INT4_F16S128 2
+/* NVFP4: E2M1 codes with one unsigned E4M3 scale byte (OCP E4M3, sign 0, at
+ * most 448) per 16 consecutive K elements and one fp32 global scale per matrix;
+ * element value = code x scale x global. */
+#define W4_FMT_NVFP4_E4M3S16 3
 
 /* Canonical layout, the only one this library reads:
  *   codes  [groups][n][k/2] bytes, element 2j in the low nibble of byte j and
  *          element 2j+1 in the high nibble;
- *   scales [groups][n][k/G] fp16 bit patterns, G = 16 (E2M1) or 128 (int4).
+ *   scales [groups][n][k/G] fp16 bit patterns, G = 16 (E2M1) or 128 (int4);
+ *          NVFP4: [groups][n][k/16] UE4M3 bytes;
+ *   global_scales (NVFP4 only) [groups] fp32.
  * With y = W x, a row is one output element.  A wave streams 1 KiB of one
  * row's codes per 128-bit load (64 lanes x 16 B = 32 elements per lane, two
  * whole E2M1 scale blocks), so this layout already gives 128-bit coalesced
@@ -77,16 +86,19 @@ extern "C" {
 #define W4_LAYOUT_CANONICAL 0
 
 /* A stack of `groups` quantised matrices W[g] of shape [n][k] (y = W x).
- * Requirements: k % 32 == 0 (E2M1) or k % 128 == 0 (int4); codes 16-byte
- * aligned; scales 4-byte aligned; both in device memory for device calls. */
+ * Requirements: k % 32 == 0 (E2M1, NVFP4) or k % 128 == 0 (int4); codes
+ * 16-byte aligned; scales and global_scales 4-byte aligned; all in device
+ * memory for device calls.  global_scales is required for NVFP4 and ignored
+ * (may be NULL) for the other formats. */
 typedef struct w4_matrix {
-    int32_t format;          /* W4_FMT_*                                   */
-    int32_t layout;          /* W4_LAYOUT_*                                */
-    int64_t groups;          /* number of stacked matrices (experts)       */
-    int64_t n;               /* rows per matrix                            */
-    int64_t k;               /* columns = reduction length                 */
-    const uint8_t *codes;    /* packed codes, see the layout above         */
-    const uint16_t *scales;  /* fp16 scale bit patterns                    */
+    int32_t format;              /* W4_FMT_*                                */
+    int32_t layout;              /* W4_LAYOUT_*                             */
+    int64_t groups;              /* number of stacked matrices (experts)    */
+    int64_t n;                   /* rows per matrix                         */
+    int64_t k;                   /* columns = reduction length              */
+    const uint8_t *codes;        /* packed codes, see the layout above      */
+    const void *scales;          /* fp16 bit patterns, or UE4M3 bytes       */
+    const float *global_scales;  /* NVFP4: fp32 [groups]; otherwise unused  */
 } w4_matrix;
 
 /* ------------------------------------------------------------------ errors */
@@ -99,15 +111,16 @@ const char *w4_version(void);
 
 /* ------------------------------------------------------------------ sizes (host) */
 /* Bytes of packed codes / scales for `groups` matrices of [n][k] in a layout:
- * codes = groups*n*k/2, scales = groups*n*(k/G)*2.  8192x2048 E2M1 gives
- * 8,388,608 + 2,097,152 = 10,485,760 B = 10.00 MiB [LE stage P1].
+ * codes = groups*n*k/2, scales = groups*n*(k/G)*2 (NVFP4: groups*n*(k/16)).
+ * 8192x2048 E2M1 gives 8,388,608 + 2,097,152 = 10,485,760 B = 10.00 MiB
+ * [LE stage P1]; NVFP4 8,388,608 + 1,048,576 = 9.00 MiB (+ 4 B global).
  * Returns 0 for an unknown format/layout or a k the format does not accept. */
 size_t w4_codes_bytes(int32_t format, int32_t layout, int64_t groups, int64_t n, int64_t k);
 size_t w4_scales_bytes(int32_t format, int32_t layout, int64_t groups, int64_t n, int64_t k);
 
 /* ------------------------------------------------------------------ quantise (host) */
-/* Quantise host fp32 weights w[n][k] (row-major) into canonical codes
- * [n][k/2] and fp16 scales [n][k/G] (host buffers of w4_codes_bytes /
+/* Quantise host fp32 weights w[n][k] (row-major, one matrix) into canonical
+ * codes [n][k/2] and scales [n][k/G] (host buffers of w4_codes_bytes /
  * w4_scales_bytes with groups = 1).  Offline step before upload [LE stage P1;
  * CI "2. INT4 weight quantization"].  Per block of G elements:
  *   scale = round-to-nearest-even fp16 of (fp32 absmax / 6)   (E2M1)
@@ -116,10 +129,16 @@ size_t w4_scales_bytes(int32_t format, int32_t layout, int64_t groups, int64_t n
  *           the even code, saturating at +-6; int4: round half to even, clip to
  *           [-8, 7]; an all-zero block has scale 0 and zero codes; a value that
  *           rounds to magnitude zero is encoded as +0.
+ * NVFP4 (the pages name the scale types, not a recipe; this is the common one):
+ *   g = fp32(absmax(w)) / 2688 (= 6 x 448), written to *global_scale;
+ *   block scale = UE4M3 round-to-nearest-even of fp32(fp32(block absmax) / 6) / g,
+ *   saturating at 448; code = nearest E2M1 value to fp32(w) / fp32(scale x g),
+ *   ties to even, +0 for zero; an all-zero matrix has g = 0.
+ * global_scale may be NULL for the FP16-scale formats.
  * Errors: W4_ERR_NONFINITE (Inf/NaN input), W4_ERR_RANGE (a block scale would
  * overflow fp16), W4_ERR_INVALID_ARG, W4_ERR_LAYOUT.  Synchronous, thread-safe. */
 int w4_quantize(int32_t format, const float *w, int64_t n, int64_t k,
-                uint8_t *codes, uint16_t *scales);
+                uint8_t *codes, void *scales, float *global_scale);
 
 /* Host helpers between one-nibble-per-byte codes [n][k] (values 0..15) and the
  * packed canonical codes [n][k/2] (low nibble = even element).  Exact inverses
@@ -131,7 +150,8 @@ int w4_unpack_nibbles(const uint8_t *packed, int64_t n, int64_t k, uint8_t *nibb
 /* y[m][n] = x[m][k] . W[n][k]^T for the single matrix W (groups must be 1):
  * the packed W4A16 matvec of [LE stage P1] (m = 1 for decode).  Codes are
  * dequantised in registers (exactly: code value x fp32(scale)), products are
- * accumulated in fp32 and each output is rounded once to bf16 (nearest even).
+ * accumulated in fp32 (NVFP4: the row sum is multiplied by the global scale)
+ * and each output is rounded once to bf16 (nearest even).
  *   x: device bf16 [m][k], 16-byte aligned;  y: device bf16 [m][n].
  * Supports 1 <= m <= 64.  Errors: W4_ERR_INVALID_ARG, _LAYOUT, _ALIGNMENT,
  * _UNSUPPORTED, _HIP. */
@@ -139,7 +159,9 @@ int w4a16_gemv(const w4_matrix *W, const uint16_t *x, int64_t m, uint16_t *y, vo
 
 /* Test hook: dequantise every element of W (all groups) to fp32
  * out[groups][n][k] on the device with the same in-register decode the GEMV
- * and MoE kernels use.  Bit-exact by construction (each product is exact). */
+ * and MoE kernels use.  Bit-exact by construction (each product is exact;
+ * NVFP4: code x scale is exact and its product with the global scale is
+ * rounded once). */
 int w4_dequant_device(const w4_matrix *W, float *out, void *stream);
 
 /* ------------------------------------------------------------------ MoE layer */
@@ -153,7 +175,8 @@ int w4_dequant_device(const w4_matrix *W, float *out, void *stream);
  *     shared_w2   groups = 1, n = H, k = shared_inter
  *     shared_gate_w bf16 [H]: sigma = sigmoid(shared_gate_w . x)
  * This build requires shared_inter == inter and H % 64 == 0; all experts and
- * the shared expert use one format. */
+ * the shared expert use one format (NVFP4: one global scale per expert matrix,
+ * applied to the gate/up sums and to the down sums). */
 typedef struct moe_w4a16_layer {
     int64_t hidden;              /* H */
     int64_t inter;               /* I (expert intermediate) */

@@ -108,6 +108,46 @@ def test_quantizer_errors():
     assert e.value.status == w4.W4_ERR_LAYOUT
 
 
+def test_quantizer_nvfp4_matches_oracle():
+    rng = np.random.default_rng(22)
+    mids = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.0] * 2, dtype=np.float32)
+    cases = [
+        (rng.standard_normal((64, 256)) * 0.02).astype(np.float32),
+        # blocks far below the matrix maximum: subnormal and zero UE4M3 scales
+        np.concatenate([(rng.standard_normal((4, 64)) * s).astype(np.float32) for s in (1.0, 1e-3, 1e-5, 1e-9)]),
+        np.zeros((3, 32), dtype=np.float32),
+        # g = 1 (absmax 2688) and a block whose scale is exactly 1.0: ratios on every
+        # E2M1 midpoint, and one ulp around them
+        np.stack([np.concatenate([np.full(16, 2688, np.float32), mids]),
+                  np.concatenate([np.full(16, 2688, np.float32), np.nextafter(mids, np.float32(np.inf))]),
+                  np.concatenate([np.full(16, 2688, np.float32), -np.nextafter(mids, np.float32(0))])]),
+        synth.expert_w13(synth.QWEN_MOE_T1, 3),
+    ]
+    for w in cases:
+        c_lib, s_lib, g_lib = w4.w4_quantize(w4.W4_FMT_NVFP4_E4M3S16, w)
+        c_or, s_or, g_or = oracle.quantize(F.FMT_NVFP4, w)
+        assert g_lib == g_or
+        assert np.array_equal(s_lib, s_or)
+        assert np.array_equal(c_lib, c_or)
+
+
+def test_quantizer_nvfp4_golden_and_sizes():
+    import test_oracle_nvfp4 as T
+    for m in T._golden_matrices():
+        c, s, g = w4.w4_quantize(w4.W4_FMT_NVFP4_E4M3S16, m["w"][None])
+        assert float(g) == m["g"] and np.array_equal(s[0], m["scales"]), m["name"]
+        assert np.array_equal(w4.w4_unpack_nibbles(c)[0], m["codes"]), m["name"]
+    fmt = w4.W4_FMT_NVFP4_E4M3S16
+    assert w4.w4_codes_bytes(fmt, 1, 8192, 2048) + w4.w4_scales_bytes(fmt, 1, 8192, 2048) == 9 * 2 ** 20
+    assert w4.w4_scales_bytes(fmt, 2, 3, 64) == oracle.scales_bytes(F.FMT_NVFP4, 2, 3, 64) == 24
+    # the global scale output is required for NVFP4
+    w = np.ones((1, 32), np.float32)
+    c = np.empty((1, 16), np.uint8)
+    sb = np.empty((1, 2), np.uint8)
+    st = w4.lib().w4_quantize(fmt, w.ctypes.data, 1, 32, c.ctypes.data, sb.ctypes.data, None)
+    assert st == w4.W4_ERR_INVALID_ARG
+
+
 def test_pack_unpack_all_bytes_and_oracle():
     b = np.arange(256, dtype=np.uint8).reshape(4, 64)
     nib = w4.w4_unpack_nibbles(b)
@@ -120,8 +160,8 @@ def test_pack_unpack_all_bytes_and_oracle():
 # ---------------------------------------------------------------- device entry validation
 
 
-def _mat(fmt=w4.W4_FMT_E2M1_F16S16, layout=0, groups=1, n=64, k=256, codes=4096, scales=8192):
-    return w4.W4Matrix(fmt, layout, groups, n, k, codes, scales)
+def _mat(fmt=w4.W4_FMT_E2M1_F16S16, layout=0, groups=1, n=64, k=256, codes=4096, scales=8192, gsc=None):
+    return w4.W4Matrix(fmt, layout, groups, n, k, codes, scales, gsc)
 
 
 def _gemv(W, x=1 << 20, m=1, y=1 << 21):
@@ -143,6 +183,10 @@ def test_gemv_validation_returns_before_launch():
     assert _gemv(_mat(), x=0) == w4.W4_ERR_INVALID_ARG
     assert "x not 16-byte aligned" in w4.w4_last_error() or True
     assert w4.lib().w4a16_gemv(None, 1 << 20, 1, 1 << 21, 0) == w4.W4_ERR_INVALID_ARG
+    nv = w4.W4_FMT_NVFP4_E4M3S16
+    assert _gemv(_mat(fmt=nv)) == w4.W4_ERR_INVALID_ARG          # NVFP4 without global scales
+    assert _gemv(_mat(fmt=nv, gsc=(1 << 23) + 2)) == w4.W4_ERR_ALIGNMENT
+    assert _gemv(_mat(fmt=nv, k=48, gsc=1 << 23)) == w4.W4_ERR_INVALID_ARG
     assert w4.lib().w4_dequant_device(C.byref(_mat()), 0, 0) == w4.W4_ERR_INVALID_ARG
 
 
