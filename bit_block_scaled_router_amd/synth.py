@@ -80,6 +80,8 @@ QWEN_MOE_T1 = MoEShape("qwen3.6-35b-a3b-moe-decode-t1", 2048, 512, 256, 8, 512, 
 GEMV_E2M1 = GemvShape("gemv-e2m1-8192x2048", 8192, 2048, "e2m1", 0)
 GEMV_INT4 = GemvShape("gemv-int4g128-8192x2048", 8192, 2048, "int4", 0)
 GEMV_NVFP4 = GemvShape("gemv-nvfp4-8192x2048", 8192, 2048, "nvfp4", 0)
+# lm_head-sized projection (vocabulary 248,320 x hidden 2048): 318 MB packed E2M1
+GEMV_LMHEAD = GemvShape("gemv-e2m1-lmhead-248320x2048", 248320, 2048, "e2m1", 0)
 QWEN_MOE_T32 = MoEShape("qwen3.6-35b-a3b-moe-batch32-zipf1.1", 2048, 512, 256, 8, 512, 32, 1.1, 0)
 QWEN_MOE_T1_NVFP4 = MoEShape("qwen3.6-35b-a3b-moe-decode-t1-nvfp4", 2048, 512, 256, 8, 512, 1, 0.0, 0, "nvfp4")
 

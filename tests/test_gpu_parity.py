@@ -260,3 +260,22 @@ def test_moe_full_batch32_zipf():
     y1 = w4.moe_w4a16_forward(dev_layer, x)
     y2 = w4.moe_w4a16_forward(dev_layer, x)
     assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+
+
+def test_gemv_lmhead_sampled_rows():
+    """The lm_head-sized projection (248,320 x 2048, 318 MB packed) in the launch
+    configuration bench.py times, checked on sampled rows (the oracle computes rows
+    independently: the first and last 256 and 2,048 random ones)."""
+    shape = synth.GEMV_LMHEAD
+    print(f"gemv {shape.name}", flush=True)
+    w = synth.dense_weight(shape)
+    codes, scales = w4.w4_quantize(w4.W4_FMT_E2M1_F16S16, w)
+    W = _upload(w4.W4_FMT_E2M1_F16S16, codes, scales)
+    del codes, scales
+    x = synth.dense_x(shape)
+    got = wl.bf16_bits(w4.w4a16_gemv(W, wl.bf16_tensor(x)))
+    rng = np.random.default_rng(17)
+    rows = np.unique(np.concatenate([np.arange(256), np.arange(shape.n - 256, shape.n),
+                                     rng.choice(shape.n, 2048, replace=False)]))
+    ref = oracle.gemv(F.FMT_E2M1, *oracle.quantize(F.FMT_E2M1, w[rows]), x)
+    assert_bf16_close(got[rows], ref, shape.name)
