@@ -28,6 +28,7 @@ from .formats import (  # noqa: F401
     FMT_E2M1,
     FMT_INT4,
     FMT_NVFP4,
+    FMT_BF16,
     E4M3_MAX,
     bf16_bits_to_f64,
     f64_to_bf16_bits,

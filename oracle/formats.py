@@ -57,6 +57,7 @@ import numpy as np
 FMT_E2M1 = 1  # E2M1 codes, FP16 scale per 16 K elements
 FMT_INT4 = 2  # two's-complement int4 codes, FP16 scale per 128 K elements
 FMT_NVFP4 = 3  # E2M1 codes, UE4M3 scale per 16 K elements, fp32 scale per matrix
+FMT_BF16 = 4  # unquantised bf16 weights (the shared expert's production format in the pages)
 
 E2M1_GROUP = 16
 INT4_GROUP = 128
@@ -263,7 +264,10 @@ def quantize(fmt, w):
 
     E2M1 / int4: (packed codes [N][K/2] uint8, scale bits [N][K/G] uint16).
     NVFP4: (packed codes, UE4M3 scale bytes [N][K/16] uint8, global scale fp32).
+    bf16: (bf16 bits [N][K] uint16,), each weight rounded to nearest even.
     """
+    if fmt == FMT_BF16:
+        return (f64_to_bf16_bits(np.asarray(w, dtype=np.float32).astype(np.float64)),)
     if fmt == FMT_E2M1:
         c, s = quantize_e2m1(w)
     elif fmt == FMT_INT4:
@@ -314,7 +318,7 @@ def scales_bytes(fmt, groups, n, k):
 # --------------------------------------------------------------------------- dequant
 
 
-def dequant(fmt, packed, scale_bits, gscale=None):
+def dequant(fmt, packed, scale_bits=None, gscale=None):
     """Canonical codes [N][K/2] + block scales [N][K/G] -> fp32 [N][K].
 
     Each product value(code) * fp32(scale) is exact in fp32: an E2M1 value has at
@@ -324,6 +328,8 @@ def dequant(fmt, packed, scale_bits, gscale=None):
     value(code) * value(scale) has at most 6 significant bits and is exact; the
     element is that product times g, rounded once to fp32.
     """
+    if fmt == FMT_BF16:  # packed = bf16 bits [N][K]; exact in fp32
+        return bf16_bits_to_f64(packed).astype(np.float32)
     g = group_size(fmt)
     nib = unpack_nibbles(packed)
     vals = _decode(fmt, nib).astype(np.float32)

@@ -136,12 +136,15 @@ class MoELayer:
       shared_gate_w bf16 bits [H] or None
     The w13/w2 fields may be callables e -> (codes, scales) so that a test can
     quantise only the experts a token selects.  For NVFP4 every (codes, scales)
-    pair carries a third element, the global scale (stacked: fp32 [E]).
+    pair carries a third element, the global scale (stacked: fp32 [E]).  The
+    shared expert may use another format (shared_fmt; FMT_BF16: 1-tuples of
+    bf16 bits, the pages' production choice for it).
     """
 
     def __init__(self, fmt, hidden, inter, num_experts, top_k, router_w, w13, w2,
-                 router_bias=None, shared_w13=None, shared_w2=None, shared_gate_w=None):
+                 router_bias=None, shared_w13=None, shared_w2=None, shared_gate_w=None, shared_fmt=None):
         self.fmt = fmt
+        self.shared_fmt = fmt if shared_fmt is None else shared_fmt
         self.hidden = hidden
         self.inter = inter
         self.num_experts = num_experts
@@ -172,7 +175,8 @@ class MoELayer:
 
     def shared(self):
         if "shared" not in self._cache:
-            self._cache["shared"] = (dequant(self.fmt, *self.shared_w13), dequant(self.fmt, *self.shared_w2))
+            self._cache["shared"] = (dequant(self.shared_fmt, *self.shared_w13),
+                                     dequant(self.shared_fmt, *self.shared_w2))
         return self._cache["shared"]
 
 

@@ -181,6 +181,35 @@ def test_shared_expert_adds_sigmoid_gated_dense_swiglu():
     np.testing.assert_allclose(out[0], routed + sig * shared, rtol=1e-12, atol=1e-15)
 
 
+def test_bf16_shared_expert_is_exact_bf16_swiglu():
+    """A bf16 shared expert (the pages' production format for it, lynn-engine README
+    P15/P37) adds sigma times the dense SwiGLU on the bf16-rounded weights."""
+    hidden, inter = 128, 128
+    shape, layer4 = _small_layer(F.FMT_E2M1, hidden, inter, 1, 1, True, 6)
+    sw13, sw2 = synth.shared_w13(shape), synth.shared_w2(shape)
+    layer = ops.MoELayer(F.FMT_E2M1, hidden, inter, 1, 1, layer4.router_w, layer4._w13, layer4._w2,
+                         shared_w13=oracle.quantize(F.FMT_BF16, sw13), shared_w2=oracle.quantize(F.FMT_BF16, sw2),
+                         shared_gate_w=layer4.shared_gate_w, shared_fmt=F.FMT_BF16)
+    x = synth.x_row(0, hidden, 2)
+    out, _, _ = ops.moe_forward(layer, x)
+    c13, s13 = layer._w13
+    c2, s2 = layer._w2
+    routed = _dense_swiglu_via_gemv(F.FMT_E2M1, (c13[0], s13[0]), (c2[0], s2[0]), x, inter)
+    # bf16 weights: fp32 -> bf16 round to nearest even, written out bit by bit
+    def rne(a):
+        u = a.astype(np.float32).view(np.uint32).astype(np.uint64)
+        return (((u + 0x7FFF + ((u >> 16) & 1)) >> 16) << 16).astype(np.uint32).view(np.float32).astype(np.float64)
+    xf = oracle.bf16_bits_to_f64(x)
+    gu = rne(sw13) @ xf
+    h = gu[:inter] * expit(gu[:inter]) * gu[inter:]
+    shared = rne(sw2) @ h
+    sig = expit(oracle.bf16_bits_to_f64(layer.shared_gate_w) @ xf)
+    np.testing.assert_allclose(out[0], routed + sig * shared, rtol=1e-12, atol=1e-15)
+    # and it differs from the 4-bit shared expert by the quantisation error only
+    out4, _, _ = ops.moe_forward(layer4, x)
+    assert not np.allclose(out4, out, rtol=1e-6) and np.allclose(out4, out, rtol=0.2, atol=0.05)
+
+
 def test_zero_input_gives_zero_output():
     _, layer = _small_layer(F.FMT_E2M1, 256, 128, 8, 2, True, 5)
     out, _, _ = ops.moe_forward(layer, np.zeros(256, dtype=np.uint16))
