@@ -155,7 +155,8 @@ def clone_layer(w4, layer):
     """A deep copy of a device MoE layer (new addresses, same contents)."""
     def cq(q):
         g = q.global_scales.clone() if q.global_scales is not None else None
-        return w4.QMatrix(q.fmt, q.groups, q.n, q.k, q.codes.clone(), q.scales.clone(), g)
+        sc = q.scales.clone() if q.scales is not None else None
+        return w4.QMatrix(q.fmt, q.groups, q.n, q.k, q.codes.clone(), sc, g)
 
     kw = {}
     if layer.has_shared:
@@ -171,6 +172,8 @@ def weight_bytes(fmt, n, k):
     128; NVFP4: one UE4M3 byte per 16 plus a 4-byte global scale)."""
     if fmt == "nvfp4":
         return n * k // 2 + n * k // 16 + 4
+    if fmt == "bf16":
+        return n * k * 2
     return n * k // 2 + n * k // (128 if fmt == "int4" else 16) * 2
 
 
@@ -182,9 +185,10 @@ def moe_bytes(shape, distinct):
     bf16 [H]; x and y bf16 [T][H]."""
     H, I, E, T = shape.hidden, shape.inter, shape.num_experts, shape.tokens
     per_expert = weight_bytes(shape.fmt, 2 * I, H) + weight_bytes(shape.fmt, H, I)
+    sfmt = shape.shared_fmt or shape.fmt
     b = E * H * 2 + distinct * per_expert + 2 * T * H * 2
     if shape.has_shared:
-        b += per_expert + H * 2
+        b += weight_bytes(sfmt, 2 * I, H) + weight_bytes(sfmt, H, I) + H * 2
     return b
 
 
@@ -199,13 +203,17 @@ def stage_bytes(shape, distinct, n_stages=3):
     S = K + (1 if shape.has_shared else 0)
     w13 = weight_bytes(shape.fmt, 2 * I, H)
     w2 = weight_bytes(shape.fmt, H, I)
-    nexp = distinct + (1 if shape.has_shared else 0)
+    sfmt = shape.shared_fmt or shape.fmt
+    sh = 1 if shape.has_shared else 0
+    # the shared expert's matrices replace one routed expert's in the sums below
+    dw13, dw2 = sh * (weight_bytes(sfmt, 2 * I, H) - w13), sh * (weight_bytes(sfmt, H, I) - w2)
+    nexp = distinct + sh
     router = E * H * 2 + (H * 2 if shape.has_shared else 0) + T * H * 2 + T * (E + 1) * 4
     if n_stages == 3:
         return {
             "k_router": router,
-            "k_moe_w13": nexp * w13 + T * H * 2 + T * E * 4 + T * S * I * 4,
-            "k_moe_down": nexp * w2 + T * S * I * 4 + T * K * 8 + T * H * 2,
+            "k_moe_w13": nexp * w13 + dw13 + T * H * 2 + T * E * 4 + T * S * I * 4,
+            "k_moe_down": nexp * w2 + dw2 + T * S * I * 4 + T * K * 8 + T * H * 2,
         }
     rows = T * K + T  # routed pairs + shared rows
     return {
@@ -242,14 +250,16 @@ def cpu_baseline_moe(shape, tokens, reps):
     for t in range(tokens):
         ids, _ = ops.route(ops.router_logits(rw, xs[t], bias), shape.top_k)
         need.update(int(e) for e in ids)
-    fmt = {"e2m1": oracle.FMT_E2M1, "int4": oracle.FMT_INT4, "nvfp4": oracle.FMT_NVFP4}[shape.fmt]
+    ofmts = {"e2m1": oracle.FMT_E2M1, "int4": oracle.FMT_INT4, "nvfp4": oracle.FMT_NVFP4, "bf16": oracle.FMT_BF16}
+    fmt = ofmts[shape.fmt]
+    sfmt = ofmts[shape.shared_fmt] if shape.shared_fmt else fmt
     q13 = {e: oracle.quantize(fmt, synth.expert_w13(shape, e)) for e in need}
     q2 = {e: oracle.quantize(fmt, synth.expert_w2(shape, e)) for e in need}
     kw = {}
     if shape.has_shared:
-        kw = dict(shared_w13=oracle.quantize(fmt, synth.shared_w13(shape)),
-                  shared_w2=oracle.quantize(fmt, synth.shared_w2(shape)),
-                  shared_gate_w=synth.shared_gate_weight(shape))
+        kw = dict(shared_w13=oracle.quantize(sfmt, synth.shared_w13(shape)),
+                  shared_w2=oracle.quantize(sfmt, synth.shared_w2(shape)),
+                  shared_gate_w=synth.shared_gate_weight(shape), shared_fmt=sfmt)
     times = []
     for _ in range(reps):
         layer = ops.MoELayer(fmt, shape.hidden, shape.inter, shape.num_experts, shape.top_k, rw,
@@ -297,7 +307,7 @@ def cpu_baseline_gemv(shape, reps, max_rows=8192):
 
 def run_moe(args, torch, w4, wl, synth):
     shape = {"qwen-t1": synth.QWEN_MOE_T1, "qwen-t32": synth.QWEN_MOE_T32, "tiny": synth.TINY_MOE,
-             "qwen-t1-nvfp4": synth.QWEN_MOE_T1_NVFP4}[args.workload]
+             "qwen-t1-nvfp4": synth.QWEN_MOE_T1_NVFP4, "qwen-t1-bf16shared": synth.QWEN_MOE_T1_BF16SH}[args.workload]
     T = shape.tokens
     print(f"[bench] building {shape.name} ({args.replicas} replicas)", file=sys.stderr, flush=True)
     base = wl.build_moe_layer(shape, device="cuda")
@@ -392,7 +402,8 @@ def run_moe(args, torch, w4, wl, synth):
             "top_k": shape.top_k, "inter": shape.inter, "shared_inter": shape.shared_inter,
             "tokens_per_step": T, "zipf_s": shape.zipf_s, "weights": {"e2m1": "E2M1 codes + FP16 scale per 16",
                         "nvfp4": "E2M1 codes + UE4M3 scale per 16 + fp32 scale per matrix",
-                        "int4": "int4 codes + FP16 scale per 128"}[shape.fmt],
+                        "int4": "int4 codes + FP16 scale per 128"}[shape.fmt]
+                       + (", shared expert bf16" if shape.shared_fmt == "bf16" else ""),
             "activations": "bf16", "accumulate": "fp32", "layer_replicas": R, "token_pool": P,
             "mean_distinct_experts": d_mean, "timing": "HIP graph replay of the K steps",
         },
@@ -467,7 +478,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="qwen-t1",
                     choices=["qwen-t1", "qwen-t32", "tiny", "gemv-e2m1", "gemv-int4", "qwen-t1-nvfp4", "gemv-nvfp4",
-                             "gemv-lmhead"])
+                             "gemv-lmhead", "qwen-t1-bf16shared"])
     ap.add_argument("--replicas", type=int, default=0, help="weight replicas (0 = workload default)")
     ap.add_argument("--pool", type=int, default=64, help="token pool (MoE workloads)")
     ap.add_argument("--cpu-tokens", type=int, default=1)
@@ -483,7 +494,7 @@ def main():
         names = {"qwen-t1": synth.QWEN_MOE_T1, "qwen-t32": synth.QWEN_MOE_T32, "tiny": synth.TINY_MOE,
                  "gemv-e2m1": synth.GEMV_E2M1, "gemv-int4": synth.GEMV_INT4,
                  "qwen-t1-nvfp4": synth.QWEN_MOE_T1_NVFP4, "gemv-nvfp4": synth.GEMV_NVFP4,
-                 "gemv-lmhead": synth.GEMV_LMHEAD}
+                 "gemv-lmhead": synth.GEMV_LMHEAD, "qwen-t1-bf16shared": synth.QWEN_MOE_T1_BF16SH}
         ingest_counters(args.ingest_counters, names[args.workload].name)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:

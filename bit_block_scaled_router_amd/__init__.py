@@ -24,6 +24,7 @@ from ._lib import (  # noqa: F401
     W4_FMT_E2M1_F16S16,
     W4_FMT_INT4_F16S128,
     W4_FMT_NVFP4_E4M3S16,
+    W4_FMT_BF16,
     W4_LAYOUT_CANONICAL,
     W4_OK,
     MoELayerDesc,
@@ -34,7 +35,8 @@ from ._lib import (  # noqa: F401
 )
 
 GROUP = {W4_FMT_E2M1_F16S16: 16, W4_FMT_INT4_F16S128: 128, W4_FMT_NVFP4_E4M3S16: 16}
-FORMATS = {"e2m1": W4_FMT_E2M1_F16S16, "int4": W4_FMT_INT4_F16S128, "nvfp4": W4_FMT_NVFP4_E4M3S16}
+FORMATS = {"e2m1": W4_FMT_E2M1_F16S16, "int4": W4_FMT_INT4_F16S128, "nvfp4": W4_FMT_NVFP4_E4M3S16,
+           "bf16": W4_FMT_BF16}
 # numpy dtype of one block scale per format (FP16 bit patterns or UE4M3 bytes)
 SCALE_DTYPE = {W4_FMT_E2M1_F16S16: np.uint16, W4_FMT_INT4_F16S128: np.uint16, W4_FMT_NVFP4_E4M3S16: np.uint8}
 
@@ -86,11 +88,16 @@ def w4_quantize(fmt, w, codes=None, scales=None):
     """Quantise host fp32 w[n][k] (one matrix).
 
     Returns (codes uint8 [n][k/2], scales [n][k/G]): FP16 bit patterns (uint16)
-    for E2M1/int4; for NVFP4 (codes, UE4M3 bytes uint8, global scale float)."""
+    for E2M1/int4; for NVFP4 (codes, UE4M3 bytes uint8, global scale float);
+    for bf16 (bf16 bits uint16 [n][k],)."""
     w = np.ascontiguousarray(w, dtype=np.float32)
     if w.ndim != 2:
         raise ValueError("w must be 2-D")
     n, k = w.shape
+    if fmt == W4_FMT_BF16:
+        out = np.empty((n, k), dtype=np.uint16) if codes is None else codes
+        check(lib().w4_quantize(fmt, _ptr(w), n, k, _ptr(out), None, None))
+        return (out,)
     g = GROUP.get(fmt, 1)
     if codes is None:
         codes = np.empty((n, k // 2), dtype=np.uint8)
@@ -131,6 +138,15 @@ class QMatrix:
         # fp32 [groups] global scales (NVFP4)
         self.codes, self.scales, self.global_scales = codes, scales, global_scales
         self.desc = W4Matrix(fmt, layout, groups, n, k, _ptr(codes), _ptr(scales), _ptr(global_scales))
+
+    @classmethod
+    def upload_bf16(cls, bits_np, device="cuda"):
+        """bf16 bits [G][n][k] (or [n][k]) -> a W4_FMT_BF16 matrix (no scales)."""
+        b = np.ascontiguousarray(bits_np, dtype=np.uint16)
+        if b.ndim == 2:
+            b = b[None]
+        groups, n, k = b.shape
+        return cls(W4_FMT_BF16, groups, n, k, _torch().from_numpy(b.view(np.int16)).to(device), None)
 
     @classmethod
     def upload(cls, fmt, codes_np, scales_np, device="cuda", global_np=None):

@@ -247,6 +247,38 @@ __device__ __forceinline__ f32x2 block_scales2(uint32_t sc) {
     }
 }
 
+// 32 bf16 weights (4 x 16 bytes) of one lane against its bf16 activations
+// (the unpermuted slice: load_xslice without prep_xslice).
+template <int FMT>
+__device__ __forceinline__ float bf16w_dot_bf16(const uint4 *w, const XSlice<FMT> &xs, float acc) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        acc = dot2(as_bf16x2(w[i].x), xs.v[i].x, acc);
+        acc = dot2(as_bf16x2(w[i].y), xs.v[i].y, acc);
+        acc = dot2(as_bf16x2(w[i].z), xs.v[i].z, acc);
+        acc = dot2(as_bf16x2(w[i].w), xs.v[i].w, acc);
+    }
+    return acc;
+}
+
+// 32 bf16 weights of one lane against its 32 fp32 activations h[8] (float4 q
+// holds elements 4q..4q+3).
+__device__ __forceinline__ float bf16w_dot_f32(const uint4 *w, const float4 *h, float acc) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t d[4] = {w[i].x, w[i].y, w[i].z, w[i].w};
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const int e = 8 * i + 2 * m;  // elements e, e+1
+            const float4 hq = h[e >> 2];
+            const float h0 = (e & 3) ? hq.z : hq.x, h1 = (e & 3) ? hq.w : hq.y;
+            acc = fmaf(__uint_as_float(d[m] << 16), h0, acc);
+            acc = fmaf(__uint_as_float(d[m] & 0xFFFF0000u), h1, acc);
+        }
+    }
+    return acc;
+}
+
 // One lane's 32 elements (16 bytes of codes + its scales) against bf16
 // activations, added to acc in a fixed order.  E2M1: the dword `sc` holds the
 // two FP16 scales of the lane's two blocks (low half = first block).  int4: the

@@ -33,6 +33,7 @@ int group_of(int32_t format) {
     case W4_FMT_E2M1_F16S16: return 16;
     case W4_FMT_INT4_F16S128: return 128;
     case W4_FMT_NVFP4_E4M3S16: return 16;
+    case W4_FMT_BF16: return 32;  // no scale blocks; k must be a multiple of 32
     default: return 0;
     }
 }
@@ -177,11 +178,13 @@ const char *w4_version(void) { return "w4moe 0.1 gfx950"; }
 
 size_t w4_codes_bytes(int32_t format, int32_t layout, int64_t groups, int64_t n, int64_t k) {
     if (check_shape(format, layout, groups, n, k) != W4_OK) return 0;
+    if (format == W4_FMT_BF16) return (size_t)groups * (size_t)n * (size_t)k * 2;
     return (size_t)groups * (size_t)n * (size_t)(k / 2);
 }
 
 size_t w4_scales_bytes(int32_t format, int32_t layout, int64_t groups, int64_t n, int64_t k) {
     if (check_shape(format, layout, groups, n, k) != W4_OK) return 0;
+    if (format == W4_FMT_BF16) return 0;
     const size_t bytes = format == W4_FMT_NVFP4_E4M3S16 ? 1 : 2;
     return (size_t)groups * (size_t)n * (size_t)(k / group_of(format)) * bytes;
 }
@@ -191,6 +194,18 @@ int w4_quantize(int32_t format, const float *w, int64_t n, int64_t k, uint8_t *c
     clear_error();
     int st = check_shape(format, W4_LAYOUT_CANONICAL, 1, n, k);
     if (st) return st;
+    if (format == W4_FMT_BF16) {  // plain round to nearest even, no scales
+        if (!w || !codes) return fail(W4_ERR_INVALID_ARG, "null pointer");
+        for (int64_t i = 0; i < n * k; ++i)
+            if (!std::isfinite(w[i])) return fail(W4_ERR_NONFINITE, "non-finite weight at index %lld", (long long)i);
+        uint16_t *out = reinterpret_cast<uint16_t *>(codes);
+        for (int64_t i = 0; i < n * k; ++i) {
+            uint32_t u;
+            std::memcpy(&u, &w[i], 4);
+            out[i] = (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+        }
+        return W4_OK;
+    }
     if (!w || !codes || !scales) return fail(W4_ERR_INVALID_ARG, "null pointer");
     const bool nv = format == W4_FMT_NVFP4_E4M3S16;
     if (nv && !global_scale) return fail(W4_ERR_INVALID_ARG, "NVFP4 needs a global_scale output");

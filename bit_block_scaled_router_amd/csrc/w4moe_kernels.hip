@@ -204,6 +204,7 @@ struct W13Args {
     const uint8_t *s_codes;       // shared W13 [2I][H/2] (or null)
     const uint8_t *s_scales;
     const float *gs, *s_gs;       // NVFP4 global scales: routed [E], shared [1]
+    int s_bf16;                   // shared expert in bf16 (s_codes = bf16 [2I][H])
     const uint16_t *x;            // [T][H]
     const float *logits;          // [T][lstride] (routed mode)
     const float *bias;            // [E] or null
@@ -231,8 +232,10 @@ __device__ __forceinline__ int h_index(int i, int L2) {
 // slot): block b covers tiles [tb*WPB, tb*WPB + WPB) of slot j of token t.  For
 // a routed slot, wave 0 of the block ranks the experts once and publishes the
 // ids through LDS; the block's writer (token t, slot 0, first tile block) also
-// stores the routing weights for the down kernel and the caller.
-template <int FMT, int L, int RT, int PL>
+// stores the routing weights for the down kernel and the caller.  SBF: the
+// layer's shared expert is bf16 (its slot streams bf16 rows; a separate
+// instantiation so that 4-bit-only layers keep the smaller register budget).
+template <int FMT, int L, int RT, int PL, bool SBF>
 __global__ __launch_bounds__(1024) void k_moe_w13(W13Args a) {
     constexpr int RG = 64 / L;
     __shared__ int s_ids[16];
@@ -309,7 +312,35 @@ __global__ __launch_bounds__(1024) void k_moe_w13(W13Args a) {
     float ag[RT], au[RT];
 #pragma unroll
     for (int r = 0; r < RT; ++r) ag[r] = au[r] = 0.f;
-    for (int s = 0; s < ks; ++s) {
+    const bool sbf = SBF && j == a.K;  // bf16 shared expert slot (uniform per block)
+    if (sbf) {
+        const uint32_t rowb = (uint32_t)H * 2u;
+        const Buf wb = make_buf(cbase, (uint32_t)(2 * I) * rowb);
+        for (int s = 0; s < ks; ++s) {
+            const int k0 = 32 * (L * s + lk);
+            const bool kv = k0 < H;
+            XSlice<FMT> xs;
+            if (s == 0) xs = xs0;
+            else load_xslice<FMT>(xs, xb, kv ? (uint32_t)k0 * 2u : OOB);
+            uint4 wg[RT][4], wu[RT][4];
+#pragma unroll
+            for (int r = 0; r < RT; ++r) {
+                const int i = i0 + r * RG + rsub;
+                const bool v = kv && i < I;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    wg[r][q] = ld128(wb, v ? (uint32_t)i * rowb + (uint32_t)k0 * 2u + 16u * q : OOB);
+                    wu[r][q] = ld128(wb, v ? (uint32_t)(I + i) * rowb + (uint32_t)k0 * 2u + 16u * q : OOB);
+                }
+            }
+#pragma unroll
+            for (int r = 0; r < RT; ++r) {
+                ag[r] = bf16w_dot_bf16<FMT>(wg[r], xs, ag[r]);
+                au[r] = bf16w_dot_bf16<FMT>(wu[r], xs, au[r]);
+            }
+        }
+    }
+    for (int s = 0; s < (sbf ? 0 : ks); ++s) {
         const int k0 = 32 * (L * s + lk);
         const bool kv = k0 < H;
         XSlice<FMT> xs;
@@ -335,7 +366,7 @@ __global__ __launch_bounds__(1024) void k_moe_w13(W13Args a) {
         }
     }
     float gsc = 1.f;
-    if constexpr (FMT == FMT_NVFP4) gsc = ld_uniform(gp, 0);
+    if constexpr (FMT == FMT_NVFP4) gsc = sbf ? 1.f : ld_uniform(gp, 0);
     float *hrow = a.h + ((size_t)t * a.S + j) * a.hstride;
 #pragma unroll
     for (int r = 0; r < RT; ++r) {
@@ -358,6 +389,7 @@ struct DownArgs {
     const uint8_t *s_codes;       // shared W2 [H][I/2]
     const uint8_t *s_scales;
     const float *gs, *s_gs;       // NVFP4 global scales: routed [E], shared [1]
+    int s_bf16;                   // shared expert in bf16 (s_codes = bf16 [H][I])
     const int32_t *ids;           // [T][k]
     const float *w;               // [T][k]
     const float *logits;          // [T][lstride]; column E = shared-gate logit
@@ -368,7 +400,7 @@ struct DownArgs {
 
 // Block = W waves; tile of RT*64/L output rows of one token.  LDS holds one
 // fp32 partial per (slot, row); the final sum runs over slots in order.
-template <int FMT, int L, int RT>
+template <int FMT, int L, int RT, bool SBF>
 __global__ __launch_bounds__(1024) void k_moe_down(DownArgs a) {
     constexpr int RG = 64 / L;
     constexpr int ROWS = RT * RG;
@@ -414,13 +446,42 @@ __global__ __launch_bounds__(1024) void k_moe_down(DownArgs a) {
             gp = a.gs ? a.gs + eo : nullptr;
             coef = ld_uniform(a.w, t * a.K + j);
         }
-        if constexpr (FMT == FMT_NVFP4) coef *= ld_uniform(gp, 0);  // (w x g) x row sum
-        const Buf cb = make_buf(cbase, valid ? mat_codes : 0u);
+        const bool sbf = SBF && j == a.K;  // bf16 shared expert slot (uniform per wave)
+        if constexpr (FMT == FMT_NVFP4) {
+            if (!sbf) coef *= ld_uniform(gp, 0);  // (w x g) x row sum
+        }
+        const Buf cb = make_buf(cbase, valid ? (sbf ? (uint32_t)H * (uint32_t)I * 2u : mat_codes) : 0u);
         const Buf sb = make_buf(sbase, valid ? mat_scales : 0u);
         float acc[RT];
 #pragma unroll
         for (int r = 0; r < RT; ++r) acc[r] = 0.f;
-        for (int s = 0; s < ks; ++s) {
+        if (sbf) {
+            for (int s = 0; s < ks; ++s) {
+                const int k0 = 32 * (L * s + lk);
+                const bool kv = k0 < I;
+                float4 hv[8];
+                if (s == 0) {
+#pragma unroll
+                    for (int q = 0; q < 8; ++q) hv[q] = hv0[q];
+                } else {
+                    const uint32_t h0 = ((uint32_t)s * 32u * L + (uint32_t)lk * 4u) * 4u;
+#pragma unroll
+                    for (int q = 0; q < 8; ++q)
+                        hv[q] = __builtin_bit_cast(float4, ld128(hb, kv ? h0 + (uint32_t)q * L * 16u : OOB));
+                }
+#pragma unroll
+                for (int r = 0; r < RT; ++r) {
+                    const int row = row0 + r * RG + rsub;
+                    const bool v = kv && row < H;
+                    uint4 w[4];
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        w[q] = ld128(cb, v ? (uint32_t)row * (uint32_t)I * 2u + (uint32_t)k0 * 2u + 16u * q : OOB);
+                    acc[r] = bf16w_dot_f32(w, hv, acc[r]);
+                }
+            }
+        }
+        for (int s = 0; s < (sbf ? 0 : ks); ++s) {
             const int k0 = 32 * (L * s + lk);
             const bool kv = k0 < I;
             float4 hv[8];  // activations first
@@ -503,7 +564,8 @@ int check_matrix(const w4_matrix *W, const char *what) {
     if (!W) return fail(W4_ERR_INVALID_ARG, "%s: null matrix", what);
     int st = w4::check_shape(W->format, W->layout, W->groups, W->n, W->k);
     if (st) return st;
-    if (!W->codes || !W->scales) return fail(W4_ERR_INVALID_ARG, "%s: null codes/scales", what);
+    if (!W->codes || (!W->scales && W->format != W4_FMT_BF16))
+        return fail(W4_ERR_INVALID_ARG, "%s: null codes/scales", what);
     if (!aligned(W->codes, 16)) return fail(W4_ERR_ALIGNMENT, "%s: codes not 16-byte aligned", what);
     if (!aligned(W->scales, 4)) return fail(W4_ERR_ALIGNMENT, "%s: scales not 4-byte aligned", what);
     if (W->format == W4_FMT_NVFP4_E4M3S16) {
@@ -512,7 +574,7 @@ int check_matrix(const w4_matrix *W, const char *what) {
     }
     if (W->n > (1 << 30) || W->k > (1 << 20)) return fail(W4_ERR_UNSUPPORTED, "%s: dimension too large", what);
     // one matrix of the stack is addressed through 32-bit buffer offsets
-    if ((uint64_t)W->n * (uint64_t)W->k / 2 >= (1ull << 31))
+    if ((uint64_t)W->n * (uint64_t)W->k * (W->format == W4_FMT_BF16 ? 2 : 1) / 2 >= (1ull << 31))
         return fail(W4_ERR_UNSUPPORTED, "%s: one matrix must hold fewer than 2^31 code bytes", what);
     return W4_OK;
 }
@@ -620,6 +682,7 @@ int check_layer(const moe_w4a16_layer *Lr, int64_t T, MoEPlan &p) {
     if ((st = check_matrix(&Lr->w13, "w13"))) return st;
     if ((st = check_matrix(&Lr->w2, "w2"))) return st;
     const int32_t fmt = Lr->w13.format;
+    if (fmt == W4_FMT_BF16) return fail(W4_ERR_UNSUPPORTED, "routed experts must be 4-bit (bf16 is for the shared expert)");
     if (Lr->w2.format != fmt) return fail(W4_ERR_LAYOUT, "w13 and w2 formats differ");
     if (Lr->w13.groups != E || Lr->w13.n != 2 * I || Lr->w13.k != H)
         return fail(W4_ERR_INVALID_ARG, "w13 must be [E][2I][H]");
@@ -630,8 +693,9 @@ int check_layer(const moe_w4a16_layer *Lr, int64_t T, MoEPlan &p) {
             return fail(W4_ERR_UNSUPPORTED, "shared_inter=%lld must equal inter=%lld", (long long)Lr->shared_inter, (long long)I);
         if ((st = check_matrix(&Lr->shared_w13, "shared_w13"))) return st;
         if ((st = check_matrix(&Lr->shared_w2, "shared_w2"))) return st;
-        if (Lr->shared_w13.format != fmt || Lr->shared_w2.format != fmt)
-            return fail(W4_ERR_LAYOUT, "shared expert format differs from the routed experts");
+        const int32_t sf = Lr->shared_w13.format;
+        if ((sf != fmt && sf != W4_FMT_BF16) || Lr->shared_w2.format != sf)
+            return fail(W4_ERR_LAYOUT, "shared expert must use the routed experts' format or bf16 for both matrices");
         if (Lr->shared_w13.groups != 1 || Lr->shared_w13.n != 2 * I || Lr->shared_w13.k != H)
             return fail(W4_ERR_INVALID_ARG, "shared_w13 must be [1][2I][H]");
         if (Lr->shared_w2.groups != 1 || Lr->shared_w2.n != H || Lr->shared_w2.k != I)
@@ -653,7 +717,8 @@ int check_layer(const moe_w4a16_layer *Lr, int64_t T, MoEPlan &p) {
     p.Gmax = (int)(E < p.P ? E : p.P);
     // (the VALU small-group path keeps at most 2 k-steps of 32 x 64 elements)
     p.grouped = T >= W4_GROUPED_MIN_T && fmt == W4_FMT_E2M1_F16S16 && H % 128 == 0 && I % 128 == 0 &&
-                p.P <= MAX_GROUPED_PAIRS && H <= 4096 && I <= 4096;
+                p.P <= MAX_GROUPED_PAIRS && H <= 4096 && I <= 4096 &&
+                !(Lr->has_shared && Lr->shared_w13.format == W4_FMT_BF16);
     size_t off = 0;
     p.off_logits = off; off = align_up(off + (size_t)T * p.lstride * 4, 256);
     p.off_ids = off;    off = align_up(off + (size_t)T * K * 4, 256);
@@ -715,11 +780,16 @@ void launch_w13_L(const MoEPlan &p, W13Args &a, const Launch &st) {
     const int blocks = p.T * p.S * tblocks;
     const int pl = (p.E + 63) / 64;
     const dim3 g(blocks), bl(64 * wpb);
-    if (pl <= 1) go(st, k_moe_w13<FMT, L, RT, 1>, g, bl, 0, a);
-    else if (pl <= 2) go(st, k_moe_w13<FMT, L, RT, 2>, g, bl, 0, a);
-    else if (pl <= 4) go(st, k_moe_w13<FMT, L, RT, 4>, g, bl, 0, a);
-    else if (pl <= 8) go(st, k_moe_w13<FMT, L, RT, 8>, g, bl, 0, a);
-    else go(st, k_moe_w13<FMT, L, RT, 16>, g, bl, 0, a);
+    auto with_pl = [&](auto SBFc) {
+        constexpr bool SB = decltype(SBFc)::value;
+        if (pl <= 1) go(st, k_moe_w13<FMT, L, RT, 1, SB>, g, bl, 0, a);
+        else if (pl <= 2) go(st, k_moe_w13<FMT, L, RT, 2, SB>, g, bl, 0, a);
+        else if (pl <= 4) go(st, k_moe_w13<FMT, L, RT, 4, SB>, g, bl, 0, a);
+        else if (pl <= 8) go(st, k_moe_w13<FMT, L, RT, 8, SB>, g, bl, 0, a);
+        else go(st, k_moe_w13<FMT, L, RT, 16, SB>, g, bl, 0, a);
+    };
+    if (a.s_bf16) with_pl(std::true_type());
+    else with_pl(std::false_type());
 }
 
 template <int FMT>
@@ -751,7 +821,8 @@ void launch_down_L(const MoEPlan &p, DownArgs &a, const Launch &st) {
     int nw = p.S < W4_DOWN_WAVES ? p.S : W4_DOWN_WAVES;
     nw = (p.S + ((p.S + nw - 1) / nw) - 1) / ((p.S + nw - 1) / nw);  // equal slots per wave
     const size_t lds = (size_t)p.S * ROWS * sizeof(float);
-    go(st, k_moe_down<FMT, L, RT>, dim3(p.T * a.blocks_per_tok), dim3(64 * nw), (uint32_t)lds, a);
+    if (a.s_bf16) go(st, k_moe_down<FMT, L, RT, true>, dim3(p.T * a.blocks_per_tok), dim3(64 * nw), (uint32_t)lds, a);
+    else go(st, k_moe_down<FMT, L, RT, false>, dim3(p.T * a.blocks_per_tok), dim3(64 * nw), (uint32_t)lds, a);
 }
 
 template <int FMT>
@@ -825,6 +896,7 @@ int run_moe(const moe_w4a16_layer *Lr, const uint16_t *x, int64_t T, const int32
     a.s_codes = Lr->has_shared ? Lr->shared_w13.codes : nullptr;
     a.s_scales = Lr->has_shared ? (const uint8_t *)Lr->shared_w13.scales : nullptr;
     a.s_gs = Lr->has_shared ? Lr->shared_w13.global_scales : nullptr;
+    a.s_bf16 = Lr->has_shared && Lr->shared_w13.format == W4_FMT_BF16;
     a.x = x;
     a.logits = logits;
     a.bias = Lr->router_bias;
@@ -849,6 +921,7 @@ int run_moe(const moe_w4a16_layer *Lr, const uint16_t *x, int64_t T, const int32
     d.s_codes = Lr->has_shared ? Lr->shared_w2.codes : nullptr;
     d.s_scales = Lr->has_shared ? (const uint8_t *)Lr->shared_w2.scales : nullptr;
     d.s_gs = Lr->has_shared ? Lr->shared_w2.global_scales : nullptr;
+    d.s_bf16 = Lr->has_shared && Lr->shared_w2.format == W4_FMT_BF16;
     d.ids = route ? ids_ws : ids_in;
     d.w = route ? w_ws : w_in;
     d.logits = logits;
@@ -930,6 +1003,7 @@ int w4a16_gemv(const w4_matrix *W, const uint16_t *x, int64_t m, uint16_t *y, vo
     int st = check_matrix(W, "W");
     if (st) return st;
     if (W->groups != 1) return fail(W4_ERR_INVALID_ARG, "gemv needs groups == 1");
+    if (W->format == W4_FMT_BF16) return fail(W4_ERR_UNSUPPORTED, "bf16 matrices serve only as the shared expert");
     if (m < 1 || m > 64) return fail(W4_ERR_UNSUPPORTED, "m=%lld out of [1, 64]", (long long)m);
     if (!x || !y) return fail(W4_ERR_INVALID_ARG, "null x or y");
     if (!aligned(x, 16)) return fail(W4_ERR_ALIGNMENT, "x not 16-byte aligned");
@@ -946,6 +1020,7 @@ int w4_dequant_device(const w4_matrix *W, float *out, void *stream) {
     w4::clear_error();
     int st = check_matrix(W, "W");
     if (st) return st;
+    if (W->format == W4_FMT_BF16) return fail(W4_ERR_UNSUPPORTED, "bf16 matrices need no dequantisation");
     if (!out) return fail(W4_ERR_INVALID_ARG, "null out");
     if (!aligned(out, 16)) return fail(W4_ERR_ALIGNMENT, "out not 16-byte aligned");
     (void)hipGetLastError();

@@ -15,6 +15,7 @@ from . import (
     MoELayer,
     QMatrix,
     W4_FMT_NVFP4_E4M3S16,
+    W4_FMT_BF16,
     w4_quantize,
 )
 
@@ -34,6 +35,8 @@ def quantize_stack(fmt, gen, groups, n, k):
 
 def upload(fmt, q, device):
     """QMatrix from the output of quantize_stack / w4_quantize."""
+    if fmt == W4_FMT_BF16:
+        return QMatrix.upload_bf16(q[0], device)
     return QMatrix.upload(fmt, q[0], q[1], device, global_np=q[2] if len(q) > 2 else None)
 
 
@@ -54,9 +57,10 @@ def build_moe_layer(shape, fmt=None, device="cuda"):
     router_bias = torch.from_numpy(bias).to(device) if bias is not None else None
     kw = {}
     if shape.has_shared:
+        sfmt = FORMATS[shape.shared_fmt] if shape.shared_fmt else fmt
         kw = dict(
-            shared_w13=upload(fmt, w4_quantize(fmt, synth.shared_w13(shape)), device),
-            shared_w2=upload(fmt, w4_quantize(fmt, synth.shared_w2(shape)), device),
+            shared_w13=upload(sfmt, w4_quantize(sfmt, synth.shared_w13(shape)), device),
+            shared_w2=upload(sfmt, w4_quantize(sfmt, synth.shared_w2(shape)), device),
             shared_gate_w=torch.from_numpy(synth.shared_gate_weight(shape).view(np.int16)).to(device),
         )
     return MoELayer(shape.hidden, shape.inter, shape.num_experts, shape.top_k, router_w, w13, w2,

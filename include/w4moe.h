@@ -72,6 +72,11 @@ extern "C" {
  * most 448) per 16 consecutive K elements and one fp32 global scale per matrix;
  * element value = code x scale x global. */
 #define W4_FMT_NVFP4_E4M3S16 3
+/* Unquantised bf16 weights: `codes` holds bf16 bit patterns [groups][n][k]
+ * (2 bytes per element), no scales.  Accepted for the shared expert of an MoE
+ * layer (the pages' engine keeps it in bf16: lynn-engine README P15/P37) and by
+ * w4_quantize (round to nearest even); the GEMV and dequant hook reject it. */
+#define W4_FMT_BF16 4
 
 /* Canonical layout, the only one this library reads:
  *   codes  [groups][n][k/2] bytes, element 2j in the low nibble of byte j and
@@ -134,6 +139,8 @@ size_t w4_scales_bytes(int32_t format, int32_t layout, int64_t groups, int64_t n
  *   block scale = UE4M3 round-to-nearest-even of fp32(fp32(block absmax) / 6) / g,
  *   saturating at 448; code = nearest E2M1 value to fp32(w) / fp32(scale x g),
  *   ties to even, +0 for zero; an all-zero matrix has g = 0.
+ * bf16: codes receives bf16 bit patterns [n][k] (round to nearest even), scales
+ * and global_scale are unused.
  * global_scale may be NULL for the FP16-scale formats.
  * Errors: W4_ERR_NONFINITE (Inf/NaN input), W4_ERR_RANGE (a block scale would
  * overflow fp16), W4_ERR_INVALID_ARG, W4_ERR_LAYOUT.  Synchronous, thread-safe. */
@@ -173,10 +180,11 @@ int w4_dequant_device(const w4_matrix *W, float *out, void *stream);
  *   has_shared    0/1; if 1:
  *     shared_w13  groups = 1, n = 2*shared_inter, k = H
  *     shared_w2   groups = 1, n = H, k = shared_inter
+ *                 in the routed experts' format or both W4_FMT_BF16
  *     shared_gate_w bf16 [H]: sigma = sigmoid(shared_gate_w . x)
- * This build requires shared_inter == inter and H % 64 == 0; all experts and
- * the shared expert use one format (NVFP4: one global scale per expert matrix,
- * applied to the gate/up sums and to the down sums). */
+ * This build requires shared_inter == inter and H % 64 == 0; the routed experts
+ * use one format (NVFP4: one global scale per expert matrix, applied to the
+ * gate/up sums and to the down sums), the shared expert that format or bf16. */
 typedef struct moe_w4a16_layer {
     int64_t hidden;              /* H */
     int64_t inter;               /* I (expert intermediate) */

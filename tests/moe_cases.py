@@ -24,13 +24,19 @@ MEAN_MIN = 256
 GAP = 1e-3  # minimum adjacent gap among the k+1 largest logits of a parity token
 
 
-def oracle_layer(shape, fmt=F.FMT_E2M1):
-    """Oracle view of a synth layer; experts are quantised lazily by the oracle."""
+_OFMT = {"e2m1": F.FMT_E2M1, "int4": F.FMT_INT4, "nvfp4": F.FMT_NVFP4, "bf16": F.FMT_BF16}
+
+
+def oracle_layer(shape, fmt=None):
+    """Oracle view of a synth layer; experts are quantised lazily by the oracle.
+    fmt: oracle format of the routed experts (default: the shape's)."""
+    fmt = _OFMT[shape.fmt] if fmt is None else fmt
+    sfmt = _OFMT[shape.shared_fmt] if shape.shared_fmt else fmt
     kw = {}
     if shape.has_shared:
-        kw = dict(shared_w13=oracle.quantize(fmt, synth.shared_w13(shape)),
-                  shared_w2=oracle.quantize(fmt, synth.shared_w2(shape)),
-                  shared_gate_w=synth.shared_gate_weight(shape))
+        kw = dict(shared_w13=oracle.quantize(sfmt, synth.shared_w13(shape)),
+                  shared_w2=oracle.quantize(sfmt, synth.shared_w2(shape)),
+                  shared_gate_w=synth.shared_gate_weight(shape), shared_fmt=sfmt)
     return ops.MoELayer(
         fmt, shape.hidden, shape.inter, shape.num_experts, shape.top_k, synth.router_weight(shape),
         lambda e: oracle.quantize(fmt, synth.expert_w13(shape, e)),

@@ -279,3 +279,29 @@ def test_gemv_lmhead_sampled_rows():
                                      rng.choice(shape.n, 2048, replace=False)]))
     ref = oracle.gemv(F.FMT_E2M1, *oracle.quantize(F.FMT_E2M1, w[rows]), x)
     assert_bf16_close(got[rows], ref, shape.name)
+
+
+# ---------------------------------------------------------------- bf16 shared expert
+
+
+@pytest.mark.parametrize("shape", [synth.TINY_MOE_BF16SH, synth.QWEN_MOE_T1_BF16SH], ids=lambda s: s.name)
+def test_moe_bf16_shared_expert(shape):
+    """Routed E2M1 experts with an unquantised bf16 shared expert."""
+    print(f"building {shape.name}", flush=True)
+    dev_layer = wl.build_moe_layer(shape, device=DEV)
+    assert dev_layer.shared_w13.fmt == w4.W4_FMT_BF16
+    or_layer = oracle_layer(shape)
+    for t in range(2):
+        print(f"bf16 shared token {t}", flush=True)
+        print(_check_moe(shape, dev_layer, or_layer, tie_free_tokens(shape, or_layer, 1, first=t), f"{shape.name} t={t}"),
+              flush=True)
+    # batches of this layer take the single-token path
+    assert w4.moe_w4a16_stage_count(dev_layer, 6) == 3
+    _check_moe(shape, dev_layer, or_layer, tie_free_tokens(shape, or_layer, 6, first=40), f"{shape.name} T=6")
+
+
+def test_moe_nvfp4_with_bf16_shared_expert():
+    shape = synth.MoEShape("tiny-nvfp4-bf16shared", 256, 128, 8, 2, 128, 1, 0.0, 0, "nvfp4", "bf16")
+    dev_layer = wl.build_moe_layer(shape, device=DEV)
+    or_layer = oracle_layer(shape)
+    _check_moe(shape, dev_layer, or_layer, tie_free_tokens(shape, or_layer, 3, first=7), "nvfp4 + bf16 shared")

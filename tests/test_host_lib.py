@@ -148,6 +148,27 @@ def test_quantizer_nvfp4_golden_and_sizes():
     assert st == w4.W4_ERR_INVALID_ARG
 
 
+def test_bf16_format_quantiser_sizes_and_rules():
+    rng = np.random.default_rng(23)
+    w = (rng.standard_normal((5, 64)) * 0.02).astype(np.float32)
+    w[0, :4] = [1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, -0.0, 3.0e38]  # ties and extremes
+    (bits,) = w4.w4_quantize(w4.W4_FMT_BF16, w)
+    (ref,) = oracle.quantize(F.FMT_BF16, w)
+    assert np.array_equal(bits, ref)
+    fmt = w4.W4_FMT_BF16
+    assert w4.w4_codes_bytes(fmt, 2, 3, 64) == 2 * 3 * 64 * 2 and w4.w4_scales_bytes(fmt, 2, 3, 64) == 0
+    # the GEMV rejects bf16 matrices; a bf16 routed expert stack is unsupported
+    assert w4.lib().w4a16_gemv(C.byref(_mat(fmt=fmt, scales=None)), 1 << 20, 1, 1 << 21, 0) == w4.W4_ERR_UNSUPPORTED
+    H, I, E = 256, 128, 8
+    L = _layer(shared_w13=_mat(fmt=fmt, groups=1, n=2 * I, k=H, scales=None),
+               shared_w2=_mat(fmt=fmt, groups=1, n=H, k=I, scales=None))
+    assert w4.lib().moe_w4a16_workspace_bytes(C.byref(L), 1) > 0
+    assert w4.lib().moe_w4a16_stage_count(C.byref(L), 8) == 3  # batches take the single-token path
+    assert _fwd(_layer(w13=_mat(fmt=fmt, groups=E, n=2 * I, k=H, scales=None),
+                       w2=_mat(fmt=fmt, groups=E, n=H, k=I, scales=None))) == w4.W4_ERR_UNSUPPORTED
+    assert _fwd(_layer(shared_w13=_mat(fmt=fmt, groups=1, n=2 * I, k=H, scales=None))) == w4.W4_ERR_LAYOUT
+
+
 def test_pack_unpack_all_bytes_and_oracle():
     b = np.arange(256, dtype=np.uint8).reshape(4, 64)
     nib = w4.w4_unpack_nibbles(b)
