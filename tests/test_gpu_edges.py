@@ -1,0 +1,81 @@
+"""GPU parity at the edges of the supported ranges: the largest expert count and
+top-k, hidden sizes off the 128 grid (single-token path), int4 experts, the
+largest grouped batch (T k = 4096 pairs) and the largest token count."""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import formats as F
+from oracle import ops
+import bit_block_scaled_router_amd as w4
+from bit_block_scaled_router_amd import synth, workloads as wl
+from moe_cases import assert_bf16_close, oracle_layer, tie_free_tokens
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+DEV = "cuda"
+
+
+def _run(shape, dev_layer, x_bits):
+    T = x_bits.shape[0]
+    ids = torch.full((T, shape.top_k), -7, dtype=torch.int32, device=DEV)
+    wts = torch.zeros((T, shape.top_k), dtype=torch.float32, device=DEV)
+    y = w4.moe_w4a16_forward(dev_layer, wl.bf16_tensor(x_bits), topk_ids=ids, topk_w=wts)
+    return wl.bf16_bits(y), ids.cpu().numpy(), wts.cpu().numpy()
+
+
+def _check(shape, dev_layer, or_layer, x_bits, what, rows=None):
+    got, ids, wts = _run(shape, dev_layer, x_bits)
+    rows = np.arange(x_bits.shape[0]) if rows is None else rows
+    ref, rids, rw = ops.moe_forward(or_layer, x_bits, tokens=list(rows))
+    assert np.array_equal(ids[rows], rids), what
+    np.testing.assert_allclose(wts[rows], rw, rtol=2e-6, atol=1e-7)
+    return assert_bf16_close(got[rows], ref, what)
+
+
+EDGE_SHAPES = [
+    # largest expert count and top-k (64 lanes x 16 logits ranked per wave); T = 5 is grouped
+    (synth.MoEShape("edge-e1024-k16", 256, 128, 1024, 16, 0, 1, 0.0, 3), (1, 5)),
+    # hidden off the 128 grid, ragged intermediate: the single-token path for every T
+    (synth.MoEShape("edge-h320-i96", 320, 96, 16, 4, 96, 1, 0.0, 4), (1, 6)),
+    # int4 experts (FP16 scale per 128) with an int4 shared expert
+    (synth.MoEShape("edge-int4", 256, 128, 8, 2, 128, 1, 0.0, 5, "int4"), (1, 6)),
+]
+
+
+@pytest.mark.parametrize("shape,Ts", EDGE_SHAPES, ids=lambda v: v.name if hasattr(v, "name") else str(v))
+def test_edge_layers(shape, Ts):
+    print(f"edge {shape.name}", flush=True)
+    dev_layer = wl.build_moe_layer(shape, device=DEV)
+    or_layer = oracle_layer(shape)
+    for T in Ts:
+        print(f"  T={T} stages={w4.moe_w4a16_stage_count(dev_layer, T)}", flush=True)
+        _check(shape, dev_layer, or_layer, tie_free_tokens(shape, or_layer, T, first=11 * T), f"{shape.name} T={T}")
+
+
+def test_largest_grouped_batch():
+    """T k = 4096 (token, slot) pairs, the grouped path's limit; groups of ~64 rows
+    run several 32-column MFMA passes."""
+    shape = synth.MoEShape("edge-pairs4096", 256, 128, 64, 8, 128, 512, 0.0, 6)
+    dev_layer = wl.build_moe_layer(shape, device=DEV)
+    assert w4.moe_w4a16_stage_count(dev_layer, 512) == 5
+    or_layer = oracle_layer(shape)
+    print("pairs 4096", flush=True)
+    _check(shape, dev_layer, or_layer, tie_free_tokens(shape, or_layer, 512), "T=512 k=8")
+
+
+def test_largest_token_count_sampled():
+    """T = 4096 on the single-token path (int4 experts), checked on 48 sampled tokens."""
+    shape = synth.MoEShape("edge-t4096-int4", 256, 128, 8, 2, 128, 4096, 0.0, 7, "int4")
+    dev_layer = wl.build_moe_layer(shape, device=DEV)
+    assert w4.moe_w4a16_stage_count(dev_layer, 4096) == 3
+    or_layer = oracle_layer(shape)
+    x = np.stack([synth.x_row(shape.seed, shape.hidden, t) for t in range(4096)])
+    rng = np.random.default_rng(9)
+    rows = np.unique(np.concatenate([[0, 4095], rng.choice(4096, 46, replace=False)]))
+    # sampled tokens must be tie-free for the id comparison
+    keep = [r for r in rows if __import__("moe_cases").min_gap(or_layer, x[r]) >= 1e-3]
+    print(f"T=4096 sampled {len(keep)}", flush=True)
+    _check(shape, dev_layer, or_layer, x, "T=4096", rows=np.array(keep))
