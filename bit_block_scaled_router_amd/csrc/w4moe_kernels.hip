@@ -203,8 +203,6 @@ struct W13Args {
     const uint8_t *scales;        // routed W13 scales (bytes)
     const uint8_t *s_codes;       // shared W13 [2I][H/2] (or null)
     const uint8_t *s_scales;
-    const float *gs, *s_gs;       // NVFP4 global scales: routed [E], shared [1]
-    int s_bf16;                   // shared expert in bf16 (s_codes = bf16 [2I][H])
     const uint16_t *x;            // [T][H]
     const float *logits;          // [T][lstride] (routed mode)
     const float *bias;            // [E] or null
@@ -216,6 +214,10 @@ struct W13Args {
     float *h;                     // [T][S][hstride] fp32, order of the down kernel's lanes
     int H, I, E, K, S, T, tiles, lstride, hstride, route;
     int L2;                       // lanes per row of the down kernel (h order)
+    // (fields of the format variants last: the fields above keep the argument
+    // offsets the prologue's first loads were tuned for, ~0.25 us per step)
+    int s_bf16;                   // shared expert in bf16 (s_codes = bf16 [2I][H])
+    const float *gs, *s_gs;       // NVFP4 global scales: routed [E], shared [1]
 };
 
 // h index of intermediate element i in the down kernel's lane order: lane lk of
@@ -388,14 +390,14 @@ struct DownArgs {
     const uint8_t *scales;        // (bytes)
     const uint8_t *s_codes;       // shared W2 [H][I/2]
     const uint8_t *s_scales;
-    const float *gs, *s_gs;       // NVFP4 global scales: routed [E], shared [1]
-    int s_bf16;                   // shared expert in bf16 (s_codes = bf16 [H][I])
     const int32_t *ids;           // [T][k]
     const float *w;               // [T][k]
     const float *logits;          // [T][lstride]; column E = shared-gate logit
     const float *h;               // [T][S][hstride]
     uint16_t *y;                  // [T][H] bf16
     int H, I, E, K, S, T, lstride, hstride, blocks_per_tok;
+    int s_bf16;                   // shared expert in bf16 (s_codes = bf16 [H][I])
+    const float *gs, *s_gs;       // NVFP4 global scales: routed [E], shared [1]
 };
 
 // Block = W waves; tile of RT*64/L output rows of one token.  LDS holds one
