@@ -29,6 +29,8 @@ from .formats import (  # noqa: F401
     FMT_INT4,
     FMT_NVFP4,
     FMT_BF16,
+    FMT_MXFP4,
+    MX_BLOCK,
     E4M3_MAX,
     bf16_bits_to_f64,
     f64_to_bf16_bits,
@@ -39,6 +41,9 @@ from .formats import (  # noqa: F401
     quantize_e2m1,
     quantize_int4,
     quantize_nvfp4,
+    quantize_mxfp4,
+    e8m0_value,
+    mx_e4m3,
     quantize,
     pack_nibbles,
     unpack_nibbles,

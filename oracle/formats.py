@@ -15,6 +15,15 @@ Everything here is written from the definitions, in float32/float64 NumPy:
   block of 16 and the 2-byte scale).
 * Signed int4 with one FP16 scale per group of 128 along K: "cuda_inf" article,
   section "2. INT4 weight quantization".
+* MXFP4 (OCP Microscaling v1.0, the vendor format the README notes P17/P54 and
+  R5-B bridge to, "e8m0/group32"): E2M1 codes with one E8M0 scale (a power of
+  two, 2^(byte - 127); byte 0xFF is NaN) per 32 K elements.  Shared exponent and
+  element rounding follow the MX specification's conversion: X =
+  floor(log2(absmax)) - emax_elem (emax_elem = 2 for E2M1, 8 for E4M3), elements
+  round to nearest even after division by 2^X and clamp to the largest normal.
+  The MX path computes with MXFP8 activations (E4M3 elements, E8M0 per 32): the
+  layer input and the SwiGLU intermediate are quantised that way before each
+  scaled MFMA, so it is a W4A8 variant with its own parity reference.
 * NVFP4 proper: E2M1 codes, one unsigned E4M3 (UE4M3) scale per 16 K elements and
   one fp32 global scale per matrix.  The lynn-engine README names this variant
   (status notes P17/P54 "per-16/e4m3" scales, R5-C0 "UE4M3" block-16 scales,
@@ -58,12 +67,14 @@ FMT_E2M1 = 1  # E2M1 codes, FP16 scale per 16 K elements
 FMT_INT4 = 2  # two's-complement int4 codes, FP16 scale per 128 K elements
 FMT_NVFP4 = 3  # E2M1 codes, UE4M3 scale per 16 K elements, fp32 scale per matrix
 FMT_BF16 = 4  # unquantised bf16 weights (the shared expert's production format in the pages)
+FMT_MXFP4 = 5  # E2M1 codes, E8M0 scale per 32 K elements (OCP MX); activations MXFP8
+MX_BLOCK = 32
 
 E2M1_GROUP = 16
 INT4_GROUP = 128
 
-_GROUP = {FMT_E2M1: E2M1_GROUP, FMT_INT4: INT4_GROUP, FMT_NVFP4: E2M1_GROUP}
-_SCALE_BYTES = {FMT_E2M1: 2, FMT_INT4: 2, FMT_NVFP4: 1}
+_GROUP = {FMT_E2M1: E2M1_GROUP, FMT_INT4: INT4_GROUP, FMT_NVFP4: E2M1_GROUP, FMT_MXFP4: MX_BLOCK}
+_SCALE_BYTES = {FMT_E2M1: 2, FMT_INT4: 2, FMT_NVFP4: 1, FMT_MXFP4: 1}
 
 E4M3_MAX = 448.0
 
@@ -147,7 +158,13 @@ _UE4M3 = e4m3_value(np.arange(0x7F))
 def f32_to_ue4m3(v):
     """Non-negative fp32 values -> UE4M3 bytes: nearest representable value, ties
     to the even code (round to nearest even), saturating at 448."""
-    x = np.asarray(v, dtype=np.float32).astype(np.float64)
+    return _ue4m3_rne(np.asarray(v, dtype=np.float32).astype(np.float64))
+
+
+def _ue4m3_rne(x):
+    """Non-negative float64 values -> UE4M3 bytes, round to nearest even (no
+    intermediate rounding), saturating at 448."""
+    x = np.asarray(x, dtype=np.float64)
     if np.any(x < 0) or not np.all(np.isfinite(x)):
         raise ValueError("UE4M3 input must be finite and non-negative")
     x = np.minimum(x, E4M3_MAX)
@@ -158,8 +175,59 @@ def f32_to_ue4m3(v):
     return np.where(pick_hi, i, i - 1).astype(np.uint8)
 
 
+def e8m0_value(byte):
+    """OCP E8M0 scale byte -> float64: 2^(byte - 127); 0xFF is NaN."""
+    b = np.asarray(byte, dtype=np.int64)
+    return np.where(b == 0xFF, np.nan, np.exp2(b.astype(np.float64) - 127.0))
+
+
+def _mx_exponent(amax, emax_elem):
+    """Shared MX exponent of a block: floor(log2(amax)) - emax_elem, amax > 0
+    (exact: frexp gives amax = f 2^e with f in [0.5, 1), floor(log2) = e - 1),
+    limited to the E8M0 range [-127, 127]."""
+    _, e = np.frexp(np.asarray(amax, dtype=np.float64))
+    return np.clip(e.astype(np.int64) - 1 - emax_elem, -127, 127)
+
+
+def quantize_mxfp4(w):
+    """fp32 weights [N][K] -> (codes [N][K] uint8 0..15, E8M0 scale bytes [N][K/32]).
+
+    Per 32-element block (OCP MX v1.0 conversion): X = floor(log2(absmax)) - 2;
+    element = nearest E2M1 value to w / 2^X (exact division), ties to the even
+    code, saturating at 6; an all-zero block gets X = -127 (byte 0) and zero codes;
+    -0 is never emitted."""
+    w32 = _check_input(w, MX_BLOCK)
+    n, k = w32.shape
+    blk = np.abs(w32.reshape(n, k // MX_BLOCK, MX_BLOCK)).max(axis=2).astype(np.float64)
+    X = np.where(blk > 0, _mx_exponent(np.where(blk > 0, blk, 1.0), 2), -127)
+    r = w32.astype(np.float64) / np.exp2(np.repeat(X, MX_BLOCK, axis=1).astype(np.float64))
+    mag = _nearest_e2m1_magnitude_code(np.abs(r))
+    neg = (r < 0) & (mag != 0)
+    codes = (mag + 8 * neg).astype(np.uint8)
+    return codes, (X + 127).astype(np.uint8)
+
+
+def mx_e4m3(v):
+    """MXFP8 (E4M3 elements, E8M0 per 32) quantisation of activations along the
+    last axis, returned dequantised (float64, exact) with the scale exponents.
+
+    Per block: X = floor(log2(absmax)) - 8; q = E4M3 round-to-nearest-even of
+    clamp(v / 2^X, +-448) (sign of zero kept); value = q * 2^X.  A zero block has
+    X = -127 and zero values."""
+    a = np.asarray(v, dtype=np.float64)
+    shp = a.shape
+    if shp[-1] % MX_BLOCK:
+        raise ValueError("length not a multiple of 32")
+    b = a.reshape(shp[:-1] + (shp[-1] // MX_BLOCK, MX_BLOCK))
+    amax = np.abs(b).max(axis=-1)
+    X = np.where(amax > 0, _mx_exponent(np.where(amax > 0, amax, 1.0), 8), -127)
+    r = np.clip(b / np.exp2(X.astype(np.float64))[..., None], -E4M3_MAX, E4M3_MAX)
+    q = e4m3_value(_ue4m3_rne(np.abs(r))) * np.where(np.signbit(r), -1.0, 1.0)
+    return (q * np.exp2(X.astype(np.float64))[..., None]).reshape(shp), X
+
+
 def _decode(fmt, code):
-    if fmt in (FMT_E2M1, FMT_NVFP4):
+    if fmt in (FMT_E2M1, FMT_NVFP4, FMT_MXFP4):
         return e2m1_value(code)
     if fmt == FMT_INT4:
         return int4_value(code)
@@ -275,6 +343,9 @@ def quantize(fmt, w):
     elif fmt == FMT_NVFP4:
         c, sb, g = quantize_nvfp4(w)
         return pack_nibbles(c), sb, g
+    elif fmt == FMT_MXFP4:
+        c, sb = quantize_mxfp4(w)
+        return pack_nibbles(c), sb
     else:
         raise ValueError(f"unknown format {fmt}")
     return pack_nibbles(c), s.view(np.uint16)
@@ -333,6 +404,11 @@ def dequant(fmt, packed, scale_bits=None, gscale=None):
     g = group_size(fmt)
     nib = unpack_nibbles(packed)
     vals = _decode(fmt, nib).astype(np.float32)
+    if fmt == FMT_MXFP4:  # value(code) * 2^(byte - 127): exact in fp32 for the bytes the quantiser emits
+        s_full = np.repeat(e8m0_value(np.asarray(scale_bits, dtype=np.uint8)), g, axis=-1)
+        out = vals.astype(np.float64) * s_full
+        assert np.array_equal(out.astype(np.float32).astype(np.float64), out)
+        return out.astype(np.float32)
     if fmt == FMT_NVFP4:
         if gscale is None:
             raise ValueError("NVFP4 needs the global scale")

@@ -37,7 +37,7 @@ x = 0 gives exactly 0; one-hot x picks a column of the dequantised matrix.
 
 import numpy as np
 
-from .formats import FMT_E2M1, bf16_bits_to_f64, dequant
+from .formats import FMT_E2M1, FMT_MXFP4, bf16_bits_to_f64, dequant, mx_e4m3
 
 
 def _as_x(x_bits):
@@ -114,14 +114,21 @@ def silu(g):
     return g / (1.0 + np.exp(-g))
 
 
-def expert_ffn(w13_f32, w2_f32, x):
-    """SwiGLU expert on dequantised weights; x float64 [H] -> float64 [H]."""
+def expert_ffn(w13_f32, w2_f32, x, mx_act=False):
+    """SwiGLU expert on dequantised weights; x float64 [H] -> float64 [H].
+
+    mx_act: the MXFP4 path's activations — x and the intermediate h are
+    quantised to MXFP8 (formats.mx_e4m3) before their products."""
     w13 = np.asarray(w13_f32, dtype=np.float64)
     w2 = np.asarray(w2_f32, dtype=np.float64)
     inter = w13.shape[0] // 2
+    if mx_act:
+        x = mx_e4m3(x)[0]
     gu = w13 @ x
     g, u = gu[:inter], gu[inter:]
     h = silu(g) * u
+    if mx_act:
+        h = mx_e4m3(h)[0]
     return w2 @ h
 
 
@@ -193,13 +200,14 @@ def moe_experts(layer, x_bits, ids, weights):
     for t in range(xs.shape[0]):
         x = xs[t]
         acc = np.zeros(layer.hidden, dtype=np.float64)
+        mx = layer.fmt == FMT_MXFP4
         for j in range(ids.shape[1]):
             w13, w2 = layer.expert(int(ids[t, j]))
-            acc += weights[t, j] * expert_ffn(w13, w2, x)
+            acc += weights[t, j] * expert_ffn(w13, w2, x, mx)
         if layer.has_shared:
             sw13, sw2 = layer.shared()
             sig = shared_gate(layer.shared_gate_w, np.atleast_2d(x_bits)[t])
-            acc += sig * expert_ffn(sw13, sw2, x)
+            acc += sig * expert_ffn(sw13, sw2, x, mx and layer.shared_fmt == FMT_MXFP4)
         out[t] = acc
     return out
 
