@@ -169,9 +169,12 @@ def clone_layer(w4, layer):
 
 def weight_bytes(fmt, n, k):
     """Bytes of one quantised [n][k] matrix: codes, block scales (FP16 per 16 or per
-    128; NVFP4: one UE4M3 byte per 16 plus a 4-byte global scale)."""
+    128; NVFP4: one UE4M3 byte per 16 plus a 4-byte global scale; MXFP4: one
+    E8M0 byte per 32)."""
     if fmt == "nvfp4":
         return n * k // 2 + n * k // 16 + 4
+    if fmt == "mxfp4":
+        return n * k // 2 + n * k // 32
     if fmt == "bf16":
         return n * k * 2
     return n * k // 2 + n * k // (128 if fmt == "int4" else 16) * 2
@@ -216,6 +219,15 @@ def stage_bytes(shape, distinct, n_stages=3):
             "k_moe_down": nexp * w2 + dw2 + T * S * I * 4 + T * K * 8 + T * H * 2,
         }
     rows = T * K + T  # routed pairs + shared rows
+    if n_stages == 6:  # MX: x and h travel as MXFP8 (a byte per element + a scale byte per 32)
+        return {
+            "k_router": router,
+            "k_mx_quant": T * H * 2 + T * H * 33 // 32,
+            "k_moe_route_group": T * E * 4 + T * K * 8 + rows * 4,
+            "k_moe_mx13": nexp * w13 + T * H * 33 // 32 + rows * I * 33 // 32,
+            "k_moe_mx2": nexp * w2 + rows * I * 33 // 32 + rows * H * 4,
+            "k_moe_gcombine": rows * H * 4 + T * K * 8 + T * H * 2,
+        }
     return {
         "k_router": router,
         "k_moe_route_group": T * E * 4 + T * K * 8 + rows * 4,
@@ -226,7 +238,8 @@ def stage_bytes(shape, distinct, n_stages=3):
 
 
 STAGES = {3: ["k_router", "k_moe_w13", "k_moe_down"],
-          5: ["k_router", "k_moe_route_group", "k_moe_gw13", "k_moe_gw2", "k_moe_gcombine"]}
+          5: ["k_router", "k_moe_route_group", "k_moe_gw13", "k_moe_gw2", "k_moe_gcombine"],
+          6: ["k_router", "k_mx_quant", "k_moe_route_group", "k_moe_mx13", "k_moe_mx2", "k_moe_gcombine"]}
 
 
 # ----------------------------------------------------------------------------- CPU baseline
@@ -250,7 +263,8 @@ def cpu_baseline_moe(shape, tokens, reps):
     for t in range(tokens):
         ids, _ = ops.route(ops.router_logits(rw, xs[t], bias), shape.top_k)
         need.update(int(e) for e in ids)
-    ofmts = {"e2m1": oracle.FMT_E2M1, "int4": oracle.FMT_INT4, "nvfp4": oracle.FMT_NVFP4, "bf16": oracle.FMT_BF16}
+    ofmts = {"e2m1": oracle.FMT_E2M1, "int4": oracle.FMT_INT4, "nvfp4": oracle.FMT_NVFP4, "bf16": oracle.FMT_BF16,
+             "mxfp4": oracle.FMT_MXFP4}
     fmt = ofmts[shape.fmt]
     sfmt = ofmts[shape.shared_fmt] if shape.shared_fmt else fmt
     q13 = {e: oracle.quantize(fmt, synth.expert_w13(shape, e)) for e in need}
@@ -305,9 +319,21 @@ def cpu_baseline_gemv(shape, reps, max_rows=8192):
 # ----------------------------------------------------------------------------- GPU runs
 
 
+def workload_shapes(synth):
+    """bench workload name -> synth shape."""
+    return {"qwen-t1": synth.QWEN_MOE_T1, "qwen-t32": synth.QWEN_MOE_T32, "tiny": synth.TINY_MOE,
+            "gemv-e2m1": synth.GEMV_E2M1, "gemv-int4": synth.GEMV_INT4,
+            "qwen-t1-nvfp4": synth.QWEN_MOE_T1_NVFP4, "gemv-nvfp4": synth.GEMV_NVFP4,
+            "gemv-lmhead": synth.GEMV_LMHEAD, "qwen-t1-bf16shared": synth.QWEN_MOE_T1_BF16SH,
+            "qwen-t1-mxfp4": synth.QWEN_MOE_T1_MX, "qwen-t32-mxfp4": synth.QWEN_MOE_T32_MX}
+
+
+WORKLOADS = ["qwen-t1", "qwen-t32", "tiny", "gemv-e2m1", "gemv-int4", "qwen-t1-nvfp4", "gemv-nvfp4", "gemv-lmhead",
+             "qwen-t1-bf16shared", "qwen-t1-mxfp4", "qwen-t32-mxfp4"]
+
+
 def run_moe(args, torch, w4, wl, synth):
-    shape = {"qwen-t1": synth.QWEN_MOE_T1, "qwen-t32": synth.QWEN_MOE_T32, "tiny": synth.TINY_MOE,
-             "qwen-t1-nvfp4": synth.QWEN_MOE_T1_NVFP4, "qwen-t1-bf16shared": synth.QWEN_MOE_T1_BF16SH}[args.workload]
+    shape = workload_shapes(synth)[args.workload]
     T = shape.tokens
     print(f"[bench] building {shape.name} ({args.replicas} replicas)", file=sys.stderr, flush=True)
     base = wl.build_moe_layer(shape, device="cuda")
@@ -402,9 +428,11 @@ def run_moe(args, torch, w4, wl, synth):
             "top_k": shape.top_k, "inter": shape.inter, "shared_inter": shape.shared_inter,
             "tokens_per_step": T, "zipf_s": shape.zipf_s, "weights": {"e2m1": "E2M1 codes + FP16 scale per 16",
                         "nvfp4": "E2M1 codes + UE4M3 scale per 16 + fp32 scale per matrix",
-                        "int4": "int4 codes + FP16 scale per 128"}[shape.fmt]
+                        "int4": "int4 codes + FP16 scale per 128",
+                        "mxfp4": "E2M1 codes + E8M0 scale per 32"}[shape.fmt]
                        + (", shared expert bf16" if shape.shared_fmt == "bf16" else ""),
-            "activations": "bf16", "accumulate": "fp32", "layer_replicas": R, "token_pool": P,
+            "activations": ("bf16; MXFP8 (E4M3 + E8M0 per 32) inside the experts" if shape.fmt == "mxfp4"
+                            else "bf16"), "accumulate": "fp32", "layer_replicas": R, "token_pool": P,
             "mean_distinct_experts": d_mean, "timing": "HIP graph replay of the K steps",
         },
         "hbm_gbps": step_bytes / (ms_step * 1e-3) / 1e9,
@@ -426,8 +454,7 @@ def run_moe(args, torch, w4, wl, synth):
 
 
 def run_gemv(args, torch, w4, wl, synth):
-    shape = {"gemv-e2m1": synth.GEMV_E2M1, "gemv-int4": synth.GEMV_INT4, "gemv-nvfp4": synth.GEMV_NVFP4,
-             "gemv-lmhead": synth.GEMV_LMHEAD}[args.workload]
+    shape = workload_shapes(synth)[args.workload]
     print(f"[bench] building {shape.name} ({args.replicas} replicas)", file=sys.stderr, flush=True)
     base = wl.build_dense(shape, "cuda")
     reps = [base] + [w4.QMatrix(base.fmt, 1, base.n, base.k, base.codes.clone(), base.scales.clone(),
@@ -477,8 +504,7 @@ def main():
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="qwen-t1",
-                    choices=["qwen-t1", "qwen-t32", "tiny", "gemv-e2m1", "gemv-int4", "qwen-t1-nvfp4", "gemv-nvfp4",
-                             "gemv-lmhead", "qwen-t1-bf16shared"])
+                    choices=WORKLOADS)
     ap.add_argument("--replicas", type=int, default=0, help="weight replicas (0 = workload default)")
     ap.add_argument("--pool", type=int, default=64, help="token pool (MoE workloads)")
     ap.add_argument("--cpu-tokens", type=int, default=1)
@@ -491,18 +517,14 @@ def main():
     args = ap.parse_args()
     if args.ingest_counters:
         from bit_block_scaled_router_amd import synth
-        names = {"qwen-t1": synth.QWEN_MOE_T1, "qwen-t32": synth.QWEN_MOE_T32, "tiny": synth.TINY_MOE,
-                 "gemv-e2m1": synth.GEMV_E2M1, "gemv-int4": synth.GEMV_INT4,
-                 "qwen-t1-nvfp4": synth.QWEN_MOE_T1_NVFP4, "gemv-nvfp4": synth.GEMV_NVFP4,
-                 "gemv-lmhead": synth.GEMV_LMHEAD, "qwen-t1-bf16shared": synth.QWEN_MOE_T1_BF16SH}
-        ingest_counters(args.ingest_counters, names[args.workload].name)
+        ingest_counters(args.ingest_counters, workload_shapes(synth)[args.workload].name)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1).", file=sys.stderr)
         sys.exit(2)
     if args.replicas <= 0:  # enough weight bytes that the 256 MB Infinity Cache cannot hold them
         args.replicas = 4 if args.workload in ("gemv-lmhead",) or not args.workload.startswith("gemv") else 128
-    if args.workload == "qwen-t32":
+    if args.workload.startswith("qwen-t32"):
         args.pool = min(args.pool, 8)
 
     import torch

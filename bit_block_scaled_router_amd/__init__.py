@@ -25,6 +25,7 @@ from ._lib import (  # noqa: F401
     W4_FMT_INT4_F16S128,
     W4_FMT_NVFP4_E4M3S16,
     W4_FMT_BF16,
+    W4_FMT_MXFP4_E8M0S32,
     W4_LAYOUT_CANONICAL,
     W4_OK,
     MoELayerDesc,
@@ -34,11 +35,12 @@ from ._lib import (  # noqa: F401
     lib,
 )
 
-GROUP = {W4_FMT_E2M1_F16S16: 16, W4_FMT_INT4_F16S128: 128, W4_FMT_NVFP4_E4M3S16: 16}
+GROUP = {W4_FMT_E2M1_F16S16: 16, W4_FMT_INT4_F16S128: 128, W4_FMT_NVFP4_E4M3S16: 16, W4_FMT_MXFP4_E8M0S32: 32}
 FORMATS = {"e2m1": W4_FMT_E2M1_F16S16, "int4": W4_FMT_INT4_F16S128, "nvfp4": W4_FMT_NVFP4_E4M3S16,
-           "bf16": W4_FMT_BF16}
-# numpy dtype of one block scale per format (FP16 bit patterns or UE4M3 bytes)
-SCALE_DTYPE = {W4_FMT_E2M1_F16S16: np.uint16, W4_FMT_INT4_F16S128: np.uint16, W4_FMT_NVFP4_E4M3S16: np.uint8}
+           "bf16": W4_FMT_BF16, "mxfp4": W4_FMT_MXFP4_E8M0S32}
+# numpy dtype of one block scale per format (FP16 bit patterns, UE4M3 or E8M0 bytes)
+SCALE_DTYPE = {W4_FMT_E2M1_F16S16: np.uint16, W4_FMT_INT4_F16S128: np.uint16, W4_FMT_NVFP4_E4M3S16: np.uint8,
+               W4_FMT_MXFP4_E8M0S32: np.uint8}
 
 
 def _torch():
@@ -89,6 +91,7 @@ def w4_quantize(fmt, w, codes=None, scales=None):
 
     Returns (codes uint8 [n][k/2], scales [n][k/G]): FP16 bit patterns (uint16)
     for E2M1/int4; for NVFP4 (codes, UE4M3 bytes uint8, global scale float);
+    for MXFP4 (codes, E8M0 bytes uint8 [n][k/32]);
     for bf16 (bf16 bits uint16 [n][k],)."""
     w = np.ascontiguousarray(w, dtype=np.float32)
     if w.ndim != 2:
@@ -135,7 +138,7 @@ class QMatrix:
     def __init__(self, fmt, groups, n, k, codes, scales, global_scales=None, layout=W4_LAYOUT_CANONICAL):
         self.fmt, self.groups, self.n, self.k = fmt, groups, n, k
         # torch device tensors: uint8 codes, int16 (FP16 bits) or uint8 (UE4M3) scales,
-        # fp32 [groups] global scales (NVFP4)
+        # uint8 (E8M0) for MXFP4, fp32 [groups] global scales (NVFP4)
         self.codes, self.scales, self.global_scales = codes, scales, global_scales
         self.desc = W4Matrix(fmt, layout, groups, n, k, _ptr(codes), _ptr(scales), _ptr(global_scales))
 
@@ -151,7 +154,7 @@ class QMatrix:
     @classmethod
     def upload(cls, fmt, codes_np, scales_np, device="cuda", global_np=None):
         """codes_np [G][n][k/2] (or [n][k/2]), scales_np [G][n][k/Gs] (uint16 FP16 bits,
-        or uint8 UE4M3 for NVFP4), global_np fp32 [G] (NVFP4) -> device."""
+        or uint8 UE4M3 / E8M0 for NVFP4 / MXFP4), global_np fp32 [G] (NVFP4) -> device."""
         torch = _torch()
         c = np.ascontiguousarray(codes_np)
         s = np.ascontiguousarray(scales_np)

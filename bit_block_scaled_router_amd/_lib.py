@@ -25,6 +25,7 @@ W4_FMT_E2M1_F16S16 = 1
 W4_FMT_INT4_F16S128 = 2
 W4_FMT_NVFP4_E4M3S16 = 3
 W4_FMT_BF16 = 4
+W4_FMT_MXFP4_E8M0S32 = 5
 W4_LAYOUT_CANONICAL = 0
 
 # every symbol the header declares

@@ -21,11 +21,12 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 constexpr int FMT_E2M1 = 1;
 constexpr int FMT_INT4 = 2;
 constexpr int FMT_NVFP4 = 3;  // E2M1 codes, UE4M3 scale byte per 16, fp32 global scale per matrix
+constexpr int FMT_MXFP4 = 5;  // E2M1 codes, E8M0 scale byte per 32
 
 // bytes per block scale
 template <int FMT>
 constexpr uint32_t scale_bytes() {
-    return FMT == FMT_NVFP4 ? 1u : 2u;
+    return (FMT == FMT_NVFP4 || FMT == FMT_MXFP4) ? 1u : 2u;
 }
 
 // ---------------------------------------------------------------- conversions
@@ -165,6 +166,9 @@ __device__ __forceinline__ uint4 ld128(Buf b, uint32_t off) {
 __device__ __forceinline__ uint32_t ld32(Buf b, uint32_t off) {
     return __builtin_amdgcn_raw_buffer_load_b32(b.r, off, 0, 0);
 }
+__device__ __forceinline__ uint32_t ld8(Buf b, uint32_t off) {
+    return (uint32_t)(uint8_t)__builtin_amdgcn_raw_buffer_load_b8(b.r, off, 0, 0);
+}
 __device__ __forceinline__ uint32_t ld16(Buf b, uint32_t off) {
     return (uint32_t)(uint16_t)__builtin_amdgcn_raw_buffer_load_b16(b.r, off, 0, 0);
 }
@@ -242,6 +246,9 @@ template <int FMT>
 __device__ __forceinline__ f32x2 block_scales2(uint32_t sc) {
     if constexpr (FMT == FMT_NVFP4) {
         return __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(sc, 1.0f, false);
+    } else if constexpr (FMT == FMT_MXFP4) {  // one E8M0 byte for all 32 elements
+        const float s = __builtin_amdgcn_ldexpf(1.0f, (int)(sc & 0xFFu) - 127);
+        return f32x2{s, s};
     } else {
         return f32x2{f16_bits_to_f32(sc), f16_bits_to_f32(sc >> 16)};
     }
@@ -354,20 +361,23 @@ __device__ __forceinline__ float chunk_dot_f32(uint4 c, uint32_t sc, const float
 // zero.
 template <int FMT>
 __device__ __forceinline__ uint32_t scale_off(uint32_t row_elem0, int k0) {
-    return FMT == FMT_INT4 ? (row_elem0 + (uint32_t)(k0 >> 7)) * 2u
-                           : (row_elem0 + (uint32_t)(k0 >> 4)) * scale_bytes<FMT>();
+    return FMT == FMT_INT4    ? (row_elem0 + (uint32_t)(k0 >> 7)) * 2u
+           : FMT == FMT_MXFP4 ? (row_elem0 + (uint32_t)(k0 >> 5))
+                              : (row_elem0 + (uint32_t)(k0 >> 4)) * scale_bytes<FMT>();
 }
 template <int FMT>
 __device__ __forceinline__ uint32_t ld_scales(Buf b, uint32_t off) {
     if constexpr (FMT == FMT_E2M1)
         return ld32(b, off);
+    else if constexpr (FMT == FMT_MXFP4)
+        return ld8(b, off);  // one E8M0 byte
     else
         return ld16(b, off);  // int4: one FP16; NVFP4: two UE4M3 bytes
 }
 
 template <int FMT>
 __device__ __forceinline__ int scales_per_row(int k) {
-    return FMT == FMT_INT4 ? (k >> 7) : (k >> 4);
+    return FMT == FMT_INT4 ? (k >> 7) : FMT == FMT_MXFP4 ? (k >> 5) : (k >> 4);
 }
 
 // ---------------------------------------------------------------- top-k
@@ -463,6 +473,42 @@ __device__ __forceinline__ void e2m1x8_split(uint32_t c, float s_hi, float s_lo,
     v = e2m1x2_f32<3>(c); h[3] = pack_bf16_exact(v.x * s_hi, v.y * s_hi); l[3] = pack_bf16_exact(v.x * s_lo, v.y * s_lo);
     hi = __builtin_bit_cast(bf16x8, make_uint4(h[0], h[1], h[2], h[3]));
     lo = __builtin_bit_cast(bf16x8, make_uint4(l[0], l[1], l[2], l[3]));
+}
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+// Scaled FP4 x FP8 MFMA (gfx950 v_mfma_scale_f32_16x16x128_f8f6f4): D += A B with
+// A 16 rows x 128 K of E2M1 codes and B 128 K x 16 columns of E4M3 values, each
+// block of 32 K elements scaled by its E8M0 byte.  Lane l (g = l / 16): A holds
+// row l % 16, K = 32 g .. 32 g + 31 (16 bytes, low nibble = even element) and
+// that block's scale `sa`; B holds column l % 16, K = 16 g .. 16 g + 15 (b_lo) and
+// 64 + 16 g .. 64 + 16 g + 15 (b_hi), plus the column's scale of block g (`sb`);
+// D[4 g + j][l % 16] in component j (operand mapping measured on the device).
+__device__ __forceinline__ f32x4 mfma_mx(uint4 a, uint4 b_lo, uint4 b_hi, uint32_t sa, uint32_t sb, f32x4 c) {
+    const i32x8 A = {(int)a.x, (int)a.y, (int)a.z, (int)a.w, 0, 0, 0, 0};
+    const i32x8 B = {(int)b_lo.x, (int)b_lo.y, (int)b_lo.z, (int)b_lo.w,
+                     (int)b_hi.x, (int)b_hi.y, (int)b_hi.z, (int)b_hi.w};
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, B, c, 4, 0, 0, (int)sa, 0, (int)sb);
+}
+
+// MXFP8 quantisation of activations: shared exponent of a block with maximum
+// magnitude `amax`: floor(log2 amax) - 8 (E4M3's largest exponent), limited to
+// [-127, 127]; -127 for an all-zero block.
+__device__ __forceinline__ int mx8_exponent(float amax) {
+    if (!(amax > 0.f)) return -127;
+    int X = __builtin_amdgcn_frexp_expf(amax) - 1 - 8;  // amax = m 2^e, m in [0.5, 1)
+    return X < -127 ? -127 : (X > 127 ? 127 : X);
+}
+
+// Four activations -> four E4M3 bytes of v / 2^X, clamped to +-448, round to
+// nearest even (the conversion instruction with unit scale).
+__device__ __forceinline__ uint32_t mx8_pack4(float a, float b, float c, float d, int X) {
+    auto cl = [&](float v) { return fminf(fmaxf(__builtin_amdgcn_ldexpf(v, -X), -448.f), 448.f); };
+    typedef short s16x2 __attribute__((ext_vector_type(2)));
+    s16x2 w = {0, 0};
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w, cl(a), cl(b), 1.0f, false);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w, cl(c), cl(d), 1.0f, true);
+    return __builtin_bit_cast(uint32_t, w);
 }
 
 // One fp32 value -> bf16 hi (truncated) + bf16 lo (residual, rounded to

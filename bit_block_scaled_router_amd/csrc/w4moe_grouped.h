@@ -62,7 +62,47 @@ struct GCombineArgs {
     int H, E, K, T, P, lstride, has_shared;
 };
 
+// MX path (MXFP4 weights, MXFP8 activations): quantised activations in the
+// workspace, natural K order: xq [T][H] E4M3 bytes + xs [T][H/32] E8M0 bytes;
+// hq [P + T][I] + hs [P + T][I/32] likewise for the SwiGLU intermediate.
+struct MXQuantArgs {
+    const uint16_t *x;      // [rows][n] bf16
+    uint8_t *q;             // [rows][n]
+    uint8_t *s;             // [rows][n/32]
+    int rows, n;
+};
+
+struct MX13Args {
+    const uint8_t *codes;   // routed W13 [E][2I][H/2]
+    const uint8_t *scales;  // [E][2I][H/32] E8M0
+    const uint8_t *s_codes; // shared W13 or null
+    const uint8_t *s_scales;
+    const uint8_t *xq;      // [T][H]
+    const uint8_t *xs;      // [T][H/32]
+    const int32_t *grp;
+    const int32_t *pairs;
+    uint8_t *hq;            // [P + T][I]
+    uint8_t *hs;            // [P + T][I/32]
+    int H, I, K, T, P, Gmax, tiles;
+};
+
+struct MX2Args {
+    const uint8_t *codes;   // routed W2 [E][H][I/2]
+    const uint8_t *scales;  // [E][H][I/32]
+    const uint8_t *s_codes;
+    const uint8_t *s_scales;
+    const int32_t *grp;
+    const int32_t *pairs;
+    const uint8_t *hq;
+    const uint8_t *hs;
+    float *out;             // [P + T][H]
+    int H, I, K, T, P, Gmax, tiles;
+};
+
 size_t grouped_lds_bytes(int E, int P);
+void launch_mx_quant(MXQuantArgs &a, hipStream_t st, hipEvent_t e0, hipEvent_t e1);
+void launch_mx13(MX13Args &a, hipStream_t st, hipEvent_t e0, hipEvent_t e1);
+void launch_mx2(MX2Args &a, hipStream_t st, hipEvent_t e0, hipEvent_t e1);
 void launch_route_group(GroupArgs &a, hipStream_t st, hipEvent_t e0, hipEvent_t e1);
 void launch_gw13(GW13Args &a, hipStream_t st, hipEvent_t e0, hipEvent_t e1);
 void launch_gw2(GW2Args &a, hipStream_t st, hipEvent_t e0, hipEvent_t e1);

@@ -120,16 +120,18 @@ __global__ __launch_bounds__(1024) void k_moe_route_group(GroupArgs a) {
 // Which expert and which pairs a work unit covers.  Group slot 0 is the shared
 // expert (pairs P .. P+T-1, one per token) when there is one; the routed groups
 // follow in the order of the group table.
+template <typename S>
 struct GroupView {
     const uint8_t *codes;
-    const uint16_t *scales;
+    const S *scales;
     int off, m;  // first entry in the pair list, number of pairs
 };
 
-__device__ __forceinline__ GroupView group_view(const int32_t *grp, int gs, int Gmax, int P, int T, const uint8_t *codes,
-                                                const uint16_t *scales, size_t mat_codes, size_t mat_scales,
-                                                const uint8_t *s_codes, const uint16_t *s_scales) {
-    GroupView v{};
+template <typename S>
+__device__ __forceinline__ GroupView<S> group_view(const int32_t *grp, int gs, int Gmax, int P, int T,
+                                                   const uint8_t *codes, const S *scales, size_t mat_codes,
+                                                   size_t mat_scales, const uint8_t *s_codes, const S *s_scales) {
+    GroupView<S> v{};
     if (s_codes != nullptr) {
         if (gs == 0) {
             v.codes = s_codes, v.scales = s_scales, v.off = P, v.m = T;
@@ -164,7 +166,7 @@ __device__ __forceinline__ void gw13_unit(const GW13Args &a, int gs, int tile, f
     const int H = a.H, I = a.I;
     const uint32_t spr = (uint32_t)(H >> 4);
     const size_t mat_codes = (size_t)(2 * I) * (H >> 1), mat_scales = (size_t)(2 * I) * spr;
-    const GroupView gv = group_view(a.grp, gs, a.Gmax, a.P, a.T, a.codes, a.scales, mat_codes, mat_scales, a.s_codes,
+    const GroupView<uint16_t> gv = group_view(a.grp, gs, a.Gmax, a.P, a.T, a.codes, a.scales, mat_codes, mat_scales, a.s_codes,
                                     a.s_scales);
     const Buf cb = make_buf(gv.codes, (uint32_t)mat_codes);
     const Buf sb = make_buf(gv.scales, (uint32_t)(mat_scales * 2));
@@ -355,7 +357,7 @@ __device__ __forceinline__ void gw2_unit(const GW2Args &a, int gs, int tile, flo
     const int H = a.H, I = a.I;
     const uint32_t spr = (uint32_t)(I >> 4);
     const size_t mat_codes = (size_t)H * (I >> 1), mat_scales = (size_t)H * spr;
-    const GroupView gv = group_view(a.grp, gs, a.Gmax, a.P, a.T, a.codes, a.scales, mat_codes, mat_scales, a.s_codes,
+    const GroupView<uint16_t> gv = group_view(a.grp, gs, a.Gmax, a.P, a.T, a.codes, a.scales, mat_codes, mat_scales, a.s_codes,
                                     a.s_scales);
     const Buf cb = make_buf(gv.codes, (uint32_t)mat_codes);
     const Buf sb = make_buf(gv.scales, (uint32_t)(mat_scales * 2));
@@ -524,6 +526,269 @@ __global__ __launch_bounds__(256) void k_moe_gw2(GW2Args a) {
     }
 }
 
+// ================================================================= MX path
+
+// The MX path (MXFP4 weights, MXFP8 activations) runs every group on gfx950's
+// scaled FP4 MFMA (16 x 16 x 128 per instruction, E8M0 scale per 32 K on both
+// operands), so its units need no exact split of the scales.  Quantisation of
+// activations follows the OCP Microscaling conversion (mx8_exponent, mx8_pack4).
+
+// x bf16 [rows][n] -> MXFP8: one thread per 32-element block.
+__global__ __launch_bounds__(256) void k_mx_quant(MXQuantArgs a) {
+    const int nb = a.n >> 5;
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= a.rows * nb) return;
+    const int r = i / nb, b = i - r * nb;
+    const uint4 *src = reinterpret_cast<const uint4 *>(a.x + (size_t)r * a.n + 32 * b);
+    float v[32];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const uint4 u = src[q];
+        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+            v[8 * q + 2 * d] = __uint_as_float(w[d] << 16);
+            v[8 * q + 2 * d + 1] = __uint_as_float(w[d] & 0xFFFF0000u);
+        }
+    }
+    float amax = 0.f;
+#pragma unroll
+    for (int e = 0; e < 32; ++e) amax = fmaxf(amax, fabsf(v[e]));
+    const int X = mx8_exponent(amax);
+    uint32_t o[8];
+#pragma unroll
+    for (int d = 0; d < 8; ++d) o[d] = mx8_pack4(v[4 * d], v[4 * d + 1], v[4 * d + 2], v[4 * d + 3], X);
+    uint4 *dst = reinterpret_cast<uint4 *>(a.q + (size_t)r * a.n + 32 * b);
+    dst[0] = make_uint4(o[0], o[1], o[2], o[3]);
+    dst[1] = make_uint4(o[4], o[5], o[6], o[7]);
+    a.s[i] = (uint8_t)(X + 127);
+}
+
+// One unit of the MX W13 launch: group slot gs, gate rows 32 tile .. +32 and the
+// matching up rows (four 16-row MFMA tiles), so that each 32-element block of h
+// is complete here and is quantised in the epilogue.
+__device__ __forceinline__ void mx13_unit(const MX13Args &a, int gs, int tile, float (*red)[32][64]) {
+    const int lane = threadIdx.x & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int H = a.H, I = a.I;
+    const uint32_t spr = (uint32_t)(H >> 5);
+    const size_t mat_codes = (size_t)(2 * I) * (H >> 1), mat_scales = (size_t)(2 * I) * spr;
+    const GroupView<uint8_t> gv = group_view(a.grp, gs, a.Gmax, a.P, a.T, a.codes, a.scales, mat_codes, mat_scales, a.s_codes,
+                              a.s_scales);
+    const Buf cb = make_buf(gv.codes, (uint32_t)mat_codes);
+    const Buf sb = make_buf(gv.scales, (uint32_t)mat_scales);
+    const Buf xqb = make_buf(a.xq, (uint32_t)a.T * (uint32_t)H);
+    const Buf xsb = make_buf(a.xs, (uint32_t)a.T * (uint32_t)(H >> 5));
+    const int *plist = a.pairs + gv.off;
+    const int i0 = tile * 32;
+    const int r = lane & 15, g = lane >> 4;
+    const uint32_t rows[4] = {(uint32_t)(i0 + r), (uint32_t)(i0 + 16 + r), (uint32_t)(I + i0 + r),
+                              (uint32_t)(I + i0 + 16 + r)};
+    const int nchunks = H >> 7;
+    for (int n0 = 0; n0 < gv.m; n0 += 32) {
+        int pr[2], tk[2];
+        bool pv[2];
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+            const int idx = n0 + nt * 16 + r;
+            pv[nt] = idx < gv.m;
+            pr[nt] = pv[nt] ? plist[idx] : 0;
+            tk[nt] = token_of(pr[nt], a.P, a.K);
+        }
+        const bool two = n0 + 16 < gv.m;  // second column tile in use (uniform)
+        f32x4 acc[4][2];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) acc[t][0] = acc[t][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int c = wv; c < nchunks; c += 4) {
+            const int k0 = c * 128;
+            uint4 av[4];
+            uint32_t as[4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                av[t] = ld128(cb, rows[t] * (uint32_t)(H >> 1) + (uint32_t)((k0 + 32 * g) >> 1));
+                as[t] = ld8(sb, rows[t] * spr + (uint32_t)(k0 >> 5) + (uint32_t)g);
+            }
+            uint4 blo[2], bhi[2];
+            uint32_t bs[2];
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt) {
+                const bool on = (nt == 0 || two) && pv[nt];
+                const uint32_t xo = (uint32_t)(tk[nt] * H + k0 + 16 * g);
+                blo[nt] = ld128(xqb, on ? xo : OOB);
+                bhi[nt] = ld128(xqb, on ? xo + 64u : OOB);
+                bs[nt] = ld8(xsb, on ? (uint32_t)(tk[nt] * (H >> 5) + (k0 >> 5) + g) : OOB);
+            }
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+#pragma unroll
+                for (int nt = 0; nt < 2; ++nt) {
+                    if (nt == 1 && !two) break;
+                    acc[t][nt] = mfma_mx(av[t], blo[nt], bhi[nt], as[t], bs[nt], acc[t][nt]);
+                }
+        }
+        // fixed-order sum of the four K partials
+        if (wv > 0) {
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+#pragma unroll
+                for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) red[wv - 1][t * 8 + nt * 4 + j][lane] = acc[t][nt][j];
+        }
+        __syncthreads();
+        if (wv == 0) {
+#pragma unroll
+            for (int w = 0; w < 3; ++w)
+#pragma unroll
+                for (int t = 0; t < 4; ++t)
+#pragma unroll
+                    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) acc[t][nt][j] += red[w][t * 8 + nt * 4 + j][lane];
+            // lane holds rows 4g + j of both 16-row halves of column r: h of rows
+            // i0 + 4g + j (tile 0) and i0 + 16 + 4g + j (tile 1)
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt) {
+                float h[8];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const float g0 = acc[0][nt][j], u0 = acc[2][nt][j];
+                    const float g1 = acc[1][nt][j], u1 = acc[3][nt][j];
+                    h[j] = (g0 / (1.f + expf(-g0))) * u0;
+                    h[4 + j] = (g1 / (1.f + expf(-g1))) * u1;
+                }
+                float m = 0.f;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(h[e]));
+                m = fmaxf(m, __shfl_xor(m, 16));  // the 32 rows of column r sit in lanes r, r+16, r+32, r+48
+                m = fmaxf(m, __shfl_xor(m, 32));
+                const int X = mx8_exponent(m);
+                if (pv[nt]) {
+                    const size_t o = (size_t)pr[nt] * I + i0 + 4 * g;
+                    *reinterpret_cast<uint32_t *>(a.hq + o) = mx8_pack4(h[0], h[1], h[2], h[3], X);
+                    *reinterpret_cast<uint32_t *>(a.hq + o + 16) = mx8_pack4(h[4], h[5], h[6], h[7], X);
+                    if (g == 0) a.hs[(size_t)pr[nt] * (I >> 5) + (i0 >> 5)] = (uint8_t)(X + 127);
+                }
+            }
+        }
+        __syncthreads();
+    }
+}
+
+__global__ __launch_bounds__(256) void k_moe_mx13(MX13Args a) {
+    __shared__ float red[3][32][64];  // K partials of waves 1..3
+    const int nu = unit_count(a.grp, a.s_codes != nullptr, a.tiles);
+    for (int u = blockIdx.x; u < nu; u += gridDim.x) {
+        const int gs = u / a.tiles;
+        mx13_unit(a, gs, u - gs * a.tiles, red);
+    }
+}
+
+// One unit of the MX down launch: group slot gs, output rows 64 tile .. +64; the
+// waves split K (128-element chunks), each multiplies its chunk into all four
+// 16-row tiles, partials summed in wave order through LDS.
+__device__ __forceinline__ void mx2_unit(const MX2Args &a, int gs, int tile, float (*red)[4][8][64]) {
+    const int lane = threadIdx.x & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int H = a.H, I = a.I;
+    const uint32_t spr = (uint32_t)(I >> 5);
+    const size_t mat_codes = (size_t)H * (I >> 1), mat_scales = (size_t)H * spr;
+    const GroupView<uint8_t> gv = group_view(a.grp, gs, a.Gmax, a.P, a.T, a.codes, a.scales, mat_codes, mat_scales, a.s_codes,
+                              a.s_scales);
+    const Buf cb = make_buf(gv.codes, (uint32_t)mat_codes);
+    const Buf sb = make_buf(gv.scales, (uint32_t)mat_scales);
+    const uint32_t rowsall = (uint32_t)(a.P + a.T);
+    const Buf hqb = make_buf(a.hq, rowsall * (uint32_t)I);
+    const Buf hsb = make_buf(a.hs, rowsall * (uint32_t)(I >> 5));
+    const int *plist = a.pairs + gv.off;
+    const int r = lane & 15, g = lane >> 4;
+    const int u0 = tile * 64;
+    const int nchunks = I >> 7;
+    for (int n0 = 0; n0 < gv.m; n0 += 32) {
+        int pr[2];
+        bool pv[2];
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+            const int idx = n0 + nt * 16 + r;
+            pv[nt] = idx < gv.m;
+            pr[nt] = pv[nt] ? plist[idx] : 0;
+        }
+        const bool two = n0 + 16 < gv.m;
+        f32x4 acc[4][2];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) acc[t][0] = acc[t][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int c = wv; c < nchunks; c += 4) {
+            const int k0 = c * 128;
+            uint4 av[4];
+            uint32_t as[4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const uint32_t row = (uint32_t)(u0 + 16 * t + r);
+                const bool rv = (int)row < H;
+                av[t] = ld128(cb, rv ? row * (uint32_t)(I >> 1) + (uint32_t)((k0 + 32 * g) >> 1) : OOB);
+                as[t] = ld8(sb, rv ? row * spr + (uint32_t)(k0 >> 5) + (uint32_t)g : OOB);
+            }
+            uint4 blo[2], bhi[2];
+            uint32_t bs[2];
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt) {
+                const bool on = (nt == 0 || two) && pv[nt];
+                const uint32_t ho = (uint32_t)(pr[nt] * I + k0 + 16 * g);
+                blo[nt] = ld128(hqb, on ? ho : OOB);
+                bhi[nt] = ld128(hqb, on ? ho + 64u : OOB);
+                bs[nt] = ld8(hsb, on ? (uint32_t)(pr[nt] * (I >> 5) + (k0 >> 5) + g) : OOB);
+            }
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+#pragma unroll
+                for (int nt = 0; nt < 2; ++nt) {
+                    if (nt == 1 && !two) break;
+                    acc[t][nt] = mfma_mx(av[t], blo[nt], bhi[nt], as[t], bs[nt], acc[t][nt]);
+                }
+        }
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) red[wv][t][nt * 4 + j][lane] = acc[t][nt][j];
+        __syncthreads();
+        float v[2][4];
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                float sum = red[0][wv][nt * 4 + j][lane];
+#pragma unroll
+                for (int w = 1; w < 4; ++w) sum += red[w][wv][nt * 4 + j][lane];
+                v[nt][j] = sum;
+            }
+        __syncthreads();
+        const int rb = u0 + 16 * wv + 4 * g;  // lane holds rows rb .. rb+3 of column r
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+            if (!pv[nt]) continue;
+            float *op = a.out + (size_t)pr[nt] * H + rb;
+            if (rb + 3 < H) {
+                *reinterpret_cast<float4 *>(op) = make_float4(v[nt][0], v[nt][1], v[nt][2], v[nt][3]);
+            } else {
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    if (rb + j < H) op[j] = v[nt][j];
+            }
+        }
+    }
+}
+
+__global__ __launch_bounds__(256) void k_moe_mx2(MX2Args a) {
+    __shared__ float red[4][4][8][64];
+    const int nu = unit_count(a.grp, a.s_codes != nullptr, a.tiles);
+    for (int u = blockIdx.x; u < nu; u += gridDim.x) {
+        const int gs = u / a.tiles;
+        mx2_unit(a, gs, u - gs * a.tiles, red);
+    }
+}
+
 // ================================================================= combine
 
 __global__ __launch_bounds__(256) void k_moe_gcombine(GCombineArgs a) {
@@ -615,6 +880,21 @@ void launch_gw2(GW2Args &a, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
     case 32: go_ev(st, e0, e1, k_moe_gw2<32>, g, b, 0, a); break;
     default: go_ev(st, e0, e1, k_moe_gw2<64>, g, b, 0, a); break;
     }
+}
+
+void launch_mx_quant(MXQuantArgs &a, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
+    const int blocks = a.rows * (a.n >> 5);
+    go_ev(st, e0, e1, k_mx_quant, dim3((unsigned)((blocks + 255) / 256)), dim3(256), 0, a);
+}
+
+void launch_mx13(MX13Args &a, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
+    a.tiles = a.I / 32;
+    go_ev(st, e0, e1, k_moe_mx13, dim3(grouped_grid(a.Gmax, a.tiles)), dim3(256), 0, a);
+}
+
+void launch_mx2(MX2Args &a, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
+    a.tiles = (a.H + 63) / 64;
+    go_ev(st, e0, e1, k_moe_mx2, dim3(grouped_grid(a.Gmax, a.tiles)), dim3(256), 0, a);
 }
 
 void launch_gcombine(GCombineArgs &a, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {

@@ -34,6 +34,7 @@ int group_of(int32_t format) {
     case W4_FMT_INT4_F16S128: return 128;
     case W4_FMT_NVFP4_E4M3S16: return 16;
     case W4_FMT_BF16: return 32;  // no scale blocks; k must be a multiple of 32
+    case W4_FMT_MXFP4_E8M0S32: return 32;
     default: return 0;
     }
 }
@@ -119,7 +120,17 @@ static void quantize_rows(int32_t format, const float *w, int64_t r0, int64_t r1
             float a = 0.f;
             for (int i = 0; i < g; ++i) a = std::fmax(a, std::fabs(wb[i]));
             float s;  // the divisor of the codes
-            if (format == W4_FMT_NVFP4_E4M3S16) {
+            if (format == W4_FMT_MXFP4_E8M0S32) {  // shared exponent floor(log2 a) - 2
+                int X = -127;
+                if (a > 0.f) {
+                    int e;
+                    std::frexp(a, &e);  // a = f 2^e, f in [0.5, 1): floor(log2 a) = e - 1
+                    X = e - 1 - 2;
+                    X = X < -127 ? -127 : (X > 127 ? 127 : X);
+                }
+                static_cast<uint8_t *>(scales)[r * nb + b] = (uint8_t)(X + 127);
+                s = a > 0.f ? std::ldexp(1.0f, X) : 0.f;  // power of two: the division below is exact
+            } else if (format == W4_FMT_NVFP4_E4M3S16) {
                 const uint8_t sb = gscale != 0.f ? f32_to_ue4m3((a / 6.0f) / gscale) : 0;
                 static_cast<uint8_t *>(scales)[r * nb + b] = sb;
                 s = ue4m3_to_f32(sb) * gscale;  // fp32 product
@@ -185,7 +196,7 @@ size_t w4_codes_bytes(int32_t format, int32_t layout, int64_t groups, int64_t n,
 size_t w4_scales_bytes(int32_t format, int32_t layout, int64_t groups, int64_t n, int64_t k) {
     if (check_shape(format, layout, groups, n, k) != W4_OK) return 0;
     if (format == W4_FMT_BF16) return 0;
-    const size_t bytes = format == W4_FMT_NVFP4_E4M3S16 ? 1 : 2;
+    const size_t bytes = (format == W4_FMT_NVFP4_E4M3S16 || format == W4_FMT_MXFP4_E8M0S32) ? 1 : 2;
     return (size_t)groups * (size_t)n * (size_t)(k / group_of(format)) * bytes;
 }
 
@@ -221,7 +232,7 @@ int w4_quantize(int32_t format, const float *w, int64_t n, int64_t k, uint8_t *c
         for (int64_t i = 0; i < total; ++i) amax = std::fmax(amax, std::fabs(w[i]));
         gscale = amax / 2688.0f;  // 6 x 448
         *global_scale = gscale;
-    } else {
+    } else if (format != W4_FMT_MXFP4_E8M0S32) {  // E8M0 covers every finite fp32 block
         for (int64_t b = 0; b < total / g; ++b) {
             float a = 0.f;
             for (int i = 0; i < g; ++i) a = std::fmax(a, std::fabs(w[b * g + i]));

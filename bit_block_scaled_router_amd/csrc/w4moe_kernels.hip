@@ -112,7 +112,7 @@ __global__ __launch_bounds__(256) void k_dequant(const uint8_t *__restrict__ cod
         const uint32_t sc = ld_scales<FMT>(sb, rv ? scale_off<FMT>(rl * spr, k0) : OOB);
         const uint32_t cw[4] = {c.x, c.y, c.z, c.w};
         float v[32];
-        if constexpr (FMT == FMT_E2M1 || FMT == FMT_NVFP4) {
+        if constexpr (FMT != FMT_INT4) {
             const f32x2 s2 = block_scales2<FMT>(sc);
 #pragma unroll
             for (int d = 0; d < 4; ++d) {
@@ -662,10 +662,10 @@ constexpr int MAX_GROUPED_PAIRS = 4096;
 struct MoEPlan {
     int H, I, E, K, S, T;
     int L13, L2, hstride, lstride;
-    bool grouped;
+    bool grouped, mx;
     int P, Gmax;
     size_t off_logits, off_ids, off_w, off_h, total;
-    size_t off_grp, off_pairs, off_hp, off_out;
+    size_t off_grp, off_pairs, off_hp, off_out, off_xq;
 };
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
@@ -698,6 +698,8 @@ int check_layer(const moe_w4a16_layer *Lr, int64_t T, MoEPlan &p) {
         const int32_t sf = Lr->shared_w13.format;
         if ((sf != fmt && sf != W4_FMT_BF16) || Lr->shared_w2.format != sf)
             return fail(W4_ERR_LAYOUT, "shared expert must use the routed experts' format or bf16 for both matrices");
+        if (fmt == W4_FMT_MXFP4_E8M0S32 && sf == W4_FMT_BF16)
+            return fail(W4_ERR_UNSUPPORTED, "the MXFP4 path takes an MXFP4 shared expert");
         if (Lr->shared_w13.groups != 1 || Lr->shared_w13.n != 2 * I || Lr->shared_w13.k != H)
             return fail(W4_ERR_INVALID_ARG, "shared_w13 must be [1][2I][H]");
         if (Lr->shared_w2.groups != 1 || Lr->shared_w2.n != H || Lr->shared_w2.k != I)
@@ -718,9 +720,18 @@ int check_layer(const moe_w4a16_layer *Lr, int64_t T, MoEPlan &p) {
     p.P = (int)(T * K);
     p.Gmax = (int)(E < p.P ? E : p.P);
     // (the VALU small-group path keeps at most 2 k-steps of 32 x 64 elements)
+    p.mx = fmt == W4_FMT_MXFP4_E8M0S32;
     p.grouped = T >= W4_GROUPED_MIN_T && fmt == W4_FMT_E2M1_F16S16 && H % 128 == 0 && I % 128 == 0 &&
                 p.P <= MAX_GROUPED_PAIRS && H <= 4096 && I <= 4096 &&
                 !(Lr->has_shared && Lr->shared_w13.format == W4_FMT_BF16);
+    if (p.mx) {  // every batch size runs grouped, all on the scaled FP4 MFMA
+        if (H % 128 || I % 128)
+            return fail(W4_ERR_UNSUPPORTED, "MXFP4 layers need hidden and inter multiples of 128");
+        if (p.P > MAX_GROUPED_PAIRS)
+            return fail(W4_ERR_UNSUPPORTED, "MXFP4 layers take at most %d (token, slot) pairs per call",
+                        MAX_GROUPED_PAIRS);
+        p.grouped = true;
+    }
     size_t off = 0;
     p.off_logits = off; off = align_up(off + (size_t)T * p.lstride * 4, 256);
     p.off_ids = off;    off = align_up(off + (size_t)T * K * 4, 256);
@@ -731,8 +742,11 @@ int check_layer(const moe_w4a16_layer *Lr, int64_t T, MoEPlan &p) {
         const size_t rows = (size_t)p.P + (size_t)T;
         p.off_grp = off;   off = align_up(off + (size_t)(1 + 3 * p.Gmax) * 4, 256);
         p.off_pairs = off; off = align_up(off + rows * 4, 256);
-        p.off_hp = off;    off = align_up(off + rows * (size_t)I * 4, 256);  // h_hi then h_lo, bf16
+        p.off_hp = off;    off = align_up(off + rows * (size_t)I * 4, 256);  // h_hi then h_lo, bf16 (MX: codes, scales)
         p.off_out = off;   off = align_up(off + rows * (size_t)H * 4, 256);
+        if (p.mx) {  // x as MXFP8: codes [T][H], then scales [T][H/32]
+            p.off_xq = off; off = align_up(off + (size_t)T * H + (size_t)T * (H / 32), 256);
+        }
     }
     p.total = off;
     return W4_OK;
@@ -869,7 +883,7 @@ int run_moe(const moe_w4a16_layer *Lr, const uint16_t *x, int64_t T, const int32
     float *h = (float *)(wsb + p.off_h);
 
     if (events) {
-        const int need = p.grouped ? 10 : 6;
+        const int need = p.mx ? 12 : p.grouped ? 10 : 6;
         if (n_events < need)
             return fail(W4_ERR_INVALID_ARG, "%s path needs %d events, got %d", p.grouped ? "grouped" : "single-token",
                         need, n_events);
@@ -966,6 +980,34 @@ int run_grouped(const moe_w4a16_layer *Lr, const MoEPlan &p, const uint16_t *x, 
     ga.ids_user = route ? topk_ids : nullptr, ga.w_user = route ? topk_w : nullptr;
     ga.grp = grp, ga.pairs = pairs;
     ga.E = p.E, ga.K = p.K, ga.T = p.T, ga.P = p.P, ga.Gmax = p.Gmax, ga.lstride = p.lstride, ga.route = route ? 1 : 0;
+    if (p.mx) {
+        // x -> MXFP8 (its own stage, recorded between router and grouping)
+        uint8_t *xq = (uint8_t *)(wsb + p.off_xq);
+        MXQuantArgs q{};
+        q.x = x, q.q = xq, q.s = xq + (size_t)p.T * p.H, q.rows = p.T, q.n = p.H;
+        launch_mx_quant(q, sm, ev(2), ev(3));
+        if ((st = hip_status("mx quantise launch"))) return st;
+        launch_route_group(ga, sm, ev(4), ev(5));
+        if ((st = hip_status("route/group launch"))) return st;
+        const size_t rows = (size_t)p.P + p.T;
+        uint8_t *hq = (uint8_t *)(wsb + p.off_hp), *hs = hq + rows * p.I;
+        MX13Args a{};
+        a.codes = Lr->w13.codes, a.scales = (const uint8_t *)Lr->w13.scales;
+        a.s_codes = Lr->has_shared ? Lr->shared_w13.codes : nullptr;
+        a.s_scales = Lr->has_shared ? (const uint8_t *)Lr->shared_w13.scales : nullptr;
+        a.xq = q.q, a.xs = q.s, a.grp = grp, a.pairs = pairs, a.hq = hq, a.hs = hs;
+        a.H = p.H, a.I = p.I, a.K = p.K, a.T = p.T, a.P = p.P, a.Gmax = p.Gmax;
+        launch_mx13(a, sm, ev(6), ev(7));
+        if ((st = hip_status("mx w13 launch"))) return st;
+        MX2Args d{};
+        d.codes = Lr->w2.codes, d.scales = (const uint8_t *)Lr->w2.scales;
+        d.s_codes = Lr->has_shared ? Lr->shared_w2.codes : nullptr;
+        d.s_scales = Lr->has_shared ? (const uint8_t *)Lr->shared_w2.scales : nullptr;
+        d.grp = grp, d.pairs = pairs, d.hq = hq, d.hs = hs, d.out = outp;
+        d.H = p.H, d.I = p.I, d.K = p.K, d.T = p.T, d.P = p.P, d.Gmax = p.Gmax;
+        launch_mx2(d, sm, ev(8), ev(9));
+        if ((st = hip_status("mx w2 launch"))) return st;
+    } else {
     launch_route_group(ga, sm, ev(2), ev(3));
     if ((st = hip_status("route/group launch"))) return st;
     // 3) grouped W13 + SiLU
@@ -986,13 +1028,14 @@ int run_grouped(const moe_w4a16_layer *Lr, const MoEPlan &p, const uint16_t *x, 
     d.H = p.H, d.I = p.I, d.K = p.K, d.T = p.T, d.P = p.P, d.Gmax = p.Gmax, d.mfma_min = W4_MFMA_MIN;
     launch_gw2(d, sm, ev(6), ev(7));
     if ((st = hip_status("grouped w2 launch"))) return st;
+    }
     // 5) ordered combine
     GCombineArgs c{};
     c.ids = route ? ids_ws : ids_in;
     c.w = route ? w_ws : w_in;
     c.logits = logits, c.out = outp, c.y = y;
     c.H = p.H, c.E = p.E, c.K = p.K, c.T = p.T, c.P = p.P, c.lstride = p.lstride, c.has_shared = Lr->has_shared;
-    launch_gcombine(c, sm, ev(8), ev(9));
+    launch_gcombine(c, sm, ev(p.mx ? 10 : 8), ev(p.mx ? 11 : 9));
     return hip_status("combine launch");
 }
 
@@ -1006,6 +1049,8 @@ int w4a16_gemv(const w4_matrix *W, const uint16_t *x, int64_t m, uint16_t *y, vo
     if (st) return st;
     if (W->groups != 1) return fail(W4_ERR_INVALID_ARG, "gemv needs groups == 1");
     if (W->format == W4_FMT_BF16) return fail(W4_ERR_UNSUPPORTED, "bf16 matrices serve only as the shared expert");
+    if (W->format == W4_FMT_MXFP4_E8M0S32)
+        return fail(W4_ERR_UNSUPPORTED, "MXFP4 matrices serve the MoE layer (MXFP8 activations), not the GEMV");
     if (m < 1 || m > 64) return fail(W4_ERR_UNSUPPORTED, "m=%lld out of [1, 64]", (long long)m);
     if (!x || !y) return fail(W4_ERR_INVALID_ARG, "null x or y");
     if (!aligned(x, 16)) return fail(W4_ERR_ALIGNMENT, "x not 16-byte aligned");
@@ -1029,6 +1074,7 @@ int w4_dequant_device(const w4_matrix *W, float *out, void *stream) {
     hipStream_t sm = (hipStream_t)stream;
     if (W->format == W4_FMT_E2M1_F16S16) launch_dequant<FMT_E2M1>(W, out, sm);
     else if (W->format == W4_FMT_NVFP4_E4M3S16) launch_dequant<FMT_NVFP4>(W, out, sm);
+    else if (W->format == W4_FMT_MXFP4_E8M0S32) launch_dequant<FMT_MXFP4>(W, out, sm);
     else launch_dequant<FMT_INT4>(W, out, sm);
     return hip_status("dequant launch");
 }
@@ -1056,7 +1102,7 @@ int moe_w4a16_forward_timed(const moe_w4a16_layer *L, const uint16_t *x, int64_t
 int moe_w4a16_stage_count(const moe_w4a16_layer *L, int64_t T) {
     MoEPlan p;
     if (check_layer(L, T, p) != W4_OK) return 0;
-    return p.grouped ? 5 : 3;
+    return p.mx ? 6 : p.grouped ? 5 : 3;
 }
 
 int moe_w4a16_experts(const moe_w4a16_layer *L, const uint16_t *x, int64_t T, const int32_t *ids, const float *w,

@@ -77,6 +77,15 @@ extern "C" {
  * layer (the pages' engine keeps it in bf16: lynn-engine README P15/P37) and by
  * w4_quantize (round to nearest even); the GEMV and dequant hook reject it. */
 #define W4_FMT_BF16 4
+/* MXFP4 (OCP Microscaling v1.0): E2M1 codes with one E8M0 scale byte (2^(byte -
+ * 127)) per 32 K elements; scales [groups][n][k/32] bytes.  The vendor
+ * block-scaled format the pages bridge to (README P17/P54, R5-B "e8m0/group32").
+ * In an MoE layer it runs on gfx950's scaled FP4 MFMA with MXFP8 activations:
+ * the layer input and the SwiGLU intermediate are quantised to E4M3 elements with
+ * an E8M0 scale per 32 (X = floor(log2 absmax) - 8, round to nearest even,
+ * clamp to +-448), so such a layer computes W4A8 (MX), every T on the batched
+ * path; the dense GEMV does not take this format. */
+#define W4_FMT_MXFP4_E8M0S32 5
 
 /* Canonical layout, the only one this library reads:
  *   codes  [groups][n][k/2] bytes, element 2j in the low nibble of byte j and
@@ -141,6 +150,9 @@ size_t w4_scales_bytes(int32_t format, int32_t layout, int64_t groups, int64_t n
  *   ties to even, +0 for zero; an all-zero matrix has g = 0.
  * bf16: codes receives bf16 bit patterns [n][k] (round to nearest even), scales
  * and global_scale are unused.
+ * MXFP4: per 32 elements X = floor(log2 absmax) - 2 (limited to [-127, 127]),
+ * scale byte X + 127, code = nearest E2M1 value to w / 2^X, ties to even,
+ * clamped to +-6, +0 for zero; an all-zero block has byte 0.
  * global_scale may be NULL for the FP16-scale formats.
  * Errors: W4_ERR_NONFINITE (Inf/NaN input), W4_ERR_RANGE (a block scale would
  * overflow fp16), W4_ERR_INVALID_ARG, W4_ERR_LAYOUT.  Synchronous, thread-safe. */

@@ -207,20 +207,24 @@ def quantize_mxfp4(w):
     return codes, (X + 127).astype(np.uint8)
 
 
-def mx_e4m3(v):
+def mx_e4m3(v, X=None):
     """MXFP8 (E4M3 elements, E8M0 per 32) quantisation of activations along the
     last axis, returned dequantised (float64, exact) with the scale exponents.
 
     Per block: X = floor(log2(absmax)) - 8; q = E4M3 round-to-nearest-even of
     clamp(v / 2^X, +-448) (sign of zero kept); value = q * 2^X.  A zero block has
-    X = -127 and zero values."""
+    X = -127 and zero values.  X (int array, one per block) may be given to
+    quantise under another shared exponent (the other side of an absmax that
+    sits on a power of two)."""
     a = np.asarray(v, dtype=np.float64)
     shp = a.shape
     if shp[-1] % MX_BLOCK:
         raise ValueError("length not a multiple of 32")
     b = a.reshape(shp[:-1] + (shp[-1] // MX_BLOCK, MX_BLOCK))
     amax = np.abs(b).max(axis=-1)
-    X = np.where(amax > 0, _mx_exponent(np.where(amax > 0, amax, 1.0), 8), -127)
+    if X is None:
+        X = np.where(amax > 0, _mx_exponent(np.where(amax > 0, amax, 1.0), 8), -127)
+    X = np.asarray(X, dtype=np.int64)
     r = np.clip(b / np.exp2(X.astype(np.float64))[..., None], -E4M3_MAX, E4M3_MAX)
     q = e4m3_value(_ue4m3_rne(np.abs(r))) * np.where(np.signbit(r), -1.0, 1.0)
     return (q * np.exp2(X.astype(np.float64))[..., None]).reshape(shp), X

@@ -148,6 +148,65 @@ def test_quantizer_nvfp4_golden_and_sizes():
     assert st == w4.W4_ERR_INVALID_ARG
 
 
+def test_quantizer_mxfp4_matches_oracle():
+    import test_oracle_mx as T
+    rng = np.random.default_rng(24)
+    cases = [
+        (rng.standard_normal((64, 256)) * 0.02 * np.exp2(rng.integers(-8, 8, (64, 1)))).astype(np.float32),
+        np.concatenate([(rng.standard_normal((4, 64)) * s).astype(np.float32) for s in (1.0, 1e-3, 1e-30, 1e-40)]),
+        np.zeros((3, 64), dtype=np.float32),
+        synth.expert_w13(synth.QWEN_MOE_T1, 5),
+    ]
+    fmt = w4.W4_FMT_MXFP4_E8M0S32
+    for w in cases:
+        c_lib, s_lib = w4.w4_quantize(fmt, w)
+        c_or, s_or = oracle.quantize(F.FMT_MXFP4, w)
+        assert s_lib.dtype == np.uint8 and np.array_equal(s_lib, s_or)
+        assert np.array_equal(c_lib, c_or)
+    for b in T._blocks():
+        c, s = w4.w4_quantize(fmt, b["w"][None])
+        assert int(s[0, 0]) == b["scale"] and np.array_equal(w4.w4_unpack_nibbles(c)[0], b["codes"]), b["name"]
+    assert w4.w4_scales_bytes(fmt, 2, 3, 64) == oracle.scales_bytes(F.FMT_MXFP4, 2, 3, 64) == 12
+    with pytest.raises(w4.W4Error) as e:
+        w4.w4_quantize(fmt, np.zeros((1, 48), dtype=np.float32))  # k must be a multiple of 32
+    assert e.value.status == w4.W4_ERR_INVALID_ARG
+
+
+def test_mxfp4_layer_plan_and_validation():
+    mx = w4.W4_FMT_MXFP4_E8M0S32
+    H, I, E = 256, 128, 8
+
+    def mxl(**over):
+        d = dict(w13=_mat(fmt=mx, groups=E, n=2 * I, k=H), w2=_mat(fmt=mx, groups=E, n=H, k=I),
+                 shared_w13=_mat(fmt=mx, groups=1, n=2 * I, k=H), shared_w2=_mat(fmt=mx, groups=1, n=H, k=I))
+        d.update(over)
+        return _layer(**d)
+
+    L = mxl()
+    # every batch size takes the grouped MX path: router, x -> MXFP8, grouping,
+    # W13, W2, combine
+    assert w4.lib().moe_w4a16_stage_count(C.byref(L), 1) == 6
+    assert w4.lib().moe_w4a16_stage_count(C.byref(L), 64) == 6
+    assert w4.lib().moe_w4a16_workspace_bytes(C.byref(L), 1) > 0
+    # 2048 tokens x top-2 = 4096 pairs is the limit
+    assert w4.lib().moe_w4a16_workspace_bytes(C.byref(L), 2048) > 0
+    assert w4.lib().moe_w4a16_workspace_bytes(C.byref(L), 2049) == 0
+    assert _fwd(L, T=2049, ws_bytes=1 << 30) == w4.W4_ERR_UNSUPPORTED
+    # inter off the 128 grid, a bf16 shared expert, mixed formats
+    bad_i = _layer(inter=96, shared_inter=96, w13=_mat(fmt=mx, groups=E, n=192, k=H), w2=_mat(fmt=mx, groups=E, n=H, k=96),
+                   has_shared=0)
+    assert _fwd(bad_i, ws_bytes=1 << 30) == w4.W4_ERR_UNSUPPORTED
+    bf = w4.W4_FMT_BF16
+    assert _fwd(mxl(shared_w13=_mat(fmt=bf, groups=1, n=2 * I, k=H, scales=None),
+                    shared_w2=_mat(fmt=bf, groups=1, n=H, k=I, scales=None)), ws_bytes=1 << 30) == w4.W4_ERR_UNSUPPORTED
+    assert _fwd(mxl(w2=_mat(groups=E, n=H, k=I)), ws_bytes=1 << 30) == w4.W4_ERR_LAYOUT
+    # the timed entry point wants 12 events on the MX path
+    ev = (C.c_void_p * 10)(*([1] * 10))
+    st = w4.lib().moe_w4a16_forward_timed(C.byref(L), 1 << 20, 1, 1 << 21, None, None, 1 << 24,
+                                          w4.lib().moe_w4a16_workspace_bytes(C.byref(L), 1), 0, ev, 10)
+    assert st == w4.W4_ERR_INVALID_ARG
+
+
 def test_bf16_format_quantiser_sizes_and_rules():
     rng = np.random.default_rng(23)
     w = (rng.standard_normal((5, 64)) * 0.02).astype(np.float32)
@@ -190,7 +249,8 @@ def _gemv(W, x=1 << 20, m=1, y=1 << 21):
 
 
 def test_gemv_validation_returns_before_launch():
-    assert _gemv(_mat(fmt=5)) == w4.W4_ERR_LAYOUT
+    assert _gemv(_mat(fmt=9)) == w4.W4_ERR_LAYOUT
+    assert _gemv(_mat(fmt=w4.W4_FMT_MXFP4_E8M0S32)) == w4.W4_ERR_UNSUPPORTED  # MX serves the MoE layer
     assert _gemv(_mat(layout=1)) == w4.W4_ERR_LAYOUT
     assert _gemv(_mat(k=48)) == w4.W4_ERR_INVALID_ARG
     assert _gemv(_mat(fmt=w4.W4_FMT_INT4_F16S128, k=64)) == w4.W4_ERR_INVALID_ARG
