@@ -196,7 +196,8 @@ int w4_dequant_device(const w4_matrix *W, float *out, void *stream);
  *     shared_gate_w bf16 [H]: sigma = sigmoid(shared_gate_w . x)
  * This build requires shared_inter == inter and H % 64 == 0; the routed experts
  * use one format (NVFP4: one global scale per expert matrix, applied to the
- * gate/up sums and to the down sums), the shared expert that format or bf16. */
+ * gate/up sums and to the down sums), the shared expert that format or bf16
+ * (MXFP4: that format only). */
 typedef struct moe_w4a16_layer {
     int64_t hidden;              /* H */
     int64_t inter;               /* I (expert intermediate) */
@@ -252,7 +253,10 @@ int moe_w4a16_forward_timed(const moe_w4a16_layer *L, const uint16_t *x, int64_t
  * group, on MFMA for groups of at least 4 tokens; W2 per expert group; ordered
  * combine).  The batched path serves E2M1 layers with H and I multiples of 128
  * and at most 4096, T >= 4 and T * top_k <= 4096; other requests take the
- * single-token path.
+ * single-token path.  MXFP4 layers always run 6 kernels (router; x to MXFP8;
+ * top-k and grouping; W13 + SiLU with h quantised to MXFP8; W2; ordered
+ * combine), need H and I multiples of 128 and T * top_k <= 4096, and a shared
+ * expert in MXFP4 (W4_ERR_UNSUPPORTED otherwise).
  * Sources: lynn-engine README, R5 notes (tokens-per-expert grouping, inverse
  * scatter) and P85-P92 (per-16 scales applied exactly). */
 int moe_w4a16_stage_count(const moe_w4a16_layer *L, int64_t T);
