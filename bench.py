@@ -35,6 +35,9 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X published HBM3E bandwidth
+# MI355X published dense matrix peaks (TFLOP/s): the exact-split E2M1 path runs
+# bf16 MFMA; the MX path's fp4 x fp8 scaled MFMA is priced at the fp8 rate
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0}
 METRIC = "MoE-layer µs/token and achieved HBM GB/s (% of peak), W4A16 decode"
 
 
@@ -219,6 +222,14 @@ def stage_bytes(shape, distinct, n_stages=3):
             "k_moe_down": nexp * w2 + dw2 + T * S * I * 4 + T * K * 8 + T * H * 2,
         }
     rows = T * K + T  # routed pairs + shared rows
+    if n_stages in (7, 8):  # grouping over three launches (large batches)
+        b = stage_bytes(shape, distinct, n_stages - 2)
+        b.pop("k_moe_route_group")
+        nblk = (T + 15) // 16
+        b["k_route_topk"] = T * E * 4 + T * K * 12 + nblk * E * 4
+        b["k_route_scan"] = 2 * nblk * E * 4 + E * 4 + (1 + 3 * min(E, T * K)) * 4
+        b["k_route_scatter"] = T * K * 4 + nblk * E * 4 + E * 4 + rows * 4
+        return b
     if n_stages == 6:  # MX: x and h travel as MXFP8 (a byte per element + a scale byte per 32)
         return {
             "k_router": router,
@@ -237,9 +248,27 @@ def stage_bytes(shape, distinct, n_stages=3):
     }
 
 
-STAGES = {3: ["k_router", "k_moe_w13", "k_moe_down"],
-          5: ["k_router", "k_moe_route_group", "k_moe_gw13", "k_moe_gw2", "k_moe_gcombine"],
-          6: ["k_router", "k_mx_quant", "k_moe_route_group", "k_moe_mx13", "k_moe_mx2", "k_moe_gcombine"]}
+ROUTER_MFMA_MIN_T = 64  # the library runs the router as an MFMA GEMM from this batch size
+
+
+def stage_names(n_stages, T, mx):
+    """Kernel names in launch order for the library's stage count at T tokens."""
+    router = "k_router_mfma" if T >= ROUTER_MFMA_MIN_T else "k_router"
+    if n_stages == 3:
+        return [router, "k_moe_w13", "k_moe_down"]
+    grouping = ["k_moe_route_group"] if n_stages in (5, 6) else ["k_route_topk", "k_route_scan", "k_route_scatter"]
+    experts = ["k_mx_quant"] if mx else []
+    proj = ["k_moe_mx13", "k_moe_mx2"] if mx else ["k_moe_gw13", "k_moe_gw2"]
+    return [router] + experts + grouping + proj + ["k_moe_gcombine"]
+
+
+def stage_flops(shape):
+    """Algorithmic flops per launch of the grouped projections (2 per multiply-add:
+    every routed pair and every shared row through W13 and W2)."""
+    rows = shape.tokens * shape.top_k + (shape.tokens if shape.has_shared else 0)
+    w13 = 2 * rows * 2 * shape.inter * shape.hidden
+    w2 = 2 * rows * shape.hidden * shape.inter
+    return {"k_moe_gw13": w13, "k_moe_gw2": w2, "k_moe_mx13": w13, "k_moe_mx2": w2}
 
 
 # ----------------------------------------------------------------------------- CPU baseline
@@ -325,11 +354,12 @@ def workload_shapes(synth):
             "gemv-e2m1": synth.GEMV_E2M1, "gemv-int4": synth.GEMV_INT4,
             "qwen-t1-nvfp4": synth.QWEN_MOE_T1_NVFP4, "gemv-nvfp4": synth.GEMV_NVFP4,
             "gemv-lmhead": synth.GEMV_LMHEAD, "qwen-t1-bf16shared": synth.QWEN_MOE_T1_BF16SH,
-            "qwen-t1-mxfp4": synth.QWEN_MOE_T1_MX, "qwen-t32-mxfp4": synth.QWEN_MOE_T32_MX}
+            "qwen-t1-mxfp4": synth.QWEN_MOE_T1_MX, "qwen-t32-mxfp4": synth.QWEN_MOE_T32_MX,
+            "qwen-prefill": synth.QWEN_MOE_PREFILL, "qwen-prefill-mxfp4": synth.QWEN_MOE_PREFILL_MX}
 
 
 WORKLOADS = ["qwen-t1", "qwen-t32", "tiny", "gemv-e2m1", "gemv-int4", "qwen-t1-nvfp4", "gemv-nvfp4", "gemv-lmhead",
-             "qwen-t1-bf16shared", "qwen-t1-mxfp4", "qwen-t32-mxfp4"]
+             "qwen-t1-bf16shared", "qwen-t1-mxfp4", "qwen-t32-mxfp4", "qwen-prefill", "qwen-prefill-mxfp4"]
 
 
 def run_moe(args, torch, w4, wl, synth):
@@ -379,7 +409,7 @@ def run_moe(args, torch, w4, wl, synth):
     # per-kernel durations: the same K steps launched eagerly through the
     # measurement entry point, whose kernels carry start/stop HIP events
     n_stages = w4.moe_w4a16_stage_count(base, T)
-    names = STAGES[n_stages]
+    names = stage_names(n_stages, T, shape.fmt == "mxfp4")
     hip = HipEvents()
     ne = 2 * n_stages
     evs = hip.create(ne * n_steps)
@@ -407,9 +437,26 @@ def run_moe(args, torch, w4, wl, synth):
     us_token = ms_step * 1e3 / T
     step_bytes = moe_bytes(shape, d_mean)
     sb = stage_bytes(shape, d_mean, n_stages)
+    if T >= ROUTER_MFMA_MIN_T:
+        sb["k_router_mfma"] = sb.pop("k_router")
     dom = max(stage_us, key=stage_us.get)
     achieved = sb[dom] / (stage_us[dom] * 1e-6) / 1e9
     traffic = load_traffic(dom, shape.name)
+    # the dominant kernel's bound: HBM bytes or MFMA flops, whichever takes longer
+    # at the published peaks
+    fl = stage_flops(shape).get(dom)
+    mfma_peak = MFMA_PEAK_TFLOPS["fp8" if shape.fmt == "mxfp4" else "bf16"]
+    roof = {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS}
+    if fl is not None:
+        tflops = fl / (stage_us[dom] * 1e-6) / 1e12
+        roof["mfma_tflops"] = tflops
+        roof["mfma_frac"] = tflops / mfma_peak
+        roof["mfma_peak"] = mfma_peak
+        roof["algorithmic_flops_per_launch"] = fl
+        if fl / (mfma_peak * 1e12) > sb[dom] / (HBM_PEAK_GBS * 1e9):
+            roof.update({"bound": "mfma", "achieved": tflops, "peak": mfma_peak, "unit": "TFLOP/s",
+                         "frac": tflops / mfma_peak, "hbm_gbps": achieved})
     res = {
         "metric": METRIC,
         "value": us_token,
@@ -442,8 +489,7 @@ def run_moe(args, torch, w4, wl, synth):
         "eager_ms_per_step": eager_ms,
         "wall_s_timed": t_wall,
         "roofline": {
-            "bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": achieved / HBM_PEAK_GBS,
+            **roof,
             "traffic": traffic,
             "algorithmic_bytes_per_launch": sb[dom], "avg_launch_us": stage_us[dom],
             "note": "avg launch duration from start/stop HIP events the runtime records around each "
@@ -526,6 +572,8 @@ def main():
         args.replicas = 4 if args.workload in ("gemv-lmhead",) or not args.workload.startswith("gemv") else 128
     if args.workload.startswith("qwen-t32"):
         args.pool = min(args.pool, 8)
+    if args.workload.startswith("qwen-prefill"):  # 2048 tokens per step
+        args.pool = min(args.pool, 2)
 
     import torch
 

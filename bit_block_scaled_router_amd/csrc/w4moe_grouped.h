@@ -27,6 +27,24 @@ struct GroupArgs {
     int E, K, T, P, Gmax, lstride, route;
 };
 
+// Column tiles of the large-batch kernels: the routed groups' 64-column tiles in
+// group order, ctg[2c] = group index, ctg[2c + 1] = first column; their number
+// is grp[1 + 3*Gmax] (the shared expert's ceil(T/64) tiles follow implicitly).
+// Large batches group their pairs over three launches (k_route_topk,
+// k_route_scan, k_route_scatter) instead of one block: per-block expert
+// histograms in cntb [nblk][E] (turned into each block's base offsets by the
+// scan), the expert of every pair in e_of [P], each expert's first pair-list
+// entry in off_e [E].
+struct RouteArgs {
+    GroupArgs g;
+    int32_t *e_of;
+    int32_t *cntb;
+    int32_t *off_e;
+    int32_t *ctg;  // [2 x column tiles]: routed group, first column (see k_route_scan)
+    int nblk;
+};
+constexpr int ROUTE_TOKENS_PER_BLOCK = 16;
+
 struct GW13Args {
     const uint8_t *codes;   // routed W13 [E][2I][H/2]
     const uint16_t *scales;
@@ -38,6 +56,7 @@ struct GW13Args {
     uint16_t *h_hi;         // [P + T][I] bf16: h = h_hi + h_lo (see split_bf16)
     uint16_t *h_lo;
     int H, I, K, T, P, Gmax, tiles, mfma_min;
+    const int32_t *ctg;     // column tiles (large-batch kernels only)
 };
 
 struct GW2Args {
@@ -51,6 +70,7 @@ struct GW2Args {
     const uint16_t *h_lo;
     float *out;             // [P + T][H]
     int H, I, K, T, P, Gmax, tiles, mfma_min;
+    const int32_t *ctg;     // column tiles (large-batch kernels only)
 };
 
 struct GCombineArgs {
@@ -100,6 +120,10 @@ struct MX2Args {
 };
 
 size_t grouped_lds_bytes(int E, int P);
+// large groups (prefill-sized batches): LDS-staged activations, 64-row units
+void launch_pf13(GW13Args &a, hipStream_t st, hipEvent_t e0, hipEvent_t e1);
+void launch_pf2(GW2Args &a, hipStream_t st, hipEvent_t e0, hipEvent_t e1);
+void launch_route_multi(RouteArgs &a, hipStream_t st, hipEvent_t *ev);  // ev: 6 events or null
 void launch_mx_quant(MXQuantArgs &a, hipStream_t st, hipEvent_t e0, hipEvent_t e1);
 void launch_mx13(MX13Args &a, hipStream_t st, hipEvent_t e0, hipEvent_t e1);
 void launch_mx2(MX2Args &a, hipStream_t st, hipEvent_t e0, hipEvent_t e1);

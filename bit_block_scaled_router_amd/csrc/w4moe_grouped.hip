@@ -40,6 +40,61 @@ constexpr int KS_VALU = 2;
 
 // ================================================================= route + group
 
+// Wave-wide exclusive scans over the experts' pair counts cnt[E]: off[e] =
+// where expert e's pair list starts; the group table lists the experts with
+// pairs in expert order (grp[0] = their number).
+__device__ __forceinline__ void scan_groups(const int *cnt, int *off, int32_t *grp, int E, int Gmax, int lane) {
+    int run = 0, grun = 0;
+    for (int base = 0; base < E; base += 64) {
+        const int e = base + lane;
+        const int c = e < E ? cnt[e] : 0;
+        const int nz = c > 0 ? 1 : 0;
+        int inc = c, ginc = nz;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const int u = __shfl_up(inc, d), gu = __shfl_up(ginc, d);
+            if (lane >= d) inc += u, ginc += gu;
+        }
+        const int ex = run + inc - c, gex = grun + ginc - nz;
+        if (e < E) off[e] = ex;
+        if (nz) {
+            grp[1 + gex] = e;
+            grp[1 + Gmax + gex] = ex;
+            grp[1 + 2 * Gmax + gex] = c;
+        }
+        run += __shfl(inc, 63);
+        grun += __shfl(ginc, 63);
+    }
+    if (lane == 0) grp[0] = grun;
+}
+
+// Top-k and routing weights of token t by wave `lane`s (K lanes hold the
+// selected ids and weights); returns the lane's expert (-1 for lanes >= K).
+template <int PL>
+__device__ __forceinline__ int route_token(const GroupArgs &a, int t, int lane) {
+    const int K = a.K;
+    if (a.route) {
+        int my_id;
+        float my_val;
+        wave_topk<PL>(a.logits + (size_t)t * a.lstride, a.bias, a.E, K, 0, my_id, my_val);
+        const float vmax = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_val), 0));
+        const float ex = lane < K ? expf(my_val - vmax) : 0.f;
+        const float sum = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(group_sum<64>(ex)), 63));
+        if (lane < K) {
+            const float w = ex / sum;
+            a.ids_ws[t * K + lane] = my_id;
+            a.w_ws[t * K + lane] = w;
+            if (a.ids_user) a.ids_user[t * K + lane] = my_id;
+            if (a.w_user) a.w_user[t * K + lane] = w;
+            return my_id;
+        }
+        return -1;
+    }
+    if (lane >= K) return -1;
+    const int e = a.ids_in[t * K + lane];
+    return (e >= 0 && e < a.E) ? e : -1;  // invalid ids join no group
+}
+
 template <int PL>
 __global__ __launch_bounds__(1024) void k_moe_route_group(GroupArgs a) {
     extern __shared__ int g_lds[];
@@ -52,28 +107,9 @@ __global__ __launch_bounds__(1024) void k_moe_route_group(GroupArgs a) {
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6), nw = blockDim.x >> 6;
     for (int i = tid; i < E; i += blockDim.x) cnt[i] = 0;
 
-    if (a.route) {
-        for (int t = wv; t < T; t += nw) {
-            int my_id;
-            float my_val;
-            wave_topk<PL>(a.logits + (size_t)t * a.lstride, a.bias, E, K, 0, my_id, my_val);
-            const float vmax = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_val), 0));
-            const float ex = lane < K ? expf(my_val - vmax) : 0.f;
-            const float sum = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(group_sum<64>(ex)), 63));
-            if (lane < K) {
-                const float w = ex / sum;
-                a.ids_ws[t * K + lane] = my_id;
-                a.w_ws[t * K + lane] = w;
-                if (a.ids_user) a.ids_user[t * K + lane] = my_id;
-                if (a.w_user) a.w_user[t * K + lane] = w;
-                e_of[t * K + lane] = my_id;
-            }
-        }
-    } else {
-        for (int p = tid; p < P; p += blockDim.x) {
-            const int e = a.ids_in[p];
-            e_of[p] = (e >= 0 && e < E) ? e : -1;  // invalid ids join no group
-        }
+    for (int t = wv; t < T; t += nw) {
+        const int e = route_token<PL>(a, t, lane);
+        if (lane < K) e_of[t * K + lane] = e;
     }
     __syncthreads();
     // position of each pair inside its expert's group (LDS atomics: the order
@@ -85,36 +121,111 @@ __global__ __launch_bounds__(1024) void k_moe_route_group(GroupArgs a) {
     __syncthreads();
     // exclusive scans over the experts: where each expert's pair list starts,
     // and the group index of each active expert (groups in expert order)
-    if (wv == 0) {
-        int run = 0, grun = 0;
-        for (int base = 0; base < E; base += 64) {
-            const int e = base + lane;
-            const int c = e < E ? cnt[e] : 0;
-            const int nz = c > 0 ? 1 : 0;
-            int inc = c, ginc = nz;
-#pragma unroll
-            for (int d = 1; d < 64; d <<= 1) {
-                const int u = __shfl_up(inc, d), gu = __shfl_up(ginc, d);
-                if (lane >= d) inc += u, ginc += gu;
-            }
-            const int ex = run + inc - c, gex = grun + ginc - nz;
-            if (e < E) off[e] = ex;
-            if (nz) {
-                a.grp[1 + gex] = e;
-                a.grp[1 + a.Gmax + gex] = ex;
-                a.grp[1 + 2 * a.Gmax + gex] = c;
-            }
-            run += __shfl(inc, 63);
-            grun += __shfl(ginc, 63);
-        }
-        if (lane == 0) a.grp[0] = grun;
-    }
+    if (wv == 0) scan_groups(cnt, off, a.grp, E, a.Gmax, lane);
     __syncthreads();
     for (int p = tid; p < P; p += blockDim.x) {
         const int e = e_of[p];
         if (e >= 0) a.pairs[off[e] + pos[p]] = p;
     }
     for (int t = tid; t < T; t += blockDim.x) a.pairs[P + t] = P + t;
+}
+
+// Large batches: ROUTE_TOKENS_PER_BLOCK tokens per block (4 waves), top-k and
+// weights per token, the expert of each pair, and the block's expert histogram
+// (LDS counts; only the totals are used, so the order of the increments is free).
+template <int PL>
+__global__ __launch_bounds__(256) void k_route_topk(RouteArgs r) {
+    __shared__ int hist[1024];
+    const GroupArgs &a = r.g;
+    const int E = a.E, K = a.K;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    for (int i = tid; i < E; i += blockDim.x) hist[i] = 0;
+    __syncthreads();
+    const int t0 = blockIdx.x * ROUTE_TOKENS_PER_BLOCK;
+    const int t1 = min(t0 + ROUTE_TOKENS_PER_BLOCK, a.T);
+    for (int t = t0 + wv; t < t1; t += 4) {
+        const int e = route_token<PL>(a, t, lane);
+        if (lane < K) {
+            r.e_of[t * K + lane] = e;
+            if (e >= 0) atomicAdd(&hist[e], 1);
+        }
+    }
+    __syncthreads();
+    for (int i = tid; i < E; i += blockDim.x) r.cntb[(size_t)blockIdx.x * E + i] = hist[i];
+}
+
+// One block: per expert, the exclusive scan of the block histograms (in place:
+// cntb becomes each block's base inside the expert's list) and the expert's
+// total; then the group table and each expert's list start.
+__global__ __launch_bounds__(1024) void k_route_scan(RouteArgs r) {
+    __shared__ int tot[1024], off[1024];
+    const int E = r.g.E, Gmax = r.g.Gmax;
+    const int tid = threadIdx.x;
+    for (int e = tid; e < E; e += blockDim.x) {
+        int run = 0;
+        for (int b0 = 0; b0 < r.nblk; b0 += 16) {  // 16 loads in flight, then the running sums
+            int c[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) c[i] = b0 + i < r.nblk ? r.cntb[(size_t)(b0 + i) * E + e] : 0;
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                if (b0 + i < r.nblk) {
+                    r.cntb[(size_t)(b0 + i) * E + e] = run;
+                    run += c[i];
+                }
+        }
+        tot[e] = run;
+    }
+    __syncthreads();
+    if (tid < 64) {
+        scan_groups(tot, off, r.g.grp, E, Gmax, tid);
+        // the routed groups' 64-column tiles in group order (groups = experts with pairs)
+        int crun = 0, grun = 0;
+        for (int base = 0; base < E; base += 64) {
+            const int e = base + tid;
+            const int c = e < E ? tot[e] : 0;
+            const int nct = (c + 63) / 64, nz = c > 0 ? 1 : 0;
+            int inc = nct, ginc = nz;
+#pragma unroll
+            for (int d = 1; d < 64; d <<= 1) {
+                const int u = __shfl_up(inc, d), gu = __shfl_up(ginc, d);
+                if (tid >= d) inc += u, ginc += gu;
+            }
+            const int c0 = crun + inc - nct, g = grun + ginc - nz;
+            for (int j = 0; j < nct; ++j) {
+                r.ctg[2 * (c0 + j)] = g;
+                r.ctg[2 * (c0 + j) + 1] = 64 * j;
+            }
+            crun += __shfl(inc, 63);
+            grun += __shfl(ginc, 63);
+        }
+        if (tid == 0) r.g.grp[1 + 3 * Gmax] = crun;
+    }
+    __syncthreads();
+    for (int e = tid; e < E; e += blockDim.x) r.off_e[e] = off[e];
+}
+
+// Same blocks as k_route_topk: each pair goes to off_e[e] + the block's base
+// for e + its rank among the block's earlier pairs of expert e.
+__global__ __launch_bounds__(256) void k_route_scatter(RouteArgs r) {
+    __shared__ int es[ROUTE_TOKENS_PER_BLOCK * 16];
+    const GroupArgs &a = r.g;
+    const int E = a.E, K = a.K;
+    const int tid = threadIdx.x;
+    const int t0 = blockIdx.x * ROUTE_TOKENS_PER_BLOCK;
+    const int t1 = min(t0 + ROUTE_TOKENS_PER_BLOCK, a.T);
+    const int p0 = t0 * K, np = (t1 - t0) * K;
+    for (int i = tid; i < np; i += blockDim.x) es[i] = r.e_of[p0 + i];
+    __syncthreads();
+    for (int i = tid; i < np; i += blockDim.x) {
+        const int e = es[i];
+        if (e < 0) continue;
+        int rank = 0;
+        for (int q = 0; q < i; ++q) rank += es[q] == e ? 1 : 0;
+        a.pairs[r.off_e[e] + r.cntb[(size_t)blockIdx.x * E + e] + rank] = p0 + i;
+    }
+    for (int t = t0 + tid; t < t1; t += blockDim.x) a.pairs[a.P + t] = a.P + t;
 }
 
 // Which expert and which pairs a work unit covers.  Group slot 0 is the shared
@@ -526,6 +637,289 @@ __global__ __launch_bounds__(256) void k_moe_gw2(GW2Args a) {
     }
 }
 
+// ================================================================= prefill (large groups)
+
+// Large batches (groups of tens to hundreds of rows): a block owns 128 weight
+// rows of one group (two 16-row tiles per wave) for the whole K and one 64-column
+// tile of the group.  The column tile's activations are staged in LDS one
+// 128-wide K chunk at a time (double buffered, one barrier per chunk) and shared
+// by the 4 waves; each wave keeps its rows' codes in registers (the next chunk's
+// are loaded while the current one is multiplied) and owns its outputs
+// outright, so no partial sums cross waves.  Operands as in gw13/gw2: every
+// dequantised weight is two exact bf16 terms; h is read as its two bf16 terms.
+constexpr int PF_COLS = 64;     // columns (pairs) per tile
+constexpr int PF_KC = 128;      // K per chunk
+constexpr int PF_LROW = PF_KC;  // bf16 per LDS row (256 B); 16-byte units are XOR-swizzled by column
+constexpr int PF_ROWS = 128;    // weight rows (W13: h rows) per unit
+
+// LDS address of 16-byte unit j (K elements 8j .. 8j+7) of column c: unit j is
+// stored at position j ^ (c % 16), so that the 16 columns an MFMA operand read
+// touches (and the 16 lanes of a store) cover all 64 banks once.
+__device__ __forceinline__ const bf16x8 *pf_unit_ptr(const uint16_t (*rows)[PF_LROW], int c, int j) {
+    return reinterpret_cast<const bf16x8 *>(&rows[c][8 * (j ^ (c & 15))]);
+}
+
+// The loader role of thread tid: column tid / 4 of the tile, K elements
+// 32 (tid % 4) .. +31 of the chunk (four 16-byte loads).
+__device__ __forceinline__ void pf_load(const Buf &b, uint32_t off, bool on, uint4 (&v)[4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = ld128(b, on ? off + 16u * i : OOB);
+}
+__device__ __forceinline__ void pf_store(uint16_t *row, int c, int lq, const uint4 (&v)[4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4 *>(row + 8 * ((4 * lq + i) ^ (c & 15))) = v[i];
+}
+
+// Work units of the large-batch kernels: (column tile, row tile).  Unit u runs on
+// XCD u % 8 (blocks are dealt to the XCDs round-robin and the grid is a multiple
+// of 8), so the column tiles are dealt to the XCDs in turn and each XCD walks
+// all row tiles of its column tiles: a tile's activations are fetched into one
+// L2 and reused there.  The shared expert's ceil(T/64) tiles follow the routed
+// groups' (group table entry 1 + 3 Gmax and the column-tile map).
+__device__ __forceinline__ int pf_tile_count(const int32_t *grp, int Gmax, bool shared, int T) {
+    return ld_uniform(grp, 1 + 3 * Gmax) + (shared ? (T + PF_COLS - 1) / PF_COLS : 0);
+}
+__device__ __forceinline__ int pf_unit_count(int nct, int tiles) { return (nct + 7) / 8 * 8 * tiles; }
+// false for the padding units of the last round of column tiles
+__device__ __forceinline__ bool pf_unit(const int32_t *grp, const int32_t *ctg, int Gmax, bool shared, int nct, int u,
+                                        int tiles, int &gs, int &rt, int &n0) {
+    const int x = u & 7, j = u >> 3;
+    const int ct = 8 * (j / tiles) + x;
+    rt = j - (j / tiles) * tiles;
+    if (ct >= nct) return false;
+    const int nrc = ld_uniform(grp, 1 + 3 * Gmax);
+    if (ct < nrc) {
+        gs = ld_uniform(ctg, 2 * ct) + (shared ? 1 : 0);
+        n0 = ld_uniform(ctg, 2 * ct + 1);
+    } else {
+        gs = 0;
+        n0 = (ct - nrc) * PF_COLS;
+    }
+    return true;
+}
+
+__device__ __forceinline__ void pf13_unit(const GW13Args &a, int gs, int rt, int n0,
+                                          uint16_t (*xs)[PF_COLS][PF_LROW]) {
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int H = a.H, I = a.I;
+    const uint32_t spr = (uint32_t)(H >> 4);
+    const size_t mat_codes = (size_t)(2 * I) * (H >> 1), mat_scales = (size_t)(2 * I) * spr;
+    const GroupView<uint16_t> gv = group_view(a.grp, gs, a.Gmax, a.P, a.T, a.codes, a.scales, mat_codes, mat_scales,
+                                              a.s_codes, a.s_scales);
+    const Buf cb = make_buf(gv.codes, (uint32_t)mat_codes);
+    const Buf sb = make_buf(gv.scales, (uint32_t)(mat_scales * 2));
+    const Buf xall = make_buf(a.x, (uint32_t)a.T * (uint32_t)H * 2u);
+    const int *plist = a.pairs + gv.off;
+    const int r = lane & 15, q = lane >> 4;
+    const int i0 = rt * PF_ROWS + 32 * wv;  // the wave's first gate row: tiles i0 and i0 + 16
+    // code rows: gate tile 0, gate tile 1, up tile 0, up tile 1
+    const uint32_t rows[4] = {(uint32_t)(i0 + r), (uint32_t)(i0 + 16 + r), (uint32_t)(I + i0 + r),
+                              (uint32_t)(I + i0 + 16 + r)};
+    const int lc = tid >> 2, lq = tid & 3;
+    const int nch = H / PF_KC;
+    const bool lv = n0 + lc < gv.m;
+    const uint32_t xo = lv ? (uint32_t)(token_of(plist[n0 + lc], a.P, a.K) * H + 32 * lq) * 2u : 0u;
+    uint4 xr[4];
+    pf_load(xall, xo, lv, xr);
+    uint4 cw[4];
+    uint32_t sw[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        cw[t] = ld128(cb, rows[t] * (uint32_t)(H >> 1) + (uint32_t)(16 * q));
+        sw[t] = ld32(sb, (rows[t] * spr + (uint32_t)(2 * q)) * 2u);
+    }
+    f32x4 acc[4][4];  // [gate 0, gate 1, up 0, up 1][column tile]
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) acc[t][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int ch = 0; ch < nch; ++ch) {
+        uint16_t(*xb)[PF_LROW] = xs[ch & 1];
+        pf_store(xb[lc], lc, lq, xr);
+        __syncthreads();
+        uint4 cc[4];
+        uint32_t sc[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) cc[t] = cw[t], sc[t] = sw[t];
+        if (ch + 1 < nch) {  // next chunk: activations to registers, this wave's codes
+            const uint32_t kn = (uint32_t)((ch + 1) * PF_KC);
+            pf_load(xall, xo + kn * 2u, lv, xr);
+            const uint32_t kq = kn + 32u * (uint32_t)q;
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                cw[t] = ld128(cb, rows[t] * (uint32_t)(H >> 1) + (kq >> 1));
+                sw[t] = ld32(sb, (rows[t] * spr + (kq >> 4)) * 2u);
+            }
+        }
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            bf16x8 b[4];
+#pragma unroll
+            for (int nt = 0; nt < 4; ++nt) b[nt] = *pf_unit_ptr(xb, 16 * nt + r, 4 * q + s);
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const uint32_t cws[4] = {cc[t].x, cc[t].y, cc[t].z, cc[t].w};
+                float hi, lo;
+                split_scale(f16_bits_to_f32(s < 2 ? sc[t] : (sc[t] >> 16)), hi, lo);
+                bf16x8 ah, al;
+                e2m1x8_split(cws[s], hi, lo, ah, al);
+#pragma unroll
+                for (int nt = 0; nt < 4; ++nt) acc[t][nt] = mfma16x16x32(ah, b[nt], acc[t][nt]);
+#pragma unroll
+                for (int nt = 0; nt < 4; ++nt) acc[t][nt] = mfma16x16x32(al, b[nt], acc[t][nt]);
+            }
+        }
+    }
+    // lane holds rows 4q + j of each 16-row tile, column 16 nt + r
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+        const int idx = n0 + 16 * nt + r;
+        if (idx < gv.m) {
+            const int p = plist[idx];
+#pragma unroll
+            for (int ht = 0; ht < 2; ++ht) {
+                uint16_t bh[4], bl[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const float gg = acc[ht][nt][j], uu = acc[2 + ht][nt][j];
+                    split_bf16((gg / (1.f + expf(-gg))) * uu, bh[j], bl[j]);
+                }
+                const size_t o = (size_t)p * I + i0 + 16 * ht + 4 * q;
+                *reinterpret_cast<uint2 *>(a.h_hi + o) =
+                    make_uint2(bh[0] | ((uint32_t)bh[1] << 16), bh[2] | ((uint32_t)bh[3] << 16));
+                *reinterpret_cast<uint2 *>(a.h_lo + o) =
+                    make_uint2(bl[0] | ((uint32_t)bl[1] << 16), bl[2] | ((uint32_t)bl[3] << 16));
+            }
+        }
+    }
+    __syncthreads();  // the LDS buffers are refilled by the next unit
+}
+
+__global__ __launch_bounds__(256) void k_moe_pf13(GW13Args a) {
+    __shared__ __align__(16) uint16_t xs[2][PF_COLS][PF_LROW];
+    const bool sh = a.s_codes != nullptr;
+    const int nct = pf_tile_count(a.grp, a.Gmax, sh, a.T);
+    const int nu = pf_unit_count(nct, a.tiles);
+    for (int u = blockIdx.x; u < nu; u += gridDim.x) {
+        int gs, rt, n0;
+        if (pf_unit(a.grp, a.ctg, a.Gmax, sh, nct, u, a.tiles, gs, rt, n0)) pf13_unit(a, gs, rt, n0, xs);
+    }
+}
+
+__device__ __forceinline__ void pf2_unit(const GW2Args &a, int gs, int rt, int n0,
+                                         uint16_t (*hs)[2][PF_COLS][PF_LROW]) {
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int H = a.H, I = a.I;
+    const uint32_t spr = (uint32_t)(I >> 4);
+    const size_t mat_codes = (size_t)H * (I >> 1), mat_scales = (size_t)H * spr;
+    const GroupView<uint16_t> gv = group_view(a.grp, gs, a.Gmax, a.P, a.T, a.codes, a.scales, mat_codes, mat_scales,
+                                              a.s_codes, a.s_scales);
+    const Buf cb = make_buf(gv.codes, (uint32_t)mat_codes);
+    const Buf sb = make_buf(gv.scales, (uint32_t)(mat_scales * 2));
+    const uint32_t hbytes = (uint32_t)(a.P + a.T) * (uint32_t)I * 2u;
+    const Buf hhi = make_buf(a.h_hi, hbytes), hlo = make_buf(a.h_lo, hbytes);
+    const int *plist = a.pairs + gv.off;
+    const int r = lane & 15, q = lane >> 4;
+    const int o0 = rt * PF_ROWS + 32 * wv;  // the wave's first output row: tiles o0 and o0 + 16
+    const uint32_t rows[2] = {(uint32_t)(o0 + r), (uint32_t)(o0 + 16 + r)};
+    const int lc = tid >> 2, lq = tid & 3;
+    const int nch = I / PF_KC;
+    const bool lv = n0 + lc < gv.m;
+    const uint32_t ho = lv ? (uint32_t)(plist[n0 + lc] * I + 32 * lq) * 2u : 0u;
+    uint4 hr[4], lr[4];
+    pf_load(hhi, ho, lv, hr);
+    pf_load(hlo, ho, lv, lr);
+    uint4 cw[2];
+    uint32_t sw[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+        cw[t] = ld128(cb, rows[t] * (uint32_t)(I >> 1) + (uint32_t)(16 * q));
+        sw[t] = ld32(sb, (rows[t] * spr + (uint32_t)(2 * q)) * 2u);
+    }
+    f32x4 acc[2][4], acc2[2][4];  // [row tile][column tile]; weight hi / lo terms
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) acc[t][nt] = acc2[t][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int ch = 0; ch < nch; ++ch) {
+        uint16_t(*bh)[PF_LROW] = hs[ch & 1][0];
+        uint16_t(*bl)[PF_LROW] = hs[ch & 1][1];
+        pf_store(bh[lc], lc, lq, hr);
+        pf_store(bl[lc], lc, lq, lr);
+        __syncthreads();
+        uint4 cc[2];
+        uint32_t sc[2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) cc[t] = cw[t], sc[t] = sw[t];
+        if (ch + 1 < nch) {
+            const uint32_t kn = (uint32_t)((ch + 1) * PF_KC);
+            pf_load(hhi, ho + kn * 2u, lv, hr);
+            pf_load(hlo, ho + kn * 2u, lv, lr);
+            const uint32_t kq = kn + 32u * (uint32_t)q;
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                cw[t] = ld128(cb, rows[t] * (uint32_t)(I >> 1) + (kq >> 1));
+                sw[t] = ld32(sb, (rows[t] * spr + (kq >> 4)) * 2u);
+            }
+        }
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            bf16x8 b0[4], b1[4];
+#pragma unroll
+            for (int nt = 0; nt < 4; ++nt) {
+                b0[nt] = *pf_unit_ptr(bh, 16 * nt + r, 4 * q + s);
+                b1[nt] = *pf_unit_ptr(bl, 16 * nt + r, 4 * q + s);
+            }
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                const uint32_t cws[4] = {cc[t].x, cc[t].y, cc[t].z, cc[t].w};
+                float hi, lo;
+                split_scale(f16_bits_to_f32(s < 2 ? sc[t] : (sc[t] >> 16)), hi, lo);
+                bf16x8 ah, al;
+                e2m1x8_split(cws[s], hi, lo, ah, al);
+                // all four terms (al can reach 2^-5 of the weight, h_lo 2^-8 of h)
+#pragma unroll
+                for (int nt = 0; nt < 4; ++nt) {
+                    acc[t][nt] = mfma16x16x32(ah, b0[nt], acc[t][nt]);
+                    acc2[t][nt] = mfma16x16x32(al, b0[nt], acc2[t][nt]);
+                }
+#pragma unroll
+                for (int nt = 0; nt < 4; ++nt) {
+                    acc[t][nt] = mfma16x16x32(ah, b1[nt], acc[t][nt]);
+                    acc2[t][nt] = mfma16x16x32(al, b1[nt], acc2[t][nt]);
+                }
+            }
+        }
+    }
+    // lane holds rows 4q + j of each 16-row tile, column 16 nt + r
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+        const int idx = n0 + 16 * nt + r;
+        if (idx < gv.m) {
+            float *op = a.out + (size_t)plist[idx] * H + o0 + 4 * q;
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                const f32x4 v = acc[t][nt] + acc2[t][nt];
+                *reinterpret_cast<float4 *>(op + 16 * t) = make_float4(v[0], v[1], v[2], v[3]);
+            }
+        }
+    }
+    __syncthreads();
+}
+
+__global__ __launch_bounds__(256) void k_moe_pf2(GW2Args a) {
+    __shared__ __align__(16) uint16_t hs[2][2][PF_COLS][PF_LROW];  // [buffer][hi, lo][column][K]
+    const bool sh = a.s_codes != nullptr;
+    const int nct = pf_tile_count(a.grp, a.Gmax, sh, a.T);
+    const int nu = pf_unit_count(nct, a.tiles);
+    for (int u = blockIdx.x; u < nu; u += gridDim.x) {
+        int gs, rt, n0;
+        if (pf_unit(a.grp, a.ctg, a.Gmax, sh, nct, u, a.tiles, gs, rt, n0)) pf2_unit(a, gs, rt, n0, hs);
+    }
+}
+
 // ================================================================= MX path
 
 // The MX path (MXFP4 weights, MXFP8 activations) runs every group on gfx950's
@@ -844,6 +1238,21 @@ void launch_route_group(GroupArgs &a, hipStream_t st, hipEvent_t e0, hipEvent_t 
     else go_ev(st, e0, e1, k_moe_route_group<16>, g, b, shm, a);
 }
 
+void launch_route_multi(RouteArgs &a, hipStream_t st, hipEvent_t *ev) {
+    const int pl = (a.g.E + 63) / 64;
+    const dim3 g((unsigned)a.nblk), b(256);
+    hipEvent_t e[6] = {};
+    if (ev)
+        for (int i = 0; i < 6; ++i) e[i] = ev[i];
+    if (pl <= 1) go_ev(st, e[0], e[1], k_route_topk<1>, g, b, 0, a);
+    else if (pl <= 2) go_ev(st, e[0], e[1], k_route_topk<2>, g, b, 0, a);
+    else if (pl <= 4) go_ev(st, e[0], e[1], k_route_topk<4>, g, b, 0, a);
+    else if (pl <= 8) go_ev(st, e[0], e[1], k_route_topk<8>, g, b, 0, a);
+    else go_ev(st, e[0], e[1], k_route_topk<16>, g, b, 0, a);
+    go_ev(st, e[2], e[3], k_route_scan, dim3(1), dim3(1024), 0, a);
+    go_ev(st, e[4], e[5], k_route_scatter, g, b, 0, a);
+}
+
 // blocks of the grid-stride W13 and down launches
 #ifndef W4_GROUPED_BLOCKS
 #define W4_GROUPED_BLOCKS 1024
@@ -880,6 +1289,22 @@ void launch_gw2(GW2Args &a, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
     case 32: go_ev(st, e0, e1, k_moe_gw2<32>, g, b, 0, a); break;
     default: go_ev(st, e0, e1, k_moe_gw2<64>, g, b, 0, a); break;
     }
+}
+
+// blocks of the large-batch launches (grid-stride over the units)
+#ifndef W4_PF_BLOCKS
+#define W4_PF_BLOCKS 1024  // a multiple of 8: unit u must stay on XCD u % 8
+#endif
+static_assert(W4_PF_BLOCKS % 8 == 0, "the large-batch unit order assumes a grid that is a multiple of 8");
+
+void launch_pf13(GW13Args &a, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
+    a.tiles = a.I / PF_ROWS;
+    go_ev(st, e0, e1, k_moe_pf13, dim3(W4_PF_BLOCKS), dim3(256), 0, a);
+}
+
+void launch_pf2(GW2Args &a, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
+    a.tiles = a.H / PF_ROWS;
+    go_ev(st, e0, e1, k_moe_pf2, dim3(W4_PF_BLOCKS), dim3(256), 0, a);
 }
 
 void launch_mx_quant(MXQuantArgs &a, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {

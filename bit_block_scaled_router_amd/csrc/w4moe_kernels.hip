@@ -196,6 +196,64 @@ __global__ __launch_bounds__(512) void k_router(const uint16_t *__restrict__ wr,
     }
 }
 
+// Large batches: the router as a bf16 GEMM on MFMA, logits[t][r] = Wr[r] . x[t]
+// for rows r_begin <= r < r_end (row E = the shared-gate weight).  A block
+// covers 64 rows x 64 tokens: wave w owns rows 16 w .. 16 w + 15 against four
+// 16-token column tiles, K in steps of 32 (one 16x16x32 MFMA per tile).  Every
+// x tile is read by ceil(rows / 64) blocks and every router row by ceil(T / 64),
+// instead of all T tokens per row as in k_router.
+__global__ __launch_bounds__(256) void k_router_mfma(const uint16_t *__restrict__ wr,
+                                                     const uint16_t *__restrict__ wsg,
+                                                     const uint16_t *__restrict__ x, float *__restrict__ logits,
+                                                     int E, int H, int T, int r_begin, int r_end, int lstride) {
+    const int lane = threadIdx.x & 63, wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int r = lane & 15, q = lane >> 4;
+    const int row = r_begin + (int)blockIdx.y * 64 + 16 * wv + r;  // this lane's A row
+    const int tok0 = (int)blockIdx.x * 64;
+    const Buf wb = make_buf(wr, (uint32_t)E * (uint32_t)H * 2u);
+    const Buf gb = make_buf(wsg, wsg ? (uint32_t)H * 2u : 0u);
+    const Buf xb = make_buf(x, (uint32_t)T * (uint32_t)H * 2u);
+    const bool in_wr = row < E && row < r_end, in_g = row == E && row < r_end;
+    const uint32_t aoff = (uint32_t)row * (uint32_t)H * 2u;
+    uint32_t xoff[4];
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+        const int t = tok0 + 16 * nt + r;
+        xoff[nt] = t < T ? (uint32_t)t * (uint32_t)H * 2u : OOB;
+    }
+    f32x4 acc[4];
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int k0 = 0; k0 < H; k0 += 128) {
+        uint4 av[4], bv[4][4];
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const uint32_t kb = (uint32_t)(k0 + 32 * s + 8 * q) * 2u;
+            const bool kv = k0 + 32 * s < H;
+            const uint4 u = ld128(wb, (in_wr && kv) ? aoff + kb : OOB);
+            const uint4 v = ld128(gb, (in_g && kv) ? kb : OOB);
+            av[s] = make_uint4(u.x | v.x, u.y | v.y, u.z | v.z, u.w | v.w);
+#pragma unroll
+            for (int nt = 0; nt < 4; ++nt) bv[s][nt] = ld128(xb, (kv && xoff[nt] != OOB) ? xoff[nt] + kb : OOB);
+        }
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+            for (int nt = 0; nt < 4; ++nt) acc[nt] = mfma16x16x32(__builtin_bit_cast(bf16x8, av[s]), __builtin_bit_cast(bf16x8, bv[s][nt]), acc[nt]);
+    }
+    // lane holds rows 4q + j of the wave's 16, token column r of each tile
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+        const int t = tok0 + 16 * nt + r;
+        if (t >= T) continue;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int rr = r_begin + (int)blockIdx.y * 64 + 16 * wv + 4 * q + j;
+            if (rr < r_end) logits[(size_t)t * lstride + rr] = acc[nt][j];
+        }
+    }
+}
+
 // ================================================================= MoE W13 + SiLU
 
 struct W13Args {
@@ -649,23 +707,27 @@ void launch_dequant(const w4_matrix *W, float *out, hipStream_t st) {
 
 constexpr int MAX_TOPK = 16;
 constexpr int MAX_EXPERTS = 1024;  // 64 lanes x 16 logits per lane
-constexpr int MAX_TOKENS = 4096;
+constexpr int MAX_TOKENS = 16384;
 
 #ifndef W4_GROUPED_MIN_T
 #define W4_GROUPED_MIN_T 4  // batches of at least this many tokens group their pairs by expert
 #endif
+#ifndef W4_ROUTER_MFMA_MIN_T
+#define W4_ROUTER_MFMA_MIN_T 64  // batches of at least this many tokens run the router on MFMA
+#endif
 #ifndef W4_MFMA_MIN
 #define W4_MFMA_MIN 4  // expert groups of at least this many rows run on MFMA (smaller ones on VALU)
 #endif
-constexpr int MAX_GROUPED_PAIRS = 4096;
+constexpr int MAX_GROUPED_PAIRS = 65536;  // (token, slot) pairs of one grouped call
+constexpr int MAX_ONE_BLOCK_PAIRS = 4096;  // up to this many, one block groups them (LDS counting sort)
 
 struct MoEPlan {
     int H, I, E, K, S, T;
     int L13, L2, hstride, lstride;
-    bool grouped, mx;
-    int P, Gmax;
+    bool grouped, mx, multi;  // multi: grouping over three launches (large batches)
+    int P, Gmax, nblk;
     size_t off_logits, off_ids, off_w, off_h, total;
-    size_t off_grp, off_pairs, off_hp, off_out, off_xq;
+    size_t off_grp, off_pairs, off_hp, off_out, off_xq, off_route;
 };
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
@@ -732,6 +794,8 @@ int check_layer(const moe_w4a16_layer *Lr, int64_t T, MoEPlan &p) {
                         MAX_GROUPED_PAIRS);
         p.grouped = true;
     }
+    p.multi = p.grouped && p.P > MAX_ONE_BLOCK_PAIRS;
+    p.nblk = (int)((T + ROUTE_TOKENS_PER_BLOCK - 1) / ROUTE_TOKENS_PER_BLOCK);
     size_t off = 0;
     p.off_logits = off; off = align_up(off + (size_t)T * p.lstride * 4, 256);
     p.off_ids = off;    off = align_up(off + (size_t)T * K * 4, 256);
@@ -740,12 +804,17 @@ int check_layer(const moe_w4a16_layer *Lr, int64_t T, MoEPlan &p) {
         p.off_h = off;  off = align_up(off + (size_t)T * p.S * p.hstride * 4, 256);
     } else {
         const size_t rows = (size_t)p.P + (size_t)T;
-        p.off_grp = off;   off = align_up(off + (size_t)(1 + 3 * p.Gmax) * 4, 256);
+        p.off_grp = off;   off = align_up(off + (size_t)(2 + 3 * p.Gmax) * 4, 256);
         p.off_pairs = off; off = align_up(off + rows * 4, 256);
         p.off_hp = off;    off = align_up(off + rows * (size_t)I * 4, 256);  // h_hi then h_lo, bf16 (MX: codes, scales)
         p.off_out = off;   off = align_up(off + rows * (size_t)H * 4, 256);
         if (p.mx) {  // x as MXFP8: codes [T][H], then scales [T][H/32]
             p.off_xq = off; off = align_up(off + (size_t)T * H + (size_t)T * (H / 32), 256);
+        }
+        if (p.multi) {  // e_of [P], off_e [E], cntb [nblk][E], column tiles [2][Gmax + P/64]
+            p.off_route = off;
+            off = align_up(off + ((size_t)p.P + (size_t)E + (size_t)p.nblk * (size_t)E +
+                                  2 * ((size_t)p.Gmax + (size_t)p.P / 64 + 1)) * 4, 256);
         }
     }
     p.total = off;
@@ -756,6 +825,11 @@ int launch_router(const moe_w4a16_layer *Lr, const MoEPlan &p, const uint16_t *x
                   int r_end, const Launch &st) {
     const int nrows = r_end - r_begin;
     if (nrows <= 0) return W4_OK;
+    if (p.T >= W4_ROUTER_MFMA_MIN_T) {
+        go(st, k_router_mfma, dim3((unsigned)((p.T + 63) / 64), (unsigned)((nrows + 63) / 64)), dim3(256), 0,
+           Lr->router_w, Lr->shared_gate_w, x, logits, p.E, p.H, p.T, r_begin, r_end, p.lstride);
+        return W4_OK;
+    }
     const int ns = (p.H + 511) / 512;
     // tokens per chunk: 1 for single-token decode, else 4 (activation loads in flight together)
     auto with_ns = [&](auto NSc) {
@@ -858,6 +932,11 @@ int run_grouped(const moe_w4a16_layer *Lr, const MoEPlan &p, const uint16_t *x, 
                 const float *w_in, uint16_t *y, int32_t *topk_ids, float *topk_w, char *wsb, hipStream_t sm,
                 void *const *events);
 
+int stage_count(const MoEPlan &p) {
+    if (!p.grouped) return 3;
+    return 5 + (p.mx ? 1 : 0) + (p.multi ? 2 : 0);
+}
+
 int run_moe(const moe_w4a16_layer *Lr, const uint16_t *x, int64_t T, const int32_t *ids_in, const float *w_in,
             uint16_t *y, int32_t *topk_ids, float *topk_w, void *ws, size_t ws_bytes, void *stream,
             void *const *events = nullptr, int n_events = 0) {
@@ -883,7 +962,7 @@ int run_moe(const moe_w4a16_layer *Lr, const uint16_t *x, int64_t T, const int32
     float *h = (float *)(wsb + p.off_h);
 
     if (events) {
-        const int need = p.mx ? 12 : p.grouped ? 10 : 6;
+        const int need = 2 * stage_count(p);
         if (n_events < need)
             return fail(W4_ERR_INVALID_ARG, "%s path needs %d events, got %d", p.grouped ? "grouped" : "single-token",
                         need, n_events);
@@ -964,6 +1043,25 @@ int run_grouped(const moe_w4a16_layer *Lr, const MoEPlan &p, const uint16_t *x, 
     uint16_t *h_lo = h_hi + ((size_t)p.P + p.T) * p.I;
     float *outp = (float *)(wsb + p.off_out);
     auto ev = [&](int i) { return events ? (hipEvent_t)events[i] : (hipEvent_t) nullptr; };
+    // stage events after the router (and the MX quantiser): the grouping takes
+    // 1 launch, or 3 for large batches
+    int next_ev = p.mx ? 4 : 2;
+    auto group = [&](GroupArgs &ga) {
+        if (!p.multi) {
+            launch_route_group(ga, sm, ev(next_ev), ev(next_ev + 1));
+            next_ev += 2;
+            return;
+        }
+        RouteArgs r{};
+        r.g = ga;
+        int32_t *rb = (int32_t *)(wsb + p.off_route);
+        r.e_of = rb, r.off_e = rb + p.P, r.cntb = rb + p.P + p.E, r.nblk = p.nblk;
+        r.ctg = r.cntb + (size_t)p.nblk * p.E;
+        hipEvent_t e6[6];
+        for (int i = 0; i < 6; ++i) e6[i] = ev(next_ev + i);
+        launch_route_multi(r, sm, events ? e6 : nullptr);
+        next_ev += 6;
+    };
     int st;
     (void)hipGetLastError();
     // 1) router logits (and the shared-gate logit)
@@ -987,7 +1085,7 @@ int run_grouped(const moe_w4a16_layer *Lr, const MoEPlan &p, const uint16_t *x, 
         q.x = x, q.q = xq, q.s = xq + (size_t)p.T * p.H, q.rows = p.T, q.n = p.H;
         launch_mx_quant(q, sm, ev(2), ev(3));
         if ((st = hip_status("mx quantise launch"))) return st;
-        launch_route_group(ga, sm, ev(4), ev(5));
+        group(ga);
         if ((st = hip_status("route/group launch"))) return st;
         const size_t rows = (size_t)p.P + p.T;
         uint8_t *hq = (uint8_t *)(wsb + p.off_hp), *hs = hq + rows * p.I;
@@ -997,7 +1095,7 @@ int run_grouped(const moe_w4a16_layer *Lr, const MoEPlan &p, const uint16_t *x, 
         a.s_scales = Lr->has_shared ? (const uint8_t *)Lr->shared_w13.scales : nullptr;
         a.xq = q.q, a.xs = q.s, a.grp = grp, a.pairs = pairs, a.hq = hq, a.hs = hs;
         a.H = p.H, a.I = p.I, a.K = p.K, a.T = p.T, a.P = p.P, a.Gmax = p.Gmax;
-        launch_mx13(a, sm, ev(6), ev(7));
+        launch_mx13(a, sm, ev(next_ev), ev(next_ev + 1));
         if ((st = hip_status("mx w13 launch"))) return st;
         MX2Args d{};
         d.codes = Lr->w2.codes, d.scales = (const uint8_t *)Lr->w2.scales;
@@ -1005,10 +1103,11 @@ int run_grouped(const moe_w4a16_layer *Lr, const MoEPlan &p, const uint16_t *x, 
         d.s_scales = Lr->has_shared ? (const uint8_t *)Lr->shared_w2.scales : nullptr;
         d.grp = grp, d.pairs = pairs, d.hq = hq, d.hs = hs, d.out = outp;
         d.H = p.H, d.I = p.I, d.K = p.K, d.T = p.T, d.P = p.P, d.Gmax = p.Gmax;
-        launch_mx2(d, sm, ev(8), ev(9));
+        launch_mx2(d, sm, ev(next_ev + 2), ev(next_ev + 3));
         if ((st = hip_status("mx w2 launch"))) return st;
+        next_ev += 4;
     } else {
-    launch_route_group(ga, sm, ev(2), ev(3));
+    group(ga);
     if ((st = hip_status("route/group launch"))) return st;
     // 3) grouped W13 + SiLU
     GW13Args a{};
@@ -1017,7 +1116,10 @@ int run_grouped(const moe_w4a16_layer *Lr, const MoEPlan &p, const uint16_t *x, 
     a.s_scales = Lr->has_shared ? (const uint16_t *)Lr->shared_w13.scales : nullptr;
     a.x = x, a.grp = grp, a.pairs = pairs, a.h_hi = h_hi, a.h_lo = h_lo;
     a.H = p.H, a.I = p.I, a.K = p.K, a.T = p.T, a.P = p.P, a.Gmax = p.Gmax, a.mfma_min = W4_MFMA_MIN;
-    launch_gw13(a, sm, ev(4), ev(5));
+    int32_t *ctg = p.multi ? (int32_t *)(wsb + p.off_route) + p.P + p.E + (size_t)p.nblk * p.E : nullptr;
+    a.ctg = ctg;
+    if (p.multi) launch_pf13(a, sm, ev(next_ev), ev(next_ev + 1));
+    else launch_gw13(a, sm, ev(next_ev), ev(next_ev + 1));
     if ((st = hip_status("grouped w13 launch"))) return st;
     // 4) grouped W2
     GW2Args d{};
@@ -1026,7 +1128,10 @@ int run_grouped(const moe_w4a16_layer *Lr, const MoEPlan &p, const uint16_t *x, 
     d.s_scales = Lr->has_shared ? (const uint16_t *)Lr->shared_w2.scales : nullptr;
     d.grp = grp, d.pairs = pairs, d.h_hi = h_hi, d.h_lo = h_lo, d.out = outp;
     d.H = p.H, d.I = p.I, d.K = p.K, d.T = p.T, d.P = p.P, d.Gmax = p.Gmax, d.mfma_min = W4_MFMA_MIN;
-    launch_gw2(d, sm, ev(6), ev(7));
+    d.ctg = ctg;
+    if (p.multi) launch_pf2(d, sm, ev(next_ev + 2), ev(next_ev + 3));
+    else launch_gw2(d, sm, ev(next_ev + 2), ev(next_ev + 3));
+    next_ev += 4;
     if ((st = hip_status("grouped w2 launch"))) return st;
     }
     // 5) ordered combine
@@ -1035,7 +1140,7 @@ int run_grouped(const moe_w4a16_layer *Lr, const MoEPlan &p, const uint16_t *x, 
     c.w = route ? w_ws : w_in;
     c.logits = logits, c.out = outp, c.y = y;
     c.H = p.H, c.E = p.E, c.K = p.K, c.T = p.T, c.P = p.P, c.lstride = p.lstride, c.has_shared = Lr->has_shared;
-    launch_gcombine(c, sm, ev(p.mx ? 10 : 8), ev(p.mx ? 11 : 9));
+    launch_gcombine(c, sm, ev(next_ev), ev(next_ev + 1));
     return hip_status("combine launch");
 }
 
@@ -1102,7 +1207,7 @@ int moe_w4a16_forward_timed(const moe_w4a16_layer *L, const uint16_t *x, int64_t
 int moe_w4a16_stage_count(const moe_w4a16_layer *L, int64_t T) {
     MoEPlan p;
     if (check_layer(L, T, p) != W4_OK) return 0;
-    return p.mx ? 6 : p.grouped ? 5 : 3;
+    return stage_count(p);
 }
 
 int moe_w4a16_experts(const moe_w4a16_layer *L, const uint16_t *x, int64_t T, const int32_t *ids, const float *w,

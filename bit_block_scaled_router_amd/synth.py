@@ -93,6 +93,10 @@ TINY_MOE_BF16SH = MoEShape("tiny-moe-h256-e8-k2-i128-bf16shared", 256, 128, 8, 2
 TINY_MOE_MX = MoEShape("tiny-moe-h256-e8-k2-i128-mxfp4", 256, 128, 8, 2, 128, 1, 0.0, 0, "mxfp4")
 QWEN_MOE_T1_MX = MoEShape("qwen3.6-35b-a3b-moe-decode-t1-mxfp4", 2048, 512, 256, 8, 512, 1, 0.0, 0, "mxfp4")
 QWEN_MOE_T32_MX = MoEShape("qwen3.6-35b-a3b-moe-batch32-zipf1.1-mxfp4", 2048, 512, 256, 8, 512, 32, 1.1, 0, "mxfp4")
+# prefill-sized batches: 2048 tokens x top-8 = 16,384 (token, slot) pairs, ~64 per
+# expert (no popularity bias), the MFMA-bound regime of the grouped path
+QWEN_MOE_PREFILL = MoEShape("qwen3.6-35b-a3b-moe-prefill2048", 2048, 512, 256, 8, 512, 2048, 0.0, 0)
+QWEN_MOE_PREFILL_MX = MoEShape("qwen3.6-35b-a3b-moe-prefill2048-mxfp4", 2048, 512, 256, 8, 512, 2048, 0.0, 0, "mxfp4")
 
 
 # --------------------------------------------------------------------------- draws

@@ -56,8 +56,8 @@ def test_edge_layers(shape, Ts):
 
 
 def test_largest_grouped_batch():
-    """T k = 4096 (token, slot) pairs, the grouped path's limit; groups of ~64 rows
-    run several 32-column MFMA passes."""
+    """T k = 4096 (token, slot) pairs, the largest batch one block groups; groups
+    of ~64 rows run several 32-column MFMA passes."""
     shape = synth.MoEShape("edge-pairs4096", 256, 128, 64, 8, 128, 512, 0.0, 6)
     dev_layer = wl.build_moe_layer(shape, device=DEV)
     assert w4.moe_w4a16_stage_count(dev_layer, 512) == 5

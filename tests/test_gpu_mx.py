@@ -66,7 +66,7 @@ def _ws_layout(shape, T):
     the library's order (each region 256-byte aligned): logits [T][ceil64(E+1)]
     fp32, ids and weights [T][k], group table, pair list, h (codes [P+T][I] then
     E8M0 scales [P+T][I/32]), expert outputs fp32 [P+T][H], x codes [T][H] then
-    scales [T][H/32]."""
+    scales [T][H/32], and past 4096 pairs the multi-launch grouping's arrays."""
     def up(v):
         return (v + 255) // 256 * 256
     H, I, E, K = shape.hidden, shape.inter, shape.num_experts, shape.top_k
@@ -80,7 +80,10 @@ def _ws_layout(shape, T):
     off_h = off
     off = up(off + rows * I * 4)
     off = up(off + rows * H * 4)
-    return off_h, off, up(off + T * H + T * (H // 32))
+    total = up(off + T * H + T * (H // 32))
+    if P > 4096:  # grouping over three launches: pair experts, list starts, block histograms
+        total = up(total + (P + E + (T + 15) // 16 * E) * 4)
+    return off_h, off, total
 
 
 def _e4m3(codes):
@@ -268,3 +271,15 @@ def test_mx_full_t512_sampled(full_mx):
     print("mx full T=512 (sampled)", flush=True)
     xb = tie_free_tokens(shape, or_layer, 512, first=1000)
     _mx_case(shape, dev_layer, or_layer, xb, "mx full T=512", tokens=range(5, 512, 64))
+
+
+def test_mx_prefill_sampled():
+    """T = 2048 (16,384 pairs, ~64 per expert): MFMA router, grouping over three
+    launches, MX expert kernels with several column passes per group."""
+    shape = synth.QWEN_MOE_PREFILL_MX
+    dev_layer = wl.build_moe_layer(shape, device=DEV)
+    assert w4.moe_w4a16_stage_count(dev_layer, shape.tokens) == 8
+    or_layer = oracle_layer(shape)
+    print("mx prefill T=2048 (sampled)", flush=True)
+    xb = tie_free_tokens(shape, or_layer, shape.tokens)
+    _mx_case(shape, dev_layer, or_layer, xb, "mx prefill T=2048", tokens=[0, 1, 700, 1300, 2046, 2047])

@@ -188,10 +188,15 @@ def test_mxfp4_layer_plan_and_validation():
     assert w4.lib().moe_w4a16_stage_count(C.byref(L), 1) == 6
     assert w4.lib().moe_w4a16_stage_count(C.byref(L), 64) == 6
     assert w4.lib().moe_w4a16_workspace_bytes(C.byref(L), 1) > 0
-    # 2048 tokens x top-2 = 4096 pairs is the limit
-    assert w4.lib().moe_w4a16_workspace_bytes(C.byref(L), 2048) > 0
-    assert w4.lib().moe_w4a16_workspace_bytes(C.byref(L), 2049) == 0
-    assert _fwd(L, T=2049, ws_bytes=1 << 30) == w4.W4_ERR_UNSUPPORTED
+    # more than 4096 pairs group over three launches: 2 more stages
+    assert w4.lib().moe_w4a16_stage_count(C.byref(L), 2048) == 6
+    assert w4.lib().moe_w4a16_stage_count(C.byref(L), 2049) == 8
+    # at most 65536 pairs per call, at most 16384 tokens
+    L8 = mxl(top_k=8)
+    assert w4.lib().moe_w4a16_workspace_bytes(C.byref(L8), 8192) > 0
+    assert w4.lib().moe_w4a16_workspace_bytes(C.byref(L8), 8193) == 0
+    assert _fwd(L8, T=8193, ws_bytes=1 << 40) == w4.W4_ERR_UNSUPPORTED
+    assert _fwd(L, T=16385, ws_bytes=1 << 40) == w4.W4_ERR_INVALID_ARG
     # inter off the 128 grid, a bf16 shared expert, mixed formats
     bad_i = _layer(inter=96, shared_inter=96, w13=_mat(fmt=mx, groups=E, n=192, k=H), w2=_mat(fmt=mx, groups=E, n=H, k=96),
                    has_shared=0)
@@ -200,6 +205,10 @@ def test_mxfp4_layer_plan_and_validation():
     assert _fwd(mxl(shared_w13=_mat(fmt=bf, groups=1, n=2 * I, k=H, scales=None),
                     shared_w2=_mat(fmt=bf, groups=1, n=H, k=I, scales=None)), ws_bytes=1 << 30) == w4.W4_ERR_UNSUPPORTED
     assert _fwd(mxl(w2=_mat(groups=E, n=H, k=I)), ws_bytes=1 << 30) == w4.W4_ERR_LAYOUT
+    # E2M1: batched path from T = 4, three grouping launches past 4096 pairs;
+    # past 65536 pairs the single-token path
+    E2 = _layer(top_k=8)
+    assert [w4.lib().moe_w4a16_stage_count(C.byref(E2), T) for T in (3, 4, 512, 513, 8192, 8193)] == [3, 5, 5, 7, 7, 3]
     # the timed entry point wants 12 events on the MX path
     ev = (C.c_void_p * 10)(*([1] * 10))
     st = w4.lib().moe_w4a16_forward_timed(C.byref(L), 1 << 20, 1, 1 << 21, None, None, 1 << 24,
