@@ -104,6 +104,7 @@ struct MX13Args {
     uint8_t *hq;            // [P + T][I]
     uint8_t *hs;            // [P + T][I/32]
     int H, I, K, T, P, Gmax, tiles;
+    const int32_t *ctg;     // column tiles (large-batch kernels only)
 };
 
 struct MX2Args {
@@ -117,6 +118,7 @@ struct MX2Args {
     const uint8_t *hs;
     float *out;             // [P + T][H]
     int H, I, K, T, P, Gmax, tiles;
+    const int32_t *ctg;     // column tiles (large-batch kernels only)
 };
 
 size_t grouped_lds_bytes(int E, int P);
@@ -125,6 +127,8 @@ void launch_pf13(GW13Args &a, hipStream_t st, hipEvent_t e0, hipEvent_t e1);
 void launch_pf2(GW2Args &a, hipStream_t st, hipEvent_t e0, hipEvent_t e1);
 void launch_route_multi(RouteArgs &a, hipStream_t st, hipEvent_t *ev);  // ev: 6 events or null
 void launch_mx_quant(MXQuantArgs &a, hipStream_t st, hipEvent_t e0, hipEvent_t e1);
+void launch_pfmx13(MX13Args &a, hipStream_t st, hipEvent_t e0, hipEvent_t e1);  // large batches
+void launch_pfmx2(MX2Args &a, hipStream_t st, hipEvent_t e0, hipEvent_t e1);
 void launch_mx13(MX13Args &a, hipStream_t st, hipEvent_t e0, hipEvent_t e1);
 void launch_mx2(MX2Args &a, hipStream_t st, hipEvent_t e0, hipEvent_t e1);
 void launch_route_group(GroupArgs &a, hipStream_t st, hipEvent_t e0, hipEvent_t e1);

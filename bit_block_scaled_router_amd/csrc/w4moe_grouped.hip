@@ -1183,24 +1183,272 @@ __global__ __launch_bounds__(256) void k_moe_mx2(MX2Args a) {
     }
 }
 
+// Large batches, MX: the structure of k_moe_pf13 / k_moe_pf2 with fp8
+// activations (one byte per element, an E8M0 scale per 32) in the LDS tile and
+// the scaled FP4 MFMA (16 x 16 x 128, both block scales fed to the instruction).
+// A column's 128-byte chunk is 8 units of 16 bytes stored at j ^ ((c / 2) % 8),
+// so the 16 columns one operand read touches cover all 64 banks once.
+constexpr int PFX_LROW = PF_KC;  // bytes per LDS row
+__device__ __forceinline__ uint4 pfx_unit(const uint8_t (*rows)[PFX_LROW], int c, int j) {
+    return *reinterpret_cast<const uint4 *>(&rows[c][16 * (j ^ ((c >> 1) & 7))]);
+}
+// loader role of thread tid: column tid / 4, bytes 32 (tid % 4) .. +31 of the
+// chunk and the column's E8M0 scale byte of block tid % 4
+__device__ __forceinline__ void pfx_store(uint8_t *row, int c, int lq, const uint4 (&v)[2]) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) *reinterpret_cast<uint4 *>(row + 16 * ((2 * lq + i) ^ ((c >> 1) & 7))) = v[i];
+}
+
+__device__ __forceinline__ void pfmx13_unit(const MX13Args &a, int gs, int rt, int n0, uint8_t (*xs)[PF_COLS][PFX_LROW],
+                                            uint8_t (*xsc)[PF_COLS][4]) {
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int H = a.H, I = a.I;
+    const uint32_t spr = (uint32_t)(H >> 5);
+    const size_t mat_codes = (size_t)(2 * I) * (H >> 1), mat_scales = (size_t)(2 * I) * spr;
+    const GroupView<uint8_t> gv = group_view(a.grp, gs, a.Gmax, a.P, a.T, a.codes, a.scales, mat_codes, mat_scales,
+                                             a.s_codes, a.s_scales);
+    const Buf cb = make_buf(gv.codes, (uint32_t)mat_codes);
+    const Buf sb = make_buf(gv.scales, (uint32_t)mat_scales);
+    const Buf xqb = make_buf(a.xq, (uint32_t)a.T * (uint32_t)H);
+    const Buf xsb = make_buf(a.xs, (uint32_t)a.T * (uint32_t)(H >> 5));
+    const int *plist = a.pairs + gv.off;
+    const int r = lane & 15, g = lane >> 4;
+    const int i0 = rt * PF_ROWS + 32 * wv;  // the wave's 32 h rows: tiles i0, i0 + 16
+    const uint32_t rows[4] = {(uint32_t)(i0 + r), (uint32_t)(i0 + 16 + r), (uint32_t)(I + i0 + r),
+                              (uint32_t)(I + i0 + 16 + r)};
+    const int lc = tid >> 2, lq = tid & 3;
+    const int nch = H / PF_KC;
+    const bool lv = n0 + lc < gv.m;
+    const int tok = lv ? token_of(plist[n0 + lc], a.P, a.K) : 0;
+    const uint32_t xo = (uint32_t)(tok * H + 32 * lq), so = (uint32_t)(tok * (H >> 5) + lq);
+    uint4 xr[2];
+    uint32_t sr;
+    xr[0] = ld128(xqb, lv ? xo : OOB);
+    xr[1] = ld128(xqb, lv ? xo + 16u : OOB);
+    sr = ld8(xsb, lv ? so : OOB);
+    uint4 cw[4];
+    uint32_t sw[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        cw[t] = ld128(cb, rows[t] * (uint32_t)(H >> 1) + (uint32_t)(16 * g));
+        sw[t] = ld8(sb, rows[t] * spr + (uint32_t)g);
+    }
+    f32x4 acc[4][4];  // [gate 0, gate 1, up 0, up 1][column tile]
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) acc[t][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int ch = 0; ch < nch; ++ch) {
+        uint8_t(*xb)[PFX_LROW] = xs[ch & 1];
+        uint8_t(*xc)[4] = xsc[ch & 1];
+        pfx_store(xb[lc], lc, lq, xr);
+        xc[lc][lq] = (uint8_t)sr;
+        __syncthreads();
+        uint4 cc[4];
+        uint32_t sc[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) cc[t] = cw[t], sc[t] = sw[t];
+        if (ch + 1 < nch) {
+            const uint32_t kn = (uint32_t)((ch + 1) * PF_KC);
+            xr[0] = ld128(xqb, lv ? xo + kn : OOB);
+            xr[1] = ld128(xqb, lv ? xo + kn + 16u : OOB);
+            sr = ld8(xsb, lv ? so + (kn >> 5) : OOB);
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                cw[t] = ld128(cb, rows[t] * (uint32_t)(H >> 1) + ((kn + 32u * (uint32_t)g) >> 1));
+                sw[t] = ld8(sb, rows[t] * spr + (kn >> 5) + (uint32_t)g);
+            }
+        }
+        uint4 blo[4], bhi[4];
+        uint32_t bs[4];
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) {
+            blo[nt] = pfx_unit(xb, 16 * nt + r, g);
+            bhi[nt] = pfx_unit(xb, 16 * nt + r, 4 + g);
+            bs[nt] = xc[16 * nt + r][g];
+        }
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int nt = 0; nt < 4; ++nt) acc[t][nt] = mfma_mx(cc[t], blo[nt], bhi[nt], sc[t], bs[nt], acc[t][nt]);
+    }
+    // lane holds rows 4g + j of each 16-row tile, column 16 nt + r; the 32 h rows
+    // of the wave form one MX block per column, spread over lanes r, r+16, r+32, r+48
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+        float h[8];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const float g0 = acc[0][nt][j], u0 = acc[2][nt][j];
+            const float g1 = acc[1][nt][j], u1 = acc[3][nt][j];
+            h[j] = (g0 / (1.f + expf(-g0))) * u0;
+            h[4 + j] = (g1 / (1.f + expf(-g1))) * u1;
+        }
+        float m = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(h[e]));
+        m = fmaxf(m, __shfl_xor(m, 16));
+        m = fmaxf(m, __shfl_xor(m, 32));
+        const int X = mx8_exponent(m);
+        const int idx = n0 + 16 * nt + r;
+        if (idx < gv.m) {
+            const int p = plist[idx];
+            const size_t o = (size_t)p * I + i0 + 4 * g;
+            *reinterpret_cast<uint32_t *>(a.hq + o) = mx8_pack4(h[0], h[1], h[2], h[3], X);
+            *reinterpret_cast<uint32_t *>(a.hq + o + 16) = mx8_pack4(h[4], h[5], h[6], h[7], X);
+            if (g == 0) a.hs[(size_t)p * (I >> 5) + (i0 >> 5)] = (uint8_t)(X + 127);
+        }
+    }
+    __syncthreads();
+}
+
+__global__ __launch_bounds__(256) void k_moe_pfmx13(MX13Args a) {
+    __shared__ __align__(16) uint8_t xs[2][PF_COLS][PFX_LROW];
+    __shared__ uint8_t xsc[2][PF_COLS][4];
+    const bool sh = a.s_codes != nullptr;
+    const int nct = pf_tile_count(a.grp, a.Gmax, sh, a.T);
+    const int nu = pf_unit_count(nct, a.tiles);
+    for (int u = blockIdx.x; u < nu; u += gridDim.x) {
+        int gs, rt, n0;
+        if (pf_unit(a.grp, a.ctg, a.Gmax, sh, nct, u, a.tiles, gs, rt, n0)) pfmx13_unit(a, gs, rt, n0, xs, xsc);
+    }
+}
+
+__device__ __forceinline__ void pfmx2_unit(const MX2Args &a, int gs, int rt, int n0, uint8_t (*hsm)[PF_COLS][PFX_LROW],
+                                           uint8_t (*hsc)[PF_COLS][4]) {
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int H = a.H, I = a.I;
+    const uint32_t spr = (uint32_t)(I >> 5);
+    const size_t mat_codes = (size_t)H * (I >> 1), mat_scales = (size_t)H * spr;
+    const GroupView<uint8_t> gv = group_view(a.grp, gs, a.Gmax, a.P, a.T, a.codes, a.scales, mat_codes, mat_scales,
+                                             a.s_codes, a.s_scales);
+    const Buf cb = make_buf(gv.codes, (uint32_t)mat_codes);
+    const Buf sb = make_buf(gv.scales, (uint32_t)mat_scales);
+    const uint32_t rowsall = (uint32_t)(a.P + a.T);
+    const Buf hqb = make_buf(a.hq, rowsall * (uint32_t)I);
+    const Buf hsb = make_buf(a.hs, rowsall * (uint32_t)(I >> 5));
+    const int *plist = a.pairs + gv.off;
+    const int r = lane & 15, g = lane >> 4;
+    const int o0 = rt * PF_ROWS + 32 * wv;  // the wave's output rows: tiles o0, o0 + 16
+    const uint32_t rows[2] = {(uint32_t)(o0 + r), (uint32_t)(o0 + 16 + r)};
+    const int lc = tid >> 2, lq = tid & 3;
+    const int nch = I / PF_KC;
+    const bool lv = n0 + lc < gv.m;
+    const int pr = lv ? plist[n0 + lc] : 0;
+    const uint32_t ho = (uint32_t)(pr * I + 32 * lq), so = (uint32_t)(pr * (I >> 5) + lq);
+    uint4 hr[2];
+    uint32_t sr;
+    hr[0] = ld128(hqb, lv ? ho : OOB);
+    hr[1] = ld128(hqb, lv ? ho + 16u : OOB);
+    sr = ld8(hsb, lv ? so : OOB);
+    uint4 cw[2];
+    uint32_t sw[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+        cw[t] = ld128(cb, rows[t] * (uint32_t)(I >> 1) + (uint32_t)(16 * g));
+        sw[t] = ld8(sb, rows[t] * spr + (uint32_t)g);
+    }
+    f32x4 acc[2][4];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) acc[t][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int ch = 0; ch < nch; ++ch) {
+        uint8_t(*hb)[PFX_LROW] = hsm[ch & 1];
+        uint8_t(*hc)[4] = hsc[ch & 1];
+        pfx_store(hb[lc], lc, lq, hr);
+        hc[lc][lq] = (uint8_t)sr;
+        __syncthreads();
+        uint4 cc[2];
+        uint32_t sc[2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) cc[t] = cw[t], sc[t] = sw[t];
+        if (ch + 1 < nch) {
+            const uint32_t kn = (uint32_t)((ch + 1) * PF_KC);
+            hr[0] = ld128(hqb, lv ? ho + kn : OOB);
+            hr[1] = ld128(hqb, lv ? ho + kn + 16u : OOB);
+            sr = ld8(hsb, lv ? so + (kn >> 5) : OOB);
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                cw[t] = ld128(cb, rows[t] * (uint32_t)(I >> 1) + ((kn + 32u * (uint32_t)g) >> 1));
+                sw[t] = ld8(sb, rows[t] * spr + (kn >> 5) + (uint32_t)g);
+            }
+        }
+        uint4 blo[4], bhi[4];
+        uint32_t bs[4];
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) {
+            blo[nt] = pfx_unit(hb, 16 * nt + r, g);
+            bhi[nt] = pfx_unit(hb, 16 * nt + r, 4 + g);
+            bs[nt] = hc[16 * nt + r][g];
+        }
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int nt = 0; nt < 4; ++nt) acc[t][nt] = mfma_mx(cc[t], blo[nt], bhi[nt], sc[t], bs[nt], acc[t][nt]);
+    }
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+        const int idx = n0 + 16 * nt + r;
+        if (idx < gv.m) {
+            float *op = a.out + (size_t)plist[idx] * H + o0 + 4 * g;
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+                *reinterpret_cast<float4 *>(op + 16 * t) = make_float4(acc[t][nt][0], acc[t][nt][1], acc[t][nt][2],
+                                                                      acc[t][nt][3]);
+        }
+    }
+    __syncthreads();
+}
+
+__global__ __launch_bounds__(256) void k_moe_pfmx2(MX2Args a) {
+    __shared__ __align__(16) uint8_t hsm[2][PF_COLS][PFX_LROW];
+    __shared__ uint8_t hsc[2][PF_COLS][4];
+    const bool sh = a.s_codes != nullptr;
+    const int nct = pf_tile_count(a.grp, a.Gmax, sh, a.T);
+    const int nu = pf_unit_count(nct, a.tiles);
+    for (int u = blockIdx.x; u < nu; u += gridDim.x) {
+        int gs, rt, n0;
+        if (pf_unit(a.grp, a.ctg, a.Gmax, sh, nct, u, a.tiles, gs, rt, n0)) pfmx2_unit(a, gs, rt, n0, hsm, hsc);
+    }
+}
+
 // ================================================================= combine
 
 __global__ __launch_bounds__(256) void k_moe_gcombine(GCombineArgs a) {
+    // four consecutive outputs per thread (H is a multiple of 64); every element
+    // is summed in slot order, then the shared expert, as one scalar would be
     const int t = blockIdx.y;
-    const int n = blockIdx.x * blockDim.x + threadIdx.x;
+    const int n = 4 * (blockIdx.x * blockDim.x + threadIdx.x);
     if (n >= a.H) return;
-    float v = 0.f;
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
     for (int j = 0; j < a.K; ++j) {
         const int p = t * a.K + j;
         const int e = ld_uniform(a.ids, p);
         const float w = ld_uniform(a.w, p);
-        v += (e >= 0 && e < a.E) ? w * a.out[(size_t)p * a.H + n] : __builtin_nanf("");
+        if (e >= 0 && e < a.E) {
+            const float4 o = *reinterpret_cast<const float4 *>(a.out + (size_t)p * a.H + n);
+            v.x += w * o.x, v.y += w * o.y, v.z += w * o.z, v.w += w * o.w;
+        } else {
+            v = make_float4(__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""));
+        }
     }
     if (a.has_shared) {
         const float sig = 1.f / (1.f + expf(-ld_uniform(a.logits, t * a.lstride + a.E)));
-        v += sig * a.out[(size_t)(a.P + t) * a.H + n];
+        const float4 o = *reinterpret_cast<const float4 *>(a.out + (size_t)(a.P + t) * a.H + n);
+        v.x += sig * o.x, v.y += sig * o.y, v.z += sig * o.z, v.w += sig * o.w;
     }
-    a.y[(size_t)t * a.H + n] = f32_to_bf16_rne(v);
+    uint16_t *yp = a.y + (size_t)t * a.H + n;
+    if ((reinterpret_cast<uintptr_t>(a.y) & 7) == 0) {  // y needs only 2-byte alignment
+        const uint32_t lo = f32_to_bf16_rne(v.x) | ((uint32_t)f32_to_bf16_rne(v.y) << 16);
+        const uint32_t hi = f32_to_bf16_rne(v.z) | ((uint32_t)f32_to_bf16_rne(v.w) << 16);
+        *reinterpret_cast<uint2 *>(yp) = make_uint2(lo, hi);
+    } else {
+        yp[0] = f32_to_bf16_rne(v.x), yp[1] = f32_to_bf16_rne(v.y);
+        yp[2] = f32_to_bf16_rne(v.z), yp[3] = f32_to_bf16_rne(v.w);
+    }
 }
 
 }  // namespace w4k
@@ -1312,6 +1560,16 @@ void launch_mx_quant(MXQuantArgs &a, hipStream_t st, hipEvent_t e0, hipEvent_t e
     go_ev(st, e0, e1, k_mx_quant, dim3((unsigned)((blocks + 255) / 256)), dim3(256), 0, a);
 }
 
+void launch_pfmx13(MX13Args &a, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
+    a.tiles = a.I / PF_ROWS;
+    go_ev(st, e0, e1, k_moe_pfmx13, dim3(W4_PF_BLOCKS), dim3(256), 0, a);
+}
+
+void launch_pfmx2(MX2Args &a, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
+    a.tiles = a.H / PF_ROWS;
+    go_ev(st, e0, e1, k_moe_pfmx2, dim3(W4_PF_BLOCKS), dim3(256), 0, a);
+}
+
 void launch_mx13(MX13Args &a, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
     a.tiles = a.I / 32;
     go_ev(st, e0, e1, k_moe_mx13, dim3(grouped_grid(a.Gmax, a.tiles)), dim3(256), 0, a);
@@ -1323,7 +1581,7 @@ void launch_mx2(MX2Args &a, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
 }
 
 void launch_gcombine(GCombineArgs &a, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
-    const dim3 g((unsigned)((a.H + 255) / 256), (unsigned)a.T), b(256);
+    const dim3 g((unsigned)((a.H / 4 + 255) / 256), (unsigned)a.T), b(256);
     go_ev(st, e0, e1, k_moe_gcombine, g, b, 0, a);
 }
 

@@ -198,17 +198,20 @@ __global__ __launch_bounds__(512) void k_router(const uint16_t *__restrict__ wr,
 
 // Large batches: the router as a bf16 GEMM on MFMA, logits[t][r] = Wr[r] . x[t]
 // for rows r_begin <= r < r_end (row E = the shared-gate weight).  A block
-// covers 64 rows x 64 tokens: wave w owns rows 16 w .. 16 w + 15 against four
-// 16-token column tiles, K in steps of 32 (one 16x16x32 MFMA per tile).  Every
-// x tile is read by ceil(rows / 64) blocks and every router row by ceil(T / 64),
-// instead of all T tokens per row as in k_router.
+// covers 16 rows x 64 tokens (four 16-token MFMA column tiles); its 4 waves
+// split K into quarters (16x16x32 MFMAs, the next 128-wide chunk loaded while
+// the current one is multiplied) and the partial sums are added in wave order
+// through LDS.  Every x tile is read by ceil(rows / 16) blocks and every router
+// row by ceil(T / 64), instead of all T tokens per row as in k_router.
 __global__ __launch_bounds__(256) void k_router_mfma(const uint16_t *__restrict__ wr,
                                                      const uint16_t *__restrict__ wsg,
                                                      const uint16_t *__restrict__ x, float *__restrict__ logits,
                                                      int E, int H, int T, int r_begin, int r_end, int lstride) {
+    __shared__ float red[3][16][64];
     const int lane = threadIdx.x & 63, wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int r = lane & 15, q = lane >> 4;
-    const int row = r_begin + (int)blockIdx.y * 64 + 16 * wv + r;  // this lane's A row
+    const int row0 = r_begin + (int)blockIdx.y * 16;
+    const int row = row0 + r;  // this lane's A row
     const int tok0 = (int)blockIdx.x * 64;
     const Buf wb = make_buf(wr, (uint32_t)E * (uint32_t)H * 2u);
     const Buf gb = make_buf(wsg, wsg ? (uint32_t)H * 2u : 0u);
@@ -221,35 +224,60 @@ __global__ __launch_bounds__(256) void k_router_mfma(const uint16_t *__restrict_
         const int t = tok0 + 16 * nt + r;
         xoff[nt] = t < T ? (uint32_t)t * (uint32_t)H * 2u : OOB;
     }
-    f32x4 acc[4];
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int k0 = 0; k0 < H; k0 += 128) {
-        uint4 av[4], bv[4][4];
+    // this wave's K range: chunks of 128 dealt round-robin
+    auto load = [&](int k0, uint4 (&av)[4], uint4 (&bv)[4][4]) {
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
             const uint32_t kb = (uint32_t)(k0 + 32 * s + 8 * q) * 2u;
-            const bool kv = k0 + 32 * s < H;
+            const bool kv = k0 >= 0 && k0 + 32 * s < H;
             const uint4 u = ld128(wb, (in_wr && kv) ? aoff + kb : OOB);
             const uint4 v = ld128(gb, (in_g && kv) ? kb : OOB);
             av[s] = make_uint4(u.x | v.x, u.y | v.y, u.z | v.z, u.w | v.w);
 #pragma unroll
             for (int nt = 0; nt < 4; ++nt) bv[s][nt] = ld128(xb, (kv && xoff[nt] != OOB) ? xoff[nt] + kb : OOB);
         }
+    };
+    f32x4 acc[4];
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    uint4 av[4], bv[4][4];
+    int k0 = 128 * wv;
+    load(k0 < H ? k0 : -1, av, bv);
+    for (; k0 < H; k0 += 512) {
+        uint4 ac[4], bc[4][4];
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            ac[s] = av[s];
+#pragma unroll
+            for (int nt = 0; nt < 4; ++nt) bc[s][nt] = bv[s][nt];
+        }
+        if (k0 + 512 < H) load(k0 + 512, av, bv);
 #pragma unroll
         for (int s = 0; s < 4; ++s)
 #pragma unroll
-            for (int nt = 0; nt < 4; ++nt) acc[nt] = mfma16x16x32(__builtin_bit_cast(bf16x8, av[s]), __builtin_bit_cast(bf16x8, bv[s][nt]), acc[nt]);
+            for (int nt = 0; nt < 4; ++nt)
+                acc[nt] = mfma16x16x32(__builtin_bit_cast(bf16x8, ac[s]), __builtin_bit_cast(bf16x8, bc[s][nt]), acc[nt]);
     }
-    // lane holds rows 4q + j of the wave's 16, token column r of each tile
+    if (wv > 0) {
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-        const int t = tok0 + 16 * nt + r;
-        if (t >= T) continue;
+        for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int rr = r_begin + (int)blockIdx.y * 64 + 16 * wv + 4 * q + j;
-            if (rr < r_end) logits[(size_t)t * lstride + rr] = acc[nt][j];
+            for (int j = 0; j < 4; ++j) red[wv - 1][nt * 4 + j][lane] = acc[nt][j];
+    }
+    __syncthreads();
+    if (wv == 0) {
+        // lane holds rows 4q + j, token column r of each tile
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) {
+            const int t = tok0 + 16 * nt + r;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                float v = acc[nt][j];
+#pragma unroll
+                for (int w = 0; w < 3; ++w) v += red[w][nt * 4 + j][lane];
+                const int rr = row0 + 4 * q + j;
+                if (t < T && rr < r_end) logits[(size_t)t * lstride + rr] = v;
+            }
         }
     }
 }
@@ -826,7 +854,7 @@ int launch_router(const moe_w4a16_layer *Lr, const MoEPlan &p, const uint16_t *x
     const int nrows = r_end - r_begin;
     if (nrows <= 0) return W4_OK;
     if (p.T >= W4_ROUTER_MFMA_MIN_T) {
-        go(st, k_router_mfma, dim3((unsigned)((p.T + 63) / 64), (unsigned)((nrows + 63) / 64)), dim3(256), 0,
+        go(st, k_router_mfma, dim3((unsigned)((p.T + 63) / 64), (unsigned)((nrows + 15) / 16)), dim3(256), 0,
            Lr->router_w, Lr->shared_gate_w, x, logits, p.E, p.H, p.T, r_begin, r_end, p.lstride);
         return W4_OK;
     }
@@ -1095,7 +1123,10 @@ int run_grouped(const moe_w4a16_layer *Lr, const MoEPlan &p, const uint16_t *x, 
         a.s_scales = Lr->has_shared ? (const uint8_t *)Lr->shared_w13.scales : nullptr;
         a.xq = q.q, a.xs = q.s, a.grp = grp, a.pairs = pairs, a.hq = hq, a.hs = hs;
         a.H = p.H, a.I = p.I, a.K = p.K, a.T = p.T, a.P = p.P, a.Gmax = p.Gmax;
-        launch_mx13(a, sm, ev(next_ev), ev(next_ev + 1));
+        int32_t *ctg = p.multi ? (int32_t *)(wsb + p.off_route) + p.P + p.E + (size_t)p.nblk * p.E : nullptr;
+        a.ctg = ctg;
+        if (p.multi) launch_pfmx13(a, sm, ev(next_ev), ev(next_ev + 1));
+        else launch_mx13(a, sm, ev(next_ev), ev(next_ev + 1));
         if ((st = hip_status("mx w13 launch"))) return st;
         MX2Args d{};
         d.codes = Lr->w2.codes, d.scales = (const uint8_t *)Lr->w2.scales;
@@ -1103,7 +1134,9 @@ int run_grouped(const moe_w4a16_layer *Lr, const MoEPlan &p, const uint16_t *x, 
         d.s_scales = Lr->has_shared ? (const uint8_t *)Lr->shared_w2.scales : nullptr;
         d.grp = grp, d.pairs = pairs, d.hq = hq, d.hs = hs, d.out = outp;
         d.H = p.H, d.I = p.I, d.K = p.K, d.T = p.T, d.P = p.P, d.Gmax = p.Gmax;
-        launch_mx2(d, sm, ev(next_ev + 2), ev(next_ev + 3));
+        d.ctg = ctg;
+        if (p.multi) launch_pfmx2(d, sm, ev(next_ev + 2), ev(next_ev + 3));
+        else launch_mx2(d, sm, ev(next_ev + 2), ev(next_ev + 3));
         if ((st = hip_status("mx w2 launch"))) return st;
         next_ev += 4;
     } else {

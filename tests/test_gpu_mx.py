@@ -75,14 +75,14 @@ def _ws_layout(shape, T):
     off = up(T * ((E + 1 + 63) // 64 * 64) * 4)
     off = up(off + T * K * 4)
     off = up(off + T * K * 4)
-    off = up(off + (1 + 3 * min(E, P)) * 4)
+    off = up(off + (2 + 3 * min(E, P)) * 4)
     off = up(off + rows * 4)
     off_h = off
     off = up(off + rows * I * 4)
     off = up(off + rows * H * 4)
     total = up(off + T * H + T * (H // 32))
-    if P > 4096:  # grouping over three launches: pair experts, list starts, block histograms
-        total = up(total + (P + E + (T + 15) // 16 * E) * 4)
+    if P > 4096:  # grouping over three launches: pair experts, list starts, block histograms, column tiles
+        total = up(total + (P + E + (T + 15) // 16 * E + 2 * (min(E, P) + P // 64 + 1)) * 4)
     return off_h, off, total
 
 
