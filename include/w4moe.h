@@ -219,7 +219,8 @@ typedef struct moe_w4a16_layer {
  * its contents need no initialisation and are scratch between calls. */
 size_t moe_w4a16_workspace_bytes(const moe_w4a16_layer *L, int64_t T);
 
-/* Full layer for T tokens (decode: T = 1; batched decode: T > 1):
+/* Full layer for T tokens, 1 <= T <= 16384 (decode: T = 1; batched decode and
+ * prefill: T > 1):
  *   logits = Wr x (+ bias); p = softmax over all E; ids = the k largest p,
  *   sorted by descending p, ties to the lower expert id; w = p[ids] / sum
  *   (computed as softmax over the k selected logits, the equal form [TUT 06]);
@@ -252,11 +253,17 @@ int moe_w4a16_forward_timed(const moe_w4a16_layer *L, const uint16_t *x, int64_t
  * and grouping of the (token, slot) pairs by expert; W13 + SiLU per expert
  * group, on MFMA for groups of at least 4 tokens; W2 per expert group; ordered
  * combine).  The batched path serves E2M1 layers with H and I multiples of 128
- * and at most 4096, T >= 4 and T * top_k <= 4096; other requests take the
+ * and at most 4096, T >= 4 and T * top_k <= 65536; other requests take the
  * single-token path.  MXFP4 layers always run 6 kernels (router; x to MXFP8;
  * top-k and grouping; W13 + SiLU with h quantised to MXFP8; W2; ordered
- * combine), need H and I multiples of 128 and T * top_k <= 4096, and a shared
- * expert in MXFP4 (W4_ERR_UNSUPPORTED otherwise).
+ * combine), need H and I multiples of 128 and a shared expert in MXFP4
+ * (W4_ERR_UNSUPPORTED otherwise).  Batches of more than 4096 (token, slot)
+ * pairs (prefill sizes; at most 65536 pairs, T <= 16384) group their pairs
+ * over three launches (per-block top-k and expert histograms; one scan; a
+ * scatter) instead of one, so the grouped path takes 7 kernels (MXFP4: 8), and
+ * run W13 and W2 as grouped GEMMs with LDS-staged activations; from T = 64
+ * the router runs on MFMA.  E2M1 requests beyond 65536 pairs take the
+ * single-token path; MXFP4 ones fail with W4_ERR_UNSUPPORTED.
  * Sources: lynn-engine README, R5 notes (tokens-per-expert grouping, inverse
  * scatter) and P85-P92 (per-16 scales applied exactly). */
 int moe_w4a16_stage_count(const moe_w4a16_layer *L, int64_t T);
