@@ -42,8 +42,9 @@ struct RouteArgs {
     int32_t *off_e;
     int32_t *ctg;  // [2 x column tiles]: routed group, first column (see k_route_scan)
     int nblk;
+    int tpb;       // tokens per block of k_route_topk / k_route_scatter (<= ROUTE_MAX_TPB)
 };
-constexpr int ROUTE_TOKENS_PER_BLOCK = 16;
+constexpr int ROUTE_MAX_TPB = 16;
 
 struct GW13Args {
     const uint8_t *codes;   // routed W13 [E][2I][H/2]

@@ -130,7 +130,7 @@ __global__ __launch_bounds__(1024) void k_moe_route_group(GroupArgs a) {
     for (int t = tid; t < T; t += blockDim.x) a.pairs[P + t] = P + t;
 }
 
-// Large batches: ROUTE_TOKENS_PER_BLOCK tokens per block (4 waves), top-k and
+// Multi-launch grouping: r.tpb tokens per block (4 waves), top-k and
 // weights per token, the expert of each pair, and the block's expert histogram
 // (LDS counts; only the totals are used, so the order of the increments is free).
 template <int PL>
@@ -142,8 +142,8 @@ __global__ __launch_bounds__(256) void k_route_topk(RouteArgs r) {
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
     for (int i = tid; i < E; i += blockDim.x) hist[i] = 0;
     __syncthreads();
-    const int t0 = blockIdx.x * ROUTE_TOKENS_PER_BLOCK;
-    const int t1 = min(t0 + ROUTE_TOKENS_PER_BLOCK, a.T);
+    const int t0 = blockIdx.x * r.tpb;
+    const int t1 = min(t0 + r.tpb, a.T);
     for (int t = t0 + wv; t < t1; t += 4) {
         const int e = route_token<PL>(a, t, lane);
         if (lane < K) {
@@ -209,12 +209,12 @@ __global__ __launch_bounds__(1024) void k_route_scan(RouteArgs r) {
 // Same blocks as k_route_topk: each pair goes to off_e[e] + the block's base
 // for e + its rank among the block's earlier pairs of expert e.
 __global__ __launch_bounds__(256) void k_route_scatter(RouteArgs r) {
-    __shared__ int es[ROUTE_TOKENS_PER_BLOCK * 16];
+    __shared__ int es[ROUTE_MAX_TPB * 16];
     const GroupArgs &a = r.g;
     const int E = a.E, K = a.K;
     const int tid = threadIdx.x;
-    const int t0 = blockIdx.x * ROUTE_TOKENS_PER_BLOCK;
-    const int t1 = min(t0 + ROUTE_TOKENS_PER_BLOCK, a.T);
+    const int t0 = blockIdx.x * r.tpb;
+    const int t1 = min(t0 + r.tpb, a.T);
     const int p0 = t0 * K, np = (t1 - t0) * K;
     for (int i = tid; i < np; i += blockDim.x) es[i] = r.e_of[p0 + i];
     __syncthreads();

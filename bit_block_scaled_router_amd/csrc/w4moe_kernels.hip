@@ -740,6 +740,9 @@ constexpr int MAX_TOKENS = 16384;
 #ifndef W4_GROUPED_MIN_T
 #define W4_GROUPED_MIN_T 4  // batches of at least this many tokens group their pairs by expert
 #endif
+#ifndef W4_MULTI_ROUTE_MIN_T
+#define W4_MULTI_ROUTE_MIN_T (1 << 30)  // smaller batches than this (and <= 4096 pairs) group in one block
+#endif
 #ifndef W4_ROUTER_MFMA_MIN_T
 #define W4_ROUTER_MFMA_MIN_T 64  // batches of at least this many tokens run the router on MFMA
 #endif
@@ -752,8 +755,10 @@ constexpr int MAX_ONE_BLOCK_PAIRS = 4096;  // up to this many, one block groups 
 struct MoEPlan {
     int H, I, E, K, S, T;
     int L13, L2, hstride, lstride;
-    bool grouped, mx, multi;  // multi: grouping over three launches (large batches)
-    int P, Gmax, nblk;
+    bool grouped, mx;
+    bool multi;  // grouping over three launches (large batches, or T >= W4_MULTI_ROUTE_MIN_T)
+    bool pf;     // W13 / W2 as large-batch grouped GEMMs (more than MAX_ONE_BLOCK_PAIRS pairs)
+    int P, Gmax, nblk, tpb;
     size_t off_logits, off_ids, off_w, off_h, total;
     size_t off_grp, off_pairs, off_hp, off_out, off_xq, off_route;
 };
@@ -822,8 +827,10 @@ int check_layer(const moe_w4a16_layer *Lr, int64_t T, MoEPlan &p) {
                         MAX_GROUPED_PAIRS);
         p.grouped = true;
     }
-    p.multi = p.grouped && p.P > MAX_ONE_BLOCK_PAIRS;
-    p.nblk = (int)((T + ROUTE_TOKENS_PER_BLOCK - 1) / ROUTE_TOKENS_PER_BLOCK);
+    p.pf = p.grouped && p.P > MAX_ONE_BLOCK_PAIRS;
+    p.multi = p.pf || (p.grouped && T >= W4_MULTI_ROUTE_MIN_T);
+    p.tpb = T <= 256 ? 4 : ROUTE_MAX_TPB;  // one token per wave while that keeps the scan short
+    p.nblk = (int)((T + p.tpb - 1) / p.tpb);
     size_t off = 0;
     p.off_logits = off; off = align_up(off + (size_t)T * p.lstride * 4, 256);
     p.off_ids = off;    off = align_up(off + (size_t)T * K * 4, 256);
@@ -1083,7 +1090,7 @@ int run_grouped(const moe_w4a16_layer *Lr, const MoEPlan &p, const uint16_t *x, 
         RouteArgs r{};
         r.g = ga;
         int32_t *rb = (int32_t *)(wsb + p.off_route);
-        r.e_of = rb, r.off_e = rb + p.P, r.cntb = rb + p.P + p.E, r.nblk = p.nblk;
+        r.e_of = rb, r.off_e = rb + p.P, r.cntb = rb + p.P + p.E, r.nblk = p.nblk, r.tpb = p.tpb;
         r.ctg = r.cntb + (size_t)p.nblk * p.E;
         hipEvent_t e6[6];
         for (int i = 0; i < 6; ++i) e6[i] = ev(next_ev + i);
@@ -1125,7 +1132,7 @@ int run_grouped(const moe_w4a16_layer *Lr, const MoEPlan &p, const uint16_t *x, 
         a.H = p.H, a.I = p.I, a.K = p.K, a.T = p.T, a.P = p.P, a.Gmax = p.Gmax;
         int32_t *ctg = p.multi ? (int32_t *)(wsb + p.off_route) + p.P + p.E + (size_t)p.nblk * p.E : nullptr;
         a.ctg = ctg;
-        if (p.multi) launch_pfmx13(a, sm, ev(next_ev), ev(next_ev + 1));
+        if (p.pf) launch_pfmx13(a, sm, ev(next_ev), ev(next_ev + 1));
         else launch_mx13(a, sm, ev(next_ev), ev(next_ev + 1));
         if ((st = hip_status("mx w13 launch"))) return st;
         MX2Args d{};
@@ -1135,7 +1142,7 @@ int run_grouped(const moe_w4a16_layer *Lr, const MoEPlan &p, const uint16_t *x, 
         d.grp = grp, d.pairs = pairs, d.hq = hq, d.hs = hs, d.out = outp;
         d.H = p.H, d.I = p.I, d.K = p.K, d.T = p.T, d.P = p.P, d.Gmax = p.Gmax;
         d.ctg = ctg;
-        if (p.multi) launch_pfmx2(d, sm, ev(next_ev + 2), ev(next_ev + 3));
+        if (p.pf) launch_pfmx2(d, sm, ev(next_ev + 2), ev(next_ev + 3));
         else launch_mx2(d, sm, ev(next_ev + 2), ev(next_ev + 3));
         if ((st = hip_status("mx w2 launch"))) return st;
         next_ev += 4;
@@ -1151,7 +1158,7 @@ int run_grouped(const moe_w4a16_layer *Lr, const MoEPlan &p, const uint16_t *x, 
     a.H = p.H, a.I = p.I, a.K = p.K, a.T = p.T, a.P = p.P, a.Gmax = p.Gmax, a.mfma_min = W4_MFMA_MIN;
     int32_t *ctg = p.multi ? (int32_t *)(wsb + p.off_route) + p.P + p.E + (size_t)p.nblk * p.E : nullptr;
     a.ctg = ctg;
-    if (p.multi) launch_pf13(a, sm, ev(next_ev), ev(next_ev + 1));
+    if (p.pf) launch_pf13(a, sm, ev(next_ev), ev(next_ev + 1));
     else launch_gw13(a, sm, ev(next_ev), ev(next_ev + 1));
     if ((st = hip_status("grouped w13 launch"))) return st;
     // 4) grouped W2
@@ -1162,7 +1169,7 @@ int run_grouped(const moe_w4a16_layer *Lr, const MoEPlan &p, const uint16_t *x, 
     d.grp = grp, d.pairs = pairs, d.h_hi = h_hi, d.h_lo = h_lo, d.out = outp;
     d.H = p.H, d.I = p.I, d.K = p.K, d.T = p.T, d.P = p.P, d.Gmax = p.Gmax, d.mfma_min = W4_MFMA_MIN;
     d.ctg = ctg;
-    if (p.multi) launch_pf2(d, sm, ev(next_ev + 2), ev(next_ev + 3));
+    if (p.pf) launch_pf2(d, sm, ev(next_ev + 2), ev(next_ev + 3));
     else launch_gw2(d, sm, ev(next_ev + 2), ev(next_ev + 3));
     next_ev += 4;
     if ((st = hip_status("grouped w2 launch"))) return st;
