@@ -251,15 +251,35 @@ def stage_bytes(shape, distinct, n_stages=3):
 ROUTER_MFMA_MIN_T = 64  # the library runs the router as an MFMA GEMM from this batch size
 
 
-def stage_names(n_stages, T, mx):
+LARGE_BATCH_PAIRS = 4096  # past this many (token, slot) pairs the grouped GEMM kernels run
+
+
+def stage_names(n_stages, T, K, mx):
     """Kernel names in launch order for the library's stage count at T tokens."""
     router = "k_router_mfma" if T >= ROUTER_MFMA_MIN_T else "k_router"
     if n_stages == 3:
         return [router, "k_moe_w13", "k_moe_down"]
     grouping = ["k_moe_route_group"] if n_stages in (5, 6) else ["k_route_topk", "k_route_scan", "k_route_scatter"]
     experts = ["k_mx_quant"] if mx else []
-    proj = ["k_moe_mx13", "k_moe_mx2"] if mx else ["k_moe_gw13", "k_moe_gw2"]
+    large = T * K > LARGE_BATCH_PAIRS
+    if mx:
+        proj = ["k_moe_pfmx13", "k_moe_pfmx2"] if large else ["k_moe_mx13", "k_moe_mx2"]
+    else:
+        proj = ["k_moe_pf13", "k_moe_pf2"] if large else ["k_moe_gw13", "k_moe_gw2"]
     return [router] + experts + grouping + proj + ["k_moe_gcombine"]
+
+
+def launch_bytes(shape, distinct, n_stages):
+    """stage_bytes keyed by the kernel names stage_names gives for the same call."""
+    sb = stage_bytes(shape, distinct, n_stages)
+    if shape.tokens >= ROUTER_MFMA_MIN_T:
+        sb["k_router_mfma"] = sb.pop("k_router")
+    if shape.tokens * shape.top_k > LARGE_BATCH_PAIRS:  # the grouped GEMM kernels move the same algorithmic bytes
+        for a, b in (("k_moe_gw13", "k_moe_pf13"), ("k_moe_gw2", "k_moe_pf2"), ("k_moe_mx13", "k_moe_pfmx13"),
+                     ("k_moe_mx2", "k_moe_pfmx2")):
+            if a in sb:
+                sb[b] = sb.pop(a)
+    return sb
 
 
 def stage_flops(shape):
@@ -268,7 +288,8 @@ def stage_flops(shape):
     rows = shape.tokens * shape.top_k + (shape.tokens if shape.has_shared else 0)
     w13 = 2 * rows * 2 * shape.inter * shape.hidden
     w2 = 2 * rows * shape.hidden * shape.inter
-    return {"k_moe_gw13": w13, "k_moe_gw2": w2, "k_moe_mx13": w13, "k_moe_mx2": w2}
+    return {"k_moe_gw13": w13, "k_moe_gw2": w2, "k_moe_mx13": w13, "k_moe_mx2": w2, "k_moe_pf13": w13,
+            "k_moe_pf2": w2, "k_moe_pfmx13": w13, "k_moe_pfmx2": w2}
 
 
 # ----------------------------------------------------------------------------- CPU baseline
@@ -409,7 +430,7 @@ def run_moe(args, torch, w4, wl, synth):
     # per-kernel durations: the same K steps launched eagerly through the
     # measurement entry point, whose kernels carry start/stop HIP events
     n_stages = w4.moe_w4a16_stage_count(base, T)
-    names = stage_names(n_stages, T, shape.fmt == "mxfp4")
+    names = stage_names(n_stages, T, shape.top_k, shape.fmt == "mxfp4")
     hip = HipEvents()
     ne = 2 * n_stages
     evs = hip.create(ne * n_steps)
@@ -436,9 +457,7 @@ def run_moe(args, torch, w4, wl, synth):
     ms_step = ms_total / n_steps
     us_token = ms_step * 1e3 / T
     step_bytes = moe_bytes(shape, d_mean)
-    sb = stage_bytes(shape, d_mean, n_stages)
-    if T >= ROUTER_MFMA_MIN_T:
-        sb["k_router_mfma"] = sb.pop("k_router")
+    sb = launch_bytes(shape, d_mean, n_stages)
     dom = max(stage_us, key=stage_us.get)
     achieved = sb[dom] / (stage_us[dom] * 1e-6) / 1e9
     traffic = load_traffic(dom, shape.name)

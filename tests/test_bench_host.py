@@ -1,0 +1,56 @@
+"""Host-side checks of bench.py's bookkeeping (no GPU): for every MoE workload
+the stage names match the library's stage count and every named kernel has an
+algorithmic byte count; the flop counts cover the projections; a multi-GPU
+request exits with a message."""
+
+import subprocess
+import sys
+import ctypes as C
+
+import pytest
+
+import bench
+import bit_block_scaled_router_amd as w4
+from bit_block_scaled_router_amd import synth
+from conftest import ROOT
+
+
+def _desc(shape):
+    """A layer descriptor with fake device pointers (planning only, nothing launched)."""
+    fmt = w4.FORMATS[shape.fmt]
+    H, I, E = shape.hidden, shape.inter, shape.num_experts
+    sfmt = w4.FORMATS[shape.shared_fmt] if shape.shared_fmt else fmt
+    g = w4.GROUP.get(fmt, 1)
+
+    def mat(f, groups, n, k):
+        return w4.W4Matrix(f, 0, groups, n, k, 1 << 20, None if f == w4.W4_FMT_BF16 else 1 << 21,
+                           (1 << 22) if f == w4.W4_FMT_NVFP4_E4M3S16 else None)
+
+    return w4.MoELayerDesc(H, I, E, shape.top_k, shape.shared_inter or I, 1 << 16, None,
+                           mat(fmt, E, 2 * I, H), mat(fmt, E, H, I), 1 if shape.has_shared else 0,
+                           mat(sfmt, 1, 2 * I, H), mat(sfmt, 1, H, I), 1 << 17)
+
+
+MOE = [w for w in bench.WORKLOADS if not w.startswith("gemv")]
+
+
+@pytest.mark.parametrize("name", MOE)
+def test_stage_names_and_bytes(name):
+    shape = bench.workload_shapes(synth)[name]
+    T = shape.tokens
+    n = w4.lib().moe_w4a16_stage_count(C.byref(_desc(shape)), T)
+    assert n in (3, 5, 6, 7, 8), n
+    names = bench.stage_names(n, T, shape.top_k, shape.fmt == "mxfp4")
+    assert len(names) == n
+    sb = bench.launch_bytes(shape, 8.0, n)
+    assert set(sb) == set(names), (sorted(sb), names)
+    assert all(v > 0 for v in sb.values())
+    fl = bench.stage_flops(shape)
+    proj = [k for k in names if k in fl]
+    assert len(proj) == (0 if n == 3 else 2)
+
+
+def test_multi_gpu_request_exits_with_message():
+    r = subprocess.run([sys.executable, "bench.py", "--gpus", "2"], cwd=ROOT, capture_output=True, text=True,
+                       timeout=120)
+    assert r.returncode == 2 and "one GPU" in r.stderr
