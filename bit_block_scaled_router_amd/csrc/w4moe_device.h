@@ -475,6 +475,19 @@ __device__ __forceinline__ void e2m1x8_split(uint32_t c, float s_hi, float s_lo,
     lo = __builtin_bit_cast(bf16x8, make_uint4(l[0], l[1], l[2], l[3]));
 }
 
+// 8 E2M1 codes of one dword (elements 0..7) times a scale whose product with
+// every code is exact in bf16 (an NVFP4 UE4M3 block scale: at most 4
+// significant bits, a code at most 2) -> bf16x8.
+__device__ __forceinline__ bf16x8 e2m1x8_scaled(uint32_t c, float s) {
+    uint32_t h[4];
+    f32x2 v;
+    v = e2m1x2_f32<0>(c); h[0] = pack_bf16_exact(v.x * s, v.y * s);
+    v = e2m1x2_f32<1>(c); h[1] = pack_bf16_exact(v.x * s, v.y * s);
+    v = e2m1x2_f32<2>(c); h[2] = pack_bf16_exact(v.x * s, v.y * s);
+    v = e2m1x2_f32<3>(c); h[3] = pack_bf16_exact(v.x * s, v.y * s);
+    return __builtin_bit_cast(bf16x8, make_uint4(h[0], h[1], h[2], h[3]));
+}
+
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 // Scaled FP4 x FP8 MFMA (gfx950 v_mfma_scale_f32_16x16x128_f8f6f4): D += A B with

@@ -58,6 +58,8 @@ struct GW13Args {
     uint16_t *h_lo;
     int H, I, K, T, P, Gmax, tiles, mfma_min;
     const int32_t *ctg;     // column tiles (large-batch kernels only)
+    int fmt;                // FMT_E2M1 or FMT_NVFP4 (gw13 / gw2)
+    const float *gs, *s_gs; // NVFP4 global scales: routed [E], shared [1]
 };
 
 struct GW2Args {
@@ -72,6 +74,8 @@ struct GW2Args {
     float *out;             // [P + T][H]
     int H, I, K, T, P, Gmax, tiles, mfma_min;
     const int32_t *ctg;     // column tiles (large-batch kernels only)
+    int fmt;                // FMT_E2M1 or FMT_NVFP4
+    const float *gs, *s_gs; // NVFP4 global scales: routed [E], shared [1]
 };
 
 struct GCombineArgs {

@@ -31,6 +31,7 @@
 #include "w4moe_grouped.h"
 
 #include <hip/hip_ext.h>
+#include <type_traits>
 #include <hip/hip_runtime.h>
 
 namespace w4k {
@@ -236,6 +237,7 @@ struct GroupView {
     const uint8_t *codes;
     const S *scales;
     int off, m;  // first entry in the pair list, number of pairs
+    int e;       // expert id (-1: the shared expert)
 };
 
 template <typename S>
@@ -245,12 +247,13 @@ __device__ __forceinline__ GroupView<S> group_view(const int32_t *grp, int gs, i
     GroupView<S> v{};
     if (s_codes != nullptr) {
         if (gs == 0) {
-            v.codes = s_codes, v.scales = s_scales, v.off = P, v.m = T;
+            v.codes = s_codes, v.scales = s_scales, v.off = P, v.m = T, v.e = -1;
             return v;
         }
         --gs;
     }
     const int e = ld_uniform(grp, 1 + gs);
+    v.e = e;
     v.off = ld_uniform(grp, 1 + Gmax + gs);
     v.m = ld_uniform(grp, 1 + 2 * Gmax + gs);
     v.codes = codes + (size_t)e * mat_codes;
@@ -268,19 +271,25 @@ __device__ __forceinline__ int token_of(int p, int P, int K) { return p < P ? p 
 // ================================================================= grouped W13 + SiLU
 
 // One work unit of the W13 launch: group slot gs, gate rows 16*tile .. +16 (and
-// the matching up rows).
-template <int L>
+// the matching up rows).  FMT: E2M1 (FP16 scale per 16: every weight is two
+// exact bf16 terms) or NVFP4 (UE4M3 scale per 16: code x scale has at most 6
+// significant bits, one exact bf16 term; the matrix's global scale multiplies
+// the gate and up sums).
+template <int FMT, int L>
 __device__ __forceinline__ void gw13_unit(const GW13Args &a, int gs, int tile, float (*red)[16][64]) {
+    using SC = typename std::conditional<FMT == FMT_NVFP4, uint8_t, uint16_t>::type;
     constexpr int RG = 64 / L;
     const int lane = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int H = a.H, I = a.I;
     const uint32_t spr = (uint32_t)(H >> 4);
     const size_t mat_codes = (size_t)(2 * I) * (H >> 1), mat_scales = (size_t)(2 * I) * spr;
-    const GroupView<uint16_t> gv = group_view(a.grp, gs, a.Gmax, a.P, a.T, a.codes, a.scales, mat_codes, mat_scales, a.s_codes,
-                                    a.s_scales);
+    const GroupView<SC> gv = group_view(a.grp, gs, a.Gmax, a.P, a.T, a.codes, reinterpret_cast<const SC *>(a.scales),
+                                        mat_codes, mat_scales, a.s_codes, reinterpret_cast<const SC *>(a.s_scales));
     const Buf cb = make_buf(gv.codes, (uint32_t)mat_codes);
-    const Buf sb = make_buf(gv.scales, (uint32_t)(mat_scales * 2));
+    const Buf sb = make_buf(gv.scales, (uint32_t)(mat_scales * sizeof(SC)));
+    float gsc = 1.f;  // NVFP4 global scale of the matrix
+    if constexpr (FMT == FMT_NVFP4) gsc = gv.e < 0 ? ld_uniform(a.s_gs, 0) : ld_uniform(a.gs, gv.e);
     const int i0 = tile * 16;  // first gate row of the tile
     const int *plist = a.pairs + gv.off;
 
@@ -319,25 +328,38 @@ __device__ __forceinline__ void gw13_unit(const GW13Args &a, int gs, int tile, f
                 }
                 const uint4 cg = ld128(cb, rg_ok ? rowg * (uint32_t)(H >> 1) + (uint32_t)(k0 >> 1) : OOB);
                 const uint4 cu = ld128(cb, rg_ok ? rowu * (uint32_t)(H >> 1) + (uint32_t)(k0 >> 1) : OOB);
-                const uint32_t sg = ld32(sb, rg_ok ? (rowg * spr + (uint32_t)(k0 >> 4)) * 2u : OOB);
-                const uint32_t su = ld32(sb, rg_ok ? (rowu * spr + (uint32_t)(k0 >> 4)) * 2u : OOB);
+                const uint32_t sg = ld_scales<FMT>(sb, rg_ok ? scale_off<FMT>(rowg * spr, k0) : OOB);
+                const uint32_t su = ld_scales<FMT>(sb, rg_ok ? scale_off<FMT>(rowu * spr, k0) : OOB);
                 const uint32_t cgw[4] = {cg.x, cg.y, cg.z, cg.w}, cuw[4] = {cu.x, cu.y, cu.z, cu.w};
 #pragma unroll
                 for (int s = 0; s < 4; ++s) {
-                    float gh, gl, uh, ul;
-                    split_scale(f16_bits_to_f32(s < 2 ? sg : (sg >> 16)), gh, gl);
-                    split_scale(f16_bits_to_f32(s < 2 ? su : (su >> 16)), uh, ul);
-                    bf16x8 agh, agl, auh, aul;
-                    e2m1x8_split(cgw[s], gh, gl, agh, agl);
-                    e2m1x8_split(cuw[s], uh, ul, auh, aul);
+                    if constexpr (FMT == FMT_NVFP4) {
+                        const f32x2 sgv = block_scales2<FMT>(sg), suv = block_scales2<FMT>(su);
+                        const bf16x8 ag1 = e2m1x8_scaled(cgw[s], s < 2 ? sgv.x : sgv.y);
+                        const bf16x8 au1 = e2m1x8_scaled(cuw[s], s < 2 ? suv.x : suv.y);
 #pragma unroll
-                    for (int nt = 0; nt < 2; ++nt) {
-                        if (nt == 1 && !two) break;
-                        const bf16x8 b = __builtin_bit_cast(bf16x8, xb[nt][s]);
-                        ag[nt] = mfma16x16x32(agh, b, ag[nt]);
-                        ag[nt] = mfma16x16x32(agl, b, ag[nt]);
-                        au[nt] = mfma16x16x32(auh, b, au[nt]);
-                        au[nt] = mfma16x16x32(aul, b, au[nt]);
+                        for (int nt = 0; nt < 2; ++nt) {
+                            if (nt == 1 && !two) break;
+                            const bf16x8 b = __builtin_bit_cast(bf16x8, xb[nt][s]);
+                            ag[nt] = mfma16x16x32(ag1, b, ag[nt]);
+                            au[nt] = mfma16x16x32(au1, b, au[nt]);
+                        }
+                    } else {
+                        float gh, gl, uh, ul;
+                        split_scale(f16_bits_to_f32(s < 2 ? sg : (sg >> 16)), gh, gl);
+                        split_scale(f16_bits_to_f32(s < 2 ? su : (su >> 16)), uh, ul);
+                        bf16x8 agh, agl, auh, aul;
+                        e2m1x8_split(cgw[s], gh, gl, agh, agl);
+                        e2m1x8_split(cuw[s], uh, ul, auh, aul);
+#pragma unroll
+                        for (int nt = 0; nt < 2; ++nt) {
+                            if (nt == 1 && !two) break;
+                            const bf16x8 b = __builtin_bit_cast(bf16x8, xb[nt][s]);
+                            ag[nt] = mfma16x16x32(agh, b, ag[nt]);
+                            ag[nt] = mfma16x16x32(agl, b, ag[nt]);
+                            au[nt] = mfma16x16x32(auh, b, au[nt]);
+                            au[nt] = mfma16x16x32(aul, b, au[nt]);
+                        }
                     }
                 }
             }
@@ -371,7 +393,8 @@ __device__ __forceinline__ void gw13_unit(const GW13Args &a, int gs, int tile, f
                         float hv[4];
 #pragma unroll
                         for (int j = 0; j < 4; ++j) {
-                            const float gg = ag[nt][j], uu = au[nt][j];
+                            float gg = ag[nt][j], uu = au[nt][j];
+                            if constexpr (FMT == FMT_NVFP4) gg *= gsc, uu *= gsc;
                             hv[j] = (gg / (1.f + expf(-gg))) * uu;
                         }
                         // I is a multiple of 128 (host check): rows i0 + 4q .. +3 all exist
@@ -408,8 +431,8 @@ __device__ __forceinline__ void gw13_unit(const GW13Args &a, int gs, int tile, f
             const uint32_t rg = (uint32_t)i, ru = (uint32_t)(I + i);
             cg[s][l] = ld128(cb, v ? rg * (uint32_t)(H >> 1) + (uint32_t)(k0 >> 1) : OOB);
             cu[s][l] = ld128(cb, v ? ru * (uint32_t)(H >> 1) + (uint32_t)(k0 >> 1) : OOB);
-            sg[s][l] = ld32(sb, v ? (rg * spr + (uint32_t)(k0 >> 4)) * 2u : OOB);
-            su[s][l] = ld32(sb, v ? (ru * spr + (uint32_t)(k0 >> 4)) * 2u : OOB);
+            sg[s][l] = ld_scales<FMT>(sb, v ? scale_off<FMT>(rg * spr, k0) : OOB);
+            su[s][l] = ld_scales<FMT>(sb, v ? scale_off<FMT>(ru * spr, k0) : OOB);
         }
     for (int idx = 0; idx < gv.m; ++idx) {
         const int p = ld_uniform(plist, idx);
@@ -422,18 +445,18 @@ __device__ __forceinline__ void gw13_unit(const GW13Args &a, int gs, int tile, f
         for (int s = 0; s < KS_VALU; ++s) {
             if (s >= ks) break;
             const int k0 = 32 * (L * s + lk);
-            XSlice<FMT_E2M1> xs;
-            load_xslice<FMT_E2M1>(xs, xb, k0 < H ? (uint32_t)k0 * 2u : OOB);
+            XSlice<FMT> xs;
+            load_xslice<FMT>(xs, xb, k0 < H ? (uint32_t)k0 * 2u : OOB);
 #pragma unroll
             for (int l = 0; l < NLG; ++l) {
-                accg[l] = chunk_dot_bf16<FMT_E2M1>(cg[s][l], sg[s][l], xs, accg[l]);
-                accu[l] = chunk_dot_bf16<FMT_E2M1>(cu[s][l], su[s][l], xs, accu[l]);
+                accg[l] = chunk_dot_bf16<FMT>(cg[s][l], sg[s][l], xs, accg[l]);
+                accu[l] = chunk_dot_bf16<FMT>(cu[s][l], su[s][l], xs, accu[l]);
             }
         }
 #pragma unroll
         for (int l = 0; l < NLG; ++l) {
-            const float gg = group_sum<L>(accg[l]);
-            const float uu = group_sum<L>(accu[l]);
+            const float gg = group_sum<L>(accg[l]) * gsc;
+            const float uu = group_sum<L>(accu[l]) * gsc;
             const int i = i0 + 4 * wv + l * RG + rsub;
             if (group_leader<L>(lane) && i < I && (l * RG + rsub) < 4) {
                 uint16_t bh, bl;
@@ -447,31 +470,35 @@ __device__ __forceinline__ void gw13_unit(const GW13Args &a, int gs, int tile, f
 
 // Blocks walk the work units (group slot x row tile) with a grid stride, so the
 // grid needs no bound on the number of active experts.
-template <int L>
+template <int FMT, int L>
 __global__ __launch_bounds__(256) void k_moe_gw13(GW13Args a) {
     __shared__ float red[3][16][64];  // MFMA K-split partials of waves 1..3
     const int nu = unit_count(a.grp, a.s_codes != nullptr, a.tiles);
     for (int u = blockIdx.x; u < nu; u += gridDim.x) {
         const int gs = u / a.tiles;
-        gw13_unit<L>(a, gs, u - gs * a.tiles, red);
+        gw13_unit<FMT, L>(a, gs, u - gs * a.tiles, red);
     }
 }
 
 // ================================================================= grouped W2
 
 // One work unit of the down launch: group slot gs, output rows 64*tile .. +64.
-template <int L>
+// FMT as in gw13_unit (NVFP4: one bf16 weight term, sums times the global scale).
+template <int FMT, int L>
 __device__ __forceinline__ void gw2_unit(const GW2Args &a, int gs, int tile, float (*red)[4][8][64]) {
+    using SC = typename std::conditional<FMT == FMT_NVFP4, uint8_t, uint16_t>::type;
     constexpr int RG = 64 / L;
     const int lane = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int H = a.H, I = a.I;
     const uint32_t spr = (uint32_t)(I >> 4);
     const size_t mat_codes = (size_t)H * (I >> 1), mat_scales = (size_t)H * spr;
-    const GroupView<uint16_t> gv = group_view(a.grp, gs, a.Gmax, a.P, a.T, a.codes, a.scales, mat_codes, mat_scales, a.s_codes,
-                                    a.s_scales);
+    const GroupView<SC> gv = group_view(a.grp, gs, a.Gmax, a.P, a.T, a.codes, reinterpret_cast<const SC *>(a.scales),
+                                        mat_codes, mat_scales, a.s_codes, reinterpret_cast<const SC *>(a.s_scales));
     const Buf cb = make_buf(gv.codes, (uint32_t)mat_codes);
-    const Buf sb = make_buf(gv.scales, (uint32_t)(mat_scales * 2));
+    const Buf sb = make_buf(gv.scales, (uint32_t)(mat_scales * sizeof(SC)));
+    float gsc = 1.f;  // NVFP4 global scale of the matrix
+    if constexpr (FMT == FMT_NVFP4) gsc = gv.e < 0 ? ld_uniform(a.s_gs, 0) : ld_uniform(a.gs, gv.e);
     const int *plist = a.pairs + gv.off;
     const uint32_t hbytes = (uint32_t)(a.P + a.T) * (uint32_t)I * 2u;
     const Buf hhi = make_buf(a.h_hi, hbytes), hlo = make_buf(a.h_lo, hbytes);
@@ -506,7 +533,7 @@ __device__ __forceinline__ void gw2_unit(const GW2Args &a, int gs, int tile, flo
                     const int rr = u0 + 16 * rt + r;
                     const bool rv = rr < H;
                     cw[rt] = ld128(cb, rv ? (uint32_t)rr * (uint32_t)(I >> 1) + (uint32_t)(k0 >> 1) : OOB);
-                    sc[rt] = ld32(sb, rv ? ((uint32_t)rr * spr + (uint32_t)(k0 >> 4)) * 2u : OOB);
+                    sc[rt] = ld_scales<FMT>(sb, rv ? scale_off<FMT>((uint32_t)rr * spr, k0) : OOB);
                 }
                 uint4 bh[2][4], bl[2][4];
 #pragma unroll
@@ -524,22 +551,33 @@ __device__ __forceinline__ void gw2_unit(const GW2Args &a, int gs, int tile, flo
                     const uint32_t cws[4] = {cw[rt].x, cw[rt].y, cw[rt].z, cw[rt].w};
 #pragma unroll
                     for (int s = 0; s < 4; ++s) {
-                        float sh, sl;
-                        split_scale(f16_bits_to_f32(s < 2 ? sc[rt] : (sc[rt] >> 16)), sh, sl);
-                        bf16x8 ah, al;
-                        e2m1x8_split(cws[s], sh, sl, ah, al);
+                        if constexpr (FMT == FMT_NVFP4) {
+                            const f32x2 sv = block_scales2<FMT>(sc[rt]);
+                            const bf16x8 a1 = e2m1x8_scaled(cws[s], s < 2 ? sv.x : sv.y);
 #pragma unroll
-                        for (int nt = 0; nt < 2; ++nt) {
-                            if (nt == 1 && !two) break;
-                            const bf16x8 b0 = __builtin_bit_cast(bf16x8, bh[nt][s]);
-                            const bf16x8 b1 = __builtin_bit_cast(bf16x8, bl[nt][s]);
-                            // all four terms: al can reach 2^-5 of the weight and
-                            // h_lo 2^-8 of h, so al * h_lo is not negligible after
-                            // cancellation in the sum over K
-                            acc[rt][nt] = mfma16x16x32(ah, b0, acc[rt][nt]);
-                            acc[rt][nt] = mfma16x16x32(ah, b1, acc[rt][nt]);
-                            acc[rt][nt] = mfma16x16x32(al, b0, acc[rt][nt]);
-                            acc[rt][nt] = mfma16x16x32(al, b1, acc[rt][nt]);
+                            for (int nt = 0; nt < 2; ++nt) {
+                                if (nt == 1 && !two) break;
+                                acc[rt][nt] = mfma16x16x32(a1, __builtin_bit_cast(bf16x8, bh[nt][s]), acc[rt][nt]);
+                                acc[rt][nt] = mfma16x16x32(a1, __builtin_bit_cast(bf16x8, bl[nt][s]), acc[rt][nt]);
+                            }
+                        } else {
+                            float sh, sl;
+                            split_scale(f16_bits_to_f32(s < 2 ? sc[rt] : (sc[rt] >> 16)), sh, sl);
+                            bf16x8 ah, al;
+                            e2m1x8_split(cws[s], sh, sl, ah, al);
+#pragma unroll
+                            for (int nt = 0; nt < 2; ++nt) {
+                                if (nt == 1 && !two) break;
+                                const bf16x8 b0 = __builtin_bit_cast(bf16x8, bh[nt][s]);
+                                const bf16x8 b1 = __builtin_bit_cast(bf16x8, bl[nt][s]);
+                                // all four terms: al can reach 2^-5 of the weight and
+                                // h_lo 2^-8 of h, so al * h_lo is not negligible after
+                                // cancellation in the sum over K
+                                acc[rt][nt] = mfma16x16x32(ah, b0, acc[rt][nt]);
+                                acc[rt][nt] = mfma16x16x32(ah, b1, acc[rt][nt]);
+                                acc[rt][nt] = mfma16x16x32(al, b0, acc[rt][nt]);
+                                acc[rt][nt] = mfma16x16x32(al, b1, acc[rt][nt]);
+                            }
                         }
                     }
                 }
@@ -560,7 +598,7 @@ __device__ __forceinline__ void gw2_unit(const GW2Args &a, int gs, int tile, flo
                     float t = red[0][wv][nt * 4 + j][lane];
 #pragma unroll
                     for (int w = 1; w < 4; ++w) t += red[w][wv][nt * 4 + j][lane];
-                    v[nt][j] = t;
+                    v[nt][j] = t * gsc;
                 }
             __syncthreads();  // red is reused by the next pass or unit
             // lane holds rows u0 + 16wv + 4q + j of column r
@@ -597,7 +635,7 @@ __device__ __forceinline__ void gw2_unit(const GW2Args &a, int gs, int tile, flo
             const int rr = row0 + l * RG + rsub;
             const bool v = s < ks && k0 < I && rr < H && (l * RG + rsub) < 16;
             cw[s][l] = ld128(cb, v ? (uint32_t)rr * (uint32_t)(I >> 1) + (uint32_t)(k0 >> 1) : OOB);
-            sc[s][l] = ld32(sb, v ? ((uint32_t)rr * spr + (uint32_t)(k0 >> 4)) * 2u : OOB);
+            sc[s][l] = ld_scales<FMT>(sb, v ? scale_off<FMT>((uint32_t)rr * spr, k0) : OOB);
         }
     for (int idx = 0; idx < gv.m; ++idx) {
         const int p = ld_uniform(plist, idx);
@@ -609,31 +647,31 @@ __device__ __forceinline__ void gw2_unit(const GW2Args &a, int gs, int tile, flo
             if (s >= ks) break;
             const int k0 = 32 * (L * s + lk);
             const uint32_t ho = (uint32_t)(p * I + k0) * 2u;
-            XSlice<FMT_E2M1> xh, xl;
-            load_xslice<FMT_E2M1>(xh, hhi, k0 < I ? ho : OOB);
-            load_xslice<FMT_E2M1>(xl, hlo, k0 < I ? ho : OOB);
+            XSlice<FMT> xh, xl;
+            load_xslice<FMT>(xh, hhi, k0 < I ? ho : OOB);
+            load_xslice<FMT>(xl, hlo, k0 < I ? ho : OOB);
 #pragma unroll
             for (int l = 0; l < NLG; ++l) {
-                acc[l] = chunk_dot_bf16<FMT_E2M1>(cw[s][l], sc[s][l], xh, acc[l]);
-                acc[l] = chunk_dot_bf16<FMT_E2M1>(cw[s][l], sc[s][l], xl, acc[l]);
+                acc[l] = chunk_dot_bf16<FMT>(cw[s][l], sc[s][l], xh, acc[l]);
+                acc[l] = chunk_dot_bf16<FMT>(cw[s][l], sc[s][l], xl, acc[l]);
             }
         }
 #pragma unroll
         for (int l = 0; l < NLG; ++l) {
-            const float v = group_sum<L>(acc[l]);
+            const float v = group_sum<L>(acc[l]) * gsc;
             const int rr = row0 + l * RG + rsub;
             if (group_leader<L>(lane) && rr < H && (l * RG + rsub) < 16) a.out[(size_t)p * H + rr] = v;
         }
     }
 }
 
-template <int L>
+template <int FMT, int L>
 __global__ __launch_bounds__(256) void k_moe_gw2(GW2Args a) {
     __shared__ float red[4][4][8][64];  // MFMA partials: [wave][row tile][column tile x 4 + j][lane]
     const int nu = unit_count(a.grp, a.s_codes != nullptr, a.tiles);
     for (int u = blockIdx.x; u < nu; u += gridDim.x) {
         const int gs = u / a.tiles;
-        gw2_unit<L>(a, gs, u - gs * a.tiles, red);
+        gw2_unit<FMT, L>(a, gs, u - gs * a.tiles, red);
     }
 }
 
@@ -1514,29 +1552,39 @@ unsigned grouped_grid(int Gmax, int tiles) {
 void launch_gw13(GW13Args &a, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
     a.tiles = (a.I + 15) / 16;
     const dim3 g(grouped_grid(a.Gmax, a.tiles)), b(256);
-    switch (lanes_for_k(a.H)) {
-    case 1: go_ev(st, e0, e1, k_moe_gw13<1>, g, b, 0, a); break;
-    case 2: go_ev(st, e0, e1, k_moe_gw13<2>, g, b, 0, a); break;
-    case 4: go_ev(st, e0, e1, k_moe_gw13<4>, g, b, 0, a); break;
-    case 8: go_ev(st, e0, e1, k_moe_gw13<8>, g, b, 0, a); break;
-    case 16: go_ev(st, e0, e1, k_moe_gw13<16>, g, b, 0, a); break;
-    case 32: go_ev(st, e0, e1, k_moe_gw13<32>, g, b, 0, a); break;
-    default: go_ev(st, e0, e1, k_moe_gw13<64>, g, b, 0, a); break;
-    }
+    auto with_fmt = [&](auto F) {
+        constexpr int FMT = decltype(F)::value;
+        switch (lanes_for_k(a.H)) {
+        case 1: go_ev(st, e0, e1, k_moe_gw13<FMT, 1>, g, b, 0, a); break;
+        case 2: go_ev(st, e0, e1, k_moe_gw13<FMT, 2>, g, b, 0, a); break;
+        case 4: go_ev(st, e0, e1, k_moe_gw13<FMT, 4>, g, b, 0, a); break;
+        case 8: go_ev(st, e0, e1, k_moe_gw13<FMT, 8>, g, b, 0, a); break;
+        case 16: go_ev(st, e0, e1, k_moe_gw13<FMT, 16>, g, b, 0, a); break;
+        case 32: go_ev(st, e0, e1, k_moe_gw13<FMT, 32>, g, b, 0, a); break;
+        default: go_ev(st, e0, e1, k_moe_gw13<FMT, 64>, g, b, 0, a); break;
+        }
+    };
+    if (a.fmt == FMT_NVFP4) with_fmt(std::integral_constant<int, FMT_NVFP4>());
+    else with_fmt(std::integral_constant<int, FMT_E2M1>());
 }
 
 void launch_gw2(GW2Args &a, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
     a.tiles = (a.H + 63) / 64;
     const dim3 g(grouped_grid(a.Gmax, a.tiles)), b(256);
-    switch (lanes_for_k(a.I)) {
-    case 1: go_ev(st, e0, e1, k_moe_gw2<1>, g, b, 0, a); break;
-    case 2: go_ev(st, e0, e1, k_moe_gw2<2>, g, b, 0, a); break;
-    case 4: go_ev(st, e0, e1, k_moe_gw2<4>, g, b, 0, a); break;
-    case 8: go_ev(st, e0, e1, k_moe_gw2<8>, g, b, 0, a); break;
-    case 16: go_ev(st, e0, e1, k_moe_gw2<16>, g, b, 0, a); break;
-    case 32: go_ev(st, e0, e1, k_moe_gw2<32>, g, b, 0, a); break;
-    default: go_ev(st, e0, e1, k_moe_gw2<64>, g, b, 0, a); break;
-    }
+    auto with_fmt = [&](auto F) {
+        constexpr int FMT = decltype(F)::value;
+        switch (lanes_for_k(a.I)) {
+        case 1: go_ev(st, e0, e1, k_moe_gw2<FMT, 1>, g, b, 0, a); break;
+        case 2: go_ev(st, e0, e1, k_moe_gw2<FMT, 2>, g, b, 0, a); break;
+        case 4: go_ev(st, e0, e1, k_moe_gw2<FMT, 4>, g, b, 0, a); break;
+        case 8: go_ev(st, e0, e1, k_moe_gw2<FMT, 8>, g, b, 0, a); break;
+        case 16: go_ev(st, e0, e1, k_moe_gw2<FMT, 16>, g, b, 0, a); break;
+        case 32: go_ev(st, e0, e1, k_moe_gw2<FMT, 32>, g, b, 0, a); break;
+        default: go_ev(st, e0, e1, k_moe_gw2<FMT, 64>, g, b, 0, a); break;
+        }
+    };
+    if (a.fmt == FMT_NVFP4) with_fmt(std::integral_constant<int, FMT_NVFP4>());
+    else with_fmt(std::integral_constant<int, FMT_E2M1>());
 }
 
 // blocks of the large-batch launches (grid-stride over the units)

@@ -816,8 +816,11 @@ int check_layer(const moe_w4a16_layer *Lr, int64_t T, MoEPlan &p) {
     p.Gmax = (int)(E < p.P ? E : p.P);
     // (the VALU small-group path keeps at most 2 k-steps of 32 x 64 elements)
     p.mx = fmt == W4_FMT_MXFP4_E8M0S32;
-    p.grouped = T >= W4_GROUPED_MIN_T && fmt == W4_FMT_E2M1_F16S16 && H % 128 == 0 && I % 128 == 0 &&
-                p.P <= MAX_GROUPED_PAIRS && H <= 4096 && I <= 4096 &&
+    // (NVFP4 batches group up to MAX_ONE_BLOCK_PAIRS pairs; the large-batch GEMM
+    // kernels are E2M1 and MX only)
+    p.grouped = T >= W4_GROUPED_MIN_T && H % 128 == 0 && I % 128 == 0 && H <= 4096 && I <= 4096 &&
+                (fmt == W4_FMT_E2M1_F16S16 ? p.P <= MAX_GROUPED_PAIRS
+                                           : fmt == W4_FMT_NVFP4_E4M3S16 && p.P <= MAX_ONE_BLOCK_PAIRS) &&
                 !(Lr->has_shared && Lr->shared_w13.format == W4_FMT_BF16);
     if (p.mx) {  // every batch size runs grouped, all on the scaled FP4 MFMA
         if (H % 128 || I % 128)
@@ -1156,6 +1159,8 @@ int run_grouped(const moe_w4a16_layer *Lr, const MoEPlan &p, const uint16_t *x, 
     a.s_scales = Lr->has_shared ? (const uint16_t *)Lr->shared_w13.scales : nullptr;
     a.x = x, a.grp = grp, a.pairs = pairs, a.h_hi = h_hi, a.h_lo = h_lo;
     a.H = p.H, a.I = p.I, a.K = p.K, a.T = p.T, a.P = p.P, a.Gmax = p.Gmax, a.mfma_min = W4_MFMA_MIN;
+    a.fmt = Lr->w13.format == W4_FMT_NVFP4_E4M3S16 ? FMT_NVFP4 : FMT_E2M1;
+    a.gs = Lr->w13.global_scales, a.s_gs = Lr->has_shared ? Lr->shared_w13.global_scales : nullptr;
     int32_t *ctg = p.multi ? (int32_t *)(wsb + p.off_route) + p.P + p.E + (size_t)p.nblk * p.E : nullptr;
     a.ctg = ctg;
     if (p.pf) launch_pf13(a, sm, ev(next_ev), ev(next_ev + 1));
@@ -1168,6 +1173,8 @@ int run_grouped(const moe_w4a16_layer *Lr, const MoEPlan &p, const uint16_t *x, 
     d.s_scales = Lr->has_shared ? (const uint16_t *)Lr->shared_w2.scales : nullptr;
     d.grp = grp, d.pairs = pairs, d.h_hi = h_hi, d.h_lo = h_lo, d.out = outp;
     d.H = p.H, d.I = p.I, d.K = p.K, d.T = p.T, d.P = p.P, d.Gmax = p.Gmax, d.mfma_min = W4_MFMA_MIN;
+    d.fmt = a.fmt;
+    d.gs = Lr->w2.global_scales, d.s_gs = Lr->has_shared ? Lr->shared_w2.global_scales : nullptr;
     d.ctg = ctg;
     if (p.pf) launch_pf2(d, sm, ev(next_ev + 2), ev(next_ev + 3));
     else launch_gw2(d, sm, ev(next_ev + 2), ev(next_ev + 3));

@@ -85,6 +85,7 @@ GEMV_NVFP4 = GemvShape("gemv-nvfp4-8192x2048", 8192, 2048, "nvfp4", 0)
 GEMV_LMHEAD = GemvShape("gemv-e2m1-lmhead-248320x2048", 248320, 2048, "e2m1", 0)
 QWEN_MOE_T32 = MoEShape("qwen3.6-35b-a3b-moe-batch32-zipf1.1", 2048, 512, 256, 8, 512, 32, 1.1, 0)
 QWEN_MOE_T1_NVFP4 = MoEShape("qwen3.6-35b-a3b-moe-decode-t1-nvfp4", 2048, 512, 256, 8, 512, 1, 0.0, 0, "nvfp4")
+QWEN_MOE_T32_NVFP4 = MoEShape("qwen3.6-35b-a3b-moe-batch32-zipf1.1-nvfp4", 2048, 512, 256, 8, 512, 32, 1.1, 0, "nvfp4")
 # bf16 shared expert (the pages' production choice for it), E2M1 routed experts
 QWEN_MOE_T1_BF16SH = MoEShape("qwen3.6-35b-a3b-moe-decode-t1-bf16shared", 2048, 512, 256, 8, 512, 1, 0.0, 0, "e2m1",
                               "bf16")

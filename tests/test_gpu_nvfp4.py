@@ -108,9 +108,45 @@ def test_nvfp4_moe_tiny(tiny_nv):
     for t in range(3):
         print(f"nvfp4 moe tiny token {t}", flush=True)
         _check_moe(shape, dev_layer, or_layer, tie_free_tokens(shape, or_layer, 1, first=t), f"nvfp4 tiny t={t}")
-    # batches take the single-token path for this format
-    assert w4.moe_w4a16_stage_count(dev_layer, 7) == 3
-    _check_moe(shape, dev_layer, or_layer, tie_free_tokens(shape, or_layer, 7, first=10), "nvfp4 tiny T=7")
+    # batches of 4 or more take the grouped path (MFMA for groups of >= 4 rows)
+    assert w4.moe_w4a16_stage_count(dev_layer, 3) == 3
+    assert w4.moe_w4a16_stage_count(dev_layer, 7) == 5
+    _check_moe(shape, dev_layer, or_layer, tie_free_tokens(shape, or_layer, 3, first=30), "nvfp4 tiny T=3")
+    for T in (7, 40, 300):
+        print(f"nvfp4 moe tiny T={T}", flush=True)
+        _check_moe(shape, dev_layer, or_layer, tie_free_tokens(shape, or_layer, T, first=10), f"nvfp4 tiny T={T}")
+
+
+def test_nvfp4_moe_tiny_batched_experts_entry(tiny_nv):
+    """Caller routing on the grouped path: one group of >= 16 rows (MFMA), small
+    groups (VALU), an invalid id that turns its token into NaN."""
+    shape, dev_layer, or_layer = tiny_nv
+    T = 24
+    xb = tie_free_tokens(shape, or_layer, T, first=300)
+    rng = np.random.default_rng(6)
+    ids = np.stack([rng.choice(shape.num_experts, shape.top_k, replace=False) for _ in range(T)]).astype(np.int32)
+    ids[:20, 0] = 3
+    ids[:20, 1] = np.where(ids[:20, 1] == 3, 4, ids[:20, 1])
+    w = rng.uniform(0.1, 1.0, size=(T, shape.top_k)).astype(np.float32)
+    y = w4.moe_w4a16_experts(dev_layer, wl.bf16_tensor(xb), torch.from_numpy(ids).to(DEV), torch.from_numpy(w).to(DEV))
+    assert_bf16_close(wl.bf16_bits(y), ops.moe_experts(or_layer, xb, ids, w.astype(np.float64)), "nvfp4 batched entry")
+    bad = ids.copy()
+    bad[7, 1] = -1
+    y2 = w4.moe_w4a16_experts(dev_layer, wl.bf16_tensor(xb), torch.from_numpy(bad).to(DEV),
+                              torch.from_numpy(w).to(DEV))
+    g = oracle.bf16_bits_to_f64(wl.bf16_bits(y2))
+    assert np.all(np.isnan(g[7])) and np.all(np.isfinite(np.delete(g, 7, axis=0)))
+
+
+def test_nvfp4_moe_batch32_zipf():
+    """The 35B-A3B-shaped NVFP4 layer, 32 tokens with the Zipf(1.1) routing bias:
+    the grouped path, every token checked."""
+    shape = synth.QWEN_MOE_T32_NVFP4
+    dev_layer = wl.build_moe_layer(shape, device=DEV)
+    assert w4.moe_w4a16_stage_count(dev_layer, 32) == 5
+    or_layer = oracle_layer(shape)
+    print("nvfp4 batch 32", flush=True)
+    print(_check_moe(shape, dev_layer, or_layer, tie_free_tokens(shape, or_layer, 32, first=50), shape.name), flush=True)
 
 
 def test_nvfp4_moe_tiny_experts_entry(tiny_nv):
