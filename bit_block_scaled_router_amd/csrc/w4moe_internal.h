@@ -10,7 +10,8 @@ namespace w4 {
 int fail(int status, const char *fmt, ...);
 void clear_error();
 
-// Scale block length of a format (16 or 128), 0 for an unknown tag.
+// Scale block length of a format (16, 32 or 128; bf16: 32, its K granule), 0 for
+// an unknown tag.
 int group_of(int32_t format);
 
 // Validate format/layout tags and dimensions of a matrix stack.
