@@ -93,3 +93,34 @@ def test_prefill_full_sampled(shape):
     rows = [0, 1, 511, 1024, 1500, 2000, 2046, 2047]
     ref, _, _ = ops.moe_forward(or_layer, xb, tokens=rows)
     print(assert_bf16_close(y[rows], ref, shape.name), flush=True)
+
+
+def _sampled_check(shape, T, rows, what):
+    dev_layer = wl.build_moe_layer(shape, device=DEV)
+    or_layer = oracle_layer(shape)
+    xb = np.stack([synth.x_row(shape.seed, shape.hidden, t) for t in range(T)])
+    y, ids, wts = _run(dev_layer, xb, shape.top_k)
+    import moe_cases
+    keep = [r for r in rows if moe_cases.min_gap(or_layer, xb[r]) >= moe_cases.GAP]
+    print(f"{what}: {len(keep)} tie-free sampled tokens", flush=True)
+    _check_routing(or_layer, xb[keep], ids[keep], wts[keep], shape.top_k)
+    ref, _, _ = ops.moe_forward(or_layer, xb, tokens=keep)
+    print(assert_bf16_close(y[keep], ref, what), flush=True)
+
+
+def test_prefill_largest_pair_count():
+    """65,536 (token, slot) pairs, the largest grouped call: T = 8192 on the
+    35B-A3B shape (~256 pairs per expert, four column tiles per group)."""
+    shape = synth.MoEShape("qwen-prefill-8192", 2048, 512, 256, 8, 512, 8192, 0.0, 21)
+    rng = np.random.default_rng(31)
+    rows = np.unique(np.concatenate([[0, 8191], rng.choice(8192, 10, replace=False)]))
+    _sampled_check(shape, 8192, rows, "T=8192 (65536 pairs)")
+
+
+def test_prefill_largest_token_count():
+    """T = 16384 tokens (the entry points' limit) on the tiny layer, top-2:
+    32,768 pairs, groups of ~4000 rows."""
+    shape = synth.MoEShape("tiny-prefill-16384", 256, 128, 8, 2, 128, 16384, 0.0, 22)
+    rng = np.random.default_rng(32)
+    rows = np.unique(np.concatenate([[0, 16383], rng.choice(16384, 30, replace=False)]))
+    _sampled_check(shape, 16384, rows, "T=16384 tiny")
