@@ -129,3 +129,19 @@ def test_mx_expert_quantises_x_and_h():
     want = w2.astype(np.float64) @ O.mx_e4m3(h)[0]
     assert np.array_equal(got, want)
     assert not np.allclose(got, ops.expert_ffn(w13, w2, x), rtol=1e-6)
+
+
+def test_mxfp8_given_exponent():
+    """mx_e4m3 with the shared exponents given: the computed ones reproduce the
+    default result; one more (a coarser block scale) matches torch's E4M3
+    rounding of v / 2^(X+1), clamped to +-448."""
+    rng = np.random.default_rng(17)
+    x = (rng.standard_normal((6, 128)) * np.exp2(rng.integers(-6, 6, (6, 1)))).astype(np.float64)
+    q, X = O.mx_e4m3(x)
+    q1, X1 = O.mx_e4m3(x, X)
+    assert np.array_equal(q, q1) and np.array_equal(X, X1)
+    q2, X2 = O.mx_e4m3(x, X + 1)
+    assert np.array_equal(X2, X + 1)
+    s = np.repeat(np.exp2((X + 1).astype(np.float64)), 32, axis=-1)
+    t = torch.from_numpy(np.clip(x / s, -448, 448).astype(np.float32)).to(torch.float8_e4m3fn).to(torch.float64)
+    assert np.array_equal(q2, t.numpy() * s)
