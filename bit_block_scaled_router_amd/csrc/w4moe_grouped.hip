@@ -38,6 +38,9 @@ namespace w4k {
 
 // k-steps (32 elements per lane each) the VALU small-group paths keep in registers
 constexpr int KS_VALU = 2;
+#ifndef W4_GW_MINBLK
+#define W4_GW_MINBLK 3  // blocks per CU the batched W13 / W2 kernels are compiled to fit
+#endif                  // (W2 with I > 512 keeps its registers: fitting 3 would spill)
 
 // ================================================================= route + group
 
@@ -471,7 +474,7 @@ __device__ __forceinline__ void gw13_unit(const GW13Args &a, int gs, int tile, f
 // Blocks walk the work units (group slot x row tile) with a grid stride, so the
 // grid needs no bound on the number of active experts.
 template <int FMT, int L>
-__global__ __launch_bounds__(256) void k_moe_gw13(GW13Args a) {
+__global__ __launch_bounds__(256, W4_GW_MINBLK) void k_moe_gw13(GW13Args a) {
     __shared__ float red[3][16][64];  // MFMA K-split partials of waves 1..3
     const int nu = unit_count(a.grp, a.s_codes != nullptr, a.tiles);
     for (int u = blockIdx.x; u < nu; u += gridDim.x) {
@@ -666,7 +669,7 @@ __device__ __forceinline__ void gw2_unit(const GW2Args &a, int gs, int tile, flo
 }
 
 template <int FMT, int L>
-__global__ __launch_bounds__(256) void k_moe_gw2(GW2Args a) {
+__global__ __launch_bounds__(256, L <= 16 ? W4_GW_MINBLK : 1) void k_moe_gw2(GW2Args a) {
     __shared__ float red[4][4][8][64];  // MFMA partials: [wave][row tile][column tile x 4 + j][lane]
     const int nu = unit_count(a.grp, a.s_codes != nullptr, a.tiles);
     for (int u = blockIdx.x; u < nu; u += gridDim.x) {
