@@ -173,6 +173,47 @@ __device__ __forceinline__ uint32_t ld16(Buf b, uint32_t off) {
     return (uint32_t)(uint16_t)__builtin_amdgcn_raw_buffer_load_b16(b.r, off, 0, 0);
 }
 
+// ---------------------------------------------------------------- MXFP8
+
+// MXFP8 quantisation of activations: shared exponent of a block with maximum
+// magnitude `amax`: floor(log2 amax) - 8 (E4M3's largest exponent), limited to
+// [-127, 127]; -127 for an all-zero block.
+__device__ __forceinline__ int mx8_exponent(float amax) {
+    if (!(amax > 0.f)) return -127;
+    int X = __builtin_amdgcn_frexp_expf(amax) - 1 - 8;  // amax = m 2^e, m in [0.5, 1)
+    return X < -127 ? -127 : (X > 127 ? 127 : X);
+}
+
+// Four activations -> four E4M3 bytes of v / 2^X, clamped to +-448, round to
+// nearest even (the conversion instruction with unit scale).
+__device__ __forceinline__ uint32_t mx8_pack4(float a, float b, float c, float d, int X) {
+    auto cl = [&](float v) { return fminf(fmaxf(__builtin_amdgcn_ldexpf(v, -X), -448.f), 448.f); };
+    typedef short s16x2 __attribute__((ext_vector_type(2)));
+    s16x2 w = {0, 0};
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w, cl(a), cl(b), 1.0f, false);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w, cl(c), cl(d), 1.0f, true);
+    return __builtin_bit_cast(uint32_t, w);
+}
+
+// One MXFP8 block of 32 fp32 values (float4 q holds elements 4q .. 4q+3), in
+// place: each value becomes its E4M3 element E4M3(v / 2^X) (exact in fp32);
+// returns the block's shared exponent X.
+__device__ __forceinline__ int mx8_block_f32(float4 *v) {
+    float amax = 0.f;
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+        amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v[q].x), fabsf(v[q].y)), fmaxf(fabsf(v[q].z), fabsf(v[q].w))));
+    const int X = mx8_exponent(amax);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+        const uint32_t w = mx8_pack4(v[q].x, v[q].y, v[q].z, v[q].w, X);
+        const f32x2 a = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w, 1.0f, false);
+        const f32x2 b = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w, 1.0f, true);
+        v[q] = make_float4(a.x, a.y, b.x, b.y);
+    }
+    return X;
+}
+
 // ---------------------------------------------------------------- activations
 
 // Activation slice of one lane for one step: 32 bf16 values as 16 dwords.  For
@@ -182,6 +223,7 @@ template <int FMT>
 struct XSlice {
     uint4 v[4];
     float sum;
+    int X;  // MXFP4 layers: shared exponent of the slice's MXFP8 block
 };
 
 // Load the slice at byte offset `off` of the activation buffer (OOB -> zeros).
@@ -212,6 +254,34 @@ __device__ __forceinline__ void prep_xslice(XSlice<FMT> &xs) {
             xs.v[i] = b;
         }
         xs.sum = s;
+    } else if constexpr (FMT == FMT_MXFP4) {
+        // the slice is one MXFP8 block: each bf16 becomes its E4M3 element
+        // (at most 4 significant bits, exact in bf16) and X is kept for the scale
+        float amax = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t d[4] = {xs.v[i].x, xs.v[i].y, xs.v[i].z, xs.v[i].w};
+#pragma unroll
+            for (int m = 0; m < 4; ++m)
+                amax = fmaxf(amax, fmaxf(fabsf(__uint_as_float(d[m] << 16)), fabsf(__uint_as_float(d[m] & 0xFFFF0000u))));
+        }
+        const int X = mx8_exponent(amax);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            uint32_t d[4] = {xs.v[i].x, xs.v[i].y, xs.v[i].z, xs.v[i].w};
+#pragma unroll
+            for (int m = 0; m < 4; m += 2) {
+                const uint32_t w = mx8_pack4(__uint_as_float(d[m] << 16), __uint_as_float(d[m] & 0xFFFF0000u),
+                                             __uint_as_float(d[m + 1] << 16), __uint_as_float(d[m + 1] & 0xFFFF0000u), X);
+                const f32x2 a = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w, 1.0f, false);
+                const f32x2 b = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w, 1.0f, true);
+                d[m] = __builtin_amdgcn_perm(__float_as_uint(a.y), __float_as_uint(a.x), 0x07060302u);
+                d[m + 1] = __builtin_amdgcn_perm(__float_as_uint(b.y), __float_as_uint(b.x), 0x07060302u);
+            }
+            xs.v[i] = make_uint4(d[0], d[1], d[2], d[3]);
+        }
+        xs.sum = 0.f;
+        xs.X = X;
     } else {
         xs.sum = 0.f;
     }
@@ -300,6 +370,14 @@ __device__ __forceinline__ float chunk_dot_bf16(uint4 c, uint32_t sc, const XSli
         const f32x2 s = block_scales2<FMT>(sc);
         acc = fmaf(p0, s.x, acc);
         acc = fmaf(p1, s.y, acc);
+    } else if constexpr (FMT == FMT_MXFP4) {
+        // one block: E2M1 codes x E4M3 activations (exact products), then both
+        // shared exponents at once (the E8M0 byte and the slice's X)
+        float p = e2m1_dot8(c.x, xs.v[0], 0.f);
+        p = e2m1_dot8(c.y, xs.v[1], p);
+        p = e2m1_dot8(c.z, xs.v[2], p);
+        p = e2m1_dot8(c.w, xs.v[3], p);
+        acc += __builtin_amdgcn_ldexpf(p, (int)(sc & 0xFFu) - 127 + xs.X);
     } else {
         float p = u4_dot8(c.x, xs.v[0], 0.f);
         p = u4_dot8(c.y, xs.v[1], p);
@@ -312,11 +390,25 @@ __device__ __forceinline__ float chunk_dot_bf16(uint4 c, uint32_t sc, const XSli
 }
 
 // Same against fp32 activations h[32] (the down projection's SiLU(gate)*up).
-// hs = sum of the 32 activations (int4 offset correction).
+// hs = sum of the 32 activations (int4 offset correction).  MXFP4: h holds the
+// E4M3 elements of one MXFP8 block and hx its shared exponent.
 template <int FMT>
-__device__ __forceinline__ float chunk_dot_f32(uint4 c, uint32_t sc, const float4 *h, float hs, float acc) {
+__device__ __forceinline__ float chunk_dot_f32(uint4 c, uint32_t sc, const float4 *h, float hs, float acc,
+                                               int hx = 0) {
     const uint32_t cw[4] = {c.x, c.y, c.z, c.w};
-    if constexpr (FMT == FMT_E2M1 || FMT == FMT_NVFP4) {
+    if constexpr (FMT == FMT_MXFP4) {
+        float q = 0.f;
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {  // dword d: elements 8d .. 8d+7
+            const float4 h0 = h[2 * d], h1 = h[2 * d + 1];
+            f32x2 w;
+            w = e2m1x2_f32<0>(cw[d]); q = fmaf(w.x, h0.x, q); q = fmaf(w.y, h0.y, q);
+            w = e2m1x2_f32<1>(cw[d]); q = fmaf(w.x, h0.z, q); q = fmaf(w.y, h0.w, q);
+            w = e2m1x2_f32<2>(cw[d]); q = fmaf(w.x, h1.x, q); q = fmaf(w.y, h1.y, q);
+            w = e2m1x2_f32<3>(cw[d]); q = fmaf(w.x, h1.z, q); q = fmaf(w.y, h1.w, q);
+        }
+        acc += __builtin_amdgcn_ldexpf(q, (int)(sc & 0xFFu) - 127 + hx);
+    } else if constexpr (FMT == FMT_E2M1 || FMT == FMT_NVFP4) {
         float p[2];
 #pragma unroll
         for (int b = 0; b < 2; ++b) {
@@ -502,26 +594,6 @@ __device__ __forceinline__ f32x4 mfma_mx(uint4 a, uint4 b_lo, uint4 b_hi, uint32
     const i32x8 B = {(int)b_lo.x, (int)b_lo.y, (int)b_lo.z, (int)b_lo.w,
                      (int)b_hi.x, (int)b_hi.y, (int)b_hi.z, (int)b_hi.w};
     return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, B, c, 4, 0, 0, (int)sa, 0, (int)sb);
-}
-
-// MXFP8 quantisation of activations: shared exponent of a block with maximum
-// magnitude `amax`: floor(log2 amax) - 8 (E4M3's largest exponent), limited to
-// [-127, 127]; -127 for an all-zero block.
-__device__ __forceinline__ int mx8_exponent(float amax) {
-    if (!(amax > 0.f)) return -127;
-    int X = __builtin_amdgcn_frexp_expf(amax) - 1 - 8;  // amax = m 2^e, m in [0.5, 1)
-    return X < -127 ? -127 : (X > 127 ? 127 : X);
-}
-
-// Four activations -> four E4M3 bytes of v / 2^X, clamped to +-448, round to
-// nearest even (the conversion instruction with unit scale).
-__device__ __forceinline__ uint32_t mx8_pack4(float a, float b, float c, float d, int X) {
-    auto cl = [&](float v) { return fminf(fmaxf(__builtin_amdgcn_ldexpf(v, -X), -448.f), 448.f); };
-    typedef short s16x2 __attribute__((ext_vector_type(2)));
-    s16x2 w = {0, 0};
-    w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w, cl(a), cl(b), 1.0f, false);
-    w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w, cl(c), cl(d), 1.0f, true);
-    return __builtin_bit_cast(uint32_t, w);
 }
 
 // One fp32 value -> bf16 hi (truncated) + bf16 lo (residual, rounded to

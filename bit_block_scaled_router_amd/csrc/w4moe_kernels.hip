@@ -592,12 +592,14 @@ __global__ __launch_bounds__(1024) void k_moe_down(DownArgs a) {
                 sw[r] = ld_scales<FMT>(sb, v ? scale_off<FMT>((uint32_t)row * spr, k0) : OOB);
             }
             float hs = 0.f;
+            int hx = 0;
             if constexpr (FMT == FMT_INT4) {
 #pragma unroll
                 for (int q = 0; q < 8; ++q) hs += (hv[q].x + hv[q].y) + (hv[q].z + hv[q].w);
             }
+            if constexpr (FMT == FMT_MXFP4) hx = mx8_block_f32(hv);  // the lane's 32 h values: one MXFP8 block
 #pragma unroll
-            for (int r = 0; r < RT; ++r) acc[r] = chunk_dot_f32<FMT>(cw[r], sw[r], hv, hs, acc[r]);
+            for (int r = 0; r < RT; ++r) acc[r] = chunk_dot_f32<FMT>(cw[r], sw[r], hv, hs, acc[r], hx);
         }
 #pragma unroll
         for (int r = 0; r < RT; ++r) {
@@ -822,13 +824,13 @@ int check_layer(const moe_w4a16_layer *Lr, int64_t T, MoEPlan &p) {
                 (fmt == W4_FMT_E2M1_F16S16 ? p.P <= MAX_GROUPED_PAIRS
                                            : fmt == W4_FMT_NVFP4_E4M3S16 && p.P <= MAX_ONE_BLOCK_PAIRS) &&
                 !(Lr->has_shared && Lr->shared_w13.format == W4_FMT_BF16);
-    if (p.mx) {  // every batch size runs grouped, all on the scaled FP4 MFMA
+    if (p.mx) {  // batches run grouped on the scaled FP4 MFMA; single tokens on the VALU kernels
         if (H % 128 || I % 128)
             return fail(W4_ERR_UNSUPPORTED, "MXFP4 layers need hidden and inter multiples of 128");
         if (p.P > MAX_GROUPED_PAIRS)
             return fail(W4_ERR_UNSUPPORTED, "MXFP4 layers take at most %d (token, slot) pairs per call",
                         MAX_GROUPED_PAIRS);
-        p.grouped = true;
+        p.grouped = T >= W4_GROUPED_MIN_T;
     }
     p.pf = p.grouped && p.P > MAX_ONE_BLOCK_PAIRS;
     p.multi = p.pf || (p.grouped && T >= W4_MULTI_ROUTE_MIN_T);
@@ -1043,6 +1045,7 @@ int run_moe(const moe_w4a16_layer *Lr, const uint16_t *x, int64_t T, const int32
     a.lstride = p.lstride, a.hstride = p.hstride, a.route = route ? 1 : 0, a.L2 = p.L2;
     if (Lr->w13.format == W4_FMT_E2M1_F16S16) launch_w13<FMT_E2M1>(p, a, l_w13);
     else if (Lr->w13.format == W4_FMT_NVFP4_E4M3S16) launch_w13<FMT_NVFP4>(p, a, l_w13);
+    else if (Lr->w13.format == W4_FMT_MXFP4_E8M0S32) launch_w13<FMT_MXFP4>(p, a, l_w13);
     else launch_w13<FMT_INT4>(p, a, l_w13);
     if ((st = hip_status("w13 launch"))) return st;
 
@@ -1064,6 +1067,7 @@ int run_moe(const moe_w4a16_layer *Lr, const uint16_t *x, int64_t T, const int32
     d.lstride = p.lstride, d.hstride = p.hstride;
     if (Lr->w2.format == W4_FMT_E2M1_F16S16) launch_down<FMT_E2M1>(p, d, l_down);
     else if (Lr->w2.format == W4_FMT_NVFP4_E4M3S16) launch_down<FMT_NVFP4>(p, d, l_down);
+    else if (Lr->w2.format == W4_FMT_MXFP4_E8M0S32) launch_down<FMT_MXFP4>(p, d, l_down);
     else launch_down<FMT_INT4>(p, d, l_down);
     return hip_status("down launch");
 }

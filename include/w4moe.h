@@ -80,11 +80,12 @@ extern "C" {
 /* MXFP4 (OCP Microscaling v1.0): E2M1 codes with one E8M0 scale byte (2^(byte -
  * 127)) per 32 K elements; scales [groups][n][k/32] bytes.  The vendor
  * block-scaled format the pages bridge to (README P17/P54, R5-B "e8m0/group32").
- * In an MoE layer it runs on gfx950's scaled FP4 MFMA with MXFP8 activations:
- * the layer input and the SwiGLU intermediate are quantised to E4M3 elements with
- * an E8M0 scale per 32 (X = floor(log2 absmax) - 8, round to nearest even,
- * clamp to +-448), so such a layer computes W4A8 (MX), every T on the batched
- * path; the dense GEMV does not take this format. */
+ * In an MoE layer it takes MXFP8 activations: the layer input and the SwiGLU
+ * intermediate are quantised to E4M3 elements with an E8M0 scale per 32
+ * (X = floor(log2 absmax) - 8, round to nearest even, clamp to +-448), so such a
+ * layer computes W4A8 (MX): batches on gfx950's scaled FP4 MFMA, 1-3 tokens on
+ * the single-token VALU kernels (exact products, fp32 sums); the dense GEMV
+ * does not take this format. */
 #define W4_FMT_MXFP4_E8M0S32 5
 
 /* Canonical layout, the only one this library reads:
@@ -256,10 +257,11 @@ int moe_w4a16_forward_timed(const moe_w4a16_layer *L, const uint16_t *x, int64_t
  * and at most 4096, T >= 4 and T * top_k <= 65536 (NVFP4 layers: the same,
  * up to T * top_k = 4096, with one exact bf16 MFMA term per weight instead of
  * two and the global scales applied to the sums); other requests take the
- * single-token path.  MXFP4 layers always run 6 kernels (router; x to MXFP8;
- * top-k and grouping; W13 + SiLU with h quantised to MXFP8; W2; ordered
- * combine), need H and I multiples of 128 and a shared expert in MXFP4
- * (W4_ERR_UNSUPPORTED otherwise).  Batches of more than 4096 (token, slot)
+ * single-token path.  MXFP4 layers need H and I multiples of 128 and a shared
+ * expert in MXFP4 (W4_ERR_UNSUPPORTED otherwise); from T = 4 they run 6
+ * kernels (router; x to MXFP8; top-k and grouping; W13 + SiLU with h quantised
+ * to MXFP8; W2; ordered combine), below it the 3 single-token kernels, which
+ * quantise x and h in registers.  Batches of more than 4096 (token, slot)
  * pairs (prefill sizes; at most 65536 pairs, T <= 16384) group their pairs
  * over three launches (per-block top-k and expert histograms; one scan; a
  * scatter) instead of one, so the grouped path takes 7 kernels (MXFP4: 8), and

@@ -1,7 +1,8 @@
 """GPU parity of the MX variant (MXFP4 experts: E2M1 codes with an E8M0 scale
 per 32; activations and h quantised to MXFP8 per the OCP Microscaling
-conversion; every product on the scaled FP4 MFMA) through the C ABI against the
-CPU oracle.
+conversion) through the C ABI against the CPU oracle.  Batches of 4 or more
+tokens run every product on the scaled FP4 MFMA (the model below); 1-3 tokens
+run the single-token VALU kernels (exact products, fp32 sums; last section).
 
 Bit-exact: dequantised weights, routing ids, x as MXFP8 (codes and scales).
 
@@ -219,15 +220,7 @@ def tiny_mx():
     return shape, wl.build_moe_layer(shape, device=DEV), oracle_layer(shape)
 
 
-def test_mx_tiny_single_tokens(tiny_mx):
-    shape, dev_layer, or_layer = tiny_mx
-    assert w4.moe_w4a16_stage_count(dev_layer, 1) == 6  # the MX path is grouped at every T
-    for t in range(3):
-        print(f"mx tiny token {t}", flush=True)
-        _mx_case(shape, dev_layer, or_layer, tie_free_tokens(shape, or_layer, 1, first=t), f"mx tiny t={t}")
-
-
-@pytest.mark.parametrize("T", [2, 7, 40, 300])
+@pytest.mark.parametrize("T", [4, 7, 40, 300])
 def test_mx_tiny_batches(tiny_mx, T):
     # 8 experts, top-2: groups from 1 row (a partial 16-column tile) to ~75 rows
     shape, dev_layer, or_layer = tiny_mx
@@ -237,9 +230,9 @@ def test_mx_tiny_batches(tiny_mx, T):
 
 def test_mx_tiny_experts_entry(tiny_mx):
     shape, dev_layer, or_layer = tiny_mx
-    xb = tie_free_tokens(shape, or_layer, 3, first=20)
-    ids = np.array([[1, 6], [6, 1], [3, 3]], dtype=np.int32)
-    w = np.array([[0.7, 0.3], [0.5, 0.5], [1.0, 0.25]], dtype=np.float32)
+    xb = tie_free_tokens(shape, or_layer, 4, first=20)
+    ids = np.array([[1, 6], [6, 1], [3, 3], [0, 7]], dtype=np.int32)
+    w = np.array([[0.7, 0.3], [0.5, 0.5], [1.0, 0.25], [0.125, -0.5]], dtype=np.float32)
     _mx_case(shape, dev_layer, or_layer, xb, "mx experts", ids=ids, w=w)
 
 
@@ -248,13 +241,6 @@ def full_mx():
     shape = synth.QWEN_MOE_T32_MX
     print("building the 35B-A3B-shaped MXFP4 layer", flush=True)
     return shape, wl.build_moe_layer(shape, device=DEV), oracle_layer(shape)
-
-
-def test_mx_full_t1(full_mx):
-    shape, dev_layer, or_layer = full_mx
-    for t in range(2):
-        print(f"mx full token {t}", flush=True)
-        _mx_case(shape, dev_layer, or_layer, tie_free_tokens(shape, or_layer, 1, first=t), f"mx full t={t}")
 
 
 def test_mx_full_t32_sampled(full_mx):
@@ -283,3 +269,167 @@ def test_mx_prefill_sampled():
     print("mx prefill T=2048 (sampled)", flush=True)
     xb = tie_free_tokens(shape, or_layer, shape.tokens)
     _mx_case(shape, dev_layer, or_layer, xb, "mx prefill T=2048", tokens=[0, 1, 700, 1300, 2046, 2047])
+
+
+# ------------------------------------------------------------------ 1-3 tokens
+#
+# The single-token kernels quantise in registers: each lane's 32 activations of
+# x (W13) and of h (down) are one MXFP8 block.  E2M1 x E4M3 products are exact
+# in fp32; a lane's 32-element sum, its scaling by both shared exponents (exact)
+# and the wave reduction add at most 32 + 1 + 6 fp32 roundings (W13, 64 lanes)
+# or 32 + 1 + 4 + 1 (down, 16 lanes, times the routing weight), each within
+# 2**-24 of the partial sum, itself at most sum |w_k v_k|: EPS_VALU = 64 * 2**-24
+# per unit of that sum bounds both.  h is stored in fp32 before the down kernel
+# quantises it, so the stored h is checked against the oracle's fp64 h, and its
+# MXFP8 rounding (the oracle's quantiser applied to the device h: the kernel's
+# conversion is bit-exact) may differ from the oracle's own only across a
+# midpoint within that bound.
+
+EPS_VALU = 64 * 2.0 ** -24
+
+
+def _lanes(k):
+    need, L = (k + 31) // 32, 1
+    while L < need and L < 64:
+        L *= 2
+    return L
+
+
+def _ws_layout_single(shape, T):
+    """Offset of h in the single-token path's workspace: logits [T][ceil64(E+1)]
+    fp32, ids and weights [T][k], then h [T][S][hstride] fp32 in the down
+    kernel's lane order; returns (offset, hstride, lanes per row of the down
+    kernel, total bytes)."""
+    def up(v):
+        return (v + 255) // 256 * 256
+    H, I, E, K = shape.hidden, shape.inter, shape.num_experts, shape.top_k
+    S = K + (1 if shape.has_shared else 0)
+    L2 = _lanes(I)
+    hstride = (I + 32 * L2 - 1) // (32 * L2) * 32 * L2
+    off = up(T * ((E + 1 + 63) // 64 * 64) * 4)
+    off = up(off + T * K * 4)
+    off_h = up(off + T * K * 4)
+    return off_h, hstride, L2, up(off_h + T * S * hstride * 4)
+
+
+def _h_order(I, L2):
+    """Position of h element i in the down kernel's lane order: lane lk of step s
+    holds elements 32 (L2 s + lk) .. +31 as 8 float4."""
+    i = np.arange(I)
+    span = 32 * L2
+    st, rem = i // span, i % span
+    return st * span + ((rem & 31) // 4 * L2 + rem // 32) * 4 + (i & 3)
+
+
+def _valu_bound(w, v):
+    return EPS_VALU * (np.abs(w) * np.abs(v)[None, :]).sum(axis=1)
+
+
+def _mx_case_single(shape, dev_layer, or_layer, xb, what, ids=None, w=None):
+    T = xb.shape[0]
+    H, I, K = shape.hidden, shape.inter, shape.top_k
+    S = K + (1 if shape.has_shared else 0)
+    assert w4.moe_w4a16_stage_count(dev_layer, T) == 3
+    ws = w4.alloc_workspace(dev_layer, T)
+    off_h, hstride, L2, total = _ws_layout_single(shape, T)
+    assert ws.numel() == total
+    if ids is None:
+        ids_t = torch.full((T, K), -7, dtype=torch.int32, device=DEV)
+        w_t = torch.zeros((T, K), dtype=torch.float32, device=DEV)
+        y = w4.moe_w4a16_forward(dev_layer, wl.bf16_tensor(xb), topk_ids=ids_t, topk_w=w_t, ws=ws)
+    else:
+        ids_t, w_t = torch.from_numpy(ids).to(DEV), torch.from_numpy(w).to(DEV)
+        y = w4.moe_w4a16_experts(dev_layer, wl.bf16_tensor(xb), ids_t, w_t, ws=ws)
+    torch.cuda.synchronize()
+    hws = ws.cpu().numpy()[off_h:off_h + T * S * hstride * 4].view(np.float32).reshape(T, S, hstride)
+    hdev = hws[:, :, _h_order(I, L2)].astype(np.float64)
+    ydev = wl.bf16_bits(y)
+    ids_dev, w_dev = ids_t.cpu().numpy(), w_t.cpu().numpy()
+    xo = F.mx_e4m3(oracle.bf16_bits_to_f64(xb))[0]
+    want, plain, allows = [], [], []
+    flips = blocks = 0
+    worst = 0.0
+    for t in range(T):
+        if ids is None:
+            rids, rw = ops.route(ops.router_logits(or_layer.router_w, xb[t], or_layer.router_bias), K)
+            assert np.array_equal(ids_dev[t], rids), (what, t)
+            np.testing.assert_allclose(w_dev[t], rw, rtol=2e-6, atol=1e-7)
+        else:
+            rids, rw = ids[t], w[t].astype(np.float64)
+        slots = [(or_layer.expert(int(rids[j])), rw[j]) for j in range(K)]
+        if or_layer.has_shared:
+            slots.append((or_layer.shared(), ops.shared_gate(or_layer.shared_gate_w, xb[t])))
+        acc, allow, mag = np.zeros(H), np.zeros(H), np.zeros(H)
+        for j, ((w13, w2), coef) in enumerate(slots):
+            g, u = w13[:I] @ xo[t], w13[I:] @ xo[t]
+            e = _valu_bound(w13, xo[t])
+            eg, eu = e[:I], e[I:]
+            sig = 1.0 / (1.0 + np.exp(-g))
+            dsilu = sig * (1.0 + g * (1.0 - sig))
+            h = ops.silu(g) * u
+            err = (np.abs(dsilu) + eg) * eg * (np.abs(u) + eu) + np.abs(ops.silu(g)) * eu + 8 * 2.0 ** -24 * np.abs(h)
+            hd = hdev[t, j]
+            bad = np.abs(hd - h) > err
+            assert not bad.any(), (what, t, j, int(bad.sum()), np.max(np.abs(hd - h) / err))
+            # the down kernel's MXFP8 rounding of the stored h (bit-exact), against the oracle's own
+            hq, Xd = F.mx_e4m3(hd)
+            codes = _e4m3_codes(hq / np.exp2(np.repeat(Xd, 32).astype(np.float64)))
+            hq2, nf, nb, wr = _validate_h(h, err, codes, Xd)
+            assert np.array_equal(hq2, hq)
+            flips, blocks, worst = flips + nf, blocks + nb, max(worst, wr)
+            yp = w2 @ hq
+            acc += coef * yp
+            allow += abs(coef) * _valu_bound(w2, hq)
+            mag += np.abs(coef * yp)
+        want.append(acc)
+        allows.append(allow + EPS_ADD * len(slots) * mag)
+        plain.append(ops.moe_experts(or_layer, xb[t:t + 1], rids[None], np.asarray(rw)[None])[0])
+    want, plain, allows = np.array(want), np.array(plain), np.array(allows)
+    rep = assert_bf16_close(ydev, want, what, elem_abs=0.0, elem_allow=allows)
+    rep_plain = oracle.error_report(oracle.bf16_bits_to_f64(ydev), plain)
+    n_h = T * S * I
+    print(f"{what}: {rep}; h elements on the other side of a midpoint {flips} of {n_h}, blocks with the other "
+          f"exponent {blocks}, largest |h - midpoint| / bound {worst:.3g}; vs the oracle's own roundings {rep_plain}",
+          flush=True)
+    assert flips <= max(4, MAX_FLIP_FRAC * n_h), what
+    # the plain oracle output (its own h roundings) within the parity bar
+    assert rep_plain["max_abs"] <= 1e-2 * rep_plain["max_ref"], (what, rep_plain)
+    return rep
+
+
+@pytest.mark.parametrize("T", [1, 2, 3])
+def test_mx_tiny_single_tokens(tiny_mx, T):
+    shape, dev_layer, or_layer = tiny_mx
+    for first in range(0, 3 * T, T):
+        print(f"mx tiny single-token path T={T} first={first}", flush=True)
+        _mx_case_single(shape, dev_layer, or_layer, tie_free_tokens(shape, or_layer, T, first=first),
+                        f"mx tiny T={T} first={first}")
+
+
+def test_mx_tiny_single_tokens_experts_entry(tiny_mx):
+    # supplied routing: a repeated expert, a negative weight, an id out of range
+    # (its slot reads nothing and the token's output is NaN)
+    shape, dev_layer, or_layer = tiny_mx
+    xb = tie_free_tokens(shape, or_layer, 3, first=30)
+    ids = np.array([[1, 6], [3, 3], [0, 7]], dtype=np.int32)
+    w = np.array([[0.7, 0.3], [1.0, 0.25], [0.125, -0.5]], dtype=np.float32)
+    _mx_case_single(shape, dev_layer, or_layer, xb, "mx single experts", ids=ids, w=w)
+    ids_bad = ids.copy()
+    ids_bad[1, 0] = 8
+    y = w4.moe_w4a16_experts(dev_layer, wl.bf16_tensor(xb), torch.from_numpy(ids_bad).to(DEV),
+                             torch.from_numpy(w).to(DEV))
+    yb = oracle.bf16_bits_to_f64(wl.bf16_bits(y))
+    assert np.all(np.isnan(yb[1])) and np.all(np.isfinite(yb[[0, 2]]))
+
+
+def test_mx_full_t1(full_mx):
+    shape, dev_layer, or_layer = full_mx
+    for t in range(2):
+        print(f"mx full token {t}", flush=True)
+        _mx_case_single(shape, dev_layer, or_layer, tie_free_tokens(shape, or_layer, 1, first=t), f"mx full t={t}")
+
+
+def test_mx_full_t3(full_mx):
+    shape, dev_layer, or_layer = full_mx
+    print("mx full T=3", flush=True)
+    _mx_case_single(shape, dev_layer, or_layer, tie_free_tokens(shape, or_layer, 3, first=10), "mx full T=3")

@@ -183,10 +183,10 @@ def test_mxfp4_layer_plan_and_validation():
         return _layer(**d)
 
     L = mxl()
-    # every batch size takes the grouped MX path: router, x -> MXFP8, grouping,
-    # W13, W2, combine
-    assert w4.lib().moe_w4a16_stage_count(C.byref(L), 1) == 6
-    assert w4.lib().moe_w4a16_stage_count(C.byref(L), 64) == 6
+    # 1-3 tokens: the single-token kernels (router, W13 with x quantised per
+    # lane, down with h quantised per lane); from 4 tokens the grouped MX path:
+    # router, x -> MXFP8, grouping, W13, W2, combine
+    assert [w4.lib().moe_w4a16_stage_count(C.byref(L), T) for T in (1, 2, 3, 4, 64)] == [3, 3, 3, 6, 6]
     assert w4.lib().moe_w4a16_workspace_bytes(C.byref(L), 1) > 0
     # more than 4096 pairs group over three launches: 2 more stages
     assert w4.lib().moe_w4a16_stage_count(C.byref(L), 2048) == 6
@@ -209,10 +209,10 @@ def test_mxfp4_layer_plan_and_validation():
     # past 65536 pairs the single-token path
     E2 = _layer(top_k=8)
     assert [w4.lib().moe_w4a16_stage_count(C.byref(E2), T) for T in (3, 4, 512, 513, 8192, 8193)] == [3, 5, 5, 7, 7, 3]
-    # the timed entry point wants 12 events on the MX path
+    # the timed entry point wants 12 events on the grouped MX path
     ev = (C.c_void_p * 10)(*([1] * 10))
-    st = w4.lib().moe_w4a16_forward_timed(C.byref(L), 1 << 20, 1, 1 << 21, None, None, 1 << 24,
-                                          w4.lib().moe_w4a16_workspace_bytes(C.byref(L), 1), 0, ev, 10)
+    st = w4.lib().moe_w4a16_forward_timed(C.byref(L), 1 << 20, 4, 1 << 21, None, None, 1 << 24,
+                                          w4.lib().moe_w4a16_workspace_bytes(C.byref(L), 4), 0, ev, 10)
     assert st == w4.W4_ERR_INVALID_ARG
 
 
