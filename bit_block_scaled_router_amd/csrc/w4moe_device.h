@@ -482,52 +482,89 @@ __device__ __forceinline__ uint32_t order_key(float f) {
 }
 
 // One wave ranks E <= 64*PL logits (+ bias) by descending value, ties to the
-// lower expert id, for `rounds` rounds.  Ranking by logit equals ranking by
-// softmax probability (exp is increasing).  Lane l holds experts l*PL ..
-// l*PL+PL-1, so "lowest lane, then lowest slot" is the lowest id.  A round
-// takes each lane's best remaining entry (first index on equal keys), the
-// wave maximum of those and the lowest lane holding it; that lane removes the
-// entry.  Lane j < rounds receives the j-th id and its (biased) logit; the id
-// of round `want` is returned to every lane.
+// lower expert id, for `rounds` rounds, for NT tokens at once (their rounds
+// interleave: independent reductions hide each other's latency).  Ranking by
+// logit equals ranking by softmax probability (exp is increasing).  Lane l
+// holds experts l*PL .. l*PL+PL-1, so "lowest lane, then lowest slot" is the
+// lowest id.  A round takes each lane's best remaining entry (first index on
+// equal keys), the wave maximum of those and the lowest lane holding it; that
+// lane removes the entry.  Lane j < rounds receives token n's j-th id and its
+// (biased) logit in my_id[n], my_val[n]; token 0's id of round `want` is
+// returned to every lane.  Tokens n >= nvalid read nothing (their results are
+// meaningless).
+template <int PL, int NT>
+__device__ __forceinline__ int wave_topk_n(const float *const *lg, const float *__restrict__ bias, int E, int nvalid,
+                                           int rounds, int want, int *my_id, float *my_val) {
+    const int lane = threadIdx.x & 63;
+    const Buf bb = make_buf(bias, bias ? (uint32_t)E * 4u : 0u);
+    uint32_t key[NT][PL];
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+        const Buf lb = make_buf(lg[n], n < nvalid ? (uint32_t)E * 4u : 0u);
+#pragma unroll
+        for (int i = 0; i < PL; ++i) {
+            const int e = lane * PL + i;
+            const uint32_t off = e < E ? (uint32_t)e * 4u : OOB;
+            const float v = __uint_as_float(ld32(lb, off)) + __uint_as_float(ld32(bb, off));
+            key[n][i] = e < E ? order_key(v) : 0u;
+        }
+        my_id[n] = -1;
+        my_val[n] = 0.f;
+    }
+    int sel = 0;
+    for (int j = 0; j < rounds; ++j) {
+        uint32_t best[NT];
+        int bi[NT];
+#pragma unroll
+        for (int n = 0; n < NT; ++n) {
+            best[n] = key[n][0];
+            bi[n] = 0;
+#pragma unroll
+            for (int i = 1; i < PL; ++i) {
+                const bool gt = key[n][i] > best[n];
+                best[n] = gt ? key[n][i] : best[n];
+                bi[n] = gt ? i : bi[n];
+            }
+        }
+        uint32_t m[NT];
+#pragma unroll
+        for (int n = 0; n < NT; ++n) m[n] = wave_max_u32(best[n]);
+#pragma unroll
+        for (int n = 0; n < NT; ++n) {
+            const uint64_t mask = __ballot(best[n] == m[n]);
+            const int winner = __ffsll((unsigned long long)mask) - 1;
+            const int wid = __builtin_amdgcn_readlane(lane * PL + bi[n], winner);
+            const bool pop = lane == winner;
+#pragma unroll
+            for (int i = 0; i < PL; ++i) key[n][i] = (pop && i == bi[n]) ? 0u : key[n][i];
+            const bool mine = lane == j;
+            my_id[n] = mine ? wid : my_id[n];
+            my_val[n] = mine ? __uint_as_float((m[n] & 0x80000000u) ? (m[n] & 0x7FFFFFFFu) : ~m[n]) : my_val[n];
+            if (n == 0) sel = j == want ? wid : sel;
+        }
+    }
+    return sel;
+}
+
+// One token (lane j < rounds receives the j-th id and logit; the id of round
+// `want` is returned to every lane).
 template <int PL>
 __device__ __forceinline__ int wave_topk(const float *__restrict__ lg, const float *__restrict__ bias, int E,
                                          int rounds, int want, int &my_id, float &my_val) {
-    const int lane = threadIdx.x & 63;
-    const Buf lb = make_buf(lg, (uint32_t)E * 4u);
-    const Buf bb = make_buf(bias, bias ? (uint32_t)E * 4u : 0u);
-    uint32_t key[PL];
-#pragma unroll
-    for (int i = 0; i < PL; ++i) {
-        const int e = lane * PL + i;
-        const uint32_t off = e < E ? (uint32_t)e * 4u : OOB;
-        const float v = __uint_as_float(ld32(lb, off)) + __uint_as_float(ld32(bb, off));
-        key[i] = e < E ? order_key(v) : 0u;
-    }
-    int sel = 0;
-    my_id = -1;
-    my_val = 0.f;
-    for (int j = 0; j < rounds; ++j) {
-        uint32_t best = key[0];
-        int bi = 0;
-#pragma unroll
-        for (int i = 1; i < PL; ++i) {
-            const bool gt = key[i] > best;
-            best = gt ? key[i] : best;
-            bi = gt ? i : bi;
-        }
-        const uint32_t m = wave_max_u32(best);
-        const uint64_t mask = __ballot(best == m);
-        const int winner = __ffsll((unsigned long long)mask) - 1;
-        const int wid = __builtin_amdgcn_readlane(lane * PL + bi, winner);
-        const bool pop = lane == winner;
-#pragma unroll
-        for (int i = 0; i < PL; ++i) key[i] = (pop && i == bi) ? 0u : key[i];
-        const bool mine = lane == j;
-        my_id = mine ? wid : my_id;
-        my_val = mine ? __uint_as_float((m & 0x80000000u) ? (m & 0x7FFFFFFFu) : ~m) : my_val;
-        sel = j == want ? wid : sel;
-    }
-    return sel;
+    const float *l[1] = {lg};
+    return wave_topk_n<PL, 1>(l, bias, E, 1, rounds, want, &my_id, &my_val);
+}
+
+// Inclusive prefix sum over the 64 lanes in lane order: shifts within each row
+// of 16 lanes, then the row totals by row broadcasts.  All lanes active.
+__device__ __forceinline__ int wave_incl_scan(int v) {
+    v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, true);   // row_shr:1
+    v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, true);   // row_shr:2
+    v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, true);   // row_shr:4
+    v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, true);   // row_shr:8
+    v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);  // row_bcast:15 into rows 1, 3
+    v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);  // row_bcast:31 into rows 2, 3
+    return v;
 }
 
 // ---------------------------------------------------------------- MFMA helpers

@@ -44,59 +44,77 @@ constexpr int KS_VALU = 2;
 
 // ================================================================= route + group
 
-// Wave-wide exclusive scans over the experts' pair counts cnt[E]: off[e] =
+// Exclusive scans over the experts' pair counts cnt[E] by one wave: off[e] =
 // where expert e's pair list starts; the group table lists the experts with
-// pairs in expert order (grp[0] = their number).
+// pairs in expert order (grp[0] = their number).  Lane l owns experts l*PL ..
+// l*PL+PL-1; the counts (sums < 2^17) and the has-pairs flags (sums < 2^11)
+// share one 32-bit scan.
+template <int PL>
 __device__ __forceinline__ void scan_groups(const int *cnt, int *off, int32_t *grp, int E, int Gmax, int lane) {
-    int run = 0, grun = 0;
-    for (int base = 0; base < E; base += 64) {
-        const int e = base + lane;
-        const int c = e < E ? cnt[e] : 0;
-        const int nz = c > 0 ? 1 : 0;
-        int inc = c, ginc = nz;
+    constexpr int GSH = 17;
+    int c[PL], loc = 0;
 #pragma unroll
-        for (int d = 1; d < 64; d <<= 1) {
-            const int u = __shfl_up(inc, d), gu = __shfl_up(ginc, d);
-            if (lane >= d) inc += u, ginc += gu;
-        }
-        const int ex = run + inc - c, gex = grun + ginc - nz;
+    for (int i = 0; i < PL; ++i) {
+        const int e = lane * PL + i;
+        c[i] = e < E ? cnt[e] : 0;
+        loc += c[i] + (c[i] > 0 ? (1 << GSH) : 0);
+    }
+    const int inc = wave_incl_scan(loc);
+    int run = inc - loc;
+#pragma unroll
+    for (int i = 0; i < PL; ++i) {
+        const int e = lane * PL + i;
+        const int ex = run & ((1 << GSH) - 1), gex = run >> GSH;
         if (e < E) off[e] = ex;
-        if (nz) {
+        if (c[i] > 0) {
             grp[1 + gex] = e;
             grp[1 + Gmax + gex] = ex;
-            grp[1 + 2 * Gmax + gex] = c;
+            grp[1 + 2 * Gmax + gex] = c[i];
         }
-        run += __shfl(inc, 63);
-        grun += __shfl(ginc, 63);
+        run += c[i] + (c[i] > 0 ? (1 << GSH) : 0);
     }
-    if (lane == 0) grp[0] = grun;
+    if (lane == 63) grp[0] = inc >> GSH;
 }
 
-// Top-k and routing weights of token t by wave `lane`s (K lanes hold the
-// selected ids and weights); returns the lane's expert (-1 for lanes >= K).
+// Top-k and routing weights of tokens t and t2 (t2 < 0: none) by one wave,
+// their rankings interleaved; lanes j < K write the j-th id and weight of each
+// and get them back in e[0], e[1] (-1 for lanes >= K, invalid supplied ids and
+// the missing token).
 template <int PL>
-__device__ __forceinline__ int route_token(const GroupArgs &a, int t, int lane) {
+__device__ __forceinline__ void route_tokens2(const GroupArgs &a, int t, int t2, int lane, int (&e)[2]) {
     const int K = a.K;
+    const int tt[2] = {t, t2};
     if (a.route) {
-        int my_id;
-        float my_val;
-        wave_topk<PL>(a.logits + (size_t)t * a.lstride, a.bias, a.E, K, 0, my_id, my_val);
-        const float vmax = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_val), 0));
-        const float ex = lane < K ? expf(my_val - vmax) : 0.f;
-        const float sum = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(group_sum<64>(ex)), 63));
-        if (lane < K) {
-            const float w = ex / sum;
-            a.ids_ws[t * K + lane] = my_id;
-            a.w_ws[t * K + lane] = w;
-            if (a.ids_user) a.ids_user[t * K + lane] = my_id;
-            if (a.w_user) a.w_user[t * K + lane] = w;
-            return my_id;
+        const float *lg[2] = {a.logits + (size_t)t * a.lstride, a.logits + (size_t)(t2 >= 0 ? t2 : t) * a.lstride};
+        int my_id[2];
+        float my_val[2];
+        wave_topk_n<PL, 2>(lg, a.bias, a.E, t2 >= 0 ? 2 : 1, K, 0, my_id, my_val);
+#pragma unroll
+        for (int n = 0; n < 2; ++n) {
+            e[n] = -1;
+            if (tt[n] < 0) continue;
+            const float vmax = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_val[n]), 0));
+            const float ex = lane < K ? expf(my_val[n] - vmax) : 0.f;
+            const float sum = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(group_sum<64>(ex)), 63));
+            if (lane < K) {
+                const float w = ex / sum;
+                const int o = tt[n] * K + lane;
+                a.ids_ws[o] = my_id[n];
+                a.w_ws[o] = w;
+                if (a.ids_user) a.ids_user[o] = my_id[n];
+                if (a.w_user) a.w_user[o] = w;
+                e[n] = my_id[n];
+            }
         }
-        return -1;
+        return;
     }
-    if (lane >= K) return -1;
-    const int e = a.ids_in[t * K + lane];
-    return (e >= 0 && e < a.E) ? e : -1;  // invalid ids join no group
+#pragma unroll
+    for (int n = 0; n < 2; ++n) {
+        e[n] = -1;
+        if (tt[n] < 0 || lane >= K) continue;
+        const int v = a.ids_in[tt[n] * K + lane];
+        e[n] = (v >= 0 && v < a.E) ? v : -1;  // invalid ids join no group
+    }
 }
 
 template <int PL>
@@ -111,9 +129,14 @@ __global__ __launch_bounds__(1024) void k_moe_route_group(GroupArgs a) {
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6), nw = blockDim.x >> 6;
     for (int i = tid; i < E; i += blockDim.x) cnt[i] = 0;
 
-    for (int t = wv; t < T; t += nw) {
-        const int e = route_token<PL>(a, t, lane);
-        if (lane < K) e_of[t * K + lane] = e;
+    for (int t = wv; t < T; t += 2 * nw) {  // tokens t and t + nw, ranked together
+        const int t2 = t + nw < T ? t + nw : -1;
+        int e[2];
+        route_tokens2<PL>(a, t, t2, lane, e);
+        if (lane < K) {
+            e_of[t * K + lane] = e[0];
+            if (t2 >= 0) e_of[t2 * K + lane] = e[1];
+        }
     }
     __syncthreads();
     // position of each pair inside its expert's group (LDS atomics: the order
@@ -125,7 +148,7 @@ __global__ __launch_bounds__(1024) void k_moe_route_group(GroupArgs a) {
     __syncthreads();
     // exclusive scans over the experts: where each expert's pair list starts,
     // and the group index of each active expert (groups in expert order)
-    if (wv == 0) scan_groups(cnt, off, a.grp, E, a.Gmax, lane);
+    if (wv == 0) scan_groups<PL>(cnt, off, a.grp, E, a.Gmax, lane);
     __syncthreads();
     for (int p = tid; p < P; p += blockDim.x) {
         const int e = e_of[p];
@@ -148,11 +171,17 @@ __global__ __launch_bounds__(256) void k_route_topk(RouteArgs r) {
     __syncthreads();
     const int t0 = blockIdx.x * r.tpb;
     const int t1 = min(t0 + r.tpb, a.T);
-    for (int t = t0 + wv; t < t1; t += 4) {
-        const int e = route_token<PL>(a, t, lane);
+    for (int t = t0 + wv; t < t1; t += 8) {  // tokens t and t + 4, ranked together
+        const int t2 = t + 4 < t1 ? t + 4 : -1;
+        int e[2];
+        route_tokens2<PL>(a, t, t2, lane, e);
         if (lane < K) {
-            r.e_of[t * K + lane] = e;
-            if (e >= 0) atomicAdd(&hist[e], 1);
+            r.e_of[t * K + lane] = e[0];
+            if (e[0] >= 0) atomicAdd(&hist[e[0]], 1);
+            if (t2 >= 0) {
+                r.e_of[t2 * K + lane] = e[1];
+                if (e[1] >= 0) atomicAdd(&hist[e[1]], 1);
+            }
         }
     }
     __syncthreads();
@@ -183,7 +212,7 @@ __global__ __launch_bounds__(1024) void k_route_scan(RouteArgs r) {
     }
     __syncthreads();
     if (tid < 64) {
-        scan_groups(tot, off, r.g.grp, E, Gmax, tid);
+        scan_groups<16>(tot, off, r.g.grp, E, Gmax, tid);  // (any E up to 1024)
         // the routed groups' 64-column tiles in group order (groups = experts with pairs)
         int crun = 0, grun = 0;
         for (int base = 0; base < E; base += 64) {
