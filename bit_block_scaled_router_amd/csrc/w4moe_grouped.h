@@ -25,6 +25,7 @@ struct GroupArgs {
     int32_t *grp;
     int32_t *pairs;
     int E, K, T, P, Gmax, lstride, route;
+    int mfma_min;          // one-launch grouping: groups of >= 16 pairs first, then >= mfma_min, then the rest
 };
 
 // Column tiles of the large-batch kernels: the routed groups' 64-column tiles in

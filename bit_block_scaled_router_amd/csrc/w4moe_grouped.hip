@@ -46,32 +46,52 @@ constexpr int KS_VALU = 2;
 
 // Exclusive scans over the experts' pair counts cnt[E] by one wave: off[e] =
 // where expert e's pair list starts; the group table lists the experts with
-// pairs in expert order (grp[0] = their number).  Lane l owns experts l*PL ..
-// l*PL+PL-1; the counts (sums < 2^17) and the has-pairs flags (sums < 2^11)
-// share one 32-bit scan.
-template <int PL>
-__device__ __forceinline__ void scan_groups(const int *cnt, int *off, int32_t *grp, int E, int Gmax, int lane) {
-    constexpr int GSH = 17;
-    int c[PL], loc = 0;
+// pairs (grp[0] = their number).  Lane l owns experts l*PL .. l*PL+PL-1; the
+// counts (sums < 2^17) and the has-pairs flags (sums < 2^11) share one 32-bit
+// scan.  ORDER = false: groups in expert order.  ORDER = true: by size class,
+// groups of at least 16 pairs, then of at least `mid`, then the rest (expert
+// order within a class), so that the expert launches, which walk their units in
+// table order, start the longest units first.
+template <int PL, bool ORDER>
+__device__ __forceinline__ void scan_groups(const int *cnt, int *off, int32_t *grp, int E, int Gmax, int lane,
+                                            int mid = 0) {
+    constexpr int GSH = 17, CSH = 11, BIG = 16;
+    auto cls = [&](int c) { return ORDER ? (c >= BIG ? 1 : 0) + (c >= mid && c < BIG ? (1 << CSH) : 0) : 0; };
+    int c[PL], loc = 0, cl = 0;
 #pragma unroll
     for (int i = 0; i < PL; ++i) {
         const int e = lane * PL + i;
         c[i] = e < E ? cnt[e] : 0;
         loc += c[i] + (c[i] > 0 ? (1 << GSH) : 0);
+        cl += cls(c[i]);
     }
     const int inc = wave_incl_scan(loc);
     int run = inc - loc;
+    int crun = 0, n0 = 0, n1 = 0;
+    if constexpr (ORDER) {  // class ranks: large groups in the low field, middle ones above
+        const int cinc = wave_incl_scan(cl);
+        crun = cinc - cl;
+        const int tot = __builtin_amdgcn_readlane(cinc, 63);
+        n0 = tot & ((1 << CSH) - 1);
+        n1 = tot >> CSH;
+    }
 #pragma unroll
     for (int i = 0; i < PL; ++i) {
         const int e = lane * PL + i;
         const int ex = run & ((1 << GSH) - 1), gex = run >> GSH;
         if (e < E) off[e] = ex;
         if (c[i] > 0) {
-            grp[1 + gex] = e;
-            grp[1 + Gmax + gex] = ex;
-            grp[1 + 2 * Gmax + gex] = c[i];
+            int g = gex;
+            if constexpr (ORDER) {
+                const int r0 = crun & ((1 << CSH) - 1), r1 = crun >> CSH;
+                g = c[i] >= BIG ? r0 : c[i] >= mid ? n0 + r1 : n0 + n1 + (gex - r0 - r1);
+            }
+            grp[1 + g] = e;
+            grp[1 + Gmax + g] = ex;
+            grp[1 + 2 * Gmax + g] = c[i];
         }
         run += c[i] + (c[i] > 0 ? (1 << GSH) : 0);
+        crun += cls(c[i]);
     }
     if (lane == 63) grp[0] = inc >> GSH;
 }
@@ -147,8 +167,8 @@ __global__ __launch_bounds__(1024) void k_moe_route_group(GroupArgs a) {
     }
     __syncthreads();
     // exclusive scans over the experts: where each expert's pair list starts,
-    // and the group index of each active expert (groups in expert order)
-    if (wv == 0) scan_groups<PL>(cnt, off, a.grp, E, a.Gmax, lane);
+    // and the group index of each active expert (groups by size class, largest first)
+    if (wv == 0) scan_groups<PL, true>(cnt, off, a.grp, E, a.Gmax, lane, a.mfma_min);
     __syncthreads();
     for (int p = tid; p < P; p += blockDim.x) {
         const int e = e_of[p];
@@ -212,7 +232,7 @@ __global__ __launch_bounds__(1024) void k_route_scan(RouteArgs r) {
     }
     __syncthreads();
     if (tid < 64) {
-        scan_groups<16>(tot, off, r.g.grp, E, Gmax, tid);  // (any E up to 1024)
+        scan_groups<16, false>(tot, off, r.g.grp, E, Gmax, tid);  // (any E up to 1024; column tiles need expert order)
         // the routed groups' 64-column tiles in group order (groups = experts with pairs)
         int crun = 0, grun = 0;
         for (int base = 0; base < E; base += 64) {

@@ -1120,6 +1120,7 @@ int run_grouped(const moe_w4a16_layer *Lr, const MoEPlan &p, const uint16_t *x, 
     ga.ids_user = route ? topk_ids : nullptr, ga.w_user = route ? topk_w : nullptr;
     ga.grp = grp, ga.pairs = pairs;
     ga.E = p.E, ga.K = p.K, ga.T = p.T, ga.P = p.P, ga.Gmax = p.Gmax, ga.lstride = p.lstride, ga.route = route ? 1 : 0;
+    ga.mfma_min = W4_MFMA_MIN;
     if (p.mx) {
         // x -> MXFP8 (its own stage, recorded between router and grouping)
         uint8_t *xq = (uint8_t *)(wsb + p.off_xq);
