@@ -242,8 +242,8 @@ def stage_bytes(shape, distinct, n_stages=3):
     return {
         "k_router": router,
         "k_moe_route_group": T * E * 4 + T * K * 8 + rows * 4,
-        "k_moe_gw13": nexp * w13 + T * H * 2 + rows * I * 4,
-        "k_moe_gw2": nexp * w2 + rows * I * 4 + rows * H * 4,
+        "k_moe_gw13": nexp * w13 + dw13 + T * H * 2 + rows * I * 4,
+        "k_moe_gw2": nexp * w2 + dw2 + rows * I * 4 + rows * H * 4,
         "k_moe_gcombine": rows * H * 4 + T * K * 8 + T * H * 2,
     }
 
@@ -377,12 +377,12 @@ def workload_shapes(synth):
             "gemv-lmhead": synth.GEMV_LMHEAD, "qwen-t1-bf16shared": synth.QWEN_MOE_T1_BF16SH,
             "qwen-t1-mxfp4": synth.QWEN_MOE_T1_MX, "qwen-t32-mxfp4": synth.QWEN_MOE_T32_MX,
             "qwen-prefill": synth.QWEN_MOE_PREFILL, "qwen-prefill-mxfp4": synth.QWEN_MOE_PREFILL_MX,
-            "qwen-t32-nvfp4": synth.QWEN_MOE_T32_NVFP4}
+            "qwen-t32-nvfp4": synth.QWEN_MOE_T32_NVFP4, "qwen-t32-bf16shared": synth.QWEN_MOE_T32_BF16SH}
 
 
 WORKLOADS = ["qwen-t1", "qwen-t32", "tiny", "gemv-e2m1", "gemv-int4", "qwen-t1-nvfp4", "gemv-nvfp4", "gemv-lmhead",
              "qwen-t1-bf16shared", "qwen-t1-mxfp4", "qwen-t32-mxfp4", "qwen-prefill", "qwen-prefill-mxfp4",
-             "qwen-t32-nvfp4"]
+             "qwen-t32-nvfp4", "qwen-t32-bf16shared"]
 
 
 def run_moe(args, torch, w4, wl, synth):

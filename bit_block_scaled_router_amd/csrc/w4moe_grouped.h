@@ -61,6 +61,7 @@ struct GW13Args {
     const int32_t *ctg;     // column tiles (large-batch kernels only)
     int fmt;                // FMT_E2M1 or FMT_NVFP4 (gw13 / gw2)
     const float *gs, *s_gs; // NVFP4 global scales: routed [E], shared [1]
+    int s_bf16;             // the shared expert is bf16 (s_codes = bf16 rows, no scales)
 };
 
 struct GW2Args {
@@ -77,6 +78,7 @@ struct GW2Args {
     const int32_t *ctg;     // column tiles (large-batch kernels only)
     int fmt;                // FMT_E2M1 or FMT_NVFP4
     const float *gs, *s_gs; // NVFP4 global scales: routed [E], shared [1]
+    int s_bf16;             // the shared expert is bf16 (s_codes = bf16 rows, no scales)
 };
 
 struct GCombineArgs {

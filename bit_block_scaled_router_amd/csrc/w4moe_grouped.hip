@@ -40,7 +40,8 @@ namespace w4k {
 constexpr int KS_VALU = 2;
 #ifndef W4_GW_MINBLK
 #define W4_GW_MINBLK 3  // blocks per CU the batched W13 / W2 kernels are compiled to fit
-#endif                  // (W2 with I > 512 keeps its registers: fitting 3 would spill)
+#endif                  // (W2 with I > 512, and layers with a bf16 shared expert, fit 2 or 1:
+                        // fitting 3 would spill)
 
 // ================================================================= route + group
 
@@ -326,8 +327,10 @@ __device__ __forceinline__ int token_of(int p, int P, int K) { return p < P ? p 
 // the matching up rows).  FMT: E2M1 (FP16 scale per 16: every weight is two
 // exact bf16 terms) or NVFP4 (UE4M3 scale per 16: code x scale has at most 6
 // significant bits, one exact bf16 term; the matrix's global scale multiplies
-// the gate and up sums).
-template <int FMT, int L>
+// the gate and up sums).  SB: the layer's shared expert is bf16 (its rows are
+// the MFMA operands; a separate instantiation keeps the 4-bit-only kernels'
+// register budget).
+template <int FMT, int L, bool SB>
 __device__ __forceinline__ void gw13_unit(const GW13Args &a, int gs, int tile, float (*red)[16][64]) {
     using SC = typename std::conditional<FMT == FMT_NVFP4, uint8_t, uint16_t>::type;
     constexpr int RG = 64 / L;
@@ -338,131 +341,161 @@ __device__ __forceinline__ void gw13_unit(const GW13Args &a, int gs, int tile, f
     const size_t mat_codes = (size_t)(2 * I) * (H >> 1), mat_scales = (size_t)(2 * I) * spr;
     const GroupView<SC> gv = group_view(a.grp, gs, a.Gmax, a.P, a.T, a.codes, reinterpret_cast<const SC *>(a.scales),
                                         mat_codes, mat_scales, a.s_codes, reinterpret_cast<const SC *>(a.s_scales));
-    const Buf cb = make_buf(gv.codes, (uint32_t)mat_codes);
-    const Buf sb = make_buf(gv.scales, (uint32_t)(mat_scales * sizeof(SC)));
+    // a bf16 shared expert: its rows are the MFMA operands themselves (the
+    // MFMA branch takes every size of that group)
+    const bool sbf = SB && gv.e < 0;
+    const Buf cb = make_buf(gv.codes, (uint32_t)(sbf ? 4 * mat_codes : mat_codes));
+    const Buf sb = make_buf(gv.scales, sbf ? 0u : (uint32_t)(mat_scales * sizeof(SC)));
     float gsc = 1.f;  // NVFP4 global scale of the matrix
-    if constexpr (FMT == FMT_NVFP4) gsc = gv.e < 0 ? ld_uniform(a.s_gs, 0) : ld_uniform(a.gs, gv.e);
+    if constexpr (FMT == FMT_NVFP4) gsc = sbf ? 1.f : gv.e < 0 ? ld_uniform(a.s_gs, 0) : ld_uniform(a.gs, gv.e);
     const int i0 = tile * 16;  // first gate row of the tile
     const int *plist = a.pairs + gv.off;
 
-    if (gv.m >= a.mfma_min) {
-        // ---- MFMA: 16 gate + 16 up rows x 16-token column tiles; the 128-wide K
-        // chunks are dealt round-robin to the 4 waves and summed in wave order.
-        const int r = lane & 15, q = lane >> 4;
-        const bool rg_ok = i0 + r < I;
-        const uint32_t rowg = (uint32_t)(i0 + r), rowu = (uint32_t)(I + i0 + r);
-        const int nchunks = H >> 7;
-        const Buf xall = make_buf(a.x, (uint32_t)a.T * (uint32_t)H * 2u);
-        for (int n0 = 0; n0 < gv.m; n0 += 32) {
-            // two 16-column tiles: pairs n0 + lane%16 and n0 + 16 + lane%16
-            int pr[2], tk[2];
-            bool pv[2];
-#pragma unroll
-            for (int nt = 0; nt < 2; ++nt) {
-                const int idx = n0 + nt * 16 + r;
-                pv[nt] = idx < gv.m;
-                pr[nt] = pv[nt] ? plist[idx] : 0;
-                tk[nt] = token_of(pr[nt], a.P, a.K);
-            }
-            const bool two = n0 + 16 < gv.m;  // second column tile in use (uniform)
-            f32x4 ag[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-            f32x4 au[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-            for (int c = wv; c < nchunks; c += 4) {
-                const int k0 = c * 128 + 32 * q;  // this lane's 32 elements
-                // B: 32 activations of each column token
-                uint4 xb[2][4];
-#pragma unroll
-                for (int nt = 0; nt < 2; ++nt) {
-                    const uint32_t xo = (uint32_t)(tk[nt] * H + k0) * 2u;
-#pragma unroll
-                    for (int s = 0; s < 4; ++s)
-                        xb[nt][s] = (nt == 0 || two) ? ld128(xall, pv[nt] ? xo + 16u * s : OOB) : make_uint4(0, 0, 0, 0);
-                }
-                const uint4 cg = ld128(cb, rg_ok ? rowg * (uint32_t)(H >> 1) + (uint32_t)(k0 >> 1) : OOB);
-                const uint4 cu = ld128(cb, rg_ok ? rowu * (uint32_t)(H >> 1) + (uint32_t)(k0 >> 1) : OOB);
-                const uint32_t sg = ld_scales<FMT>(sb, rg_ok ? scale_off<FMT>(rowg * spr, k0) : OOB);
-                const uint32_t su = ld_scales<FMT>(sb, rg_ok ? scale_off<FMT>(rowu * spr, k0) : OOB);
-                const uint32_t cgw[4] = {cg.x, cg.y, cg.z, cg.w}, cuw[4] = {cu.x, cu.y, cu.z, cu.w};
-#pragma unroll
-                for (int s = 0; s < 4; ++s) {
-                    if constexpr (FMT == FMT_NVFP4) {
-                        const f32x2 sgv = block_scales2<FMT>(sg), suv = block_scales2<FMT>(su);
-                        const bf16x8 ag1 = e2m1x8_scaled(cgw[s], s < 2 ? sgv.x : sgv.y);
-                        const bf16x8 au1 = e2m1x8_scaled(cuw[s], s < 2 ? suv.x : suv.y);
-#pragma unroll
-                        for (int nt = 0; nt < 2; ++nt) {
-                            if (nt == 1 && !two) break;
-                            const bf16x8 b = __builtin_bit_cast(bf16x8, xb[nt][s]);
-                            ag[nt] = mfma16x16x32(ag1, b, ag[nt]);
-                            au[nt] = mfma16x16x32(au1, b, au[nt]);
-                        }
-                    } else {
-                        float gh, gl, uh, ul;
-                        split_scale(f16_bits_to_f32(s < 2 ? sg : (sg >> 16)), gh, gl);
-                        split_scale(f16_bits_to_f32(s < 2 ? su : (su >> 16)), uh, ul);
-                        bf16x8 agh, agl, auh, aul;
-                        e2m1x8_split(cgw[s], gh, gl, agh, agl);
-                        e2m1x8_split(cuw[s], uh, ul, auh, aul);
-#pragma unroll
-                        for (int nt = 0; nt < 2; ++nt) {
-                            if (nt == 1 && !two) break;
-                            const bf16x8 b = __builtin_bit_cast(bf16x8, xb[nt][s]);
-                            ag[nt] = mfma16x16x32(agh, b, ag[nt]);
-                            ag[nt] = mfma16x16x32(agl, b, ag[nt]);
-                            au[nt] = mfma16x16x32(auh, b, au[nt]);
-                            au[nt] = mfma16x16x32(aul, b, au[nt]);
-                        }
-                    }
-                }
-            }
-            // fixed-order sum of the four K partials
-            if (wv > 0) {
-#pragma unroll
-                for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        red[wv - 1][nt * 8 + j][lane] = ag[nt][j];
-                        red[wv - 1][nt * 8 + 4 + j][lane] = au[nt][j];
-                    }
-            }
-            __syncthreads();
-            if (wv == 0) {
-#pragma unroll
-                for (int w = 0; w < 3; ++w)
-#pragma unroll
-                    for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-                        for (int j = 0; j < 4; ++j) {
-                            ag[nt][j] += red[w][nt * 8 + j][lane];
-                            au[nt][j] += red[w][nt * 8 + 4 + j][lane];
-                        }
-                // lane holds rows i0 + 4q + j of column r
-#pragma unroll
+    if (gv.m >= a.mfma_min || sbf) {
+        auto mfma = [&](auto SBFc) {
+            constexpr bool SBF = decltype(SBFc)::value;
+            // ---- MFMA: 16 gate + 16 up rows x 16-token column tiles; the 128-wide K
+            // chunks are dealt round-robin to the 4 waves and summed in wave order.
+            const int r = lane & 15, q = lane >> 4;
+            const bool rg_ok = i0 + r < I;
+            const uint32_t rowg = (uint32_t)(i0 + r), rowu = (uint32_t)(I + i0 + r);
+            const int nchunks = H >> 7;
+            const Buf xall = make_buf(a.x, (uint32_t)a.T * (uint32_t)H * 2u);
+            for (int n0 = 0; n0 < gv.m; n0 += 32) {
+                // two 16-column tiles: pairs n0 + lane%16 and n0 + 16 + lane%16
+                int pr[2], tk[2];
+                bool pv[2];
+    #pragma unroll
                 for (int nt = 0; nt < 2; ++nt) {
                     const int idx = n0 + nt * 16 + r;
-                    if (idx < gv.m) {
-                        const int p = plist[idx];
-                        float hv[4];
-#pragma unroll
-                        for (int j = 0; j < 4; ++j) {
-                            float gg = ag[nt][j], uu = au[nt][j];
-                            if constexpr (FMT == FMT_NVFP4) gg *= gsc, uu *= gsc;
-                            hv[j] = (gg / (1.f + expf(-gg))) * uu;
+                    pv[nt] = idx < gv.m;
+                    pr[nt] = pv[nt] ? plist[idx] : 0;
+                    tk[nt] = token_of(pr[nt], a.P, a.K);
+                }
+                const bool two = n0 + 16 < gv.m;  // second column tile in use (uniform)
+                f32x4 ag[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+                f32x4 au[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+                for (int c = wv; c < nchunks; c += 4) {
+                    const int k0 = c * 128 + 32 * q;  // this lane's 32 elements
+                    // B: 32 activations of each column token
+                    uint4 xb[2][4];
+    #pragma unroll
+                    for (int nt = 0; nt < 2; ++nt) {
+                        const uint32_t xo = (uint32_t)(tk[nt] * H + k0) * 2u;
+    #pragma unroll
+                        for (int s = 0; s < 4; ++s)
+                            xb[nt][s] = (nt == 0 || two) ? ld128(xall, pv[nt] ? xo + 16u * s : OOB) : make_uint4(0, 0, 0, 0);
+                    }
+                    if constexpr (SBF) {  // bf16 rows, 8 weights per MFMA step
+                        const uint32_t rb = (uint32_t)H * 2u;
+    #pragma unroll
+                        for (int s = 0; s < 4; ++s) {
+                            const uint32_t ko = (uint32_t)(k0 + 8 * s) * 2u;
+                            const bf16x8 wg = __builtin_bit_cast(bf16x8, ld128(cb, rg_ok ? rowg * rb + ko : OOB));
+                            const bf16x8 wu = __builtin_bit_cast(bf16x8, ld128(cb, rg_ok ? rowu * rb + ko : OOB));
+    #pragma unroll
+                            for (int nt = 0; nt < 2; ++nt) {
+                                if (nt == 1 && !two) break;
+                                const bf16x8 b = __builtin_bit_cast(bf16x8, xb[nt][s]);
+                                ag[nt] = mfma16x16x32(wg, b, ag[nt]);
+                                au[nt] = mfma16x16x32(wu, b, au[nt]);
+                            }
                         }
-                        // I is a multiple of 128 (host check): rows i0 + 4q .. +3 all exist
-                        uint16_t bh[4], bl[4];
-#pragma unroll
-                        for (int j = 0; j < 4; ++j) split_bf16(hv[j], bh[j], bl[j]);
-                        const size_t o = (size_t)p * I + i0 + 4 * q;
-                        *reinterpret_cast<uint2 *>(a.h_hi + o) =
-                            make_uint2(bh[0] | ((uint32_t)bh[1] << 16), bh[2] | ((uint32_t)bh[3] << 16));
-                        *reinterpret_cast<uint2 *>(a.h_lo + o) =
-                            make_uint2(bl[0] | ((uint32_t)bl[1] << 16), bl[2] | ((uint32_t)bl[3] << 16));
+                        continue;
+                    }
+                    const uint4 cg = ld128(cb, rg_ok ? rowg * (uint32_t)(H >> 1) + (uint32_t)(k0 >> 1) : OOB);
+                    const uint4 cu = ld128(cb, rg_ok ? rowu * (uint32_t)(H >> 1) + (uint32_t)(k0 >> 1) : OOB);
+                    const uint32_t sg = ld_scales<FMT>(sb, rg_ok ? scale_off<FMT>(rowg * spr, k0) : OOB);
+                    const uint32_t su = ld_scales<FMT>(sb, rg_ok ? scale_off<FMT>(rowu * spr, k0) : OOB);
+                    const uint32_t cgw[4] = {cg.x, cg.y, cg.z, cg.w}, cuw[4] = {cu.x, cu.y, cu.z, cu.w};
+    #pragma unroll
+                    for (int s = 0; s < 4; ++s) {
+                        if constexpr (FMT == FMT_NVFP4) {
+                            const f32x2 sgv = block_scales2<FMT>(sg), suv = block_scales2<FMT>(su);
+                            const bf16x8 ag1 = e2m1x8_scaled(cgw[s], s < 2 ? sgv.x : sgv.y);
+                            const bf16x8 au1 = e2m1x8_scaled(cuw[s], s < 2 ? suv.x : suv.y);
+    #pragma unroll
+                            for (int nt = 0; nt < 2; ++nt) {
+                                if (nt == 1 && !two) break;
+                                const bf16x8 b = __builtin_bit_cast(bf16x8, xb[nt][s]);
+                                ag[nt] = mfma16x16x32(ag1, b, ag[nt]);
+                                au[nt] = mfma16x16x32(au1, b, au[nt]);
+                            }
+                        } else {
+                            float gh, gl, uh, ul;
+                            split_scale(f16_bits_to_f32(s < 2 ? sg : (sg >> 16)), gh, gl);
+                            split_scale(f16_bits_to_f32(s < 2 ? su : (su >> 16)), uh, ul);
+                            bf16x8 agh, agl, auh, aul;
+                            e2m1x8_split(cgw[s], gh, gl, agh, agl);
+                            e2m1x8_split(cuw[s], uh, ul, auh, aul);
+    #pragma unroll
+                            for (int nt = 0; nt < 2; ++nt) {
+                                if (nt == 1 && !two) break;
+                                const bf16x8 b = __builtin_bit_cast(bf16x8, xb[nt][s]);
+                                ag[nt] = mfma16x16x32(agh, b, ag[nt]);
+                                ag[nt] = mfma16x16x32(agl, b, ag[nt]);
+                                au[nt] = mfma16x16x32(auh, b, au[nt]);
+                                au[nt] = mfma16x16x32(aul, b, au[nt]);
+                            }
+                        }
                     }
                 }
+                // fixed-order sum of the four K partials
+                if (wv > 0) {
+    #pragma unroll
+                    for (int nt = 0; nt < 2; ++nt)
+    #pragma unroll
+                        for (int j = 0; j < 4; ++j) {
+                            red[wv - 1][nt * 8 + j][lane] = ag[nt][j];
+                            red[wv - 1][nt * 8 + 4 + j][lane] = au[nt][j];
+                        }
+                }
+                __syncthreads();
+                if (wv == 0) {
+    #pragma unroll
+                    for (int w = 0; w < 3; ++w)
+    #pragma unroll
+                        for (int nt = 0; nt < 2; ++nt)
+    #pragma unroll
+                            for (int j = 0; j < 4; ++j) {
+                                ag[nt][j] += red[w][nt * 8 + j][lane];
+                                au[nt][j] += red[w][nt * 8 + 4 + j][lane];
+                            }
+                    // lane holds rows i0 + 4q + j of column r
+    #pragma unroll
+                    for (int nt = 0; nt < 2; ++nt) {
+                        const int idx = n0 + nt * 16 + r;
+                        if (idx < gv.m) {
+                            const int p = plist[idx];
+                            float hv[4];
+    #pragma unroll
+                            for (int j = 0; j < 4; ++j) {
+                                float gg = ag[nt][j], uu = au[nt][j];
+                                if constexpr (FMT == FMT_NVFP4) gg *= gsc, uu *= gsc;
+                                hv[j] = (gg / (1.f + expf(-gg))) * uu;
+                            }
+                            // I is a multiple of 128 (host check): rows i0 + 4q .. +3 all exist
+                            uint16_t bh[4], bl[4];
+    #pragma unroll
+                            for (int j = 0; j < 4; ++j) split_bf16(hv[j], bh[j], bl[j]);
+                            const size_t o = (size_t)p * I + i0 + 4 * q;
+                            *reinterpret_cast<uint2 *>(a.h_hi + o) =
+                                make_uint2(bh[0] | ((uint32_t)bh[1] << 16), bh[2] | ((uint32_t)bh[3] << 16));
+                            *reinterpret_cast<uint2 *>(a.h_lo + o) =
+                                make_uint2(bl[0] | ((uint32_t)bl[1] << 16), bl[2] | ((uint32_t)bl[3] << 16));
+                        }
+                    }
+                }
+                __syncthreads();
             }
-            __syncthreads();
+        };
+        if constexpr (SB) {
+            if (sbf) {
+                mfma(std::true_type());
+                return;
+            }
         }
+        mfma(std::false_type());
         return;
     }
 
@@ -522,21 +555,21 @@ __device__ __forceinline__ void gw13_unit(const GW13Args &a, int gs, int tile, f
 
 // Blocks walk the work units (group slot x row tile) with a grid stride, so the
 // grid needs no bound on the number of active experts.
-template <int FMT, int L>
-__global__ __launch_bounds__(256, W4_GW_MINBLK) void k_moe_gw13(GW13Args a) {
+template <int FMT, int L, bool SB>
+__global__ __launch_bounds__(256, SB ? 2 : W4_GW_MINBLK) void k_moe_gw13(GW13Args a) {
     __shared__ float red[3][16][64];  // MFMA K-split partials of waves 1..3
     const int nu = unit_count(a.grp, a.s_codes != nullptr, a.tiles);
     for (int u = blockIdx.x; u < nu; u += gridDim.x) {
         const int gs = u / a.tiles;
-        gw13_unit<FMT, L>(a, gs, u - gs * a.tiles, red);
+        gw13_unit<FMT, L, SB>(a, gs, u - gs * a.tiles, red);
     }
 }
 
 // ================================================================= grouped W2
 
 // One work unit of the down launch: group slot gs, output rows 64*tile .. +64.
-// FMT as in gw13_unit (NVFP4: one bf16 weight term, sums times the global scale).
-template <int FMT, int L>
+// FMT, SB as in gw13_unit (NVFP4: one bf16 weight term, sums times the global scale).
+template <int FMT, int L, bool SB>
 __device__ __forceinline__ void gw2_unit(const GW2Args &a, int gs, int tile, float (*red)[4][8][64]) {
     using SC = typename std::conditional<FMT == FMT_NVFP4, uint8_t, uint16_t>::type;
     constexpr int RG = 64 / L;
@@ -547,127 +580,159 @@ __device__ __forceinline__ void gw2_unit(const GW2Args &a, int gs, int tile, flo
     const size_t mat_codes = (size_t)H * (I >> 1), mat_scales = (size_t)H * spr;
     const GroupView<SC> gv = group_view(a.grp, gs, a.Gmax, a.P, a.T, a.codes, reinterpret_cast<const SC *>(a.scales),
                                         mat_codes, mat_scales, a.s_codes, reinterpret_cast<const SC *>(a.s_scales));
-    const Buf cb = make_buf(gv.codes, (uint32_t)mat_codes);
-    const Buf sb = make_buf(gv.scales, (uint32_t)(mat_scales * sizeof(SC)));
+    const bool sbf = SB && gv.e < 0;  // bf16 shared expert (MFMA branch at every size)
+    const Buf cb = make_buf(gv.codes, (uint32_t)(sbf ? 4 * mat_codes : mat_codes));
+    const Buf sb = make_buf(gv.scales, sbf ? 0u : (uint32_t)(mat_scales * sizeof(SC)));
     float gsc = 1.f;  // NVFP4 global scale of the matrix
-    if constexpr (FMT == FMT_NVFP4) gsc = gv.e < 0 ? ld_uniform(a.s_gs, 0) : ld_uniform(a.gs, gv.e);
+    if constexpr (FMT == FMT_NVFP4) gsc = sbf ? 1.f : gv.e < 0 ? ld_uniform(a.s_gs, 0) : ld_uniform(a.gs, gv.e);
     const int *plist = a.pairs + gv.off;
     const uint32_t hbytes = (uint32_t)(a.P + a.T) * (uint32_t)I * 2u;
     const Buf hhi = make_buf(a.h_hi, hbytes), hlo = make_buf(a.h_lo, hbytes);
 
-    if (gv.m >= a.mfma_min) {
-        // ---- MFMA: the 64 rows of the unit x up to 32 columns per pass.  The
-        // 128-wide K chunks are dealt round-robin to the 4 waves, so each h
-        // element is read once per unit; each wave multiplies its chunk into all
-        // four 16-row tiles, and the partials are summed in wave order via LDS.
-        const int r = lane & 15, q = lane >> 4;
-        const int nchunks = I >> 7;
-        const int u0 = tile * 64;  // first row of the unit
-        for (int n0 = 0; n0 < gv.m; n0 += 32) {
-            int pr[2];
-            bool pv[2];
-#pragma unroll
-            for (int nt = 0; nt < 2; ++nt) {
-                const int idx = n0 + nt * 16 + r;
-                pv[nt] = idx < gv.m;
-                pr[nt] = pv[nt] ? plist[idx] : 0;
-            }
-            const bool two = n0 + 16 < gv.m;  // second column tile in use (uniform)
-            f32x4 acc[4][2];
-#pragma unroll
-            for (int rt = 0; rt < 4; ++rt) acc[rt][0] = acc[rt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-            for (int c = wv; c < nchunks; c += 4) {
-                const int k0 = c * 128 + 32 * q;
-                uint4 cw[4];
-                uint32_t sc[4];
-#pragma unroll
-                for (int rt = 0; rt < 4; ++rt) {
-                    const int rr = u0 + 16 * rt + r;
-                    const bool rv = rr < H;
-                    cw[rt] = ld128(cb, rv ? (uint32_t)rr * (uint32_t)(I >> 1) + (uint32_t)(k0 >> 1) : OOB);
-                    sc[rt] = ld_scales<FMT>(sb, rv ? scale_off<FMT>((uint32_t)rr * spr, k0) : OOB);
-                }
-                uint4 bh[2][4], bl[2][4];
-#pragma unroll
+    if (gv.m >= a.mfma_min || sbf) {
+        auto mfma = [&](auto SBFc) {
+            constexpr bool SBF = decltype(SBFc)::value;
+            // ---- MFMA: the 64 rows of the unit x up to 32 columns per pass.  The
+            // 128-wide K chunks are dealt round-robin to the 4 waves, so each h
+            // element is read once per unit; each wave multiplies its chunk into all
+            // four 16-row tiles, and the partials are summed in wave order via LDS.
+            const int r = lane & 15, q = lane >> 4;
+            const int nchunks = I >> 7;
+            const int u0 = tile * 64;  // first row of the unit
+            for (int n0 = 0; n0 < gv.m; n0 += 32) {
+                int pr[2];
+                bool pv[2];
+    #pragma unroll
                 for (int nt = 0; nt < 2; ++nt) {
-                    const uint32_t ho = (uint32_t)(pr[nt] * I + k0) * 2u;
-#pragma unroll
-                    for (int s = 0; s < 4; ++s) {
-                        const bool on = nt == 0 || two;
-                        bh[nt][s] = on ? ld128(hhi, pv[nt] ? ho + 16u * s : OOB) : make_uint4(0, 0, 0, 0);
-                        bl[nt][s] = on ? ld128(hlo, pv[nt] ? ho + 16u * s : OOB) : make_uint4(0, 0, 0, 0);
-                    }
+                    const int idx = n0 + nt * 16 + r;
+                    pv[nt] = idx < gv.m;
+                    pr[nt] = pv[nt] ? plist[idx] : 0;
                 }
-#pragma unroll
-                for (int rt = 0; rt < 4; ++rt) {
-                    const uint32_t cws[4] = {cw[rt].x, cw[rt].y, cw[rt].z, cw[rt].w};
-#pragma unroll
-                    for (int s = 0; s < 4; ++s) {
-                        if constexpr (FMT == FMT_NVFP4) {
-                            const f32x2 sv = block_scales2<FMT>(sc[rt]);
-                            const bf16x8 a1 = e2m1x8_scaled(cws[s], s < 2 ? sv.x : sv.y);
-#pragma unroll
-                            for (int nt = 0; nt < 2; ++nt) {
-                                if (nt == 1 && !two) break;
-                                acc[rt][nt] = mfma16x16x32(a1, __builtin_bit_cast(bf16x8, bh[nt][s]), acc[rt][nt]);
-                                acc[rt][nt] = mfma16x16x32(a1, __builtin_bit_cast(bf16x8, bl[nt][s]), acc[rt][nt]);
+                const bool two = n0 + 16 < gv.m;  // second column tile in use (uniform)
+                f32x4 acc[4][2];
+    #pragma unroll
+                for (int rt = 0; rt < 4; ++rt) acc[rt][0] = acc[rt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+                for (int c = wv; c < nchunks; c += 4) {
+                    const int k0 = c * 128 + 32 * q;
+                    uint4 cw[4];
+                    uint32_t sc[4];
+                    if constexpr (!SBF) {
+    #pragma unroll
+                        for (int rt = 0; rt < 4; ++rt) {
+                            const int rr = u0 + 16 * rt + r;
+                            const bool rv = rr < H;
+                            cw[rt] = ld128(cb, rv ? (uint32_t)rr * (uint32_t)(I >> 1) + (uint32_t)(k0 >> 1) : OOB);
+                            sc[rt] = ld_scales<FMT>(sb, rv ? scale_off<FMT>((uint32_t)rr * spr, k0) : OOB);
+                        }
+                    }
+                    uint4 bh[2][4], bl[2][4];
+    #pragma unroll
+                    for (int nt = 0; nt < 2; ++nt) {
+                        const uint32_t ho = (uint32_t)(pr[nt] * I + k0) * 2u;
+    #pragma unroll
+                        for (int s = 0; s < 4; ++s) {
+                            const bool on = nt == 0 || two;
+                            bh[nt][s] = on ? ld128(hhi, pv[nt] ? ho + 16u * s : OOB) : make_uint4(0, 0, 0, 0);
+                            bl[nt][s] = on ? ld128(hlo, pv[nt] ? ho + 16u * s : OOB) : make_uint4(0, 0, 0, 0);
+                        }
+                    }
+                    if constexpr (SBF) {  // bf16 rows: the weights are the operands; h as hi + lo
+    #pragma unroll
+                        for (int rt = 0; rt < 4; ++rt) {
+                            const int rr = u0 + 16 * rt + r;
+                            const bool rv = rr < H;
+    #pragma unroll
+                            for (int s = 0; s < 4; ++s) {
+                                const uint32_t o = (uint32_t)rr * (uint32_t)I * 2u + (uint32_t)(k0 + 8 * s) * 2u;
+                                const bf16x8 w = __builtin_bit_cast(bf16x8, ld128(cb, rv ? o : OOB));
+    #pragma unroll
+                                for (int nt = 0; nt < 2; ++nt) {
+                                    if (nt == 1 && !two) break;
+                                    acc[rt][nt] = mfma16x16x32(w, __builtin_bit_cast(bf16x8, bh[nt][s]), acc[rt][nt]);
+                                    acc[rt][nt] = mfma16x16x32(w, __builtin_bit_cast(bf16x8, bl[nt][s]), acc[rt][nt]);
+                                }
                             }
-                        } else {
-                            float sh, sl;
-                            split_scale(f16_bits_to_f32(s < 2 ? sc[rt] : (sc[rt] >> 16)), sh, sl);
-                            bf16x8 ah, al;
-                            e2m1x8_split(cws[s], sh, sl, ah, al);
-#pragma unroll
-                            for (int nt = 0; nt < 2; ++nt) {
-                                if (nt == 1 && !two) break;
-                                const bf16x8 b0 = __builtin_bit_cast(bf16x8, bh[nt][s]);
-                                const bf16x8 b1 = __builtin_bit_cast(bf16x8, bl[nt][s]);
-                                // all four terms: al can reach 2^-5 of the weight and
-                                // h_lo 2^-8 of h, so al * h_lo is not negligible after
-                                // cancellation in the sum over K
-                                acc[rt][nt] = mfma16x16x32(ah, b0, acc[rt][nt]);
-                                acc[rt][nt] = mfma16x16x32(ah, b1, acc[rt][nt]);
-                                acc[rt][nt] = mfma16x16x32(al, b0, acc[rt][nt]);
-                                acc[rt][nt] = mfma16x16x32(al, b1, acc[rt][nt]);
+                        }
+                        continue;
+                    }
+    #pragma unroll
+                    for (int rt = 0; rt < 4; ++rt) {
+                        const uint32_t cws[4] = {cw[rt].x, cw[rt].y, cw[rt].z, cw[rt].w};
+    #pragma unroll
+                        for (int s = 0; s < 4; ++s) {
+                            if constexpr (FMT == FMT_NVFP4) {
+                                const f32x2 sv = block_scales2<FMT>(sc[rt]);
+                                const bf16x8 a1 = e2m1x8_scaled(cws[s], s < 2 ? sv.x : sv.y);
+    #pragma unroll
+                                for (int nt = 0; nt < 2; ++nt) {
+                                    if (nt == 1 && !two) break;
+                                    acc[rt][nt] = mfma16x16x32(a1, __builtin_bit_cast(bf16x8, bh[nt][s]), acc[rt][nt]);
+                                    acc[rt][nt] = mfma16x16x32(a1, __builtin_bit_cast(bf16x8, bl[nt][s]), acc[rt][nt]);
+                                }
+                            } else {
+                                float sh, sl;
+                                split_scale(f16_bits_to_f32(s < 2 ? sc[rt] : (sc[rt] >> 16)), sh, sl);
+                                bf16x8 ah, al;
+                                e2m1x8_split(cws[s], sh, sl, ah, al);
+    #pragma unroll
+                                for (int nt = 0; nt < 2; ++nt) {
+                                    if (nt == 1 && !two) break;
+                                    const bf16x8 b0 = __builtin_bit_cast(bf16x8, bh[nt][s]);
+                                    const bf16x8 b1 = __builtin_bit_cast(bf16x8, bl[nt][s]);
+                                    // all four terms: al can reach 2^-5 of the weight and
+                                    // h_lo 2^-8 of h, so al * h_lo is not negligible after
+                                    // cancellation in the sum over K
+                                    acc[rt][nt] = mfma16x16x32(ah, b0, acc[rt][nt]);
+                                    acc[rt][nt] = mfma16x16x32(ah, b1, acc[rt][nt]);
+                                    acc[rt][nt] = mfma16x16x32(al, b0, acc[rt][nt]);
+                                    acc[rt][nt] = mfma16x16x32(al, b1, acc[rt][nt]);
+                                }
                             }
                         }
                     }
                 }
-            }
-            // partials of all waves -> LDS; wave w sums row tile w in wave order
-#pragma unroll
-            for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
+                // partials of all waves -> LDS; wave w sums row tile w in wave order
+    #pragma unroll
+                for (int rt = 0; rt < 4; ++rt)
+    #pragma unroll
+                    for (int nt = 0; nt < 2; ++nt)
+    #pragma unroll
+                        for (int j = 0; j < 4; ++j) red[wv][rt][nt * 4 + j][lane] = acc[rt][nt][j];
+                __syncthreads();
+                float v[2][4];
+    #pragma unroll
                 for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) red[wv][rt][nt * 4 + j][lane] = acc[rt][nt][j];
-            __syncthreads();
-            float v[2][4];
-#pragma unroll
-            for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    float t = red[0][wv][nt * 4 + j][lane];
-#pragma unroll
-                    for (int w = 1; w < 4; ++w) t += red[w][wv][nt * 4 + j][lane];
-                    v[nt][j] = t * gsc;
+    #pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        float t = red[0][wv][nt * 4 + j][lane];
+    #pragma unroll
+                        for (int w = 1; w < 4; ++w) t += red[w][wv][nt * 4 + j][lane];
+                        v[nt][j] = t * gsc;
+                    }
+                __syncthreads();  // red is reused by the next pass or unit
+                // lane holds rows u0 + 16wv + 4q + j of column r
+                const int rb = u0 + 16 * wv + 4 * q;
+    #pragma unroll
+                for (int nt = 0; nt < 2; ++nt) {
+                    if (!pv[nt]) continue;
+                    float *op = a.out + (size_t)pr[nt] * H + rb;
+                    if (rb + 3 < H) {
+                        *reinterpret_cast<float4 *>(op) = make_float4(v[nt][0], v[nt][1], v[nt][2], v[nt][3]);
+                    } else {
+    #pragma unroll
+                        for (int j = 0; j < 4; ++j)
+                            if (rb + j < H) op[j] = v[nt][j];
+                    }
                 }
-            __syncthreads();  // red is reused by the next pass or unit
-            // lane holds rows u0 + 16wv + 4q + j of column r
-            const int rb = u0 + 16 * wv + 4 * q;
-#pragma unroll
-            for (int nt = 0; nt < 2; ++nt) {
-                if (!pv[nt]) continue;
-                float *op = a.out + (size_t)pr[nt] * H + rb;
-                if (rb + 3 < H) {
-                    *reinterpret_cast<float4 *>(op) = make_float4(v[nt][0], v[nt][1], v[nt][2], v[nt][3]);
-                } else {
-#pragma unroll
-                    for (int j = 0; j < 4; ++j)
-                        if (rb + j < H) op[j] = v[nt][j];
-                }
+            }
+        };
+        if constexpr (SB) {
+            if (sbf) {
+                mfma(std::true_type());
+                return;
             }
         }
+        mfma(std::false_type());
         return;
     }
 
@@ -717,13 +782,13 @@ __device__ __forceinline__ void gw2_unit(const GW2Args &a, int gs, int tile, flo
     }
 }
 
-template <int FMT, int L>
-__global__ __launch_bounds__(256, L <= 16 ? W4_GW_MINBLK : 1) void k_moe_gw2(GW2Args a) {
+template <int FMT, int L, bool SB>
+__global__ __launch_bounds__(256, L <= 16 ? (SB ? 2 : W4_GW_MINBLK) : 1) void k_moe_gw2(GW2Args a) {
     __shared__ float red[4][4][8][64];  // MFMA partials: [wave][row tile][column tile x 4 + j][lane]
     const int nu = unit_count(a.grp, a.s_codes != nullptr, a.tiles);
     for (int u = blockIdx.x; u < nu; u += gridDim.x) {
         const int gs = u / a.tiles;
-        gw2_unit<FMT, L>(a, gs, u - gs * a.tiles, red);
+        gw2_unit<FMT, L, SB>(a, gs, u - gs * a.tiles, red);
     }
 }
 
@@ -1604,39 +1669,49 @@ unsigned grouped_grid(int Gmax, int tiles) {
 void launch_gw13(GW13Args &a, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
     a.tiles = (a.I + 15) / 16;
     const dim3 g(grouped_grid(a.Gmax, a.tiles)), b(256);
-    auto with_fmt = [&](auto F) {
+    auto with_fmt = [&](auto F, auto SBc) {
         constexpr int FMT = decltype(F)::value;
+        constexpr bool SB = decltype(SBc)::value;
         switch (lanes_for_k(a.H)) {
-        case 1: go_ev(st, e0, e1, k_moe_gw13<FMT, 1>, g, b, 0, a); break;
-        case 2: go_ev(st, e0, e1, k_moe_gw13<FMT, 2>, g, b, 0, a); break;
-        case 4: go_ev(st, e0, e1, k_moe_gw13<FMT, 4>, g, b, 0, a); break;
-        case 8: go_ev(st, e0, e1, k_moe_gw13<FMT, 8>, g, b, 0, a); break;
-        case 16: go_ev(st, e0, e1, k_moe_gw13<FMT, 16>, g, b, 0, a); break;
-        case 32: go_ev(st, e0, e1, k_moe_gw13<FMT, 32>, g, b, 0, a); break;
-        default: go_ev(st, e0, e1, k_moe_gw13<FMT, 64>, g, b, 0, a); break;
+        case 1: go_ev(st, e0, e1, k_moe_gw13<FMT, 1, SB>, g, b, 0, a); break;
+        case 2: go_ev(st, e0, e1, k_moe_gw13<FMT, 2, SB>, g, b, 0, a); break;
+        case 4: go_ev(st, e0, e1, k_moe_gw13<FMT, 4, SB>, g, b, 0, a); break;
+        case 8: go_ev(st, e0, e1, k_moe_gw13<FMT, 8, SB>, g, b, 0, a); break;
+        case 16: go_ev(st, e0, e1, k_moe_gw13<FMT, 16, SB>, g, b, 0, a); break;
+        case 32: go_ev(st, e0, e1, k_moe_gw13<FMT, 32, SB>, g, b, 0, a); break;
+        default: go_ev(st, e0, e1, k_moe_gw13<FMT, 64, SB>, g, b, 0, a); break;
         }
     };
-    if (a.fmt == FMT_NVFP4) with_fmt(std::integral_constant<int, FMT_NVFP4>());
-    else with_fmt(std::integral_constant<int, FMT_E2M1>());
+    auto with_sb = [&](auto F) {
+        if (a.s_bf16) with_fmt(F, std::true_type());
+        else with_fmt(F, std::false_type());
+    };
+    if (a.fmt == FMT_NVFP4) with_sb(std::integral_constant<int, FMT_NVFP4>());
+    else with_sb(std::integral_constant<int, FMT_E2M1>());
 }
 
 void launch_gw2(GW2Args &a, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
     a.tiles = (a.H + 63) / 64;
     const dim3 g(grouped_grid(a.Gmax, a.tiles)), b(256);
-    auto with_fmt = [&](auto F) {
+    auto with_fmt = [&](auto F, auto SBc) {
         constexpr int FMT = decltype(F)::value;
+        constexpr bool SB = decltype(SBc)::value;
         switch (lanes_for_k(a.I)) {
-        case 1: go_ev(st, e0, e1, k_moe_gw2<FMT, 1>, g, b, 0, a); break;
-        case 2: go_ev(st, e0, e1, k_moe_gw2<FMT, 2>, g, b, 0, a); break;
-        case 4: go_ev(st, e0, e1, k_moe_gw2<FMT, 4>, g, b, 0, a); break;
-        case 8: go_ev(st, e0, e1, k_moe_gw2<FMT, 8>, g, b, 0, a); break;
-        case 16: go_ev(st, e0, e1, k_moe_gw2<FMT, 16>, g, b, 0, a); break;
-        case 32: go_ev(st, e0, e1, k_moe_gw2<FMT, 32>, g, b, 0, a); break;
-        default: go_ev(st, e0, e1, k_moe_gw2<FMT, 64>, g, b, 0, a); break;
+        case 1: go_ev(st, e0, e1, k_moe_gw2<FMT, 1, SB>, g, b, 0, a); break;
+        case 2: go_ev(st, e0, e1, k_moe_gw2<FMT, 2, SB>, g, b, 0, a); break;
+        case 4: go_ev(st, e0, e1, k_moe_gw2<FMT, 4, SB>, g, b, 0, a); break;
+        case 8: go_ev(st, e0, e1, k_moe_gw2<FMT, 8, SB>, g, b, 0, a); break;
+        case 16: go_ev(st, e0, e1, k_moe_gw2<FMT, 16, SB>, g, b, 0, a); break;
+        case 32: go_ev(st, e0, e1, k_moe_gw2<FMT, 32, SB>, g, b, 0, a); break;
+        default: go_ev(st, e0, e1, k_moe_gw2<FMT, 64, SB>, g, b, 0, a); break;
         }
     };
-    if (a.fmt == FMT_NVFP4) with_fmt(std::integral_constant<int, FMT_NVFP4>());
-    else with_fmt(std::integral_constant<int, FMT_E2M1>());
+    auto with_sb = [&](auto F) {
+        if (a.s_bf16) with_fmt(F, std::true_type());
+        else with_fmt(F, std::false_type());
+    };
+    if (a.fmt == FMT_NVFP4) with_sb(std::integral_constant<int, FMT_NVFP4>());
+    else with_sb(std::integral_constant<int, FMT_E2M1>());
 }
 
 // blocks of the large-batch launches (grid-stride over the units)

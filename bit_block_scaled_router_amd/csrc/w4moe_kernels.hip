@@ -823,7 +823,7 @@ int check_layer(const moe_w4a16_layer *Lr, int64_t T, MoEPlan &p) {
     p.grouped = T >= W4_GROUPED_MIN_T && H % 128 == 0 && I % 128 == 0 && H <= 4096 && I <= 4096 &&
                 (fmt == W4_FMT_E2M1_F16S16 ? p.P <= MAX_GROUPED_PAIRS
                                            : fmt == W4_FMT_NVFP4_E4M3S16 && p.P <= MAX_ONE_BLOCK_PAIRS) &&
-                !(Lr->has_shared && Lr->shared_w13.format == W4_FMT_BF16);
+                !(Lr->has_shared && Lr->shared_w13.format == W4_FMT_BF16 && p.P > MAX_ONE_BLOCK_PAIRS);
     if (p.mx) {  // batches run grouped on the scaled FP4 MFMA; single tokens on the VALU kernels
         if (H % 128 || I % 128)
             return fail(W4_ERR_UNSUPPORTED, "MXFP4 layers need hidden and inter multiples of 128");
@@ -1166,6 +1166,7 @@ int run_grouped(const moe_w4a16_layer *Lr, const MoEPlan &p, const uint16_t *x, 
     a.H = p.H, a.I = p.I, a.K = p.K, a.T = p.T, a.P = p.P, a.Gmax = p.Gmax, a.mfma_min = W4_MFMA_MIN;
     a.fmt = Lr->w13.format == W4_FMT_NVFP4_E4M3S16 ? FMT_NVFP4 : FMT_E2M1;
     a.gs = Lr->w13.global_scales, a.s_gs = Lr->has_shared ? Lr->shared_w13.global_scales : nullptr;
+    a.s_bf16 = Lr->has_shared && Lr->shared_w13.format == W4_FMT_BF16;  // (up to 4096 pairs: the plan)
     int32_t *ctg = p.multi ? (int32_t *)(wsb + p.off_route) + p.P + p.E + (size_t)p.nblk * p.E : nullptr;
     a.ctg = ctg;
     if (p.pf) launch_pf13(a, sm, ev(next_ev), ev(next_ev + 1));
@@ -1180,6 +1181,7 @@ int run_grouped(const moe_w4a16_layer *Lr, const MoEPlan &p, const uint16_t *x, 
     d.H = p.H, d.I = p.I, d.K = p.K, d.T = p.T, d.P = p.P, d.Gmax = p.Gmax, d.mfma_min = W4_MFMA_MIN;
     d.fmt = a.fmt;
     d.gs = Lr->w2.global_scales, d.s_gs = Lr->has_shared ? Lr->shared_w2.global_scales : nullptr;
+    d.s_bf16 = a.s_bf16;
     d.ctg = ctg;
     if (p.pf) launch_pf2(d, sm, ev(next_ev + 2), ev(next_ev + 3));
     else launch_gw2(d, sm, ev(next_ev + 2), ev(next_ev + 3));

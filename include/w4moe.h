@@ -256,7 +256,8 @@ int moe_w4a16_forward_timed(const moe_w4a16_layer *L, const uint16_t *x, int64_t
  * combine).  The batched path serves E2M1 layers with H and I multiples of 128
  * and at most 4096, T >= 4 and T * top_k <= 65536 (NVFP4 layers: the same,
  * up to T * top_k = 4096, with one exact bf16 MFMA term per weight instead of
- * two and the global scales applied to the sums); other requests take the
+ * two and the global scales applied to the sums; a bf16 shared expert, its
+ * rows the MFMA operands, likewise up to 4096 pairs); other requests take the
  * single-token path.  MXFP4 layers need H and I multiples of 128 and a shared
  * expert in MXFP4 (W4_ERR_UNSUPPORTED otherwise); from T = 4 they run 6
  * kernels (router; x to MXFP8; top-k and grouping; W13 + SiLU with h quantised

@@ -295,9 +295,38 @@ def test_moe_bf16_shared_expert(shape):
         print(f"bf16 shared token {t}", flush=True)
         print(_check_moe(shape, dev_layer, or_layer, tie_free_tokens(shape, or_layer, 1, first=t), f"{shape.name} t={t}"),
               flush=True)
-    # batches of this layer take the single-token path
-    assert w4.moe_w4a16_stage_count(dev_layer, 6) == 3
+    # batches of up to 4096 pairs run grouped, the shared expert's bf16 rows as MFMA operands
+    assert w4.moe_w4a16_stage_count(dev_layer, 6) == 5
     _check_moe(shape, dev_layer, or_layer, tie_free_tokens(shape, or_layer, 6, first=40), f"{shape.name} T=6")
+
+
+def test_moe_bf16_shared_expert_batches():
+    """Tiny layer: grouped batches (the shared expert a 300-row bf16 MFMA group)
+    and, past 4096 pairs, the single-token path."""
+    shape = synth.TINY_MOE_BF16SH
+    dev_layer = wl.build_moe_layer(shape, device=DEV)
+    or_layer = oracle_layer(shape)
+    for T, stages in ((300, 5), (2048, 5), (2049, 3)):  # top-2: 4096 pairs at T = 2048
+        print(f"bf16 shared tiny T={T}", flush=True)
+        assert w4.moe_w4a16_stage_count(dev_layer, T) == stages, T
+        _check_moe(shape, dev_layer, or_layer, tie_free_tokens(shape, or_layer, T, first=500), f"bf16 shared T={T}")
+
+
+def test_moe_bf16_shared_expert_t32_zipf_sampled():
+    """35B-A3B shape, T = 32 with the Zipf router bias: the whole batch on the
+    device, every fourth token against the oracle."""
+    shape = synth.QWEN_MOE_T32_BF16SH
+    print(f"building {shape.name}", flush=True)
+    dev_layer = wl.build_moe_layer(shape, device=DEV)
+    or_layer = oracle_layer(shape)
+    xb = tie_free_tokens(shape, or_layer, shape.tokens, first=60)
+    assert w4.moe_w4a16_stage_count(dev_layer, shape.tokens) == 5
+    ids = torch.full((shape.tokens, shape.top_k), -7, dtype=torch.int32, device=DEV)
+    y = wl.bf16_bits(w4.moe_w4a16_forward(dev_layer, wl.bf16_tensor(xb), topk_ids=ids))
+    rows = list(range(0, shape.tokens, 4))
+    ref, rids, _ = ops.moe_forward(or_layer, xb[rows])
+    assert np.array_equal(ids.cpu().numpy()[rows], rids)
+    print(assert_bf16_close(y[rows], ref, "bf16 shared T=32"), flush=True)
 
 
 def test_moe_nvfp4_with_bf16_shared_expert():
@@ -305,3 +334,5 @@ def test_moe_nvfp4_with_bf16_shared_expert():
     dev_layer = wl.build_moe_layer(shape, device=DEV)
     or_layer = oracle_layer(shape)
     _check_moe(shape, dev_layer, or_layer, tie_free_tokens(shape, or_layer, 3, first=7), "nvfp4 + bf16 shared")
+    assert w4.moe_w4a16_stage_count(dev_layer, 40) == 5
+    _check_moe(shape, dev_layer, or_layer, tie_free_tokens(shape, or_layer, 40, first=70), "nvfp4 + bf16 shared T=40")

@@ -216,6 +216,20 @@ def test_mxfp4_layer_plan_and_validation():
     assert st == w4.W4_ERR_INVALID_ARG
 
 
+def test_bf16_shared_expert_plan():
+    """A bf16 shared expert joins the grouped path up to 4096 (token, slot)
+    pairs (its rows are MFMA operands there); larger batches take the
+    single-token path, which streams bf16 rows too."""
+    bf = w4.W4_FMT_BF16
+    for fmt in (w4.W4_FMT_E2M1_F16S16, w4.W4_FMT_NVFP4_E4M3S16):
+        g = 1 << 22 if fmt == w4.W4_FMT_NVFP4_E4M3S16 else None
+        L = _layer(w13=_mat(fmt=fmt, groups=8, n=256, k=256, gsc=g), w2=_mat(fmt=fmt, groups=8, n=256, k=128, gsc=g),
+                   shared_w13=_mat(fmt=bf, groups=1, n=256, k=256, scales=None),
+                   shared_w2=_mat(fmt=bf, groups=1, n=256, k=128, scales=None))
+        got = [w4.lib().moe_w4a16_stage_count(C.byref(L), T) for T in (1, 3, 4, 2048, 2049)]
+        assert got == [3, 3, 5, 5, 3], (fmt, got)
+
+
 def test_bf16_format_quantiser_sizes_and_rules():
     rng = np.random.default_rng(23)
     w = (rng.standard_normal((5, 64)) * 0.02).astype(np.float32)
@@ -231,7 +245,7 @@ def test_bf16_format_quantiser_sizes_and_rules():
     L = _layer(shared_w13=_mat(fmt=fmt, groups=1, n=2 * I, k=H, scales=None),
                shared_w2=_mat(fmt=fmt, groups=1, n=H, k=I, scales=None))
     assert w4.lib().moe_w4a16_workspace_bytes(C.byref(L), 1) > 0
-    assert w4.lib().moe_w4a16_stage_count(C.byref(L), 8) == 3  # batches take the single-token path
+    assert w4.lib().moe_w4a16_stage_count(C.byref(L), 8) == 5  # batches run grouped (see the plan test)
     assert _fwd(_layer(w13=_mat(fmt=fmt, groups=E, n=2 * I, k=H, scales=None),
                        w2=_mat(fmt=fmt, groups=E, n=H, k=I, scales=None))) == w4.W4_ERR_UNSUPPORTED
     assert _fwd(_layer(shared_w13=_mat(fmt=fmt, groups=1, n=2 * I, k=H, scales=None))) == w4.W4_ERR_LAYOUT
