@@ -853,17 +853,24 @@ __device__ __forceinline__ bool pf_unit(const int32_t *grp, const int32_t *ctg, 
     return true;
 }
 
+// FMT, SB as in gw13_unit: E2M1 weights as two exact bf16 terms, NVFP4 as one
+// (the global scale multiplies the sums), a bf16 shared expert's rows as they are.
+template <int FMT, bool SB>
 __device__ __forceinline__ void pf13_unit(const GW13Args &a, int gs, int rt, int n0,
                                           uint16_t (*xs)[PF_COLS][PF_LROW]) {
+    using SC = typename std::conditional<FMT == FMT_NVFP4, uint8_t, uint16_t>::type;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int H = a.H, I = a.I;
     const uint32_t spr = (uint32_t)(H >> 4);
     const size_t mat_codes = (size_t)(2 * I) * (H >> 1), mat_scales = (size_t)(2 * I) * spr;
-    const GroupView<uint16_t> gv = group_view(a.grp, gs, a.Gmax, a.P, a.T, a.codes, a.scales, mat_codes, mat_scales,
-                                              a.s_codes, a.s_scales);
-    const Buf cb = make_buf(gv.codes, (uint32_t)mat_codes);
-    const Buf sb = make_buf(gv.scales, (uint32_t)(mat_scales * 2));
+    const GroupView<SC> gv = group_view(a.grp, gs, a.Gmax, a.P, a.T, a.codes, reinterpret_cast<const SC *>(a.scales),
+                                        mat_codes, mat_scales, a.s_codes, reinterpret_cast<const SC *>(a.s_scales));
+    const bool sbf = SB && gv.e < 0;
+    const Buf cb = make_buf(gv.codes, (uint32_t)(sbf ? 4 * mat_codes : mat_codes));
+    const Buf sb = make_buf(gv.scales, sbf ? 0u : (uint32_t)(mat_scales * sizeof(SC)));
+    float gsc = 1.f;  // NVFP4 global scale of the matrix
+    if constexpr (FMT == FMT_NVFP4) gsc = sbf ? 1.f : gv.e < 0 ? ld_uniform(a.s_gs, 0) : ld_uniform(a.gs, gv.e);
     const Buf xall = make_buf(a.x, (uint32_t)a.T * (uint32_t)H * 2u);
     const int *plist = a.pairs + gv.off;
     const int r = lane & 15, q = lane >> 4;
@@ -881,8 +888,8 @@ __device__ __forceinline__ void pf13_unit(const GW13Args &a, int gs, int rt, int
     uint32_t sw[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-        cw[t] = ld128(cb, rows[t] * (uint32_t)(H >> 1) + (uint32_t)(16 * q));
-        sw[t] = ld32(sb, (rows[t] * spr + (uint32_t)(2 * q)) * 2u);
+        cw[t] = ld128(cb, sbf ? OOB : rows[t] * (uint32_t)(H >> 1) + (uint32_t)(16 * q));
+        sw[t] = ld_scales<FMT>(sb, sbf ? OOB : scale_off<FMT>(rows[t] * spr, 32 * q));
     }
     f32x4 acc[4][4];  // [gate 0, gate 1, up 0, up 1][column tile]
 #pragma unroll
@@ -901,10 +908,31 @@ __device__ __forceinline__ void pf13_unit(const GW13Args &a, int gs, int rt, int
             const uint32_t kn = (uint32_t)((ch + 1) * PF_KC);
             pf_load(xall, xo + kn * 2u, lv, xr);
             const uint32_t kq = kn + 32u * (uint32_t)q;
+            if (!sbf) {
 #pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                cw[t] = ld128(cb, rows[t] * (uint32_t)(H >> 1) + (kq >> 1));
-                sw[t] = ld32(sb, (rows[t] * spr + (kq >> 4)) * 2u);
+                for (int t = 0; t < 4; ++t) {
+                    cw[t] = ld128(cb, rows[t] * (uint32_t)(H >> 1) + (kq >> 1));
+                    sw[t] = ld_scales<FMT>(sb, scale_off<FMT>(rows[t] * spr, (int)kq));
+                }
+            }
+        }
+        if constexpr (SB) {
+            if (sbf) {  // bf16 rows: 8 weights of each row per MFMA step, read as needed
+                const uint32_t kq = (uint32_t)(ch * PF_KC + 32 * q);
+#pragma unroll
+                for (int s = 0; s < 4; ++s) {
+                    bf16x8 b[4];
+#pragma unroll
+                    for (int nt = 0; nt < 4; ++nt) b[nt] = *pf_unit_ptr(xb, 16 * nt + r, 4 * q + s);
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) {
+                        const bf16x8 w = __builtin_bit_cast(
+                            bf16x8, ld128(cb, rows[t] * (uint32_t)H * 2u + (kq + 8u * (uint32_t)s) * 2u));
+#pragma unroll
+                        for (int nt = 0; nt < 4; ++nt) acc[t][nt] = mfma16x16x32(w, b[nt], acc[t][nt]);
+                    }
+                }
+                continue;
             }
         }
 #pragma unroll
@@ -915,14 +943,21 @@ __device__ __forceinline__ void pf13_unit(const GW13Args &a, int gs, int rt, int
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
                 const uint32_t cws[4] = {cc[t].x, cc[t].y, cc[t].z, cc[t].w};
-                float hi, lo;
-                split_scale(f16_bits_to_f32(s < 2 ? sc[t] : (sc[t] >> 16)), hi, lo);
-                bf16x8 ah, al;
-                e2m1x8_split(cws[s], hi, lo, ah, al);
+                if constexpr (FMT == FMT_NVFP4) {
+                    const f32x2 sv = block_scales2<FMT>(sc[t]);
+                    const bf16x8 a1 = e2m1x8_scaled(cws[s], s < 2 ? sv.x : sv.y);
 #pragma unroll
-                for (int nt = 0; nt < 4; ++nt) acc[t][nt] = mfma16x16x32(ah, b[nt], acc[t][nt]);
+                    for (int nt = 0; nt < 4; ++nt) acc[t][nt] = mfma16x16x32(a1, b[nt], acc[t][nt]);
+                } else {
+                    float hi, lo;
+                    split_scale(f16_bits_to_f32(s < 2 ? sc[t] : (sc[t] >> 16)), hi, lo);
+                    bf16x8 ah, al;
+                    e2m1x8_split(cws[s], hi, lo, ah, al);
 #pragma unroll
-                for (int nt = 0; nt < 4; ++nt) acc[t][nt] = mfma16x16x32(al, b[nt], acc[t][nt]);
+                    for (int nt = 0; nt < 4; ++nt) acc[t][nt] = mfma16x16x32(ah, b[nt], acc[t][nt]);
+#pragma unroll
+                    for (int nt = 0; nt < 4; ++nt) acc[t][nt] = mfma16x16x32(al, b[nt], acc[t][nt]);
+                }
             }
         }
     }
@@ -937,7 +972,7 @@ __device__ __forceinline__ void pf13_unit(const GW13Args &a, int gs, int rt, int
                 uint16_t bh[4], bl[4];
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    const float gg = acc[ht][nt][j], uu = acc[2 + ht][nt][j];
+                    const float gg = acc[ht][nt][j] * gsc, uu = acc[2 + ht][nt][j] * gsc;
                     split_bf16((gg / (1.f + expf(-gg))) * uu, bh[j], bl[j]);
                 }
                 const size_t o = (size_t)p * I + i0 + 16 * ht + 4 * q;
@@ -951,6 +986,7 @@ __device__ __forceinline__ void pf13_unit(const GW13Args &a, int gs, int rt, int
     __syncthreads();  // the LDS buffers are refilled by the next unit
 }
 
+template <int FMT, bool SB>
 __global__ __launch_bounds__(256) void k_moe_pf13(GW13Args a) {
     __shared__ __align__(16) uint16_t xs[2][PF_COLS][PF_LROW];
     const bool sh = a.s_codes != nullptr;
@@ -958,21 +994,27 @@ __global__ __launch_bounds__(256) void k_moe_pf13(GW13Args a) {
     const int nu = pf_unit_count(nct, a.tiles);
     for (int u = blockIdx.x; u < nu; u += gridDim.x) {
         int gs, rt, n0;
-        if (pf_unit(a.grp, a.ctg, a.Gmax, sh, nct, u, a.tiles, gs, rt, n0)) pf13_unit(a, gs, rt, n0, xs);
+        if (pf_unit(a.grp, a.ctg, a.Gmax, sh, nct, u, a.tiles, gs, rt, n0)) pf13_unit<FMT, SB>(a, gs, rt, n0, xs);
     }
 }
 
+// FMT, SB as in pf13_unit.
+template <int FMT, bool SB>
 __device__ __forceinline__ void pf2_unit(const GW2Args &a, int gs, int rt, int n0,
                                          uint16_t (*hs)[2][PF_COLS][PF_LROW]) {
+    using SC = typename std::conditional<FMT == FMT_NVFP4, uint8_t, uint16_t>::type;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int H = a.H, I = a.I;
     const uint32_t spr = (uint32_t)(I >> 4);
     const size_t mat_codes = (size_t)H * (I >> 1), mat_scales = (size_t)H * spr;
-    const GroupView<uint16_t> gv = group_view(a.grp, gs, a.Gmax, a.P, a.T, a.codes, a.scales, mat_codes, mat_scales,
-                                              a.s_codes, a.s_scales);
-    const Buf cb = make_buf(gv.codes, (uint32_t)mat_codes);
-    const Buf sb = make_buf(gv.scales, (uint32_t)(mat_scales * 2));
+    const GroupView<SC> gv = group_view(a.grp, gs, a.Gmax, a.P, a.T, a.codes, reinterpret_cast<const SC *>(a.scales),
+                                        mat_codes, mat_scales, a.s_codes, reinterpret_cast<const SC *>(a.s_scales));
+    const bool sbf = SB && gv.e < 0;
+    const Buf cb = make_buf(gv.codes, (uint32_t)(sbf ? 4 * mat_codes : mat_codes));
+    const Buf sb = make_buf(gv.scales, sbf ? 0u : (uint32_t)(mat_scales * sizeof(SC)));
+    float gsc = 1.f;  // NVFP4 global scale of the matrix
+    if constexpr (FMT == FMT_NVFP4) gsc = sbf ? 1.f : gv.e < 0 ? ld_uniform(a.s_gs, 0) : ld_uniform(a.gs, gv.e);
     const uint32_t hbytes = (uint32_t)(a.P + a.T) * (uint32_t)I * 2u;
     const Buf hhi = make_buf(a.h_hi, hbytes), hlo = make_buf(a.h_lo, hbytes);
     const int *plist = a.pairs + gv.off;
@@ -990,8 +1032,8 @@ __device__ __forceinline__ void pf2_unit(const GW2Args &a, int gs, int rt, int n
     uint32_t sw[2];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-        cw[t] = ld128(cb, rows[t] * (uint32_t)(I >> 1) + (uint32_t)(16 * q));
-        sw[t] = ld32(sb, (rows[t] * spr + (uint32_t)(2 * q)) * 2u);
+        cw[t] = ld128(cb, sbf ? OOB : rows[t] * (uint32_t)(I >> 1) + (uint32_t)(16 * q));
+        sw[t] = ld_scales<FMT>(sb, sbf ? OOB : scale_off<FMT>(rows[t] * spr, 32 * q));
     }
     f32x4 acc[2][4], acc2[2][4];  // [row tile][column tile]; weight hi / lo terms
 #pragma unroll
@@ -1013,10 +1055,37 @@ __device__ __forceinline__ void pf2_unit(const GW2Args &a, int gs, int rt, int n
             pf_load(hhi, ho + kn * 2u, lv, hr);
             pf_load(hlo, ho + kn * 2u, lv, lr);
             const uint32_t kq = kn + 32u * (uint32_t)q;
+            if (!sbf) {
 #pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                cw[t] = ld128(cb, rows[t] * (uint32_t)(I >> 1) + (kq >> 1));
-                sw[t] = ld32(sb, (rows[t] * spr + (kq >> 4)) * 2u);
+                for (int t = 0; t < 2; ++t) {
+                    cw[t] = ld128(cb, rows[t] * (uint32_t)(I >> 1) + (kq >> 1));
+                    sw[t] = ld_scales<FMT>(sb, scale_off<FMT>(rows[t] * spr, (int)kq));
+                }
+            }
+        }
+        if constexpr (SB) {
+            if (sbf) {  // bf16 rows, read as needed; h as hi + lo
+                const uint32_t kq = (uint32_t)(ch * PF_KC + 32 * q);
+#pragma unroll
+                for (int s = 0; s < 4; ++s) {
+                    bf16x8 b0[4], b1[4];
+#pragma unroll
+                    for (int nt = 0; nt < 4; ++nt) {
+                        b0[nt] = *pf_unit_ptr(bh, 16 * nt + r, 4 * q + s);
+                        b1[nt] = *pf_unit_ptr(bl, 16 * nt + r, 4 * q + s);
+                    }
+#pragma unroll
+                    for (int t = 0; t < 2; ++t) {
+                        const bf16x8 w = __builtin_bit_cast(
+                            bf16x8, ld128(cb, rows[t] * (uint32_t)I * 2u + (kq + 8u * (uint32_t)s) * 2u));
+#pragma unroll
+                        for (int nt = 0; nt < 4; ++nt) {
+                            acc[t][nt] = mfma16x16x32(w, b0[nt], acc[t][nt]);
+                            acc2[t][nt] = mfma16x16x32(w, b1[nt], acc2[t][nt]);
+                        }
+                    }
+                }
+                continue;
             }
         }
 #pragma unroll
@@ -1030,6 +1099,16 @@ __device__ __forceinline__ void pf2_unit(const GW2Args &a, int gs, int rt, int n
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
                 const uint32_t cws[4] = {cc[t].x, cc[t].y, cc[t].z, cc[t].w};
+                if constexpr (FMT == FMT_NVFP4) {  // one exact weight term
+                    const f32x2 sv = block_scales2<FMT>(sc[t]);
+                    const bf16x8 a1 = e2m1x8_scaled(cws[s], s < 2 ? sv.x : sv.y);
+#pragma unroll
+                    for (int nt = 0; nt < 4; ++nt) {
+                        acc[t][nt] = mfma16x16x32(a1, b0[nt], acc[t][nt]);
+                        acc2[t][nt] = mfma16x16x32(a1, b1[nt], acc2[t][nt]);
+                    }
+                    continue;
+                }
                 float hi, lo;
                 split_scale(f16_bits_to_f32(s < 2 ? sc[t] : (sc[t] >> 16)), hi, lo);
                 bf16x8 ah, al;
@@ -1056,7 +1135,7 @@ __device__ __forceinline__ void pf2_unit(const GW2Args &a, int gs, int rt, int n
             float *op = a.out + (size_t)plist[idx] * H + o0 + 4 * q;
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
-                const f32x4 v = acc[t][nt] + acc2[t][nt];
+                const f32x4 v = (acc[t][nt] + acc2[t][nt]) * gsc;
                 *reinterpret_cast<float4 *>(op + 16 * t) = make_float4(v[0], v[1], v[2], v[3]);
             }
         }
@@ -1064,6 +1143,7 @@ __device__ __forceinline__ void pf2_unit(const GW2Args &a, int gs, int rt, int n
     __syncthreads();
 }
 
+template <int FMT, bool SB>
 __global__ __launch_bounds__(256) void k_moe_pf2(GW2Args a) {
     __shared__ __align__(16) uint16_t hs[2][2][PF_COLS][PF_LROW];  // [buffer][hi, lo][column][K]
     const bool sh = a.s_codes != nullptr;
@@ -1071,7 +1151,7 @@ __global__ __launch_bounds__(256) void k_moe_pf2(GW2Args a) {
     const int nu = pf_unit_count(nct, a.tiles);
     for (int u = blockIdx.x; u < nu; u += gridDim.x) {
         int gs, rt, n0;
-        if (pf_unit(a.grp, a.ctg, a.Gmax, sh, nct, u, a.tiles, gs, rt, n0)) pf2_unit(a, gs, rt, n0, hs);
+        if (pf_unit(a.grp, a.ctg, a.Gmax, sh, nct, u, a.tiles, gs, rt, n0)) pf2_unit<FMT, SB>(a, gs, rt, n0, hs);
     }
 }
 
@@ -1722,12 +1802,18 @@ static_assert(W4_PF_BLOCKS % 8 == 0, "the large-batch unit order assumes a grid 
 
 void launch_pf13(GW13Args &a, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
     a.tiles = a.I / PF_ROWS;
-    go_ev(st, e0, e1, k_moe_pf13, dim3(W4_PF_BLOCKS), dim3(256), 0, a);
+    const dim3 g(W4_PF_BLOCKS), b(256);
+    const bool nv = a.fmt == FMT_NVFP4;
+    if (a.s_bf16) go_ev(st, e0, e1, nv ? k_moe_pf13<FMT_NVFP4, true> : k_moe_pf13<FMT_E2M1, true>, g, b, 0, a);
+    else go_ev(st, e0, e1, nv ? k_moe_pf13<FMT_NVFP4, false> : k_moe_pf13<FMT_E2M1, false>, g, b, 0, a);
 }
 
 void launch_pf2(GW2Args &a, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
     a.tiles = a.H / PF_ROWS;
-    go_ev(st, e0, e1, k_moe_pf2, dim3(W4_PF_BLOCKS), dim3(256), 0, a);
+    const dim3 g(W4_PF_BLOCKS), b(256);
+    const bool nv = a.fmt == FMT_NVFP4;
+    if (a.s_bf16) go_ev(st, e0, e1, nv ? k_moe_pf2<FMT_NVFP4, true> : k_moe_pf2<FMT_E2M1, true>, g, b, 0, a);
+    else go_ev(st, e0, e1, nv ? k_moe_pf2<FMT_NVFP4, false> : k_moe_pf2<FMT_E2M1, false>, g, b, 0, a);
 }
 
 void launch_mx_quant(MXQuantArgs &a, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {

@@ -100,6 +100,10 @@ QWEN_MOE_T32_MX = MoEShape("qwen3.6-35b-a3b-moe-batch32-zipf1.1-mxfp4", 2048, 51
 # expert (no popularity bias), the MFMA-bound regime of the grouped path
 QWEN_MOE_PREFILL = MoEShape("qwen3.6-35b-a3b-moe-prefill2048", 2048, 512, 256, 8, 512, 2048, 0.0, 0)
 QWEN_MOE_PREFILL_MX = MoEShape("qwen3.6-35b-a3b-moe-prefill2048-mxfp4", 2048, 512, 256, 8, 512, 2048, 0.0, 0, "mxfp4")
+QWEN_MOE_PREFILL_NVFP4 = MoEShape("qwen3.6-35b-a3b-moe-prefill2048-nvfp4", 2048, 512, 256, 8, 512, 2048, 0.0, 0,
+                                  "nvfp4")
+QWEN_MOE_PREFILL_BF16SH = MoEShape("qwen3.6-35b-a3b-moe-prefill2048-bf16shared", 2048, 512, 256, 8, 512, 2048, 0.0, 0,
+                                   "e2m1", "bf16")
 
 
 # --------------------------------------------------------------------------- draws

@@ -301,12 +301,12 @@ def test_moe_bf16_shared_expert(shape):
 
 
 def test_moe_bf16_shared_expert_batches():
-    """Tiny layer: grouped batches (the shared expert a 300-row bf16 MFMA group)
-    and, past 4096 pairs, the single-token path."""
+    """Tiny layer: grouped batches (the shared expert a bf16 MFMA group of T
+    rows), past 4096 pairs with the three-launch grouping."""
     shape = synth.TINY_MOE_BF16SH
     dev_layer = wl.build_moe_layer(shape, device=DEV)
     or_layer = oracle_layer(shape)
-    for T, stages in ((300, 5), (2048, 5), (2049, 3)):  # top-2: 4096 pairs at T = 2048
+    for T, stages in ((300, 5), (2048, 5), (2049, 7)):  # top-2: 4096 pairs at T = 2048
         print(f"bf16 shared tiny T={T}", flush=True)
         assert w4.moe_w4a16_stage_count(dev_layer, T) == stages, T
         _check_moe(shape, dev_layer, or_layer, tie_free_tokens(shape, or_layer, T, first=500), f"bf16 shared T={T}")

@@ -3,7 +3,7 @@ router as an MFMA GEMM, the grouping over three launches (per-block top-k and
 expert histograms, one scan, a scatter), and the grouped expert kernels with
 groups of hundreds of rows.  Routing ids are compared for every token; outputs
 for every token of the tiny layer and for sampled tokens of the 35B-A3B-shaped
-layer (E2M1 and MX)."""
+layer (E2M1, NVFP4, a bf16 shared expert, and MX)."""
 
 import numpy as np
 import pytest
@@ -37,18 +37,21 @@ def _check_routing(or_layer, xb, ids, wts, K):
         np.testing.assert_allclose(wts[t], rw, rtol=2e-6, atol=1e-7)
 
 
-def test_prefill_tiny_every_token():
-    """Tiny layer (8 experts, top-2), T = 3000: 6000 pairs, groups of ~750 rows."""
-    shape = synth.MoEShape("tiny-prefill-3000", 256, 128, 8, 2, 128, 3000, 0.0, 11)
+@pytest.mark.parametrize("fmt,shared_fmt", [("e2m1", None), ("nvfp4", None), ("e2m1", "bf16"), ("nvfp4", "bf16")])
+def test_prefill_tiny_every_token(fmt, shared_fmt):
+    """Tiny layer (8 experts, top-2), T = 3000: 6000 pairs, groups of ~750 rows;
+    E2M1 or NVFP4 routed experts, the shared expert in their format or bf16."""
+    shape = synth.MoEShape("tiny-prefill-3000", 256, 128, 8, 2, 128, 3000, 0.0, 11, fmt, shared_fmt)
     dev_layer = wl.build_moe_layer(shape, device=DEV)
     assert w4.moe_w4a16_stage_count(dev_layer, 3000) == 7
     or_layer = oracle_layer(shape)
     xb = tie_free_tokens(shape, or_layer, 3000)
-    print("tiny prefill T=3000", flush=True)
+    what = f"tiny prefill T=3000 {fmt} shared {shared_fmt or fmt}"
+    print(what, flush=True)
     y, ids, wts = _run(dev_layer, xb, shape.top_k)
     _check_routing(or_layer, xb, ids, wts, shape.top_k)
     ref, _, _ = ops.moe_forward(or_layer, xb)
-    print(assert_bf16_close(y, ref, "tiny prefill T=3000"), flush=True)
+    print(assert_bf16_close(y, ref, what), flush=True)
 
 
 def test_prefill_tiny_experts_entry_with_invalid_ids():
@@ -79,7 +82,8 @@ def test_prefill_tiny_experts_entry_with_invalid_ids():
     print(assert_bf16_close(wl.bf16_bits(y)[sample], ref, "tiny prefill experts entry"), flush=True)
 
 
-@pytest.mark.parametrize("shape", [synth.QWEN_MOE_PREFILL], ids=lambda s: s.name)
+@pytest.mark.parametrize("shape", [synth.QWEN_MOE_PREFILL, synth.QWEN_MOE_PREFILL_NVFP4, synth.QWEN_MOE_PREFILL_BF16SH],
+                         ids=lambda s: s.name)
 def test_prefill_full_sampled(shape):
     """35B-A3B shape, T = 2048 (16,384 pairs): ids for every token, outputs for 8."""
     dev_layer = wl.build_moe_layer(shape, device=DEV)

@@ -217,17 +217,16 @@ def test_mxfp4_layer_plan_and_validation():
 
 
 def test_bf16_shared_expert_plan():
-    """A bf16 shared expert joins the grouped path up to 4096 (token, slot)
-    pairs (its rows are MFMA operands there); larger batches take the
-    single-token path, which streams bf16 rows too."""
+    """A bf16 shared expert joins the grouped path (its rows are MFMA operands
+    there), past 4096 (token, slot) pairs with the three-launch grouping."""
     bf = w4.W4_FMT_BF16
     for fmt in (w4.W4_FMT_E2M1_F16S16, w4.W4_FMT_NVFP4_E4M3S16):
         g = 1 << 22 if fmt == w4.W4_FMT_NVFP4_E4M3S16 else None
         L = _layer(w13=_mat(fmt=fmt, groups=8, n=256, k=256, gsc=g), w2=_mat(fmt=fmt, groups=8, n=256, k=128, gsc=g),
                    shared_w13=_mat(fmt=bf, groups=1, n=256, k=256, scales=None),
                    shared_w2=_mat(fmt=bf, groups=1, n=256, k=128, scales=None))
-        got = [w4.lib().moe_w4a16_stage_count(C.byref(L), T) for T in (1, 3, 4, 2048, 2049)]
-        assert got == [3, 3, 5, 5, 3], (fmt, got)
+        got = [w4.lib().moe_w4a16_stage_count(C.byref(L), T) for T in (1, 3, 4, 2048, 2049, 16384)]
+        assert got == [3, 3, 5, 5, 7, 7], (fmt, got)
 
 
 def test_bf16_format_quantiser_sizes_and_rules():
