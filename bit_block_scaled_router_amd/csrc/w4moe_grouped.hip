@@ -213,23 +213,44 @@ __global__ __launch_bounds__(256) void k_route_topk(RouteArgs r) {
 // cntb becomes each block's base inside the expert's list) and the expert's
 // total; then the group table and each expert's list start.
 __global__ __launch_bounds__(1024) void k_route_scan(RouteArgs r) {
-    __shared__ int tot[1024], off[1024];
+    __shared__ int tot[1024], off[1024], part[1024];
     const int E = r.g.E, Gmax = r.g.Gmax;
     const int tid = threadIdx.x;
-    for (int e = tid; e < E; e += blockDim.x) {
-        int run = 0;
-        for (int b0 = 0; b0 < r.nblk; b0 += 16) {  // 16 loads in flight, then the running sums
+    // F threads per expert, each owning a contiguous range of the blocks: the
+    // range sums first (16 loads in flight), then each thread rewrites its range
+    // as running sums from the sums of the ranges before it
+    int F = 1;
+    while (2 * F * E <= (int)blockDim.x && F < 16) F *= 2;
+    const int e = tid % E, f = tid / E;
+    const int per = (r.nblk + F - 1) / F, b_lo = f * per, b_hi = min(r.nblk, b_lo + per);
+    const bool act = f < F;
+    int sum = 0;
+    if (act) {
+        for (int b0 = b_lo; b0 < b_hi; b0 += 16) {
             int c[16];
 #pragma unroll
-            for (int i = 0; i < 16; ++i) c[i] = b0 + i < r.nblk ? r.cntb[(size_t)(b0 + i) * E + e] : 0;
+            for (int i = 0; i < 16; ++i) c[i] = b0 + i < b_hi ? r.cntb[(size_t)(b0 + i) * E + e] : 0;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) sum += c[i];
+        }
+        part[f * E + e] = sum;
+    }
+    __syncthreads();
+    if (act) {
+        int run = 0;
+        for (int g = 0; g < f; ++g) run += part[g * E + e];
+        for (int b0 = b_lo; b0 < b_hi; b0 += 16) {
+            int c[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) c[i] = b0 + i < b_hi ? r.cntb[(size_t)(b0 + i) * E + e] : 0;
 #pragma unroll
             for (int i = 0; i < 16; ++i)
-                if (b0 + i < r.nblk) {
+                if (b0 + i < b_hi) {
                     r.cntb[(size_t)(b0 + i) * E + e] = run;
                     run += c[i];
                 }
         }
-        tot[e] = run;
+        if (f == F - 1) tot[e] = run;
     }
     __syncthreads();
     if (tid < 64) {
