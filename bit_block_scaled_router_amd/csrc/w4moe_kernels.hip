@@ -683,6 +683,7 @@ int hip_status(const char *what) {
 #ifndef W4_GEMV_WPB
 #define W4_GEMV_WPB 4  // waves per block of the dense GEMV
 #endif
+static_assert(W4_GEMV_WPB >= 1 && W4_GEMV_WPB * 64 <= 256, "k_gemv is compiled for blocks of at most 256 threads");
 
 template <int FMT, int L>
 void launch_gemv_L(const w4_matrix *W, const uint16_t *x, int m, uint16_t *y, hipStream_t st) {
@@ -895,6 +896,7 @@ int launch_router(const moe_w4a16_layer *Lr, const MoEPlan &p, const uint16_t *x
 #ifndef W4_W13_WPB
 #define W4_W13_WPB 4  // waves per block of the W13 kernel
 #endif
+static_assert(W4_W13_WPB >= 1 && W4_W13_WPB <= 16, "k_moe_w13 is compiled for blocks of at most 1024 threads");
 
 template <int FMT, int L>
 void launch_w13_L(const MoEPlan &p, W13Args &a, const Launch &st) {
@@ -937,6 +939,7 @@ void launch_w13(const MoEPlan &p, W13Args &a, const Launch &st) {
 #ifndef W4_DOWN_WAVES
 #define W4_DOWN_WAVES 16  // at most this many waves per block; the slots are spread over them
 #endif
+static_assert(W4_DOWN_WAVES >= 1 && W4_DOWN_WAVES <= 16, "k_moe_down is compiled for blocks of at most 1024 threads");
 
 template <int FMT, int L>
 void launch_down_L(const MoEPlan &p, DownArgs &a, const Launch &st) {
