@@ -377,12 +377,13 @@ def workload_shapes(synth):
             "gemv-lmhead": synth.GEMV_LMHEAD, "qwen-t1-bf16shared": synth.QWEN_MOE_T1_BF16SH,
             "qwen-t1-mxfp4": synth.QWEN_MOE_T1_MX, "qwen-t32-mxfp4": synth.QWEN_MOE_T32_MX,
             "qwen-prefill": synth.QWEN_MOE_PREFILL, "qwen-prefill-mxfp4": synth.QWEN_MOE_PREFILL_MX,
-            "qwen-t32-nvfp4": synth.QWEN_MOE_T32_NVFP4, "qwen-t32-bf16shared": synth.QWEN_MOE_T32_BF16SH}
+            "qwen-t32-nvfp4": synth.QWEN_MOE_T32_NVFP4, "qwen-t32-bf16shared": synth.QWEN_MOE_T32_BF16SH,
+            "qwen-t32-int4": synth.QWEN_MOE_T32_INT4}
 
 
 WORKLOADS = ["qwen-t1", "qwen-t32", "tiny", "gemv-e2m1", "gemv-int4", "qwen-t1-nvfp4", "gemv-nvfp4", "gemv-lmhead",
              "qwen-t1-bf16shared", "qwen-t1-mxfp4", "qwen-t32-mxfp4", "qwen-prefill", "qwen-prefill-mxfp4",
-             "qwen-t32-nvfp4", "qwen-t32-bf16shared"]
+             "qwen-t32-nvfp4", "qwen-t32-bf16shared", "qwen-t32-int4"]
 
 
 def run_moe(args, torch, w4, wl, synth):

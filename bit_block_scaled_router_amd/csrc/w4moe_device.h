@@ -16,6 +16,7 @@
 namespace w4k {
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int FMT_E2M1 = 1;
@@ -78,6 +79,22 @@ __device__ __forceinline__ bf16x2 u4x2_bf16(uint32_t bytes) {
 template <bool W>
 __device__ __forceinline__ f32x2 u4x2_f32(uint32_t bytes) {
     return __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(bytes, 512.0f, W);
+}
+
+// 8 int4 codes of one dword (element i in nibble i) -> their offset values
+// u = q + 8 in [0, 15], exact in bf16, in element order (an MFMA operand).
+__device__ __forceinline__ bf16x8 u4x8_bf16(uint32_t c) {
+    uint32_t lo, hi;
+    int4_split(c, lo, hi);                                          // lo: elements 0,2,4,6; hi: 1,3,5,7
+    const uint32_t a = __builtin_amdgcn_perm(hi, lo, 0x05010400u);  // elements 0 1 2 3, one per byte
+    const uint32_t b = __builtin_amdgcn_perm(hi, lo, 0x07030602u);  // elements 4 5 6 7
+    const bf16x2 p0 = u4x2_bf16<false>(a), p1 = u4x2_bf16<true>(a), p2 = u4x2_bf16<false>(b), p3 = u4x2_bf16<true>(b);
+    return bf16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+}
+
+// bf16 8.0 in all eight elements: the int4 offset as an MFMA operand.
+__device__ __forceinline__ bf16x8 bf16x8_splat8() {
+    return __builtin_bit_cast(bf16x8, make_uint4(0x41004100u, 0x41004100u, 0x41004100u, 0x41004100u));
 }
 
 // ---------------------------------------------------------------- reductions
@@ -569,7 +586,6 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
 
 // ---------------------------------------------------------------- MFMA helpers
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 // D += A(16x32) B(32x16), bf16 in, fp32 accumulate.  Lane i holds

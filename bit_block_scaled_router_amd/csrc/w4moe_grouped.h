@@ -59,7 +59,7 @@ struct GW13Args {
     uint16_t *h_lo;
     int H, I, K, T, P, Gmax, tiles, mfma_min;
     const int32_t *ctg;     // column tiles (large-batch kernels only)
-    int fmt;                // FMT_E2M1 or FMT_NVFP4 (gw13 / gw2)
+    int fmt;                // FMT_E2M1, FMT_NVFP4 or FMT_INT4 (gw13 / gw2; the large-batch kernels: not INT4)
     const float *gs, *s_gs; // NVFP4 global scales: routed [E], shared [1]
     int s_bf16;             // the shared expert is bf16 (s_codes = bf16 rows, no scales)
 };
@@ -76,7 +76,7 @@ struct GW2Args {
     float *out;             // [P + T][H]
     int H, I, K, T, P, Gmax, tiles, mfma_min;
     const int32_t *ctg;     // column tiles (large-batch kernels only)
-    int fmt;                // FMT_E2M1 or FMT_NVFP4
+    int fmt;                // as GW13Args
     const float *gs, *s_gs; // NVFP4 global scales: routed [E], shared [1]
     int s_bf16;             // the shared expert is bf16 (s_codes = bf16 rows, no scales)
 };

@@ -40,8 +40,8 @@ namespace w4k {
 constexpr int KS_VALU = 2;
 #ifndef W4_GW_MINBLK
 #define W4_GW_MINBLK 3  // blocks per CU the batched W13 / W2 kernels are compiled to fit
-#endif                  // (W2 with I > 512, and layers with a bf16 shared expert, fit 2 or 1:
-                        // fitting 3 would spill)
+#endif                  // (W2 with I > 512, int4 layers, and layers with a bf16 shared expert
+                        // fit 2 or 1: fitting 3 would spill)
 
 // ================================================================= route + group
 
@@ -358,7 +358,7 @@ __device__ __forceinline__ void gw13_unit(const GW13Args &a, int gs, int tile, f
     const int lane = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int H = a.H, I = a.I;
-    const uint32_t spr = (uint32_t)(H >> 4);
+    const uint32_t spr = (uint32_t)scales_per_row<FMT>(H);
     const size_t mat_codes = (size_t)(2 * I) * (H >> 1), mat_scales = (size_t)(2 * I) * spr;
     const GroupView<SC> gv = group_view(a.grp, gs, a.Gmax, a.P, a.T, a.codes, reinterpret_cast<const SC *>(a.scales),
                                         mat_codes, mat_scales, a.s_codes, reinterpret_cast<const SC *>(a.s_scales));
@@ -386,7 +386,7 @@ __device__ __forceinline__ void gw13_unit(const GW13Args &a, int gs, int tile, f
                 // two 16-column tiles: pairs n0 + lane%16 and n0 + 16 + lane%16
                 int pr[2], tk[2];
                 bool pv[2];
-    #pragma unroll
+#pragma unroll
                 for (int nt = 0; nt < 2; ++nt) {
                     const int idx = n0 + nt * 16 + r;
                     pv[nt] = idx < gv.m;
@@ -400,21 +400,21 @@ __device__ __forceinline__ void gw13_unit(const GW13Args &a, int gs, int tile, f
                     const int k0 = c * 128 + 32 * q;  // this lane's 32 elements
                     // B: 32 activations of each column token
                     uint4 xb[2][4];
-    #pragma unroll
+#pragma unroll
                     for (int nt = 0; nt < 2; ++nt) {
                         const uint32_t xo = (uint32_t)(tk[nt] * H + k0) * 2u;
-    #pragma unroll
+#pragma unroll
                         for (int s = 0; s < 4; ++s)
                             xb[nt][s] = (nt == 0 || two) ? ld128(xall, pv[nt] ? xo + 16u * s : OOB) : make_uint4(0, 0, 0, 0);
                     }
                     if constexpr (SBF) {  // bf16 rows, 8 weights per MFMA step
                         const uint32_t rb = (uint32_t)H * 2u;
-    #pragma unroll
+#pragma unroll
                         for (int s = 0; s < 4; ++s) {
                             const uint32_t ko = (uint32_t)(k0 + 8 * s) * 2u;
                             const bf16x8 wg = __builtin_bit_cast(bf16x8, ld128(cb, rg_ok ? rowg * rb + ko : OOB));
                             const bf16x8 wu = __builtin_bit_cast(bf16x8, ld128(cb, rg_ok ? rowu * rb + ko : OOB));
-    #pragma unroll
+#pragma unroll
                             for (int nt = 0; nt < 2; ++nt) {
                                 if (nt == 1 && !two) break;
                                 const bf16x8 b = __builtin_bit_cast(bf16x8, xb[nt][s]);
@@ -426,16 +426,56 @@ __device__ __forceinline__ void gw13_unit(const GW13Args &a, int gs, int tile, f
                     }
                     const uint4 cg = ld128(cb, rg_ok ? rowg * (uint32_t)(H >> 1) + (uint32_t)(k0 >> 1) : OOB);
                     const uint4 cu = ld128(cb, rg_ok ? rowu * (uint32_t)(H >> 1) + (uint32_t)(k0 >> 1) : OOB);
+                    if constexpr (FMT == FMT_INT4) {
+                        // the chunk is one scale group: MFMAs on the raw offset codes
+                        // u = q + 8 (exact bf16) and on 8 (the offset), then the
+                        // difference times the scales of the lane's output rows
+                        float so_g[4], so_u[4];
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) {
+                            const uint32_t o = (uint32_t)(i0 + 4 * q + j);
+                            const bool ov = o < (uint32_t)I;
+                            so_g[j] = f16_bits_to_f32(ld16(sb, ov ? (o * spr + (uint32_t)c) * 2u : OOB));
+                            so_u[j] = f16_bits_to_f32(ld16(sb, ov ? (((uint32_t)I + o) * spr + (uint32_t)c) * 2u : OOB));
+                        }
+                        const uint32_t cgw[4] = {cg.x, cg.y, cg.z, cg.w}, cuw[4] = {cu.x, cu.y, cu.z, cu.w};
+                        f32x4 tg[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}}, tu[2] = {tg[0], tg[0]},
+                              tc[2] = {tg[0], tg[0]};
+#pragma unroll
+                        for (int s = 0; s < 4; ++s) {
+                            const bf16x8 ug = u4x8_bf16(cgw[s]), uu = u4x8_bf16(cuw[s]);
+                            // both column tiles unconditionally (a missing second tile has
+                            // zero activations): the chunk's sums are read right after
+                            // these MFMAs, and straight-line code keeps the compiler's
+                            // MFMA-result wait states in place (behind a branch they were
+                            // not, and the first read saw a stale accumulator)
+#pragma unroll
+                            for (int nt = 0; nt < 2; ++nt) {
+                                const bf16x8 b = __builtin_bit_cast(bf16x8, xb[nt][s]);
+                                tg[nt] = mfma16x16x32(ug, b, tg[nt]);
+                                tu[nt] = mfma16x16x32(uu, b, tu[nt]);
+                                tc[nt] = mfma16x16x32(bf16x8_splat8(), b, tc[nt]);
+                            }
+                        }
+#pragma unroll
+                        for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+                            for (int j = 0; j < 4; ++j) {
+                                ag[nt][j] = fmaf(so_g[j], tg[nt][j] - tc[nt][j], ag[nt][j]);
+                                au[nt][j] = fmaf(so_u[j], tu[nt][j] - tc[nt][j], au[nt][j]);
+                            }
+                        continue;
+                    }
                     const uint32_t sg = ld_scales<FMT>(sb, rg_ok ? scale_off<FMT>(rowg * spr, k0) : OOB);
                     const uint32_t su = ld_scales<FMT>(sb, rg_ok ? scale_off<FMT>(rowu * spr, k0) : OOB);
                     const uint32_t cgw[4] = {cg.x, cg.y, cg.z, cg.w}, cuw[4] = {cu.x, cu.y, cu.z, cu.w};
-    #pragma unroll
+#pragma unroll
                     for (int s = 0; s < 4; ++s) {
                         if constexpr (FMT == FMT_NVFP4) {
                             const f32x2 sgv = block_scales2<FMT>(sg), suv = block_scales2<FMT>(su);
                             const bf16x8 ag1 = e2m1x8_scaled(cgw[s], s < 2 ? sgv.x : sgv.y);
                             const bf16x8 au1 = e2m1x8_scaled(cuw[s], s < 2 ? suv.x : suv.y);
-    #pragma unroll
+#pragma unroll
                             for (int nt = 0; nt < 2; ++nt) {
                                 if (nt == 1 && !two) break;
                                 const bf16x8 b = __builtin_bit_cast(bf16x8, xb[nt][s]);
@@ -449,7 +489,7 @@ __device__ __forceinline__ void gw13_unit(const GW13Args &a, int gs, int tile, f
                             bf16x8 agh, agl, auh, aul;
                             e2m1x8_split(cgw[s], gh, gl, agh, agl);
                             e2m1x8_split(cuw[s], uh, ul, auh, aul);
-    #pragma unroll
+#pragma unroll
                             for (int nt = 0; nt < 2; ++nt) {
                                 if (nt == 1 && !two) break;
                                 const bf16x8 b = __builtin_bit_cast(bf16x8, xb[nt][s]);
@@ -463,9 +503,9 @@ __device__ __forceinline__ void gw13_unit(const GW13Args &a, int gs, int tile, f
                 }
                 // fixed-order sum of the four K partials
                 if (wv > 0) {
-    #pragma unroll
+#pragma unroll
                     for (int nt = 0; nt < 2; ++nt)
-    #pragma unroll
+#pragma unroll
                         for (int j = 0; j < 4; ++j) {
                             red[wv - 1][nt * 8 + j][lane] = ag[nt][j];
                             red[wv - 1][nt * 8 + 4 + j][lane] = au[nt][j];
@@ -473,23 +513,23 @@ __device__ __forceinline__ void gw13_unit(const GW13Args &a, int gs, int tile, f
                 }
                 __syncthreads();
                 if (wv == 0) {
-    #pragma unroll
+#pragma unroll
                     for (int w = 0; w < 3; ++w)
-    #pragma unroll
+#pragma unroll
                         for (int nt = 0; nt < 2; ++nt)
-    #pragma unroll
+#pragma unroll
                             for (int j = 0; j < 4; ++j) {
                                 ag[nt][j] += red[w][nt * 8 + j][lane];
                                 au[nt][j] += red[w][nt * 8 + 4 + j][lane];
                             }
                     // lane holds rows i0 + 4q + j of column r
-    #pragma unroll
+#pragma unroll
                     for (int nt = 0; nt < 2; ++nt) {
                         const int idx = n0 + nt * 16 + r;
                         if (idx < gv.m) {
                             const int p = plist[idx];
                             float hv[4];
-    #pragma unroll
+#pragma unroll
                             for (int j = 0; j < 4; ++j) {
                                 float gg = ag[nt][j], uu = au[nt][j];
                                 if constexpr (FMT == FMT_NVFP4) gg *= gsc, uu *= gsc;
@@ -497,7 +537,7 @@ __device__ __forceinline__ void gw13_unit(const GW13Args &a, int gs, int tile, f
                             }
                             // I is a multiple of 128 (host check): rows i0 + 4q .. +3 all exist
                             uint16_t bh[4], bl[4];
-    #pragma unroll
+#pragma unroll
                             for (int j = 0; j < 4; ++j) split_bf16(hv[j], bh[j], bl[j]);
                             const size_t o = (size_t)p * I + i0 + 4 * q;
                             *reinterpret_cast<uint2 *>(a.h_hi + o) =
@@ -553,6 +593,7 @@ __device__ __forceinline__ void gw13_unit(const GW13Args &a, int gs, int tile, f
             const int k0 = 32 * (L * s + lk);
             XSlice<FMT> xs;
             load_xslice<FMT>(xs, xb, k0 < H ? (uint32_t)k0 * 2u : OOB);
+            prep_xslice<FMT>(xs);
 #pragma unroll
             for (int l = 0; l < NLG; ++l) {
                 accg[l] = chunk_dot_bf16<FMT>(cg[s][l], sg[s][l], xs, accg[l]);
@@ -577,7 +618,7 @@ __device__ __forceinline__ void gw13_unit(const GW13Args &a, int gs, int tile, f
 // Blocks walk the work units (group slot x row tile) with a grid stride, so the
 // grid needs no bound on the number of active experts.
 template <int FMT, int L, bool SB>
-__global__ __launch_bounds__(256, SB ? 2 : W4_GW_MINBLK) void k_moe_gw13(GW13Args a) {
+__global__ __launch_bounds__(256, FMT == FMT_INT4 ? 1 : SB ? 2 : W4_GW_MINBLK) void k_moe_gw13(GW13Args a) {
     __shared__ float red[3][16][64];  // MFMA K-split partials of waves 1..3
     const int nu = unit_count(a.grp, a.s_codes != nullptr, a.tiles);
     for (int u = blockIdx.x; u < nu; u += gridDim.x) {
@@ -597,7 +638,7 @@ __device__ __forceinline__ void gw2_unit(const GW2Args &a, int gs, int tile, flo
     const int lane = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int H = a.H, I = a.I;
-    const uint32_t spr = (uint32_t)(I >> 4);
+    const uint32_t spr = (uint32_t)scales_per_row<FMT>(I);
     const size_t mat_codes = (size_t)H * (I >> 1), mat_scales = (size_t)H * spr;
     const GroupView<SC> gv = group_view(a.grp, gs, a.Gmax, a.P, a.T, a.codes, reinterpret_cast<const SC *>(a.scales),
                                         mat_codes, mat_scales, a.s_codes, reinterpret_cast<const SC *>(a.s_scales));
@@ -623,7 +664,7 @@ __device__ __forceinline__ void gw2_unit(const GW2Args &a, int gs, int tile, flo
             for (int n0 = 0; n0 < gv.m; n0 += 32) {
                 int pr[2];
                 bool pv[2];
-    #pragma unroll
+#pragma unroll
                 for (int nt = 0; nt < 2; ++nt) {
                     const int idx = n0 + nt * 16 + r;
                     pv[nt] = idx < gv.m;
@@ -631,14 +672,14 @@ __device__ __forceinline__ void gw2_unit(const GW2Args &a, int gs, int tile, flo
                 }
                 const bool two = n0 + 16 < gv.m;  // second column tile in use (uniform)
                 f32x4 acc[4][2];
-    #pragma unroll
+#pragma unroll
                 for (int rt = 0; rt < 4; ++rt) acc[rt][0] = acc[rt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
                 for (int c = wv; c < nchunks; c += 4) {
                     const int k0 = c * 128 + 32 * q;
                     uint4 cw[4];
                     uint32_t sc[4];
                     if constexpr (!SBF) {
-    #pragma unroll
+#pragma unroll
                         for (int rt = 0; rt < 4; ++rt) {
                             const int rr = u0 + 16 * rt + r;
                             const bool rv = rr < H;
@@ -647,10 +688,10 @@ __device__ __forceinline__ void gw2_unit(const GW2Args &a, int gs, int tile, flo
                         }
                     }
                     uint4 bh[2][4], bl[2][4];
-    #pragma unroll
+#pragma unroll
                     for (int nt = 0; nt < 2; ++nt) {
                         const uint32_t ho = (uint32_t)(pr[nt] * I + k0) * 2u;
-    #pragma unroll
+#pragma unroll
                         for (int s = 0; s < 4; ++s) {
                             const bool on = nt == 0 || two;
                             bh[nt][s] = on ? ld128(hhi, pv[nt] ? ho + 16u * s : OOB) : make_uint4(0, 0, 0, 0);
@@ -658,15 +699,15 @@ __device__ __forceinline__ void gw2_unit(const GW2Args &a, int gs, int tile, flo
                         }
                     }
                     if constexpr (SBF) {  // bf16 rows: the weights are the operands; h as hi + lo
-    #pragma unroll
+#pragma unroll
                         for (int rt = 0; rt < 4; ++rt) {
                             const int rr = u0 + 16 * rt + r;
                             const bool rv = rr < H;
-    #pragma unroll
+#pragma unroll
                             for (int s = 0; s < 4; ++s) {
                                 const uint32_t o = (uint32_t)rr * (uint32_t)I * 2u + (uint32_t)(k0 + 8 * s) * 2u;
                                 const bf16x8 w = __builtin_bit_cast(bf16x8, ld128(cb, rv ? o : OOB));
-    #pragma unroll
+#pragma unroll
                                 for (int nt = 0; nt < 2; ++nt) {
                                     if (nt == 1 && !two) break;
                                     acc[rt][nt] = mfma16x16x32(w, __builtin_bit_cast(bf16x8, bh[nt][s]), acc[rt][nt]);
@@ -676,15 +717,53 @@ __device__ __forceinline__ void gw2_unit(const GW2Args &a, int gs, int tile, flo
                         }
                         continue;
                     }
-    #pragma unroll
+                    if constexpr (FMT == FMT_INT4) {
+                        // as in gw13: raw offset codes and the offset 8 on the MFMA,
+                        // the difference times the output rows' scales of the chunk
+                        f32x4 tcor[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+                        for (int s = 0; s < 4; ++s)
+#pragma unroll
+                            for (int nt = 0; nt < 2; ++nt) {  // both tiles: no branch before the reads below
+                                tcor[nt] = mfma16x16x32(bf16x8_splat8(), __builtin_bit_cast(bf16x8, bh[nt][s]), tcor[nt]);
+                                tcor[nt] = mfma16x16x32(bf16x8_splat8(), __builtin_bit_cast(bf16x8, bl[nt][s]), tcor[nt]);
+                            }
+#pragma unroll
+                        for (int rt = 0; rt < 4; ++rt) {
+                            float so[4];
+#pragma unroll
+                            for (int j = 0; j < 4; ++j) {
+                                const uint32_t o = (uint32_t)(u0 + 16 * rt + 4 * q + j);
+                                so[j] = f16_bits_to_f32(ld16(sb, o < (uint32_t)H ? (o * spr + (uint32_t)c) * 2u : OOB));
+                            }
+                            const uint32_t cws[4] = {cw[rt].x, cw[rt].y, cw[rt].z, cw[rt].w};
+                            f32x4 t[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+                            for (int s = 0; s < 4; ++s) {
+                                const bf16x8 u = u4x8_bf16(cws[s]);
+#pragma unroll
+                                for (int nt = 0; nt < 2; ++nt) {
+                                    t[nt] = mfma16x16x32(u, __builtin_bit_cast(bf16x8, bh[nt][s]), t[nt]);
+                                    t[nt] = mfma16x16x32(u, __builtin_bit_cast(bf16x8, bl[nt][s]), t[nt]);
+                                }
+                            }
+#pragma unroll
+                            for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+                                for (int j = 0; j < 4; ++j)
+                                    acc[rt][nt][j] = fmaf(so[j], t[nt][j] - tcor[nt][j], acc[rt][nt][j]);
+                        }
+                        continue;
+                    }
+#pragma unroll
                     for (int rt = 0; rt < 4; ++rt) {
                         const uint32_t cws[4] = {cw[rt].x, cw[rt].y, cw[rt].z, cw[rt].w};
-    #pragma unroll
+#pragma unroll
                         for (int s = 0; s < 4; ++s) {
                             if constexpr (FMT == FMT_NVFP4) {
                                 const f32x2 sv = block_scales2<FMT>(sc[rt]);
                                 const bf16x8 a1 = e2m1x8_scaled(cws[s], s < 2 ? sv.x : sv.y);
-    #pragma unroll
+#pragma unroll
                                 for (int nt = 0; nt < 2; ++nt) {
                                     if (nt == 1 && !two) break;
                                     acc[rt][nt] = mfma16x16x32(a1, __builtin_bit_cast(bf16x8, bh[nt][s]), acc[rt][nt]);
@@ -695,7 +774,7 @@ __device__ __forceinline__ void gw2_unit(const GW2Args &a, int gs, int tile, flo
                                 split_scale(f16_bits_to_f32(s < 2 ? sc[rt] : (sc[rt] >> 16)), sh, sl);
                                 bf16x8 ah, al;
                                 e2m1x8_split(cws[s], sh, sl, ah, al);
-    #pragma unroll
+#pragma unroll
                                 for (int nt = 0; nt < 2; ++nt) {
                                     if (nt == 1 && !two) break;
                                     const bf16x8 b0 = __builtin_bit_cast(bf16x8, bh[nt][s]);
@@ -713,34 +792,34 @@ __device__ __forceinline__ void gw2_unit(const GW2Args &a, int gs, int tile, flo
                     }
                 }
                 // partials of all waves -> LDS; wave w sums row tile w in wave order
-    #pragma unroll
+#pragma unroll
                 for (int rt = 0; rt < 4; ++rt)
-    #pragma unroll
+#pragma unroll
                     for (int nt = 0; nt < 2; ++nt)
-    #pragma unroll
+#pragma unroll
                         for (int j = 0; j < 4; ++j) red[wv][rt][nt * 4 + j][lane] = acc[rt][nt][j];
                 __syncthreads();
                 float v[2][4];
-    #pragma unroll
+#pragma unroll
                 for (int nt = 0; nt < 2; ++nt)
-    #pragma unroll
+#pragma unroll
                     for (int j = 0; j < 4; ++j) {
                         float t = red[0][wv][nt * 4 + j][lane];
-    #pragma unroll
+#pragma unroll
                         for (int w = 1; w < 4; ++w) t += red[w][wv][nt * 4 + j][lane];
                         v[nt][j] = t * gsc;
                     }
                 __syncthreads();  // red is reused by the next pass or unit
                 // lane holds rows u0 + 16wv + 4q + j of column r
                 const int rb = u0 + 16 * wv + 4 * q;
-    #pragma unroll
+#pragma unroll
                 for (int nt = 0; nt < 2; ++nt) {
                     if (!pv[nt]) continue;
                     float *op = a.out + (size_t)pr[nt] * H + rb;
                     if (rb + 3 < H) {
                         *reinterpret_cast<float4 *>(op) = make_float4(v[nt][0], v[nt][1], v[nt][2], v[nt][3]);
                     } else {
-    #pragma unroll
+#pragma unroll
                         for (int j = 0; j < 4; ++j)
                             if (rb + j < H) op[j] = v[nt][j];
                     }
@@ -788,6 +867,8 @@ __device__ __forceinline__ void gw2_unit(const GW2Args &a, int gs, int tile, flo
             XSlice<FMT> xh, xl;
             load_xslice<FMT>(xh, hhi, k0 < I ? ho : OOB);
             load_xslice<FMT>(xl, hlo, k0 < I ? ho : OOB);
+            prep_xslice<FMT>(xh);
+            prep_xslice<FMT>(xl);
 #pragma unroll
             for (int l = 0; l < NLG; ++l) {
                 acc[l] = chunk_dot_bf16<FMT>(cw[s][l], sc[s][l], xh, acc[l]);
@@ -804,7 +885,7 @@ __device__ __forceinline__ void gw2_unit(const GW2Args &a, int gs, int tile, flo
 }
 
 template <int FMT, int L, bool SB>
-__global__ __launch_bounds__(256, L <= 16 ? (SB ? 2 : W4_GW_MINBLK) : 1) void k_moe_gw2(GW2Args a) {
+__global__ __launch_bounds__(256, L <= 16 && FMT != FMT_INT4 ? (SB ? 2 : W4_GW_MINBLK) : 1) void k_moe_gw2(GW2Args a) {
     __shared__ float red[4][4][8][64];  // MFMA partials: [wave][row tile][column tile x 4 + j][lane]
     const int nu = unit_count(a.grp, a.s_codes != nullptr, a.tiles);
     for (int u = blockIdx.x; u < nu; u += gridDim.x) {
@@ -1788,6 +1869,7 @@ void launch_gw13(GW13Args &a, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
         else with_fmt(F, std::false_type());
     };
     if (a.fmt == FMT_NVFP4) with_sb(std::integral_constant<int, FMT_NVFP4>());
+    else if (a.fmt == FMT_INT4) with_sb(std::integral_constant<int, FMT_INT4>());
     else with_sb(std::integral_constant<int, FMT_E2M1>());
 }
 
@@ -1812,6 +1894,7 @@ void launch_gw2(GW2Args &a, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
         else with_fmt(F, std::false_type());
     };
     if (a.fmt == FMT_NVFP4) with_sb(std::integral_constant<int, FMT_NVFP4>());
+    else if (a.fmt == FMT_INT4) with_sb(std::integral_constant<int, FMT_INT4>());
     else with_sb(std::integral_constant<int, FMT_E2M1>());
 }
 

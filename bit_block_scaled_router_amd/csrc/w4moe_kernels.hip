@@ -814,13 +814,16 @@ int check_layer(const moe_w4a16_layer *Lr, int64_t T, MoEPlan &p) {
     p.hstride = ks2 * 32 * p.L2;
     p.lstride = (int)align_up((size_t)E + 1, 64);
     // batches: group the (token, slot) pairs by expert (E2M1 or NVFP4 weights,
-    // 128-wide K chunks for the MFMA tiles; the shared expert 4-bit or bf16)
+    // and int4 up to MAX_ONE_BLOCK_PAIRS pairs; 128-wide K chunks for the MFMA
+    // tiles; the shared expert 4-bit or bf16)
     p.P = (int)(T * K);
     p.Gmax = (int)(E < p.P ? E : p.P);
     // (the VALU small-group path keeps at most 2 k-steps of 32 x 64 elements)
     p.mx = fmt == W4_FMT_MXFP4_E8M0S32;
     p.grouped = T >= W4_GROUPED_MIN_T && H % 128 == 0 && I % 128 == 0 && H <= 4096 && I <= 4096 &&
-                (fmt == W4_FMT_E2M1_F16S16 || fmt == W4_FMT_NVFP4_E4M3S16) && p.P <= MAX_GROUPED_PAIRS;
+                ((fmt == W4_FMT_E2M1_F16S16 || fmt == W4_FMT_NVFP4_E4M3S16) ? p.P <= MAX_GROUPED_PAIRS
+                                                                          : fmt == W4_FMT_INT4_F16S128 &&
+                                                                                p.P <= MAX_ONE_BLOCK_PAIRS);
     if (p.mx) {  // batches run grouped on the scaled FP4 MFMA; single tokens on the VALU kernels
         if (H % 128 || I % 128)
             return fail(W4_ERR_UNSUPPORTED, "MXFP4 layers need hidden and inter multiples of 128");
@@ -1163,7 +1166,9 @@ int run_grouped(const moe_w4a16_layer *Lr, const MoEPlan &p, const uint16_t *x, 
     a.s_scales = Lr->has_shared ? (const uint16_t *)Lr->shared_w13.scales : nullptr;
     a.x = x, a.grp = grp, a.pairs = pairs, a.h_hi = h_hi, a.h_lo = h_lo;
     a.H = p.H, a.I = p.I, a.K = p.K, a.T = p.T, a.P = p.P, a.Gmax = p.Gmax, a.mfma_min = W4_MFMA_MIN;
-    a.fmt = Lr->w13.format == W4_FMT_NVFP4_E4M3S16 ? FMT_NVFP4 : FMT_E2M1;
+    a.fmt = Lr->w13.format == W4_FMT_NVFP4_E4M3S16 ? FMT_NVFP4
+            : Lr->w13.format == W4_FMT_INT4_F16S128 ? FMT_INT4
+                                                    : FMT_E2M1;
     a.gs = Lr->w13.global_scales, a.s_gs = Lr->has_shared ? Lr->shared_w13.global_scales : nullptr;
     a.s_bf16 = Lr->has_shared && Lr->shared_w13.format == W4_FMT_BF16;
     int32_t *ctg = p.multi ? (int32_t *)(wsb + p.off_route) + p.P + p.E + (size_t)p.nblk * p.E : nullptr;

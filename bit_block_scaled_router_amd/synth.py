@@ -90,6 +90,7 @@ QWEN_MOE_T32_NVFP4 = MoEShape("qwen3.6-35b-a3b-moe-batch32-zipf1.1-nvfp4", 2048,
 QWEN_MOE_T1_BF16SH = MoEShape("qwen3.6-35b-a3b-moe-decode-t1-bf16shared", 2048, 512, 256, 8, 512, 1, 0.0, 0, "e2m1",
                               "bf16")
 TINY_MOE_BF16SH = MoEShape("tiny-moe-h256-e8-k2-i128-bf16shared", 256, 128, 8, 2, 128, 1, 0.0, 0, "e2m1", "bf16")
+QWEN_MOE_T32_INT4 = MoEShape("qwen3.6-35b-a3b-moe-batch32-zipf1.1-int4", 2048, 512, 256, 8, 512, 32, 1.1, 0, "int4")
 QWEN_MOE_T32_BF16SH = MoEShape("qwen3.6-35b-a3b-moe-batch32-zipf1.1-bf16shared", 2048, 512, 256, 8, 512, 32, 1.1, 0,
                                "e2m1", "bf16")
 # MXFP4 experts with MXFP8 activations (the scaled FP4 MFMA path)

@@ -256,8 +256,9 @@ int moe_w4a16_forward_timed(const moe_w4a16_layer *L, const uint16_t *x, int64_t
  * combine).  The batched path serves E2M1 and NVFP4 layers with H and I
  * multiples of 128 and at most 4096, T >= 4 and T * top_k <= 65536 (NVFP4: one
  * exact bf16 MFMA term per weight instead of two, the global scales applied to
- * the sums; a bf16 shared expert: its rows are the MFMA operands); other
- * requests take the single-token path.  MXFP4 layers need H and I multiples of 128 and a shared
+ * the sums; a bf16 shared expert: its rows are the MFMA operands), and int4
+ * layers up to T * top_k = 4096 (the codes on the MFMA, each 128-wide chunk's
+ * sums times its scale); other requests take the single-token path.  MXFP4 layers need H and I multiples of 128 and a shared
  * expert in MXFP4 (W4_ERR_UNSUPPORTED otherwise); from T = 4 they run 6
  * kernels (router; x to MXFP8; top-k and grouping; W13 + SiLU with h quantised
  * to MXFP8; W2; ordered combine), below it the 3 single-token kernels, which

@@ -329,6 +329,45 @@ def test_moe_bf16_shared_expert_t32_zipf_sampled():
     print(assert_bf16_close(y[rows], ref, "bf16 shared T=32"), flush=True)
 
 
+# ---------------------------------------------------------------- int4 batches
+
+
+def test_moe_int4_batches_tiny():
+    """int4 experts (FP16 scale per 128) on the grouped path: tiny layer, groups
+    from 1 row (VALU) to ~75 rows (MFMA; the scale applied per 128-wide chunk),
+    caller routing with a repeated expert; past 4096 pairs the single-token path."""
+    shape = synth.MoEShape("tiny-int4", 256, 128, 8, 2, 128, 1, 0.0, 5, "int4")
+    dev_layer = wl.build_moe_layer(shape, device=DEV)
+    or_layer = oracle_layer(shape)
+    for T, stages in ((5, 5), (40, 5), (300, 5), (2049, 3)):
+        print(f"int4 tiny T={T}", flush=True)
+        assert w4.moe_w4a16_stage_count(dev_layer, T) == stages, T
+        _check_moe(shape, dev_layer, or_layer, tie_free_tokens(shape, or_layer, T, first=900), f"int4 T={T}")
+    xb = tie_free_tokens(shape, or_layer, 6, first=30)
+    ids = np.array([[1, 6], [6, 1], [3, 3], [0, 7], [2, 5], [4, 4]], dtype=np.int32)
+    w = np.array([[0.7, 0.3], [0.5, 0.5], [1.0, 0.25], [0.125, -0.5], [0.9, 0.1], [0.3, 0.3]], dtype=np.float32)
+    y = w4.moe_w4a16_experts(dev_layer, wl.bf16_tensor(xb), torch.from_numpy(ids).to(DEV), torch.from_numpy(w).to(DEV))
+    ref = ops.moe_experts(or_layer, xb, ids, w.astype(np.float64))
+    print(assert_bf16_close(wl.bf16_bits(y), ref, "int4 experts entry"), flush=True)
+
+
+def test_moe_int4_t32_zipf_sampled():
+    """35B-A3B shape with int4 experts at T = 32 with the Zipf bias: every
+    fourth token against the oracle."""
+    shape = synth.QWEN_MOE_T32_INT4
+    print(f"building {shape.name}", flush=True)
+    dev_layer = wl.build_moe_layer(shape, device=DEV)
+    or_layer = oracle_layer(shape)
+    xb = tie_free_tokens(shape, or_layer, shape.tokens, first=80)
+    assert w4.moe_w4a16_stage_count(dev_layer, shape.tokens) == 5
+    ids = torch.full((shape.tokens, shape.top_k), -7, dtype=torch.int32, device=DEV)
+    y = wl.bf16_bits(w4.moe_w4a16_forward(dev_layer, wl.bf16_tensor(xb), topk_ids=ids))
+    rows = list(range(0, shape.tokens, 4))
+    ref, rids, _ = ops.moe_forward(or_layer, xb[rows])
+    assert np.array_equal(ids.cpu().numpy()[rows], rids)
+    print(assert_bf16_close(y[rows], ref, "int4 T=32"), flush=True)
+
+
 def test_moe_nvfp4_with_bf16_shared_expert():
     shape = synth.MoEShape("tiny-nvfp4-bf16shared", 256, 128, 8, 2, 128, 1, 0.0, 0, "nvfp4", "bf16")
     dev_layer = wl.build_moe_layer(shape, device=DEV)

@@ -229,6 +229,15 @@ def test_bf16_shared_expert_plan():
         assert got == [3, 3, 5, 5, 7, 7], (fmt, got)
 
 
+def test_int4_layer_plan():
+    """int4 experts take the grouped path from T = 4 up to 4096 (token, slot)
+    pairs, the single-token path beyond."""
+    i4 = w4.W4_FMT_INT4_F16S128
+    L = _layer(w13=_mat(fmt=i4, groups=8, n=256, k=256), w2=_mat(fmt=i4, groups=8, n=256, k=128),
+               shared_w13=_mat(fmt=i4, groups=1, n=256, k=256), shared_w2=_mat(fmt=i4, groups=1, n=256, k=128))
+    assert [w4.lib().moe_w4a16_stage_count(C.byref(L), T) for T in (1, 3, 4, 2048, 2049)] == [3, 3, 5, 5, 3]
+
+
 def test_bf16_format_quantiser_sizes_and_rules():
     rng = np.random.default_rng(23)
     w = (rng.standard_normal((5, 64)) * 0.02).astype(np.float32)
