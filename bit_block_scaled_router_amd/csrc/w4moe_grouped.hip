@@ -581,6 +581,17 @@ __device__ __forceinline__ void gw13_unit(const GW13Args &a, int gs, int tile, f
             su[s][l] = ld_scales<FMT>(sb, v ? scale_off<FMT>(ru * spr, k0) : OOB);
         }
     for (int idx = 0; idx < gv.m; ++idx) {
+        if constexpr (FMT == FMT_INT4) {
+            // keep the int4 decode inside the token loop: hoisted, every row's
+            // decoded pairs stay live (about 300 registers, one block per CU)
+#pragma unroll
+            for (int s = 0; s < KS_VALU; ++s)
+#pragma unroll
+                for (int l = 0; l < NLG; ++l) {
+                    asm volatile("" : "+v"(cg[s][l].x), "+v"(cg[s][l].y), "+v"(cg[s][l].z), "+v"(cg[s][l].w));
+                    asm volatile("" : "+v"(cu[s][l].x), "+v"(cu[s][l].y), "+v"(cu[s][l].z), "+v"(cu[s][l].w));
+                }
+        }
         const int p = ld_uniform(plist, idx);
         const int t = token_of(p, a.P, a.K);
         const Buf xb = make_buf(a.x + (size_t)t * H, (uint32_t)H * 2u);
@@ -855,6 +866,13 @@ __device__ __forceinline__ void gw2_unit(const GW2Args &a, int gs, int tile, flo
             sc[s][l] = ld_scales<FMT>(sb, v ? scale_off<FMT>((uint32_t)rr * spr, k0) : OOB);
         }
     for (int idx = 0; idx < gv.m; ++idx) {
+        if constexpr (FMT == FMT_INT4) {  // as in gw13_unit: the decode stays in the token loop
+#pragma unroll
+            for (int s = 0; s < KS_VALU; ++s)
+#pragma unroll
+                for (int l = 0; l < NLG; ++l)
+                    asm volatile("" : "+v"(cw[s][l].x), "+v"(cw[s][l].y), "+v"(cw[s][l].z), "+v"(cw[s][l].w));
+        }
         const int p = ld_uniform(plist, idx);
         float acc[NLG];
 #pragma unroll
