@@ -947,10 +947,12 @@ __device__ __forceinline__ void pf_store(uint16_t *row, int c, int lq, const uin
 
 // Work units of the large-batch kernels: (column tile, row tile).  Unit u runs on
 // XCD u % 8 (blocks are dealt to the XCDs round-robin and the grid is a multiple
-// of 8), so the column tiles are dealt to the XCDs in turn and each XCD walks
-// all row tiles of its column tiles: a tile's activations are fetched into one
-// L2 and reused there.  The shared expert's ceil(T/64) tiles follow the routed
-// groups' (group table entry 1 + 3 Gmax and the column-tile map).
+// of 8).  XCD x takes the contiguous column tiles [x nct / 8, (x + 1) nct / 8)
+// and walks all row tiles of each: a tile's activations are fetched into one L2
+// and reused there, and since a group's tiles are consecutive, the tiles of one
+// expert (which read the same weight rows) mostly share an L2 as well.  The
+// shared expert's ceil(T/64) tiles follow the routed groups' (group table entry
+// 1 + 3 Gmax and the column-tile map).
 __device__ __forceinline__ int pf_tile_count(const int32_t *grp, int Gmax, bool shared, int T) {
     return ld_uniform(grp, 1 + 3 * Gmax) + (shared ? (T + PF_COLS - 1) / PF_COLS : 0);
 }
@@ -959,9 +961,9 @@ __device__ __forceinline__ int pf_unit_count(int nct, int tiles) { return (nct +
 __device__ __forceinline__ bool pf_unit(const int32_t *grp, const int32_t *ctg, int Gmax, bool shared, int nct, int u,
                                         int tiles, int &gs, int &rt, int &n0) {
     const int x = u & 7, j = u >> 3;
-    const int ct = 8 * (j / tiles) + x;
+    const int ct = ((x * nct) >> 3) + j / tiles;
     rt = j - (j / tiles) * tiles;
-    if (ct >= nct) return false;
+    if (ct >= (((x + 1) * nct) >> 3)) return false;
     const int nrc = ld_uniform(grp, 1 + 3 * Gmax);
     if (ct < nrc) {
         gs = ld_uniform(ctg, 2 * ct) + (shared ? 1 : 0);
