@@ -1,7 +1,8 @@
 """Host-side checks of bench.py's bookkeeping (no GPU): for every MoE workload
 the stage names match the library's stage count and every named kernel has an
 algorithmic byte count; the flop counts cover the projections; a multi-GPU
-request exits with a message."""
+request exits with a message; the HBM traffic bookkeeping scales counters by
+the copy calibration and goes stale with the kernel sources."""
 
 import subprocess
 import sys
@@ -54,3 +55,35 @@ def test_multi_gpu_request_exits_with_message():
     r = subprocess.run([sys.executable, "bench.py", "--gpus", "2"], cwd=ROOT, capture_output=True, text=True,
                        timeout=120)
     assert r.returncode == 2 and "one GPU" in r.stderr
+
+
+def test_traffic_ingest_scaling_and_invalidation(tmp_path, monkeypatch, capsys):
+    """ingest_counters scales each counter by what it reads for the 256 MiB copy
+    (mean of the first three copy dispatches), stores HBM bytes per dispatch with
+    the kernel source digest, and load_traffic drops the record once a kernel
+    source changes."""
+    csrc = tmp_path / "bit_block_scaled_router_amd" / "csrc"
+    csrc.mkdir(parents=True)
+    (csrc / "k.hip").write_text("// v1\n")
+    (tmp_path / "profiles").mkdir()
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+
+    def csv(path, counter, copy_kib, kern_vals):
+        rows = ["Kernel_Name,Counter_Name,Counter_Value"]
+        rows += [f"__amd_rocclr_copyBuffer,{counter},{v}" for v in copy_kib]
+        rows += [f"void w4k::k_moe_w13<1>(w4k::Args),{counter},{v}" for v in kern_vals]
+        path.write_text("\n".join(rows) + "\n")
+        return str(path)
+
+    # FETCH_SIZE reads half the copied bytes (factor 2), WRITE_SIZE all of them;
+    # a fourth copy dispatch is ignored
+    f = csv(tmp_path / "f.csv", "FETCH_SIZE", [131072, 131072, 131072, 1], [100.0, 300.0])
+    w = csv(tmp_path / "w.csv", "WRITE_SIZE", [262144, 262144, 262144], [10.0, 30.0])
+    bench.ingest_counters([f, w], "wl")
+    capsys.readouterr()
+    want = (200.0 * 2 + 20.0 * 1) * 1024
+    assert bench.load_traffic("k_moe_w13", "wl") == round(want)
+    assert bench.load_traffic("k_moe_w13", "other") is None
+    assert bench.load_traffic("k_moe_w2", "wl") is None
+    (csrc / "k.hip").write_text("// v2\n")
+    assert bench.load_traffic("k_moe_w13", "wl") is None
