@@ -36,6 +36,16 @@ def test_library_exports_every_declared_function():
         assert hasattr(L, n), n
 
 
+def test_missing_library_fails_loudly(tmp_path, monkeypatch):
+    """Without the built library the binding raises instead of falling back to
+    anything else (there is no CPU path in the package)."""
+    from bit_block_scaled_router_amd import _lib
+    monkeypatch.setattr(_lib, "_lib", None)
+    monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "libw4moe.so"))
+    with pytest.raises(ImportError, match="is missing"):
+        _lib.lib()
+
+
 def test_status_strings_and_version():
     assert w4.w4_status_string(0) == "W4_OK"
     assert w4.w4_status_string(w4.W4_ERR_LAYOUT) == "W4_ERR_LAYOUT"
