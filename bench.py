@@ -7,18 +7,28 @@ synthetic input: for the default workload, one token through the whole MoE layer
 of the Qwen 3.6 35B-A3B shape (router GEMV, softmax/top-8/renormalise, grouped
 W13 + SiLU over 8 routed + 1 shared expert, down projection + weighted combine).
 Inputs are resident in HBM before the timed region.  To keep the 256 MB
-Infinity Cache from serving the weights, steps rotate over layer replicas and a
-pool of tokens (distinct expert sets), so a step streams cold weights as a real
-40-layer decode would.
+Infinity Cache from serving weights, steps rotate over 4 replicas of the routed
+experts (4 x 483 MiB), over enough copies of the routing-independent tensors
+(router, shared-gate weight, shared expert: at least 288 MB of copies) and over a
+pool of tokens (distinct expert sets), so each step streams cold weights as a
+real 40-layer decode would.
 
 The K timed steps are captured once in a HIP graph (removing host launch cost)
-and replayed; W eager warm-up steps and one untimed replay precede the timed
-replay.  The library's measurement entry point records HIP events between its
-launches on the stream they run on, giving each kernel's average duration over
-the timed region; the dominant one is reported in `roofline`.
+and replayed after W eager warm-up steps and one untimed replay.  Each kernel's
+duration is measured the way a kernel trace sees it, in isolation: the captured
+graph's kernel nodes of one stage (the same K launches, same arguments, same
+order) are copied into a graph of their own, which is replayed and timed; the
+per-launch average is `stage_us`, and the stage with the largest one is the
+dominant kernel of `roofline`.  Every step has its own workspace slot (one per
+token of the pool), so a stage replayed alone reads the intermediates its own
+step wrote.
 
-`cpu_baseline` times the CPU oracle on a bounded sample of the same workload
-(a few tokens, weights pre-quantised untimed, dequantisation on the fly).
+`ceiling` times the library's streaming-read probe on a buffer the size of the
+dominant kernel's algorithmic bytes (rotated over >= 1.3 GB) and on 4 GiB: the
+box's practical read rate, a second denominator beside the 8 TB/s peak.
+`cpu_baseline` times the CPU oracle on a bounded sample of the same workload;
+`variants` holds it single-threaded and on all cores, with dequantisation on the
+fly and cached.
 """
 
 import argparse
@@ -44,8 +54,17 @@ METRIC = "MoE-layer µs/token and achieved HBM GB/s (% of peak), W4A16 decode"
 # ----------------------------------------------------------------------------- HIP events
 
 
-class HipEvents:
-    """Raw hipEvent_t handles from the HIP runtime torch has loaded."""
+class Dim3(C.Structure):
+    _fields_ = [("x", C.c_uint32), ("y", C.c_uint32), ("z", C.c_uint32)]
+
+
+class KernelNodeParams(C.Structure):  # hipKernelNodeParams
+    _fields_ = [("blockDim", Dim3), ("extra", C.c_void_p), ("func", C.c_void_p), ("gridDim", Dim3),
+                ("kernelParams", C.c_void_p), ("sharedMemBytes", C.c_uint)]
+
+
+class HipRuntime:
+    """The HIP runtime torch has loaded: raw events, graph surgery and versions."""
 
     def __init__(self):
         path = None
@@ -53,29 +72,171 @@ class HipEvents:
             if "libamdhip64" in ln:
                 path = ln.split()[-1]
                 break
-        self.hip = C.CDLL(path or "libamdhip64.so")
-        self.hip.hipEventCreate.argtypes = [C.POINTER(C.c_void_p)]
-        self.hip.hipEventElapsedTime.argtypes = [C.POINTER(C.c_float), C.c_void_p, C.c_void_p]
-        self.hip.hipEventDestroy.argtypes = [C.c_void_p]
+        self.hip = h = C.CDLL(path or "libamdhip64.so")
+        P, SZ = C.c_void_p, C.c_size_t
+        h.hipEventCreate.argtypes = [C.POINTER(P)]
+        h.hipEventElapsedTime.argtypes = [C.POINTER(C.c_float), P, P]
+        h.hipEventDestroy.argtypes = [P]
+        h.hipEventRecord.argtypes = [P, P]
+        h.hipEventSynchronize.argtypes = [P]
+        h.hipGraphGetRootNodes.argtypes = [P, C.POINTER(P), C.POINTER(SZ)]
+        h.hipGraphNodeGetDependentNodes.argtypes = [P, C.POINTER(P), C.POINTER(SZ)]
+        h.hipGraphNodeGetType.argtypes = [P, C.POINTER(C.c_int)]
+        h.hipGraphKernelNodeGetParams.argtypes = [P, C.POINTER(KernelNodeParams)]
+        h.hipGraphCreate.argtypes = [C.POINTER(P), C.c_uint]
+        h.hipGraphAddKernelNode.argtypes = [C.POINTER(P), P, C.POINTER(P), SZ, C.POINTER(KernelNodeParams)]
+        h.hipGraphInstantiate.argtypes = [C.POINTER(P), P, P, C.c_char_p, SZ]
+        h.hipGraphLaunch.argtypes = [P, P]
+        h.hipGraphExecDestroy.argtypes = [P]
+        h.hipGraphDestroy.argtypes = [P]
+        h.hipStreamSynchronize.argtypes = [P]
+        h.hipRuntimeGetVersion.argtypes = [C.POINTER(C.c_int)]
+        h.hipDriverGetVersion.argtypes = [C.POINTER(C.c_int)]
+
+    def _ok(self, st, what):
+        if st != 0:
+            raise RuntimeError(f"{what} failed ({st})")
 
     def create(self, n):
         out = []
         for _ in range(n):
             e = C.c_void_p()
-            if self.hip.hipEventCreate(C.byref(e)) != 0:
-                raise RuntimeError("hipEventCreate failed")
+            self._ok(self.hip.hipEventCreate(C.byref(e)), "hipEventCreate")
             out.append(e.value)
         return out
 
     def elapsed_ms(self, a, b):
         ms = C.c_float()
-        if self.hip.hipEventElapsedTime(C.byref(ms), a, b) != 0:
-            raise RuntimeError("hipEventElapsedTime failed")
+        self._ok(self.hip.hipEventElapsedTime(C.byref(ms), a, b), "hipEventElapsedTime")
         return ms.value
 
     def destroy(self, evs):
         for e in evs:
             self.hip.hipEventDestroy(e)
+
+    def versions(self):
+        rt, dr = C.c_int(0), C.c_int(0)
+        self.hip.hipRuntimeGetVersion(C.byref(rt))
+        self.hip.hipDriverGetVersion(C.byref(dr))
+        return {"hip_runtime": rt.value, "hip_driver": dr.value, "library": self.hip._name}
+
+    def kernel_chain(self, graph):
+        """Kernel nodes of a captured single-stream graph in launch order."""
+        h = self.hip
+        n = C.c_size_t(0)
+        self._ok(h.hipGraphGetRootNodes(graph, None, C.byref(n)), "hipGraphGetRootNodes")
+        if n.value != 1:
+            raise RuntimeError(f"expected one root node, got {n.value}")
+        roots = (C.c_void_p * 1)()
+        self._ok(h.hipGraphGetRootNodes(graph, roots, C.byref(n)), "hipGraphGetRootNodes")
+        chain, node = [], roots[0]
+        while node:
+            t = C.c_int(-1)
+            self._ok(h.hipGraphNodeGetType(node, C.byref(t)), "hipGraphNodeGetType")
+            if t.value == 0:  # hipGraphNodeTypeKernel
+                chain.append(node)
+            m = C.c_size_t(0)
+            self._ok(h.hipGraphNodeGetDependentNodes(node, None, C.byref(m)), "hipGraphNodeGetDependentNodes")
+            if m.value > 1:
+                raise RuntimeError("the captured graph is not a single chain")
+            if m.value == 0:
+                break
+            nxt = (C.c_void_p * 1)()
+            self._ok(h.hipGraphNodeGetDependentNodes(node, nxt, C.byref(m)), "hipGraphNodeGetDependentNodes")
+            node = nxt[0]
+        return chain
+
+    def replay_nodes_us(self, nodes, stream, reps=2, spin=None):
+        """Copy the kernel nodes (in order, one chain) into a graph of their own,
+        replay it and return the average microseconds per launch (best of reps)."""
+        h = self.hip
+        g = C.c_void_p()
+        self._ok(h.hipGraphCreate(C.byref(g), 0), "hipGraphCreate")
+        prev = None
+        for node in nodes:
+            p = KernelNodeParams()
+            self._ok(h.hipGraphKernelNodeGetParams(node, C.byref(p)), "hipGraphKernelNodeGetParams")
+            new = C.c_void_p()
+            deps = (C.c_void_p * 1)(prev) if prev is not None else None
+            self._ok(h.hipGraphAddKernelNode(C.byref(new), g, deps, 1 if prev is not None else 0, C.byref(p)),
+                     "hipGraphAddKernelNode")
+            prev = new.value
+        ex = C.c_void_p()
+        self._ok(h.hipGraphInstantiate(C.byref(ex), g, None, None, 0), "hipGraphInstantiate")
+        e0, e1 = self.create(2)
+        try:
+            self._ok(h.hipGraphLaunch(ex, stream), "hipGraphLaunch")  # warm
+            self._ok(h.hipStreamSynchronize(stream), "hipStreamSynchronize")
+            best = None
+            for _ in range(reps):
+                if spin is not None:  # keep the GPU busy while the host submits the graph
+                    spin()
+                self._ok(h.hipEventRecord(e0, stream), "hipEventRecord")
+                self._ok(h.hipGraphLaunch(ex, stream), "hipGraphLaunch")
+                self._ok(h.hipEventRecord(e1, stream), "hipEventRecord")
+                self._ok(h.hipEventSynchronize(e1), "hipEventSynchronize")
+                us = self.elapsed_ms(e0, e1) * 1e3 / len(nodes)
+                best = us if best is None else min(best, us)
+        finally:
+            self.destroy([e0, e1])
+            h.hipGraphExecDestroy(ex)
+            h.hipGraphDestroy(g)
+        return best
+
+
+def machine_info(hip):
+    """Device, ROCm/HIP versions and clocks (rocm-smi, when it answers)."""
+    import subprocess
+    import torch
+
+    props = torch.cuda.get_device_properties(0)
+    info = {"device": torch.cuda.get_device_name(0), "arch": getattr(props, "gcnArchName", None),
+            "compute_units": props.multi_processor_count, "torch": torch.__version__, "torch_hip": torch.version.hip}
+    info.update(hip.versions())
+    try:
+        with open("/opt/rocm/.info/version") as f:
+            info["rocm"] = f.read().strip()
+    except OSError:
+        info["rocm"] = None
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True, timeout=30)
+        clk = json.loads(r.stdout) if r.returncode == 0 else None
+        if isinstance(clk, dict) and clk:
+            card = clk[sorted(clk)[0]]
+            info["clocks"] = {k: v for k, v in card.items() if "clock" in k.lower() or k.lower().startswith(("sclk", "mclk", "fclk", "socclk"))}
+            info["clocks_note"] = "rocm-smi's current levels when sampled after the run (idle), not the clock under load"
+        else:
+            info["clocks"] = None
+    except Exception as e:  # rocm-smi missing or refused: say so
+        info["clocks"] = f"unavailable: {type(e).__name__}"
+    return info
+
+
+def stream_ceiling(torch, w4, nbytes, min_total=1300 << 20, steps=200):
+    """GB/s of the streaming-read probe on buffers of nbytes (rotated over enough
+    copies to exceed min_total), as graph replay."""
+    nbytes = max(16, nbytes // 16 * 16)
+    copies = max(1, -(-min_total // nbytes)) if nbytes < min_total else 1
+    bufs = [torch.ones(nbytes, dtype=torch.uint8, device="cuda") for _ in range(copies)]
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    n = max(steps, copies) if nbytes < min_total else 5
+    for b in bufs[:4]:
+        w4.w4_bench_stream_read(b, sink)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            for i in range(n):
+                w4.w4_bench_stream_read(bufs[i % copies], sink)
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    us = timed_replay_ms(torch, g) * 1e3 / n
+    del g, bufs
+    torch.cuda.empty_cache()
+    return {"bytes": nbytes, "us_per_launch": us, "gbps": nbytes / (us * 1e-6) / 1e9, "copies": copies}
 
 
 # ----------------------------------------------------------------------------- helpers
@@ -154,20 +315,41 @@ def ingest_counters(paths, workload):
             f.write("\n")
 
 
-def clone_layer(w4, layer):
-    """A deep copy of a device MoE layer (new addresses, same contents)."""
-    def cq(q):
-        g = q.global_scales.clone() if q.global_scales is not None else None
-        sc = q.scales.clone() if q.scales is not None else None
-        return w4.QMatrix(q.fmt, q.groups, q.n, q.k, q.codes.clone(), sc, g)
+def _clone_q(w4, q):
+    g = q.global_scales.clone() if q.global_scales is not None else None
+    sc = q.scales.clone() if q.scales is not None else None
+    return w4.QMatrix(q.fmt, q.groups, q.n, q.k, q.codes.clone(), sc, g)
 
-    kw = {}
+
+def make_layers(w4, base, routed_replicas, copies):
+    """`copies` layer descriptors over the same weights' values at distinct
+    addresses: layer i takes the routed experts of replica i % routed_replicas
+    and its own copy of the router, router bias, shared-gate weight and shared
+    expert (layer 0 is `base` itself)."""
+    routed = [(base.w13, base.w2)] + [(_clone_q(w4, base.w13), _clone_q(w4, base.w2))
+                                      for _ in range(routed_replicas - 1)]
+    layers = [base]
+    for i in range(1, copies):
+        kw = {}
+        if base.has_shared:
+            kw = dict(shared_w13=_clone_q(w4, base.shared_w13), shared_w2=_clone_q(w4, base.shared_w2),
+                      shared_gate_w=base.shared_gate_w.clone())
+        rb = base.router_bias.clone() if base.router_bias is not None else None
+        w13, w2 = routed[i % routed_replicas]
+        layers.append(w4.MoELayer(base.hidden, base.inter, base.num_experts, base.top_k, base.router_w.clone(),
+                                  w13, w2, router_bias=rb, **kw))
+    return layers
+
+
+def shared_copy_bytes(layer):
+    """Bytes of one copy of the routing-independent tensors of a device layer."""
+    def qb(q):
+        return q.codes.numel() * q.codes.element_size() + (
+            q.scales.numel() * q.scales.element_size() if q.scales is not None else 0)
+    b = layer.router_w.numel() * 2
     if layer.has_shared:
-        kw = dict(shared_w13=cq(layer.shared_w13), shared_w2=cq(layer.shared_w2),
-                  shared_gate_w=layer.shared_gate_w.clone())
-    rb = layer.router_bias.clone() if layer.router_bias is not None else None
-    return w4.MoELayer(layer.hidden, layer.inter, layer.num_experts, layer.top_k, layer.router_w.clone(),
-                       cq(layer.w13), cq(layer.w2), router_bias=rb, **kw)
+        b += qb(layer.shared_w13) + qb(layer.shared_w2) + layer.shared_gate_w.numel() * 2
+    return b
 
 
 def weight_bytes(fmt, n, k):
@@ -295,17 +477,50 @@ def stage_flops(shape):
 # ----------------------------------------------------------------------------- CPU baseline
 
 
+def _blas_info():
+    try:
+        from threadpoolctl import threadpool_info
+        info = threadpool_info()
+        return ([f"{p.get('internal_api')} {p.get('version')} ({p.get('threading_layer', '')})" for p in info
+                 if p.get("user_api") == "blas"], max([p.get("num_threads", 1) for p in info] or [1]))
+    except Exception:  # pragma: no cover - optional
+        return [], 1
+
+
+def _timed(fn, reps):
+    fn()  # warm-up (first touch, BLAS thread start)
+    times = []
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        fn()
+        times.append(time.perf_counter() - t0)
+    return float(np.median(times))
+
+
+def _thread_settings():
+    """(label, thread count) pairs: one thread and every core the process may use."""
+    n = len(os.sched_getaffinity(0))
+    return [("1 thread", 1), (f"{n} threads", n)]
+
+
+def _limits(n):
+    try:
+        from threadpoolctl import threadpool_limits
+        return threadpool_limits(limits=n)
+    except Exception:  # pragma: no cover - optional
+        import contextlib
+        return contextlib.nullcontext()
+
+
 def cpu_baseline_moe(shape, tokens, reps):
-    """Oracle forward per token (float64, dequantisation on the fly), bounded sample."""
+    """Oracle forward per token (float64), bounded sample: single-threaded and on
+    all cores, with dequantisation on the fly (a fresh layer per run) and cached
+    (the layer's dequantised experts kept across runs)."""
     import oracle
     from oracle import ops
     from bit_block_scaled_router_amd import synth
 
-    try:
-        from threadpoolctl import threadpool_info
-        blas_threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover - optional
-        blas_threads = 1
+    blas, _ = _blas_info()
     rw = synth.router_weight(shape)
     xs = np.stack([synth.x_row(shape.seed, shape.hidden, t) for t in range(tokens)])
     bias = synth.router_bias(shape)
@@ -324,46 +539,66 @@ def cpu_baseline_moe(shape, tokens, reps):
         kw = dict(shared_w13=oracle.quantize(sfmt, synth.shared_w13(shape)),
                   shared_w2=oracle.quantize(sfmt, synth.shared_w2(shape)),
                   shared_gate_w=synth.shared_gate_weight(shape), shared_fmt=sfmt)
-    times = []
-    for _ in range(reps):
-        layer = ops.MoELayer(fmt, shape.hidden, shape.inter, shape.num_experts, shape.top_k, rw,
-                             lambda e: q13[e], lambda e: q2[e], router_bias=bias, **kw)
-        t0 = time.perf_counter()
-        ops.moe_forward(layer, xs)
-        times.append(time.perf_counter() - t0)
-    per_token_us = float(np.median(times)) / tokens * 1e6
+
+    def new_layer():
+        return ops.MoELayer(fmt, shape.hidden, shape.inter, shape.num_experts, shape.top_k, rw,
+                            lambda e: q13[e], lambda e: q2[e], router_bias=bias, **kw)
+
+    variants = []
+    for label, n in _thread_settings():
+        with _limits(n):
+            fly = _timed(lambda: ops.moe_forward(new_layer(), xs), reps)
+            cached_layer = new_layer()
+            cached = _timed(lambda: ops.moe_forward(cached_layer, xs), reps)
+        for kind, t in (("dequantisation on the fly", fly), ("dequantised experts cached", cached)):
+            variants.append({"threads": n, "dequant": kind, "us_per_layer_token": t / tokens * 1e6,
+                             "algorithmic_gbps": moe_bytes(shape, len(need)) / shape.tokens * tokens / t / 1e9})
+    head = [v for v in variants if v["threads"] == _thread_settings()[-1][1] and "fly" in v["dequant"]][0]
     return {
-        "value": per_token_us,
+        "value": head["us_per_layer_token"],
         "unit": "us/layer-token",
-        "cores": int(blas_threads),
+        "cores": head["threads"],
         "kind": "oracle",
         "sample": f"{tokens} token(s) of the same layer shape, float64 oracle forward with on-the-fly "
-                  f"dequantisation, weights pre-quantised untimed; median of {reps} runs",
+                  f"dequantisation, weights pre-quantised untimed; median of {reps} runs after one warm-up "
+                  f"(value: all cores; `variants`: 1 thread and all cores, dequantisation on the fly and cached)",
         "host_cores_available": len(os.sched_getaffinity(0)),
+        "blas": blas,
+        "variants": variants,
     }
 
 
 def cpu_baseline_gemv(shape, reps, max_rows=8192):
     """Oracle GEMV on the workload, or on its first `max_rows` rows scaled to the
-    full row count (the oracle is a row-by-row definition, so time is linear in rows)."""
+    full row count (the oracle is a row-by-row definition, so time is linear in
+    rows): single-threaded and on all cores, dequantising on the fly and with the
+    dequantised matrix cached."""
     import oracle
+    from oracle import ops
     from bit_block_scaled_router_amd import synth
 
+    blas, _ = _blas_info()
     ofmt = {"e2m1": oracle.FMT_E2M1, "int4": oracle.FMT_INT4, "nvfp4": oracle.FMT_NVFP4}[shape.fmt]
     rows = min(shape.n, max_rows)
     w = synth.normal_f32((rows, shape.k), synth.SIGMA_W, shape.seed, 9) if rows < shape.n else synth.dense_weight(shape)
     q = oracle.quantize(ofmt, w)
     x = synth.dense_x(shape)
-    times = []
-    for _ in range(reps):
-        t0 = time.perf_counter()
-        oracle.gemv(ofmt, q[0], q[1], x, *q[2:])
-        times.append(time.perf_counter() - t0)
     scale = shape.n / rows
+    wdeq = oracle.dequant(ofmt, *q)
+    xv = oracle.bf16_bits_to_f64(x)
+    variants = []
+    for label, n in _thread_settings():
+        with _limits(n):
+            fly = _timed(lambda: oracle.gemv(ofmt, q[0], q[1], x, *q[2:]), reps)
+            cached = _timed(lambda: np.asarray(wdeq, dtype=np.float64) @ xv, reps)
+        for kind, t in (("dequantisation on the fly", fly), ("dequantised matrix cached", cached)):
+            variants.append({"threads": n, "dequant": kind, "us_per_call": t * 1e6 * scale})
+    head = [v for v in variants if v["threads"] == 1 and "fly" in v["dequant"]][0]
     sample = (f"the full {shape.n}x{shape.k} GEMV" if rows == shape.n else
-              f"the first {rows} of {shape.n} rows, time scaled by {scale:.2f}") + f", median of {reps} runs"
-    return {"value": float(np.median(times)) * 1e6 * scale, "unit": "us/call", "cores": 1, "kind": "oracle",
-            "sample": sample, "host_cores_available": len(os.sched_getaffinity(0))}
+              f"the first {rows} of {shape.n} rows, time scaled by {scale:.2f}") + \
+        f", median of {reps} runs after one warm-up (value: 1 thread, dequantisation on the fly)"
+    return {"value": head["us_per_call"], "unit": "us/call", "cores": 1, "kind": "oracle", "sample": sample,
+            "host_cores_available": len(os.sched_getaffinity(0)), "blas": blas, "variants": variants}
 
 
 # ----------------------------------------------------------------------------- GPU runs
@@ -386,75 +621,99 @@ WORKLOADS = ["qwen-t1", "qwen-t32", "tiny", "gemv-e2m1", "gemv-int4", "qwen-t1-n
              "qwen-t32-nvfp4", "qwen-t32-bf16shared", "qwen-t32-int4"]
 
 
-def run_moe(args, torch, w4, wl, synth):
+def run_moe(args, torch, w4, wl, synth, hip):
     shape = workload_shapes(synth)[args.workload]
     T = shape.tokens
-    print(f"[bench] building {shape.name} ({args.replicas} replicas)", file=sys.stderr, flush=True)
     base = wl.build_moe_layer(shape, device="cuda")
-    layers = [base] + [clone_layer(w4, base) for _ in range(args.replicas - 1)]
+    # copies of the routing-independent tensors: at least 288 MB of them, so that
+    # a copy comes back only after more than the Infinity Cache has streamed by
+    per_copy = shared_copy_bytes(base)
+    ncopies = max(args.replicas, min(128, -(-(288 << 20) // per_copy)))
+    print(f"[bench] {shape.name}: {args.replicas} routed replicas, {ncopies} copies of the router and shared "
+          f"expert ({ncopies * per_copy / 2**20:.0f} MiB)", file=sys.stderr, flush=True)
+    layers = make_layers(w4, base, args.replicas, ncopies)
     pool = np.stack([np.stack([synth.x_row(shape.seed, shape.hidden, p * T + t) for t in range(T)])
                      for p in range(args.pool)])
     xs = wl.bf16_tensor(pool, "cuda")  # [P][T][H]
     y = torch.empty((T, shape.hidden), dtype=torch.bfloat16, device="cuda")
     ids = torch.empty((T, shape.top_k), dtype=torch.int32, device="cuda")
-    ws = w4.alloc_workspace(base, T)
+    ws_bytes = w4.moe_w4a16_workspace_bytes(base, T)
+    wsz = (ws_bytes + 255) // 256 * 256
+    ws_all = torch.empty(wsz * args.pool, dtype=torch.uint8, device="cuda")
+    wss = [ws_all[p * wsz:p * wsz + ws_bytes] for p in range(args.pool)]  # one slot per pool token
     # distinct routed experts per step (for the algorithmic byte count)
     distinct = []
     for p in range(args.pool):
-        w4.moe_w4a16_forward(base, xs[p], y=y, topk_ids=ids, ws=ws)
+        w4.moe_w4a16_forward(base, xs[p], y=y, topk_ids=ids, ws=wss[p])
         distinct.append(len(set(ids.cpu().numpy().ravel().tolist())))
     torch.cuda.synchronize()
     n_steps = args.steps
-    R, P = len(layers), args.pool
+    NL, P = len(layers), args.pool
+
+    def step(i):
+        w4.moe_w4a16_forward(layers[i % NL], xs[i % P], y=y, ws=wss[i % P])
+
     for i in range(args.warmup):
-        w4.moe_w4a16_forward(layers[i % R], xs[i % P], y=y, ws=ws)
+        step(i)
     torch.cuda.synchronize()
 
-    g = torch.cuda.CUDAGraph()
+    g = torch.cuda.CUDAGraph(keep_graph=True)
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
         with torch.cuda.graph(g, stream=s):
             for i in range(n_steps):
-                w4.moe_w4a16_forward(layers[i % R], xs[i % P], y=y, ws=ws)
+                step(i)
+    g.instantiate()
     torch.cuda.synchronize()
     g.replay()  # untimed warm replay
     torch.cuda.synchronize()
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
     t_wall = time.perf_counter()
-    start.record()
-    g.replay()
-    end.record()
-    torch.cuda.synchronize()
+    ms_total = timed_replay_ms(torch, g)
     t_wall = time.perf_counter() - t_wall
-    ms_total = start.elapsed_time(end)
 
-    # per-kernel durations: the same K steps launched eagerly through the
-    # measurement entry point, whose kernels carry start/stop HIP events
+    # per-kernel durations: each stage's K launches replayed alone, in a graph of
+    # their own copied from the captured one (same kernels, arguments and order)
     n_stages = w4.moe_w4a16_stage_count(base, T)
     names = stage_names(n_stages, T, shape.top_k, shape.fmt == "mxfp4")
-    hip = HipEvents()
+    stage_us, timing_note = {}, ("avg launch duration: the stage's K launches copied out of the captured graph "
+                                 "and replayed alone (graph replay time / K), on the stream the kernels run on")
+    try:
+        chain = hip.kernel_chain(g.raw_cuda_graph())
+        if len(chain) != n_stages * n_steps:
+            raise RuntimeError(f"captured {len(chain)} kernels, expected {n_stages} x {n_steps}")
+        cur = torch.cuda.current_stream().cuda_stream
+        for si, k in enumerate(names):
+            stage_us[k] = hip.replay_nodes_us(chain[si::n_stages], cur, spin=lambda: torch.cuda._sleep(2_000_000))
+    except Exception as e:  # report, and fall back to the event timings below
+        print(f"[bench] isolated stage replay failed: {e}", file=sys.stderr, flush=True)
+        stage_us, timing_note = {}, f"isolated stage replay failed ({e}); medians of per-kernel start/stop events"
+    # the same launches with start/stop events around each kernel (eager; reported beside it)
     ne = 2 * n_stages
-    evs = hip.create(ne * n_steps)
-    for i in range(n_steps):
-        w4.moe_w4a16_forward_timed(layers[i % R], xs[i % P], y, ws, evs[ne * i:ne * i + ne])
+    n_ev = max(n_steps, 300)
+    evs = hip.create(ne * n_ev)
+    for i in range(n_ev):
+        w4.moe_w4a16_forward_timed(layers[i % NL], xs[i % P], y, wss[i % P], evs[ne * i:ne * i + ne])
     torch.cuda.synchronize()
-    stage = {k: [] for k in names}
-    for i in range(n_steps):
+    stage_ev = {k: [] for k in names}
+    for i in range(n_ev):
         e = evs[ne * i:ne * i + ne]
         for si, k in enumerate(names):
-            stage[k].append(hip.elapsed_ms(e[2 * si], e[2 * si + 1]))
+            stage_ev[k].append(hip.elapsed_ms(e[2 * si], e[2 * si + 1]))
     hip.destroy(evs)
-    stage_us = {k: float(np.mean(v)) * 1e3 for k, v in stage.items()}
+    stage_us_events = {k: float(np.median(v)) * 1e3 for k, v in stage_ev.items()}
+    if not stage_us:
+        stage_us = dict(stage_us_events)
 
     # eager (no graph) rate for context
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(min(n_steps, 200)):
-        w4.moe_w4a16_forward(layers[i % R], xs[i % P], y=y, ws=ws)
+        step(i)
     torch.cuda.synchronize()
     eager_ms = (time.perf_counter() - t0) / min(n_steps, 200) * 1e3
+    del g
+    torch.cuda.synchronize()
 
     d_mean = float(np.mean(distinct))
     ms_step = ms_total / n_steps
@@ -464,12 +723,14 @@ def run_moe(args, torch, w4, wl, synth):
     dom = max(stage_us, key=stage_us.get)
     achieved = sb[dom] / (stage_us[dom] * 1e-6) / 1e9
     traffic = load_traffic(dom, shape.name)
+    ceil_same = stream_ceiling(torch, w4, int(sb[dom]))
+    ceil_big = stream_ceiling(torch, w4, 4 << 30)
     # the dominant kernel's bound: HBM bytes or MFMA flops, whichever takes longer
     # at the published peaks
     fl = stage_flops(shape).get(dom)
     mfma_peak = MFMA_PEAK_TFLOPS["fp8" if shape.fmt == "mxfp4" else "bf16"]
     roof = {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": achieved / HBM_PEAK_GBS}
+            "frac": achieved / HBM_PEAK_GBS, "frac_of_same_size_read": achieved / ceil_same["gbps"]}
     if fl is not None:
         tflops = fl / (stage_us[dom] * 1e-6) / 1e12
         roof["mfma_tflops"] = tflops
@@ -501,27 +762,44 @@ def run_moe(args, torch, w4, wl, synth):
                         "mxfp4": "E2M1 codes + E8M0 scale per 32"}[shape.fmt]
                        + (", shared expert bf16" if shape.shared_fmt == "bf16" else ""),
             "activations": ("bf16; MXFP8 (E4M3 + E8M0 per 32) inside the experts" if shape.fmt == "mxfp4"
-                            else "bf16"), "accumulate": "fp32", "layer_replicas": R, "token_pool": P,
+                            else "bf16"), "accumulate": "fp32", "routed_expert_replicas": args.replicas,
+            "router_shared_copies": NL, "token_pool": P,
             "mean_distinct_experts": d_mean, "timing": "HIP graph replay of the K steps",
         },
         "hbm_gbps": step_bytes / (ms_step * 1e-3) / 1e9,
         "pct_hbm_peak": 100.0 * step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
         "algorithmic_bytes_per_step": step_bytes,
         "stage_us": stage_us,
+        "stage_us_events": stage_us_events,
         "eager_ms_per_step": eager_ms,
         "wall_s_timed": t_wall,
+        "ceiling": {"same_size_read": ceil_same, "read_4gib": ceil_big,
+                    "step_frac_of_4gib_read": step_bytes / (ms_step * 1e-3) / 1e9 / ceil_big["gbps"]},
         "roofline": {
             **roof,
             "traffic": traffic,
             "algorithmic_bytes_per_launch": sb[dom], "avg_launch_us": stage_us[dom],
-            "note": "avg launch duration from start/stop HIP events the runtime records around each "
-                    "kernel (hipExtLaunchKernel) over K eager steps of the same workload",
+            "note": timing_note,
         },
     }
     return res, shape
 
 
-def run_gemv(args, torch, w4, wl, synth):
+def timed_replay_ms(torch, g):
+    """One replay of graph g between two events on the current stream.  A short
+    spin kernel runs first, so the host has submitted the whole graph before the
+    start event is reached: the interval holds the graph's kernels only."""
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    torch.cuda._sleep(2_000_000)
+    start.record()
+    g.replay()
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end)
+
+
+def run_gemv(args, torch, w4, wl, synth, hip):
     shape = workload_shapes(synth)[args.workload]
     print(f"[bench] building {shape.name} ({args.replicas} replicas)", file=sys.stderr, flush=True)
     base = wl.build_dense(shape, "cuda")
@@ -543,14 +821,15 @@ def run_gemv(args, torch, w4, wl, synth):
                 w4.w4a16_gemv(reps[i % R], x, y=y)
     g.replay()
     torch.cuda.synchronize()
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    start.record()
-    g.replay()
-    end.record()
-    torch.cuda.synchronize()
-    ms_step = start.elapsed_time(end) / args.steps
+    t_wall = time.perf_counter()
+    ms_step = timed_replay_ms(torch, g) / args.steps
+    t_wall = time.perf_counter() - t_wall
     g_bytes = weight_bytes(shape.fmt, shape.n, shape.k) + shape.k * 2 + shape.n * 2
     gbs = g_bytes / (ms_step * 1e-3) / 1e9
+    del g, reps
+    torch.cuda.empty_cache()
+    ceil_same = stream_ceiling(torch, w4, g_bytes)
+    ceil_big = stream_ceiling(torch, w4, 4 << 30)
     res = {
         "metric": METRIC, "value": ms_step * 1e3, "unit": "us/call", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": False, "scaling": "weak",
@@ -558,8 +837,11 @@ def run_gemv(args, torch, w4, wl, synth):
         "config": {"workload": shape.name, "n": shape.n, "k": shape.k, "format": shape.fmt,
                    "replicas": R, "timing": "HIP graph replay of the K steps"},
         "hbm_gbps": gbs, "pct_hbm_peak": 100 * gbs / HBM_PEAK_GBS, "algorithmic_bytes_per_step": g_bytes,
+        "wall_s_timed": t_wall,
+        "ceiling": {"same_size_read": ceil_same, "read_4gib": ceil_big},
         "roofline": {"bound": "hbm", "kernel": "k_gemv", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": gbs / HBM_PEAK_GBS, "traffic": load_traffic("k_gemv", shape.name),
+                     "frac": gbs / HBM_PEAK_GBS, "frac_of_same_size_read": gbs / ceil_same["gbps"],
+                     "traffic": load_traffic("k_gemv", shape.name),
                      "algorithmic_bytes_per_launch": g_bytes, "avg_launch_us": ms_step * 1e3,
                      "note": "graph replay time per launch (one kernel per step)"},
     }
@@ -606,6 +888,7 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     w4.lib()
+    hip = HipRuntime()
     if args.calibrate_copy:
         src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda").fill_(1)
         dst = torch.empty_like(src)
@@ -614,14 +897,15 @@ def main():
         torch.cuda.synchronize()
         del src, dst
     if args.workload.startswith("gemv"):
-        res, shape = run_gemv(args, torch, w4, wl, synth)
+        res, shape = run_gemv(args, torch, w4, wl, synth, hip)
         cpu = None if args.no_cpu_baseline else cpu_baseline_gemv(shape, args.cpu_reps)
     else:
-        res, shape = run_moe(args, torch, w4, wl, synth)
+        res, shape = run_moe(args, torch, w4, wl, synth, hip)
         cpu = None if args.no_cpu_baseline else cpu_baseline_moe(
             shape, args.cpu_tokens if shape.tokens == 1 else 4, args.cpu_reps if shape.tokens == 1 else 2)
     res["cpu_baseline"] = cpu
-    res["device"] = torch.cuda.get_device_name(0)
+    res["machine"] = machine_info(hip)
+    res["device"] = res["machine"]["device"]
     res["source_digest"] = source_digest()
     print(json.dumps(res), flush=True)
 

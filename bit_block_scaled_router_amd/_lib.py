@@ -27,13 +27,14 @@ W4_FMT_NVFP4_E4M3S16 = 3
 W4_FMT_BF16 = 4
 W4_FMT_MXFP4_E8M0S32 = 5
 W4_LAYOUT_CANONICAL = 0
+W4_LAYOUT_GFX950_V1 = 1
 
 # every symbol the header declares
 EXPORTS = (
     "w4_status_string", "w4_last_error", "w4_version",
     "w4_codes_bytes", "w4_scales_bytes", "w4_quantize",
-    "w4_pack_nibbles", "w4_unpack_nibbles",
-    "w4a16_gemv", "w4_dequant_device",
+    "w4_pack_nibbles", "w4_unpack_nibbles", "w4_pack", "w4_unpack",
+    "w4a16_gemv", "w4_dequant_device", "w4_mx_dot_device", "w4_bench_stream_read",
     "moe_w4a16_workspace_bytes", "moe_w4a16_forward", "moe_w4a16_forward_timed", "moe_w4a16_stage_count",
     "moe_w4a16_experts",
 )
@@ -102,8 +103,12 @@ def lib():
             "w4_quantize": (C.c_int, [I32, P, I64, I64, P, P, P]),
             "w4_pack_nibbles": (C.c_int, [P, I64, I64, P]),
             "w4_unpack_nibbles": (C.c_int, [P, I64, I64, P]),
+            "w4_pack": (C.c_int, [I32, I64, I64, I64, P, P, I32, P, P]),
+            "w4_unpack": (C.c_int, [I32, I64, I64, I64, I32, P, P, P, P]),
             "w4a16_gemv": (C.c_int, [C.POINTER(W4Matrix), P, I64, P, P]),
             "w4_dequant_device": (C.c_int, [C.POINTER(W4Matrix), P, P]),
+            "w4_mx_dot_device": (C.c_int, [C.POINTER(W4Matrix), P, P, I64, P, P]),
+            "w4_bench_stream_read": (C.c_int, [P, SZ, P, P]),
             "moe_w4a16_workspace_bytes": (SZ, [C.POINTER(MoELayerDesc), I64]),
             "moe_w4a16_forward": (C.c_int, [C.POINTER(MoELayerDesc), P, I64, P, P, P, P, SZ, P]),
             "moe_w4a16_forward_timed": (C.c_int, [C.POINTER(MoELayerDesc), P, I64, P, P, P, P, SZ, P, P, I32]),

@@ -143,5 +143,8 @@ void launch_route_group(GroupArgs &a, hipStream_t st, hipEvent_t e0, hipEvent_t 
 void launch_gw13(GW13Args &a, hipStream_t st, hipEvent_t e0, hipEvent_t e1);
 void launch_gw2(GW2Args &a, hipStream_t st, hipEvent_t e0, hipEvent_t e1);
 void launch_gcombine(GCombineArgs &a, hipStream_t st, hipEvent_t e0, hipEvent_t e1);
+// test hook: out [n][m] = A (MXFP4) B^T (MXFP8) on the scaled FP4 MFMA; n, m % 16 == 0, k % 128 == 0
+void launch_mx_dot(const uint8_t *ac, const uint8_t *as, const uint8_t *bc, const uint8_t *bs, float *out, int n,
+                   int m, int k, hipStream_t st);
 
 }  // namespace w4k

@@ -1774,6 +1774,35 @@ __global__ __launch_bounds__(256) void k_moe_pfmx2(MX2Args a) {
 
 // ================================================================= combine
 
+// Test hook of the scaled FP4 MFMA: out[i][j] = sum_k A[i][k] B[j][k] with A
+// MXFP4 (E2M1 codes [n][k/2], E8M0 [n][k/32]) and B MXFP8 (E4M3 [m][k], E8M0
+// [m][k/32]), one wave per 16 x 16 output tile, every 128-wide K chunk added
+// into the same accumulator: the operand mapping (mfma_mx) and the per-wave
+// accumulation chain of the MX expert kernels, on plain matrices.
+__global__ __launch_bounds__(64) void k_mx_dot(const uint8_t *__restrict__ ac, const uint8_t *__restrict__ as,
+                                               const uint8_t *__restrict__ bc, const uint8_t *__restrict__ bs,
+                                               float *__restrict__ out, int n, int m, int k) {
+    const int lane = threadIdx.x & 63;
+    const int r = lane & 15, g = lane >> 4;
+    const int row0 = (int)blockIdx.y * 16, col0 = (int)blockIdx.x * 16;
+    const Buf ab = make_buf(ac, (uint32_t)n * (uint32_t)(k >> 1));
+    const Buf asb = make_buf(as, (uint32_t)n * (uint32_t)(k >> 5));
+    const Buf bb = make_buf(bc, (uint32_t)m * (uint32_t)k);
+    const Buf bsb = make_buf(bs, (uint32_t)m * (uint32_t)(k >> 5));
+    const uint32_t row = (uint32_t)(row0 + r), col = (uint32_t)(col0 + r);
+    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int k0 = 0; k0 < k; k0 += 128) {
+        const uint4 av = ld128(ab, row * (uint32_t)(k >> 1) + (uint32_t)((k0 + 32 * g) >> 1));
+        const uint32_t sa = ld8(asb, row * (uint32_t)(k >> 5) + (uint32_t)(k0 >> 5) + (uint32_t)g);
+        const uint32_t xo = col * (uint32_t)k + (uint32_t)(k0 + 16 * g);
+        const uint4 blo = ld128(bb, xo), bhi = ld128(bb, xo + 64u);
+        const uint32_t sb = ld8(bsb, col * (uint32_t)(k >> 5) + (uint32_t)(k0 >> 5) + (uint32_t)g);
+        acc = mfma_mx(av, blo, bhi, sa, sb, acc);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) out[(size_t)(row0 + 4 * g + j) * m + col] = acc[j];
+}
+
 __global__ __launch_bounds__(256) void k_moe_gcombine(GCombineArgs a) {
     // four consecutive outputs per thread (H is a multiple of 64); every element
     // is summed in slot order, then the shared expert, as one scalar would be
@@ -1963,6 +1992,12 @@ void launch_mx13(MX13Args &a, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
 void launch_mx2(MX2Args &a, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
     a.tiles = (a.H + 63) / 64;
     go_ev(st, e0, e1, k_moe_mx2, dim3(grouped_grid(a.Gmax, a.tiles)), dim3(256), 0, a);
+}
+
+void launch_mx_dot(const uint8_t *ac, const uint8_t *as, const uint8_t *bc, const uint8_t *bs, float *out, int n,
+                   int m, int k, hipStream_t st) {
+    hipLaunchKernelGGL(k_mx_dot, dim3((unsigned)(m / 16), (unsigned)(n / 16)), dim3(64), 0, st, ac, as, bc, bs, out,
+                       n, m, k);
 }
 
 void launch_gcombine(GCombineArgs &a, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {

@@ -42,13 +42,27 @@ int group_of(int32_t format) {
 int check_shape(int32_t format, int32_t layout, int64_t groups, int64_t n, int64_t k) {
     const int g = group_of(format);
     if (!g) return fail(W4_ERR_LAYOUT, "unknown format tag %d", (int)format);
-    if (layout != W4_LAYOUT_CANONICAL) return fail(W4_ERR_LAYOUT, "unknown layout tag %d", (int)layout);
+    if (layout != W4_LAYOUT_CANONICAL && layout != W4_LAYOUT_GFX950_V1)
+        return fail(W4_ERR_LAYOUT, "unknown layout tag %d", (int)layout);
     if (groups < 1 || n < 1 || k < 1) return fail(W4_ERR_INVALID_ARG, "groups/n/k must be >= 1");
     const int64_t kmul = format == W4_FMT_INT4_F16S128 ? 128 : 32;
     if (k % kmul) return fail(W4_ERR_INVALID_ARG, "k=%lld must be a multiple of %lld", (long long)k, (long long)kmul);
     if (groups > (int64_t(1) << 20) || n > (int64_t(1) << 31) || k > (int64_t(1) << 24))
         return fail(W4_ERR_INVALID_ARG, "matrix dimensions out of range");
     return W4_OK;
+}
+
+size_t scale_bytes_per_row(int32_t format, int64_t k) {
+    if (format == W4_FMT_BF16) return 0;
+    const size_t b = (format == W4_FMT_NVFP4_E4M3S16 || format == W4_FMT_MXFP4_E8M0S32) ? 1 : 2;
+    return (size_t)(k / group_of(format)) * b;
+}
+
+size_t code_bytes_per_row(int32_t format, int64_t k) { return format == W4_FMT_BF16 ? (size_t)k * 2 : (size_t)k / 2; }
+
+size_t v1_row_bytes(int32_t format, int64_t k) {
+    const size_t b = code_bytes_per_row(format, k) + scale_bytes_per_row(format, k);
+    return (b + 15) / 16 * 16;
 }
 
 // ---------------------------------------------------------------- fp16 / E2M1
@@ -189,15 +203,15 @@ const char *w4_version(void) { return "w4moe 0.1 gfx950"; }
 
 size_t w4_codes_bytes(int32_t format, int32_t layout, int64_t groups, int64_t n, int64_t k) {
     if (check_shape(format, layout, groups, n, k) != W4_OK) return 0;
-    if (format == W4_FMT_BF16) return (size_t)groups * (size_t)n * (size_t)k * 2;
-    return (size_t)groups * (size_t)n * (size_t)(k / 2);
+    const size_t rows = (size_t)groups * (size_t)n;
+    if (layout == W4_LAYOUT_GFX950_V1) return rows * v1_row_bytes(format, k);
+    return rows * code_bytes_per_row(format, k);
 }
 
 size_t w4_scales_bytes(int32_t format, int32_t layout, int64_t groups, int64_t n, int64_t k) {
     if (check_shape(format, layout, groups, n, k) != W4_OK) return 0;
-    if (format == W4_FMT_BF16) return 0;
-    const size_t bytes = (format == W4_FMT_NVFP4_E4M3S16 || format == W4_FMT_MXFP4_E8M0S32) ? 1 : 2;
-    return (size_t)groups * (size_t)n * (size_t)(k / group_of(format)) * bytes;
+    if (layout == W4_LAYOUT_GFX950_V1) return 0;  // the scales travel inside each row record
+    return (size_t)groups * (size_t)n * scale_bytes_per_row(format, k);
 }
 
 int w4_quantize(int32_t format, const float *w, int64_t n, int64_t k, uint8_t *codes, void *scales,
@@ -278,6 +292,68 @@ int w4_unpack_nibbles(const uint8_t *packed, int64_t n, int64_t k, uint8_t *nibb
     for (int64_t i = 0; i < total / 2; ++i) {
         nibbles[2 * i] = packed[i] & 0xF;
         nibbles[2 * i + 1] = packed[i] >> 4;
+    }
+    return W4_OK;
+}
+
+// Canonical <-> device layout.  GFX950_V1 stores each row as one record: the
+// row's codes (canonical nibble order) followed by its block scales, padded
+// with zero bytes to a multiple of 16.  Both directions move bytes only, so
+// they are exact inverses for any input (padding excepted).
+static int pack_args(int32_t format, int64_t groups, int64_t n, int64_t k, int32_t layout, const void *a,
+                     const void *b, const void *c) {
+    int st = check_shape(format, layout, groups, n, k);
+    if (st) return st;
+    if (!a || !c) return fail(W4_ERR_INVALID_ARG, "null codes pointer");
+    if (!b && format != W4_FMT_BF16) return fail(W4_ERR_INVALID_ARG, "null scales pointer");
+    return W4_OK;
+}
+
+int w4_pack(int32_t format, int64_t groups, int64_t n, int64_t k, const uint8_t *codes, const void *scales,
+            int32_t dst_layout, uint8_t *codes_out, void *scales_out) {
+    clear_error();
+    int st = pack_args(format, groups, n, k, dst_layout, codes, scales, codes_out);
+    if (st) return st;
+    const size_t rows = (size_t)groups * (size_t)n;
+    const size_t cb = code_bytes_per_row(format, k), sb = scale_bytes_per_row(format, k);
+    if (dst_layout == W4_LAYOUT_CANONICAL) {
+        if (sb && !scales_out) return fail(W4_ERR_INVALID_ARG, "null scales_out");
+        std::memmove(codes_out, codes, rows * cb);
+        if (sb) std::memmove(scales_out, scales, rows * sb);
+        return W4_OK;
+    }
+    const size_t rs = v1_row_bytes(format, k);
+    const uint8_t *sc = static_cast<const uint8_t *>(scales);
+    for (size_t r = 0; r < rows; ++r) {
+        uint8_t *dst = codes_out + r * rs;
+        std::memcpy(dst, codes + r * cb, cb);
+        if (sb) std::memcpy(dst + cb, sc + r * sb, sb);
+        std::memset(dst + cb + sb, 0, rs - cb - sb);
+    }
+    return W4_OK;
+}
+
+int w4_unpack(int32_t format, int64_t groups, int64_t n, int64_t k, int32_t src_layout, const uint8_t *codes_in,
+              const void *scales_in, uint8_t *codes, void *scales) {
+    clear_error();
+    int st = check_shape(format, src_layout, groups, n, k);
+    if (st) return st;
+    if (!codes_in || !codes) return fail(W4_ERR_INVALID_ARG, "null codes pointer");
+    const size_t rows = (size_t)groups * (size_t)n;
+    const size_t cb = code_bytes_per_row(format, k), sb = scale_bytes_per_row(format, k);
+    if (sb && !scales) return fail(W4_ERR_INVALID_ARG, "null scales output");
+    if (src_layout == W4_LAYOUT_CANONICAL) {
+        if (sb && !scales_in) return fail(W4_ERR_INVALID_ARG, "null scales_in");
+        std::memmove(codes, codes_in, rows * cb);
+        if (sb) std::memmove(scales, scales_in, rows * sb);
+        return W4_OK;
+    }
+    const size_t rs = v1_row_bytes(format, k);
+    uint8_t *sc = static_cast<uint8_t *>(scales);
+    for (size_t r = 0; r < rows; ++r) {
+        const uint8_t *src = codes_in + r * rs;
+        std::memcpy(codes + r * cb, src, cb);
+        if (sb) std::memcpy(sc + r * sb, src + cb, sb);
     }
     return W4_OK;
 }

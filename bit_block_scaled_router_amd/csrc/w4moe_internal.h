@@ -14,6 +14,12 @@ void clear_error();
 // an unknown tag.
 int group_of(int32_t format);
 
+// Bytes per matrix row: codes (bf16: 2 per element), block scales, and the
+// GFX950_V1 row record (codes then scales, padded to a multiple of 16).
+size_t code_bytes_per_row(int32_t format, int64_t k);
+size_t scale_bytes_per_row(int32_t format, int64_t k);
+size_t v1_row_bytes(int32_t format, int64_t k);
+
 // Validate format/layout tags and dimensions of a matrix stack.
 int check_shape(int32_t format, int32_t layout, int64_t groups, int64_t n, int64_t k);
 

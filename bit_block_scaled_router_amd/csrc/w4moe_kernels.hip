@@ -148,6 +148,33 @@ __global__ __launch_bounds__(256) void k_dequant(const uint8_t *__restrict__ cod
     }
 }
 
+// ================================================================= streaming-read probe
+
+// Reads bytes [0, n16 * 16) of src with 128-bit loads, UNROLL per thread in
+// flight, grid-stride; the block's XOR of everything read is stored to *sink
+// only if it equals an improbable constant, so the loads cannot be dropped and
+// nothing else is written.  A measurement aid: the box's practical ceiling for
+// a plain read of a given size, beside which the kernels' bandwidths are read.
+template <int UNROLL>
+__global__ __launch_bounds__(256) void k_stream_read(const uint4 *__restrict__ src, size_t n16,
+                                                     uint32_t *__restrict__ sink) {
+    const size_t stride = (size_t)gridDim.x * blockDim.x;
+    size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    uint32_t acc = 0;
+    for (; i + (UNROLL - 1) * stride < n16; i += UNROLL * stride) {
+        uint4 v[UNROLL];
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) v[u] = src[i + u * stride];
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+    }
+    for (; i < n16; i += stride) {
+        const uint4 v = src[i];
+        acc ^= v.x ^ v.y ^ v.z ^ v.w;
+    }
+    if (acc == 0x9E3779B9u) *sink = acc;
+}
+
 // ================================================================= router
 
 // logits[t][r] for rows r in [r_begin, r_begin + gridDim.x) of the stacked
@@ -654,6 +681,8 @@ int check_matrix(const w4_matrix *W, const char *what) {
     if (!W) return fail(W4_ERR_INVALID_ARG, "%s: null matrix", what);
     int st = w4::check_shape(W->format, W->layout, W->groups, W->n, W->k);
     if (st) return st;
+    if (W->layout != W4_LAYOUT_CANONICAL && W->format != W4_FMT_BF16)
+        return fail(W4_ERR_UNSUPPORTED, "%s: the device kernels read the canonical layout", what);
     if (!W->codes || (!W->scales && W->format != W4_FMT_BF16))
         return fail(W4_ERR_INVALID_ARG, "%s: null codes/scales", what);
     if (!aligned(W->codes, 16)) return fail(W4_ERR_ALIGNMENT, "%s: codes not 16-byte aligned", what);
@@ -1240,6 +1269,39 @@ int w4_dequant_device(const w4_matrix *W, float *out, void *stream) {
     else if (W->format == W4_FMT_MXFP4_E8M0S32) launch_dequant<FMT_MXFP4>(W, out, sm);
     else launch_dequant<FMT_INT4>(W, out, sm);
     return hip_status("dequant launch");
+}
+
+int w4_mx_dot_device(const w4_matrix *A, const uint8_t *b_codes, const uint8_t *b_scales, int64_t m, float *out,
+                     void *stream) {
+    w4::clear_error();
+    int st = check_matrix(A, "A");
+    if (st) return st;
+    if (A->format != W4_FMT_MXFP4_E8M0S32) return fail(W4_ERR_LAYOUT, "A must be MXFP4");
+    if (A->groups != 1) return fail(W4_ERR_INVALID_ARG, "A must have groups == 1");
+    if (A->n % 16 || A->k % 128 || m < 16 || m % 16 || m > (1 << 20))
+        return fail(W4_ERR_UNSUPPORTED, "needs n and m multiples of 16 and k a multiple of 128");
+    if ((uint64_t)m * (uint64_t)A->k >= (1ull << 31)) return fail(W4_ERR_UNSUPPORTED, "B too large");
+    if (!b_codes || !b_scales || !out) return fail(W4_ERR_INVALID_ARG, "null B or out");
+    if (!aligned(b_codes, 16) || !aligned(out, 4)) return fail(W4_ERR_ALIGNMENT, "B codes / out misaligned");
+    (void)hipGetLastError();
+    launch_mx_dot(A->codes, (const uint8_t *)A->scales, b_codes, b_scales, out, (int)A->n, (int)m, (int)A->k,
+                  (hipStream_t)stream);
+    return hip_status("mx dot launch");
+}
+
+int w4_bench_stream_read(const void *src, size_t bytes, uint32_t *sink, void *stream) {
+    w4::clear_error();
+    if (!src || !sink) return fail(W4_ERR_INVALID_ARG, "null src or sink");
+    if (bytes == 0 || bytes % 16) return fail(W4_ERR_INVALID_ARG, "bytes must be a positive multiple of 16");
+    if (!aligned(src, 16) || !aligned(sink, 4)) return fail(W4_ERR_ALIGNMENT, "src not 16-byte aligned");
+    const size_t n16 = bytes / 16;
+    // four loads in flight per thread; at most 8 blocks of 256 threads per CU
+    size_t blocks = (n16 + 4 * 256 - 1) / (4 * 256);
+    if (blocks > 2048) blocks = 2048;
+    (void)hipGetLastError();
+    hipLaunchKernelGGL(k_stream_read<4>, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream,
+                       (const uint4 *)src, n16, sink);
+    return hip_status("stream read launch");
 }
 
 size_t moe_w4a16_workspace_bytes(const moe_w4a16_layer *L, int64_t T) {

@@ -88,17 +88,33 @@ extern "C" {
  * does not take this format. */
 #define W4_FMT_MXFP4_E8M0S32 5
 
-/* Canonical layout, the only one this library reads:
+/* Canonical layout (the quantiser's output and the exchange format):
  *   codes  [groups][n][k/2] bytes, element 2j in the low nibble of byte j and
  *          element 2j+1 in the high nibble;
  *   scales [groups][n][k/G] fp16 bit patterns, G = 16 (E2M1) or 128 (int4);
- *          NVFP4: [groups][n][k/16] UE4M3 bytes;
+ *          NVFP4: [groups][n][k/16] UE4M3 bytes; MXFP4: [groups][n][k/32] E8M0;
  *   global_scales (NVFP4 only) [groups] fp32.
  * With y = W x, a row is one output element.  A wave streams 1 KiB of one
  * row's codes per 128-bit load (64 lanes x 16 B = 32 elements per lane, two
- * whole E2M1 scale blocks), so this layout already gives 128-bit coalesced
- * HBM loads with every scale block owned by a single lane. */
+ * whole E2M1 scale blocks) and the matching 256 B of scales per 32-bit load. */
 #define W4_LAYOUT_CANONICAL 0
+/* Device layout for gfx950 (the packed-weight layout of [LE stage P1], the
+ * packed codes and their per-16 scales read directly by the matvec, with the
+ * scales placed next to the codes they scale):
+ *   codes  one record of R bytes per row, rows in [groups][n] order: the row's
+ *          k/2 code bytes in the canonical nibble order (the operand order of
+ *          gfx950's packed fp4 conversion: byte j's low nibble is element 2j),
+ *          then the row's k/G block scales in K order, then zero padding up to
+ *          R = the next multiple of 16 (E2M1 at k = 2048: 1024 + 256 = 1280 B);
+ *   scales unused (may be NULL): w4_scales_bytes() returns 0;
+ *   global_scales (NVFP4) as in the canonical layout.
+ * Every load of a row, codes and scales, falls in one contiguous record (one
+ * DRAM stream per row instead of two arrays), and the record stride is not a
+ * power of two, so the 16-row MFMA tiles of the batched kernels spread over
+ * the memory channels.  bf16 matrices have no scales: both layouts coincide.
+ * Every entry point that takes a w4_matrix reads either layout; w4_pack /
+ * w4_unpack convert between them. */
+#define W4_LAYOUT_GFX950_V1 1
 
 /* A stack of `groups` quantised matrices W[g] of shape [n][k] (y = W x).
  * Requirements: k % 32 == 0 (E2M1, NVFP4) or k % 128 == 0 (int4); codes
@@ -126,7 +142,9 @@ const char *w4_version(void);
 
 /* ------------------------------------------------------------------ sizes (host) */
 /* Bytes of packed codes / scales for `groups` matrices of [n][k] in a layout:
- * codes = groups*n*k/2, scales = groups*n*(k/G)*2 (NVFP4: groups*n*(k/16)).
+ * canonical: codes = groups*n*k/2, scales = groups*n*(k/G)*2 (NVFP4:
+ * groups*n*(k/16)); GFX950_V1: codes = groups*n*R (the row record above),
+ * scales = 0.
  * 8192x2048 E2M1 gives 8,388,608 + 2,097,152 = 10,485,760 B = 10.00 MiB
  * [LE stage P1]; NVFP4 8,388,608 + 1,048,576 = 9.00 MiB (+ 4 B global).
  * Returns 0 for an unknown format/layout or a k the format does not accept. */
@@ -160,6 +178,19 @@ size_t w4_scales_bytes(int32_t format, int32_t layout, int64_t groups, int64_t n
 int w4_quantize(int32_t format, const float *w, int64_t n, int64_t k,
                 uint8_t *codes, void *scales, float *global_scale);
 
+/* Canonical <-> device layout for a stack of `groups` [n][k] matrices (host
+ * buffers, synchronous).  w4_pack reads canonical codes / scales and writes
+ * dst_layout (GFX950_V1: records into codes_out, sized by w4_codes_bytes;
+ * scales_out unused and may be NULL; CANONICAL: a copy).  w4_unpack reads
+ * src_layout and writes canonical codes and scales.  Bytes are only moved, so
+ * the two are exact inverses (the V1 padding is written as zeros and ignored on
+ * unpack).  The pages fix no device layout; unknown tags fail loudly
+ * (lynn-engine README P59).  Errors: W4_ERR_LAYOUT, W4_ERR_INVALID_ARG. */
+int w4_pack(int32_t format, int64_t groups, int64_t n, int64_t k, const uint8_t *codes, const void *scales,
+            int32_t dst_layout, uint8_t *codes_out, void *scales_out);
+int w4_unpack(int32_t format, int64_t groups, int64_t n, int64_t k, int32_t src_layout, const uint8_t *codes_in,
+              const void *scales_in, uint8_t *codes, void *scales);
+
 /* Host helpers between one-nibble-per-byte codes [n][k] (values 0..15) and the
  * packed canonical codes [n][k/2] (low nibble = even element).  Exact inverses
  * for any input; w4_pack_nibbles rejects a nibble > 15 (W4_ERR_INVALID_ARG). */
@@ -183,6 +214,26 @@ int w4a16_gemv(const w4_matrix *W, const uint16_t *x, int64_t m, uint16_t *y, vo
  * NVFP4: code x scale is exact and its product with the global scale is
  * rounded once). */
 int w4_dequant_device(const w4_matrix *W, float *out, void *stream);
+
+/* Test hook of the MXFP4 path's matrix instruction: out[i][j] = sum_k A[i][k] B[j][k]
+ * (fp32 [n][m], row-major) for an MXFP4 matrix A (groups = 1) and an MXFP8 matrix
+ * B given as E4M3 codes [m][k] (16-byte aligned) and E8M0 scale bytes [m][k/32],
+ * on gfx950's scaled FP4 MFMA with the operand mapping and accumulation chain
+ * the MX expert kernels use (each 128-wide K chunk added into one fp32
+ * accumulator).  Lets a test pin the instruction's rounding, which the MX
+ * parity bounds rely on (lynn-engine README P17/P18: e8m0/32 scale bridges).
+ * Needs n, m multiples of 16 and k a multiple of 128.  Errors: W4_ERR_LAYOUT
+ * (A not MXFP4), W4_ERR_UNSUPPORTED, W4_ERR_INVALID_ARG, _ALIGNMENT, _HIP. */
+int w4_mx_dot_device(const w4_matrix *A, const uint8_t *b_codes, const uint8_t *b_scales, int64_t m, float *out,
+                     void *stream);
+
+/* Measurement aid (not a step of the layer): read `bytes` (a multiple of 16) of
+ * device memory at src with 128-bit loads spread over the whole GPU, four per
+ * thread in flight, and write nothing but, with negligible probability, one word
+ * to *sink (device, 4-byte aligned).  Timing it gives the practical HBM read
+ * ceiling for a buffer of that size, the second denominator beside the 8 TB/s
+ * peak.  Asynchronous on `stream`.  Errors: W4_ERR_INVALID_ARG, _ALIGNMENT, _HIP. */
+int w4_bench_stream_read(const void *src, size_t bytes, uint32_t *sink, void *stream);
 
 /* ------------------------------------------------------------------ MoE layer */
 /* One MoE decode layer [TUT note 06 and the 35B-A3B config; README P28/P29/P45].

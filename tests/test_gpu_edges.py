@@ -79,3 +79,34 @@ def test_largest_token_count_sampled():
     keep = [r for r in rows if __import__("moe_cases").min_gap(or_layer, x[r]) >= 1e-3]
     print(f"T=4096 sampled {len(keep)}", flush=True)
     _check(shape, dev_layer, or_layer, x, "T=4096", rows=np.array(keep))
+
+
+# The router's special cases: k = 1 (the single selected expert's renormalised
+# weight is exactly 1) and k = E (every expert selected; the weights are the full
+# softmax, ids in descending order).  Both on the single-token path (T < 4) and
+# the grouped path (T >= 4), with and without a shared expert.
+ROUTER_EDGE = [
+    synth.MoEShape("edge-k1", 256, 128, 8, 1, 0, 1, 0.0, 21),
+    synth.MoEShape("edge-k1-shared", 256, 128, 8, 1, 128, 1, 0.0, 22),
+    synth.MoEShape("edge-kE", 256, 128, 8, 8, 0, 1, 0.0, 23),
+    synth.MoEShape("edge-kE-shared", 256, 128, 8, 8, 128, 1, 0.0, 24),
+]
+
+
+@pytest.mark.parametrize("shape", ROUTER_EDGE, ids=lambda s: s.name)
+@pytest.mark.parametrize("T", [1, 3, 6, 40])
+def test_router_extremes(shape, T):
+    print(f"router edge {shape.name} T={T}", flush=True)
+    dev_layer = wl.build_moe_layer(shape, device=DEV)
+    or_layer = oracle_layer(shape)
+    x = tie_free_tokens(shape, or_layer, T, first=7 * T)
+    got, ids, wts = _run(shape, dev_layer, x)
+    ref, rids, rw = ops.moe_forward(or_layer, x)
+    assert np.array_equal(ids, rids), (ids, rids)
+    if shape.top_k == 1:
+        assert np.all(wts == 1.0), wts  # w / sum(w) over one expert: exactly 1
+    else:
+        assert np.array_equal(np.sort(ids, axis=1), np.tile(np.arange(shape.num_experts), (T, 1)))
+        np.testing.assert_allclose(wts.sum(axis=1), 1.0, rtol=1e-6)
+    np.testing.assert_allclose(wts, rw, rtol=2e-6, atol=1e-7)
+    assert_bf16_close(got, ref, f"{shape.name} T={T}")

@@ -35,7 +35,7 @@ from oracle import formats as F
 from oracle import ops
 import bit_block_scaled_router_amd as w4
 from bit_block_scaled_router_amd import synth, workloads as wl
-from moe_cases import assert_bf16_close, oracle_layer, tie_free_tokens
+from moe_cases import MAX_REL, MEAN_MIN, MEAN_REL, assert_bf16_close, oracle_layer, tie_free_tokens
 
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
@@ -150,7 +150,7 @@ def _validate_h(h, err, hq_dev, X_dev):
     return hd, int(d.sum()), int(other.sum()), worst
 
 
-def _mx_case(shape, dev_layer, or_layer, xb, what, tokens=None, ids=None, w=None):
+def _mx_case(shape, dev_layer, or_layer, xb, what, tokens=None, ids=None, w=None, xfail_on_flips=False):
     T = xb.shape[0]
     H, I, K = shape.hidden, shape.inter, shape.top_k
     P = T * K
@@ -211,7 +211,25 @@ def _mx_case(shape, dev_layer, or_layer, xb, what, tokens=None, ids=None, w=None
           f"exponent {blocks}, largest |h - midpoint| / bound {worst:.3g}; vs the oracle's own roundings {rep_plain}",
           flush=True)
     assert flips <= max(4, MAX_FLIP_FRAC * n_h), what
+    _plain_bar(rep_plain, ydev[rows].size, what, flips, xfail_on_flips)
     return rep
+
+
+def _plain_bar(rep_plain, size, what, flips, xfail_on_flips=False):
+    """The parity bar against the plain oracle (its own h roundings throughout).
+
+    xfail_on_flips: the case's outputs are few enough that a single h element on
+    the other side of an MXFP8 midpoint (caused by the scaled MFMA's per-block
+    truncation, within the error model checked above) moves the mean error past
+    the bar; such a case is an expected failure when, and only when, the checks
+    above show that flips are the whole difference."""
+    ok = rep_plain["max_abs"] <= MAX_REL * rep_plain["max_ref"] and (size < MEAN_MIN or rep_plain["rel_l1"] <= MEAN_REL)
+    if ok:
+        return
+    if xfail_on_flips and flips > 0 and rep_plain["max_abs"] <= MAX_REL * rep_plain["max_ref"]:
+        pytest.xfail(f"{what}: {flips} h element(s) rounded to the neighbouring MXFP8 value by the scaled MFMA's "
+                     f"per-block truncation; relative L1 against the plain oracle {rep_plain['rel_l1']:.3g}")
+    raise AssertionError((what, "plain oracle", rep_plain))
 
 
 @pytest.fixture(scope="module")
@@ -233,7 +251,8 @@ def test_mx_tiny_experts_entry(tiny_mx):
     xb = tie_free_tokens(shape, or_layer, 4, first=20)
     ids = np.array([[1, 6], [6, 1], [3, 3], [0, 7]], dtype=np.int32)
     w = np.array([[0.7, 0.3], [0.5, 0.5], [1.0, 0.25], [0.125, -0.5]], dtype=np.float32)
-    _mx_case(shape, dev_layer, or_layer, xb, "mx experts", ids=ids, w=w)
+    # four tokens (1,024 outputs): one h flip moves the mean error by ~4e-4
+    _mx_case(shape, dev_layer, or_layer, xb, "mx experts", ids=ids, w=w, xfail_on_flips=True)
 
 
 @pytest.fixture(scope="module")
@@ -393,7 +412,7 @@ def _mx_case_single(shape, dev_layer, or_layer, xb, what, ids=None, w=None):
           flush=True)
     assert flips <= max(4, MAX_FLIP_FRAC * n_h), what
     # the plain oracle output (its own h roundings) within the parity bar
-    assert rep_plain["max_abs"] <= 1e-2 * rep_plain["max_ref"], (what, rep_plain)
+    _plain_bar(rep_plain, ydev.size, what, flips)
     return rep
 
 
@@ -433,3 +452,75 @@ def test_mx_full_t3(full_mx):
     shape, dev_layer, or_layer = full_mx
     print("mx full T=3", flush=True)
     _mx_case_single(shape, dev_layer, or_layer, tie_free_tokens(shape, or_layer, 3, first=10), "mx full T=3")
+
+
+# ------------------------------------------------------------------ the instruction's rounding
+#
+# The MX batch bounds above rest on one property of v_mfma_scale_f32_16x16x128_f8f6f4:
+# a 32-element block's sum (both operands' E8M0 scales applied) is within
+# EPS_BLOCK of the block's largest |product| of the exact sum, and sums across
+# blocks and chunks add fp32 roundings.  The test hook runs the instruction with
+# the MX kernels' operand mapping on plain matrices and checks that bound against
+# the exact (float64) products, on random full-range operands and on blocks built
+# to expose the truncation (one large product beside 31 small ones).
+
+def _mx_dot_case(a_codes, a_scales, b_codes, b_scales):
+    n, m = a_codes.shape[0], b_codes.shape[0]
+    A = w4.QMatrix.upload(MX, a_codes, a_scales, DEV)
+    out = w4.w4_mx_dot_device(A, torch.from_numpy(b_codes).to(DEV), torch.from_numpy(b_scales).to(DEV))
+    dev = out.cpu().numpy().astype(np.float64)
+    wa = oracle.dequant(F.FMT_MXFP4, a_codes, a_scales).astype(np.float64)
+    wb = _e4m3(b_codes) * np.repeat(np.exp2(b_scales.astype(np.float64) - 127.0), 32, axis=1)
+    exact = wa @ wb.T
+    p = np.abs(wa)[:, None, :] * np.abs(wb)[None, :, :]  # [n][m][k]
+    blocks = p.reshape(n, m, -1, 32)
+    bmax = blocks.max(axis=3).sum(axis=2)
+    bound = EPS_BLOCK * bmax + EPS_ADD * blocks.shape[2] * p.sum(axis=2)
+    err = np.abs(dev - exact)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        ratio = np.where(bmax > 0, err / bmax, 0.0)
+    return err, bound, float(ratio.max()), int((err > 0).sum())
+
+
+def _valid_e4m3(rng, shape):
+    b = rng.integers(0, 256, size=shape, dtype=np.uint8)
+    b[(b & 0x7F) == 0x7F] = 0x70  # no NaN codes
+    return b
+
+
+def test_scaled_mfma_error_model_random():
+    rng = np.random.default_rng(2027)
+    n, m, k = 64, 64, 1024
+    a = rng.integers(0, 256, size=(n, k // 2), dtype=np.uint8)
+    sa = rng.integers(118, 137, size=(n, k // 32), dtype=np.uint8)
+    b = _valid_e4m3(rng, (m, k))
+    sb = rng.integers(118, 137, size=(m, k // 32), dtype=np.uint8)
+    err, bound, worst, inexact = _mx_dot_case(a, sa, b, sb)
+    print(f"scaled MFMA, random operands: {inexact} of {n * m} sums inexact, worst |error| / "
+          f"sum of block maxima = 2^{np.log2(worst) if worst > 0 else -np.inf:.2f}", flush=True)
+    assert np.all(err <= bound), (float((err / bound).max()),)
+    assert worst <= EPS_BLOCK
+
+
+def test_scaled_mfma_error_model_directed():
+    # A = 1.0 everywhere (code 0x2, scale byte 127); column j of B holds, in each
+    # 32-block, 256 at one position and v_j at the 31 others (E4M3 bytes with
+    # scale byte 127), so the block sums are 256 + 31 v_j.
+    n, k = 16, 256
+    a = np.full((n, k // 2), 0x22, dtype=np.uint8)
+    sa = np.full((n, k // 32), 127, dtype=np.uint8)
+    smalls = [2.0 ** -9, 2.0 ** -8, 2.0 ** -7, 2.0 ** -6, 0.0234375, 2.0 ** -3, 0.75, 3.0, 2.0 ** -9 * 3,
+              2.0 ** -5 * 1.125, 2.0 ** -4 * 1.875, 1.0, 0.5, 2.0 ** -2 * 1.25, 0.0, 7.0]
+    m = len(smalls)
+    vals = np.empty((m, k))
+    for j, v in enumerate(smalls):
+        vals[j] = v
+        vals[j, (np.arange(k // 32) * 32 + (j % 32))] = 256.0
+    b = _e4m3_codes(vals)
+    assert np.array_equal(_e4m3(b), vals)
+    sb = np.full((m, k // 32), 127, dtype=np.uint8)
+    err, bound, worst, inexact = _mx_dot_case(a, sa, b, sb)
+    print(f"scaled MFMA, one large product per block: {inexact} of {n * m} sums inexact, worst |error| / sum of "
+          f"block maxima = 2^{np.log2(worst) if worst > 0 else -np.inf:.2f}", flush=True)
+    assert np.all(err <= bound), (float((err / bound).max()),)
+    assert worst <= EPS_BLOCK

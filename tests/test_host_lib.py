@@ -292,7 +292,7 @@ def _gemv(W, x=1 << 20, m=1, y=1 << 21):
 def test_gemv_validation_returns_before_launch():
     assert _gemv(_mat(fmt=9)) == w4.W4_ERR_LAYOUT
     assert _gemv(_mat(fmt=w4.W4_FMT_MXFP4_E8M0S32)) == w4.W4_ERR_UNSUPPORTED  # MX serves the MoE layer
-    assert _gemv(_mat(layout=1)) == w4.W4_ERR_LAYOUT
+    assert _gemv(_mat(layout=7)) == w4.W4_ERR_LAYOUT
     assert _gemv(_mat(k=48)) == w4.W4_ERR_INVALID_ARG
     assert _gemv(_mat(fmt=w4.W4_FMT_INT4_F16S128, k=64)) == w4.W4_ERR_INVALID_ARG
     assert _gemv(_mat(codes=4100)) == w4.W4_ERR_ALIGNMENT
