@@ -238,7 +238,7 @@ def w4a16_gemv(W, x, y=None, stream=None):
     m = x2.shape[0]
     _require(x2, "x", torch.bfloat16, (m, W.k))
     if y is None:
-        y = torch.empty((m, W.n), dtype=torch.bfloat16, device=x.device)
+        y = torch.empty((m, W.n) if x.dim() == 2 else (W.n,), dtype=torch.bfloat16, device=x.device)
     if not isinstance(y, torch.Tensor) or y.dim() != x.dim():
         raise ValueError("y must have as many dimensions as x ([n] or [m][n])")
     _require(y if y.dim() == 2 else y.unsqueeze(0), "y", torch.bfloat16, (m, W.n), x.device)
