@@ -362,6 +362,15 @@ def moe_w4a16_forward(layer, x, y=None, topk_ids=None, topk_w=None, ws=None, str
     return y
 
 
+def moe_w4a16_forward_noalloc(layer, x, y, topk_ids=None, topk_w=None, stream=None):
+    """moe_w4a16_forward on the library's per-GPU scratch: nothing is allocated,
+    so y (bf16 [T][H]) must be given."""
+    T = _check_moe_args(layer, x, y, None, topk_ids, topk_w)
+    check(lib().moe_w4a16_forward_noalloc(C.byref(layer.desc), _ptr(x), T, _ptr(y), _ptr(topk_ids), _ptr(topk_w),
+                                          _stream(stream)))
+    return y
+
+
 def moe_w4a16_stage_count(layer, T):
     n = lib().moe_w4a16_stage_count(C.byref(layer.desc), T)
     if n == 0:

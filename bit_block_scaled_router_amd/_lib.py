@@ -36,7 +36,7 @@ EXPORTS = (
     "w4_pack_nibbles", "w4_unpack_nibbles", "w4_pack", "w4_unpack",
     "w4a16_gemv", "w4_dequant_device", "w4_mx_dot_device", "w4_bench_stream_read",
     "moe_w4a16_workspace_bytes", "moe_w4a16_forward", "moe_w4a16_forward_timed", "moe_w4a16_stage_count",
-    "moe_w4a16_experts",
+    "moe_w4a16_experts", "moe_w4a16_forward_noalloc",
 )
 
 
@@ -114,6 +114,7 @@ def lib():
             "moe_w4a16_forward_timed": (C.c_int, [C.POINTER(MoELayerDesc), P, I64, P, P, P, P, SZ, P, P, I32]),
             "moe_w4a16_stage_count": (C.c_int, [C.POINTER(MoELayerDesc), I64]),
             "moe_w4a16_experts": (C.c_int, [C.POINTER(MoELayerDesc), P, I64, P, P, P, P, SZ, P]),
+            "moe_w4a16_forward_noalloc": (C.c_int, [C.POINTER(MoELayerDesc), P, I64, P, P, P, P]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)

@@ -26,6 +26,7 @@
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
+#include <mutex>
 #include <type_traits>
 
 namespace w4k {
@@ -645,6 +646,14 @@ __global__ __launch_bounds__(1024) void k_moe_down(DownArgs a) {
 }
 
 }  // namespace w4k
+
+// ================================================================= scratch of the no-allocation entry point
+
+// The workspace of moe_w4a16_forward_noalloc: one array per GPU, in the code
+// object's device memory (each device that loads the library holds its own copy
+// until the process ends).  Host code must use the address hipGetSymbolAddress
+// returns for it on each device, never this name.
+static __device__ __align__(256) unsigned char scratch[W4_NOALLOC_SCRATCH_BYTES];
 
 // ================================================================= host side
 
@@ -1322,6 +1331,46 @@ int moe_w4a16_forward_timed(const moe_w4a16_layer *L, const uint16_t *x, int64_t
     w4::clear_error();
     if (!events) return fail(W4_ERR_INVALID_ARG, "null events");
     return run_moe(L, x, T, nullptr, nullptr, y, topk_ids, topk_w, ws, ws_bytes, stream, events, n_events);
+}
+
+namespace {
+constexpr int MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void *g_scratch[MAX_DEVICES] = {};
+
+// Device address of the current device's scratch array, looked up once per
+// device (with that device current) and kept.
+int scratch_of_current_device(void **out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(W4_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= MAX_DEVICES) return fail(W4_ERR_UNSUPPORTED, "device %d: at most %d devices", dev, MAX_DEVICES);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch[dev]) {
+        void *ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !ptr)
+            return fail(W4_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+        g_scratch[dev] = ptr;
+    }
+    *out = g_scratch[dev];
+    return W4_OK;
+}
+}  // namespace
+
+int moe_w4a16_forward_noalloc(const moe_w4a16_layer *L, const uint16_t *x, int64_t T, uint16_t *y,
+                              int32_t *topk_ids, float *topk_w, void *stream) {
+    w4::clear_error();
+    MoEPlan p;
+    int st = check_layer(L, T, p);
+    if (st) return st;
+    if (p.total > W4_NOALLOC_SCRATCH_BYTES)
+        return fail(W4_ERR_WORKSPACE, "T=%lld needs %zu bytes of workspace, more than the %zu-byte scratch of the "
+                                      "no-allocation entry point (use moe_w4a16_forward with a workspace)",
+                    (long long)T, p.total, (size_t)W4_NOALLOC_SCRATCH_BYTES);
+    void *ws = nullptr;
+    if ((st = scratch_of_current_device(&ws))) return st;
+    return run_moe(L, x, T, nullptr, nullptr, y, topk_ids, topk_w, ws, W4_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 int moe_w4a16_stage_count(const moe_w4a16_layer *L, int64_t T) {

@@ -37,8 +37,9 @@
  *   - bf16 and fp16 values are passed as their 16-bit patterns (uint16_t).
  *   - Results are deterministic: fixed reduction orders, no float atomics.
  *   - Thread safety: no global mutable state besides the thread-local error
- *     message; concurrent calls on distinct streams with distinct outputs and
- *     workspaces are safe.
+ *     message and the per-device scratch address of moe_w4a16_forward_noalloc
+ *     (set once under a lock); concurrent calls on distinct streams with
+ *     distinct outputs and workspaces are safe.
  */
 #ifndef W4MOE_H
 #define W4MOE_H
@@ -323,6 +324,28 @@ int moe_w4a16_forward_timed(const moe_w4a16_layer *L, const uint16_t *x, int64_t
  * Sources: lynn-engine README, R5 notes (tokens-per-expert grouping, inverse
  * scatter) and P85-P92 (per-16 scales applied exactly). */
 int moe_w4a16_stage_count(const moe_w4a16_layer *L, int64_t T);
+
+/* Size of the scratch array of moe_w4a16_forward_noalloc (per GPU). */
+#define W4_NOALLOC_SCRATCH_BYTES ((size_t)8 << 20)
+
+/* moe_w4a16_forward without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  The intermediates live in a scratch array
+ * of W4_NOALLOC_SCRATCH_BYTES (8 MiB) that the library keeps in each GPU's
+ * memory until the process ends; this call allocates nothing (no hipMalloc, no
+ * hipFree, no allocating library routine).  The first call on a device looks up
+ * that device's scratch address (hipGetSymbolAddress) with the device current,
+ * so call it with the device of `stream` current.  Arguments and results as
+ * moe_w4a16_forward; the caller still owns x, y, topk_ids and topk_w.  A batch
+ * whose workspace (moe_w4a16_workspace_bytes) exceeds the scratch fails with
+ * W4_ERR_WORKSPACE before anything is launched (about T = 64 tokens at the
+ * 35B-A3B shape fit).  Every call on a GPU shares that GPU's scratch: calls
+ * that overlap on one GPU (other streams, other threads) race, so serialise
+ * them; the scratch keeps the last call's contents, none of which a later call
+ * reads before writing it.  Errors as moe_w4a16_forward, plus W4_ERR_HIP if the
+ * scratch address cannot be obtained. */
+int moe_w4a16_forward_noalloc(const moe_w4a16_layer *L, const uint16_t *x, int64_t T, uint16_t *y,
+                              int32_t *topk_ids, float *topk_w, void *stream);
 
 /* Experts and combine only, with caller-supplied routing (the one-call shape of
  * README P45): ids int32 [T][k] in [0, E), w fp32 [T][k] (used as given).  The

@@ -352,3 +352,17 @@ def test_moe_workspace_size_and_validation():
         == w4.W4_ERR_INVALID_ARG
     assert w4.lib().moe_w4a16_experts(C.byref(L), 1 << 20, 1, 1 << 22, None, 1 << 21, 1 << 24, ws, 0) \
         == w4.W4_ERR_INVALID_ARG
+
+
+def test_noalloc_refuses_batches_beyond_its_scratch_before_any_hip_call():
+    """A batch whose workspace exceeds the no-allocation entry point's scratch is
+    refused during validation (fake device pointers: nothing is touched)."""
+    L = _layer()
+    T = 4096
+    need = w4.lib().moe_w4a16_workspace_bytes(C.byref(L), T)
+    assert need > 8 << 20
+    st = w4.lib().moe_w4a16_forward_noalloc(C.byref(L), 1 << 20, T, 1 << 21, None, None, 0)
+    assert st == w4.W4_ERR_WORKSPACE
+    assert "scratch" in w4.w4_last_error()
+    assert w4.lib().moe_w4a16_forward_noalloc(C.byref(_layer(top_k=9)), 1 << 20, 1, 1 << 21, None, None, 0) \
+        == w4.W4_ERR_INVALID_ARG
