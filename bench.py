@@ -318,7 +318,7 @@ def ingest_counters(paths, workload):
 def _clone_q(w4, q):
     g = q.global_scales.clone() if q.global_scales is not None else None
     sc = q.scales.clone() if q.scales is not None else None
-    return w4.QMatrix(q.fmt, q.groups, q.n, q.k, q.codes.clone(), sc, g)
+    return w4.QMatrix(q.fmt, q.groups, q.n, q.k, q.codes.clone(), sc, g, layout=q.layout)
 
 
 def make_layers(w4, base, routed_replicas, copies):
@@ -380,7 +380,7 @@ def moe_bytes(shape, distinct):
     return b
 
 
-def stage_bytes(shape, distinct, n_stages=3):
+def stage_bytes(shape, distinct, n_stages=3, decode=False):
     """Algorithmic bytes per launch of each MoE kernel (T = shape.tokens).
 
     Single-token path (3 kernels): router, W13 + SiLU over all (token, slot),
@@ -397,6 +397,13 @@ def stage_bytes(shape, distinct, n_stages=3):
     dw13, dw2 = sh * (weight_bytes(sfmt, 2 * I, H) - w13), sh * (weight_bytes(sfmt, H, I) - w2)
     nexp = distinct + sh
     router = E * H * 2 + (H * 2 if shape.has_shared else 0) + T * H * 2 + T * (E + 1) * 4
+    if decode:  # router; W13 rows + K tiles of W2 per (token, slot, tile); ordered combine of the tiles
+        part = T * S * (I // 16) * H * 4  # fp32 tile contributions (scratch: not counted for the expert launch)
+        return {
+            "k_router": router,
+            "k_moe_dec": nexp * (w13 + w2) + dw13 + dw2 + T * H * 2 + T * E * 4,
+            "k_moe_dec_combine": part + T * K * 4 + T * H * 2,
+        }
     if n_stages == 3:
         return {
             "k_router": router,
@@ -430,15 +437,30 @@ def stage_bytes(shape, distinct, n_stages=3):
     }
 
 
+# weight layouts in HBM: (gate/up and dense matrices, down projections); tags of
+# W4_LAYOUT_CANONICAL = 0, W4_LAYOUT_GFX950_V1 = 1 (row records),
+# W4_LAYOUT_GFX950_KT16 = 2 (K-tiled down projections: the decode kernels)
+LAYOUTS = {"canonical": (0, 0), "gfx950": (1, 1), "decode": (1, 2)}
+
+
+DECODE_DEFAULT = ()  # workloads measured with K-tiled down projections by default
+
+
+def default_layout(workload):
+    """The layout each workload is measured in unless --layout says otherwise."""
+    return "decode" if workload in DECODE_DEFAULT else "gfx950"
+
 ROUTER_MFMA_MIN_T = 64  # the library runs the router as an MFMA GEMM from this batch size
 
 
 LARGE_BATCH_PAIRS = 4096  # past this many (token, slot) pairs the grouped GEMM kernels run
 
 
-def stage_names(n_stages, T, K, mx):
+def stage_names(n_stages, T, K, mx, decode=False):
     """Kernel names in launch order for the library's stage count at T tokens."""
     router = "k_router_mfma" if T >= ROUTER_MFMA_MIN_T else "k_router"
+    if decode:
+        return [router, "k_moe_dec", "k_moe_dec_combine"]
     if n_stages == 3:
         return [router, "k_moe_w13", "k_moe_down"]
     grouping = ["k_moe_route_group"] if n_stages in (5, 6) else ["k_route_topk", "k_route_scan", "k_route_scatter"]
@@ -451,9 +473,9 @@ def stage_names(n_stages, T, K, mx):
     return [router] + experts + grouping + proj + ["k_moe_gcombine"]
 
 
-def launch_bytes(shape, distinct, n_stages):
+def launch_bytes(shape, distinct, n_stages, decode=False):
     """stage_bytes keyed by the kernel names stage_names gives for the same call."""
-    sb = stage_bytes(shape, distinct, n_stages)
+    sb = stage_bytes(shape, distinct, n_stages, decode)
     if shape.tokens >= ROUTER_MFMA_MIN_T:
         sb["k_router_mfma"] = sb.pop("k_router")
     if shape.tokens * shape.top_k > LARGE_BATCH_PAIRS:  # the grouped GEMM kernels move the same algorithmic bytes
@@ -624,7 +646,8 @@ WORKLOADS = ["qwen-t1", "qwen-t32", "tiny", "gemv-e2m1", "gemv-int4", "qwen-t1-n
 def run_moe(args, torch, w4, wl, synth, hip):
     shape = workload_shapes(synth)[args.workload]
     T = shape.tokens
-    base = wl.build_moe_layer(shape, device="cuda")
+    l13, l2 = LAYOUTS[args.layout]
+    base = wl.build_moe_layer(shape, device="cuda", layout=l13, w2_layout=l2)
     # copies of the routing-independent tensors: at least 288 MB of them, so that
     # a copy comes back only after more than the Infinity Cache has streamed by
     per_copy = shared_copy_bytes(base)
@@ -675,7 +698,8 @@ def run_moe(args, torch, w4, wl, synth, hip):
     # per-kernel durations: each stage's K launches replayed alone, in a graph of
     # their own copied from the captured one (same kernels, arguments and order)
     n_stages = w4.moe_w4a16_stage_count(base, T)
-    names = stage_names(n_stages, T, shape.top_k, shape.fmt == "mxfp4")
+    decode = l2 == 2
+    names = stage_names(n_stages, T, shape.top_k, shape.fmt == "mxfp4", decode)
     stage_us, timing_note = {}, ("avg launch duration: the stage's K launches copied out of the captured graph "
                                  "and replayed alone (graph replay time / K), on the stream the kernels run on")
     try:
@@ -719,7 +743,7 @@ def run_moe(args, torch, w4, wl, synth, hip):
     ms_step = ms_total / n_steps
     us_token = ms_step * 1e3 / T
     step_bytes = moe_bytes(shape, d_mean)
-    sb = launch_bytes(shape, d_mean, n_stages)
+    sb = launch_bytes(shape, d_mean, n_stages, decode)
     dom = max(stage_us, key=stage_us.get)
     achieved = sb[dom] / (stage_us[dom] * 1e-6) / 1e9
     traffic = load_traffic(dom, shape.name)
@@ -763,7 +787,7 @@ def run_moe(args, torch, w4, wl, synth, hip):
                        + (", shared expert bf16" if shape.shared_fmt == "bf16" else ""),
             "activations": ("bf16; MXFP8 (E4M3 + E8M0 per 32) inside the experts" if shape.fmt == "mxfp4"
                             else "bf16"), "accumulate": "fp32", "routed_expert_replicas": args.replicas,
-            "router_shared_copies": NL, "token_pool": P,
+            "router_shared_copies": NL, "token_pool": P, "weight_layout": args.layout,
             "mean_distinct_experts": d_mean, "timing": "HIP graph replay of the K steps",
         },
         "hbm_gbps": step_bytes / (ms_step * 1e-3) / 1e9,
@@ -802,10 +826,10 @@ def timed_replay_ms(torch, g):
 def run_gemv(args, torch, w4, wl, synth, hip):
     shape = workload_shapes(synth)[args.workload]
     print(f"[bench] building {shape.name} ({args.replicas} replicas)", file=sys.stderr, flush=True)
-    base = wl.build_dense(shape, "cuda")
-    reps = [base] + [w4.QMatrix(base.fmt, 1, base.n, base.k, base.codes.clone(), base.scales.clone(),
-                                base.global_scales.clone() if base.global_scales is not None else None)
-                     for _ in range(args.replicas - 1)]
+    if args.layout == "decode":
+        raise SystemExit("the dense GEMV reads row layouts (canonical or gfx950)")
+    base = wl.build_dense(shape, "cuda", layout=LAYOUTS[args.layout][0])
+    reps = [base] + [_clone_q(w4, base) for _ in range(args.replicas - 1)]
     x = wl.bf16_tensor(synth.dense_x(shape), "cuda")
     y = torch.empty(shape.n, dtype=torch.bfloat16, device="cuda")
     R = len(reps)
@@ -835,7 +859,7 @@ def run_gemv(args, torch, w4, wl, synth, hip):
         "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": False, "scaling": "weak",
         "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": shape.name, "n": shape.n, "k": shape.k, "format": shape.fmt,
-                   "replicas": R, "timing": "HIP graph replay of the K steps"},
+                   "replicas": R, "weight_layout": args.layout, "timing": "HIP graph replay of the K steps"},
         "hbm_gbps": gbs, "pct_hbm_peak": 100 * gbs / HBM_PEAK_GBS, "algorithmic_bytes_per_step": g_bytes,
         "wall_s_timed": t_wall,
         "ceiling": {"same_size_read": ceil_same, "read_4gib": ceil_big},
@@ -856,6 +880,9 @@ def main():
     ap.add_argument("--workload", default="qwen-t1",
                     choices=WORKLOADS)
     ap.add_argument("--replicas", type=int, default=0, help="weight replicas (0 = workload default)")
+    ap.add_argument("--layout", default=None, choices=sorted(LAYOUTS),
+                    help="weight layout in HBM: row records (gfx950), row records with K-tiled down "
+                         "projections (decode), or the canonical arrays; default per workload")
     ap.add_argument("--pool", type=int, default=64, help="token pool (MoE workloads)")
     ap.add_argument("--cpu-tokens", type=int, default=1)
     ap.add_argument("--cpu-reps", type=int, default=5)
@@ -872,6 +899,8 @@ def main():
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1).", file=sys.stderr)
         sys.exit(2)
+    if args.layout is None:
+        args.layout = default_layout(args.workload)
     if args.replicas <= 0:  # enough weight bytes that the 256 MB Infinity Cache cannot hold them
         args.replicas = 4 if args.workload in ("gemv-lmhead",) or not args.workload.startswith("gemv") else 128
     if args.workload.startswith("qwen-t32"):

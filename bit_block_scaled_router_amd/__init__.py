@@ -28,6 +28,7 @@ from ._lib import (  # noqa: F401
     W4_FMT_MXFP4_E8M0S32,
     W4_LAYOUT_CANONICAL,
     W4_LAYOUT_GFX950_V1,
+    W4_LAYOUT_GFX950_KT16,
     W4_OK,
     MoELayerDesc,
     W4Error,
@@ -139,7 +140,8 @@ def w4_pack(fmt, codes, scales, layout=W4_LAYOUT_GFX950_V1):
     """Canonical host arrays codes [G][n][k/2] (or [n][k/2]; bf16: bits [G][n][k])
     and scales [G][n][k/Gs] -> (codes, scales) in `layout`.  GFX950_V1 returns
     (records uint8 [G][n][R], None): each row's codes then its scales, padded to a
-    multiple of 16 bytes."""
+    multiple of 16 bytes; GFX950_KT16 returns (records uint8 [G][k/16][R], None):
+    per 16-wide K tile, every row's 8 code bytes, then every row's scale."""
     c = np.ascontiguousarray(codes)
     if c.ndim == 2:
         c = c[None]
@@ -156,6 +158,8 @@ def w4_pack(fmt, codes, scales, layout=W4_LAYOUT_GFX950_V1):
     check(lib().w4_pack(fmt, groups, n, k, _ptr(c), _ptr(s), layout, _ptr(out), _ptr(sout)))
     if layout == W4_LAYOUT_GFX950_V1:
         return out.reshape(groups, n, -1), None
+    if layout == W4_LAYOUT_GFX950_KT16:
+        return out.reshape(groups, k // 16, -1), None
     return out.view(c.dtype).reshape(c.shape), (sout.view(s.dtype).reshape(s.shape) if sout is not None else None)
 
 
@@ -200,6 +204,7 @@ class QMatrix:
         # torch device tensors: uint8 codes, int16 (FP16 bits) or uint8 (UE4M3) scales,
         # uint8 (E8M0) for MXFP4, fp32 [groups] global scales (NVFP4)
         self.codes, self.scales, self.global_scales = codes, scales, global_scales
+        self.layout = layout
         self.desc = W4Matrix(fmt, layout, groups, n, k, _ptr(codes), _ptr(scales), _ptr(global_scales))
 
     @classmethod
@@ -212,20 +217,25 @@ class QMatrix:
         return cls(W4_FMT_BF16, groups, n, k, _torch().from_numpy(b.view(np.int16)).to(device), None)
 
     @classmethod
-    def upload(cls, fmt, codes_np, scales_np, device="cuda", global_np=None):
+    def upload(cls, fmt, codes_np, scales_np, device="cuda", global_np=None, layout=W4_LAYOUT_CANONICAL):
         """codes_np [G][n][k/2] (or [n][k/2]), scales_np [G][n][k/Gs] (uint16 FP16 bits,
-        or uint8 UE4M3 / E8M0 for NVFP4 / MXFP4), global_np fp32 [G] (NVFP4) -> device."""
+        or uint8 UE4M3 / E8M0 for NVFP4 / MXFP4), global_np fp32 [G] (NVFP4) -> device,
+        in `layout` (GFX950_V1: packed on the host by w4_pack; the matrix then has
+        row records in `codes` and no separate scales)."""
         torch = _torch()
         c = np.ascontiguousarray(codes_np)
         s = np.ascontiguousarray(scales_np)
         if c.ndim == 2:
             c, s = c[None], s[None]
         groups, n, kh = c.shape
-        tc = torch.from_numpy(c).to(device)
-        ts = torch.from_numpy(s.view(np.int16) if s.dtype == np.uint16 else s).to(device)
         tg = None
         if global_np is not None:
             tg = torch.from_numpy(np.ascontiguousarray(global_np, dtype=np.float32).reshape(-1)).to(device)
+        if layout != W4_LAYOUT_CANONICAL:
+            rec, _ = w4_pack(fmt, c, s, layout)
+            return cls(fmt, groups, n, 2 * kh, torch.from_numpy(rec).to(device), None, tg, layout=layout)
+        tc = torch.from_numpy(c).to(device)
+        ts = torch.from_numpy(s.view(np.int16) if s.dtype == np.uint16 else s).to(device)
         return cls(fmt, groups, n, 2 * kh, tc, ts, tg)
 
 

@@ -28,6 +28,7 @@ W4_FMT_BF16 = 4
 W4_FMT_MXFP4_E8M0S32 = 5
 W4_LAYOUT_CANONICAL = 0
 W4_LAYOUT_GFX950_V1 = 1
+W4_LAYOUT_GFX950_KT16 = 2
 
 # every symbol the header declares
 EXPORTS = (

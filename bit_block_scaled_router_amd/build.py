@@ -17,7 +17,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libw4moe.so")
 OBJDIR = os.path.join(os.path.dirname(HERE), "_build")
-SOURCES = ["w4moe_kernels.hip", "w4moe_grouped.hip", "w4moe_host.cpp"]
+SOURCES = ["w4moe_kernels.hip", "w4moe_grouped.hip", "w4moe_decode.hip", "w4moe_host.cpp"]
 ARCH = "gfx950"
 NOISE = "packed-fp32-ops' is not a recognized feature"
 

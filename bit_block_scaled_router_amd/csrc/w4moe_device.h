@@ -464,16 +464,16 @@ __device__ __forceinline__ float chunk_dot_f32(uint4 c, uint32_t sc, const float
     return acc;
 }
 
-// Scales of the lane's chunk from a scale buffer: E2M1 two FP16 at element
-// k0/16 of the row, NVFP4 two UE4M3 bytes at k0/16, int4 one FP16 at k0/128.
-// `row_elem0` is the row's first scale element; an out-of-range offset yields
-// zero.
+// Byte offset, within a row's scales, of the scale(s) of the 32-element lane
+// chunk starting at K index k0 (E2M1: two FP16 at block k0/16; NVFP4: two UE4M3
+// bytes; MXFP4: one E8M0 byte at block k0/32; int4: one FP16 at group k0/128).
 template <int FMT>
-__device__ __forceinline__ uint32_t scale_off(uint32_t row_elem0, int k0) {
-    return FMT == FMT_INT4    ? (row_elem0 + (uint32_t)(k0 >> 7)) * 2u
-           : FMT == FMT_MXFP4 ? (row_elem0 + (uint32_t)(k0 >> 5))
-                              : (row_elem0 + (uint32_t)(k0 >> 4)) * scale_bytes<FMT>();
+__device__ __forceinline__ uint32_t scale_col(int k0) {
+    return FMT == FMT_INT4 ? (uint32_t)(k0 >> 7) * 2u
+           : FMT == FMT_MXFP4 ? (uint32_t)(k0 >> 5)
+                              : (uint32_t)(k0 >> 4) * scale_bytes<FMT>();
 }
+
 template <int FMT>
 __device__ __forceinline__ uint32_t ld_scales(Buf b, uint32_t off) {
     if constexpr (FMT == FMT_E2M1)
@@ -484,10 +484,6 @@ __device__ __forceinline__ uint32_t ld_scales(Buf b, uint32_t off) {
         return ld16(b, off);  // int4: one FP16; NVFP4: two UE4M3 bytes
 }
 
-template <int FMT>
-__device__ __forceinline__ int scales_per_row(int k) {
-    return FMT == FMT_INT4 ? (k >> 7) : FMT == FMT_MXFP4 ? (k >> 5) : (k >> 4);
-}
 
 // ---------------------------------------------------------------- top-k
 

@@ -9,6 +9,16 @@
 
 namespace w4k {
 
+// Row addressing of one quantised matrix stack: row r of matrix e has its codes
+// at e * n * cs + r * cs bytes from the codes base and its block scales at
+// e * n * ss + r * ss bytes from the scale base.  Canonical layout: cs = code
+// bytes per row, ss = scale bytes per row, separate arrays.  GFX950_V1: one
+// record per row, cs = ss = the record size and the scale base = codes + k/2.
+// bf16 rows: cs = 2k, no scales.
+struct RowLayout {
+    uint32_t cs, ss;
+};
+
 // Group table layout in the workspace: grp[0] = number of routed groups n,
 // grp[1 + g] = expert, grp[1 + Gmax + g] = first pair-list entry,
 // grp[1 + 2*Gmax + g] = pair count (g < n).  pairs[0 .. P) holds the routed
@@ -49,9 +59,9 @@ constexpr int ROUTE_MAX_TPB = 16;
 
 struct GW13Args {
     const uint8_t *codes;   // routed W13 [E][2I][H/2]
-    const uint16_t *scales;
+    const void *scales;     // block scales (canonical array, or inside the row records)
     const uint8_t *s_codes; // shared W13 [2I][H/2] or null
-    const uint16_t *s_scales;
+    const void *s_scales;
     const uint16_t *x;      // [T][H]
     const int32_t *grp;
     const int32_t *pairs;
@@ -62,13 +72,14 @@ struct GW13Args {
     int fmt;                // FMT_E2M1, FMT_NVFP4 or FMT_INT4 (gw13 / gw2; the large-batch kernels: not INT4)
     const float *gs, *s_gs; // NVFP4 global scales: routed [E], shared [1]
     int s_bf16;             // the shared expert is bf16 (s_codes = bf16 rows, no scales)
+    RowLayout rl, s_rl;     // row strides of the routed and shared matrices
 };
 
 struct GW2Args {
     const uint8_t *codes;   // routed W2 [E][H][I/2]
-    const uint16_t *scales;
+    const void *scales;     // block scales (canonical array, or inside the row records)
     const uint8_t *s_codes; // shared W2 [H][I/2] or null
-    const uint16_t *s_scales;
+    const void *s_scales;
     const int32_t *grp;
     const int32_t *pairs;
     const uint16_t *h_hi;   // [P + T][I]
@@ -79,6 +90,7 @@ struct GW2Args {
     int fmt;                // as GW13Args
     const float *gs, *s_gs; // NVFP4 global scales: routed [E], shared [1]
     int s_bf16;             // the shared expert is bf16 (s_codes = bf16 rows, no scales)
+    RowLayout rl, s_rl;     // row strides of the routed and shared matrices
 };
 
 struct GCombineArgs {
@@ -102,9 +114,9 @@ struct MXQuantArgs {
 
 struct MX13Args {
     const uint8_t *codes;   // routed W13 [E][2I][H/2]
-    const uint8_t *scales;  // [E][2I][H/32] E8M0
+    const void *scales;     // E8M0 per 32 (canonical [E][2I][H/32], or inside the row records)
     const uint8_t *s_codes; // shared W13 or null
-    const uint8_t *s_scales;
+    const void *s_scales;
     const uint8_t *xq;      // [T][H]
     const uint8_t *xs;      // [T][H/32]
     const int32_t *grp;
@@ -113,13 +125,14 @@ struct MX13Args {
     uint8_t *hs;            // [P + T][I/32]
     int H, I, K, T, P, Gmax, tiles;
     const int32_t *ctg;     // column tiles (large-batch kernels only)
+    RowLayout rl, s_rl;     // row strides of the routed and shared matrices
 };
 
 struct MX2Args {
     const uint8_t *codes;   // routed W2 [E][H][I/2]
-    const uint8_t *scales;  // [E][H][I/32]
+    const void *scales;     // E8M0 per 32 (canonical [E][H][I/32], or inside the row records)
     const uint8_t *s_codes;
-    const uint8_t *s_scales;
+    const void *s_scales;
     const int32_t *grp;
     const int32_t *pairs;
     const uint8_t *hq;
@@ -127,6 +140,7 @@ struct MX2Args {
     float *out;             // [P + T][H]
     int H, I, K, T, P, Gmax, tiles;
     const int32_t *ctg;     // column tiles (large-batch kernels only)
+    RowLayout rl, s_rl;     // row strides of the routed and shared matrices
 };
 
 size_t grouped_lds_bytes(int E, int P);
@@ -144,7 +158,7 @@ void launch_gw13(GW13Args &a, hipStream_t st, hipEvent_t e0, hipEvent_t e1);
 void launch_gw2(GW2Args &a, hipStream_t st, hipEvent_t e0, hipEvent_t e1);
 void launch_gcombine(GCombineArgs &a, hipStream_t st, hipEvent_t e0, hipEvent_t e1);
 // test hook: out [n][m] = A (MXFP4) B^T (MXFP8) on the scaled FP4 MFMA; n, m % 16 == 0, k % 128 == 0
-void launch_mx_dot(const uint8_t *ac, const uint8_t *as, const uint8_t *bc, const uint8_t *bs, float *out, int n,
-                   int m, int k, hipStream_t st);
+void launch_mx_dot(const uint8_t *ac, const uint8_t *as, RowLayout arl, const uint8_t *bc, const uint8_t *bs,
+                   float *out, int n, int m, int k, hipStream_t st);
 
 }  // namespace w4k

@@ -310,18 +310,23 @@ template <typename S>
 struct GroupView {
     const uint8_t *codes;
     const S *scales;
-    int off, m;  // first entry in the pair list, number of pairs
-    int e;       // expert id (-1: the shared expert)
+    int off, m;       // first entry in the pair list, number of pairs
+    int e;            // expert id (-1: the shared expert)
+    uint32_t cs, ss;  // row strides (bytes) of the group's codes and scales
+    size_t mat_codes, mat_scales;  // bytes of one matrix: n * cs, n * ss
 };
 
+// n: rows per matrix; rl / srl: row strides of the routed / shared matrices
 template <typename S>
-__device__ __forceinline__ GroupView<S> group_view(const int32_t *grp, int gs, int Gmax, int P, int T,
-                                                   const uint8_t *codes, const S *scales, size_t mat_codes,
-                                                   size_t mat_scales, const uint8_t *s_codes, const S *s_scales) {
+__device__ __forceinline__ GroupView<S> group_view(const int32_t *grp, int gs, int Gmax, int P, int T, int n,
+                                                   const uint8_t *codes, const void *scales, RowLayout rl,
+                                                   const uint8_t *s_codes, const void *s_scales, RowLayout srl) {
     GroupView<S> v{};
     if (s_codes != nullptr) {
         if (gs == 0) {
-            v.codes = s_codes, v.scales = s_scales, v.off = P, v.m = T, v.e = -1;
+            v.codes = s_codes, v.scales = reinterpret_cast<const S *>(s_scales), v.off = P, v.m = T, v.e = -1;
+            v.cs = srl.cs, v.ss = srl.ss;
+            v.mat_codes = (size_t)n * srl.cs, v.mat_scales = (size_t)n * srl.ss;
             return v;
         }
         --gs;
@@ -330,8 +335,10 @@ __device__ __forceinline__ GroupView<S> group_view(const int32_t *grp, int gs, i
     v.e = e;
     v.off = ld_uniform(grp, 1 + Gmax + gs);
     v.m = ld_uniform(grp, 1 + 2 * Gmax + gs);
-    v.codes = codes + (size_t)e * mat_codes;
-    v.scales = scales + (size_t)e * mat_scales;
+    v.cs = rl.cs, v.ss = rl.ss;
+    v.mat_codes = (size_t)n * rl.cs, v.mat_scales = (size_t)n * rl.ss;
+    v.codes = codes + (size_t)e * v.mat_codes;
+    v.scales = reinterpret_cast<const S *>(static_cast<const uint8_t *>(scales) + (size_t)e * v.mat_scales);
     return v;
 }
 
@@ -358,15 +365,14 @@ __device__ __forceinline__ void gw13_unit(const GW13Args &a, int gs, int tile, f
     const int lane = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int H = a.H, I = a.I;
-    const uint32_t spr = (uint32_t)scales_per_row<FMT>(H);
-    const size_t mat_codes = (size_t)(2 * I) * (H >> 1), mat_scales = (size_t)(2 * I) * spr;
-    const GroupView<SC> gv = group_view(a.grp, gs, a.Gmax, a.P, a.T, a.codes, reinterpret_cast<const SC *>(a.scales),
-                                        mat_codes, mat_scales, a.s_codes, reinterpret_cast<const SC *>(a.s_scales));
+    const GroupView<SC> gv = group_view<SC>(a.grp, gs, a.Gmax, a.P, a.T, 2 * I, a.codes, a.scales, a.rl, a.s_codes,
+                                            a.s_scales, a.s_rl);
+    const uint32_t cs = gv.cs, ss = gv.ss;  // row strides (bytes)
     // a bf16 shared expert: its rows are the MFMA operands themselves (the
     // MFMA branch takes every size of that group)
     const bool sbf = SB && gv.e < 0;
-    const Buf cb = make_buf(gv.codes, (uint32_t)(sbf ? 4 * mat_codes : mat_codes));
-    const Buf sb = make_buf(gv.scales, sbf ? 0u : (uint32_t)(mat_scales * sizeof(SC)));
+    const Buf cb = make_buf(gv.codes, (uint32_t)gv.mat_codes);
+    const Buf sb = make_buf(gv.scales, sbf ? 0u : (uint32_t)gv.mat_scales);
     float gsc = 1.f;  // NVFP4 global scale of the matrix
     if constexpr (FMT == FMT_NVFP4) gsc = sbf ? 1.f : gv.e < 0 ? ld_uniform(a.s_gs, 0) : ld_uniform(a.gs, gv.e);
     const int i0 = tile * 16;  // first gate row of the tile
@@ -408,7 +414,7 @@ __device__ __forceinline__ void gw13_unit(const GW13Args &a, int gs, int tile, f
                             xb[nt][s] = (nt == 0 || two) ? ld128(xall, pv[nt] ? xo + 16u * s : OOB) : make_uint4(0, 0, 0, 0);
                     }
                     if constexpr (SBF) {  // bf16 rows, 8 weights per MFMA step
-                        const uint32_t rb = (uint32_t)H * 2u;
+                        const uint32_t rb = cs;
 #pragma unroll
                         for (int s = 0; s < 4; ++s) {
                             const uint32_t ko = (uint32_t)(k0 + 8 * s) * 2u;
@@ -424,8 +430,8 @@ __device__ __forceinline__ void gw13_unit(const GW13Args &a, int gs, int tile, f
                         }
                         continue;
                     }
-                    const uint4 cg = ld128(cb, rg_ok ? rowg * (uint32_t)(H >> 1) + (uint32_t)(k0 >> 1) : OOB);
-                    const uint4 cu = ld128(cb, rg_ok ? rowu * (uint32_t)(H >> 1) + (uint32_t)(k0 >> 1) : OOB);
+                    const uint4 cg = ld128(cb, rg_ok ? rowg * cs + (uint32_t)(k0 >> 1) : OOB);
+                    const uint4 cu = ld128(cb, rg_ok ? rowu * cs + (uint32_t)(k0 >> 1) : OOB);
                     if constexpr (FMT == FMT_INT4) {
                         // the chunk is one scale group: MFMAs on the raw offset codes
                         // u = q + 8 (exact bf16) and on 8 (the offset), then the
@@ -435,8 +441,8 @@ __device__ __forceinline__ void gw13_unit(const GW13Args &a, int gs, int tile, f
                         for (int j = 0; j < 4; ++j) {
                             const uint32_t o = (uint32_t)(i0 + 4 * q + j);
                             const bool ov = o < (uint32_t)I;
-                            so_g[j] = f16_bits_to_f32(ld16(sb, ov ? (o * spr + (uint32_t)c) * 2u : OOB));
-                            so_u[j] = f16_bits_to_f32(ld16(sb, ov ? (((uint32_t)I + o) * spr + (uint32_t)c) * 2u : OOB));
+                            so_g[j] = f16_bits_to_f32(ld16(sb, ov ? o * ss + (uint32_t)c * 2u : OOB));
+                            so_u[j] = f16_bits_to_f32(ld16(sb, ov ? ((uint32_t)I + o) * ss + (uint32_t)c * 2u : OOB));
                         }
                         const uint32_t cgw[4] = {cg.x, cg.y, cg.z, cg.w}, cuw[4] = {cu.x, cu.y, cu.z, cu.w};
                         f32x4 tg[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}}, tu[2] = {tg[0], tg[0]},
@@ -466,8 +472,8 @@ __device__ __forceinline__ void gw13_unit(const GW13Args &a, int gs, int tile, f
                             }
                         continue;
                     }
-                    const uint32_t sg = ld_scales<FMT>(sb, rg_ok ? scale_off<FMT>(rowg * spr, k0) : OOB);
-                    const uint32_t su = ld_scales<FMT>(sb, rg_ok ? scale_off<FMT>(rowu * spr, k0) : OOB);
+                    const uint32_t sg = ld_scales<FMT>(sb, rg_ok ? rowg * ss + scale_col<FMT>(k0) : OOB);
+                    const uint32_t su = ld_scales<FMT>(sb, rg_ok ? rowu * ss + scale_col<FMT>(k0) : OOB);
                     const uint32_t cgw[4] = {cg.x, cg.y, cg.z, cg.w}, cuw[4] = {cu.x, cu.y, cu.z, cu.w};
 #pragma unroll
                     for (int s = 0; s < 4; ++s) {
@@ -575,10 +581,10 @@ __device__ __forceinline__ void gw13_unit(const GW13Args &a, int gs, int tile, f
             const int i = i0 + 4 * wv + l * RG + rsub;
             const bool v = s < ks && k0 < H && i < I && (l * RG + rsub) < 4;
             const uint32_t rg = (uint32_t)i, ru = (uint32_t)(I + i);
-            cg[s][l] = ld128(cb, v ? rg * (uint32_t)(H >> 1) + (uint32_t)(k0 >> 1) : OOB);
-            cu[s][l] = ld128(cb, v ? ru * (uint32_t)(H >> 1) + (uint32_t)(k0 >> 1) : OOB);
-            sg[s][l] = ld_scales<FMT>(sb, v ? scale_off<FMT>(rg * spr, k0) : OOB);
-            su[s][l] = ld_scales<FMT>(sb, v ? scale_off<FMT>(ru * spr, k0) : OOB);
+            cg[s][l] = ld128(cb, v ? rg * cs + (uint32_t)(k0 >> 1) : OOB);
+            cu[s][l] = ld128(cb, v ? ru * cs + (uint32_t)(k0 >> 1) : OOB);
+            sg[s][l] = ld_scales<FMT>(sb, v ? rg * ss + scale_col<FMT>(k0) : OOB);
+            su[s][l] = ld_scales<FMT>(sb, v ? ru * ss + scale_col<FMT>(k0) : OOB);
         }
     for (int idx = 0; idx < gv.m; ++idx) {
         if constexpr (FMT == FMT_INT4) {
@@ -649,13 +655,12 @@ __device__ __forceinline__ void gw2_unit(const GW2Args &a, int gs, int tile, flo
     const int lane = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int H = a.H, I = a.I;
-    const uint32_t spr = (uint32_t)scales_per_row<FMT>(I);
-    const size_t mat_codes = (size_t)H * (I >> 1), mat_scales = (size_t)H * spr;
-    const GroupView<SC> gv = group_view(a.grp, gs, a.Gmax, a.P, a.T, a.codes, reinterpret_cast<const SC *>(a.scales),
-                                        mat_codes, mat_scales, a.s_codes, reinterpret_cast<const SC *>(a.s_scales));
+    const GroupView<SC> gv = group_view<SC>(a.grp, gs, a.Gmax, a.P, a.T, H, a.codes, a.scales, a.rl, a.s_codes,
+                                            a.s_scales, a.s_rl);
+    const uint32_t cs = gv.cs, ss = gv.ss;  // row strides (bytes)
     const bool sbf = SB && gv.e < 0;  // bf16 shared expert (MFMA branch at every size)
-    const Buf cb = make_buf(gv.codes, (uint32_t)(sbf ? 4 * mat_codes : mat_codes));
-    const Buf sb = make_buf(gv.scales, sbf ? 0u : (uint32_t)(mat_scales * sizeof(SC)));
+    const Buf cb = make_buf(gv.codes, (uint32_t)gv.mat_codes);
+    const Buf sb = make_buf(gv.scales, sbf ? 0u : (uint32_t)gv.mat_scales);
     float gsc = 1.f;  // NVFP4 global scale of the matrix
     if constexpr (FMT == FMT_NVFP4) gsc = sbf ? 1.f : gv.e < 0 ? ld_uniform(a.s_gs, 0) : ld_uniform(a.gs, gv.e);
     const int *plist = a.pairs + gv.off;
@@ -694,8 +699,8 @@ __device__ __forceinline__ void gw2_unit(const GW2Args &a, int gs, int tile, flo
                         for (int rt = 0; rt < 4; ++rt) {
                             const int rr = u0 + 16 * rt + r;
                             const bool rv = rr < H;
-                            cw[rt] = ld128(cb, rv ? (uint32_t)rr * (uint32_t)(I >> 1) + (uint32_t)(k0 >> 1) : OOB);
-                            sc[rt] = ld_scales<FMT>(sb, rv ? scale_off<FMT>((uint32_t)rr * spr, k0) : OOB);
+                            cw[rt] = ld128(cb, rv ? (uint32_t)rr * cs + (uint32_t)(k0 >> 1) : OOB);
+                            sc[rt] = ld_scales<FMT>(sb, rv ? (uint32_t)rr * ss + scale_col<FMT>(k0) : OOB);
                         }
                     }
                     uint4 bh[2][4], bl[2][4];
@@ -716,7 +721,7 @@ __device__ __forceinline__ void gw2_unit(const GW2Args &a, int gs, int tile, flo
                             const bool rv = rr < H;
 #pragma unroll
                             for (int s = 0; s < 4; ++s) {
-                                const uint32_t o = (uint32_t)rr * (uint32_t)I * 2u + (uint32_t)(k0 + 8 * s) * 2u;
+                                const uint32_t o = (uint32_t)rr * cs + (uint32_t)(k0 + 8 * s) * 2u;
                                 const bf16x8 w = __builtin_bit_cast(bf16x8, ld128(cb, rv ? o : OOB));
 #pragma unroll
                                 for (int nt = 0; nt < 2; ++nt) {
@@ -745,7 +750,7 @@ __device__ __forceinline__ void gw2_unit(const GW2Args &a, int gs, int tile, flo
 #pragma unroll
                             for (int j = 0; j < 4; ++j) {
                                 const uint32_t o = (uint32_t)(u0 + 16 * rt + 4 * q + j);
-                                so[j] = f16_bits_to_f32(ld16(sb, o < (uint32_t)H ? (o * spr + (uint32_t)c) * 2u : OOB));
+                                so[j] = f16_bits_to_f32(ld16(sb, o < (uint32_t)H ? o * ss + (uint32_t)c * 2u : OOB));
                             }
                             const uint32_t cws[4] = {cw[rt].x, cw[rt].y, cw[rt].z, cw[rt].w};
                             f32x4 t[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
@@ -862,8 +867,8 @@ __device__ __forceinline__ void gw2_unit(const GW2Args &a, int gs, int tile, flo
             const int k0 = 32 * (L * s + lk);
             const int rr = row0 + l * RG + rsub;
             const bool v = s < ks && k0 < I && rr < H && (l * RG + rsub) < 16;
-            cw[s][l] = ld128(cb, v ? (uint32_t)rr * (uint32_t)(I >> 1) + (uint32_t)(k0 >> 1) : OOB);
-            sc[s][l] = ld_scales<FMT>(sb, v ? scale_off<FMT>((uint32_t)rr * spr, k0) : OOB);
+            cw[s][l] = ld128(cb, v ? (uint32_t)rr * cs + (uint32_t)(k0 >> 1) : OOB);
+            sc[s][l] = ld_scales<FMT>(sb, v ? (uint32_t)rr * ss + scale_col<FMT>(k0) : OOB);
         }
     for (int idx = 0; idx < gv.m; ++idx) {
         if constexpr (FMT == FMT_INT4) {  // as in gw13_unit: the decode stays in the token loop
@@ -984,13 +989,12 @@ __device__ __forceinline__ void pf13_unit(const GW13Args &a, int gs, int rt, int
     const int tid = threadIdx.x, lane = tid & 63;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int H = a.H, I = a.I;
-    const uint32_t spr = (uint32_t)(H >> 4);
-    const size_t mat_codes = (size_t)(2 * I) * (H >> 1), mat_scales = (size_t)(2 * I) * spr;
-    const GroupView<SC> gv = group_view(a.grp, gs, a.Gmax, a.P, a.T, a.codes, reinterpret_cast<const SC *>(a.scales),
-                                        mat_codes, mat_scales, a.s_codes, reinterpret_cast<const SC *>(a.s_scales));
+    const GroupView<SC> gv = group_view<SC>(a.grp, gs, a.Gmax, a.P, a.T, 2 * I, a.codes, a.scales, a.rl, a.s_codes,
+                                            a.s_scales, a.s_rl);
+    const uint32_t cs = gv.cs, ss = gv.ss;  // row strides (bytes)
     const bool sbf = SB && gv.e < 0;
-    const Buf cb = make_buf(gv.codes, (uint32_t)(sbf ? 4 * mat_codes : mat_codes));
-    const Buf sb = make_buf(gv.scales, sbf ? 0u : (uint32_t)(mat_scales * sizeof(SC)));
+    const Buf cb = make_buf(gv.codes, (uint32_t)gv.mat_codes);
+    const Buf sb = make_buf(gv.scales, sbf ? 0u : (uint32_t)gv.mat_scales);
     float gsc = 1.f;  // NVFP4 global scale of the matrix
     if constexpr (FMT == FMT_NVFP4) gsc = sbf ? 1.f : gv.e < 0 ? ld_uniform(a.s_gs, 0) : ld_uniform(a.gs, gv.e);
     const Buf xall = make_buf(a.x, (uint32_t)a.T * (uint32_t)H * 2u);
@@ -1010,8 +1014,8 @@ __device__ __forceinline__ void pf13_unit(const GW13Args &a, int gs, int rt, int
     uint32_t sw[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-        cw[t] = ld128(cb, sbf ? OOB : rows[t] * (uint32_t)(H >> 1) + (uint32_t)(16 * q));
-        sw[t] = ld_scales<FMT>(sb, sbf ? OOB : scale_off<FMT>(rows[t] * spr, 32 * q));
+        cw[t] = ld128(cb, sbf ? OOB : rows[t] * cs + (uint32_t)(16 * q));
+        sw[t] = ld_scales<FMT>(sb, sbf ? OOB : rows[t] * ss + scale_col<FMT>(32 * q));
     }
     f32x4 acc[4][4];  // [gate 0, gate 1, up 0, up 1][column tile]
 #pragma unroll
@@ -1033,8 +1037,8 @@ __device__ __forceinline__ void pf13_unit(const GW13Args &a, int gs, int rt, int
             if (!sbf) {
 #pragma unroll
                 for (int t = 0; t < 4; ++t) {
-                    cw[t] = ld128(cb, rows[t] * (uint32_t)(H >> 1) + (kq >> 1));
-                    sw[t] = ld_scales<FMT>(sb, scale_off<FMT>(rows[t] * spr, (int)kq));
+                    cw[t] = ld128(cb, rows[t] * cs + (kq >> 1));
+                    sw[t] = ld_scales<FMT>(sb, rows[t] * ss + scale_col<FMT>((int)kq));
                 }
             }
         }
@@ -1049,7 +1053,7 @@ __device__ __forceinline__ void pf13_unit(const GW13Args &a, int gs, int rt, int
 #pragma unroll
                     for (int t = 0; t < 4; ++t) {
                         const bf16x8 w = __builtin_bit_cast(
-                            bf16x8, ld128(cb, rows[t] * (uint32_t)H * 2u + (kq + 8u * (uint32_t)s) * 2u));
+                            bf16x8, ld128(cb, rows[t] * cs + (kq + 8u * (uint32_t)s) * 2u));
 #pragma unroll
                         for (int nt = 0; nt < 4; ++nt) acc[t][nt] = mfma16x16x32(w, b[nt], acc[t][nt]);
                     }
@@ -1128,13 +1132,12 @@ __device__ __forceinline__ void pf2_unit(const GW2Args &a, int gs, int rt, int n
     const int tid = threadIdx.x, lane = tid & 63;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int H = a.H, I = a.I;
-    const uint32_t spr = (uint32_t)(I >> 4);
-    const size_t mat_codes = (size_t)H * (I >> 1), mat_scales = (size_t)H * spr;
-    const GroupView<SC> gv = group_view(a.grp, gs, a.Gmax, a.P, a.T, a.codes, reinterpret_cast<const SC *>(a.scales),
-                                        mat_codes, mat_scales, a.s_codes, reinterpret_cast<const SC *>(a.s_scales));
+    const GroupView<SC> gv = group_view<SC>(a.grp, gs, a.Gmax, a.P, a.T, H, a.codes, a.scales, a.rl, a.s_codes,
+                                            a.s_scales, a.s_rl);
+    const uint32_t cs = gv.cs, ss = gv.ss;  // row strides (bytes)
     const bool sbf = SB && gv.e < 0;
-    const Buf cb = make_buf(gv.codes, (uint32_t)(sbf ? 4 * mat_codes : mat_codes));
-    const Buf sb = make_buf(gv.scales, sbf ? 0u : (uint32_t)(mat_scales * sizeof(SC)));
+    const Buf cb = make_buf(gv.codes, (uint32_t)gv.mat_codes);
+    const Buf sb = make_buf(gv.scales, sbf ? 0u : (uint32_t)gv.mat_scales);
     float gsc = 1.f;  // NVFP4 global scale of the matrix
     if constexpr (FMT == FMT_NVFP4) gsc = sbf ? 1.f : gv.e < 0 ? ld_uniform(a.s_gs, 0) : ld_uniform(a.gs, gv.e);
     const uint32_t hbytes = (uint32_t)(a.P + a.T) * (uint32_t)I * 2u;
@@ -1154,8 +1157,8 @@ __device__ __forceinline__ void pf2_unit(const GW2Args &a, int gs, int rt, int n
     uint32_t sw[2];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-        cw[t] = ld128(cb, sbf ? OOB : rows[t] * (uint32_t)(I >> 1) + (uint32_t)(16 * q));
-        sw[t] = ld_scales<FMT>(sb, sbf ? OOB : scale_off<FMT>(rows[t] * spr, 32 * q));
+        cw[t] = ld128(cb, sbf ? OOB : rows[t] * cs + (uint32_t)(16 * q));
+        sw[t] = ld_scales<FMT>(sb, sbf ? OOB : rows[t] * ss + scale_col<FMT>(32 * q));
     }
     f32x4 acc[2][4], acc2[2][4];  // [row tile][column tile]; weight hi / lo terms
 #pragma unroll
@@ -1180,8 +1183,8 @@ __device__ __forceinline__ void pf2_unit(const GW2Args &a, int gs, int rt, int n
             if (!sbf) {
 #pragma unroll
                 for (int t = 0; t < 2; ++t) {
-                    cw[t] = ld128(cb, rows[t] * (uint32_t)(I >> 1) + (kq >> 1));
-                    sw[t] = ld_scales<FMT>(sb, scale_off<FMT>(rows[t] * spr, (int)kq));
+                    cw[t] = ld128(cb, rows[t] * cs + (kq >> 1));
+                    sw[t] = ld_scales<FMT>(sb, rows[t] * ss + scale_col<FMT>((int)kq));
                 }
             }
         }
@@ -1199,7 +1202,7 @@ __device__ __forceinline__ void pf2_unit(const GW2Args &a, int gs, int rt, int n
 #pragma unroll
                     for (int t = 0; t < 2; ++t) {
                         const bf16x8 w = __builtin_bit_cast(
-                            bf16x8, ld128(cb, rows[t] * (uint32_t)I * 2u + (kq + 8u * (uint32_t)s) * 2u));
+                            bf16x8, ld128(cb, rows[t] * cs + (kq + 8u * (uint32_t)s) * 2u));
 #pragma unroll
                         for (int nt = 0; nt < 4; ++nt) {
                             acc[t][nt] = mfma16x16x32(w, b0[nt], acc[t][nt]);
@@ -1322,12 +1325,11 @@ __device__ __forceinline__ void mx13_unit(const MX13Args &a, int gs, int tile, f
     const int lane = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int H = a.H, I = a.I;
-    const uint32_t spr = (uint32_t)(H >> 5);
-    const size_t mat_codes = (size_t)(2 * I) * (H >> 1), mat_scales = (size_t)(2 * I) * spr;
-    const GroupView<uint8_t> gv = group_view(a.grp, gs, a.Gmax, a.P, a.T, a.codes, a.scales, mat_codes, mat_scales, a.s_codes,
-                              a.s_scales);
-    const Buf cb = make_buf(gv.codes, (uint32_t)mat_codes);
-    const Buf sb = make_buf(gv.scales, (uint32_t)mat_scales);
+    const GroupView<uint8_t> gv = group_view<uint8_t>(a.grp, gs, a.Gmax, a.P, a.T, 2 * I, a.codes, a.scales, a.rl,
+                                                      a.s_codes, a.s_scales, a.s_rl);
+    const uint32_t cs = gv.cs, ss = gv.ss;  // row strides (bytes)
+    const Buf cb = make_buf(gv.codes, (uint32_t)gv.mat_codes);
+    const Buf sb = make_buf(gv.scales, (uint32_t)gv.mat_scales);
     const Buf xqb = make_buf(a.xq, (uint32_t)a.T * (uint32_t)H);
     const Buf xsb = make_buf(a.xs, (uint32_t)a.T * (uint32_t)(H >> 5));
     const int *plist = a.pairs + gv.off;
@@ -1356,8 +1358,8 @@ __device__ __forceinline__ void mx13_unit(const MX13Args &a, int gs, int tile, f
             uint32_t as[4];
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
-                av[t] = ld128(cb, rows[t] * (uint32_t)(H >> 1) + (uint32_t)((k0 + 32 * g) >> 1));
-                as[t] = ld8(sb, rows[t] * spr + (uint32_t)(k0 >> 5) + (uint32_t)g);
+                av[t] = ld128(cb, rows[t] * cs + (uint32_t)((k0 + 32 * g) >> 1));
+                as[t] = ld8(sb, rows[t] * ss + (uint32_t)(k0 >> 5) + (uint32_t)g);
             }
             uint4 blo[2], bhi[2];
             uint32_t bs[2];
@@ -1442,12 +1444,11 @@ __device__ __forceinline__ void mx2_unit(const MX2Args &a, int gs, int tile, flo
     const int lane = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int H = a.H, I = a.I;
-    const uint32_t spr = (uint32_t)(I >> 5);
-    const size_t mat_codes = (size_t)H * (I >> 1), mat_scales = (size_t)H * spr;
-    const GroupView<uint8_t> gv = group_view(a.grp, gs, a.Gmax, a.P, a.T, a.codes, a.scales, mat_codes, mat_scales, a.s_codes,
-                              a.s_scales);
-    const Buf cb = make_buf(gv.codes, (uint32_t)mat_codes);
-    const Buf sb = make_buf(gv.scales, (uint32_t)mat_scales);
+    const GroupView<uint8_t> gv = group_view<uint8_t>(a.grp, gs, a.Gmax, a.P, a.T, H, a.codes, a.scales, a.rl,
+                                                      a.s_codes, a.s_scales, a.s_rl);
+    const uint32_t cs = gv.cs, ss = gv.ss;  // row strides (bytes)
+    const Buf cb = make_buf(gv.codes, (uint32_t)gv.mat_codes);
+    const Buf sb = make_buf(gv.scales, (uint32_t)gv.mat_scales);
     const uint32_t rowsall = (uint32_t)(a.P + a.T);
     const Buf hqb = make_buf(a.hq, rowsall * (uint32_t)I);
     const Buf hsb = make_buf(a.hs, rowsall * (uint32_t)(I >> 5));
@@ -1476,8 +1477,8 @@ __device__ __forceinline__ void mx2_unit(const MX2Args &a, int gs, int tile, flo
             for (int t = 0; t < 4; ++t) {
                 const uint32_t row = (uint32_t)(u0 + 16 * t + r);
                 const bool rv = (int)row < H;
-                av[t] = ld128(cb, rv ? row * (uint32_t)(I >> 1) + (uint32_t)((k0 + 32 * g) >> 1) : OOB);
-                as[t] = ld8(sb, rv ? row * spr + (uint32_t)(k0 >> 5) + (uint32_t)g : OOB);
+                av[t] = ld128(cb, rv ? row * cs + (uint32_t)((k0 + 32 * g) >> 1) : OOB);
+                as[t] = ld8(sb, rv ? row * ss + (uint32_t)(k0 >> 5) + (uint32_t)g : OOB);
             }
             uint4 blo[2], bhi[2];
             uint32_t bs[2];
@@ -1561,12 +1562,11 @@ __device__ __forceinline__ void pfmx13_unit(const MX13Args &a, int gs, int rt, i
     const int tid = threadIdx.x, lane = tid & 63;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int H = a.H, I = a.I;
-    const uint32_t spr = (uint32_t)(H >> 5);
-    const size_t mat_codes = (size_t)(2 * I) * (H >> 1), mat_scales = (size_t)(2 * I) * spr;
-    const GroupView<uint8_t> gv = group_view(a.grp, gs, a.Gmax, a.P, a.T, a.codes, a.scales, mat_codes, mat_scales,
-                                             a.s_codes, a.s_scales);
-    const Buf cb = make_buf(gv.codes, (uint32_t)mat_codes);
-    const Buf sb = make_buf(gv.scales, (uint32_t)mat_scales);
+    const GroupView<uint8_t> gv = group_view<uint8_t>(a.grp, gs, a.Gmax, a.P, a.T, 2 * I, a.codes, a.scales, a.rl,
+                                                      a.s_codes, a.s_scales, a.s_rl);
+    const uint32_t cs = gv.cs, ss = gv.ss;  // row strides (bytes)
+    const Buf cb = make_buf(gv.codes, (uint32_t)gv.mat_codes);
+    const Buf sb = make_buf(gv.scales, (uint32_t)gv.mat_scales);
     const Buf xqb = make_buf(a.xq, (uint32_t)a.T * (uint32_t)H);
     const Buf xsb = make_buf(a.xs, (uint32_t)a.T * (uint32_t)(H >> 5));
     const int *plist = a.pairs + gv.off;
@@ -1588,8 +1588,8 @@ __device__ __forceinline__ void pfmx13_unit(const MX13Args &a, int gs, int rt, i
     uint32_t sw[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-        cw[t] = ld128(cb, rows[t] * (uint32_t)(H >> 1) + (uint32_t)(16 * g));
-        sw[t] = ld8(sb, rows[t] * spr + (uint32_t)g);
+        cw[t] = ld128(cb, rows[t] * cs + (uint32_t)(16 * g));
+        sw[t] = ld8(sb, rows[t] * ss + (uint32_t)g);
     }
     f32x4 acc[4][4];  // [gate 0, gate 1, up 0, up 1][column tile]
 #pragma unroll
@@ -1613,8 +1613,8 @@ __device__ __forceinline__ void pfmx13_unit(const MX13Args &a, int gs, int rt, i
             sr = ld8(xsb, lv ? so + (kn >> 5) : OOB);
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
-                cw[t] = ld128(cb, rows[t] * (uint32_t)(H >> 1) + ((kn + 32u * (uint32_t)g) >> 1));
-                sw[t] = ld8(sb, rows[t] * spr + (kn >> 5) + (uint32_t)g);
+                cw[t] = ld128(cb, rows[t] * cs + ((kn + 32u * (uint32_t)g) >> 1));
+                sw[t] = ld8(sb, rows[t] * ss + (kn >> 5) + (uint32_t)g);
             }
         }
         uint4 blo[4], bhi[4];
@@ -1677,12 +1677,11 @@ __device__ __forceinline__ void pfmx2_unit(const MX2Args &a, int gs, int rt, int
     const int tid = threadIdx.x, lane = tid & 63;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int H = a.H, I = a.I;
-    const uint32_t spr = (uint32_t)(I >> 5);
-    const size_t mat_codes = (size_t)H * (I >> 1), mat_scales = (size_t)H * spr;
-    const GroupView<uint8_t> gv = group_view(a.grp, gs, a.Gmax, a.P, a.T, a.codes, a.scales, mat_codes, mat_scales,
-                                             a.s_codes, a.s_scales);
-    const Buf cb = make_buf(gv.codes, (uint32_t)mat_codes);
-    const Buf sb = make_buf(gv.scales, (uint32_t)mat_scales);
+    const GroupView<uint8_t> gv = group_view<uint8_t>(a.grp, gs, a.Gmax, a.P, a.T, H, a.codes, a.scales, a.rl,
+                                                      a.s_codes, a.s_scales, a.s_rl);
+    const uint32_t cs = gv.cs, ss = gv.ss;  // row strides (bytes)
+    const Buf cb = make_buf(gv.codes, (uint32_t)gv.mat_codes);
+    const Buf sb = make_buf(gv.scales, (uint32_t)gv.mat_scales);
     const uint32_t rowsall = (uint32_t)(a.P + a.T);
     const Buf hqb = make_buf(a.hq, rowsall * (uint32_t)I);
     const Buf hsb = make_buf(a.hs, rowsall * (uint32_t)(I >> 5));
@@ -1704,8 +1703,8 @@ __device__ __forceinline__ void pfmx2_unit(const MX2Args &a, int gs, int rt, int
     uint32_t sw[2];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-        cw[t] = ld128(cb, rows[t] * (uint32_t)(I >> 1) + (uint32_t)(16 * g));
-        sw[t] = ld8(sb, rows[t] * spr + (uint32_t)g);
+        cw[t] = ld128(cb, rows[t] * cs + (uint32_t)(16 * g));
+        sw[t] = ld8(sb, rows[t] * ss + (uint32_t)g);
     }
     f32x4 acc[2][4];
 #pragma unroll
@@ -1729,8 +1728,8 @@ __device__ __forceinline__ void pfmx2_unit(const MX2Args &a, int gs, int rt, int
             sr = ld8(hsb, lv ? so + (kn >> 5) : OOB);
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
-                cw[t] = ld128(cb, rows[t] * (uint32_t)(I >> 1) + ((kn + 32u * (uint32_t)g) >> 1));
-                sw[t] = ld8(sb, rows[t] * spr + (kn >> 5) + (uint32_t)g);
+                cw[t] = ld128(cb, rows[t] * cs + ((kn + 32u * (uint32_t)g) >> 1));
+                sw[t] = ld8(sb, rows[t] * ss + (kn >> 5) + (uint32_t)g);
             }
         }
         uint4 blo[4], bhi[4];
@@ -1781,19 +1780,19 @@ __global__ __launch_bounds__(256) void k_moe_pfmx2(MX2Args a) {
 // accumulation chain of the MX expert kernels, on plain matrices.
 __global__ __launch_bounds__(64) void k_mx_dot(const uint8_t *__restrict__ ac, const uint8_t *__restrict__ as,
                                                const uint8_t *__restrict__ bc, const uint8_t *__restrict__ bs,
-                                               float *__restrict__ out, int n, int m, int k) {
+                                               float *__restrict__ out, int n, int m, int k, RowLayout arl) {
     const int lane = threadIdx.x & 63;
     const int r = lane & 15, g = lane >> 4;
     const int row0 = (int)blockIdx.y * 16, col0 = (int)blockIdx.x * 16;
-    const Buf ab = make_buf(ac, (uint32_t)n * (uint32_t)(k >> 1));
-    const Buf asb = make_buf(as, (uint32_t)n * (uint32_t)(k >> 5));
+    const Buf ab = make_buf(ac, (uint32_t)n * arl.cs);
+    const Buf asb = make_buf(as, (uint32_t)n * arl.ss);
     const Buf bb = make_buf(bc, (uint32_t)m * (uint32_t)k);
     const Buf bsb = make_buf(bs, (uint32_t)m * (uint32_t)(k >> 5));
     const uint32_t row = (uint32_t)(row0 + r), col = (uint32_t)(col0 + r);
     f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
     for (int k0 = 0; k0 < k; k0 += 128) {
-        const uint4 av = ld128(ab, row * (uint32_t)(k >> 1) + (uint32_t)((k0 + 32 * g) >> 1));
-        const uint32_t sa = ld8(asb, row * (uint32_t)(k >> 5) + (uint32_t)(k0 >> 5) + (uint32_t)g);
+        const uint4 av = ld128(ab, row * arl.cs + (uint32_t)((k0 + 32 * g) >> 1));
+        const uint32_t sa = ld8(asb, row * arl.ss + (uint32_t)(k0 >> 5) + (uint32_t)g);
         const uint32_t xo = col * (uint32_t)k + (uint32_t)(k0 + 16 * g);
         const uint4 blo = ld128(bb, xo), bhi = ld128(bb, xo + 64u);
         const uint32_t sb = ld8(bsb, col * (uint32_t)(k >> 5) + (uint32_t)(k0 >> 5) + (uint32_t)g);
@@ -1994,10 +1993,10 @@ void launch_mx2(MX2Args &a, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
     go_ev(st, e0, e1, k_moe_mx2, dim3(grouped_grid(a.Gmax, a.tiles)), dim3(256), 0, a);
 }
 
-void launch_mx_dot(const uint8_t *ac, const uint8_t *as, const uint8_t *bc, const uint8_t *bs, float *out, int n,
-                   int m, int k, hipStream_t st) {
+void launch_mx_dot(const uint8_t *ac, const uint8_t *as, RowLayout arl, const uint8_t *bc, const uint8_t *bs,
+                   float *out, int n, int m, int k, hipStream_t st) {
     hipLaunchKernelGGL(k_mx_dot, dim3((unsigned)(m / 16), (unsigned)(n / 16)), dim3(64), 0, st, ac, as, bc, bs, out,
-                       n, m, k);
+                       n, m, k, arl);
 }
 
 void launch_gcombine(GCombineArgs &a, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {

@@ -42,8 +42,10 @@ int group_of(int32_t format) {
 int check_shape(int32_t format, int32_t layout, int64_t groups, int64_t n, int64_t k) {
     const int g = group_of(format);
     if (!g) return fail(W4_ERR_LAYOUT, "unknown format tag %d", (int)format);
-    if (layout != W4_LAYOUT_CANONICAL && layout != W4_LAYOUT_GFX950_V1)
+    if (layout != W4_LAYOUT_CANONICAL && layout != W4_LAYOUT_GFX950_V1 && layout != W4_LAYOUT_GFX950_KT16)
         return fail(W4_ERR_LAYOUT, "unknown layout tag %d", (int)layout);
+    if (layout == W4_LAYOUT_GFX950_KT16 && format != W4_FMT_E2M1_F16S16 && format != W4_FMT_NVFP4_E4M3S16)
+        return fail(W4_ERR_UNSUPPORTED, "the K-tiled layout holds E2M1 or NVFP4 matrices (one scale per 16-wide tile)");
     if (groups < 1 || n < 1 || k < 1) return fail(W4_ERR_INVALID_ARG, "groups/n/k must be >= 1");
     const int64_t kmul = format == W4_FMT_INT4_F16S128 ? 128 : 32;
     if (k % kmul) return fail(W4_ERR_INVALID_ARG, "k=%lld must be a multiple of %lld", (long long)k, (long long)kmul);
@@ -63,6 +65,11 @@ size_t code_bytes_per_row(int32_t format, int64_t k) { return format == W4_FMT_B
 size_t v1_row_bytes(int32_t format, int64_t k) {
     const size_t b = code_bytes_per_row(format, k) + scale_bytes_per_row(format, k);
     return (b + 15) / 16 * 16;
+}
+
+size_t kt16_tile_bytes(int32_t format, int64_t n) {
+    const size_t sb = format == W4_FMT_NVFP4_E4M3S16 ? 1 : 2;
+    return ((size_t)n * (8 + sb) + 15) / 16 * 16;
 }
 
 // ---------------------------------------------------------------- fp16 / E2M1
@@ -205,12 +212,13 @@ size_t w4_codes_bytes(int32_t format, int32_t layout, int64_t groups, int64_t n,
     if (check_shape(format, layout, groups, n, k) != W4_OK) return 0;
     const size_t rows = (size_t)groups * (size_t)n;
     if (layout == W4_LAYOUT_GFX950_V1) return rows * v1_row_bytes(format, k);
+    if (layout == W4_LAYOUT_GFX950_KT16) return (size_t)groups * (size_t)(k / 16) * kt16_tile_bytes(format, n);
     return rows * code_bytes_per_row(format, k);
 }
 
 size_t w4_scales_bytes(int32_t format, int32_t layout, int64_t groups, int64_t n, int64_t k) {
     if (check_shape(format, layout, groups, n, k) != W4_OK) return 0;
-    if (layout == W4_LAYOUT_GFX950_V1) return 0;  // the scales travel inside each row record
+    if (layout != W4_LAYOUT_CANONICAL) return 0;  // the scales travel inside the row or tile records
     return (size_t)groups * (size_t)n * scale_bytes_per_row(format, k);
 }
 
@@ -296,9 +304,11 @@ int w4_unpack_nibbles(const uint8_t *packed, int64_t n, int64_t k, uint8_t *nibb
     return W4_OK;
 }
 
-// Canonical <-> device layout.  GFX950_V1 stores each row as one record: the
+// Canonical <-> device layouts.  GFX950_V1 stores each row as one record: the
 // row's codes (canonical nibble order) followed by its block scales, padded
-// with zero bytes to a multiple of 16.  Both directions move bytes only, so
+// with zero bytes to a multiple of 16.  GFX950_KT16 stores each 16-wide K tile
+// of a matrix as one record: every row's 8 code bytes of the tile, then every
+// row's scale of the tile, padded to 16.  Both directions move bytes only, so
 // they are exact inverses for any input (padding excepted).
 static int pack_args(int32_t format, int64_t groups, int64_t n, int64_t k, int32_t layout, const void *a,
                      const void *b, const void *c) {
@@ -322,8 +332,22 @@ int w4_pack(int32_t format, int64_t groups, int64_t n, int64_t k, const uint8_t 
         if (sb) std::memmove(scales_out, scales, rows * sb);
         return W4_OK;
     }
-    const size_t rs = v1_row_bytes(format, k);
     const uint8_t *sc = static_cast<const uint8_t *>(scales);
+    if (dst_layout == W4_LAYOUT_GFX950_KT16) {
+        const size_t ts = kt16_tile_bytes(format, n), ssz = sb / (size_t)(k / 16), nt = (size_t)(k / 16);
+        for (size_t g = 0; g < (size_t)groups; ++g)
+            for (size_t t = 0; t < nt; ++t) {
+                uint8_t *dst = codes_out + (g * nt + t) * ts;
+                for (size_t r = 0; r < (size_t)n; ++r) {
+                    const size_t row = g * (size_t)n + r;
+                    std::memcpy(dst + r * 8, codes + row * cb + t * 8, 8);
+                    std::memcpy(dst + (size_t)n * 8 + r * ssz, sc + row * sb + t * ssz, ssz);
+                }
+                std::memset(dst + (size_t)n * (8 + ssz), 0, ts - (size_t)n * (8 + ssz));
+            }
+        return W4_OK;
+    }
+    const size_t rs = v1_row_bytes(format, k);
     for (size_t r = 0; r < rows; ++r) {
         uint8_t *dst = codes_out + r * rs;
         std::memcpy(dst, codes + r * cb, cb);
@@ -348,8 +372,21 @@ int w4_unpack(int32_t format, int64_t groups, int64_t n, int64_t k, int32_t src_
         if (sb) std::memmove(scales, scales_in, rows * sb);
         return W4_OK;
     }
-    const size_t rs = v1_row_bytes(format, k);
     uint8_t *sc = static_cast<uint8_t *>(scales);
+    if (src_layout == W4_LAYOUT_GFX950_KT16) {
+        const size_t ts = kt16_tile_bytes(format, n), ssz = sb / (size_t)(k / 16), nt = (size_t)(k / 16);
+        for (size_t g = 0; g < (size_t)groups; ++g)
+            for (size_t t = 0; t < nt; ++t) {
+                const uint8_t *src = codes_in + (g * nt + t) * ts;
+                for (size_t r = 0; r < (size_t)n; ++r) {
+                    const size_t row = g * (size_t)n + r;
+                    std::memcpy(codes + row * cb + t * 8, src + r * 8, 8);
+                    std::memcpy(sc + row * sb + t * ssz, src + (size_t)n * 8 + r * ssz, ssz);
+                }
+            }
+        return W4_OK;
+    }
+    const size_t rs = v1_row_bytes(format, k);
     for (size_t r = 0; r < rows; ++r) {
         const uint8_t *src = codes_in + r * rs;
         std::memcpy(codes + r * cb, src, cb);

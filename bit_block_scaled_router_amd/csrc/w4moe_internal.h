@@ -19,6 +19,8 @@ int group_of(int32_t format);
 size_t code_bytes_per_row(int32_t format, int64_t k);
 size_t scale_bytes_per_row(int32_t format, int64_t k);
 size_t v1_row_bytes(int32_t format, int64_t k);
+// GFX950_KT16 tile record of an n-row matrix: n x 8 code bytes, n scales, padded to 16.
+size_t kt16_tile_bytes(int32_t format, int64_t n);
 
 // Validate format/layout tags and dimensions of a matrix stack.
 int check_shape(int32_t format, int32_t layout, int64_t groups, int64_t n, int64_t k);

@@ -19,6 +19,7 @@
 // grouped packed tensor with top-k ids), P29 (down weighted sum), P45 (one-call
 // shape), P46/P48 (atomics drift; row-owning down kernel), P55 (gate and up rows
 // processed together); "Lynn Engine" article stage P1 (packed matvec).
+#include "w4moe_decode.h"
 #include "w4moe_device.h"
 #include "w4moe_grouped.h"
 #include "w4moe_internal.h"
@@ -39,7 +40,8 @@ namespace w4k {
 template <int FMT, int L, int RT>
 __global__ __launch_bounds__(256) void k_gemv(const uint8_t *__restrict__ codes, const uint8_t *__restrict__ scales,
                                               const float *__restrict__ gsc, const uint16_t *__restrict__ x,
-                                              uint16_t *__restrict__ y, int n, int k, int m) {
+                                              uint16_t *__restrict__ y, int n, int k, int m, uint32_t cs,
+                                              uint32_t ss) {
     constexpr int RG = 64 / L;
     const int lane = threadIdx.x & 63;
     const int wave = wave_id();
@@ -47,9 +49,8 @@ __global__ __launch_bounds__(256) void k_gemv(const uint8_t *__restrict__ codes,
     const int row0 = wave * RT * RG;
     if (row0 >= n) return;  // uniform per wave
     const int ks = (k + 32 * L - 1) / (32 * L);
-    const uint32_t spr = (uint32_t)scales_per_row<FMT>(k);
-    const Buf cb = make_buf(codes, (uint32_t)n * (uint32_t)(k >> 1));
-    const Buf sb = make_buf(scales, (uint32_t)n * spr * scale_bytes<FMT>());
+    const Buf cb = make_buf(codes, (uint32_t)n * cs);
+    const Buf sb = make_buf(scales, (uint32_t)n * ss);
     const Buf xb = make_buf(x, (uint32_t)m * (uint32_t)k * 2u);
     float g = 1.f;
     if constexpr (FMT == FMT_NVFP4) g = ld_uniform(gsc, 0);
@@ -68,8 +69,8 @@ __global__ __launch_bounds__(256) void k_gemv(const uint8_t *__restrict__ codes,
             for (int r = 0; r < RT; ++r) {
                 const int row = row0 + r * RG + rsub;
                 const bool v = kv && row < n;
-                cw[r] = ld128(cb, v ? (uint32_t)row * (uint32_t)(k >> 1) + (uint32_t)(k0 >> 1) : OOB);
-                sw[r] = ld_scales<FMT>(sb, v ? scale_off<FMT>((uint32_t)row * spr, k0) : OOB);
+                cw[r] = ld128(cb, v ? (uint32_t)row * cs + (uint32_t)(k0 >> 1) : OOB);
+                sw[r] = ld_scales<FMT>(sb, v ? (uint32_t)row * ss + scale_col<FMT>(k0) : OOB);
             }
             prep_xslice<FMT>(xs);
 #pragma unroll
@@ -92,7 +93,7 @@ __global__ __launch_bounds__(256) void k_gemv(const uint8_t *__restrict__ codes,
 template <int FMT, int L>
 __global__ __launch_bounds__(256) void k_dequant(const uint8_t *__restrict__ codes, const uint8_t *__restrict__ scales,
                                                  const float *__restrict__ gsc, float *__restrict__ out, int64_t rows,
-                                                 int64_t n, int k) {
+                                                 int64_t n, int k, uint32_t cs, uint32_t ss) {
     constexpr int RG = 64 / L;
     const int lane = threadIdx.x & 63;
     const int64_t wave = wave_id();
@@ -101,16 +102,15 @@ __global__ __launch_bounds__(256) void k_dequant(const uint8_t *__restrict__ cod
     if (row0 >= rows) return;
     const int64_t row = row0 + lane / L;
     const bool rv = row < rows;
-    const uint32_t spr = (uint32_t)scales_per_row<FMT>(k);
     const int64_t nrows = rows - row0 < RG ? rows - row0 : RG;
-    const Buf cb = make_buf(codes + row0 * (k >> 1), (uint32_t)(nrows * (k >> 1)));
-    const Buf sb = make_buf(scales + row0 * spr * scale_bytes<FMT>(), (uint32_t)(nrows * spr * scale_bytes<FMT>()));
+    const Buf cb = make_buf(codes + row0 * cs, (uint32_t)(nrows * cs));
+    const Buf sb = make_buf(scales + row0 * ss, (uint32_t)(nrows * ss));
     const uint32_t rl = (uint32_t)(lane / L);
     float g = 1.f;
     if constexpr (FMT == FMT_NVFP4) g = rv ? gsc[row / n] : 0.f;
     for (int k0 = 32 * lk; k0 < k; k0 += 32 * L) {
-        const uint4 c = ld128(cb, rv ? rl * (uint32_t)(k >> 1) + (uint32_t)(k0 >> 1) : OOB);
-        const uint32_t sc = ld_scales<FMT>(sb, rv ? scale_off<FMT>(rl * spr, k0) : OOB);
+        const uint4 c = ld128(cb, rv ? rl * cs + (uint32_t)(k0 >> 1) : OOB);
+        const uint32_t sc = ld_scales<FMT>(sb, rv ? rl * ss + scale_col<FMT>(k0) : OOB);
         const uint32_t cw[4] = {c.x, c.y, c.z, c.w};
         float v[32];
         if constexpr (FMT != FMT_INT4) {
@@ -332,6 +332,7 @@ struct W13Args {
     // offsets the prologue's first loads were tuned for, ~0.25 us per step)
     int s_bf16;                   // shared expert in bf16 (s_codes = bf16 [2I][H])
     const float *gs, *s_gs;       // NVFP4 global scales: routed [E], shared [1]
+    RowLayout rl, s_rl;           // row strides of the routed and shared matrices
 };
 
 // h index of intermediate element i in the down kernel's lane order: lane lk of
@@ -369,9 +370,10 @@ __global__ __launch_bounds__(1024) void k_moe_w13(W13Args a) {
     const int lk = lane % L, rsub = lane / L;
     const int H = a.H, I = a.I;
     const int ks = (H + 32 * L - 1) / (32 * L);
-    const uint32_t spr = (uint32_t)scales_per_row<FMT>(H);
-    const uint32_t mat_codes = (uint32_t)(2 * I) * (uint32_t)(H >> 1);
-    const uint32_t mat_scales = (uint32_t)(2 * I) * spr * scale_bytes<FMT>();
+    // row strides of this slot's matrix (the shared expert may use another layout)
+    const uint32_t cs = j == a.K ? a.s_rl.cs : a.rl.cs, ss = j == a.K ? a.s_rl.ss : a.rl.ss;
+    const uint32_t mat_codes = (uint32_t)(2 * I) * cs;
+    const uint32_t mat_scales = (uint32_t)(2 * I) * ss;
     const Buf xb = make_buf(a.x + (size_t)t * H, (uint32_t)H * 2u);
     XSlice<FMT> xs0;  // step-0 activations, in flight while the experts are ranked
     load_xslice<FMT>(xs0, xb, 32 * lk < H ? (uint32_t)(32 * lk) * 2u : OOB);
@@ -430,7 +432,7 @@ __global__ __launch_bounds__(1024) void k_moe_w13(W13Args a) {
     for (int r = 0; r < RT; ++r) ag[r] = au[r] = 0.f;
     const bool sbf = SBF && j == a.K;  // bf16 shared expert slot (uniform per block)
     if (sbf) {
-        const uint32_t rowb = (uint32_t)H * 2u;
+        const uint32_t rowb = cs;
         const Buf wb = make_buf(cbase, (uint32_t)(2 * I) * rowb);
         for (int s = 0; s < ks; ++s) {
             const int k0 = 32 * (L * s + lk);
@@ -469,10 +471,10 @@ __global__ __launch_bounds__(1024) void k_moe_w13(W13Args a) {
             const int i = i0 + r * RG + rsub;
             const bool v = kv && i < I;
             const uint32_t rg = (uint32_t)i, ru = (uint32_t)(I + i);
-            cg[r] = ld128(cb, v ? rg * (uint32_t)(H >> 1) + (uint32_t)(k0 >> 1) : OOB);
-            cu[r] = ld128(cb, v ? ru * (uint32_t)(H >> 1) + (uint32_t)(k0 >> 1) : OOB);
-            sg[r] = ld_scales<FMT>(sb, v ? scale_off<FMT>(rg * spr, k0) : OOB);
-            su[r] = ld_scales<FMT>(sb, v ? scale_off<FMT>(ru * spr, k0) : OOB);
+            cg[r] = ld128(cb, v ? rg * cs + (uint32_t)(k0 >> 1) : OOB);
+            cu[r] = ld128(cb, v ? ru * cs + (uint32_t)(k0 >> 1) : OOB);
+            sg[r] = ld_scales<FMT>(sb, v ? rg * ss + scale_col<FMT>(k0) : OOB);
+            su[r] = ld_scales<FMT>(sb, v ? ru * ss + scale_col<FMT>(k0) : OOB);
         }
         prep_xslice<FMT>(xs);
 #pragma unroll
@@ -512,6 +514,7 @@ struct DownArgs {
     int H, I, E, K, S, T, lstride, hstride, blocks_per_tok;
     int s_bf16;                   // shared expert in bf16 (s_codes = bf16 [H][I])
     const float *gs, *s_gs;       // NVFP4 global scales: routed [E], shared [1]
+    RowLayout rl, s_rl;           // row strides of the routed and shared matrices
 };
 
 // Block = W waves; tile of RT*64/L output rows of one token.  LDS holds one
@@ -529,9 +532,6 @@ __global__ __launch_bounds__(1024) void k_moe_down(DownArgs a) {
     const int lk = lane % L, rsub = lane / L;
     const int I = a.I, H = a.H;
     const int ks = (I + 32 * L - 1) / (32 * L);
-    const uint32_t spr = (uint32_t)scales_per_row<FMT>(I);
-    const uint32_t mat_codes = (uint32_t)H * (uint32_t)(I >> 1);
-    const uint32_t mat_scales = (uint32_t)H * spr * scale_bytes<FMT>();
 
     for (int j = wv; j < a.S; j += nw) {
         // step-0 activations first: they do not depend on the routing
@@ -548,6 +548,9 @@ __global__ __launch_bounds__(1024) void k_moe_down(DownArgs a) {
         const float *gp;
         float coef;
         bool valid = true;
+        // row strides of this slot's matrix (the shared expert may use another layout)
+        const uint32_t cs = j == a.K ? a.s_rl.cs : a.rl.cs, ss = j == a.K ? a.s_rl.ss : a.rl.ss;
+        const uint32_t mat_codes = (uint32_t)H * cs, mat_scales = (uint32_t)H * ss;
         if (j == a.K) {
             cbase = a.s_codes;
             sbase = a.s_scales;
@@ -566,7 +569,7 @@ __global__ __launch_bounds__(1024) void k_moe_down(DownArgs a) {
         if constexpr (FMT == FMT_NVFP4) {
             if (!sbf) coef *= ld_uniform(gp, 0);  // (w x g) x row sum
         }
-        const Buf cb = make_buf(cbase, valid ? (sbf ? (uint32_t)H * (uint32_t)I * 2u : mat_codes) : 0u);
+        const Buf cb = make_buf(cbase, valid ? mat_codes : 0u);
         const Buf sb = make_buf(sbase, valid ? mat_scales : 0u);
         float acc[RT];
 #pragma unroll
@@ -592,7 +595,7 @@ __global__ __launch_bounds__(1024) void k_moe_down(DownArgs a) {
                     uint4 w[4];
 #pragma unroll
                     for (int q = 0; q < 4; ++q)
-                        w[q] = ld128(cb, v ? (uint32_t)row * (uint32_t)I * 2u + (uint32_t)k0 * 2u + 16u * q : OOB);
+                        w[q] = ld128(cb, v ? (uint32_t)row * cs + (uint32_t)k0 * 2u + 16u * q : OOB);
                     acc[r] = bf16w_dot_f32(w, hv, acc[r]);
                 }
             }
@@ -616,8 +619,8 @@ __global__ __launch_bounds__(1024) void k_moe_down(DownArgs a) {
             for (int r = 0; r < RT; ++r) {
                 const int row = row0 + r * RG + rsub;
                 const bool v = kv && row < H;
-                cw[r] = ld128(cb, v ? (uint32_t)row * (uint32_t)(I >> 1) + (uint32_t)(k0 >> 1) : OOB);
-                sw[r] = ld_scales<FMT>(sb, v ? scale_off<FMT>((uint32_t)row * spr, k0) : OOB);
+                cw[r] = ld128(cb, v ? (uint32_t)row * cs + (uint32_t)(k0 >> 1) : OOB);
+                sw[r] = ld_scales<FMT>(sb, v ? (uint32_t)row * ss + scale_col<FMT>(k0) : OOB);
             }
             float hs = 0.f;
             int hx = 0;
@@ -686,13 +689,15 @@ int lanes_for(int64_t k) {
 
 bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
-int check_matrix(const w4_matrix *W, const char *what) {
+// kt16: the caller reads K-tiled matrices (the decode down projection); every
+// other use of a matrix dots whole rows and needs a row layout.
+int check_matrix(const w4_matrix *W, const char *what, bool kt16 = false) {
     if (!W) return fail(W4_ERR_INVALID_ARG, "%s: null matrix", what);
     int st = w4::check_shape(W->format, W->layout, W->groups, W->n, W->k);
     if (st) return st;
-    if (W->layout != W4_LAYOUT_CANONICAL && W->format != W4_FMT_BF16)
-        return fail(W4_ERR_UNSUPPORTED, "%s: the device kernels read the canonical layout", what);
-    if (!W->codes || (!W->scales && W->format != W4_FMT_BF16))
+    if (W->layout == W4_LAYOUT_GFX950_KT16 && !kt16)
+        return fail(W4_ERR_UNSUPPORTED, "%s: the K-tiled layout serves only an MoE layer's down projection", what);
+    if (!W->codes || (!W->scales && W->format != W4_FMT_BF16 && W->layout == W4_LAYOUT_CANONICAL))
         return fail(W4_ERR_INVALID_ARG, "%s: null codes/scales", what);
     if (!aligned(W->codes, 16)) return fail(W4_ERR_ALIGNMENT, "%s: codes not 16-byte aligned", what);
     if (!aligned(W->scales, 4)) return fail(W4_ERR_ALIGNMENT, "%s: scales not 4-byte aligned", what);
@@ -702,9 +707,24 @@ int check_matrix(const w4_matrix *W, const char *what) {
     }
     if (W->n > (1 << 30) || W->k > (1 << 20)) return fail(W4_ERR_UNSUPPORTED, "%s: dimension too large", what);
     // one matrix of the stack is addressed through 32-bit buffer offsets
-    if ((uint64_t)W->n * (uint64_t)W->k * (W->format == W4_FMT_BF16 ? 2 : 1) / 2 >= (1ull << 31))
-        return fail(W4_ERR_UNSUPPORTED, "%s: one matrix must hold fewer than 2^31 code bytes", what);
+    if ((uint64_t)W->n * (uint64_t)w4::v1_row_bytes(W->format, W->k) >= (1ull << 31))
+        return fail(W4_ERR_UNSUPPORTED, "%s: one matrix must hold fewer than 2^31 bytes", what);
     return W4_OK;
+}
+
+// Row strides of a matrix in its layout, and the base of its block scales (the
+// device layout keeps them inside each row record, after the codes).
+RowLayout row_layout(const w4_matrix *W) {
+    if (W->layout == W4_LAYOUT_GFX950_V1) {
+        const uint32_t r = (uint32_t)w4::v1_row_bytes(W->format, W->k);
+        return RowLayout{r, r};
+    }
+    return RowLayout{(uint32_t)w4::code_bytes_per_row(W->format, W->k), (uint32_t)w4::scale_bytes_per_row(W->format, W->k)};
+}
+
+const uint8_t *scale_base(const w4_matrix *W) {
+    if (W->layout == W4_LAYOUT_GFX950_V1) return W->codes + w4::code_bytes_per_row(W->format, W->k);
+    return static_cast<const uint8_t *>(W->scales);
 }
 
 int hip_status(const char *what) {
@@ -731,8 +751,9 @@ void launch_gemv_L(const w4_matrix *W, const uint16_t *x, int m, uint16_t *y, hi
     const int waves = (n + RT * RG - 1) / (RT * RG);
     const int wpb = W4_GEMV_WPB;
     const int blocks = (waves + wpb - 1) / wpb;
-    hipLaunchKernelGGL((k_gemv<FMT, L, RT>), dim3(blocks), dim3(64 * wpb), 0, st, W->codes,
-                       (const uint8_t *)W->scales, W->global_scales, x, y, n, k, m);
+    const RowLayout rl = row_layout(W);
+    hipLaunchKernelGGL((k_gemv<FMT, L, RT>), dim3(blocks), dim3(64 * wpb), 0, st, W->codes, scale_base(W),
+                       W->global_scales, x, y, n, k, m, rl.cs, rl.ss);
 }
 
 template <int FMT>
@@ -755,8 +776,9 @@ void launch_dequant_L(const w4_matrix *W, float *out, hipStream_t st) {
     const int64_t waves = (rows + RG - 1) / RG;
     const int wpb = 4;
     const int64_t blocks = (waves + wpb - 1) / wpb;
-    hipLaunchKernelGGL((k_dequant<FMT, L>), dim3((unsigned)blocks), dim3(64 * wpb), 0, st, W->codes,
-                       (const uint8_t *)W->scales, W->global_scales, out, rows, W->n, (int)W->k);
+    const RowLayout rl = row_layout(W);
+    hipLaunchKernelGGL((k_dequant<FMT, L>), dim3((unsigned)blocks), dim3(64 * wpb), 0, st, W->codes, scale_base(W),
+                       W->global_scales, out, rows, W->n, (int)W->k, rl.cs, rl.ss);
 }
 
 template <int FMT>
@@ -799,7 +821,9 @@ struct MoEPlan {
     bool grouped, mx;
     bool multi;  // grouping over three launches (large batches, or T >= W4_MULTI_ROUTE_MIN_T)
     bool pf;     // W13 / W2 as large-batch grouped GEMMs (more than MAX_ONE_BLOCK_PAIRS pairs)
-    int P, Gmax, nblk, tpb;
+    bool dec;    // K-tiled down projections: the decode kernels (k_moe_dec + k_moe_dec_combine)
+    int P, Gmax, nblk, tpb, tiles16;
+    size_t off_part;
     size_t off_logits, off_ids, off_w, off_h, total;
     size_t off_grp, off_pairs, off_hp, off_out, off_xq, off_route;
 };
@@ -818,7 +842,7 @@ int check_layer(const moe_w4a16_layer *Lr, int64_t T, MoEPlan &p) {
     if (!aligned(Lr->router_w, 16)) return fail(W4_ERR_ALIGNMENT, "router_w not 16-byte aligned");
     int st;
     if ((st = check_matrix(&Lr->w13, "w13"))) return st;
-    if ((st = check_matrix(&Lr->w2, "w2"))) return st;
+    if ((st = check_matrix(&Lr->w2, "w2", true))) return st;
     const int32_t fmt = Lr->w13.format;
     if (fmt == W4_FMT_BF16) return fail(W4_ERR_UNSUPPORTED, "routed experts must be 4-bit (bf16 is for the shared expert)");
     if (Lr->w2.format != fmt) return fail(W4_ERR_LAYOUT, "w13 and w2 formats differ");
@@ -830,7 +854,7 @@ int check_layer(const moe_w4a16_layer *Lr, int64_t T, MoEPlan &p) {
         if (Lr->shared_inter != I)
             return fail(W4_ERR_UNSUPPORTED, "shared_inter=%lld must equal inter=%lld", (long long)Lr->shared_inter, (long long)I);
         if ((st = check_matrix(&Lr->shared_w13, "shared_w13"))) return st;
-        if ((st = check_matrix(&Lr->shared_w2, "shared_w2"))) return st;
+        if ((st = check_matrix(&Lr->shared_w2, "shared_w2", true))) return st;
         const int32_t sf = Lr->shared_w13.format;
         if ((sf != fmt && sf != W4_FMT_BF16) || Lr->shared_w2.format != sf)
             return fail(W4_ERR_LAYOUT, "shared expert must use the routed experts' format or bf16 for both matrices");
@@ -870,6 +894,23 @@ int check_layer(const moe_w4a16_layer *Lr, int64_t T, MoEPlan &p) {
                         MAX_GROUPED_PAIRS);
         p.grouped = T >= W4_GROUPED_MIN_T;
     }
+    // K-tiled down projections: the decode kernels, for every T (batches re-read
+    // each selected expert per token there, so they suit decode, not prefill)
+    p.dec = Lr->w2.layout == W4_LAYOUT_GFX950_KT16;
+    if (Lr->has_shared && (Lr->shared_w2.layout == W4_LAYOUT_GFX950_KT16) != p.dec)
+        return fail(W4_ERR_UNSUPPORTED, "w2 and shared_w2 must both be K-tiled or both not");
+    if (p.dec) {
+        if (fmt != W4_FMT_E2M1_F16S16 && fmt != W4_FMT_NVFP4_E4M3S16)
+            return fail(W4_ERR_UNSUPPORTED, "K-tiled down projections need E2M1 or NVFP4 experts");
+        if (Lr->has_shared && Lr->shared_w13.format != fmt)
+            return fail(W4_ERR_UNSUPPORTED, "with K-tiled down projections the shared expert uses the routed format");
+        if (H > DEC_MAX_H) return fail(W4_ERR_UNSUPPORTED, "K-tiled down projections need hidden <= %d", DEC_MAX_H);
+        if (I % DEC_TILE) return fail(W4_ERR_UNSUPPORTED, "K-tiled down projections need inter a multiple of 16");
+        if (T > 1024) return fail(W4_ERR_UNSUPPORTED, "a layer with K-tiled down projections serves up to 1024 tokens");
+        p.grouped = false;
+        p.mx = false;
+    }
+    p.tiles16 = (int)(I / DEC_TILE);
     p.pf = p.grouped && p.P > MAX_ONE_BLOCK_PAIRS;
     p.multi = p.pf || (p.grouped && T >= W4_MULTI_ROUTE_MIN_T);
     p.tpb = T <= 256 ? 4 : ROUTE_MAX_TPB;  // one token per wave while that keeps the scan short
@@ -878,7 +919,9 @@ int check_layer(const moe_w4a16_layer *Lr, int64_t T, MoEPlan &p) {
     p.off_logits = off; off = align_up(off + (size_t)T * p.lstride * 4, 256);
     p.off_ids = off;    off = align_up(off + (size_t)T * K * 4, 256);
     p.off_w = off;      off = align_up(off + (size_t)T * K * 4, 256);
-    if (!p.grouped) {
+    if (p.dec) {  // fp32 contribution of every (token, slot, 16-value tile) to every output row
+        p.off_part = off; off = align_up(off + (size_t)T * p.S * p.tiles16 * H * 4, 256);
+    } else if (!p.grouped) {
         p.off_h = off;  off = align_up(off + (size_t)T * p.S * p.hstride * 4, 256);
     } else {
         const size_t rows = (size_t)p.P + (size_t)T;
@@ -1012,6 +1055,10 @@ int run_grouped(const moe_w4a16_layer *Lr, const MoEPlan &p, const uint16_t *x, 
                 const float *w_in, uint16_t *y, int32_t *topk_ids, float *topk_w, char *wsb, hipStream_t sm,
                 void *const *events);
 
+int run_decode(const moe_w4a16_layer *Lr, const MoEPlan &p, const uint16_t *x, const int32_t *ids_in,
+               const float *w_in, uint16_t *y, int32_t *topk_ids, float *topk_w, char *wsb, hipStream_t sm,
+               void *const *events);
+
 int stage_count(const MoEPlan &p) {
     if (!p.grouped) return 3;
     return 5 + (p.mx ? 1 : 0) + (p.multi ? 2 : 0);
@@ -1020,7 +1067,7 @@ int stage_count(const MoEPlan &p) {
 int run_moe(const moe_w4a16_layer *Lr, const uint16_t *x, int64_t T, const int32_t *ids_in, const float *w_in,
             uint16_t *y, int32_t *topk_ids, float *topk_w, void *ws, size_t ws_bytes, void *stream,
             void *const *events = nullptr, int n_events = 0) {
-    MoEPlan p;
+    MoEPlan p{};
     int st = check_layer(Lr, T, p);
     if (st) return st;
     if (!x || !y) return fail(W4_ERR_INVALID_ARG, "null x or y");
@@ -1049,6 +1096,7 @@ int run_moe(const moe_w4a16_layer *Lr, const uint16_t *x, int64_t T, const int32
         for (int i = 0; i < need; ++i)
             if (!events[i]) return fail(W4_ERR_INVALID_ARG, "null stage event %d", i);
     }
+    if (p.dec) return run_decode(Lr, p, x, ids_in, w_in, y, topk_ids, topk_w, wsb, sm, events);
     if (p.grouped) return run_grouped(Lr, p, x, ids_in, w_in, y, topk_ids, topk_w, wsb, sm, events);
     Launch l_router{sm}, l_w13{sm}, l_down{sm};
     if (events) {
@@ -1066,11 +1114,13 @@ int run_moe(const moe_w4a16_layer *Lr, const uint16_t *x, int64_t T, const int32
     // 2) W13 + SiLU over all (token, slot, tile)
     W13Args a{};
     a.codes = Lr->w13.codes;
-    a.scales = (const uint8_t *)Lr->w13.scales;
+    a.scales = scale_base(&Lr->w13);
+    a.rl = row_layout(&Lr->w13);
     a.gs = Lr->w13.global_scales;
     a.s_codes = Lr->has_shared ? Lr->shared_w13.codes : nullptr;
-    a.s_scales = Lr->has_shared ? (const uint8_t *)Lr->shared_w13.scales : nullptr;
+    a.s_scales = Lr->has_shared ? scale_base(&Lr->shared_w13) : nullptr;
     a.s_gs = Lr->has_shared ? Lr->shared_w13.global_scales : nullptr;
+    if (Lr->has_shared) a.s_rl = row_layout(&Lr->shared_w13);
     a.s_bf16 = Lr->has_shared && Lr->shared_w13.format == W4_FMT_BF16;
     a.x = x;
     a.logits = logits;
@@ -1092,11 +1142,13 @@ int run_moe(const moe_w4a16_layer *Lr, const uint16_t *x, int64_t T, const int32
     // 3) down projection + weighted combine
     DownArgs d{};
     d.codes = Lr->w2.codes;
-    d.scales = (const uint8_t *)Lr->w2.scales;
+    d.scales = scale_base(&Lr->w2);
+    d.rl = row_layout(&Lr->w2);
     d.gs = Lr->w2.global_scales;
     d.s_codes = Lr->has_shared ? Lr->shared_w2.codes : nullptr;
-    d.s_scales = Lr->has_shared ? (const uint8_t *)Lr->shared_w2.scales : nullptr;
+    d.s_scales = Lr->has_shared ? scale_base(&Lr->shared_w2) : nullptr;
     d.s_gs = Lr->has_shared ? Lr->shared_w2.global_scales : nullptr;
+    if (Lr->has_shared) d.s_rl = row_layout(&Lr->shared_w2);
     d.s_bf16 = Lr->has_shared && Lr->shared_w2.format == W4_FMT_BF16;
     d.ids = route ? ids_ws : ids_in;
     d.w = route ? w_ws : w_in;
@@ -1110,6 +1162,54 @@ int run_moe(const moe_w4a16_layer *Lr, const uint16_t *x, int64_t T, const int32
     else if (Lr->w2.format == W4_FMT_MXFP4_E8M0S32) launch_down<FMT_MXFP4>(p, d, l_down);
     else launch_down<FMT_INT4>(p, d, l_down);
     return hip_status("down launch");
+}
+
+int run_decode(const moe_w4a16_layer *Lr, const MoEPlan &p, const uint16_t *x, const int32_t *ids_in,
+               const float *w_in, uint16_t *y, int32_t *topk_ids, float *topk_w, char *wsb, hipStream_t sm,
+               void *const *events) {
+    const bool route = ids_in == nullptr;
+    float *logits = (float *)(wsb + p.off_logits);
+    int32_t *ids_ws = (int32_t *)(wsb + p.off_ids);
+    float *w_ws = (float *)(wsb + p.off_w);
+    float *part = (float *)(wsb + p.off_part);
+    auto ev = [&](int i) { return events ? (hipEvent_t)events[i] : (hipEvent_t) nullptr; };
+    int st;
+    (void)hipGetLastError();
+    // 1) router logits (and the shared-gate logit)
+    Launch l_router{sm, ev(0), ev(1)};
+    if (route) st = launch_router(Lr, p, x, logits, 0, p.E + (Lr->has_shared ? 1 : 0), l_router);
+    else if (Lr->has_shared) st = launch_router(Lr, p, x, logits, p.E, p.E + 1, l_router);
+    else st = W4_OK;
+    if (st) return st;
+    if ((st = hip_status("router launch"))) return st;
+    // 2) per (token, slot, 16-value tile): W13 rows, SiLU * up, the tile of W2
+    DecArgs a{};
+    a.codes13 = Lr->w13.codes, a.scales13 = scale_base(&Lr->w13), a.rl13 = row_layout(&Lr->w13);
+    a.codes2 = Lr->w2.codes;
+    a.tile_bytes = (uint32_t)w4::kt16_tile_bytes(Lr->w2.format, Lr->w2.n);
+    a.gs13 = Lr->w13.global_scales, a.gs2 = Lr->w2.global_scales;
+    if (Lr->has_shared) {
+        a.s_codes13 = Lr->shared_w13.codes, a.s_scales13 = scale_base(&Lr->shared_w13);
+        a.s_rl13 = row_layout(&Lr->shared_w13);
+        a.s_codes2 = Lr->shared_w2.codes;
+        a.s_gs13 = Lr->shared_w13.global_scales, a.s_gs2 = Lr->shared_w2.global_scales;
+    }
+    a.x = x, a.logits = logits, a.bias = Lr->router_bias, a.ids_in = ids_in;
+    a.ids_ws = ids_ws, a.w_ws = w_ws;
+    a.ids_user = route ? topk_ids : nullptr, a.w_user = route ? topk_w : nullptr;
+    a.part = part;
+    a.H = p.H, a.I = p.I, a.E = p.E, a.K = p.K, a.S = p.S, a.T = p.T, a.tiles = p.tiles16;
+    a.lstride = p.lstride, a.route = route ? 1 : 0;
+    launch_dec(a, Lr->w13.format == W4_FMT_NVFP4_E4M3S16 ? FMT_NVFP4 : FMT_E2M1, sm, ev(2), ev(3));
+    if ((st = hip_status("decode expert launch"))) return st;
+    // 3) ordered combine of the tile contributions
+    DecCombineArgs c{};
+    c.w = route ? w_ws : w_in;
+    c.logits = logits, c.part = part, c.y = y;
+    c.H = p.H, c.E = p.E, c.K = p.K, c.S = p.S, c.T = p.T, c.tiles = p.tiles16, c.lstride = p.lstride;
+    c.has_shared = Lr->has_shared;
+    launch_dec_combine(c, sm, ev(4), ev(5));
+    return hip_status("decode combine launch");
 }
 
 int run_grouped(const moe_w4a16_layer *Lr, const MoEPlan &p, const uint16_t *x, const int32_t *ids_in,
@@ -1173,9 +1273,10 @@ int run_grouped(const moe_w4a16_layer *Lr, const MoEPlan &p, const uint16_t *x, 
         const size_t rows = (size_t)p.P + p.T;
         uint8_t *hq = (uint8_t *)(wsb + p.off_hp), *hs = hq + rows * p.I;
         MX13Args a{};
-        a.codes = Lr->w13.codes, a.scales = (const uint8_t *)Lr->w13.scales;
+        a.codes = Lr->w13.codes, a.scales = scale_base(&Lr->w13), a.rl = row_layout(&Lr->w13);
         a.s_codes = Lr->has_shared ? Lr->shared_w13.codes : nullptr;
-        a.s_scales = Lr->has_shared ? (const uint8_t *)Lr->shared_w13.scales : nullptr;
+        a.s_scales = Lr->has_shared ? scale_base(&Lr->shared_w13) : nullptr;
+        if (Lr->has_shared) a.s_rl = row_layout(&Lr->shared_w13);
         a.xq = q.q, a.xs = q.s, a.grp = grp, a.pairs = pairs, a.hq = hq, a.hs = hs;
         a.H = p.H, a.I = p.I, a.K = p.K, a.T = p.T, a.P = p.P, a.Gmax = p.Gmax;
         int32_t *ctg = p.multi ? (int32_t *)(wsb + p.off_route) + p.P + p.E + (size_t)p.nblk * p.E : nullptr;
@@ -1184,9 +1285,10 @@ int run_grouped(const moe_w4a16_layer *Lr, const MoEPlan &p, const uint16_t *x, 
         else launch_mx13(a, sm, ev(next_ev), ev(next_ev + 1));
         if ((st = hip_status("mx w13 launch"))) return st;
         MX2Args d{};
-        d.codes = Lr->w2.codes, d.scales = (const uint8_t *)Lr->w2.scales;
+        d.codes = Lr->w2.codes, d.scales = scale_base(&Lr->w2), d.rl = row_layout(&Lr->w2);
         d.s_codes = Lr->has_shared ? Lr->shared_w2.codes : nullptr;
-        d.s_scales = Lr->has_shared ? (const uint8_t *)Lr->shared_w2.scales : nullptr;
+        d.s_scales = Lr->has_shared ? scale_base(&Lr->shared_w2) : nullptr;
+        if (Lr->has_shared) d.s_rl = row_layout(&Lr->shared_w2);
         d.grp = grp, d.pairs = pairs, d.hq = hq, d.hs = hs, d.out = outp;
         d.H = p.H, d.I = p.I, d.K = p.K, d.T = p.T, d.P = p.P, d.Gmax = p.Gmax;
         d.ctg = ctg;
@@ -1199,9 +1301,10 @@ int run_grouped(const moe_w4a16_layer *Lr, const MoEPlan &p, const uint16_t *x, 
     if ((st = hip_status("route/group launch"))) return st;
     // 3) grouped W13 + SiLU
     GW13Args a{};
-    a.codes = Lr->w13.codes, a.scales = (const uint16_t *)Lr->w13.scales;
+    a.codes = Lr->w13.codes, a.scales = scale_base(&Lr->w13), a.rl = row_layout(&Lr->w13);
     a.s_codes = Lr->has_shared ? Lr->shared_w13.codes : nullptr;
-    a.s_scales = Lr->has_shared ? (const uint16_t *)Lr->shared_w13.scales : nullptr;
+    a.s_scales = Lr->has_shared ? scale_base(&Lr->shared_w13) : nullptr;
+    if (Lr->has_shared) a.s_rl = row_layout(&Lr->shared_w13);
     a.x = x, a.grp = grp, a.pairs = pairs, a.h_hi = h_hi, a.h_lo = h_lo;
     a.H = p.H, a.I = p.I, a.K = p.K, a.T = p.T, a.P = p.P, a.Gmax = p.Gmax, a.mfma_min = W4_MFMA_MIN;
     a.fmt = Lr->w13.format == W4_FMT_NVFP4_E4M3S16 ? FMT_NVFP4
@@ -1216,9 +1319,10 @@ int run_grouped(const moe_w4a16_layer *Lr, const MoEPlan &p, const uint16_t *x, 
     if ((st = hip_status("grouped w13 launch"))) return st;
     // 4) grouped W2
     GW2Args d{};
-    d.codes = Lr->w2.codes, d.scales = (const uint16_t *)Lr->w2.scales;
+    d.codes = Lr->w2.codes, d.scales = scale_base(&Lr->w2), d.rl = row_layout(&Lr->w2);
     d.s_codes = Lr->has_shared ? Lr->shared_w2.codes : nullptr;
-    d.s_scales = Lr->has_shared ? (const uint16_t *)Lr->shared_w2.scales : nullptr;
+    d.s_scales = Lr->has_shared ? scale_base(&Lr->shared_w2) : nullptr;
+    if (Lr->has_shared) d.s_rl = row_layout(&Lr->shared_w2);
     d.grp = grp, d.pairs = pairs, d.h_hi = h_hi, d.h_lo = h_lo, d.out = outp;
     d.H = p.H, d.I = p.I, d.K = p.K, d.T = p.T, d.P = p.P, d.Gmax = p.Gmax, d.mfma_min = W4_MFMA_MIN;
     d.fmt = a.fmt;
@@ -1293,7 +1397,7 @@ int w4_mx_dot_device(const w4_matrix *A, const uint8_t *b_codes, const uint8_t *
     if (!b_codes || !b_scales || !out) return fail(W4_ERR_INVALID_ARG, "null B or out");
     if (!aligned(b_codes, 16) || !aligned(out, 4)) return fail(W4_ERR_ALIGNMENT, "B codes / out misaligned");
     (void)hipGetLastError();
-    launch_mx_dot(A->codes, (const uint8_t *)A->scales, b_codes, b_scales, out, (int)A->n, (int)m, (int)A->k,
+    launch_mx_dot(A->codes, scale_base(A), row_layout(A), b_codes, b_scales, out, (int)A->n, (int)m, (int)A->k,
                   (hipStream_t)stream);
     return hip_status("mx dot launch");
 }
@@ -1314,7 +1418,7 @@ int w4_bench_stream_read(const void *src, size_t bytes, uint32_t *sink, void *st
 }
 
 size_t moe_w4a16_workspace_bytes(const moe_w4a16_layer *L, int64_t T) {
-    MoEPlan p;
+    MoEPlan p{};
     if (check_layer(L, T, p) != W4_OK) return 0;
     return p.total;
 }
@@ -1361,7 +1465,7 @@ int scratch_of_current_device(void **out) {
 int moe_w4a16_forward_noalloc(const moe_w4a16_layer *L, const uint16_t *x, int64_t T, uint16_t *y,
                               int32_t *topk_ids, float *topk_w, void *stream) {
     w4::clear_error();
-    MoEPlan p;
+    MoEPlan p{};
     int st = check_layer(L, T, p);
     if (st) return st;
     if (p.total > W4_NOALLOC_SCRATCH_BYTES)
@@ -1374,7 +1478,7 @@ int moe_w4a16_forward_noalloc(const moe_w4a16_layer *L, const uint16_t *x, int64
 }
 
 int moe_w4a16_stage_count(const moe_w4a16_layer *L, int64_t T) {
-    MoEPlan p;
+    MoEPlan p{};
     if (check_layer(L, T, p) != W4_OK) return 0;
     return stage_count(p);
 }

@@ -113,9 +113,23 @@ extern "C" {
  * DRAM stream per row instead of two arrays), and the record stride is not a
  * power of two, so the 16-row MFMA tiles of the batched kernels spread over
  * the memory channels.  bf16 matrices have no scales: both layouts coincide.
- * Every entry point that takes a w4_matrix reads either layout; w4_pack /
- * w4_unpack convert between them. */
+ * Every entry point that takes a w4_matrix reads it; w4_pack / w4_unpack
+ * convert between it and the canonical layout. */
 #define W4_LAYOUT_GFX950_V1 1
+/* K-tiled device layout for down projections in decode (E2M1 and NVFP4 only):
+ *   codes  per group, per 16-wide K tile t (k/16 tiles): one record of the
+ *          tile for every row, the n rows' 8 code bytes of elements 16t..16t+15
+ *          (canonical nibble order), then the n rows' scale of that tile (FP16
+ *          or UE4M3), then zero padding to a multiple of 16 bytes (at n = 2048,
+ *          E2M1: 16,384 + 4,096 = 20,480 B per tile);
+ *   scales unused (may be NULL); global_scales (NVFP4) as canonical.
+ * A block that owns 16 intermediate values of one expert reads its whole
+ * share of that expert's down projection as one contiguous record, so the
+ * down projection can be split over K (the intermediate dimension) and run in
+ * the same launch as the gate/up rows that produce those 16 values.  The MoE
+ * layer takes it for w2 and shared_w2 (its decode kernels, any T); the dense
+ * GEMV, which dots whole rows, does not. */
+#define W4_LAYOUT_GFX950_KT16 2
 
 /* A stack of `groups` quantised matrices W[g] of shape [n][k] (y = W x).
  * Requirements: k % 32 == 0 (E2M1, NVFP4) or k % 128 == 0 (int4); codes
@@ -145,7 +159,7 @@ const char *w4_version(void);
 /* Bytes of packed codes / scales for `groups` matrices of [n][k] in a layout:
  * canonical: codes = groups*n*k/2, scales = groups*n*(k/G)*2 (NVFP4:
  * groups*n*(k/16)); GFX950_V1: codes = groups*n*R (the row record above),
- * scales = 0.
+ * scales = 0; GFX950_KT16: codes = groups*(k/16)*(tile record), scales = 0.
  * 8192x2048 E2M1 gives 8,388,608 + 2,097,152 = 10,485,760 B = 10.00 MiB
  * [LE stage P1]; NVFP4 8,388,608 + 1,048,576 = 9.00 MiB (+ 4 B global).
  * Returns 0 for an unknown format/layout or a k the format does not accept. */
@@ -181,8 +195,8 @@ int w4_quantize(int32_t format, const float *w, int64_t n, int64_t k,
 
 /* Canonical <-> device layout for a stack of `groups` [n][k] matrices (host
  * buffers, synchronous).  w4_pack reads canonical codes / scales and writes
- * dst_layout (GFX950_V1: records into codes_out, sized by w4_codes_bytes;
- * scales_out unused and may be NULL; CANONICAL: a copy).  w4_unpack reads
+ * dst_layout (GFX950_V1 / GFX950_KT16: records into codes_out, sized by
+ * w4_codes_bytes; scales_out unused and may be NULL; CANONICAL: a copy).  w4_unpack reads
  * src_layout and writes canonical codes and scales.  Bytes are only moved, so
  * the two are exact inverses (the V1 padding is written as zeros and ignored on
  * unpack).  The pages fix no device layout; unknown tags fail loudly

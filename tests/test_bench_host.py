@@ -87,3 +87,15 @@ def test_traffic_ingest_scaling_and_invalidation(tmp_path, monkeypatch, capsys):
     assert bench.load_traffic("k_moe_w2", "wl") is None
     (csrc / "k.hip").write_text("// v2\n")
     assert bench.load_traffic("k_moe_w13", "wl") is None
+
+
+@pytest.mark.parametrize("name", ["qwen-t1", "qwen-t1-nvfp4", "tiny"])
+def test_decode_stage_names_and_bytes(name):
+    shape = bench.workload_shapes(synth)[name]
+    names = bench.stage_names(3, shape.tokens, shape.top_k, False, decode=True)
+    sb = bench.launch_bytes(shape, float(shape.top_k), 3, decode=True)
+    assert set(sb) == set(names) and all(v > 0 for v in sb.values())
+    # the expert launch moves every selected expert's W13 and W2 once (and the shared expert's)
+    assert sb["k_moe_dec"] >= shape.top_k * (bench.weight_bytes(shape.fmt, 2 * shape.inter, shape.hidden)
+                                            + bench.weight_bytes(shape.fmt, shape.hidden, shape.inter))
+    assert bench.default_layout(name) in ("decode", "gfx950")

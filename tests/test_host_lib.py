@@ -366,3 +366,26 @@ def test_noalloc_refuses_batches_beyond_its_scratch_before_any_hip_call():
     assert "scratch" in w4.w4_last_error()
     assert w4.lib().moe_w4a16_forward_noalloc(C.byref(_layer(top_k=9)), 1 << 20, 1, 1 << 21, None, None, 0) \
         == w4.W4_ERR_INVALID_ARG
+
+
+def test_k_tiled_down_projection_plan_and_validation():
+    """A layer whose down projections are K-tiled runs the three decode launches
+    for every T (up to 1024); mixing K-tiled and row layouts for the two down
+    projections, other formats, or a K-tiled gate/up matrix is refused."""
+    KT, V1 = w4.W4_LAYOUT_GFX950_KT16, w4.W4_LAYOUT_GFX950_V1
+    H, I, E = 256, 128, 8
+    L = _layer(w13=_mat(groups=E, n=2 * I, k=H, layout=V1), w2=_mat(groups=E, n=H, k=I, layout=KT, scales=None),
+               shared_w13=_mat(groups=1, n=2 * I, k=H, layout=V1),
+               shared_w2=_mat(groups=1, n=H, k=I, layout=KT, scales=None))
+    for T in (1, 4, 32, 1024):
+        assert w4.lib().moe_w4a16_stage_count(C.byref(L), T) == 3
+    assert w4.lib().moe_w4a16_stage_count(C.byref(L), 1025) == 0
+    ws1 = w4.lib().moe_w4a16_workspace_bytes(C.byref(L), 1)
+    # logits, ids, weights and the fp32 contribution of every (slot, 16-value tile) to every output row
+    assert ws1 >= 3 * (I // 16) * H * 4
+    mixed = _layer(w2=_mat(groups=E, n=H, k=I, layout=KT, scales=None))
+    assert _fwd(mixed) == w4.W4_ERR_UNSUPPORTED
+    kt13 = _layer(w13=_mat(groups=E, n=2 * I, k=H, layout=KT, scales=None))
+    assert _fwd(kt13) == w4.W4_ERR_UNSUPPORTED
+    int4 = _layer(w2=_mat(fmt=w4.W4_FMT_INT4_F16S128, groups=E, n=H, k=I, layout=KT))
+    assert _fwd(int4) == w4.W4_ERR_UNSUPPORTED

@@ -94,3 +94,42 @@ def test_unknown_layout_fails_loudly():
     with pytest.raises(w4.W4Error) as e:
         w4.w4_unpack(fmt, 1, 2, 64, np.zeros(160, np.uint8), layout=9)
     assert e.value.status == w4.W4_ERR_LAYOUT
+
+
+def _kt16_records(codes, scales):
+    """Independent construction of the K-tiled records: per tile, every row's 8
+    code bytes, then every row's scale of the tile, zero padding to 16."""
+    G, n, kh = codes.shape
+    out = []
+    for g in range(G):
+        tiles = []
+        for t in range(kh // 8):
+            b = np.concatenate([codes[g, :, 8 * t:8 * t + 8].reshape(-1), scales[g, :, t].copy().view(np.uint8)])
+            tiles.append(np.concatenate([b, np.zeros((-len(b)) % 16, dtype=np.uint8)]))
+        out.append(np.stack(tiles))
+    return np.stack(out)
+
+
+@pytest.mark.parametrize("fmt_name", ["e2m1", "nvfp4"])
+@pytest.mark.parametrize("groups,n,k", [(1, 1, 32), (3, 5, 64), (2, 2048, 512), (1, 7, 256)])
+def test_kt16_matches_record_definition_and_round_trips(fmt_name, groups, n, k):
+    fmt, codes, scales = _random(fmt_name, groups, n, k, groups * 7 + n * 3 + k)
+    KT = w4.W4_LAYOUT_GFX950_KT16
+    rec, none = w4.w4_pack(fmt, codes, scales, layout=KT)
+    assert none is None
+    want = _kt16_records(codes, scales)
+    assert rec.shape == want.shape and np.array_equal(rec, want)
+    assert rec.size == w4.w4_codes_bytes(fmt, groups, n, k, KT)
+    assert w4.w4_scales_bytes(fmt, groups, n, k, KT) == 0
+    c2, s2 = w4.w4_unpack(fmt, groups, n, k, rec, layout=KT)
+    assert np.array_equal(c2, codes) and np.array_equal(s2, scales)
+
+
+def test_kt16_sizes_and_formats():
+    KT = w4.W4_LAYOUT_GFX950_KT16
+    # an expert's down projection 2048 x 512 (E2M1): 32 tiles of 2048 x (8 + 2) B
+    assert w4.w4_codes_bytes(w4.W4_FMT_E2M1_F16S16, 1, 2048, 512, KT) == 32 * 20480
+    assert w4.w4_codes_bytes(w4.W4_FMT_NVFP4_E4M3S16, 1, 2048, 512, KT) == 32 * 2048 * 9
+    # formats whose scale block is not 16 wide are refused
+    for fmt in (w4.W4_FMT_INT4_F16S128, w4.W4_FMT_MXFP4_E8M0S32, w4.W4_FMT_BF16):
+        assert w4.w4_codes_bytes(fmt, 1, 64, 256, KT) == 0
