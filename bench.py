@@ -450,7 +450,7 @@ def default_layout(workload):
     """The layout each workload is measured in unless --layout says otherwise."""
     return "decode" if workload in DECODE_DEFAULT else "gfx950"
 
-ROUTER_MFMA_MIN_T = 64  # the library runs the router as an MFMA GEMM from this batch size
+ROUTER_MFMA_MIN_T = 160  # the library runs the router as an MFMA GEMM from this batch size
 
 
 LARGE_BATCH_PAIRS = 4096  # past this many (token, slot) pairs the grouped GEMM kernels run

@@ -807,7 +807,10 @@ constexpr int MAX_TOKENS = 16384;
 #define W4_MULTI_ROUTE_MIN_T (1 << 30)  // smaller batches than this (and <= 4096 pairs) group in one block
 #endif
 #ifndef W4_ROUTER_MFMA_MIN_T
-#define W4_ROUTER_MFMA_MIN_T 64  // batches of at least this many tokens run the router on MFMA
+// batches of at least this many tokens run the router on MFMA (measured at the
+// 35B-A3B shape: the MFMA router ~12.3 us from T = 64 to 512, the per-row VALU
+// router 6.2 us at T = 64, 10.4 at 128, 18.6 at 256)
+#define W4_ROUTER_MFMA_MIN_T 160
 #endif
 #ifndef W4_MFMA_MIN
 #define W4_MFMA_MIN 4  // expert groups of at least this many rows run on MFMA (smaller ones on VALU)

@@ -332,7 +332,7 @@ int moe_w4a16_forward_timed(const moe_w4a16_layer *L, const uint16_t *x, int64_t
  * pairs (prefill sizes; at most 65536 pairs, T <= 16384) group their pairs
  * over three launches (per-block top-k and expert histograms; one scan; a
  * scatter) instead of one, so the grouped path takes 7 kernels (MXFP4: 8), and
- * run W13 and W2 as grouped GEMMs with LDS-staged activations; from T = 64
+ * run W13 and W2 as grouped GEMMs with LDS-staged activations; from T = 160
  * the router runs on MFMA.  E2M1 requests beyond 65536 pairs take the
  * single-token path; MXFP4 ones fail with W4_ERR_UNSUPPORTED.
  * Sources: lynn-engine README, R5 notes (tokens-per-expert grouping, inverse
