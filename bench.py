@@ -413,7 +413,7 @@ def stage_bytes(shape, distinct, n_stages=3, decode=False):
     rows = T * K + T  # routed pairs + shared rows
     if n_stages in (7, 8):  # grouping over three launches (large batches)
         b = stage_bytes(shape, distinct, n_stages - 2)
-        b.pop("k_moe_route_group")
+        b.pop("k_moe_rank_group")
         nblk = (T + 15) // 16
         b["k_route_topk"] = T * E * 4 + T * K * 12 + nblk * E * 4
         b["k_route_scan"] = 2 * nblk * E * 4 + E * 4 + (1 + 3 * min(E, T * K)) * 4
@@ -423,14 +423,14 @@ def stage_bytes(shape, distinct, n_stages=3, decode=False):
         return {
             "k_router": router,
             "k_mx_quant": T * H * 2 + T * H * 33 // 32,
-            "k_moe_route_group": T * E * 4 + T * K * 8 + rows * 4,
+            "k_moe_rank_group": T * E * 4 + T * K * 8 + rows * 4,
             "k_moe_mx13": nexp * w13 + T * H * 33 // 32 + rows * I * 33 // 32,
             "k_moe_mx2": nexp * w2 + rows * I * 33 // 32 + rows * H * 4,
             "k_moe_gcombine": rows * H * 4 + T * K * 8 + T * H * 2,
         }
     return {
         "k_router": router,
-        "k_moe_route_group": T * E * 4 + T * K * 8 + rows * 4,
+        "k_moe_rank_group": T * E * 4 + T * K * 8 + rows * 4,
         "k_moe_gw13": nexp * w13 + dw13 + T * H * 2 + rows * I * 4,
         "k_moe_gw2": nexp * w2 + dw2 + rows * I * 4 + rows * H * 4,
         "k_moe_gcombine": rows * H * 4 + T * K * 8 + T * H * 2,
@@ -463,7 +463,7 @@ def stage_names(n_stages, T, K, mx, decode=False):
         return [router, "k_moe_dec", "k_moe_dec_combine"]
     if n_stages == 3:
         return [router, "k_moe_w13", "k_moe_down"]
-    grouping = ["k_moe_route_group"] if n_stages in (5, 6) else ["k_route_topk", "k_route_scan", "k_route_scatter"]
+    grouping = ["k_moe_rank_group"] if n_stages in (5, 6) else ["k_route_topk", "k_route_scan", "k_route_scatter"]
     experts = ["k_mx_quant"] if mx else []
     large = T * K > LARGE_BATCH_PAIRS
     if mx:

@@ -154,6 +154,9 @@ void launch_pfmx2(MX2Args &a, hipStream_t st, hipEvent_t e0, hipEvent_t e1);
 void launch_mx13(MX13Args &a, hipStream_t st, hipEvent_t e0, hipEvent_t e1);
 void launch_mx2(MX2Args &a, hipStream_t st, hipEvent_t e0, hipEvent_t e1);
 void launch_route_group(GroupArgs &a, hipStream_t st, hipEvent_t e0, hipEvent_t e1);
+// routed batches: ranking over ceil(T / 4) blocks, grouping by the last one to
+// finish; `arrive` must read zero when the launch starts (the router zeroes it)
+void launch_rank_group(GroupArgs &a, int32_t *arrive, hipStream_t st, hipEvent_t e0, hipEvent_t e1);
 void launch_gw13(GW13Args &a, hipStream_t st, hipEvent_t e0, hipEvent_t e1);
 void launch_gw2(GW2Args &a, hipStream_t st, hipEvent_t e0, hipEvent_t e1);
 void launch_gcombine(GCombineArgs &a, hipStream_t st, hipEvent_t e0, hipEvent_t e1);

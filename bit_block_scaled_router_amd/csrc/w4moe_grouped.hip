@@ -38,6 +38,14 @@ namespace w4k {
 
 // k-steps (32 elements per lane each) the VALU small-group paths keep in registers
 constexpr int KS_VALU = 2;
+// waves per block of the multi-block ranking (two tokens per wave)
+constexpr int RG_WAVES = 2;
+constexpr int RG_TOKENS = 2 * RG_WAVES;
+// 128-wide K chunks per wave whose weights the batched W13 launch requests at once
+#ifndef W4_GW_CPW
+#define W4_GW_CPW 4
+#endif
+constexpr int GW_CPW = W4_GW_CPW;
 #ifndef W4_GW_MINBLK
 #define W4_GW_MINBLK 3  // blocks per CU the batched W13 / W2 kernels are compiled to fit
 #endif                  // (W2 with I > 512, int4 layers, and layers with a bf16 shared expert
@@ -138,27 +146,15 @@ __device__ __forceinline__ void route_tokens2(const GroupArgs &a, int t, int t2,
     }
 }
 
+// Counting sort of the pairs by expert, by the whole block, from the expert of
+// every pair in LDS e_of [P] (-1: the pair joins no group); cnt [E], off [E] and
+// pos [P] are LDS scratch.  Writes the group table and the pair lists.
 template <int PL>
-__global__ __launch_bounds__(1024) void k_moe_route_group(GroupArgs a) {
-    extern __shared__ int g_lds[];
-    const int E = a.E, K = a.K, T = a.T, P = a.P;
-    int *cnt = g_lds;        // [E]
-    int *off = cnt + E;      // [E]
-    int *e_of = off + E;     // [P]
-    int *pos = e_of + P;     // [P]
+__device__ __forceinline__ void group_pairs(const GroupArgs &a, int *cnt, int *off, const int *e_of, int *pos) {
+    const int E = a.E, T = a.T, P = a.P;
     const int tid = threadIdx.x, lane = tid & 63;
-    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6), nw = blockDim.x >> 6;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
     for (int i = tid; i < E; i += blockDim.x) cnt[i] = 0;
-
-    for (int t = wv; t < T; t += 2 * nw) {  // tokens t and t + nw, ranked together
-        const int t2 = t + nw < T ? t + nw : -1;
-        int e[2];
-        route_tokens2<PL>(a, t, t2, lane, e);
-        if (lane < K) {
-            e_of[t * K + lane] = e[0];
-            if (t2 >= 0) e_of[t2 * K + lane] = e[1];
-        }
-    }
     __syncthreads();
     // position of each pair inside its expert's group (LDS atomics: the order
     // inside a group is free, see the file header)
@@ -176,6 +172,66 @@ __global__ __launch_bounds__(1024) void k_moe_route_group(GroupArgs a) {
         if (e >= 0) a.pairs[off[e] + pos[p]] = p;
     }
     for (int t = tid; t < T; t += blockDim.x) a.pairs[P + t] = P + t;
+}
+
+template <int PL>
+__global__ __launch_bounds__(1024) void k_moe_route_group(GroupArgs a) {
+    extern __shared__ int g_lds[];
+    const int E = a.E, K = a.K, T = a.T, P = a.P;
+    int *cnt = g_lds;        // [E]
+    int *off = cnt + E;      // [E]
+    int *e_of = off + E;     // [P]
+    int *pos = e_of + P;     // [P]
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6), nw = blockDim.x >> 6;
+
+    for (int t = wv; t < T; t += 2 * nw) {  // tokens t and t + nw, ranked together
+        const int t2 = t + nw < T ? t + nw : -1;
+        int e[2];
+        route_tokens2<PL>(a, t, t2, lane, e);
+        if (lane < K) {
+            e_of[t * K + lane] = e[0];
+            if (t2 >= 0) e_of[t2 * K + lane] = e[1];
+        }
+    }
+    group_pairs<PL>(a, cnt, off, e_of, pos);
+}
+
+// Routed batches: the top-k ranking is spread over ceil(T / RG_TOKENS) blocks
+// (two tokens per wave, so that no CU ranks more than RG_TOKENS tokens), and
+// the last block to finish groups the pairs.  Each block publishes its
+// tokens' ids (release fence, then one device-scope atomic increment of the
+// arrival counter `arrive`, which the router launch before this one set to
+// zero); the block that reads gridDim.x - 1 from the counter knows that every
+// id is written, acquires them and runs the counting sort.  No block waits for
+// another, so the grid drains whatever the schedule.
+template <int PL>
+__global__ __launch_bounds__(64 * RG_WAVES) void k_moe_rank_group(GroupArgs a, int32_t *arrive) {
+    extern __shared__ int g_lds[];
+    __shared__ int s_last;
+    const int E = a.E, T = a.T, P = a.P;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int t = ((int)blockIdx.x * RG_WAVES + wv) * 2;  // this wave's tokens t, t + 1
+    if (t < T) {
+        int e[2];
+        route_tokens2<PL>(a, t, t + 1 < T ? t + 1 : -1, lane, e);
+    }
+    __syncthreads();
+    if (tid == 0) {
+        __threadfence();  // release: this block's ids and weights before its arrival
+        s_last = atomicAdd(arrive, 1) == (int)gridDim.x - 1;
+    }
+    __syncthreads();
+    if (!s_last) return;
+    __threadfence();  // acquire: every block's ids
+    int *cnt = g_lds;     // [E]
+    int *off = cnt + E;   // [E]
+    int *e_of = off + E;  // [P]
+    int *pos = e_of + P;  // [P]
+    for (int p = tid; p < P; p += blockDim.x) e_of[p] = a.ids_ws[p];
+    __syncthreads();
+    group_pairs<PL>(a, cnt, off, e_of, pos);
 }
 
 // Multi-launch grouping: r.tpb tokens per block (4 waves), top-k and
@@ -402,107 +458,129 @@ __device__ __forceinline__ void gw13_unit(const GW13Args &a, int gs, int tile, f
                 const bool two = n0 + 16 < gv.m;  // second column tile in use (uniform)
                 f32x4 ag[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
                 f32x4 au[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-                for (int c = wv; c < nchunks; c += 4) {
-                    const int k0 = c * 128 + 32 * q;  // this lane's 32 elements
-                    // B: 32 activations of each column token
-                    uint4 xb[2][4];
+                for (int cb0 = wv; cb0 < nchunks; cb0 += 4 * GW_CPW) {
+                    // the codes and scales of up to GW_CPW of this wave's chunks are
+                    // requested before the first of them is multiplied
+                    uint4 cgv[GW_CPW], cuv[GW_CPW];
+                    uint32_t sgv[GW_CPW], suv[GW_CPW];
+                    if constexpr (!SBF) {
 #pragma unroll
-                    for (int nt = 0; nt < 2; ++nt) {
-                        const uint32_t xo = (uint32_t)(tk[nt] * H + k0) * 2u;
-#pragma unroll
-                        for (int s = 0; s < 4; ++s)
-                            xb[nt][s] = (nt == 0 || two) ? ld128(xall, pv[nt] ? xo + 16u * s : OOB) : make_uint4(0, 0, 0, 0);
-                    }
-                    if constexpr (SBF) {  // bf16 rows, 8 weights per MFMA step
-                        const uint32_t rb = cs;
-#pragma unroll
-                        for (int s = 0; s < 4; ++s) {
-                            const uint32_t ko = (uint32_t)(k0 + 8 * s) * 2u;
-                            const bf16x8 wg = __builtin_bit_cast(bf16x8, ld128(cb, rg_ok ? rowg * rb + ko : OOB));
-                            const bf16x8 wu = __builtin_bit_cast(bf16x8, ld128(cb, rg_ok ? rowu * rb + ko : OOB));
-#pragma unroll
-                            for (int nt = 0; nt < 2; ++nt) {
-                                if (nt == 1 && !two) break;
-                                const bf16x8 b = __builtin_bit_cast(bf16x8, xb[nt][s]);
-                                ag[nt] = mfma16x16x32(wg, b, ag[nt]);
-                                au[nt] = mfma16x16x32(wu, b, au[nt]);
+                        for (int i = 0; i < GW_CPW; ++i) {
+                            const int c = cb0 + 4 * i;
+                            const bool cv = rg_ok && c < nchunks;
+                            const int k0 = c * 128 + 32 * q;
+                            cgv[i] = ld128(cb, cv ? rowg * cs + (uint32_t)(k0 >> 1) : OOB);
+                            cuv[i] = ld128(cb, cv ? rowu * cs + (uint32_t)(k0 >> 1) : OOB);
+                            if constexpr (FMT != FMT_INT4) {
+                                sgv[i] = ld_scales<FMT>(sb, cv ? rowg * ss + scale_col<FMT>(k0) : OOB);
+                                suv[i] = ld_scales<FMT>(sb, cv ? rowu * ss + scale_col<FMT>(k0) : OOB);
                             }
                         }
-                        continue;
                     }
-                    const uint4 cg = ld128(cb, rg_ok ? rowg * cs + (uint32_t)(k0 >> 1) : OOB);
-                    const uint4 cu = ld128(cb, rg_ok ? rowu * cs + (uint32_t)(k0 >> 1) : OOB);
-                    if constexpr (FMT == FMT_INT4) {
-                        // the chunk is one scale group: MFMAs on the raw offset codes
-                        // u = q + 8 (exact bf16) and on 8 (the offset), then the
-                        // difference times the scales of the lane's output rows
-                        float so_g[4], so_u[4];
 #pragma unroll
-                        for (int j = 0; j < 4; ++j) {
-                            const uint32_t o = (uint32_t)(i0 + 4 * q + j);
-                            const bool ov = o < (uint32_t)I;
-                            so_g[j] = f16_bits_to_f32(ld16(sb, ov ? o * ss + (uint32_t)c * 2u : OOB));
-                            so_u[j] = f16_bits_to_f32(ld16(sb, ov ? ((uint32_t)I + o) * ss + (uint32_t)c * 2u : OOB));
+                    for (int ci = 0; ci < GW_CPW; ++ci) {
+                        const int c = cb0 + 4 * ci;
+                        if (c >= nchunks) break;
+                        const int k0 = c * 128 + 32 * q;  // this lane's 32 elements
+                        // B: 32 activations of each column token
+                        uint4 xb[2][4];
+#pragma unroll
+                        for (int nt = 0; nt < 2; ++nt) {
+                            const uint32_t xo = (uint32_t)(tk[nt] * H + k0) * 2u;
+#pragma unroll
+                            for (int s = 0; s < 4; ++s)
+                                xb[nt][s] = (nt == 0 || two) ? ld128(xall, pv[nt] ? xo + 16u * s : OOB)
+                                                             : make_uint4(0, 0, 0, 0);
                         }
-                        const uint32_t cgw[4] = {cg.x, cg.y, cg.z, cg.w}, cuw[4] = {cu.x, cu.y, cu.z, cu.w};
-                        f32x4 tg[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}}, tu[2] = {tg[0], tg[0]},
-                              tc[2] = {tg[0], tg[0]};
+                        if constexpr (SBF) {  // bf16 rows, 8 weights per MFMA step
+                            const uint32_t rb = cs;
 #pragma unroll
-                        for (int s = 0; s < 4; ++s) {
-                            const bf16x8 ug = u4x8_bf16(cgw[s]), uu = u4x8_bf16(cuw[s]);
-                            // both column tiles unconditionally (a missing second tile has
-                            // zero activations): the chunk's sums are read right after
-                            // these MFMAs, and straight-line code keeps the compiler's
-                            // MFMA-result wait states in place (behind a branch they were
-                            // not, and the first read saw a stale accumulator)
+                            for (int s = 0; s < 4; ++s) {
+                                const uint32_t ko = (uint32_t)(k0 + 8 * s) * 2u;
+                                const bf16x8 wg = __builtin_bit_cast(bf16x8, ld128(cb, rg_ok ? rowg * rb + ko : OOB));
+                                const bf16x8 wu = __builtin_bit_cast(bf16x8, ld128(cb, rg_ok ? rowu * rb + ko : OOB));
 #pragma unroll
-                            for (int nt = 0; nt < 2; ++nt) {
-                                const bf16x8 b = __builtin_bit_cast(bf16x8, xb[nt][s]);
-                                tg[nt] = mfma16x16x32(ug, b, tg[nt]);
-                                tu[nt] = mfma16x16x32(uu, b, tu[nt]);
-                                tc[nt] = mfma16x16x32(bf16x8_splat8(), b, tc[nt]);
+                                for (int nt = 0; nt < 2; ++nt) {
+                                    if (nt == 1 && !two) break;
+                                    const bf16x8 b = __builtin_bit_cast(bf16x8, xb[nt][s]);
+                                    ag[nt] = mfma16x16x32(wg, b, ag[nt]);
+                                    au[nt] = mfma16x16x32(wu, b, au[nt]);
+                                }
                             }
+                            continue;
                         }
-#pragma unroll
-                        for (int nt = 0; nt < 2; ++nt)
+                        const uint4 cg = cgv[ci], cu = cuv[ci];
+                        if constexpr (FMT == FMT_INT4) {
+                            // the chunk is one scale group: MFMAs on the raw offset codes
+                            // u = q + 8 (exact bf16) and on 8 (the offset), then the
+                            // difference times the scales of the lane's output rows
+                            float so_g[4], so_u[4];
 #pragma unroll
                             for (int j = 0; j < 4; ++j) {
-                                ag[nt][j] = fmaf(so_g[j], tg[nt][j] - tc[nt][j], ag[nt][j]);
-                                au[nt][j] = fmaf(so_u[j], tu[nt][j] - tc[nt][j], au[nt][j]);
+                                const uint32_t o = (uint32_t)(i0 + 4 * q + j);
+                                const bool ov = o < (uint32_t)I;
+                                so_g[j] = f16_bits_to_f32(ld16(sb, ov ? o * ss + (uint32_t)c * 2u : OOB));
+                                so_u[j] = f16_bits_to_f32(ld16(sb, ov ? ((uint32_t)I + o) * ss + (uint32_t)c * 2u : OOB));
                             }
-                        continue;
-                    }
-                    const uint32_t sg = ld_scales<FMT>(sb, rg_ok ? rowg * ss + scale_col<FMT>(k0) : OOB);
-                    const uint32_t su = ld_scales<FMT>(sb, rg_ok ? rowu * ss + scale_col<FMT>(k0) : OOB);
-                    const uint32_t cgw[4] = {cg.x, cg.y, cg.z, cg.w}, cuw[4] = {cu.x, cu.y, cu.z, cu.w};
+                            const uint32_t cgw[4] = {cg.x, cg.y, cg.z, cg.w}, cuw[4] = {cu.x, cu.y, cu.z, cu.w};
+                            f32x4 tg[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}}, tu[2] = {tg[0], tg[0]},
+                                  tc[2] = {tg[0], tg[0]};
 #pragma unroll
-                    for (int s = 0; s < 4; ++s) {
-                        if constexpr (FMT == FMT_NVFP4) {
-                            const f32x2 sgv = block_scales2<FMT>(sg), suv = block_scales2<FMT>(su);
-                            const bf16x8 ag1 = e2m1x8_scaled(cgw[s], s < 2 ? sgv.x : sgv.y);
-                            const bf16x8 au1 = e2m1x8_scaled(cuw[s], s < 2 ? suv.x : suv.y);
+                            for (int s = 0; s < 4; ++s) {
+                                const bf16x8 ug = u4x8_bf16(cgw[s]), uu = u4x8_bf16(cuw[s]);
+                                // both column tiles unconditionally (a missing second tile has
+                                // zero activations): the chunk's sums are read right after
+                                // these MFMAs, and straight-line code keeps the compiler's
+                                // MFMA-result wait states in place (behind a branch they were
+                                // not, and the first read saw a stale accumulator)
 #pragma unroll
-                            for (int nt = 0; nt < 2; ++nt) {
-                                if (nt == 1 && !two) break;
-                                const bf16x8 b = __builtin_bit_cast(bf16x8, xb[nt][s]);
-                                ag[nt] = mfma16x16x32(ag1, b, ag[nt]);
-                                au[nt] = mfma16x16x32(au1, b, au[nt]);
+                                for (int nt = 0; nt < 2; ++nt) {
+                                    const bf16x8 b = __builtin_bit_cast(bf16x8, xb[nt][s]);
+                                    tg[nt] = mfma16x16x32(ug, b, tg[nt]);
+                                    tu[nt] = mfma16x16x32(uu, b, tu[nt]);
+                                    tc[nt] = mfma16x16x32(bf16x8_splat8(), b, tc[nt]);
+                                }
                             }
-                        } else {
-                            float gh, gl, uh, ul;
-                            split_scale(f16_bits_to_f32(s < 2 ? sg : (sg >> 16)), gh, gl);
-                            split_scale(f16_bits_to_f32(s < 2 ? su : (su >> 16)), uh, ul);
-                            bf16x8 agh, agl, auh, aul;
-                            e2m1x8_split(cgw[s], gh, gl, agh, agl);
-                            e2m1x8_split(cuw[s], uh, ul, auh, aul);
 #pragma unroll
-                            for (int nt = 0; nt < 2; ++nt) {
-                                if (nt == 1 && !two) break;
-                                const bf16x8 b = __builtin_bit_cast(bf16x8, xb[nt][s]);
-                                ag[nt] = mfma16x16x32(agh, b, ag[nt]);
-                                ag[nt] = mfma16x16x32(agl, b, ag[nt]);
-                                au[nt] = mfma16x16x32(auh, b, au[nt]);
-                                au[nt] = mfma16x16x32(aul, b, au[nt]);
+                            for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+                                for (int j = 0; j < 4; ++j) {
+                                    ag[nt][j] = fmaf(so_g[j], tg[nt][j] - tc[nt][j], ag[nt][j]);
+                                    au[nt][j] = fmaf(so_u[j], tu[nt][j] - tc[nt][j], au[nt][j]);
+                                }
+                            continue;
+                        }
+                        const uint32_t sg = sgv[ci], su = suv[ci];
+                        const uint32_t cgw[4] = {cg.x, cg.y, cg.z, cg.w}, cuw[4] = {cu.x, cu.y, cu.z, cu.w};
+#pragma unroll
+                        for (int s = 0; s < 4; ++s) {
+                            if constexpr (FMT == FMT_NVFP4) {
+                                const f32x2 sgv = block_scales2<FMT>(sg), suv = block_scales2<FMT>(su);
+                                const bf16x8 ag1 = e2m1x8_scaled(cgw[s], s < 2 ? sgv.x : sgv.y);
+                                const bf16x8 au1 = e2m1x8_scaled(cuw[s], s < 2 ? suv.x : suv.y);
+#pragma unroll
+                                for (int nt = 0; nt < 2; ++nt) {
+                                    if (nt == 1 && !two) break;
+                                    const bf16x8 b = __builtin_bit_cast(bf16x8, xb[nt][s]);
+                                    ag[nt] = mfma16x16x32(ag1, b, ag[nt]);
+                                    au[nt] = mfma16x16x32(au1, b, au[nt]);
+                                }
+                            } else {
+                                float gh, gl, uh, ul;
+                                split_scale(f16_bits_to_f32(s < 2 ? sg : (sg >> 16)), gh, gl);
+                                split_scale(f16_bits_to_f32(s < 2 ? su : (su >> 16)), uh, ul);
+                                bf16x8 agh, agl, auh, aul;
+                                e2m1x8_split(cgw[s], gh, gl, agh, agl);
+                                e2m1x8_split(cuw[s], uh, ul, auh, aul);
+#pragma unroll
+                                for (int nt = 0; nt < 2; ++nt) {
+                                    if (nt == 1 && !two) break;
+                                    const bf16x8 b = __builtin_bit_cast(bf16x8, xb[nt][s]);
+                                    ag[nt] = mfma16x16x32(agh, b, ag[nt]);
+                                    ag[nt] = mfma16x16x32(agl, b, ag[nt]);
+                                    au[nt] = mfma16x16x32(auh, b, au[nt]);
+                                    au[nt] = mfma16x16x32(aul, b, au[nt]);
+                                }
                             }
                         }
                     }
@@ -1869,6 +1947,17 @@ void launch_route_group(GroupArgs &a, hipStream_t st, hipEvent_t e0, hipEvent_t 
     else if (pl <= 4) go_ev(st, e0, e1, k_moe_route_group<4>, g, b, shm, a);
     else if (pl <= 8) go_ev(st, e0, e1, k_moe_route_group<8>, g, b, shm, a);
     else go_ev(st, e0, e1, k_moe_route_group<16>, g, b, shm, a);
+}
+
+void launch_rank_group(GroupArgs &a, int32_t *arrive, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
+    const int pl = (a.E + 63) / 64;
+    const dim3 g((unsigned)((a.T + RG_TOKENS - 1) / RG_TOKENS)), b(64 * RG_WAVES);
+    const uint32_t shm = (uint32_t)grouped_lds_bytes(a.E, a.P);
+    if (pl <= 1) go_ev(st, e0, e1, k_moe_rank_group<1>, g, b, shm, a, arrive);
+    else if (pl <= 2) go_ev(st, e0, e1, k_moe_rank_group<2>, g, b, shm, a, arrive);
+    else if (pl <= 4) go_ev(st, e0, e1, k_moe_rank_group<4>, g, b, shm, a, arrive);
+    else if (pl <= 8) go_ev(st, e0, e1, k_moe_rank_group<8>, g, b, shm, a, arrive);
+    else go_ev(st, e0, e1, k_moe_rank_group<16>, g, b, shm, a, arrive);
 }
 
 void launch_route_multi(RouteArgs &a, hipStream_t st, hipEvent_t *ev) {

@@ -187,8 +187,9 @@ __global__ __launch_bounds__(256) void k_stream_read(const uint4 *__restrict__ s
 template <int NS, int TB>
 __global__ __launch_bounds__(512) void k_router(const uint16_t *__restrict__ wr, const uint16_t *__restrict__ wsg,
                                                 const uint16_t *__restrict__ x, float *__restrict__ logits, int E,
-                                                int H, int T, int r_begin, int lstride) {
+                                                int H, int T, int r_begin, int lstride, int32_t *arrive) {
     const int lane = threadIdx.x & 63;
+    if (arrive && blockIdx.x == 0 && threadIdx.x == 0) *arrive = 0;  // the grouping launch's arrival counter
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), nw = blockDim.x >> 6;
     const int r = r_begin + blockIdx.x;
     const Buf wb = make_buf(r < E ? wr + (size_t)r * H : wsg, (uint32_t)H * 2u);
@@ -234,8 +235,11 @@ __global__ __launch_bounds__(512) void k_router(const uint16_t *__restrict__ wr,
 __global__ __launch_bounds__(256) void k_router_mfma(const uint16_t *__restrict__ wr,
                                                      const uint16_t *__restrict__ wsg,
                                                      const uint16_t *__restrict__ x, float *__restrict__ logits,
-                                                     int E, int H, int T, int r_begin, int r_end, int lstride) {
+                                                     int E, int H, int T, int r_begin, int r_end, int lstride,
+                                                     int32_t *arrive) {
     __shared__ float red[3][16][64];
+    // the arrival counter of the grouping launch that follows
+    if (arrive && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *arrive = 0;
     const int lane = threadIdx.x & 63, wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int r = lane & 15, q = lane >> 4;
     const int row0 = r_begin + (int)blockIdx.y * 16;
@@ -829,6 +833,7 @@ struct MoEPlan {
     size_t off_part;
     size_t off_logits, off_ids, off_w, off_h, total;
     size_t off_grp, off_pairs, off_hp, off_out, off_xq, off_route;
+    size_t off_arrive;  // arrival counter of the multi-block ranking (int32)
 };
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
@@ -929,6 +934,7 @@ int check_layer(const moe_w4a16_layer *Lr, int64_t T, MoEPlan &p) {
     } else {
         const size_t rows = (size_t)p.P + (size_t)T;
         p.off_grp = off;   off = align_up(off + (size_t)(2 + 3 * p.Gmax) * 4, 256);
+        p.off_arrive = off; off = align_up(off + 4, 256);
         p.off_pairs = off; off = align_up(off + rows * 4, 256);
         p.off_hp = off;    off = align_up(off + rows * (size_t)I * 4, 256);  // h_hi then h_lo, bf16 (MX: codes, scales)
         p.off_out = off;   off = align_up(off + rows * (size_t)H * 4, 256);
@@ -946,12 +952,12 @@ int check_layer(const moe_w4a16_layer *Lr, int64_t T, MoEPlan &p) {
 }
 
 int launch_router(const moe_w4a16_layer *Lr, const MoEPlan &p, const uint16_t *x, float *logits, int r_begin,
-                  int r_end, const Launch &st) {
+                  int r_end, const Launch &st, int32_t *arrive = nullptr) {
     const int nrows = r_end - r_begin;
     if (nrows <= 0) return W4_OK;
     if (p.T >= W4_ROUTER_MFMA_MIN_T) {
         go(st, k_router_mfma, dim3((unsigned)((p.T + 63) / 64), (unsigned)((nrows + 15) / 16)), dim3(256), 0,
-           Lr->router_w, Lr->shared_gate_w, x, logits, p.E, p.H, p.T, r_begin, r_end, p.lstride);
+           Lr->router_w, Lr->shared_gate_w, x, logits, p.E, p.H, p.T, r_begin, r_end, p.lstride, arrive);
         return W4_OK;
     }
     const int ns = (p.H + 511) / 512;
@@ -960,12 +966,12 @@ int launch_router(const moe_w4a16_layer *Lr, const MoEPlan &p, const uint16_t *x
         constexpr int NS = decltype(NSc)::value;
         if (p.T == 1) {
             go(st, k_router<NS, 1>, dim3(nrows), dim3(64), 0, Lr->router_w, Lr->shared_gate_w, x, logits, p.E, p.H,
-               p.T, r_begin, p.lstride);
+               p.T, r_begin, p.lstride, arrive);
         } else {  // chunks of 4 tokens (2 for the widest rows), up to 8 waves per row
             constexpr int TB = NS >= 16 ? 2 : 4;
             const int waves = (p.T + TB - 1) / TB < 8 ? (p.T + TB - 1) / TB : 8;
             go(st, k_router<NS, TB>, dim3(nrows), dim3(64 * waves), 0, Lr->router_w, Lr->shared_gate_w, x, logits,
-               p.E, p.H, p.T, r_begin, p.lstride);
+               p.E, p.H, p.T, r_begin, p.lstride, arrive);
         }
     };
     if (ns <= 1) with_ns(std::integral_constant<int, 1>());
@@ -1231,9 +1237,13 @@ int run_grouped(const moe_w4a16_layer *Lr, const MoEPlan &p, const uint16_t *x, 
     // stage events after the router (and the MX quantiser): the grouping takes
     // 1 launch, or 3 for large batches
     int next_ev = p.mx ? 4 : 2;
+    int32_t *arrive = (int32_t *)(wsb + p.off_arrive);
     auto group = [&](GroupArgs &ga) {
         if (!p.multi) {
-            launch_route_group(ga, sm, ev(next_ev), ev(next_ev + 1));
+            // routed: ranking over many blocks (the router launch zeroes the
+            // arrival counter); caller routing: one block reads the ids
+            if (route) launch_rank_group(ga, arrive, sm, ev(next_ev), ev(next_ev + 1));
+            else launch_route_group(ga, sm, ev(next_ev), ev(next_ev + 1));
             next_ev += 2;
             return;
         }
@@ -1251,7 +1261,8 @@ int run_grouped(const moe_w4a16_layer *Lr, const MoEPlan &p, const uint16_t *x, 
     (void)hipGetLastError();
     // 1) router logits (and the shared-gate logit)
     Launch l_router{sm, ev(0), ev(1)};
-    if (route) st = launch_router(Lr, p, x, logits, 0, p.E + (Lr->has_shared ? 1 : 0), l_router);
+    if (route)
+        st = launch_router(Lr, p, x, logits, 0, p.E + (Lr->has_shared ? 1 : 0), l_router, p.multi ? nullptr : arrive);
     else if (Lr->has_shared) st = launch_router(Lr, p, x, logits, p.E, p.E + 1, l_router);
     else st = W4_OK;
     if (st) return st;

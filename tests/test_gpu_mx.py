@@ -65,7 +65,8 @@ def test_mxfp4_dequant_bit_exact(n, k):
 def _ws_layout(shape, T):
     """Byte offsets of the MX path's intermediates in the layer workspace, in
     the library's order (each region 256-byte aligned): logits [T][ceil64(E+1)]
-    fp32, ids and weights [T][k], group table, pair list, h (codes [P+T][I] then
+    fp32, ids and weights [T][k], group table, the ranking's arrival counter,
+    pair list, h (codes [P+T][I] then
     E8M0 scales [P+T][I/32]), expert outputs fp32 [P+T][H], x codes [T][H] then
     scales [T][H/32], and past 4096 pairs the multi-launch grouping's arrays."""
     def up(v):
@@ -77,6 +78,7 @@ def _ws_layout(shape, T):
     off = up(off + T * K * 4)
     off = up(off + T * K * 4)
     off = up(off + (2 + 3 * min(E, P)) * 4)
+    off = up(off + 4)
     off = up(off + rows * 4)
     off_h = off
     off = up(off + rows * I * 4)
