@@ -645,6 +645,9 @@ WORKLOADS = ["qwen-t1", "qwen-t32", "tiny", "gemv-e2m1", "gemv-int4", "qwen-t1-n
 
 def run_moe(args, torch, w4, wl, synth, hip):
     shape = workload_shapes(synth)[args.workload]
+    if args.tokens:  # the same layer at another batch size (sweeps; not a reported workload)
+        import dataclasses
+        shape = dataclasses.replace(shape, tokens=args.tokens, name=f"{shape.name}@T{args.tokens}")
     T = shape.tokens
     l13, l2 = LAYOUTS[args.layout]
     base = wl.build_moe_layer(shape, device="cuda", layout=l13, w2_layout=l2)
@@ -885,6 +888,7 @@ def main():
                          "projections (decode), or the canonical arrays; default per workload")
     ap.add_argument("--pool", type=int, default=64, help="token pool (MoE workloads)")
     ap.add_argument("--cpu-tokens", type=int, default=1)
+    ap.add_argument("--tokens", type=int, default=0, help="MoE workloads: tokens per step instead of the workload's")
     ap.add_argument("--cpu-reps", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",

@@ -817,7 +817,7 @@ constexpr int MAX_TOKENS = 16384;
 #define W4_ROUTER_MFMA_MIN_T 160
 #endif
 #ifndef W4_MFMA_MIN
-#define W4_MFMA_MIN 4  // expert groups of at least this many rows run on MFMA (smaller ones on VALU)
+#define W4_MFMA_MIN 2  // expert groups of at least this many rows run on MFMA (single rows on VALU)
 #endif
 constexpr int MAX_GROUPED_PAIRS = 65536;  // (token, slot) pairs of one grouped call
 constexpr int MAX_ONE_BLOCK_PAIRS = 4096;  // up to this many, one block groups them (LDS counting sort)

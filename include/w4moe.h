@@ -318,7 +318,7 @@ int moe_w4a16_forward_timed(const moe_w4a16_layer *L, const uint16_t *x, int64_t
  * arguments): 3 for the single-token path (router; grouped W13 + SiLU over
  * every (token, slot); down + combine), 5 for the batched path (router; top-k
  * and grouping of the (token, slot) pairs by expert; W13 + SiLU per expert
- * group, on MFMA for groups of at least 4 tokens; W2 per expert group; ordered
+ * group, on MFMA for groups of at least 2 tokens; W2 per expert group; ordered
  * combine).  The batched path serves E2M1 and NVFP4 layers with H and I
  * multiples of 128 and at most 4096, T >= 4 and T * top_k <= 65536 (NVFP4: one
  * exact bf16 MFMA term per weight instead of two, the global scales applied to

@@ -110,3 +110,52 @@ def test_router_extremes(shape, T):
         np.testing.assert_allclose(wts.sum(axis=1), 1.0, rtol=1e-6)
     np.testing.assert_allclose(wts, rw, rtol=2e-6, atol=1e-7)
     assert_bf16_close(got, ref, f"{shape.name} T={T}")
+
+
+def test_ranking_blocks_across_calls():
+    """Routed batches rank their tokens over ceil(T/4) blocks and the last block to
+    arrive groups the pairs; the router launch zeroes the arrival counter in every
+    call.  One workspace serves calls of different sizes back to back (ragged T,
+    one block, 128 blocks), eagerly and replayed from a captured graph with eager
+    calls of other sizes between the replays."""
+    shape = synth.MoEShape("edge-rank", 256, 128, 64, 8, 128, 1, 0.0, 25)
+    dev_layer = wl.build_moe_layer(shape, device=DEV)
+    or_layer = oracle_layer(shape)
+    ws = w4.alloc_workspace(dev_layer, 509)
+
+    def call(x_bits):
+        T = x_bits.shape[0]
+        ids = torch.full((T, shape.top_k), -7, dtype=torch.int32, device=DEV)
+        wts = torch.zeros((T, shape.top_k), dtype=torch.float32, device=DEV)
+        y = w4.moe_w4a16_forward(dev_layer, wl.bf16_tensor(x_bits), topk_ids=ids, topk_w=wts, ws=ws)
+        return y, ids, wts
+
+    xs = {T: tie_free_tokens(shape, or_layer, T, first=13 * T) for T in (509, 7, 4, 130, 33)}
+    for T in (509, 7, 4, 130, 509):
+        print(f"rank blocks T={T}", flush=True)
+        y, ids, wts = call(xs[T])
+        ref, rids, rw = ops.moe_forward(or_layer, xs[T])
+        assert np.array_equal(ids.cpu().numpy(), rids), T
+        np.testing.assert_allclose(wts.cpu().numpy(), rw, rtol=2e-6, atol=1e-7)
+        assert_bf16_close(wl.bf16_bits(y), ref, f"rank blocks T={T}")
+    # graph replays of a T = 33 call, eager calls of other sizes in between
+    x33 = wl.bf16_tensor(xs[33])
+    y33 = torch.empty((33, shape.hidden), dtype=torch.bfloat16, device=DEV)
+    w4.moe_w4a16_forward(dev_layer, x33, y=y33, ws=ws)
+    torch.cuda.synchronize()
+    eager = y33.clone()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            w4.moe_w4a16_forward(dev_layer, x33, y=y33, ws=ws)
+    torch.cuda.current_stream().wait_stream(s)
+    for T in (7, 130, 4):
+        y33.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y33, eager), "graph replay"
+        call(xs[T])
+        torch.cuda.synchronize()

@@ -108,7 +108,7 @@ def test_nvfp4_moe_tiny(tiny_nv):
     for t in range(3):
         print(f"nvfp4 moe tiny token {t}", flush=True)
         _check_moe(shape, dev_layer, or_layer, tie_free_tokens(shape, or_layer, 1, first=t), f"nvfp4 tiny t={t}")
-    # batches of 4 or more take the grouped path (MFMA for groups of >= 4 rows)
+    # batches of 4 or more take the grouped path (MFMA for groups of >= 2 rows)
     assert w4.moe_w4a16_stage_count(dev_layer, 3) == 3
     assert w4.moe_w4a16_stage_count(dev_layer, 7) == 5
     _check_moe(shape, dev_layer, or_layer, tie_free_tokens(shape, or_layer, 3, first=30), "nvfp4 tiny T=3")
