@@ -243,8 +243,9 @@ int w4_mx_dot_device(const w4_matrix *A, const uint8_t *b_codes, const uint8_t *
                      void *stream);
 
 /* Measurement aid (not a step of the layer): read `bytes` (a multiple of 16) of
- * device memory at src with 128-bit loads spread over the whole GPU, four per
- * thread in flight, and write nothing but, with negligible probability, one word
+ * device memory at src with 128-bit loads spread over the whole GPU, one per
+ * thread in as many 256-thread blocks as the buffer needs (the fastest plain read
+ * measured on MI355X), and write nothing but, with negligible probability, one word
  * to *sink (device, 4-byte aligned).  Timing it gives the practical HBM read
  * ceiling for a buffer of that size, the second denominator beside the 8 TB/s
  * peak.  Asynchronous on `stream`.  Errors: W4_ERR_INVALID_ARG, _ALIGNMENT, _HIP. */
