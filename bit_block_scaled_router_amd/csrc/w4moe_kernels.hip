@@ -740,7 +740,7 @@ int hip_status(const char *what) {
 // ---------------------------------------------------------------- GEMV launch
 
 #ifndef W4_GEMV_ROWS
-#define W4_GEMV_ROWS 4  // rows per wave of the dense GEMV (at least one load group)
+#define W4_GEMV_ROWS 2  // rows per wave of the dense GEMV (at least one load group)
 #endif
 #ifndef W4_GEMV_WPB
 #define W4_GEMV_WPB 4  // waves per block of the dense GEMV
