@@ -43,13 +43,16 @@ struct GroupArgs {
 // is grp[1 + 3*Gmax] (the shared expert's ceil(T/64) tiles follow implicitly).
 // Large batches group their pairs over three launches (k_route_topk,
 // k_route_scan, k_route_scatter) instead of one block: per-block expert
-// histograms in cntb [nblk][E] (turned into each block's base offsets by the
-// scan), the expert of every pair in e_of [P], each expert's first pair-list
-// entry in off_e [E].
+// histograms in cntb [nblk][E], each block's base offset inside each expert's
+// list in cbase [nblk][E] (written by the scan, so that every launch reads
+// only what an earlier launch wrote and can run again on the same inputs), the
+// expert of every pair in e_of [P], each expert's first pair-list entry in
+// off_e [E].
 struct RouteArgs {
     GroupArgs g;
     int32_t *e_of;
     int32_t *cntb;
+    int32_t *cbase;
     int32_t *off_e;
     int32_t *ctg;  // [2 x column tiles]: routed group, first column (see k_route_scan)
     int nblk;

@@ -203,8 +203,9 @@ __global__ __launch_bounds__(1024) void k_moe_route_group(GroupArgs a) {
 // tokens' ids (release fence, then one device-scope atomic increment of the
 // arrival counter `arrive`, which the router launch before this one set to
 // zero); the block that reads gridDim.x - 1 from the counter knows that every
-// id is written, acquires them and runs the counting sort.  No block waits for
-// another, so the grid drains whatever the schedule.
+// id is written, acquires them, sets the counter back to zero and runs the
+// counting sort.  No block waits for another, so the grid drains whatever the
+// schedule.
 template <int PL>
 __global__ __launch_bounds__(64 * RG_WAVES) void k_moe_rank_group(GroupArgs a, int32_t *arrive) {
     extern __shared__ int g_lds[];
@@ -230,6 +231,7 @@ __global__ __launch_bounds__(64 * RG_WAVES) void k_moe_rank_group(GroupArgs a, i
     int *e_of = off + E;  // [P]
     int *pos = e_of + P;  // [P]
     for (int p = tid; p < P; p += blockDim.x) e_of[p] = a.ids_ws[p];
+    if (tid == 0) *arrive = 0;  // every block has arrived: ready for a launch without the router before it
     __syncthreads();
     group_pairs<PL>(a, cnt, off, e_of, pos);
 }
@@ -265,9 +267,9 @@ __global__ __launch_bounds__(256) void k_route_topk(RouteArgs r) {
     for (int i = tid; i < E; i += blockDim.x) r.cntb[(size_t)blockIdx.x * E + i] = hist[i];
 }
 
-// One block: per expert, the exclusive scan of the block histograms (in place:
-// cntb becomes each block's base inside the expert's list) and the expert's
-// total; then the group table and each expert's list start.
+// One block: per expert, the exclusive scan of the block histograms (cntb ->
+// cbase: each block's base inside the expert's list) and the expert's total;
+// then the group table and each expert's list start.
 __global__ __launch_bounds__(1024) void k_route_scan(RouteArgs r) {
     __shared__ int tot[1024], off[1024], part[1024];
     const int E = r.g.E, Gmax = r.g.Gmax;
@@ -302,7 +304,7 @@ __global__ __launch_bounds__(1024) void k_route_scan(RouteArgs r) {
 #pragma unroll
             for (int i = 0; i < 16; ++i)
                 if (b0 + i < b_hi) {
-                    r.cntb[(size_t)(b0 + i) * E + e] = run;
+                    r.cbase[(size_t)(b0 + i) * E + e] = run;
                     run += c[i];
                 }
         }
@@ -354,7 +356,7 @@ __global__ __launch_bounds__(256) void k_route_scatter(RouteArgs r) {
         if (e < 0) continue;
         int rank = 0;
         for (int q = 0; q < i; ++q) rank += es[q] == e ? 1 : 0;
-        a.pairs[r.off_e[e] + r.cntb[(size_t)blockIdx.x * E + e] + rank] = p0 + i;
+        a.pairs[r.off_e[e] + r.cbase[(size_t)blockIdx.x * E + e] + rank] = p0 + i;
     }
     for (int t = t0 + tid; t < t1; t += blockDim.x) a.pairs[a.P + t] = a.P + t;
 }

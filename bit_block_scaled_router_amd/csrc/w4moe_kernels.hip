@@ -232,6 +232,7 @@ __global__ __launch_bounds__(512) void k_router(const uint16_t *__restrict__ wr,
 // the current one is multiplied) and the partial sums are added in wave order
 // through LDS.  Every x tile is read by ceil(rows / 16) blocks and every router
 // row by ceil(T / 64), instead of all T tokens per row as in k_router.
+template <int NT>
 __global__ __launch_bounds__(256) void k_router_mfma(const uint16_t *__restrict__ wr,
                                                      const uint16_t *__restrict__ wsg,
                                                      const uint16_t *__restrict__ x, float *__restrict__ logits,
@@ -244,20 +245,20 @@ __global__ __launch_bounds__(256) void k_router_mfma(const uint16_t *__restrict_
     const int r = lane & 15, q = lane >> 4;
     const int row0 = r_begin + (int)blockIdx.y * 16;
     const int row = row0 + r;  // this lane's A row
-    const int tok0 = (int)blockIdx.x * 64;
+    const int tok0 = (int)blockIdx.x * (16 * NT);
     const Buf wb = make_buf(wr, (uint32_t)E * (uint32_t)H * 2u);
     const Buf gb = make_buf(wsg, wsg ? (uint32_t)H * 2u : 0u);
     const Buf xb = make_buf(x, (uint32_t)T * (uint32_t)H * 2u);
     const bool in_wr = row < E && row < r_end, in_g = row == E && row < r_end;
     const uint32_t aoff = (uint32_t)row * (uint32_t)H * 2u;
-    uint32_t xoff[4];
+    uint32_t xoff[NT];
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
+    for (int nt = 0; nt < NT; ++nt) {
         const int t = tok0 + 16 * nt + r;
         xoff[nt] = t < T ? (uint32_t)t * (uint32_t)H * 2u : OOB;
     }
     // this wave's K range: chunks of 128 dealt round-robin
-    auto load = [&](int k0, uint4 (&av)[4], uint4 (&bv)[4][4]) {
+    auto load = [&](int k0, uint4 (&av)[4], uint4 (&bv)[4][NT]) {
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
             const uint32_t kb = (uint32_t)(k0 + 32 * s + 8 * q) * 2u;
@@ -266,33 +267,33 @@ __global__ __launch_bounds__(256) void k_router_mfma(const uint16_t *__restrict_
             const uint4 v = ld128(gb, (in_g && kv) ? kb : OOB);
             av[s] = make_uint4(u.x | v.x, u.y | v.y, u.z | v.z, u.w | v.w);
 #pragma unroll
-            for (int nt = 0; nt < 4; ++nt) bv[s][nt] = ld128(xb, (kv && xoff[nt] != OOB) ? xoff[nt] + kb : OOB);
+            for (int nt = 0; nt < NT; ++nt) bv[s][nt] = ld128(xb, (kv && xoff[nt] != OOB) ? xoff[nt] + kb : OOB);
         }
     };
-    f32x4 acc[4];
+    f32x4 acc[NT];
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    uint4 av[4], bv[4][4];
+    for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    uint4 av[4], bv[4][NT];
     int k0 = 128 * wv;
     load(k0 < H ? k0 : -1, av, bv);
     for (; k0 < H; k0 += 512) {
-        uint4 ac[4], bc[4][4];
+        uint4 ac[4], bc[4][NT];
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
             ac[s] = av[s];
 #pragma unroll
-            for (int nt = 0; nt < 4; ++nt) bc[s][nt] = bv[s][nt];
+            for (int nt = 0; nt < NT; ++nt) bc[s][nt] = bv[s][nt];
         }
         if (k0 + 512 < H) load(k0 + 512, av, bv);
 #pragma unroll
         for (int s = 0; s < 4; ++s)
 #pragma unroll
-            for (int nt = 0; nt < 4; ++nt)
+            for (int nt = 0; nt < NT; ++nt)
                 acc[nt] = mfma16x16x32(__builtin_bit_cast(bf16x8, ac[s]), __builtin_bit_cast(bf16x8, bc[s][nt]), acc[nt]);
     }
     if (wv > 0) {
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt)
+        for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
             for (int j = 0; j < 4; ++j) red[wv - 1][nt * 4 + j][lane] = acc[nt][j];
     }
@@ -300,7 +301,7 @@ __global__ __launch_bounds__(256) void k_router_mfma(const uint16_t *__restrict_
     if (wv == 0) {
         // lane holds rows 4q + j, token column r of each tile
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt) {
+        for (int nt = 0; nt < NT; ++nt) {
             const int t = tok0 + 16 * nt + r;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
@@ -810,6 +811,9 @@ constexpr int MAX_TOKENS = 16384;
 #ifndef W4_MULTI_ROUTE_MIN_T
 #define W4_MULTI_ROUTE_MIN_T (1 << 30)  // smaller batches than this (and <= 4096 pairs) group in one block
 #endif
+#ifndef W4_RMFMA_NT
+#define W4_RMFMA_NT 4  // 16-token column tiles per block of the MFMA router
+#endif
 #ifndef W4_ROUTER_MFMA_MIN_T
 // batches of at least this many tokens run the router on MFMA (measured at the
 // 35B-A3B shape: the MFMA router ~12.3 us from T = 64 to 512, the per-row VALU
@@ -941,9 +945,9 @@ int check_layer(const moe_w4a16_layer *Lr, int64_t T, MoEPlan &p) {
         if (p.mx) {  // x as MXFP8: codes [T][H], then scales [T][H/32]
             p.off_xq = off; off = align_up(off + (size_t)T * H + (size_t)T * (H / 32), 256);
         }
-        if (p.multi) {  // e_of [P], off_e [E], cntb [nblk][E], column tiles [2][Gmax + P/64]
+        if (p.multi) {  // e_of [P], off_e [E], cntb [nblk][E], column tiles [2][Gmax + P/64 + 1], cbase [nblk][E]
             p.off_route = off;
-            off = align_up(off + ((size_t)p.P + (size_t)E + (size_t)p.nblk * (size_t)E +
+            off = align_up(off + ((size_t)p.P + (size_t)E + 2 * (size_t)p.nblk * (size_t)E +
                                   2 * ((size_t)p.Gmax + (size_t)p.P / 64 + 1)) * 4, 256);
         }
     }
@@ -956,7 +960,8 @@ int launch_router(const moe_w4a16_layer *Lr, const MoEPlan &p, const uint16_t *x
     const int nrows = r_end - r_begin;
     if (nrows <= 0) return W4_OK;
     if (p.T >= W4_ROUTER_MFMA_MIN_T) {
-        go(st, k_router_mfma, dim3((unsigned)((p.T + 63) / 64), (unsigned)((nrows + 15) / 16)), dim3(256), 0,
+        go(st, k_router_mfma<W4_RMFMA_NT>, dim3((unsigned)((p.T + 16 * W4_RMFMA_NT - 1) / (16 * W4_RMFMA_NT)),
+                                             (unsigned)((nrows + 15) / 16)), dim3(256), 0,
            Lr->router_w, Lr->shared_gate_w, x, logits, p.E, p.H, p.T, r_begin, r_end, p.lstride, arrive);
         return W4_OK;
     }
@@ -1252,6 +1257,7 @@ int run_grouped(const moe_w4a16_layer *Lr, const MoEPlan &p, const uint16_t *x, 
         int32_t *rb = (int32_t *)(wsb + p.off_route);
         r.e_of = rb, r.off_e = rb + p.P, r.cntb = rb + p.P + p.E, r.nblk = p.nblk, r.tpb = p.tpb;
         r.ctg = r.cntb + (size_t)p.nblk * p.E;
+        r.cbase = r.ctg + 2 * ((size_t)p.Gmax + (size_t)p.P / 64 + 1);
         hipEvent_t e6[6];
         for (int i = 0; i < 6; ++i) e6[i] = ev(next_ev + i);
         launch_route_multi(r, sm, events ? e6 : nullptr);

@@ -84,8 +84,8 @@ def _ws_layout(shape, T):
     off = up(off + rows * I * 4)
     off = up(off + rows * H * 4)
     total = up(off + T * H + T * (H // 32))
-    if P > 4096:  # grouping over three launches: pair experts, list starts, block histograms, column tiles
-        total = up(total + (P + E + (T + 15) // 16 * E + 2 * (min(E, P) + P // 64 + 1)) * 4)
+    if P > 4096:  # three-launch grouping: pair experts, list starts, block histograms, column tiles, block bases
+        total = up(total + (P + E + 2 * ((T + 15) // 16) * E + 2 * (min(E, P) + P // 64 + 1)) * 4)
     return off_h, off, total
 
 
