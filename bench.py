@@ -453,7 +453,7 @@ def default_layout(workload):
 ROUTER_MFMA_MIN_T = 160  # the library runs the router as an MFMA GEMM from this batch size
 
 
-LARGE_BATCH_PAIRS = 4096  # past this many (token, slot) pairs the grouped GEMM kernels run
+LARGE_BATCH_PAIRS = 1024  # past this many (token, slot) pairs the grouped GEMM kernels run
 
 
 def stage_names(n_stages, T, K, mx, decode=False):

@@ -812,7 +812,10 @@ constexpr int MAX_TOKENS = 16384;
 #define W4_MULTI_ROUTE_MIN_T (1 << 30)  // smaller batches than this (and <= 4096 pairs) group in one block
 #endif
 #ifndef W4_RMFMA_NT
-#define W4_RMFMA_NT 4  // 16-token column tiles per block of the MFMA router
+#define W4_RMFMA_NT 2  // 16-token column tiles per block of the MFMA router
+#endif
+#ifndef W4_PF_MIN_PAIRS
+#define W4_PF_MIN_PAIRS 1024  // batches of more pairs run W13 / W2 as LDS-staged grouped GEMMs (<= 4096: one-block grouping's limit)
 #endif
 #ifndef W4_ROUTER_MFMA_MIN_T
 // batches of at least this many tokens run the router on MFMA (measured at the
@@ -831,7 +834,7 @@ struct MoEPlan {
     int L13, L2, hstride, lstride;
     bool grouped, mx;
     bool multi;  // grouping over three launches (large batches, or T >= W4_MULTI_ROUTE_MIN_T)
-    bool pf;     // W13 / W2 as large-batch grouped GEMMs (more than MAX_ONE_BLOCK_PAIRS pairs)
+    bool pf;     // W13 / W2 as large-batch grouped GEMMs (more than W4_PF_MIN_PAIRS pairs)
     bool dec;    // K-tiled down projections: the decode kernels (k_moe_dec + k_moe_dec_combine)
     int P, Gmax, nblk, tpb, tiles16;
     size_t off_part;
@@ -923,7 +926,7 @@ int check_layer(const moe_w4a16_layer *Lr, int64_t T, MoEPlan &p) {
         p.mx = false;
     }
     p.tiles16 = (int)(I / DEC_TILE);
-    p.pf = p.grouped && p.P > MAX_ONE_BLOCK_PAIRS;
+    p.pf = p.grouped && p.P > W4_PF_MIN_PAIRS && fmt != W4_FMT_INT4_F16S128;
     p.multi = p.pf || (p.grouped && T >= W4_MULTI_ROUTE_MIN_T);
     p.tpb = T <= 256 ? 4 : ROUTE_MAX_TPB;  // one token per wave while that keeps the scan short
     p.nblk = (int)((T + p.tpb - 1) / p.tpb);

@@ -1,6 +1,7 @@
 """GPU parity at the edges of the supported ranges: the largest expert count and
 top-k, hidden sizes off the 128 grid (single-token path), int4 experts, the
-largest grouped batch (T k = 4096 pairs) and the largest token count."""
+largest batches of the two grouping paths (T k = 1024 and 4096 pairs) and the
+largest token count."""
 
 import numpy as np
 import pytest
@@ -55,15 +56,17 @@ def test_edge_layers(shape, Ts):
         _check(shape, dev_layer, or_layer, tie_free_tokens(shape, or_layer, T, first=11 * T), f"{shape.name} T={T}")
 
 
-def test_largest_grouped_batch():
-    """T k = 4096 (token, slot) pairs, the largest batch one block groups; groups
-    of ~64 rows run several 32-column MFMA passes."""
-    shape = synth.MoEShape("edge-pairs4096", 256, 128, 64, 8, 128, 512, 0.0, 6)
+@pytest.mark.parametrize("T,stages", [(128, 5), (512, 7)])
+def test_largest_grouped_batches(T, stages):
+    """T k = 1024 (token, slot) pairs, the largest batch of the one-launch
+    grouping and the per-group MFMA kernels, and T k = 4096 on the three-launch
+    grouping and the large-batch kernels (groups of ~64 rows)."""
+    shape = synth.MoEShape("edge-pairs", 256, 128, 64, 8, 128, T, 0.0, 6)
     dev_layer = wl.build_moe_layer(shape, device=DEV)
-    assert w4.moe_w4a16_stage_count(dev_layer, 512) == 5
+    assert w4.moe_w4a16_stage_count(dev_layer, T) == stages
     or_layer = oracle_layer(shape)
-    print("pairs 4096", flush=True)
-    _check(shape, dev_layer, or_layer, tie_free_tokens(shape, or_layer, 512), "T=512 k=8")
+    print(f"pairs {8 * T}", flush=True)
+    _check(shape, dev_layer, or_layer, tie_free_tokens(shape, or_layer, T), f"T={T} k=8")
 
 
 def test_largest_token_count_sampled():

@@ -68,7 +68,7 @@ def _ws_layout(shape, T):
     fp32, ids and weights [T][k], group table, the ranking's arrival counter,
     pair list, h (codes [P+T][I] then
     E8M0 scales [P+T][I/32]), expert outputs fp32 [P+T][H], x codes [T][H] then
-    scales [T][H/32], and past 4096 pairs the multi-launch grouping's arrays."""
+    scales [T][H/32], and past 1024 pairs the multi-launch grouping's arrays."""
     def up(v):
         return (v + 255) // 256 * 256
     H, I, E, K = shape.hidden, shape.inter, shape.num_experts, shape.top_k
@@ -84,8 +84,9 @@ def _ws_layout(shape, T):
     off = up(off + rows * I * 4)
     off = up(off + rows * H * 4)
     total = up(off + T * H + T * (H // 32))
-    if P > 4096:  # three-launch grouping: pair experts, list starts, block histograms, column tiles, block bases
-        total = up(total + (P + E + 2 * ((T + 15) // 16) * E + 2 * (min(E, P) + P // 64 + 1)) * 4)
+    if P > 1024:  # three-launch grouping: pair experts, list starts, block histograms, column tiles, block bases
+        tpb = 4 if T <= 256 else 16  # tokens per grouping block
+        total = up(total + (P + E + 2 * ((T + tpb - 1) // tpb) * E + 2 * (min(E, P) + P // 64 + 1)) * 4)
     return off_h, off, total
 
 
@@ -273,7 +274,7 @@ def test_mx_full_t32_sampled(full_mx):
 
 
 def test_mx_full_t512_sampled(full_mx):
-    # 512 tokens x top-8 = 4096 pairs (the largest grouped call); 8 tokens checked
+    # 512 tokens x top-8 = 4096 pairs (three-launch grouping, large-batch kernels); 8 tokens checked
     shape, dev_layer, or_layer = full_mx
     print("mx full T=512 (sampled)", flush=True)
     xb = tie_free_tokens(shape, or_layer, 512, first=1000)

@@ -295,18 +295,18 @@ def test_moe_bf16_shared_expert(shape):
         print(f"bf16 shared token {t}", flush=True)
         print(_check_moe(shape, dev_layer, or_layer, tie_free_tokens(shape, or_layer, 1, first=t), f"{shape.name} t={t}"),
               flush=True)
-    # batches of up to 4096 pairs run grouped, the shared expert's bf16 rows as MFMA operands
+    # batches run grouped, the shared expert's bf16 rows as MFMA operands
     assert w4.moe_w4a16_stage_count(dev_layer, 6) == 5
     _check_moe(shape, dev_layer, or_layer, tie_free_tokens(shape, or_layer, 6, first=40), f"{shape.name} T=6")
 
 
 def test_moe_bf16_shared_expert_batches():
     """Tiny layer: grouped batches (the shared expert a bf16 MFMA group of T
-    rows), past 4096 pairs with the three-launch grouping."""
+    rows), past 1024 pairs with the three-launch grouping."""
     shape = synth.TINY_MOE_BF16SH
     dev_layer = wl.build_moe_layer(shape, device=DEV)
     or_layer = oracle_layer(shape)
-    for T, stages in ((300, 5), (2048, 5), (2049, 7)):  # top-2: 4096 pairs at T = 2048
+    for T, stages in ((300, 5), (512, 5), (513, 7), (2049, 7)):  # top-2: 1024 pairs at T = 512
         print(f"bf16 shared tiny T={T}", flush=True)
         assert w4.moe_w4a16_stage_count(dev_layer, T) == stages, T
         _check_moe(shape, dev_layer, or_layer, tie_free_tokens(shape, or_layer, T, first=500), f"bf16 shared T={T}")

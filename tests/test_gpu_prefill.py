@@ -1,4 +1,4 @@
-"""GPU parity of prefill-sized batches (more than 4096 (token, slot) pairs): the
+"""GPU parity of prefill-sized batches (more than 1024 (token, slot) pairs): the
 router as an MFMA GEMM, the grouping over three launches (per-block top-k and
 expert histograms, one scan, a scatter), and the grouped expert kernels with
 groups of hundreds of rows.  Routing ids are compared for every token; outputs

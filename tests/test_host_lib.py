@@ -198,9 +198,9 @@ def test_mxfp4_layer_plan_and_validation():
     # router, x -> MXFP8, grouping, W13, W2, combine
     assert [w4.lib().moe_w4a16_stage_count(C.byref(L), T) for T in (1, 2, 3, 4, 64)] == [3, 3, 3, 6, 6]
     assert w4.lib().moe_w4a16_workspace_bytes(C.byref(L), 1) > 0
-    # more than 4096 pairs group over three launches: 2 more stages
-    assert w4.lib().moe_w4a16_stage_count(C.byref(L), 2048) == 6
-    assert w4.lib().moe_w4a16_stage_count(C.byref(L), 2049) == 8
+    # more than 1024 pairs group over three launches: 2 more stages
+    assert w4.lib().moe_w4a16_stage_count(C.byref(L), 512) == 6
+    assert w4.lib().moe_w4a16_stage_count(C.byref(L), 513) == 8
     # at most 65536 pairs per call, at most 16384 tokens
     L8 = mxl(top_k=8)
     assert w4.lib().moe_w4a16_workspace_bytes(C.byref(L8), 8192) > 0
@@ -215,10 +215,10 @@ def test_mxfp4_layer_plan_and_validation():
     assert _fwd(mxl(shared_w13=_mat(fmt=bf, groups=1, n=2 * I, k=H, scales=None),
                     shared_w2=_mat(fmt=bf, groups=1, n=H, k=I, scales=None)), ws_bytes=1 << 30) == w4.W4_ERR_UNSUPPORTED
     assert _fwd(mxl(w2=_mat(groups=E, n=H, k=I)), ws_bytes=1 << 30) == w4.W4_ERR_LAYOUT
-    # E2M1: batched path from T = 4, three grouping launches past 4096 pairs;
+    # E2M1: batched path from T = 4, three grouping launches past 1024 pairs;
     # past 65536 pairs the single-token path
     E2 = _layer(top_k=8)
-    assert [w4.lib().moe_w4a16_stage_count(C.byref(E2), T) for T in (3, 4, 512, 513, 8192, 8193)] == [3, 5, 5, 7, 7, 3]
+    assert [w4.lib().moe_w4a16_stage_count(C.byref(E2), T) for T in (3, 4, 128, 129, 8192, 8193)] == [3, 5, 5, 7, 7, 3]
     # the timed entry point wants 12 events on the grouped MX path
     ev = (C.c_void_p * 10)(*([1] * 10))
     st = w4.lib().moe_w4a16_forward_timed(C.byref(L), 1 << 20, 4, 1 << 21, None, None, 1 << 24,
@@ -228,14 +228,14 @@ def test_mxfp4_layer_plan_and_validation():
 
 def test_bf16_shared_expert_plan():
     """A bf16 shared expert joins the grouped path (its rows are MFMA operands
-    there), past 4096 (token, slot) pairs with the three-launch grouping."""
+    there), past 1024 (token, slot) pairs with the three-launch grouping."""
     bf = w4.W4_FMT_BF16
     for fmt in (w4.W4_FMT_E2M1_F16S16, w4.W4_FMT_NVFP4_E4M3S16):
         g = 1 << 22 if fmt == w4.W4_FMT_NVFP4_E4M3S16 else None
         L = _layer(w13=_mat(fmt=fmt, groups=8, n=256, k=256, gsc=g), w2=_mat(fmt=fmt, groups=8, n=256, k=128, gsc=g),
                    shared_w13=_mat(fmt=bf, groups=1, n=256, k=256, scales=None),
                    shared_w2=_mat(fmt=bf, groups=1, n=256, k=128, scales=None))
-        got = [w4.lib().moe_w4a16_stage_count(C.byref(L), T) for T in (1, 3, 4, 2048, 2049, 16384)]
+        got = [w4.lib().moe_w4a16_stage_count(C.byref(L), T) for T in (1, 3, 4, 512, 513, 16384)]
         assert got == [3, 3, 5, 5, 7, 7], (fmt, got)
 
 
