@@ -446,9 +446,14 @@ LAYOUTS = {"canonical": (0, 0), "gfx950": (1, 1), "decode": (1, 2)}
 DECODE_DEFAULT = ()  # workloads measured with K-tiled down projections by default
 
 
+CANONICAL_DEFAULT = ("qwen-prefill", "qwen-prefill-mxfp4")  # measured faster in the canonical layout
+
+
 def default_layout(workload):
     """The layout each workload is measured in unless --layout says otherwise."""
-    return "decode" if workload in DECODE_DEFAULT else "gfx950"
+    if workload in DECODE_DEFAULT:
+        return "decode"
+    return "canonical" if workload in CANONICAL_DEFAULT else "gfx950"
 
 ROUTER_MFMA_MIN_T = 160  # the library runs the router as an MFMA GEMM from this batch size
 
