@@ -653,6 +653,9 @@ def run_moe(args, torch, w4, wl, synth, hip):
     if args.tokens:  # the same layer at another batch size (sweeps; not a reported workload)
         import dataclasses
         shape = dataclasses.replace(shape, tokens=args.tokens, name=f"{shape.name}@T{args.tokens}")
+    if args.seed is not None:  # other synthetic weights and tokens of the same shape
+        import dataclasses
+        shape = dataclasses.replace(shape, seed=args.seed)
     T = shape.tokens
     l13, l2 = LAYOUTS[args.layout]
     base = wl.build_moe_layer(shape, device="cuda", layout=l13, w2_layout=l2)
@@ -788,7 +791,7 @@ def run_moe(args, torch, w4, wl, synth, hip):
         "config": {
             "workload": shape.name, "hidden": shape.hidden, "experts": shape.num_experts,
             "top_k": shape.top_k, "inter": shape.inter, "shared_inter": shape.shared_inter,
-            "tokens_per_step": T, "zipf_s": shape.zipf_s, "weights": {"e2m1": "E2M1 codes + FP16 scale per 16",
+            "tokens_per_step": T, "zipf_s": shape.zipf_s, "seed": shape.seed, "weights": {"e2m1": "E2M1 codes + FP16 scale per 16",
                         "nvfp4": "E2M1 codes + UE4M3 scale per 16 + fp32 scale per matrix",
                         "int4": "int4 codes + FP16 scale per 128",
                         "mxfp4": "E2M1 codes + E8M0 scale per 32"}[shape.fmt]
@@ -833,6 +836,9 @@ def timed_replay_ms(torch, g):
 
 def run_gemv(args, torch, w4, wl, synth, hip):
     shape = workload_shapes(synth)[args.workload]
+    if args.seed is not None:
+        import dataclasses
+        shape = dataclasses.replace(shape, seed=args.seed)
     print(f"[bench] building {shape.name} ({args.replicas} replicas)", file=sys.stderr, flush=True)
     if args.layout == "decode":
         raise SystemExit("the dense GEMV reads row layouts (canonical or gfx950)")
@@ -866,7 +872,7 @@ def run_gemv(args, torch, w4, wl, synth, hip):
         "metric": METRIC, "value": ms_step * 1e3, "unit": "us/call", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": False, "scaling": "weak",
         "vs_baseline": None, "dtype": "f32", "data": "synthetic",
-        "config": {"workload": shape.name, "n": shape.n, "k": shape.k, "format": shape.fmt,
+        "config": {"workload": shape.name, "n": shape.n, "k": shape.k, "format": shape.fmt, "seed": shape.seed,
                    "replicas": R, "weight_layout": args.layout, "timing": "HIP graph replay of the K steps"},
         "hbm_gbps": gbs, "pct_hbm_peak": 100 * gbs / HBM_PEAK_GBS, "algorithmic_bytes_per_step": g_bytes,
         "wall_s_timed": t_wall,
@@ -894,6 +900,7 @@ def main():
     ap.add_argument("--pool", type=int, default=64, help="token pool (MoE workloads)")
     ap.add_argument("--cpu-tokens", type=int, default=1)
     ap.add_argument("--tokens", type=int, default=0, help="MoE workloads: tokens per step instead of the workload's")
+    ap.add_argument("--seed", type=int, default=None, help="seed of the synthetic weights and inputs (default: the workload's)")
     ap.add_argument("--cpu-reps", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
