@@ -99,3 +99,18 @@ def test_decode_stage_names_and_bytes(name):
     assert sb["k_moe_dec"] >= shape.top_k * (bench.weight_bytes(shape.fmt, 2 * shape.inter, shape.hidden)
                                             + bench.weight_bytes(shape.fmt, shape.hidden, shape.inter))
     assert bench.default_layout(name) in ("decode", "gfx950", "canonical")
+
+
+@pytest.mark.parametrize("T", [4, 32, 128, 129, 159, 160, 512, 2048])
+def test_stage_names_follow_the_library_thresholds(T):
+    """bench.py names each stage from its copies of the library's thresholds
+    (large-batch kernels past 1024 pairs, MFMA router from 160 tokens); the
+    library's own stage count must agree with them at every batch size."""
+    import dataclasses
+    shape = dataclasses.replace(synth.QWEN_MOE_T32, tokens=T)
+    n = w4.lib().moe_w4a16_stage_count(C.byref(_desc(shape)), T)
+    names = bench.stage_names(n, T, shape.top_k, False)
+    assert len(names) == n == (7 if T * shape.top_k > bench.LARGE_BATCH_PAIRS else 5)
+    assert ("k_moe_pf13" in names) == (T * shape.top_k > 1024)
+    assert names[0] == ("k_router_mfma" if T >= 160 else "k_router")
+    assert set(bench.launch_bytes(shape, 8.0, n)) == set(names)
