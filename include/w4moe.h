@@ -298,7 +298,9 @@ size_t moe_w4a16_workspace_bytes(const moe_w4a16_layer *L, int64_t T);
  *   x: device bf16 [T][H] (16-byte aligned);  y: device bf16 [T][H].
  *   topk_ids: device int32 [T][k] or NULL;  topk_w: device fp32 [T][k] or NULL.
  *   ws: device workspace of at least moe_w4a16_workspace_bytes(L, T), 256-byte
- *   aligned.
+ *   aligned; its contents need no initialisation (the launches write every
+ *   intermediate, including the ranking's arrival counter, before reading it),
+ *   and two calls in flight at once must not share it.
  * Errors: W4_ERR_INVALID_ARG, _LAYOUT, _ALIGNMENT, _UNSUPPORTED, _WORKSPACE, _HIP. */
 int moe_w4a16_forward(const moe_w4a16_layer *L, const uint16_t *x, int64_t T, uint16_t *y,
                       int32_t *topk_ids, float *topk_w, void *ws, size_t ws_bytes, void *stream);
