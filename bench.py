@@ -36,6 +36,7 @@ import ctypes as C
 import hashlib
 import json
 import os
+import shutil
 import sys
 import time
 
@@ -198,8 +199,21 @@ def machine_info(hip):
             info["rocm"] = f.read().strip()
     except OSError:
         info["rocm"] = None
+    # Under a profiler the child would inherit the profiler's preloaded library,
+    # which opens the GPU before rocm-smi's "#!/usr/bin/env python3" line execs
+    # the interpreter: such a run does not sample the clocks.  Otherwise the
+    # script runs under this interpreter directly (no exec hop inside the child).
+    if any(k.startswith("ROCPROF") for k in os.environ) or "rocprof" in os.environ.get("LD_PRELOAD", ""):
+        info["clocks"] = "not sampled under a profiler"
+        return info
     try:
-        r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True, timeout=30)
+        smi = shutil.which("rocm-smi")
+        if smi is None:
+            raise FileNotFoundError("rocm-smi")
+        with open(smi, "rb") as f:
+            python_script = b"python" in f.readline()
+        cmd = ([sys.executable, smi] if python_script else [smi]) + ["--showclocks", "--json"]
+        r = subprocess.run(cmd, capture_output=True, text=True, timeout=30)
         clk = json.loads(r.stdout) if r.returncode == 0 else None
         if isinstance(clk, dict) and clk:
             card = clk[sorted(clk)[0]]

@@ -995,7 +995,7 @@ int launch_router(const moe_w4a16_layer *Lr, const MoEPlan &p, const uint16_t *x
 #define W4_W13_ROWS 2  // gate rows (and as many up rows) per wave of the W13 kernel
 #endif
 #ifndef W4_W13_WPB
-#define W4_W13_WPB 4  // waves per block of the W13 kernel
+#define W4_W13_WPB 2  // waves per block of the W13 kernel
 #endif
 static_assert(W4_W13_WPB >= 1 && W4_W13_WPB <= 16, "k_moe_w13 is compiled for blocks of at most 1024 threads");
 
