@@ -441,6 +441,12 @@ __device__ __forceinline__ void gw13_unit(const GW13Args &a, int gs, int tile, f
             constexpr bool SBF = decltype(SBFc)::value;
             // ---- MFMA: 16 gate + 16 up rows x 16-token column tiles; the 128-wide K
             // chunks are dealt round-robin to the 4 waves and summed in wave order.
+            // The weights are the A operand (lane (r, q) = (lane % 16, lane / 16)
+            // ends with rows 4q .. 4q + 3 of its column token r), except for int4
+            // codes: there the activations are A and the codes B, so the lane ends
+            // with tokens 4q .. 4q + 3 of the one row r and needs one group scale
+            // instead of four.
+            constexpr bool TR = FMT == FMT_INT4 && !SBF;
             const int r = lane & 15, q = lane >> 4;
             const bool rg_ok = i0 + r < I;
             const uint32_t rowg = (uint32_t)(i0 + r), rowu = (uint32_t)(I + i0 + r);
@@ -515,15 +521,9 @@ __device__ __forceinline__ void gw13_unit(const GW13Args &a, int gs, int tile, f
                         if constexpr (FMT == FMT_INT4) {
                             // the chunk is one scale group: MFMAs on the raw offset codes
                             // u = q + 8 (exact bf16) and on 8 (the offset), then the
-                            // difference times the scales of the lane's output rows
-                            float so_g[4], so_u[4];
-#pragma unroll
-                            for (int j = 0; j < 4; ++j) {
-                                const uint32_t o = (uint32_t)(i0 + 4 * q + j);
-                                const bool ov = o < (uint32_t)I;
-                                so_g[j] = f16_bits_to_f32(ld16(sb, ov ? o * ss + (uint32_t)c * 2u : OOB));
-                                so_u[j] = f16_bits_to_f32(ld16(sb, ov ? ((uint32_t)I + o) * ss + (uint32_t)c * 2u : OOB));
-                            }
+                            // difference times the scale of the lane's row
+                            const float so_g = f16_bits_to_f32(ld16(sb, rg_ok ? rowg * ss + (uint32_t)c * 2u : OOB));
+                            const float so_u = f16_bits_to_f32(ld16(sb, rg_ok ? rowu * ss + (uint32_t)c * 2u : OOB));
                             const uint32_t cgw[4] = {cg.x, cg.y, cg.z, cg.w}, cuw[4] = {cu.x, cu.y, cu.z, cu.w};
                             f32x4 tg[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}}, tu[2] = {tg[0], tg[0]},
                                   tc[2] = {tg[0], tg[0]};
@@ -538,17 +538,17 @@ __device__ __forceinline__ void gw13_unit(const GW13Args &a, int gs, int tile, f
 #pragma unroll
                                 for (int nt = 0; nt < 2; ++nt) {
                                     const bf16x8 b = __builtin_bit_cast(bf16x8, xb[nt][s]);
-                                    tg[nt] = mfma16x16x32(ug, b, tg[nt]);
-                                    tu[nt] = mfma16x16x32(uu, b, tu[nt]);
-                                    tc[nt] = mfma16x16x32(bf16x8_splat8(), b, tc[nt]);
+                                    tg[nt] = mfma16x16x32(b, ug, tg[nt]);
+                                    tu[nt] = mfma16x16x32(b, uu, tu[nt]);
+                                    tc[nt] = mfma16x16x32(b, bf16x8_splat8(), tc[nt]);
                                 }
                             }
 #pragma unroll
                             for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
                                 for (int j = 0; j < 4; ++j) {
-                                    ag[nt][j] = fmaf(so_g[j], tg[nt][j] - tc[nt][j], ag[nt][j]);
-                                    au[nt][j] = fmaf(so_u[j], tu[nt][j] - tc[nt][j], au[nt][j]);
+                                    ag[nt][j] = fmaf(so_g, tg[nt][j] - tc[nt][j], ag[nt][j]);
+                                    au[nt][j] = fmaf(so_u, tu[nt][j] - tc[nt][j], au[nt][j]);
                                 }
                             continue;
                         }
@@ -608,28 +608,47 @@ __device__ __forceinline__ void gw13_unit(const GW13Args &a, int gs, int tile, f
                                 ag[nt][j] += red[w][nt * 8 + j][lane];
                                 au[nt][j] += red[w][nt * 8 + 4 + j][lane];
                             }
-                    // lane holds rows i0 + 4q + j of column r
+                    if constexpr (TR) {
+                        // lane holds tokens 4q + j of each column tile for row i0 + r;
+                        // the pair of column c was read by lane c
 #pragma unroll
-                    for (int nt = 0; nt < 2; ++nt) {
-                        const int idx = n0 + nt * 16 + r;
-                        if (idx < gv.m) {
-                            const int p = plist[idx];
-                            float hv[4];
+                        for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
                             for (int j = 0; j < 4; ++j) {
-                                float gg = ag[nt][j], uu = au[nt][j];
-                                if constexpr (FMT == FMT_NVFP4) gg *= gsc, uu *= gsc;
-                                hv[j] = (gg / (1.f + expf(-gg))) * uu;
+                                const int p = __shfl(pr[nt], 4 * q + j, 64);
+                                if (rg_ok && n0 + nt * 16 + 4 * q + j < gv.m) {
+                                    const float gg = ag[nt][j], uu = au[nt][j];
+                                    uint16_t bh, bl;
+                                    split_bf16((gg / (1.f + expf(-gg))) * uu, bh, bl);
+                                    const size_t o = (size_t)p * I + rowg;
+                                    a.h_hi[o] = bh;
+                                    a.h_lo[o] = bl;
+                                }
                             }
-                            // I is a multiple of 128 (host check): rows i0 + 4q .. +3 all exist
-                            uint16_t bh[4], bl[4];
+                    } else {
+                        // lane holds rows i0 + 4q + j of column r
 #pragma unroll
-                            for (int j = 0; j < 4; ++j) split_bf16(hv[j], bh[j], bl[j]);
-                            const size_t o = (size_t)p * I + i0 + 4 * q;
-                            *reinterpret_cast<uint2 *>(a.h_hi + o) =
-                                make_uint2(bh[0] | ((uint32_t)bh[1] << 16), bh[2] | ((uint32_t)bh[3] << 16));
-                            *reinterpret_cast<uint2 *>(a.h_lo + o) =
-                                make_uint2(bl[0] | ((uint32_t)bl[1] << 16), bl[2] | ((uint32_t)bl[3] << 16));
+                        for (int nt = 0; nt < 2; ++nt) {
+                            const int idx = n0 + nt * 16 + r;
+                            if (idx < gv.m) {
+                                const int p = plist[idx];
+                                float hv[4];
+#pragma unroll
+                                for (int j = 0; j < 4; ++j) {
+                                    float gg = ag[nt][j], uu = au[nt][j];
+                                    if constexpr (FMT == FMT_NVFP4) gg *= gsc, uu *= gsc;
+                                    hv[j] = (gg / (1.f + expf(-gg))) * uu;
+                                }
+                                // I is a multiple of 128 (host check): rows i0 + 4q .. +3 all exist
+                                uint16_t bh[4], bl[4];
+#pragma unroll
+                                for (int j = 0; j < 4; ++j) split_bf16(hv[j], bh[j], bl[j]);
+                                const size_t o = (size_t)p * I + i0 + 4 * q;
+                                *reinterpret_cast<uint2 *>(a.h_hi + o) =
+                                    make_uint2(bh[0] | ((uint32_t)bh[1] << 16), bh[2] | ((uint32_t)bh[3] << 16));
+                                *reinterpret_cast<uint2 *>(a.h_lo + o) =
+                                    make_uint2(bl[0] | ((uint32_t)bl[1] << 16), bl[2] | ((uint32_t)bl[3] << 16));
+                            }
                         }
                     }
                 }
@@ -754,6 +773,9 @@ __device__ __forceinline__ void gw2_unit(const GW2Args &a, int gs, int tile, flo
             // 128-wide K chunks are dealt round-robin to the 4 waves, so each h
             // element is read once per unit; each wave multiplies its chunk into all
             // four 16-row tiles, and the partials are summed in wave order via LDS.
+            // int4 codes are the B operand (h is A), so a lane's four sums share
+            // one row and its group scale, as in gw13_unit.
+            constexpr bool TR = FMT == FMT_INT4 && !SBF;
             const int r = lane & 15, q = lane >> 4;
             const int nchunks = I >> 7;
             const int u0 = tile * 64;  // first row of the unit
@@ -821,17 +843,13 @@ __device__ __forceinline__ void gw2_unit(const GW2Args &a, int gs, int tile, flo
                         for (int s = 0; s < 4; ++s)
 #pragma unroll
                             for (int nt = 0; nt < 2; ++nt) {  // both tiles: no branch before the reads below
-                                tcor[nt] = mfma16x16x32(bf16x8_splat8(), __builtin_bit_cast(bf16x8, bh[nt][s]), tcor[nt]);
-                                tcor[nt] = mfma16x16x32(bf16x8_splat8(), __builtin_bit_cast(bf16x8, bl[nt][s]), tcor[nt]);
+                                tcor[nt] = mfma16x16x32(__builtin_bit_cast(bf16x8, bh[nt][s]), bf16x8_splat8(), tcor[nt]);
+                                tcor[nt] = mfma16x16x32(__builtin_bit_cast(bf16x8, bl[nt][s]), bf16x8_splat8(), tcor[nt]);
                             }
 #pragma unroll
                         for (int rt = 0; rt < 4; ++rt) {
-                            float so[4];
-#pragma unroll
-                            for (int j = 0; j < 4; ++j) {
-                                const uint32_t o = (uint32_t)(u0 + 16 * rt + 4 * q + j);
-                                so[j] = f16_bits_to_f32(ld16(sb, o < (uint32_t)H ? o * ss + (uint32_t)c * 2u : OOB));
-                            }
+                            const uint32_t o = (uint32_t)(u0 + 16 * rt + r);  // the lane's row
+                            const float so = f16_bits_to_f32(ld16(sb, o < (uint32_t)H ? o * ss + (uint32_t)c * 2u : OOB));
                             const uint32_t cws[4] = {cw[rt].x, cw[rt].y, cw[rt].z, cw[rt].w};
                             f32x4 t[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
@@ -839,15 +857,15 @@ __device__ __forceinline__ void gw2_unit(const GW2Args &a, int gs, int tile, flo
                                 const bf16x8 u = u4x8_bf16(cws[s]);
 #pragma unroll
                                 for (int nt = 0; nt < 2; ++nt) {
-                                    t[nt] = mfma16x16x32(u, __builtin_bit_cast(bf16x8, bh[nt][s]), t[nt]);
-                                    t[nt] = mfma16x16x32(u, __builtin_bit_cast(bf16x8, bl[nt][s]), t[nt]);
+                                    t[nt] = mfma16x16x32(__builtin_bit_cast(bf16x8, bh[nt][s]), u, t[nt]);
+                                    t[nt] = mfma16x16x32(__builtin_bit_cast(bf16x8, bl[nt][s]), u, t[nt]);
                                 }
                             }
 #pragma unroll
                             for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
                                 for (int j = 0; j < 4; ++j)
-                                    acc[rt][nt][j] = fmaf(so[j], t[nt][j] - tcor[nt][j], acc[rt][nt][j]);
+                                    acc[rt][nt][j] = fmaf(so, t[nt][j] - tcor[nt][j], acc[rt][nt][j]);
                         }
                         continue;
                     }
@@ -906,6 +924,19 @@ __device__ __forceinline__ void gw2_unit(const GW2Args &a, int gs, int tile, flo
                         v[nt][j] = t * gsc;
                     }
                 __syncthreads();  // red is reused by the next pass or unit
+                if constexpr (TR) {
+                    // lane holds columns 4q + j of each tile for row u0 + 16wv + r; the
+                    // pair of column c was read by lane c
+                    const int row = u0 + 16 * wv + r;
+#pragma unroll
+                    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) {
+                            const int p = __shfl(pr[nt], 4 * q + j, 64);
+                            if (row < H && n0 + nt * 16 + 4 * q + j < gv.m) a.out[(size_t)p * H + row] = v[nt][j];
+                        }
+                    continue;
+                }
                 // lane holds rows u0 + 16wv + 4q + j of column r
                 const int rb = u0 + 16 * wv + 4 * q;
 #pragma unroll
