@@ -472,11 +472,12 @@ def default_layout(workload):
 ROUTER_MFMA_MIN_T = 160  # the library runs the router as an MFMA GEMM from this batch size
 
 
-LARGE_BATCH_PAIRS = 1024  # past this many (token, slot) pairs the grouped GEMM kernels run
+LARGE_BATCH_PAIRS = 1024  # past this many (token, slot) pairs the grouped GEMM kernels run (not for int4)
 
 
-def stage_names(n_stages, T, K, mx, decode=False):
-    """Kernel names in launch order for the library's stage count at T tokens."""
+def stage_names(n_stages, T, K, mx, decode=False, int4=False):
+    """Kernel names in launch order for the library's stage count at T tokens
+    (int4 experts keep the per-group projection kernels past LARGE_BATCH_PAIRS)."""
     router = "k_router_mfma" if T >= ROUTER_MFMA_MIN_T else "k_router"
     if decode:
         return [router, "k_moe_dec", "k_moe_dec_combine"]
@@ -484,7 +485,7 @@ def stage_names(n_stages, T, K, mx, decode=False):
         return [router, "k_moe_w13", "k_moe_down"]
     grouping = ["k_moe_rank_group"] if n_stages in (5, 6) else ["k_route_topk", "k_route_scan", "k_route_scatter"]
     experts = ["k_mx_quant"] if mx else []
-    large = T * K > LARGE_BATCH_PAIRS
+    large = T * K > LARGE_BATCH_PAIRS and not int4
     if mx:
         proj = ["k_moe_pfmx13", "k_moe_pfmx2"] if large else ["k_moe_mx13", "k_moe_mx2"]
     else:
@@ -497,7 +498,7 @@ def launch_bytes(shape, distinct, n_stages, decode=False):
     sb = stage_bytes(shape, distinct, n_stages, decode)
     if shape.tokens >= ROUTER_MFMA_MIN_T:
         sb["k_router_mfma"] = sb.pop("k_router")
-    if shape.tokens * shape.top_k > LARGE_BATCH_PAIRS:  # the grouped GEMM kernels move the same algorithmic bytes
+    if shape.tokens * shape.top_k > LARGE_BATCH_PAIRS and shape.fmt != "int4":  # the grouped GEMM kernels move the same algorithmic bytes
         for a, b in (("k_moe_gw13", "k_moe_pf13"), ("k_moe_gw2", "k_moe_pf2"), ("k_moe_mx13", "k_moe_pfmx13"),
                      ("k_moe_mx2", "k_moe_pfmx2")):
             if a in sb:
@@ -724,7 +725,7 @@ def run_moe(args, torch, w4, wl, synth, hip):
     # their own copied from the captured one (same kernels, arguments and order)
     n_stages = w4.moe_w4a16_stage_count(base, T)
     decode = l2 == 2
-    names = stage_names(n_stages, T, shape.top_k, shape.fmt == "mxfp4", decode)
+    names = stage_names(n_stages, T, shape.top_k, shape.fmt == "mxfp4", decode, shape.fmt == "int4")
     stage_us, timing_note = {}, ("avg launch duration: the stage's K launches copied out of the captured graph "
                                  "and replayed alone (graph replay time / K), on the stream the kernels run on")
     try:

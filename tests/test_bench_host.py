@@ -41,7 +41,7 @@ def test_stage_names_and_bytes(name):
     T = shape.tokens
     n = w4.lib().moe_w4a16_stage_count(C.byref(_desc(shape)), T)
     assert n in (3, 5, 6, 7, 8), n
-    names = bench.stage_names(n, T, shape.top_k, shape.fmt == "mxfp4")
+    names = bench.stage_names(n, T, shape.top_k, shape.fmt == "mxfp4", int4=shape.fmt == "int4")
     assert len(names) == n
     sb = bench.launch_bytes(shape, 8.0, n)
     assert set(sb) == set(names), (sorted(sb), names)
@@ -113,4 +113,22 @@ def test_stage_names_follow_the_library_thresholds(T):
     assert len(names) == n == (7 if T * shape.top_k > bench.LARGE_BATCH_PAIRS else 5)
     assert ("k_moe_pf13" in names) == (T * shape.top_k > 1024)
     assert names[0] == ("k_router_mfma" if T >= 160 else "k_router")
+    assert set(bench.launch_bytes(shape, 8.0, n)) == set(names)
+
+
+@pytest.mark.parametrize("T", [32, 256, 512, 1024])
+def test_stage_names_int4_batches(T):
+    """int4 experts run the per-group projection kernels up to the one-block
+    grouping limit and the single-token kernels beyond it, never the
+    large-batch GEMM kernels: the bench's names follow the library's count."""
+    import dataclasses
+    shape = dataclasses.replace(synth.QWEN_MOE_T32, tokens=T, fmt="int4", name=f"int4@{T}")
+    n = w4.lib().moe_w4a16_stage_count(C.byref(_desc(shape)), T)
+    names = bench.stage_names(n, T, shape.top_k, False, int4=True)
+    assert len(names) == n
+    assert "k_moe_pf13" not in names and "k_moe_pf2" not in names
+    if T * shape.top_k <= 4096:
+        assert n == 5 and names[2:4] == ["k_moe_gw13", "k_moe_gw2"]
+    else:
+        assert n == 3 and names[1:] == ["k_moe_w13", "k_moe_down"]
     assert set(bench.launch_bytes(shape, 8.0, n)) == set(names)
