@@ -928,7 +928,7 @@ def main():
         ingest_counters(args.ingest_counters, workload_shapes(synth)[args.workload].name)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1).", file=sys.stderr)
+        print("bench.py measures one GPU: the library has no multi-GPU path (run with --gpus 1).", file=sys.stderr)
         sys.exit(2)
     if args.layout is None:
         args.layout = default_layout(args.workload)

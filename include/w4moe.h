@@ -56,7 +56,7 @@ extern "C" {
 #define W4_ERR_INVALID_ARG (-1)   /* null pointer, bad size or count            */
 #define W4_ERR_LAYOUT (-2)        /* unknown format or layout tag, or mismatch  */
 #define W4_ERR_ALIGNMENT (-3)     /* pointer not aligned as documented          */
-#define W4_ERR_UNSUPPORTED (-4)   /* valid request this build does not serve    */
+#define W4_ERR_UNSUPPORTED (-4)   /* valid request the library does not serve   */
 #define W4_ERR_WORKSPACE (-5)     /* workspace missing or too small             */
 #define W4_ERR_NONFINITE (-6)     /* quantise: Inf or NaN in the input          */
 #define W4_ERR_RANGE (-7)         /* quantise: block scale overflows its format */
@@ -262,7 +262,7 @@ int w4_bench_stream_read(const void *src, size_t bytes, uint32_t *sink, void *st
  *     shared_w2   groups = 1, n = H, k = shared_inter
  *                 in the routed experts' format or both W4_FMT_BF16
  *     shared_gate_w bf16 [H]: sigma = sigmoid(shared_gate_w . x)
- * This build requires shared_inter == inter and H % 64 == 0; the routed experts
+ * The library requires shared_inter == inter and H % 64 == 0; the routed experts
  * use one format (NVFP4: one global scale per expert matrix, applied to the
  * gate/up sums and to the down sums), the shared expert that format or bf16
  * (MXFP4: that format only). */
