@@ -331,12 +331,13 @@ int moe_w4a16_forward_timed(const moe_w4a16_layer *L, const uint16_t *x, int64_t
  * expert in MXFP4 (W4_ERR_UNSUPPORTED otherwise); from T = 4 they run 6
  * kernels (router; x to MXFP8; top-k and grouping; W13 + SiLU with h quantised
  * to MXFP8; W2; ordered combine), below it the 3 single-token kernels, which
- * quantise x and h in registers.  Batches of more than 1024 (token, slot)
- * pairs (T > 128 at top-8; at most 65536 pairs, T <= 16384) group their pairs
- * over three launches (per-block top-k and expert histograms; one scan; a
- * scatter) instead of one, so the grouped path takes 7 kernels (MXFP4: 8), and
- * run W13 and W2 as grouped GEMMs with LDS-staged activations; from T = 160
- * the router runs on MFMA.  E2M1 requests beyond 65536 pairs take the
+ * quantise x and h in registers.  E2M1, NVFP4 and MXFP4 batches of more than
+ * 1024 (token, slot) pairs (T > 128 at top-8; at most 65536 pairs, T <= 16384)
+ * group their pairs over three launches (per-block top-k and expert
+ * histograms; one scan; a scatter) instead of one, so the grouped path takes 7
+ * kernels (MXFP4: 8), and run W13 and W2 as grouped GEMMs with LDS-staged
+ * activations; int4 batches keep the one-launch grouping and the per-group
+ * kernels up to their 4096-pair limit; from T = 160 the router runs on MFMA.  E2M1 requests beyond 65536 pairs take the
  * single-token path; MXFP4 ones fail with W4_ERR_UNSUPPORTED.
  * Sources: lynn-engine README, R5 notes (tokens-per-expert grouping, inverse
  * scatter) and P85-P92 (per-16 scales applied exactly). */
